@@ -1,0 +1,443 @@
+"""fp64 CPU oracle of the flow-matching action-expert Euler denoise loop.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+CPU-baseline leg may import this module.  It is plain NumPy in float64,
+written from the pages' description of the method; it shares no code,
+table or constant with the GPU library.
+
+What the method computes, and where the pages fix it
+----------------------------------------------------
+* A flow-matching policy turns noise into an action chunk by integrating a
+  learned velocity field with explicit Euler steps, 10 of them: FlowEdge
+  README, "Installation" (the flow sampler run as "euler 10"), and the
+  realtime-vla write-up, "The latency table, and what it assumes" (10 flow
+  steps per prediction).
+* Each velocity evaluation runs the action expert over the suffix tokens
+  (one state token plus the noisy action chunk).  Those tokens attend to the
+  vision/prompt prefix, whose keys and values do not depend on the flow
+  time, so they are computed once and reused by every step: Reflex abstract
+  (Timestep-Invariance Property; full-batch-equivalent attention outputs).
+* The prefix context splits into a static region (prompt), a sliding window
+  of camera frames updated in O(1) per frame, and the dynamic suffix:
+  Reflex abstract.
+* AdaRMSNorm takes its modulation from the flow phase: Reflex abstract.
+* State is a 32-vector and the noise is (chunk, 32): realtime-vla write-up,
+  "Copying an inference file into your own project".
+* fp8 execution of the weights: InstinctFlash README, "Load a model"
+  (precision="fp8") and "Architecture" (HARDWARE layer, fp8/int8).
+
+Readings taken where the pages are silent
+-----------------------------------------
+* Time runs from t=1 (noise) to t=0 (action); dt = -1/N; the velocity at
+  step k is evaluated at the left end t_k = 1 - k/N, computed directly.
+* Sinusoidal time features: [sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(D/2)),
+  j < D/2, t unscaled.  Additive experts add the d-wide feature to the
+  action tokens only (not the state token); the AdaRMSNorm expert takes
+  time only through its norms.
+* AdaRMSNorm: c = SiLU(W_t tau_256(t) + b_t); each norm n has its own linear
+  giving (gamma, beta, alpha) = split3(W_n c + b_n); the norm output is
+  rms(h) * (1 + gamma) + beta and alpha scales the residual branch it feeds.
+  The final norm uses gamma and beta only.
+* RMSNorm: h / sqrt(mean(h^2) + eps) * g.  GELU is the exact erf form.
+* Transformer linears have no bias; the action-in, state, action-out, time
+  and modulation linears do.
+* Attention: scale 1/sqrt(head_dim), no mask (full to the prefix,
+  bidirectional in the suffix), no positions; query head h reads KV head
+  floor(h * Hkv / Hq).
+* fp8 weights are OCP E4M3FN with one fp32 scale per output channel,
+  s = max|w| / 448 (1 when the row is zero), codes = round-to-nearest-even
+  of the fp32 quotient w / s, saturating at +-448.  The loop then uses the
+  dequantised weights code * s exactly.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "time_grid", "sinusoid", "linear", "rms_inv", "rmsnorm", "ada_rmsnorm",
+    "silu", "gelu", "softmax_rows", "attention", "masked_attention",
+    "ada_modulation", "euler", "expert_velocity", "denoise", "denoise_robot",
+    "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_e4m3_per_channel",
+    "effective_weights", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
+    "joint_velocity", "denoise_joint", "rel_l2", "max_abs",
+]
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# Schedule and time features
+# ---------------------------------------------------------------------------
+def time_grid(n_steps: int) -> Tuple[np.ndarray, float]:
+    """Euler schedule t_k = 1 - k/N, k = 0..N-1, and dt = -1/N (see module
+    docstring: direction and left-endpoint evaluation are this code's
+    reading; the step count is the pages' 10 flow steps)."""
+    k = np.arange(n_steps, dtype=F64)
+    return 1.0 - k / n_steps, -1.0 / n_steps
+
+
+def sinusoid(t: float, dim: int) -> np.ndarray:
+    """Sinusoidal features of a scalar time: [sin(t w) | cos(t w)]."""
+    half = dim // 2
+    j = np.arange(half, dtype=F64)
+    w = 10000.0 ** (-j / half)
+    return np.concatenate([np.sin(t * w), np.cos(t * w)])
+
+
+# ---------------------------------------------------------------------------
+# Primitives
+# ---------------------------------------------------------------------------
+def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray] = None) -> np.ndarray:
+    """y = x W^T (+ b), W stored [out][in]."""
+    y = np.asarray(x, F64) @ np.asarray(w, F64).T
+    if b is not None:
+        y = y + np.asarray(b, F64)
+    return y
+
+
+def rms_inv(h: np.ndarray, eps: float) -> np.ndarray:
+    """1 / sqrt(mean over the last axis of h^2 + eps)."""
+    return 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+
+
+def rmsnorm(h: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    return h * rms_inv(h, eps) * np.asarray(g, F64)
+
+
+def ada_rmsnorm(h, gamma, beta, eps: float) -> np.ndarray:
+    """AdaRMSNorm (Reflex abstract): normalised h, scaled by (1 + gamma) and
+    shifted by beta, both taken from the flow-phase embedding."""
+    return h * rms_inv(h, eps) * (1.0 + gamma) + beta
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU: x * Phi(x) = x/2 (1 + erf(x / sqrt 2))."""
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Unmasked multi-query attention.
+
+    q [Sq][Hq][Dh], k and v [Tk][Hkv][Dh]; query head h uses KV head
+    floor(h*Hkv/Hq); scores are scaled by 1/sqrt(Dh).  Returns [Sq][Hq][Dh].
+    """
+    sq, hq, dh = q.shape
+    hkv = k.shape[1]
+    out = np.empty((sq, hq, dh), F64)
+    scale = 1.0 / math.sqrt(dh)
+    for h in range(hq):
+        j = (h * hkv) // hq
+        p = softmax_rows((q[:, h, :] @ k[:, j, :].T) * scale)
+        out[:, h, :] = p @ v[:, j, :]
+    return out
+
+
+def masked_attention(q, k, v, allowed: np.ndarray) -> np.ndarray:
+    """Attention with a boolean [Sq][Tk] mask (True = may attend).  Written
+    separately from `attention` so that the cached-prefix path can be checked
+    against a joint-sequence recompute."""
+    sq, hq, dh = q.shape
+    hkv = k.shape[1]
+    out = np.zeros((sq, hq, dh), F64)
+    for h in range(hq):
+        j = (h * hkv) // hq
+        s = np.einsum("qd,kd->qk", q[:, h, :], k[:, j, :]) / math.sqrt(dh)
+        s = np.where(allowed, s, -np.inf)
+        m = np.max(s, axis=1, keepdims=True)
+        e = np.where(allowed, np.exp(s - m), 0.0)
+        out[:, h, :] = np.einsum("qk,kd->qd", e / e.sum(axis=1, keepdims=True), v[:, j, :])
+    return out
+
+
+def rel_l2(a, ref) -> float:
+    a, ref = np.asarray(a, F64), np.asarray(ref, F64)
+    return float(np.linalg.norm((a - ref).ravel()) / np.linalg.norm(ref.ravel()))
+
+
+def max_abs(a, ref) -> float:
+    return float(np.max(np.abs(np.asarray(a, F64) - np.asarray(ref, F64))))
+
+
+# ---------------------------------------------------------------------------
+# fp8 E4M3FN (OCP) weights
+# ---------------------------------------------------------------------------
+FP8_MATRICES = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def _e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3FN code: 1 sign, 4 exponent bits (bias 7),
+    3 mantissa bits, subnormals at exponent 0, 0x7F/0xFF NaN, no infinity."""
+    sgn = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sgn * m * 2.0 ** -9
+    return sgn * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_values() -> np.ndarray:
+    """The 256 code values, indexed by code."""
+    return np.array([_e4m3_value(c) for c in range(256)], F64)
+
+
+_POS = e4m3_values()[:127]  # codes 0..126: 0 .. 448, strictly increasing
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return e4m3_values()[np.asarray(codes, np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round float32 values to E4M3FN codes: nearest, ties to the even code,
+    saturating at +-448; the sign bit follows the sign of x (so negative
+    values that round to zero give 0x80)."""
+    x = np.asarray(x, np.float32).astype(F64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dlo, dhi = a - _POS[lo], _POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    mag = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return (mag | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def quantize_e4m3_per_channel(w) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-output-channel E4M3 quantisation of W[out][in]: scale
+    s = max|w_row| / 448 in float32 (1 for an all-zero row), codes of the
+    float32 quotient w / s.  Returns (codes uint8 [out][in], s float32 [out])."""
+    w = np.asarray(w, np.float32)
+    amax = np.max(np.abs(w), axis=1)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (w / s[:, None]).astype(np.float32)
+    return e4m3_encode(q), s
+
+
+def effective_weights(cfg, W: dict) -> dict:
+    """Weights as the loop uses them, in float64.  For an fp8 workload the
+    seven per-layer matrices are replaced by their dequantised fp8 values
+    (code * scale); everything else converts exactly."""
+    out = {k: np.asarray(v, F64) for k, v in W.items() if k != "layers"}
+    out["layers"] = []
+    for L in W["layers"]:
+        E = {}
+        for k, v in L.items():
+            if cfg.weight_dtype == "fp8" and k in FP8_MATRICES:
+                codes, s = quantize_e4m3_per_channel(v)
+                E[k] = e4m3_decode(codes) * s.astype(F64)[:, None]
+            else:
+                E[k] = np.asarray(v, F64)
+        out["layers"].append(E)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The action expert's velocity and the Euler loop
+# ---------------------------------------------------------------------------
+def ada_modulation(cfg, W: dict, t: float):
+    """(gamma, beta, alpha) of every norm at flow time t: per layer
+    [(norm1), (norm2)], then the final norm."""
+    c = silu(linear(sinusoid(t, cfg.time_dim), W["w_time"], W["b_time"]))
+    d = cfg.d_model
+
+    def split(wn, bn):
+        m = linear(c, wn, bn)
+        return m[:d], m[d:2 * d], m[2 * d:]
+
+    per_layer = [(split(L["norm1_w"], L["norm1_b"]), split(L["norm2_w"], L["norm2_b"]))
+                 for L in W["layers"]]
+    return per_layer, split(W["norm_f_w"], W["norm_f_b"])
+
+
+def _norm(cfg, h, gain, mod):
+    if cfg.norm == "rms":
+        return rmsnorm(h, gain, cfg.rms_eps)
+    gamma, beta, _ = mod
+    return ada_rmsnorm(h, gamma, beta, cfg.rms_eps)
+
+
+def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
+                    v_pre: np.ndarray, state: Optional[np.ndarray]) -> np.ndarray:
+    """Velocity v(x, t) of one robot.
+
+    x [chunk][A]; k_pre, v_pre [layers][T][Hkv][Dh] in logical order; state
+    [state_dim] or None.  W holds float64 weights (see effective_weights).
+    Returns v [chunk][A].
+    """
+    S_has = 1 if cfg.state_dim else 0
+    hq, hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    act = linear(np.asarray(x, F64), W["w_in"], W["b_in"])
+    if cfg.norm == "rms":
+        act = act + sinusoid(t, cfg.d_model)
+    if S_has:
+        h = np.vstack([linear(np.asarray(state, F64), W["w_state"], W["b_state"])[None], act])
+    else:
+        h = act
+    S = h.shape[0]
+    mods, mod_f = ada_modulation(cfg, W, t) if cfg.norm == "ada" else (None, None)
+    for li, L in enumerate(W["layers"]):
+        m1, m2 = mods[li] if mods else (None, None)
+        u = _norm(cfg, h, L.get("norm1"), m1)
+        q = linear(u, L["wq"]).reshape(S, hq, dh)
+        k = linear(u, L["wk"]).reshape(S, hkv, dh)
+        v = linear(u, L["wv"]).reshape(S, hkv, dh)
+        K = np.concatenate([np.asarray(k_pre[li], F64), k], axis=0)
+        V = np.concatenate([np.asarray(v_pre[li], F64), v], axis=0)
+        o = attention(q, K, V).reshape(S, hq * dh)
+        a1 = m1[2] if m1 else 1.0
+        h = h + a1 * linear(o, L["wo"])
+        u = _norm(cfg, h, L.get("norm2"), m2)
+        z = gelu(linear(u, L["wg"])) * linear(u, L["wu"])
+        a2 = m2[2] if m2 else 1.0
+        h = h + a2 * linear(z, L["wd"])
+    u = _norm(cfg, h[S_has:], W.get("norm_f"), mod_f)
+    return linear(u, W["w_out"], W["b_out"])
+
+
+def euler(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
+          n_steps: int) -> np.ndarray:
+    """x_{k+1} = x_k + dt * v(x_k, t_k) over the schedule of time_grid."""
+    ts, dt = time_grid(n_steps)
+    x = np.asarray(x0, F64).copy()
+    for t in ts:
+        x = x + dt * velocity(x, float(t))
+    return x
+
+
+def denoise_robot(cfg, W64: dict, k_pre, v_pre, noise, state) -> np.ndarray:
+    """One robot's action chunk x at t=0 from its noise at t=1."""
+    return euler(lambda x, t: expert_velocity(cfg, W64, x, t, k_pre, v_pre, state),
+                 noise, cfg.n_steps)
+
+
+def denoise(cfg, W: dict, k_pre, v_pre, noise, state=None,
+            robots: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Batch of independent robots.  k_pre/v_pre [B][layers][T][Hkv][Dh],
+    noise [B][chunk][A], state [B][state_dim] or None.  `robots` picks a
+    subset (the result then has len(robots) rows)."""
+    W64 = effective_weights(cfg, W)
+    idx = range(noise.shape[0]) if robots is None else robots
+    return np.stack([denoise_robot(cfg, W64, k_pre[b], v_pre[b], noise[b],
+                                   None if state is None else state[b]) for b in idx])
+
+
+# ---------------------------------------------------------------------------
+# Streaming prefix: static prompt + sliding window of frames (Reflex abstract)
+# ---------------------------------------------------------------------------
+class PrefixRing:
+    """Static region plus a ring of `n_frames` frame slots.  `set` takes the
+    logical order (static, then frames oldest to newest); `append` overwrites
+    the oldest frame in O(1); `logical` returns the prefix in logical order."""
+
+    def __init__(self, static_tokens: int, frame_tokens: int, n_frames: int):
+        self.ns, self.nf, self.F = static_tokens, frame_tokens, n_frames
+        self.static = None
+        self.slots: List[np.ndarray] = []
+        self.head = 0
+
+    def set(self, kv: np.ndarray):
+        """kv [layers][static + F*frame][...]."""
+        self.static = kv[:, :self.ns]
+        self.slots = [kv[:, self.ns + j * self.nf: self.ns + (j + 1) * self.nf]
+                      for j in range(self.F)]
+        self.head = 0
+
+    def append(self, frame: np.ndarray):
+        self.slots[self.head] = frame
+        self.head = (self.head + 1) % self.F
+
+    def logical(self) -> np.ndarray:
+        order = [self.slots[(self.head + j) % self.F] for j in range(self.F)]
+        return np.concatenate([self.static] + order, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Joint-sequence recompute (checks the timestep-invariant cached prefix)
+# ---------------------------------------------------------------------------
+def _prefix_layer_qkv(cfg, Lp, hp):
+    T = hp.shape[0]
+    u = rmsnorm(hp, Lp["norm1"], cfg.rms_eps)
+    return (linear(u, Lp["wq"]).reshape(T, cfg.n_q_heads, cfg.head_dim),
+            linear(u, Lp["wk"]).reshape(T, cfg.n_kv_heads, cfg.head_dim),
+            linear(u, Lp["wv"]).reshape(T, cfg.n_kv_heads, cfg.head_dim))
+
+
+def _prefix_layer_rest(cfg, Lp, hp, o):
+    hp = hp + linear(o.reshape(hp.shape[0], -1), Lp["wo"])
+    u = rmsnorm(hp, Lp["norm2"], cfg.rms_eps)
+    return hp + linear(gelu(linear(u, Lp["wg"])) * linear(u, Lp["wu"]), Lp["wd"])
+
+
+def prefix_stack_kv(cfg, Wp: dict, tokens: np.ndarray):
+    """Run a prefix encoder (own RMSNorm transformer weights; prefix tokens
+    attend to the prefix only) and return its per-layer K and V,
+    [layers][T][Hkv][Dh]: the cache the denoise loop reads."""
+    hp = np.asarray(tokens, F64)
+    Ks, Vs = [], []
+    for Lp in Wp["layers"]:
+        q, k, v = _prefix_layer_qkv(cfg, Lp, hp)
+        Ks.append(k)
+        Vs.append(v)
+        hp = _prefix_layer_rest(cfg, Lp, hp, attention(q, k, v))
+    return np.stack(Ks), np.stack(Vs)
+
+
+def joint_velocity(cfg, W64: dict, Wp: dict, tokens, x, t, state) -> np.ndarray:
+    """Velocity from a full recompute of [prefix tokens | suffix] as one
+    sequence, every call.  Prefix rows use the prefix weights and see only
+    prefix keys; suffix rows use the expert weights and see every key."""
+    S_has = 1 if cfg.state_dim else 0
+    hq, hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    hp = np.asarray(tokens, F64)
+    T = hp.shape[0]
+    act = linear(np.asarray(x, F64), W64["w_in"], W64["b_in"])
+    if cfg.norm == "rms":
+        act = act + sinusoid(t, cfg.d_model)
+    hs = act if not S_has else np.vstack(
+        [linear(np.asarray(state, F64), W64["w_state"], W64["b_state"])[None], act])
+    S = hs.shape[0]
+    allowed = np.ones((T + S, T + S), bool)
+    allowed[:T, T:] = False
+    mods, mod_f = ada_modulation(cfg, W64, t) if cfg.norm == "ada" else (None, None)
+    for li, (L, Lp) in enumerate(zip(W64["layers"], Wp["layers"])):
+        m1, m2 = mods[li] if mods else (None, None)
+        qp, kp, vp = _prefix_layer_qkv(cfg, Lp, hp)
+        u = _norm(cfg, hs, L.get("norm1"), m1)
+        qs = linear(u, L["wq"]).reshape(S, hq, dh)
+        ks = linear(u, L["wk"]).reshape(S, hkv, dh)
+        vs = linear(u, L["wv"]).reshape(S, hkv, dh)
+        o = masked_attention(np.concatenate([qp, qs]), np.concatenate([kp, ks]),
+                             np.concatenate([vp, vs]), allowed)
+        hp = _prefix_layer_rest(cfg, Lp, hp, o[:T])
+        a1 = m1[2] if m1 else 1.0
+        hs = hs + a1 * linear(o[T:].reshape(S, hq * dh), L["wo"])
+        u = _norm(cfg, hs, L.get("norm2"), m2)
+        a2 = m2[2] if m2 else 1.0
+        hs = hs + a2 * linear(gelu(linear(u, L["wg"])) * linear(u, L["wu"]), L["wd"])
+    u = _norm(cfg, hs[S_has:], W64.get("norm_f"), mod_f)
+    return linear(u, W64["w_out"], W64["b_out"])
+
+
+def denoise_joint(cfg, W: dict, Wp: dict, tokens, noise, state=None) -> np.ndarray:
+    """Euler loop whose every step recomputes the whole joint sequence."""
+    W64 = effective_weights(cfg, W)
+    Wp64 = {"layers": [{k: np.asarray(v, F64) for k, v in L.items()} for L in Wp["layers"]]}
+    out = []
+    for b in range(noise.shape[0]):
+        st = None if state is None else state[b]
+        out.append(euler(lambda x, t: joint_velocity(cfg, W64, Wp64, tokens[b], x, t, st),
+                         noise[b], cfg.n_steps))
+    return np.stack(out)

@@ -1,0 +1,394 @@
+"""Pins of the fp64 oracle against facts it does not compute itself: closed
+forms, special cases that reduce to a simpler formula, invariants the pages
+state, brute force on tiny inputs and the OCP fp8 code table.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign, index or scale, a transposed operand) fails at least one test.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import fm_synth as S
+import oracle as O
+
+TINY = S.workload("tiny_fp32")
+
+
+def _tiny(**kw):
+    return TINY.replace(**kw)
+
+
+def _inputs(cfg):
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    return W, k, v, S.make_noise(cfg), S.make_state(cfg)
+
+
+# --- P1: the integrator and its schedule -----------------------------------
+def test_time_grid_is_left_endpoints_from_one():
+    ts, dt = O.time_grid(10)
+    assert dt == -0.1
+    assert np.allclose(ts, [1.0, 0.9, 0.8, 0.7, 0.6, 0.5, 0.4, 0.3, 0.2, 0.1], atol=0, rtol=1e-15)
+    assert ts[0] == 1.0
+
+
+def test_euler_linear_field_closed_form():
+    # v = lam * x  =>  x_N = (1 + dt*lam)^N x0 = (1 - lam/N)^N x0
+    x0 = np.array([1.5, -2.0, 0.25])
+    for lam, n in ((0.7, 10), (-1.3, 8), (2.0, 1)):
+        got = O.euler(lambda x, t: lam * x, x0, n)
+        assert np.allclose(got, (1 - lam / n) ** n * x0, rtol=1e-14, atol=0)
+
+
+def test_euler_time_field_displacement():
+    # v = t: displacement sum_k dt*t_k = -(N+1)/(2N) = -0.55 at N=10 (a right
+    # end point scheme would give -0.45, the midpoint rule -0.5).
+    got = O.euler(lambda x, t: np.full_like(x, t), np.zeros(1), 10)
+    assert abs(got[0] - (-0.55)) < 1e-15
+    got = O.euler(lambda x, t: np.full_like(x, t), np.zeros(1), 4)
+    assert abs(got[0] - (-5 / 8)) < 1e-15
+
+
+# --- P2 / P3: output plumbing of the head ------------------------------------
+def test_zero_head_leaves_noise_bitwise():
+    cfg = TINY
+    W, k, v, x0, st = _inputs(cfg)
+    W["w_out"][:] = 0
+    W["b_out"][:] = 0
+    assert np.array_equal(O.denoise(cfg, W, k, v, x0, st), x0.astype(np.float64))
+
+
+def test_bias_only_head_integrates_constant_velocity_exactly():
+    # N = 8 (dt = -1/8) with dyadic b and x0: every update is exact, so
+    # x_N = x0 + N*dt*b = x0 - b bitwise.
+    cfg = _tiny(n_steps=8)
+    W, k, v, _, st = _inputs(cfg)
+    g = np.random.default_rng(5)
+    b = g.integers(-64, 64, size=cfg.action_dim) / 16.0
+    x0 = (g.integers(-128, 128, size=(1, cfg.chunk, cfg.action_dim)) / 32.0)
+    W["w_out"][:] = 0
+    W["b_out"] = b.astype(np.float32)
+    got = O.denoise(cfg, W, k, v, x0, st)
+    assert np.array_equal(got, x0 - b)
+    # N = 10: dt is inexact, the error stays within a few ulp
+    cfg = TINY
+    got = O.denoise(cfg, W, k, v, x0, st)
+    assert np.max(np.abs(got - (x0 - b))) < 20 * np.finfo(float).eps * 8
+
+
+# --- P4: time-only velocity reduces to a short closed form -------------------
+def test_time_only_velocity_matches_closed_form():
+    cfg = TINY
+    W, k, v, x0, st = _inputs(cfg)
+    W["w_in"][:] = 0
+    for L in W["layers"]:
+        L["wo"][:] = 0
+        L["wd"][:] = 0
+    got = O.denoise(cfg, W, k, v, x0, st)[0]
+    d = cfg.d_model
+    expect = x0[0].astype(np.float64).copy()
+    for kstep in range(cfg.n_steps):
+        t = 1.0 - kstep / cfg.n_steps
+        tau = [math.sin(t * 10000.0 ** (-j / (d // 2))) for j in range(d // 2)] + \
+              [math.cos(t * 10000.0 ** (-j / (d // 2))) for j in range(d // 2)]
+        h = [float(W["b_in"][i]) + tau[i] for i in range(d)]
+        r = 1.0 / math.sqrt(math.fsum(a * a for a in h) / d + cfg.rms_eps)
+        u = [h[i] * r * float(W["norm_f"][i]) for i in range(d)]
+        vel = [math.fsum(u[i] * float(W["w_out"][a, i]) for i in range(d)) + float(W["b_out"][a])
+               for a in range(cfg.action_dim)]
+        expect = expect + (-1.0 / cfg.n_steps) * np.array(vel)[None, :]
+    assert np.max(np.abs(got - expect)) < 1e-12
+
+
+# --- P5 / P6: attention ---------------------------------------------------------
+def test_attention_scale_is_inverse_sqrt_head_dim():
+    # Dh = 4: q.k1 = 2 ln 3 -> scaled score ln 3 against 0: weights 3:1.
+    q = np.array([[[2 * math.log(3), 0, 0, 0]]])
+    k = np.array([[[1.0, 0, 0, 0]], [[0.0, 0, 0, 0]]])
+    v = np.array([[[4.0, 0, 8, 1]], [[0.0, 4, 0, 1]]])
+    out = O.attention(q, k, v)[0, 0]
+    assert np.allclose(out, (3 * v[0, 0] + v[1, 0]) / 4, rtol=0, atol=1e-14)
+
+
+def test_attention_equal_scores_give_mean_and_dominant_key_wins():
+    g = np.random.default_rng(1)
+    v = g.standard_normal((6, 1, 3))
+    q = g.standard_normal((2, 1, 3))
+    k = np.zeros((6, 1, 3))
+    assert np.allclose(O.attention(q, k, v)[:, 0], v[:, 0].mean(0), atol=1e-14)
+    k = g.standard_normal((6, 1, 3)) * 0.01
+    k[4, 0] = q[0, 0] * 400.0
+    assert np.allclose(O.attention(q[:1], k, v)[0, 0], v[4, 0], atol=1e-12)
+
+
+def test_attention_brute_force_tiny():
+    g = np.random.default_rng(2)
+    Sq, T, Dh, Hq, Hkv = 4, 6, 3, 2, 1
+    q = g.standard_normal((Sq, Hq, Dh))
+    k = g.standard_normal((T, Hkv, Dh))
+    v = g.standard_normal((T, Hkv, Dh))
+    got = O.attention(q, k, v)
+    for h in range(Hq):
+        for i in range(Sq):
+            sc = [math.fsum(q[i, h, c] * k[j, 0, c] for c in range(Dh)) / math.sqrt(Dh)
+                  for j in range(T)]
+            w = [math.exp(s) for s in sc]
+            z = math.fsum(w)
+            for c in range(Dh):
+                ref = math.fsum(w[j] * v[j, 0, c] for j in range(T)) / z
+                assert abs(got[i, h, c] - ref) < 1e-13
+    p = O.softmax_rows(g.standard_normal((5, 7)) * 30)
+    assert np.allclose(p.sum(1), 1.0, atol=1e-15)
+
+
+def test_attention_key_permutation_and_split_lse_combine():
+    g = np.random.default_rng(3)
+    q = g.standard_normal((5, 4, 8))
+    k = g.standard_normal((11, 2, 8))
+    v = g.standard_normal((11, 2, 8))
+    full = O.attention(q, k, v)
+    perm = g.permutation(11)
+    assert np.allclose(O.attention(q, k[perm], v[perm]), full, atol=1e-14)
+    # split the keys in two, combine the halves by their log-sum-exp
+    for cut in (1, 5, 10):
+        parts = []
+        for sl in (slice(0, cut), slice(cut, 11)):
+            o = O.attention(q, k[sl], v[sl])
+            lse = np.zeros((5, 4))
+            for h in range(4):
+                s = q[:, h] @ k[sl, h // 2].T / math.sqrt(8)
+                lse[:, h] = np.log(np.exp(s).sum(1))
+            parts.append((o, lse))
+        m = np.maximum(parts[0][1], parts[1][1])
+        w0, w1 = np.exp(parts[0][1] - m), np.exp(parts[1][1] - m)
+        comb = (parts[0][0] * w0[..., None] + parts[1][0] * w1[..., None]) / (w0 + w1)[..., None]
+        assert np.allclose(comb, full, atol=1e-13)
+
+
+# --- P10: grouped-query head mapping -----------------------------------------
+def test_gqa_equals_mha_with_repeated_kv():
+    g = np.random.default_rng(4)
+    q = g.standard_normal((3, 4, 8))
+    k = g.standard_normal((7, 2, 8))
+    v = g.standard_normal((7, 2, 8))
+    # query heads 0,1 -> kv head 0; 2,3 -> kv head 1
+    rep = O.attention(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1))
+    assert np.allclose(O.attention(q, k, v), rep, atol=1e-14)
+    k1, v1 = k[:, :1], v[:, :1]
+    assert np.allclose(O.attention(q, k1, v1), O.attention(q, np.repeat(k1, 4, 1), np.repeat(v1, 4, 1)),
+                       atol=1e-14)
+
+
+def test_gqa_model_equals_mha_model_with_tiled_kv_weights():
+    cfg1 = _tiny(n_kv_heads=1)
+    W, _, _, x0, st = _inputs(cfg1)
+    k, v = S.make_prefix(cfg1)
+    cfgm = _tiny(n_kv_heads=4)
+    Wm = {kk: vv for kk, vv in W.items()}
+    Wm["layers"] = [dict(L, wk=np.tile(L["wk"], (4, 1)), wv=np.tile(L["wv"], (4, 1)))
+                    for L in W["layers"]]
+    a = O.denoise(cfg1, W, k, v, x0, st)
+    b = O.denoise(cfgm, Wm, np.repeat(k, 4, axis=3), np.repeat(v, 4, axis=3), x0, st)
+    assert O.rel_l2(a, b) < 1e-13
+
+
+# --- P11: norms, GELU, SiLU, sinusoid -------------------------------------------
+def test_rmsnorm_closed_forms():
+    h = np.array([[3.0, 4.0]])
+    assert np.allclose(O.rmsnorm(h, np.ones(2), 0.0), h / math.sqrt(12.5), atol=1e-15)
+    c, eps = 0.37, 1e-6
+    g = np.array([1.0, 2.0, -0.5, 3.0])
+    assert np.allclose(O.rmsnorm(np.full((1, 4), c), g, eps), c / math.sqrt(c * c + eps) * g, atol=1e-15)
+    x = np.random.default_rng(0).standard_normal((3, 16))
+    assert np.allclose(O.rmsnorm(5.0 * x, np.ones(16), 0.0), O.rmsnorm(x, np.ones(16), 0.0), atol=1e-14)
+
+
+def test_gelu_is_exact_erf_form():
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    # Phi(1) of the standard normal distribution
+    assert abs(O.gelu(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+    x = np.linspace(-6, 6, 97)
+    assert np.allclose(O.gelu(x) - O.gelu(-x), x, atol=1e-14)
+    assert abs(O.gelu(np.array([1.0]))[0] - math.tanh(1.0)) > 1e-2  # not some other curve
+    # the tanh approximation differs by ~1e-4 at x = 1.5: the exact form is used
+    tanh_approx = 0.5 * 1.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * (1.5 + 0.044715 * 1.5 ** 3)))
+    assert abs(O.gelu(np.array([1.5]))[0] - 1.5 * 0.5 * (1 + math.erf(1.5 / math.sqrt(2)))) < 1e-15
+    assert abs(O.gelu(np.array([1.5]))[0] - tanh_approx) > 1e-5
+
+
+def test_silu_values():
+    assert abs(O.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+    assert O.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_sinusoid_values():
+    assert np.array_equal(O.sinusoid(0.0, 8), [0, 0, 0, 0, 1, 1, 1, 1])
+    got = O.sinusoid(1.0, 4)  # w = [1, 10000^(-1/2)] = [1, 0.01]
+    assert np.allclose(got, [math.sin(1), math.sin(0.01), math.cos(1), math.cos(0.01)], atol=1e-16)
+
+
+# --- P7: cached timestep-invariant prefix equals joint recompute ----------------
+@pytest.mark.parametrize("kind", ["rms_mha", "rms_gqa", "ada"])
+def test_cached_prefix_equals_joint_recompute(kind):
+    cfg = {"rms_mha": TINY, "rms_gqa": _tiny(n_kv_heads=1, batch=2),
+           "ada": _tiny(norm="ada", time_dim=16, state_dim=0)}[kind]
+    W = S.make_weights(cfg)
+    x0, st = S.make_noise(cfg), S.make_state(cfg)
+    Wp, tokens = S.make_prefix_stack(cfg, 32)
+    ks, vs = zip(*[O.prefix_stack_kv(cfg, Wp, tokens[b]) for b in range(cfg.batch)])
+    cached = O.denoise(cfg, W, np.stack(ks), np.stack(vs), x0, st)
+    joint = O.denoise_joint(cfg, W, Wp, tokens, x0, st)
+    assert O.rel_l2(cached, joint) < 1e-12
+
+
+# --- P8: ring buffer in logical order ---------------------------------------------
+def test_ring_logical_order_after_appends():
+    ns, nf, F = 2, 3, 3
+    r = O.PrefixRing(ns, nf, F)
+    base = np.arange(1 * (ns + F * nf)).reshape(1, -1)
+    r.set(base)
+    assert np.array_equal(r.logical(), base)
+    frames = [np.full((1, nf), 100 + i) for i in range(7)]
+    for i, f in enumerate(frames):
+        r.append(f)
+        last = ([base[:, ns + j * nf: ns + (j + 1) * nf] for j in range(F)] + frames[:i + 1])[-F:]
+        assert np.array_equal(r.logical(), np.concatenate([base[:, :ns]] + last, axis=1))
+
+
+# --- P9: AdaRMSNorm special values -------------------------------------------------
+def _ada_cfg():
+    return _tiny(norm="ada", time_dim=16)
+
+
+def test_ada_identity_modulation_reduces_to_rms_expert():
+    cfg_a = _ada_cfg()
+    cfg_r = TINY
+    Wa = S.make_weights(cfg_a)
+    k, v = S.make_prefix(cfg_a)
+    x0, st = S.make_noise(cfg_a), S.make_state(cfg_a)
+    d = cfg_a.d_model
+    ident = np.concatenate([np.zeros(d), np.zeros(d), np.ones(d)])
+    for L in Wa["layers"]:
+        for n in ("norm1", "norm2"):
+            L[n + "_w"][:] = 0
+            L[n + "_b"] = ident.copy()
+    Wa["norm_f_w"][:] = 0
+    Wa["norm_f_b"] = ident.copy()
+    t = 0.7
+    Wr = {kk: vv for kk, vv in Wa.items() if not kk.startswith(("norm_f", "w_time", "b_time"))}
+    Wr["b_in"] = Wa["b_in"] - O.sinusoid(t, d)  # cancel the additive time feature at t
+    Wr["norm_f"] = np.ones(d)
+    Wr["layers"] = [dict(wq=L["wq"], wk=L["wk"], wv=L["wv"], wo=L["wo"], wg=L["wg"], wu=L["wu"],
+                         wd=L["wd"], norm1=np.ones(d), norm2=np.ones(d)) for L in Wa["layers"]]
+    Wa64, Wr64 = O.effective_weights(cfg_a, Wa), O.effective_weights(cfg_r, Wr)
+    va = O.expert_velocity(cfg_a, Wa64, x0[0], t, k[0], v[0], st[0])
+    vr = O.expert_velocity(cfg_r, Wr64, x0[0], t, k[0], v[0], st[0])
+    assert O.rel_l2(va, vr) < 1e-14
+
+
+def test_ada_gamma_minus_one_and_alpha_zero():
+    # alpha = 0 turns every block into the identity, gamma_f = -1 makes the
+    # final norm output beta_f: the velocity is beta_f W_out^T + b_out for
+    # every x and t, so x_N = x0 - (beta_f W_out^T + b_out).
+    cfg = _ada_cfg()
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    x0, st = S.make_noise(cfg), S.make_state(cfg)
+    d = cfg.d_model
+    beta_f = np.random.default_rng(9).standard_normal(d)
+    for L in W["layers"]:
+        for n in ("norm1", "norm2"):
+            L[n + "_w"][:] = 0
+            L[n + "_b"] = np.concatenate([np.zeros(d), np.zeros(d), np.zeros(d)])
+    W["norm_f_w"][:] = 0
+    W["norm_f_b"] = np.concatenate([-np.ones(d), beta_f, np.zeros(d)])
+    vel = beta_f @ W["w_out"].astype(np.float64).T + W["b_out"]
+    got = O.denoise(cfg, W, k, v, x0, st)
+    assert np.max(np.abs(got - (x0 - vel))) < 1e-13
+
+
+# --- P12: robots are independent ------------------------------------------------
+def test_batch_independence():
+    cfg = _tiny(batch=3)
+    W, k, v, x0, st = _inputs(cfg)
+    full = O.denoise(cfg, W, k, v, x0, st)
+    for b in range(3):
+        one = O.denoise(cfg.replace(batch=1), W, k[b:b + 1], v[b:b + 1], x0[b:b + 1], st[b:b + 1])
+        assert np.array_equal(one[0], full[b])
+    assert O.rel_l2(full[0], full[1]) > 0.1
+
+
+# --- P13: OCP E4M3FN codes -----------------------------------------------------------
+def test_e4m3_code_table():
+    # Values of the OCP 8-bit floating point (OFP8) E4M3 format.
+    vals = O.e4m3_values()
+    assert vals[0x00] == 0.0 and vals[0x01] == 2.0 ** -9 and vals[0x07] == 7 * 2.0 ** -9
+    assert vals[0x08] == 2.0 ** -6 and vals[0x38] == 1.0 and vals[0x39] == 1.125
+    assert vals[0x7E] == 448.0 and math.isnan(vals[0x7F]) and math.isnan(vals[0xFF])
+    assert vals[0xB8] == -1.0 and vals[0xFE] == -448.0
+    finite = vals[:127]
+    assert np.all(np.diff(finite) > 0)
+
+
+def test_e4m3_encode_rounding_and_saturation():
+    vals = O.e4m3_values()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(O.e4m3_encode(vals[codes].astype(np.float32)), codes)
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02,
+             2.0 ** -10 * 1.0001: 0x01, 500.0: 0x7E, 464.0: 0x7E, 1e30: 0x7E,
+             -1e9: 0xFE, -2.0 ** -11: 0x80, 240.0: 0x77, 232.0: 0x76, 248.0: 0x78}
+    for x, c in cases.items():
+        assert O.e4m3_encode(np.float32(x))[()] == c, (x, hex(c))
+
+
+def test_e4m3_per_channel_quantisation_error_bound():
+    g = np.random.default_rng(11)
+    w = (g.standard_normal((64, 200)) * np.exp(g.standard_normal((64, 1)))).astype(np.float32)
+    w[3] = 0
+    codes, s = O.quantize_e4m3_per_channel(w)
+    assert s[3] == 1.0 and np.all(codes[3] == 0)
+    deq = O.e4m3_decode(codes) * s[:, None].astype(np.float64)
+    q = np.abs(w.astype(np.float64) / s[:, None])
+    # half a unit in the last place of the E4M3 grid at |q| (ulp 2^(e-3), min 2^-9)
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    half_ulp = 0.5 * 2.0 ** (e - 3) * s[:, None] * (1 + 1e-6)
+    assert np.all(np.abs(deq - w) <= half_ulp + 1e-30)
+    assert np.all(np.max(np.abs(O.e4m3_decode(codes[[0, 1, 2]])), axis=1) == 448.0)
+
+
+def test_fp8_workload_uses_dequantised_matrices_only():
+    cfg = _tiny(weight_dtype="fp8", act_dtype="bf16")
+    W = S.make_weights(cfg)
+    E = O.effective_weights(cfg, W)
+    codes, s = O.quantize_e4m3_per_channel(W["layers"][0]["wg"])
+    assert np.array_equal(E["layers"][0]["wg"], O.e4m3_decode(codes) * s[:, None].astype(np.float64))
+    assert np.array_equal(E["w_in"], W["w_in"].astype(np.float64))
+    assert np.array_equal(E["layers"][1]["norm1"], W["layers"][1]["norm1"].astype(np.float64))
+
+
+# --- structure: suffix rows, state token, time only on action rows --------------------
+def test_state_token_reaches_actions_only_through_attention():
+    cfg = TINY
+    W, k, v, x0, st = _inputs(cfg)
+    a = O.denoise(cfg, W, k, v, x0, st)
+    b = O.denoise(cfg, W, k, v, x0, st * 0 + 3.0)
+    assert O.rel_l2(a, b) > 1e-3
+    for L in W["layers"]:
+        L["wk"][:] = 0  # uniform attention: still reads V of the state row
+    c = O.denoise(cfg, W, k, v, x0, st)
+    for L in W["layers"]:
+        L["wv"][:] = 0
+        L["wo"][:] = 0
+    d1 = O.denoise(cfg, W, k, v, x0, st)
+    d2 = O.denoise(cfg, W, k, v, x0, st * 0 + 3.0)
+    assert np.array_equal(d1, d2) and O.rel_l2(c, d1) > 1e-4
+
+
+def test_empty_prefix_attends_within_suffix_only():
+    cfg = TINY
+    W, k, v, x0, st = _inputs(cfg)
+    e = O.denoise(cfg, W, k[:, :, :0], v[:, :, :0], x0, st)
+    assert np.all(np.isfinite(e)) and O.rel_l2(e, O.denoise(cfg, W, k, v, x0, st)) > 1e-3
