@@ -1,0 +1,191 @@
+"""MI355X (gfx950) flow-matching action-expert denoiser.
+
+A thin Python binding over libfmdenoise.so (include/fm.h).  Every function
+here only marshals arguments: torch supplies device memory and the HIP
+stream, and every step of the denoise loop runs in the library's HIP
+kernels.  Names match the C entry points; `Denoiser` bundles them.
+"""
+import ctypes
+from typing import Optional
+
+from . import _abi
+from ._abi import (FM_ABI_VERSION, FM_BF16, FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC_PERSISTENT,  # noqa: F401
+                   FM_F32, FM_FP8_E4M3, FM_OK, STATUS_NAMES, fm_config, fm_info, fm_weights)
+
+__all__ = ["FMError", "make_config", "fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv",
+           "fm_denoise", "fm_get_info", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
+           "Denoiser", "lib"]
+
+lib = _abi.lib
+
+
+class FMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_DT = {"f32": _abi.FM_F32, "bf16": _abi.FM_BF16, "fp8": _abi.FM_FP8_E4M3}
+
+
+def make_config(cfg, exec_mode: int = FM_EXEC_AUTO) -> fm_config:
+    """fm_config from any object with the workload fields (e.g. fm_synth.FMConfig)."""
+    c = fm_config()
+    c.abi_version = FM_ABI_VERSION
+    for f in ("d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "d_mlp", "action_dim", "chunk",
+              "state_dim", "batch", "n_steps", "prefix_static", "frame_tokens", "n_frames", "time_dim"):
+        setattr(c, f, int(getattr(cfg, f)))
+    c.norm = _abi.FM_ADARMSNORM if cfg.norm == "ada" else _abi.FM_RMSNORM
+    c.weight_dtype = _DT[cfg.weight_dtype]
+    c.act_dtype = _DT[cfg.act_dtype]
+    c.rms_eps = float(cfg.rms_eps)
+    c.exec_mode = int(exec_mode)
+    return c
+
+
+def _check(status: int, ctx=None):
+    if status != FM_OK:
+        raise FMError(status, fm_last_error(ctx))
+
+
+def fm_last_error(ctx=None) -> str:
+    return lib().fm_last_error(ctx).decode(errors="replace")
+
+
+def _dev_tensor(a, dtype, device):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=dtype).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype).contiguous()
+
+
+def fm_create(cfg, weights: dict, stream=None, exec_mode: int = FM_EXEC_AUTO, device="cuda"):
+    """Create a context.  `weights` follows fm_synth.make_weights' layout:
+    host or device arrays in W[out][in] convention; they are converted to
+    the model's weight dtype on `device` (bf16 for bf16 and fp8 models)."""
+    import torch
+    c = make_config(cfg, exec_mode)
+    wdt = torch.float32 if cfg.weight_dtype == "f32" else torch.bfloat16
+    keep = []
+
+    def put(a):
+        t = _dev_tensor(a, wdt, device)
+        keep.append(t)
+        return _ptr(t)
+
+    w = fm_weights()
+    w.w_in, w.b_in = put(weights["w_in"]), put(weights["b_in"])
+    if cfg.state_dim:
+        w.w_state, w.b_state = put(weights["w_state"]), put(weights["b_state"])
+    w.w_out, w.b_out = put(weights["w_out"]), put(weights["b_out"])
+    if cfg.norm == "ada":
+        w.w_time, w.b_time = put(weights["w_time"]), put(weights["b_time"])
+        w.norm_f, w.norm_f_b = put(weights["norm_f_w"]), put(weights["norm_f_b"])
+    else:
+        w.norm_f = put(weights["norm_f"])
+    names = ["wq", "wk", "wv", "wo", "wg", "wu", "wd"]
+    norms = (["norm1", None, "norm2", None] if cfg.norm == "rms"
+             else ["norm1_w", "norm1_b", "norm2_w", "norm2_b"])
+    arr = (ctypes.c_void_p * (cfg.n_layers * _abi.FM_LW_COUNT))()
+    for li, L in enumerate(weights["layers"]):
+        for si, n in enumerate(names + norms):
+            arr[li * _abi.FM_LW_COUNT + si] = put(L[n]) if n else None
+    w.layers = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    ctx = ctypes.c_void_p()
+    st = lib().fm_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(_stream(stream)), ctypes.byref(ctx))
+    _check(st)
+    del keep
+    return ctx
+
+
+def fm_set_prefix_kv(ctx, robot: int, k, v, n_tokens: int):
+    """k, v: device tensors [layers][n_tokens][kv_heads][head_dim] in the activation dtype."""
+    _check(lib().fm_set_prefix_kv(ctx, int(robot), _ptr(k), _ptr(v), int(n_tokens)), ctx)
+
+
+def fm_append_prefix_kv(ctx, robot: int, k_frame, v_frame):
+    _check(lib().fm_append_prefix_kv(ctx, int(robot), _ptr(k_frame), _ptr(v_frame)), ctx)
+
+
+def fm_denoise(ctx, noise, state, actions):
+    """noise, actions: fp32 device tensors [batch][chunk][action_dim]; state or None."""
+    _check(lib().fm_denoise(ctx, _ptr(noise), _ptr(state), _ptr(actions)), ctx)
+
+
+def fm_get_info(ctx) -> fm_info:
+    info = fm_info()
+    _check(lib().fm_get_info(ctx, ctypes.byref(info)), ctx)
+    return info
+
+
+def fm_destroy(ctx):
+    lib().fm_destroy(ctx)
+
+
+def fm_quantize_e4m3(w, codes, scales, stream=None):
+    """w: bf16 device [rows][cols]; codes: uint8 device; scales: fp32 device [rows]."""
+    rows, cols = w.shape
+    _check(lib().fm_quantize_e4m3(_ptr(w), rows, cols, _ptr(codes), _ptr(scales),
+                                  ctypes.c_void_p(_stream(stream))))
+
+
+class Denoiser:
+    """Owns one context: load the prefix, then call `denoise` per chunk."""
+
+    def __init__(self, cfg, weights: dict, stream=None, exec_mode: int = FM_EXEC_AUTO, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.device = device
+        self.act_dtype = torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16
+        self.ctx = fm_create(cfg, weights, stream, exec_mode, device)
+
+    def _act(self, a):
+        return _dev_tensor(a, self.act_dtype, self.device)
+
+    def set_prefix_kv(self, robot: int, k, v):
+        """k, v [layers][tokens][kv_heads][head_dim] (host or device)."""
+        k, v = self._act(k), self._act(v)
+        fm_set_prefix_kv(self.ctx, robot, k, v, k.shape[1])
+        return k, v  # caller keeps them alive until the stream has consumed them
+
+    def append_prefix_kv(self, robot: int, k_frame, v_frame):
+        k, v = self._act(k_frame), self._act(v_frame)
+        fm_append_prefix_kv(self.ctx, robot, k, v)
+        return k, v
+
+    def denoise(self, noise, state=None, out=None):
+        import torch
+        n = _dev_tensor(noise, torch.float32, self.device)
+        s = self._act(state) if state is not None else None
+        if out is None:
+            out = torch.empty_like(n)
+        fm_denoise(self.ctx, n, s, out)
+        return out
+
+    def info(self) -> fm_info:
+        return fm_get_info(self.ctx)
+
+    def close(self):
+        if self.ctx is not None:
+            fm_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

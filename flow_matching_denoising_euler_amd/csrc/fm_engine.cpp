@@ -1,0 +1,662 @@
+// Host side of the C ABI declared in include/fm.h: validation, the one-arena
+// plan, weight repacking / fp8 quantisation, time tables, and the hipGraph
+// of the Euler loop.
+//
+// A context holds everything the loop touches in one device allocation made
+// at create time; fm_denoise and fm_append_prefix_kv allocate nothing
+// (FlowEdge README, "Overview": a pre-sized arena, "warmup (malloc 0)").
+#include "fm.h"
+#include "fm_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace fm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+
+struct Arena {
+  char* base = nullptr;
+  size_t off = 0;
+  bool plan = true;
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = plan ? nullptr : base + off;
+    off += bytes;
+    return p;
+  }
+};
+
+int elt_of(int32_t dt) { return dt == FM_F32 ? ELT_F32 : (dt == FM_BF16 ? ELT_BF16 : ELT_FP8); }
+size_t elt_size(int elt) { return elt == ELT_F32 ? 4 : (elt == ELT_BF16 ? 2 : 1); }
+
+struct LayerW {
+  void *wqkv, *wo, *wgu, *wd;
+  float *sqkv, *so, *sgu, *sd;  // fp8 column scales
+};
+
+}  // namespace
+
+struct fm_ctx {
+  fm_config cfg;
+  hipStream_t stream = nullptr;
+  hipStream_t cap = nullptr;
+  char err[512] = "";
+  bool poisoned = false;
+  int exec_mode = FM_EXEC_GRAPH;
+  int n_cu = 0;
+
+  // dims
+  int act, wt, ge;  // activation, matrix weight, embedding/gain element types
+  int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
+  int ks_o, ks_d, nqblk, nsplit;
+
+  // arena
+  void* arena = nullptr;
+  size_t arena_bytes = 0;
+  std::vector<LayerW> lw;
+  void *wout, *w_in, *b_in, *w_state, *b_state;
+  float *temb, *g1, *g2, *gf, *a1, *a2, *bqkv, *bgu, *bout;
+  long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
+  void *kpre, *vpre;
+  int* meta;
+  float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *partials, *attn_part;
+  void *u, *uf, *qkv, *o, *z;
+  unsigned* counters;
+  size_t n_counters;
+
+  // host mirror of the prefix state
+  std::vector<int> valid, head;
+  std::vector<char> is_set;
+
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+};
+
+namespace {
+
+fm_status fail(fm_ctx* c, fm_status s, const char* fmt, ...) {
+  char* dst = c ? c->err : g_err;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(dst, 512, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fm_status hip_fail(fm_ctx* c, hipError_t e, const char* what) {
+  if (c) c->poisoned = true;
+  return fail(c, FM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCHK(ctx, call, what)                    \
+  do {                                             \
+    hipError_t e_ = (call);                        \
+    if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
+  } while (0)
+
+// largest split s <= want with (kb % s == 0) and (kb / s) % unit == 0
+int pick_split(int K, int want, int unit) {
+  const int kb = K / 32;
+  for (int s = want; s > 1; --s)
+    if (kb % s == 0 && (kb / s) % unit == 0) return s;
+  return 1;
+}
+
+fm_status validate_config(const fm_config* c) {
+  if (!c) return fail(nullptr, FM_ERR_ARG, "cfg is NULL");
+  if (c->abi_version != FM_ABI_VERSION)
+    return fail(nullptr, FM_ERR_ARG, "abi_version %d, library is %d", c->abi_version, FM_ABI_VERSION);
+  if (c->d_model <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->d_mlp <= 0 || c->action_dim <= 0 || c->chunk <= 0 || c->state_dim < 0 || c->batch <= 0 ||
+      c->n_steps <= 0 || c->prefix_static < 0 || c->frame_tokens < 0 || c->n_frames < 0 || c->time_dim < 0)
+    return fail(nullptr, FM_ERR_SHAPE, "non-positive size in fm_config");
+  if (!(c->rms_eps >= 0.f)) return fail(nullptr, FM_ERR_ARG, "rms_eps must be >= 0");
+  if (c->norm != FM_RMSNORM && c->norm != FM_ADARMSNORM) return fail(nullptr, FM_ERR_ARG, "bad norm %d", c->norm);
+  if (c->weight_dtype < FM_F32 || c->weight_dtype > FM_FP8_E4M3) return fail(nullptr, FM_ERR_ARG, "bad weight_dtype");
+  if (c->act_dtype != FM_F32 && c->act_dtype != FM_BF16) return fail(nullptr, FM_ERR_ARG, "bad act_dtype");
+  if (c->exec_mode < FM_EXEC_AUTO || c->exec_mode > FM_EXEC_PERSISTENT) return fail(nullptr, FM_ERR_ARG, "bad exec_mode");
+  if ((c->weight_dtype == FM_F32) != (c->act_dtype == FM_F32))
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "fp32 weights go with fp32 activations only");
+  if ((c->n_frames > 0) != (c->frame_tokens > 0))
+    return fail(nullptr, FM_ERR_SHAPE, "n_frames and frame_tokens must both be zero or both positive");
+  if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, FM_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+  if (c->norm == FM_RMSNORM && c->time_dim != c->d_model)
+    return fail(nullptr, FM_ERR_SHAPE, "RMSNorm expert: time_dim must equal d_model");
+  if (c->norm == FM_ADARMSNORM && (c->time_dim <= 0 || c->time_dim % 2))
+    return fail(nullptr, FM_ERR_SHAPE, "AdaRMSNorm expert: time_dim must be positive and even");
+  if (c->d_model % 2) return fail(nullptr, FM_ERR_SHAPE, "d_model must be even");
+  // kernel coverage
+  const bool f32 = c->act_dtype == FM_F32;
+  const int S = c->chunk + (c->state_dim > 0);
+  if (c->d_model % 64) return fail(nullptr, FM_ERR_UNSUPPORTED, "d_model must be a multiple of 64");
+  if (c->action_dim != 16 && c->action_dim != 32) return fail(nullptr, FM_ERR_UNSUPPORTED, "action_dim must be 16 or 32");
+  if ((c->n_q_heads * c->head_dim) % 32 || ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 16)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "head sizes must give multiples of 32 columns");
+  if (c->d_mlp % 32) return fail(nullptr, FM_ERR_UNSUPPORTED, "d_mlp must be a multiple of 32");
+  if (c->weight_dtype == FM_FP8_E4M3 &&
+      (c->d_model % 64 || (c->n_q_heads * c->head_dim) % 64 || c->d_mlp % 64))
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "fp8 weights need reduction sizes that are multiples of 64");
+  if (f32) {
+    if (c->head_dim > 64 || S > 256) return fail(nullptr, FM_ERR_UNSUPPORTED, "fp32 path: head_dim <= 64, suffix <= 256");
+  } else if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) {
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "bf16 path: head_dim must be 32, 64, 128 or 256");
+  }
+  if (c->head_dim % 8) return fail(nullptr, FM_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+  if (c->n_frames > 0 && c->frame_tokens % 8) return fail(nullptr, FM_ERR_UNSUPPORTED, "frame_tokens % 8 != 0");
+  const long tcap = (long)c->prefix_static + (long)c->n_frames * c->frame_tokens;
+  if (tcap > (1 << 24)) return fail(nullptr, FM_ERR_SHAPE, "prefix capacity too large");
+  return FM_OK;
+}
+
+fm_status validate_weights(const fm_config* c, const fm_weights* w) {
+  if (!w) return fail(nullptr, FM_ERR_ARG, "weights is NULL");
+  if (!w->w_in || !w->b_in || !w->w_out || !w->b_out || !w->norm_f || !w->layers)
+    return fail(nullptr, FM_ERR_ARG, "missing weight pointer (w_in, b_in, w_out, b_out, norm_f, layers)");
+  if (c->state_dim > 0 && (!w->w_state || !w->b_state)) return fail(nullptr, FM_ERR_ARG, "missing w_state / b_state");
+  if (c->norm == FM_ADARMSNORM && (!w->w_time || !w->b_time || !w->norm_f_b))
+    return fail(nullptr, FM_ERR_ARG, "AdaRMSNorm needs w_time, b_time, norm_f_b");
+  for (int l = 0; l < c->n_layers; ++l)
+    for (int s = 0; s < FM_LW_COUNT; ++s) {
+      const bool need = s < FM_LW_NORM1 || s == FM_LW_NORM1 || s == FM_LW_NORM2 ||
+                        (c->norm == FM_ADARMSNORM && (s == FM_LW_NORM1_B || s == FM_LW_NORM2_B));
+      if (need && !w->layers[l * FM_LW_COUNT + s]) return fail(nullptr, FM_ERR_ARG, "layer %d weight slot %d is NULL", l, s);
+    }
+  return FM_OK;
+}
+
+void derive(fm_ctx* x) {
+  const fm_config& c = x->cfg;
+  x->act = elt_of(c.act_dtype);
+  x->wt = elt_of(c.weight_dtype);
+  x->ge = x->act == ELT_F32 ? ELT_F32 : ELT_BF16;
+  x->B = c.batch; x->C = c.chunk; x->A = c.action_dim; x->SD = c.state_dim; x->hasS = c.state_dim > 0;
+  x->S = x->C + x->hasS; x->M = x->B * x->S;
+  x->d = c.d_model; x->L = c.n_layers; x->Hq = c.n_q_heads; x->Hkv = c.n_kv_heads; x->Dh = c.head_dim;
+  x->F = c.d_mlp; x->N = c.n_steps; x->HD = x->Hkv * x->Dh;
+  x->Nqkv = (x->Hq + 2 * x->Hkv) * x->Dh;
+  x->Tcap = c.prefix_static + c.n_frames * c.frame_tokens;
+  x->P = x->d / 16;
+  x->mtiles = (x->M + 63) / 64;
+  x->esplit = x->d / 64;
+  const int unit = x->wt == ELT_FP8 ? 2 : 1;
+  x->ks_o = pick_split(x->Hq * x->Dh, std::max(1, x->Hq * x->Dh / 512), unit);
+  x->ks_d = pick_split(x->F, std::max(1, x->F / 1024), unit);
+  x->nqblk = (x->S * (x->Hq / x->Hkv) + 15) / 16;
+  x->nsplit = (x->Tcap + x->S + 127) / 128;
+}
+
+// carve every buffer from the arena (plan pass when a.plan)
+void carve(fm_ctx* x, Arena& a) {
+  const size_t ew = elt_size(x->wt), ea = elt_size(x->act), eg = elt_size(x->ge);
+  const bool ada = x->cfg.norm == FM_ADARMSNORM, fp8 = x->wt == ELT_FP8;
+  const long N = x->N, L = x->L, d = x->d;
+  x->lw.resize(x->L);
+  for (int l = 0; l < x->L; ++l) {
+    LayerW& w = x->lw[l];
+    w.wqkv = a.take((size_t)x->Nqkv * d * ew);
+    w.wo = a.take((size_t)d * x->Hq * x->Dh * ew);
+    w.wgu = a.take((size_t)2 * x->F * d * ew);
+    w.wd = a.take((size_t)d * x->F * ew);
+    w.sqkv = fp8 ? (float*)a.take(x->Nqkv * 4) : nullptr;
+    w.so = fp8 ? (float*)a.take(d * 4) : nullptr;
+    w.sgu = fp8 ? (float*)a.take(2 * x->F * 4) : nullptr;
+    w.sd = fp8 ? (float*)a.take(d * 4) : nullptr;
+  }
+  x->wout = a.take((size_t)x->A * d * eg);
+  x->w_in = a.take((size_t)d * x->A * eg);
+  x->b_in = a.take(d * eg);
+  x->w_state = x->hasS ? a.take((size_t)d * x->SD * eg) : nullptr;
+  x->b_state = x->hasS ? a.take(d * eg) : nullptr;
+  x->temb = ada ? nullptr : (float*)a.take(N * d * 4);
+  const long gsz = ada ? N * L * d : L * d;
+  x->g1 = (float*)a.take(gsz * 4);
+  x->g2 = (float*)a.take(gsz * 4);
+  x->gf = (float*)a.take((ada ? N * d : d) * 4);
+  x->a1 = ada ? (float*)a.take(N * L * d * 4) : nullptr;
+  x->a2 = ada ? (float*)a.take(N * L * d * 4) : nullptr;
+  x->bqkv = ada ? (float*)a.take(N * L * x->Nqkv * 4) : nullptr;
+  x->bgu = ada ? (float*)a.take(N * L * 2 * x->F * 4) : nullptr;
+  x->bout = (float*)a.take((ada ? N * x->A : x->A) * 4);
+  x->st_g = ada ? L * d : 0;
+  x->st_gf = ada ? d : 0;
+  x->st_bqkv = L * x->Nqkv;
+  x->st_bgu = L * 2 * x->F;
+  x->st_bout = ada ? x->A : 0;
+  const size_t kv = (size_t)x->B * L * x->Tcap * x->HD * ea;
+  x->kpre = a.take(kv > 0 ? kv : 16);
+  x->vpre = a.take(kv > 0 ? kv : 16);
+  x->meta = (int*)a.take(x->B * 2 * sizeof(int));
+  const long Mp = (long)x->mtiles * 64;
+  x->h = (float*)a.take(Mp * d * 4);
+  x->hs = (float*)a.take((long)x->B * d * 4);
+  x->ssq = (float*)a.take(Mp * x->P * 4);
+  x->ssqf = (float*)a.take(Mp * x->P * 4);
+  x->xbuf0 = (float*)a.take((long)x->B * x->C * x->A * 4);
+  x->xbuf1 = (float*)a.take((long)x->B * x->C * x->A * 4);
+  x->u = a.take(Mp * d * ea);
+  x->uf = a.take(Mp * d * ea);
+  x->qkv = a.take(Mp * x->Nqkv * ea);
+  x->o = a.take(Mp * x->Hq * x->Dh * ea);
+  x->z = a.take(Mp * x->F * ea);
+  const long ks = std::max(x->ks_o, x->ks_d);
+  x->partials = (float*)a.take(ks > 1 ? ks * Mp * d * 4 : 16);
+  x->attn_part = (float*)a.take(x->act == ELT_F32 || x->nsplit == 1
+                                    ? 16
+                                    : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 2) * 4);
+  x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
+                                   (size_t)x->B * x->Hkv * x->nqblk) + 64;
+  x->counters = (unsigned*)a.take(x->n_counters * 4);
+}
+
+Tab T(const float* base, long stride) { return Tab{base, stride}; }
+
+// the launches of one Euler step's transformer layers
+fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
+  const float eps = x->cfg.rms_eps, inv_d = 1.f / (float)x->d;
+  const bool ada = x->cfg.norm == FM_ADARMSNORM;
+  const long Tl = (long)x->Tcap * x->HD;  // elements per (robot, layer) of prefix K
+  for (int l = 0; l < x->L; ++l) {
+    const LayerW& w = x->lw[l];
+    GemmArgs g{};
+    g.M = x->M; g.mtiles = x->mtiles; g.ssq = x->ssq; g.P = x->P; g.inv_d = inv_d; g.eps = eps; g.step = k;
+    g.partials = x->partials; g.counters = x->counters;
+    // 1. norm1 -> QKV
+    g.A = x->u; g.W = w.wqkv; g.wscale = w.sqkv; g.N = x->Nqkv; g.K = x->d; g.nt = 16; g.ksplit = 1;
+    g.out = x->qkv;
+    g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(nullptr, 0);
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_QKV, g, st), "qkv gemm");
+    // 2. attention over [prefix | suffix]
+    AttnArgs at{};
+    at.qkv = x->qkv;
+    at.kpre = (const char*)x->kpre + (size_t)l * Tl * elt_size(x->act);
+    at.vpre = (const char*)x->vpre + (size_t)l * Tl * elt_size(x->act);
+    at.b_stride = (long)x->L * Tl;
+    at.meta = x->meta;
+    at.B = x->B; at.S = x->S; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
+    at.n_static = x->cfg.prefix_static; at.frame_tokens = std::max(1, x->cfg.frame_tokens);
+    at.n_frames = std::max(1, x->cfg.n_frames);
+    at.nqblk = x->nqblk; at.nsplit = x->nsplit;
+    at.scale = 1.f / sqrtf((float)x->Dh);
+    at.part = x->attn_part; at.counters = x->counters;
+    at.out = x->o;
+    HIPCHK(x, launch_attn(x->act, at, st), "attention");
+    // 3. O projection + residual; writes u = act(h * g2), ssq
+    GemmArgs r = g;
+    r.A = x->o; r.W = w.wo; r.wscale = w.so; r.N = x->d; r.K = x->Hq * x->Dh; r.ksplit = x->ks_o;
+    r.h = x->h; r.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(nullptr, 0);
+    r.gnext = T(x->g2 + (long)l * x->d, x->st_g);
+    r.u_out = x->u; r.ssq_out = x->ssq;
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, r, st), "o gemm");
+    // 4. norm2 -> gate/up -> GELU gate
+    GemmArgs gu = g;
+    gu.A = x->u; gu.W = w.wgu; gu.wscale = w.sgu; gu.N = 2 * x->F; gu.K = x->d; gu.nt = 32;
+    gu.out = x->z;
+    gu.bias = ada ? T(x->bgu + (long)l * 2 * x->F, x->st_bgu) : T(nullptr, 0);
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_GELU, gu, st), "gate/up gemm");
+    // 5. down + residual; writes the next norm's input
+    GemmArgs dn = r;
+    dn.A = x->z; dn.W = w.wd; dn.wscale = w.sd; dn.N = x->d; dn.K = x->F; dn.ksplit = x->ks_d;
+    dn.alpha = ada ? T(x->a2 + (long)l * x->d, x->st_g) : T(nullptr, 0);
+    const bool last = l + 1 == x->L;
+    dn.gnext = last ? T(x->gf, x->st_gf) : T(x->g1 + (long)(l + 1) * x->d, x->st_g);
+    dn.u_out = last ? x->uf : x->u;
+    dn.ssq_out = last ? x->ssqf : x->ssq;
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, dn, st), "down gemm");
+  }
+  return FM_OK;
+}
+
+// final norm + head + Euler (+ the next step's embedding) of step k
+fm_status enqueue_tail(fm_ctx* x, int k, hipStream_t st, float* x_final) {
+  const bool ada = x->cfg.norm == FM_ADARMSNORM;
+  OutArgs o{};
+  o.uf = x->uf; o.Wout = x->wout; o.ssq = x->ssqf; o.P = x->P; o.inv_d = 1.f / (float)x->d; o.eps = x->cfg.rms_eps;
+  o.bout = T(x->bout, x->st_bout);
+  o.x_in = (k & 1) ? x->xbuf1 : x->xbuf0;
+  o.x_out = x_final ? x_final : ((k & 1) ? x->xbuf0 : x->xbuf1);
+  o.dt = -1.f / (float)x->N;
+  o.B = x->B; o.S = x->S; o.C = x->C; o.A = x->A; o.d = x->d; o.M = x->M; o.has_state = x->hasS;
+  o.mtiles = x->mtiles; o.esplit = x->esplit;
+  o.do_embed = k + 1 < x->N;
+  o.w_in = x->w_in; o.b_in = x->b_in;
+  o.temb = ada ? T(nullptr, 0) : T(x->temb, x->d);
+  o.embed_step = k + 1;
+  o.hs = x->hs; o.h = x->h; o.u = x->u; o.g1 = T(x->g1, x->st_g); o.ssq_out = x->ssq;
+  HIPCHK(x, launch_out(x->act, x->ge, o, st), "out/euler");
+  return FM_OK;
+}
+
+fm_status enqueue_embed(fm_ctx* x, const float* noise, const void* state, hipStream_t st) {
+  EmbedArgs e{};
+  const bool ada = x->cfg.norm == FM_ADARMSNORM;
+  e.noise = noise; e.state = state; e.w_state = x->w_state; e.b_state = x->b_state;
+  e.w_in = x->w_in; e.b_in = x->b_in;
+  e.temb = ada ? T(nullptr, 0) : T(x->temb, x->d);
+  e.x0 = x->xbuf0; e.hs = x->hs; e.h = x->h; e.u = x->u; e.g1 = T(x->g1, x->st_g); e.ssq_out = x->ssq;
+  e.B = x->B; e.S = x->S; e.C = x->C; e.A = x->A; e.SD = x->SD; e.d = x->d; e.M = x->M; e.has_state = x->hasS;
+  e.mtiles = x->mtiles; e.esplit = x->esplit;
+  HIPCHK(x, launch_embed(x->act, e, st), "embed");
+  return FM_OK;
+}
+
+// weights -> arena
+fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
+  const bool ada = x->cfg.norm == FM_ADARMSNORM, fp8 = x->wt == ELT_FP8;
+  const int src = x->ge;  // dtype the caller passes matrices in (bf16 for fp8 models)
+  const long N = x->N, L = x->L, d = x->d;
+  const size_t eg = elt_size(x->ge);
+  // temporaries for create only
+  uint8_t* codes = nullptr;
+  float* scales = nullptr;
+  float *c = nullptr, *beta1 = nullptr, *beta2 = nullptr, *betaf = nullptr;
+  const size_t maxm = (size_t)std::max(std::max(x->Hq * x->Dh, x->F), x->HD) * std::max(x->d, x->F);
+  std::vector<void*> tmp;
+  auto tmalloc = [&](size_t bytes) -> void* {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+    tmp.push_back(p);
+    return p;
+  };
+  auto cleanup = [&]() {
+    (void)hipStreamSynchronize(st);
+    for (void* p : tmp) (void)hipFree(p);
+  };
+  if (fp8) {
+    codes = (uint8_t*)tmalloc(maxm);
+    scales = (float*)tmalloc((size_t)std::max(std::max(x->Hq * x->Dh, x->F), x->d) * 4);
+    if (!codes || !scales) { cleanup(); return fail(x, FM_ERR_OOM, "temporary fp8 buffers"); }
+  }
+  if (ada) {
+    c = (float*)tmalloc(N * d * 4);
+    beta1 = (float*)tmalloc(N * L * d * 4);
+    beta2 = (float*)tmalloc(N * L * d * 4);
+    betaf = (float*)tmalloc(N * d * 4);
+    if (!c || !beta1 || !beta2 || !betaf) { cleanup(); return fail(x, FM_ERR_OOM, "temporary time tables"); }
+    hipError_t e = launch_ada_c(w->w_time, w->b_time, src, x->N, x->cfg.time_dim, x->d, c, st);
+    if (e != hipSuccess) { cleanup(); return hip_fail(x, e, "ada time mlp"); }
+  }
+  hipError_t e = hipSuccess;
+#define CHK(call, what)                                \
+  do {                                                 \
+    e = (call);                                        \
+    if (e != hipSuccess) { cleanup(); return hip_fail(x, e, what); } \
+  } while (0)
+  if (ada) {
+    CHK(hipMemsetAsync(x->bqkv, 0, N * L * x->Nqkv * 4, st), "memset");
+    CHK(hipMemsetAsync(x->bgu, 0, N * L * 2 * x->F * 4, st), "memset");
+  }
+  // one matrix: [rows][cols] in caller dtype -> packed (quantised for fp8);
+  // Ada: add beta W to the bias table of this GEMM
+  auto put = [&](const void* m, int rows, int cols, RowMap rm, void* dst, float* dscale, const float* beta,
+                 float* btab, long bstride) -> hipError_t {
+    hipError_t r;
+    if (fp8) {
+      if ((r = launch_quantize_e4m3(m, rows, cols, codes, scales, st)) != hipSuccess) return r;
+      if ((r = launch_pack(codes, ELT_FP8, rows, cols, rm, dst, ELT_FP8, 0, st)) != hipSuccess) return r;
+      if ((r = launch_scatter_scales(scales, rows, rm, dscale, st)) != hipSuccess) return r;
+      if (beta) return launch_bias_gemv(codes, ELT_FP8, scales, rows, cols, beta, L * d, x->N, rm, btab, bstride, st);
+    } else {
+      if ((r = launch_pack(m, src, rows, cols, rm, dst, src, 0, st)) != hipSuccess) return r;
+      if (beta) return launch_bias_gemv(m, src, nullptr, rows, cols, beta, L * d, x->N, rm, btab, bstride, st);
+    }
+    return hipSuccess;
+  };
+  const int qd = x->Hq * x->Dh;
+  for (int l = 0; l < x->L; ++l) {
+    const void* const* lp = w->layers + (size_t)l * FM_LW_COUNT;
+    LayerW& lw = x->lw[l];
+    if (ada) {
+      CHK(launch_ada_mod(c, x->N, x->d, lp[FM_LW_NORM1], lp[FM_LW_NORM1_B], src, x->g1 + l * d, beta1 + l * d,
+                         x->a1 + l * d, L * d, st), "ada norm1");
+      CHK(launch_ada_mod(c, x->N, x->d, lp[FM_LW_NORM2], lp[FM_LW_NORM2_B], src, x->g2 + l * d, beta2 + l * d,
+                         x->a2 + l * d, L * d, st), "ada norm2");
+    } else {
+      CHK(launch_copy_convert(lp[FM_LW_NORM1], src, d, x->g1 + l * d, st), "gain1");
+      CHK(launch_copy_convert(lp[FM_LW_NORM2], src, d, x->g2 + l * d, st), "gain2");
+    }
+    const float* b1 = ada ? beta1 + l * d : nullptr;
+    const float* b2 = ada ? beta2 + l * d : nullptr;
+    float* bq = ada ? x->bqkv + l * x->Nqkv : nullptr;
+    float* bg = ada ? x->bgu + l * 2 * x->F : nullptr;
+    CHK(put(lp[FM_LW_WQ], qd, x->d, RowMap{qd, 0, 0}, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wq");
+    CHK(put(lp[FM_LW_WK], x->HD, x->d, RowMap{x->HD, 0, qd}, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wk");
+    CHK(put(lp[FM_LW_WV], x->HD, x->d, RowMap{x->HD, 0, qd + x->HD}, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wv");
+    CHK(put(lp[FM_LW_WO], x->d, qd, RowMap{x->d, 0, 0}, lw.wo, lw.so, nullptr, nullptr, 0), "pack wo");
+    CHK(put(lp[FM_LW_WG], x->F, x->d, RowMap{16, 32, 0}, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wg");
+    CHK(put(lp[FM_LW_WU], x->F, x->d, RowMap{16, 32, 16}, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wu");
+    CHK(put(lp[FM_LW_WD], x->d, x->F, RowMap{x->d, 0, 0}, lw.wd, lw.sd, nullptr, nullptr, 0), "pack wd");
+  }
+  // final norm and the action head
+  for (int k = 0; k < (ada ? x->N : 1); ++k)
+    CHK(launch_copy_convert(w->b_out, src, x->A, x->bout + k * x->A, st), "b_out");
+  if (ada) {
+    CHK(launch_ada_mod(c, x->N, x->d, w->norm_f, w->norm_f_b, src, x->gf, betaf, nullptr, d, st), "ada final norm");
+    CHK(launch_bias_gemv(w->w_out, src, nullptr, x->A, x->d, betaf, d, x->N, RowMap{x->A, 0, 0}, x->bout, x->A, st),
+        "beta_f W_out");
+  } else {
+    CHK(launch_copy_convert(w->norm_f, src, d, x->gf, st), "final gain");
+    CHK(launch_time_add(x->temb, x->N, x->d, st), "time features");
+  }
+  CHK(launch_pack(w->w_out, src, x->A, x->d, RowMap{x->A, 0, 0}, x->wout, src, 0, st), "pack w_out");
+  CHK(hipMemcpyAsync(x->w_in, w->w_in, (size_t)d * x->A * eg, hipMemcpyDeviceToDevice, st), "copy w_in");
+  CHK(hipMemcpyAsync(x->b_in, w->b_in, (size_t)d * eg, hipMemcpyDeviceToDevice, st), "copy b_in");
+  if (x->hasS) {
+    CHK(hipMemcpyAsync(x->w_state, w->w_state, (size_t)d * x->SD * eg, hipMemcpyDeviceToDevice, st), "copy w_state");
+    CHK(hipMemcpyAsync(x->b_state, w->b_state, (size_t)d * eg, hipMemcpyDeviceToDevice, st), "copy b_state");
+  }
+#undef CHK
+  cleanup();
+  return FM_OK;
+}
+
+fm_status check_ctx(fm_ctx* x) {
+  if (!x) return fail(nullptr, FM_ERR_ARG, "ctx is NULL");
+  if (x->poisoned) return fail(x, FM_ERR_STATE, "context poisoned by an earlier device error");
+  return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream, fm_ctx** out) {
+  if (!out) return fail(nullptr, FM_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  fm_status s = validate_config(cfg);
+  if (s != FM_OK) return s;
+  if ((s = validate_weights(cfg, w)) != FM_OK) return s;
+  if (cfg->exec_mode == FM_EXEC_PERSISTENT)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "persistent execution is not available in this build");
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, FM_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(nullptr, FM_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "device %s is not gfx950 (MI355X)", prop.gcnArchName);
+
+  fm_ctx* x = new fm_ctx();
+  x->cfg = *cfg;
+  x->stream = (hipStream_t)hip_stream;
+  x->n_cu = prop.multiProcessorCount;
+  x->exec_mode = FM_EXEC_GRAPH;
+  derive(x);
+  Arena a;
+  carve(x, a);
+  x->arena_bytes = a.off;
+  e = hipMalloc(&x->arena, x->arena_bytes);
+  if (e != hipSuccess) {
+    fail(nullptr, FM_ERR_OOM, "arena of %zu bytes: %s", x->arena_bytes, hipGetErrorString(e));
+    delete x;
+    return FM_ERR_OOM;
+  }
+  a.plan = false;
+  a.base = (char*)x->arena;
+  a.off = 0;
+  carve(x, a);
+  x->valid.assign(x->B, 0);
+  x->head.assign(x->B, 0);
+  x->is_set.assign(x->B, 0);
+  auto bail = [&](fm_status st) {
+    snprintf(g_err, sizeof g_err, "%s", x->err);
+    fm_destroy(x);
+    return st;
+  };
+  hipStream_t st = x->stream;
+  if ((e = hipMemsetAsync(x->arena, 0, x->arena_bytes, st)) != hipSuccess) {
+    hip_fail(x, e, "arena clear");
+    return bail(FM_ERR_DEVICE);
+  }
+  if ((s = load_weights(x, w, st)) != FM_OK) return bail(s);
+  // the graph: every step's layers and tails except the last tail
+  if ((e = hipStreamCreateWithFlags(&x->cap, hipStreamNonBlocking)) != hipSuccess) {
+    hip_fail(x, e, "capture stream");
+    return bail(FM_ERR_DEVICE);
+  }
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) {
+    hip_fail(x, e, "create sync");
+    return bail(FM_ERR_DEVICE);
+  }
+  if ((e = hipStreamBeginCapture(x->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+    hip_fail(x, e, "begin capture");
+    return bail(FM_ERR_DEVICE);
+  }
+  fm_status cs = FM_OK;
+  for (int k = 0; k < x->N && cs == FM_OK; ++k) {
+    cs = enqueue_layers(x, k, x->cap);
+    if (cs == FM_OK && k + 1 < x->N) cs = enqueue_tail(x, k, x->cap, nullptr);
+  }
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(x->cap, &g);
+  if (cs != FM_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return bail(cs);
+  }
+  if (e != hipSuccess) {
+    hip_fail(x, e, "end capture");
+    return bail(FM_ERR_DEVICE);
+  }
+  x->graph = g;
+  if ((e = hipGraphInstantiate(&x->gexec, g, nullptr, nullptr, 0)) != hipSuccess) {
+    hip_fail(x, e, "graph instantiate");
+    return bail(FM_ERR_DEVICE);
+  }
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) {
+    hip_fail(x, e, "create sync");
+    return bail(FM_ERR_DEVICE);
+  }
+  *out = x;
+  return FM_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+fm_status fm_set_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* v, int32_t n_tokens) {
+  fm_status s = check_ctx(x);
+  if (s != FM_OK) return s;
+  if (robot < 0 || robot >= x->B) return fail(x, FM_ERR_ARG, "robot %d out of range [0, %d)", robot, x->B);
+  const bool ring = x->cfg.n_frames > 0;
+  if (ring ? n_tokens != x->Tcap : (n_tokens < 0 || n_tokens > x->cfg.prefix_static))
+    return fail(x, FM_ERR_SHAPE, "n_tokens %d: %s %d", n_tokens, ring ? "ring prefix needs exactly" : "must be in [0, ",
+                ring ? x->Tcap : x->cfg.prefix_static);
+  if (n_tokens > 0 && (!k || !v)) return fail(x, FM_ERR_ARG, "k or v is NULL");
+  if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k and v must be 16-byte aligned");
+  const long row = (long)n_tokens * x->HD;
+  const long Tl = (long)x->Tcap * x->HD;
+  const size_t ea = elt_size(x->act);
+  char* kd = (char*)x->kpre + (size_t)robot * x->L * Tl * ea;
+  char* vd = (char*)x->vpre + (size_t)robot * x->L * Tl * ea;
+  HIPCHK(x, launch_kv_copy(k, v, kd, vd, x->act, x->L, row, row, Tl, x->meta, robot, n_tokens, 0, x->stream),
+         "prefix copy");
+  x->valid[robot] = n_tokens;
+  x->head[robot] = 0;
+  x->is_set[robot] = 1;
+  return FM_OK;
+}
+
+fm_status fm_append_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* v) {
+  fm_status s = check_ctx(x);
+  if (s != FM_OK) return s;
+  if (robot < 0 || robot >= x->B) return fail(x, FM_ERR_ARG, "robot %d out of range [0, %d)", robot, x->B);
+  if (x->cfg.n_frames <= 0) return fail(x, FM_ERR_STATE, "the context has no frame ring");
+  if (!x->is_set[robot]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", robot);
+  if (!k || !v) return fail(x, FM_ERR_ARG, "k_frame or v_frame is NULL");
+  if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k_frame and v_frame must be 16-byte aligned");
+  const int slot = x->head[robot];
+  const int nh = (slot + 1) % x->cfg.n_frames;
+  const long row = (long)x->cfg.frame_tokens * x->HD;
+  const long Tl = (long)x->Tcap * x->HD;
+  const size_t ea = elt_size(x->act);
+  const size_t off = ((size_t)robot * x->L * Tl + (size_t)(x->cfg.prefix_static + slot * x->cfg.frame_tokens) * x->HD) * ea;
+  HIPCHK(x, launch_kv_copy(k, v, (char*)x->kpre + off, (char*)x->vpre + off, x->act, x->L, row, row, Tl, x->meta,
+                           robot, x->valid[robot], nh, x->stream),
+         "frame append");
+  x->head[robot] = nh;
+  return FM_OK;
+}
+
+fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* actions) {
+  fm_status s = check_ctx(x);
+  if (s != FM_OK) return s;
+  if (!noise || !actions) return fail(x, FM_ERR_ARG, "noise or actions is NULL");
+  if ((x->SD > 0) != (state != nullptr)) return fail(x, FM_ERR_ARG, "state must be given iff state_dim > 0");
+  for (int b = 0; b < x->B; ++b)
+    if (!x->is_set[b]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", b);
+  if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
+  HIPCHK(x, hipGraphLaunch(x->gexec, x->stream), "graph launch");
+  return enqueue_tail(x, x->N - 1, x->stream, actions);
+}
+
+fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
+  if (!x || !info) return fail(nullptr, FM_ERR_ARG, "ctx or info is NULL");
+  const size_t ew = elt_size(x->wt), eg = elt_size(x->ge), ea = elt_size(x->act);
+  size_t wb = (size_t)x->L * ((size_t)x->Nqkv * x->d + (size_t)x->d * x->Hq * x->Dh + 3ull * x->F * x->d) * ew;
+  if (x->wt == ELT_FP8) wb += (size_t)x->L * (x->Nqkv + 2 * x->d + 2 * x->F) * 4;
+  wb += (size_t)(2 * x->A * x->d + x->d) * eg;  // w_in, w_out, b_in
+  info->arena_bytes = x->arena_bytes;
+  info->weight_bytes_per_step = wb;
+  size_t kv = 0;
+  for (int b = 0; b < x->B; ++b) kv += (size_t)x->valid[b];
+  info->kv_bytes_per_step = kv * x->L * x->HD * ea * 2;
+  info->exec_mode = x->exec_mode;
+  info->n_phases = x->N * (5 * x->L + 1) + 1;
+  info->grid = x->mtiles * (2 * x->F / 32);
+  info->n_cu = x->n_cu;
+  return FM_OK;
+}
+
+void fm_destroy(fm_ctx* x) {
+  if (!x) return;
+  if (x->stream || x->arena) (void)hipStreamSynchronize(x->stream);
+  if (x->gexec) (void)hipGraphExecDestroy(x->gexec);
+  if (x->graph) (void)hipGraphDestroy(x->graph);
+  if (x->cap) (void)hipStreamDestroy(x->cap);
+  if (x->arena) (void)hipFree(x->arena);
+  delete x;
+}
+
+const char* fm_last_error(const fm_ctx* x) { return x ? x->err : g_err; }
+
+fm_status fm_quantize_e4m3(const void* w, int32_t rows, int32_t cols, uint8_t* codes, float* scales, void* hip_stream) {
+  if (!w || !codes || !scales) return fail(nullptr, FM_ERR_ARG, "NULL pointer");
+  if (rows <= 0 || cols <= 0) return fail(nullptr, FM_ERR_SHAPE, "rows and cols must be positive");
+  hipError_t e = launch_quantize_e4m3(w, rows, cols, codes, scales, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(nullptr, FM_ERR_DEVICE, "quantize: %s", hipGetErrorString(e));
+  return FM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Internal launch interface between the engine (fm_engine.cpp) and the
+// gfx950 kernels (fm_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+// Element types of activations / weights inside the library.
+enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2 };
+
+// Epilogues of the skinny GEMM.
+enum Epi : int {
+  EPI_QKV = 0,    // out = act(acc * rstd[row] + bias[col])
+  EPI_RESID = 1,  // h += alpha[col] * acc ; u = act(h * gnext[col]) ; ssq partials
+  EPI_GELU = 2,   // z = act(gelu(g * rstd + bg) * (u * rstd + bu)), tile = [16 gate | 16 up]
+};
+
+// Per-step table: element (step, i) lives at base[step * step_stride + i].
+struct Tab {
+  const float* base;
+  long step_stride;
+};
+
+struct GemmArgs {
+  const void* A;          // [M][K] activations (act type), row-major
+  const void* W;          // packed weight tiles (see pack layout)
+  const float* wscale;    // fp8: per packed output column scale, else null
+  int M, N, K;            // N = packed output columns
+  int nt;                 // columns per work item: 16 or 32
+  int ksplit;             // K split across workgroups
+  int mtiles;             // ceil(M / 64)
+  float* partials;        // [ksplit][mtiles*64][N] (ksplit > 1)
+  unsigned* counters;     // [mtiles * N/nt] zero on entry, zero on exit
+  // norm statistics of A's rows (EPI_QKV, EPI_GELU): rstd from ssq partials
+  const float* ssq;       // [M][P] partial sums of h^2, P = d/16
+  int P;
+  float inv_d, eps;
+  // epilogue operands
+  void* out;              // QKV: [M][N] act ; GELU: [M][N/2] act
+  Tab bias;               // QKV / GELU: per packed column (Ada beta W), or base null
+  float* h;               // RESID: [M][N] fp32 residual stream (in/out)
+  Tab alpha;              // RESID: per column (Ada alpha) or null
+  Tab gnext;              // RESID: gain of the next norm per column
+  void* u_out;            // RESID: [M][N] act = act(h * gnext)
+  float* ssq_out;         // RESID: [M][N/16]
+  int step;
+};
+
+struct AttnArgs {
+  const void* qkv;        // [B*S][Nqkv] act
+  const void* kpre;       // layer-l base of K: [B] blocks of stride b_stride elements, [Tcap][Hkv][Dh]
+  const void* vpre;
+  long b_stride;          // elements between robots in kpre / vpre
+  const int* meta;        // [B][2] = (valid prefix tokens, ring head)
+  int B, S, Hq, Hkv, Dh, Nqkv;
+  int n_static, frame_tokens, n_frames;
+  int nqblk, nsplit;      // query blocks of 16 per (b, kv head); key splits of 128
+  float scale;
+  float* part;            // partials
+  unsigned* counters;
+  void* out;              // [B*S][Hq*Dh] act
+};
+
+struct OutArgs {
+  // final norm + action head + Euler, then the next step's embedding
+  const void* uf;         // [M][d] act  (h * gain_f)
+  const void* Wout;       // packed [A][d] (N = A)
+  const float* ssq;       // [M][P]
+  int P;
+  float inv_d, eps;
+  Tab bout;               // [A] per step: b_out (+ Ada beta_f W_out)
+  const float* x_in;      // [B*C][A]
+  float* x_out;           // [B*C][A]
+  float dt;
+  int B, S, C, A, d, M, has_state, mtiles, esplit;
+  int do_embed;           // 0 on the last step
+  // embedding of the next step (same fields as EmbedArgs)
+  const void* w_in;       // [d][A] (plain row-major)
+  const void* b_in;       // [d]
+  Tab temb;               // [d] additive time feature per step, or null
+  int embed_step;
+  const float* hs;        // [B][d] state rows' h (constant over steps)
+  float* h;               // [M][d]
+  void* u;                // [M][d] act = act(h * g1)
+  Tab g1;                 // layer-0 norm1 gain per step
+  float* ssq_out;         // [M][P]
+};
+
+struct EmbedArgs {
+  const float* noise;     // [B*C][A]
+  const void* state;      // [B][SD] act or null
+  const void* w_state;    // [d][SD] plain
+  const void* b_state;
+  const void* w_in;       // [d][A]
+  const void* b_in;
+  Tab temb;
+  float* x0;              // [B*C][A] copy of the noise
+  float* hs;              // [B][d]
+  float* h;
+  void* u;
+  Tab g1;
+  float* ssq_out;
+  int B, S, C, A, SD, d, M, has_state, mtiles, esplit;
+};
+
+// --- launchers (fm_kernels.hip) --------------------------------------------
+hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t st);
+hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st);
+hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st);
+hipError_t launch_embed(int act, const EmbedArgs& e, hipStream_t st);
+
+// weight preparation at create time
+// row map of a source row n to the packed column: (n / blk) * stride + off + n % blk
+struct RowMap { int blk, stride, off; };
+hipError_t launch_pack(const void* src, int src_elt, int rows, int cols, RowMap rm,
+                       void* dst, int dst_elt, int Ntot, hipStream_t st);
+hipError_t launch_quantize_e4m3(const void* w_bf16, int rows, int cols, uint8_t* codes,
+                                float* scales, hipStream_t st);
+hipError_t launch_scatter_scales(const float* s, int rows, RowMap rm, float* dst, hipStream_t st);
+hipError_t launch_copy_convert(const void* src, int src_elt, long n, float* dst, hipStream_t st);
+// time tables
+hipError_t launch_time_add(float* temb, int n_steps, int d, hipStream_t st);
+hipError_t launch_ada_c(const void* w_t, const void* b_t, int wt, int n_steps, int time_dim, int d,
+                        float* c, hipStream_t st);
+hipError_t launch_ada_mod(const float* c, int n_steps, int d, const void* w_n, const void* b_n, int wt,
+                          float* gam1p, float* beta, float* alpha, long tab_step_stride, hipStream_t st);
+// out[step][map(n)] += sum_j beta[step][j] * Weff[n][j]  (Weff = codes*scale for fp8)
+hipError_t launch_bias_gemv(const void* w, int w_elt, const float* scales, int rows, int cols,
+                            const float* beta, long beta_step_stride, int n_steps, RowMap rm,
+                            float* out, long out_step_stride, hipStream_t st);
+// prefix K/V copy + meta update
+hipError_t launch_kv_copy(const void* k, const void* v, void* kd, void* vd, int elt, int layers,
+                          long row_elems, long src_pitch, long dst_pitch, int* meta, int robot,
+                          int valid, int head, hipStream_t st);
+
+}  // namespace fm

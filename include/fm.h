@@ -1,0 +1,225 @@
+/*
+ * fm.h - C ABI of the MI355X (gfx950) flow-matching action-expert denoiser.
+ *
+ * The library runs the denoising loop of a flow-matching robot policy: N
+ * explicit Euler steps x <- x + dt * v(x, t), each evaluating a small
+ * transformer (the "action expert") over the suffix tokens (an optional
+ * state token plus the noisy action chunk) that attend to a cached,
+ * timestep-invariant prefix of keys and values (vision and prompt tokens).
+ *
+ *   - Euler flow sampling with 10 steps: FlowEdge README, "Installation"
+ *     (the flow sampler run as "euler 10"); realtime-vla write-up, "The
+ *     latency table, and what it assumes" (10 flow steps per prediction).
+ *   - Prefix K/V computed once per observation and reused by every step,
+ *     with a static prompt region and a sliding window of frames updated in
+ *     O(1): Reflex abstract (Timestep-Invariance Property; static, sliding
+ *     and dynamic regions; full-batch-equivalent attention outputs).
+ *   - AdaRMSNorm gated on the flow phase: Reflex abstract.
+ *   - State (32,) and noise (chunk, 32) in, actions (chunk, 32) out:
+ *     realtime-vla write-up, "Copying an inference file into your own
+ *     project" (the forward(images, state, noise) contract).
+ *   - fp8 weights: InstinctFlash README, "Load a model" (precision="fp8").
+ *   - One pre-sized arena, nothing allocated after set-up: FlowEdge README,
+ *     "Overview" and its "load -> warmup (malloc 0)" line.
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), row-major and contiguous.  Weights follow the nn.Linear
+ *     convention W[out][in]: y = x W^T (+ b).
+ *   - `hip_stream` is a hipStream_t (NULL = the null stream).  Every call
+ *     except fm_create and fm_destroy only enqueues work on the context's
+ *     stream and returns; inputs must stay valid, and outputs are ready,
+ *     once that stream's work is done (hipMemcpyAsync semantics).
+ *   - Calls validate everything before enqueuing anything: on an error
+ *     return nothing has been enqueued and the context is unchanged.  A HIP
+ *     runtime failure returns FM_ERR_DEVICE and poisons the context: every
+ *     later call on it returns FM_ERR_STATE.
+ *   - The caller owns every buffer it passes.  fm_create copies (and
+ *     repacks / quantises) the weights into the context's own arena, so
+ *     they may be freed once fm_create returns.
+ *   - The library draws no random numbers: the noise comes from the caller.
+ *   - Identical inputs give bitwise-identical outputs (no float atomics).
+ *   - A context may be used from one host thread at a time.
+ */
+#ifndef FM_H_
+#define FM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FM_ABI_VERSION 1
+
+typedef struct fm_ctx fm_ctx;
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_ARG = 1,          /* NULL or otherwise invalid argument          */
+  FM_ERR_SHAPE = 2,        /* sizes inconsistent with the configuration   */
+  FM_ERR_STATE = 3,        /* call not valid in the context's state       */
+  FM_ERR_OOM = 4,          /* device allocation failed (fm_create only)   */
+  FM_ERR_DEVICE = 5,       /* HIP runtime error; the context is poisoned  */
+  FM_ERR_UNSUPPORTED = 6   /* valid configuration the kernels do not cover */
+} fm_status;
+
+typedef enum { FM_F32 = 0, FM_BF16 = 1, FM_FP8_E4M3 = 2 } fm_dtype;
+typedef enum { FM_RMSNORM = 0, FM_ADARMSNORM = 1 } fm_norm;
+
+/* How fm_denoise issues the loop.  FM_EXEC_AUTO picks the persistent
+ * kernel when the device can hold its grid, else the graph of kernels.
+ * Both run the same device code and give bitwise-identical results. */
+typedef enum {
+  FM_EXEC_AUTO = 0,
+  FM_EXEC_GRAPH = 1,       /* one hipGraph of per-phase kernel launches   */
+  FM_EXEC_PERSISTENT = 2   /* one cooperative kernel for the whole loop   */
+} fm_exec;
+
+/*
+ * Model and workload.  Notation: B batch (independent robots), C chunk,
+ * A action_dim, S = C + (state_dim > 0) suffix rows per robot, d d_model,
+ * L n_layers, Hq/Hkv heads, Dh head_dim, F d_mlp, N n_steps.
+ *
+ * Time runs from t = 1 (the noise) to t = 0 (the actions): step k = 0..N-1
+ * evaluates the velocity at t_k = 1 - k/N and applies dt = -1/N (the pages
+ * fix the step count, not the direction; this is the reading taken).
+ *
+ * norm = FM_RMSNORM: RMSNorm with a gain; sinusoidal features of t, d wide
+ *   ([sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(d/2))), are added to the
+ *   action tokens (not the state token); time_dim must equal d_model.
+ * norm = FM_ADARMSNORM: c = SiLU(W_t tau(t) + b_t) with tau time_dim wide;
+ *   every norm n has (gamma, beta, alpha) = split3(W_n c + b_n); the norm
+ *   gives rms(h) (1 + gamma) + beta and alpha scales the residual branch it
+ *   feeds (the final norm ignores alpha).  No additive time feature.
+ *
+ * The prefix holds prefix_static + n_frames * frame_tokens tokens per layer
+ * per robot (the static region, then a ring of frames: Reflex abstract).
+ * n_frames = 0 gives a static-only prefix.
+ *
+ * weight_dtype: FM_F32 (act_dtype must be FM_F32), FM_BF16, or FM_FP8_E4M3
+ *   (bf16 activations; the caller passes bf16 weights and the library
+ *   quantises the seven per-layer matrices to OCP E4M3FN with one fp32
+ *   scale per output row, see fm_quantize_e4m3; the other weights stay bf16).
+ * act_dtype: dtype of GEMM operands, prefix K/V and the state vector.  The
+ *   residual stream, softmax statistics and x are always fp32.
+ */
+typedef struct {
+  int32_t abi_version;               /* FM_ABI_VERSION */
+  int32_t d_model, n_layers, n_q_heads, n_kv_heads, head_dim, d_mlp;
+  int32_t action_dim, chunk, state_dim;
+  int32_t batch, n_steps;
+  int32_t prefix_static, frame_tokens, n_frames;
+  int32_t norm;                      /* fm_norm  */
+  int32_t time_dim;
+  int32_t weight_dtype;              /* fm_dtype */
+  int32_t act_dtype;                 /* fm_dtype: FM_F32 or FM_BF16 */
+  float rms_eps;                     /* e.g. 1e-6 */
+  int32_t exec_mode;                 /* fm_exec  */
+} fm_config;
+
+/* Per-layer weight slots of fm_weights.layers. */
+enum {
+  FM_LW_WQ = 0,   /* [Hq*Dh][d]                                          */
+  FM_LW_WK = 1,   /* [Hkv*Dh][d]                                         */
+  FM_LW_WV = 2,   /* [Hkv*Dh][d]                                         */
+  FM_LW_WO = 3,   /* [d][Hq*Dh]                                          */
+  FM_LW_WG = 4,   /* [F][d]   gate                                       */
+  FM_LW_WU = 5,   /* [F][d]   up                                         */
+  FM_LW_WD = 6,   /* [d][F]   down                                       */
+  FM_LW_NORM1 = 7,    /* RMS: gain [d].  Ada: W_n [3d][d]                */
+  FM_LW_NORM1_B = 8,  /* RMS: unused (NULL).  Ada: b_n [3d]              */
+  FM_LW_NORM2 = 9,
+  FM_LW_NORM2_B = 10,
+  FM_LW_COUNT = 11
+};
+
+/* Device pointers in the dtype of the weights (bf16 for an fp8 model). */
+typedef struct {
+  const void *w_in, *b_in;          /* [d][A], [d]                          */
+  const void *w_state, *b_state;    /* [d][state_dim], [d]; NULL if no state */
+  const void *w_out, *b_out;        /* [A][d], [A]                          */
+  const void *w_time, *b_time;      /* Ada: [d][time_dim], [d]; else NULL    */
+  const void *norm_f, *norm_f_b;    /* RMS: gain [d], NULL.  Ada: [3d][d], [3d] */
+  const void *const *layers;        /* HOST array of n_layers * FM_LW_COUNT
+                                       device pointers, layer-major          */
+} fm_weights;
+
+/* Sizes of a created context (for accounting and benchmarks). */
+typedef struct {
+  size_t arena_bytes;               /* device memory held by the context    */
+  size_t weight_bytes_per_step;     /* weight bytes one Euler step streams  */
+  size_t kv_bytes_per_step;         /* prefix K/V bytes one step reads      */
+  int32_t exec_mode;                /* mode actually used (GRAPH/PERSISTENT) */
+  int32_t n_phases;                 /* device phases per fm_denoise         */
+  int32_t grid;                     /* workgroups per phase / persistent grid */
+  int32_t n_cu;                     /* compute units of the device          */
+} fm_info;
+
+/*
+ * Create a context: validate, allocate one arena, copy/repack/quantise the
+ * weights, precompute the time tables (x-independent: t_k, additive time
+ * features or the AdaRMSNorm (gamma, beta, alpha) of every norm and step),
+ * and build the launch plan.  Synchronises the stream before returning.
+ * On failure *out is set to NULL and fm_last_error(NULL) explains it.
+ */
+fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream, fm_ctx** out);
+
+/*
+ * Load robot `robot`'s prefix K/V: k, v are [n_layers][n_tokens][Hkv][Dh]
+ * in act_dtype, logical order (static region, then frames oldest to
+ * newest); k and v 16-byte aligned.  Without a ring (n_frames == 0): 0 <= n_tokens <= prefix_static
+ * (0 = no prefix; attention then covers the suffix only).  With a ring:
+ * n_tokens must equal prefix_static + n_frames * frame_tokens.  Resets the
+ * ring so that slot j holds logical frame j.  Asynchronous.
+ */
+fm_status fm_set_prefix_kv(fm_ctx* ctx, int32_t robot, const void* k, const void* v,
+                           int32_t n_tokens);
+
+/*
+ * Append one frame to robot `robot`'s sliding window in O(1): k_frame,
+ * v_frame are [n_layers][frame_tokens][Hkv][Dh] act_dtype, 16-byte aligned.  The frame
+ * overwrites the oldest slot, which then becomes the newest.  Attention
+ * reads the prefix in logical order, so the result equals a fresh
+ * fm_set_prefix_kv of [static | frames oldest..newest] bit for bit.
+ * FM_ERR_STATE if the context has no ring or the prefix was never set.
+ */
+fm_status fm_append_prefix_kv(fm_ctx* ctx, int32_t robot, const void* k_frame,
+                              const void* v_frame);
+
+/*
+ * Run the whole N-step Euler loop for every robot.  noise: [B][C][A] fp32
+ * (x at t = 1); state: [B][state_dim] act_dtype, or NULL iff state_dim is
+ * 0; actions: [B][C][A] fp32 (x at t = 0).  noise and actions may alias.
+ * FM_ERR_STATE if some robot's prefix was never set.  Allocates nothing.
+ */
+fm_status fm_denoise(fm_ctx* ctx, const float* noise, const void* state, float* actions);
+
+/* Fill *info.  Never fails on a valid context. */
+fm_status fm_get_info(const fm_ctx* ctx, fm_info* info);
+
+/* Release the context and its arena (synchronises its stream). NULL-safe. */
+void fm_destroy(fm_ctx* ctx);
+
+/*
+ * Last error message of `ctx`, or of the calling thread's last failed
+ * fm_create / context-free call when ctx is NULL.  Never returns NULL.
+ */
+const char* fm_last_error(const fm_ctx* ctx);
+
+/*
+ * The per-output-row E4M3 quantiser fm_create applies to an fp8 model's
+ * per-layer matrices, exposed for checking.  w: [rows][cols] bf16 (device);
+ * codes: [rows][cols] uint8 (device, OCP E4M3FN); scales: [rows] fp32
+ * (device).  s = max|w_row| / 448 in fp32 (1 for an all-zero row); each
+ * code is the round-to-nearest-even E4M3 value of the fp32 quotient w / s,
+ * saturating at +-448, with the sign of w.  Asynchronous on hip_stream.
+ */
+fm_status fm_quantize_e4m3(const void* w, int32_t rows, int32_t cols, uint8_t* codes,
+                           float* scales, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FM_H_ */

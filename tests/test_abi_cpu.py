@@ -1,0 +1,90 @@
+"""The C ABI library loads, exports every symbol include/fm.h declares, and
+rejects bad arguments before touching a device (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fm_synth as S
+import flow_matching_denoising_euler_amd as fm
+from flow_matching_denoising_euler_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "fm.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv", "fm_denoise", "fm_destroy"):
+        assert n in names
+    assert set(names) == set(_abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fm.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(_abi.fm_config) == 21 * 4
+    assert ctypes.sizeof(_abi.fm_weights) == 11 * 8
+    assert ctypes.sizeof(_abi.fm_info) == 3 * 8 + 4 * 4
+
+
+def _cfg(**kw):
+    return fm.make_config(S.workload("tiny_fp32").replace(**kw))
+
+
+def _create(c):
+    w = _abi.fm_weights()
+    ctx = ctypes.c_void_p()
+    return fm.lib().fm_create(ctypes.byref(c) if c is not None else None, ctypes.byref(w), None, ctypes.byref(ctx)), ctx
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda c: setattr(c, "abi_version", 99), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "d_model", 0), _abi.FM_ERR_SHAPE),
+    (lambda c: setattr(c, "batch", -1), _abi.FM_ERR_SHAPE),
+    (lambda c: setattr(c, "n_kv_heads", 3), _abi.FM_ERR_SHAPE),
+    (lambda c: setattr(c, "norm", 7), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "act_dtype", _abi.FM_FP8_E4M3), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "act_dtype", _abi.FM_BF16), _abi.FM_ERR_UNSUPPORTED),
+    (lambda c: setattr(c, "d_model", 96), _abi.FM_ERR_SHAPE),   # time_dim no longer equals d_model
+    (lambda c: (setattr(c, "d_model", 96), setattr(c, "time_dim", 96)), _abi.FM_ERR_UNSUPPORTED),
+    (lambda c: setattr(c, "action_dim", 7), _abi.FM_ERR_UNSUPPORTED),
+    (lambda c: setattr(c, "n_frames", 2), _abi.FM_ERR_SHAPE),   # frames without frame_tokens
+    (lambda c: setattr(c, "rms_eps", float("nan")), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "exec_mode", 9), _abi.FM_ERR_ARG),
+])
+def test_create_rejects_bad_config_before_device_work(mutate, status):
+    c = _cfg()
+    mutate(c)
+    st, ctx = _create(c)
+    assert st == status, (st, fm.fm_last_error())
+    assert ctx.value is None
+    assert len(fm.fm_last_error()) > 0
+
+
+def test_create_rejects_missing_weights():
+    st, ctx = _create(_cfg())  # all weight pointers NULL
+    assert st == _abi.FM_ERR_ARG and "missing" in fm.fm_last_error()
+    L = fm.lib()
+    assert L.fm_create(None, None, None, None) == _abi.FM_ERR_ARG
+
+
+def test_null_context_calls_fail_cleanly():
+    L = fm.lib()
+    assert L.fm_set_prefix_kv(None, 0, None, None, 0) == _abi.FM_ERR_ARG
+    assert L.fm_append_prefix_kv(None, 0, None, None) == _abi.FM_ERR_ARG
+    assert L.fm_denoise(None, None, None, None) == _abi.FM_ERR_ARG
+    assert L.fm_get_info(None, None) == _abi.FM_ERR_ARG
+    L.fm_destroy(None)
+    assert L.fm_quantize_e4m3(None, 4, 4, None, None, None) == _abi.FM_ERR_ARG
+    assert isinstance(fm.fm_last_error(), str)

@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Tolerances: fp32 workload rel-L2 <= 1e-4; bf16 workloads rel-L2 <= 1e-2 and
+max-abs <= 3e-2; fp8-weight workload rel-L2 <= 5e-2 against the oracle run
+on the same dequantised weights.
+"""
+import numpy as np
+import pytest
+
+import fm_synth as S
+import oracle as O
+from gpu_util import announce, check, run_denoiser, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg):
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    return W, k, v, S.make_noise(cfg), S.make_state(cfg)
+
+
+# --- small and ragged shapes, full element-wise comparison -------------------
+def test_tiny_fp32():
+    cfg = S.workload("tiny_fp32")
+    announce("tiny_fp32")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("tiny_fp32", got, O.denoise(cfg, W, k, v, x0, st), 1e-4)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                                  # one m-tile, 1 key split
+    dict(batch=5, chunk=20, prefix_static=150, prefix_len=150),   # 2 m-tiles (105 rows), 2 key splits
+    dict(batch=3, chunk=7, state_dim=0, prefix_static=0, prefix_len=0),  # no state token, empty prefix
+    dict(n_kv_heads=2, n_q_heads=4, n_layers=3, n_steps=4),  # 2 KV heads, other step count
+    dict(n_q_heads=4, head_dim=256, d_mlp=2048, chunk=30, prefix_static=300, prefix_len=300),  # split-K GEMMs
+])
+def test_small_bf16(kw):
+    cfg = small_cfg(**kw)
+    announce(f"small_bf16 {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check(f"small_bf16 {kw}", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
+def test_small_prefix_shorter_than_capacity():
+    cfg = small_cfg(prefix_static=64, prefix_len=64)
+    W, k, v, x0, st = _inputs(cfg)
+    n = 37
+    announce("prefix 37 of capacity 64")
+    got = run_denoiser(cfg, W, k[:, :, :n].copy(), v[:, :, :n].copy(), x0, st)[0]
+    check("prefix 37/64", got, O.denoise(cfg, W, k[:, :, :n], v[:, :, :n], x0, st), 1e-2, 3e-2)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(batch=4, chunk=25, prefix_static=90, prefix_len=90)])
+def test_small_ada(kw):
+    cfg = small_cfg(norm="ada", time_dim=32, state_dim=0, **kw)
+    announce(f"small_ada {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check(f"small_ada {kw}", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
+def test_small_fp8():
+    cfg = small_cfg(weight_dtype="fp8")
+    announce("small_fp8")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("small_fp8", got, O.denoise(cfg, W, k, v, x0, st), 5e-2)
+
+
+# --- properties --------------------------------------------------------------------
+def test_zero_head_is_identity_bitwise():
+    cfg = small_cfg()
+    W, k, v, x0, st = _inputs(cfg)
+    W["w_out"][:] = 0
+    W["b_out"][:] = 0
+    announce("zero head")
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    assert np.array_equal(got, x0)
+
+
+def test_bias_only_head_bitwise():
+    cfg = small_cfg(n_steps=8)
+    W, k, v, _, st = _inputs(cfg)
+    g = np.random.default_rng(5)
+    b = (g.integers(-64, 64, size=cfg.action_dim) / 16.0).astype(np.float32)
+    x0 = (g.integers(-128, 128, size=(cfg.batch, cfg.chunk, cfg.action_dim)) / 32.0).astype(np.float32)
+    W["w_out"][:] = 0
+    W["b_out"] = b
+    announce("bias-only head")
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    assert np.array_equal(got, x0 - b)
+
+
+def test_run_to_run_bitwise_determinism():
+    cfg = small_cfg(batch=5, chunk=20, prefix_static=150, prefix_len=150)
+    W, k, v, x0, st = _inputs(cfg)
+    announce("determinism")
+    outs = run_denoiser(cfg, W, k, v, x0, st, repeat=3)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_batch_independence():
+    cfg = small_cfg(batch=4)
+    W, k, v, x0, st = _inputs(cfg)
+    announce("batch independence")
+    full = run_denoiser(cfg, W, k, v, x0, st)[0]
+    one = run_denoiser(cfg.replace(batch=1), W, k[2:3], v[2:3], x0[2:3], st[2:3])[0]
+    check("robot 2 alone vs in batch", one[0], full[2].astype(np.float64), 1e-5)
+
+
+def test_quantiser_codes_bit_exact():
+    import torch
+    import flow_matching_denoising_euler_amd as fm
+    g = np.random.default_rng(3)
+    w = S.round_bf16(g.standard_normal((257, 320)) * np.exp(g.standard_normal((257, 1))))
+    w[5] = 0
+    w[7, :10] = [448.0, -448.0, 1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 1e-30, -0.0, 240, 232]
+    announce("fp8 quantiser")
+    wd = torch.from_numpy(w).to("cuda", torch.bfloat16)
+    codes = torch.empty(w.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(w.shape[0], dtype=torch.float32, device="cuda")
+    fm.fm_quantize_e4m3(wd, codes, scales)
+    torch.cuda.synchronize()
+    ref_codes, ref_s = O.quantize_e4m3_per_channel(w)
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+
+
+# --- streaming ring ----------------------------------------------------------------------
+def _ring_run(cfg, ticks, oracle_ticks):
+    """Append one frame per tick to a ring context and re-set a second
+    context with the logical prefix: the two must agree bit for bit; sampled
+    ticks are checked against the oracle."""
+    import torch
+    import flow_matching_denoising_euler_amd as fm
+    W = S.make_weights(cfg)
+    st = S.make_state(cfg)
+    ks, vs = S.make_prefix(cfg, n_tokens=cfg.prefix_static)
+    frames = {t: S.make_frame(cfg, t) for t in range(-cfg.n_frames, 0)}
+    ring = fm.Denoiser(cfg, W)
+    full = fm.Denoiser(cfg, W)
+    W64 = O.effective_weights(cfg, W) if oracle_ticks else None
+    try:
+        def logical(t):
+            fs = [frames[i] for i in range(t - cfg.n_frames + 1, t + 1)]
+            return (np.concatenate([ks] + [f[0] for f in fs], axis=2),
+                    np.concatenate([vs] + [f[1] for f in fs], axis=2))
+        k0, v0 = logical(-1)
+        keep = [ring.set_prefix_kv(b, k0[b], v0[b]) for b in range(cfg.batch)]
+        for t in range(ticks):
+            frames[t] = S.make_frame(cfg, t)
+            frames.pop(t - cfg.n_frames - 1, None)
+            keep += [ring.append_prefix_kv(b, frames[t][0][b], frames[t][1][b]) for b in range(cfg.batch)]
+            x0 = S.make_tick_noise(cfg, t)
+            y_ring = ring.denoise(x0, st).cpu().numpy()
+            kl, vl = logical(t)
+            keep += [full.set_prefix_kv(b, kl[b], vl[b]) for b in range(cfg.batch)]
+            y_full = full.denoise(x0, st).cpu().numpy()
+            torch.cuda.synchronize()
+            keep = keep[-4 * cfg.batch:]
+            assert np.array_equal(y_ring, y_full), f"tick {t}: ring != full recompute"
+            if t in oracle_ticks:
+                ref = np.stack([O.denoise_robot(cfg, W64, kl[b], vl[b], x0[b], st[b])
+                                for b in range(cfg.batch)])
+                check(f"{cfg.name} tick {t}", y_ring, ref, 5e-2 if cfg.weight_dtype == "fp8" else 1e-2)
+        announce(f"{cfg.name}: {ticks} ticks ring == recompute bitwise")
+    finally:
+        ring.close()
+        full.close()
+
+
+def test_small_ring_fp8():
+    cfg = small_cfg(name="small_ring", weight_dtype="fp8", prefix_static=20, frame_tokens=16, n_frames=3,
+                    prefix_len=68, batch=2)
+    _ring_run(cfg, ticks=9, oracle_ticks={0, 4, 8})
+
+
+def test_small_ring_bf16():
+    cfg = small_cfg(name="small_ring_bf16", prefix_static=5, frame_tokens=40, n_frames=4, prefix_len=165)
+    _ring_run(cfg, ticks=6, oracle_ticks={5})
+
+
+# --- full-size workloads ---------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["pi0_1view", "pi0_3view"])
+def test_full_pi0(name):
+    cfg = S.workload(name)
+    announce(f"{name}: generating")
+    W, k, v, x0, st = _inputs(cfg)
+    announce(f"{name}: gpu")
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    announce(f"{name}: oracle")
+    check(name, got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
+def test_full_pi05_ada_b16_sampled_robots():
+    cfg = S.workload("pi05_ada_b16")
+    announce("pi05_ada_b16: generating")
+    W, k, v, x0, st = _inputs(cfg)
+    announce("pi05_ada_b16: gpu")
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    robots = [0, 7, 15]
+    announce("pi05_ada_b16: oracle on robots 0, 7, 15")
+    ref = O.denoise(cfg, W, k, v, x0, st, robots=robots)
+    check("pi05_ada_b16 robots 0,7,15", got[robots], ref, 1e-2, 3e-2)
+
+
+def test_full_stream_fp8_ticks():
+    cfg = S.workload("stream_fp8")
+    _ring_run(cfg, ticks=5, oracle_ticks={0, 3, 4})
