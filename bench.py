@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Denoise-loop benchmark on one MI355X.
+
+One step = one fm_denoise call: the whole Euler loop (10 steps of the action
+expert) for one action chunk of every robot, with weights, prefix K/V, noise
+and state already resident in HBM.  Prints one JSON line on stdout.
+
+The roofline object describes the dominant kernel of the loop, timed live
+with HIP events on the context's stream (torch's current stream) through
+fm_launch_phase; `frac` = achieved / MI355X spec peak.  The loop's own
+fraction of its roofline (algorithmic bytes or flops per chunk over the spec
+peak, against the measured ms per chunk) is reported as `loop_roofline`.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E spec
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA spec
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector spec
+
+METRIC = "denoise-loop ms per action chunk (10 steps) + % of roofline, Pi0-like bs=1"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, info):
+    """Per-chunk algorithmic bytes (weights streamed once per Euler step plus
+    the prefix K/V read once per step) and flops (2*M per matrix parameter
+    plus attention), the figures the roofline is priced on."""
+    d, L, F, Hq, Hkv, Dh = cfg.d_model, cfg.n_layers, cfg.d_mlp, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    S = cfg.suffix
+    M = cfg.batch * S
+    mat = L * (d * (Hq + 2 * Hkv) * Dh + d * Hq * Dh + 3 * d * F) + 2 * cfg.action_dim * d
+    T = cfg.prefix_len
+    attn = 4 * cfg.batch * L * S * Hq * Dh * (T + S)
+    flops = cfg.n_steps * (2 * M * mat + attn)
+    byts = cfg.n_steps * (info.weight_bytes_per_step + info.kv_bytes_per_step)
+    return byts, flops
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("fm_kernels.hip", "fm_internal.h", "fm_engine.cpp"):
+        with open(os.path.join(ROOT, "flow_matching_denoising_euler_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed PMC
+    summary, if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    return t.get("traffic_bytes") if t.get("source_sha") == kernel_source_sha() else None
+
+
+def cpu_baseline(cfg, W, k, v, x0, st, budget_s):
+    """The fp64 oracle as it stands, on this host's cores, on a bounded sample."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    W64 = O.effective_weights(cfg, W)
+    times = []
+    t_start = time.perf_counter()
+    tick = 0
+    while True:
+        b = tick % cfg.batch
+        t0 = time.perf_counter()
+        O.denoise_robot(cfg, W64, k[b], v[b], x0[b], None if st is None else st[b])
+        times.append(time.perf_counter() - t0)
+        tick += 1
+        if time.perf_counter() - t_start > budget_s or tick >= 5:
+            break
+    per_robot_ms = statistics.median(times) * 1e3
+    return {"value": per_robot_ms * cfg.batch, "unit": "ms per action chunk (all robots)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} single-robot chunks of {cfg.name} (fp64 NumPy, median), "
+                      f"scaled x{cfg.batch} robots"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="pi0_1view")
+    ap.add_argument("--exec-mode", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 256 MiB device copy (reference for PMC byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the denoise loop shards by robot with no "
+              "exchange, so there is no multi-GPU figure to measure (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fm_synth as S
+    import flow_matching_denoising_euler_amd as fm
+
+    cfg = S.workload(args.workload)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    log(f"bench: generating {cfg.name}")
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    x0 = S.make_noise(cfg)
+    st = S.make_state(cfg)
+    stream = torch.cuda.current_stream()
+    den = fm.Denoiser(cfg, W, stream=stream, exec_mode=args.exec_mode)
+    keep = [den.set_prefix_kv(b, k[b], v[b]) for b in range(cfg.batch)]
+    noise_d = torch.from_numpy(x0).to(dev)
+    state_d = None if st is None else torch.from_numpy(st).to(dev, torch.bfloat16 if cfg.act_dtype == "bf16"
+                                                              else torch.float32)
+    out = torch.empty_like(noise_d)
+    info = den.info()
+    streaming = cfg.ticks > 0
+    frames = []
+    if streaming:  # a pool of pre-generated frames, resident in HBM
+        for t in range(4):
+            kf, vf = S.make_frame(cfg, t)
+            frames.append([(den._act(kf[b]), den._act(vf[b])) for b in range(cfg.batch)])
+        noises = [torch.from_numpy(S.make_tick_noise(cfg, t)).to(dev) for t in range(4)]
+
+    def one(i):
+        if streaming:
+            for b in range(cfg.batch):
+                fm.fm_append_prefix_kv(den.ctx, b, *frames[i % 4][b])
+            fm.fm_denoise(den.ctx, noises[i % 4], state_d, out)
+        else:
+            fm.fm_denoise(den.ctx, noise_d, state_d, out)
+
+    log(f"bench: warmup {args.warmup}")
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "non-finite actions"
+    # timed region: exactly K steps, synchronised on both sides
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        one(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = total_ms / args.steps
+    pct = lambda p: per[min(len(per) - 1, int(p * len(per)))]
+    log(f"bench: {ms:.4f} ms/chunk (p10 {pct(.1):.4f} p50 {pct(.5):.4f} p90 {pct(.9):.4f} p99 {pct(.99):.4f})")
+
+    # dominant kernel: the gate/up GEMM (largest weight stream per launch)
+    fm.fm_launch_phase(den.ctx, 0, 0, fm._abi.FM_PHASE_GATEUP)
+    reps = 200
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for i in range(reps):
+        fm.fm_launch_phase(den.ctx, i % cfg.n_steps, i % cfg.n_layers, fm._abi.FM_PHASE_GATEUP)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    gu_us = k0.elapsed_time(k1) / reps * 1e3
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+    gu_bytes = 2 * cfg.d_mlp * cfg.d_model * es + (2 * cfg.d_mlp * 4 if cfg.weight_dtype == "fp8" else 0)
+    gu_flops = 2 * cfg.batch * cfg.suffix * 2 * cfg.d_mlp * cfg.d_model
+    byts, flops = algorithmic(cfg, info)
+    mfma_bound = cfg.batch * cfg.suffix * 2 > 312 * es  # arithmetic intensity above the bf16 ridge
+    if mfma_bound:
+        peak = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS
+        achieved = gu_flops / (gu_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(cfg.name)}
+        loop_roof_ms = flops / (peak * 1e12) * 1e3
+    else:
+        achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(cfg.name)}
+        loop_roof_ms = byts / (HBM_PEAK_GBS * 1e9) * 1e3
+    roof["kernel"] = "gate/up GEMM + GELU gate (one layer)"
+    roof["per_launch"] = {"bytes": gu_bytes, "flops": gu_flops, "avg_us": round(gu_us, 3)}
+    log(f"bench: gate/up kernel {gu_us:.2f} us -> {achieved:.1f} {roof['unit']} ({roof['frac']*100:.1f}% of peak)")
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on the host")
+        cpu = cpu_baseline(cfg, W, k, v, x0, st, args.cpu_budget_s)
+        log(f"bench: oracle {cpu['value']:.1f} ms/chunk on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms per action chunk" + (" (16 robots)" if cfg.batch > 1 else "") + (" incl. frame append" if streaming else ""),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
+        "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) prefix K/V and noise)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "chunk": cfg.chunk, "state_tokens": cfg.has_state,
+                   "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps, "d_model": cfg.d_model,
+                   "layers": cfg.n_layers, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
+                   "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),
+                   "parallelism": "single GPU"},
+        "chunks_per_s": round(1000.0 / ms * cfg.batch, 2),
+        "latency_ms": {"p10": round(pct(.1), 4), "p50": round(pct(.5), 4), "p90": round(pct(.9), 4),
+                       "p99": round(pct(.99), 4)},
+        "roofline": roof,
+        "loop_roofline": {"bound": roof["bound"], "roofline_ms": round(loop_roof_ms, 4),
+                          "frac": round(loop_roof_ms / ms, 4),
+                          "algorithmic_bytes_per_chunk": byts, "algorithmic_flops_per_chunk": flops},
+        "cpu_baseline": cpu,
+    }
+    den.close()
+    del keep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,7 @@ from ._abi import (FM_ABI_VERSION, FM_BF16, FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC
                    FM_F32, FM_FP8_E4M3, FM_OK, STATUS_NAMES, fm_config, fm_info, fm_weights)
 
 __all__ = ["FMError", "make_config", "fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv",
-           "fm_denoise", "fm_get_info", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
+           "fm_denoise", "fm_get_info", "fm_launch_phase", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
            "Denoiser", "lib"]
 
 lib = _abi.lib
@@ -130,6 +130,10 @@ def fm_get_info(ctx) -> fm_info:
     info = fm_info()
     _check(lib().fm_get_info(ctx, ctypes.byref(info)), ctx)
     return info
+
+
+def fm_launch_phase(ctx, step: int, layer: int, phase: int):
+    _check(lib().fm_launch_phase(ctx, int(step), int(layer), int(phase)), ctx)
 
 
 def fm_destroy(ctx):

@@ -21,7 +21,8 @@ FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC_PERSISTENT = 0, 1, 2
  FM_LW_NORM1, FM_LW_NORM1_B, FM_LW_NORM2, FM_LW_NORM2_B, FM_LW_COUNT) = range(12)
 
 EXPORTS = ("fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv", "fm_denoise", "fm_get_info",
-           "fm_destroy", "fm_last_error", "fm_quantize_e4m3")
+           "fm_destroy", "fm_last_error", "fm_quantize_e4m3", "fm_launch_phase")
+FM_PHASE_QKV, FM_PHASE_ATTN, FM_PHASE_OPROJ, FM_PHASE_GATEUP, FM_PHASE_DOWN, FM_PHASE_TAIL = range(6)
 
 
 class fm_config(ctypes.Structure):
@@ -72,5 +73,7 @@ def lib() -> ctypes.CDLL:
         L.fm_last_error.restype = ctypes.c_char_p
         L.fm_quantize_e4m3.argtypes = [vp, i32, i32, vp, vp, vp]
         L.fm_quantize_e4m3.restype = ctypes.c_int
+        L.fm_launch_phase.argtypes = [vp, i32, i32, i32]
+        L.fm_launch_phase.restype = ctypes.c_int
         _LIB = L
     return _LIB

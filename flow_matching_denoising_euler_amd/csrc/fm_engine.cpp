@@ -58,14 +58,14 @@ struct fm_ctx {
   // dims
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
   int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
-  int ks_o, ks_d, nqblk, nsplit;
+  int ks_o, ks_d, nqblk, nsplit, kps;
 
   // arena
   void* arena = nullptr;
   size_t arena_bytes = 0;
   std::vector<LayerW> lw;
   void *wout, *w_in, *b_in, *w_state, *b_state;
-  float *temb, *g1, *g2, *gf, *a1, *a2, *bqkv, *bgu, *bout;
+  float *temb, *g1, *g2, *gf, *a1, *a2, *bqkv, *bgu, *bout, *ones, *zeros;
   long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
   void *kpre, *vpre;
   int* meta;
@@ -138,7 +138,8 @@ fm_status validate_config(const fm_config* c) {
   // kernel coverage
   const bool f32 = c->act_dtype == FM_F32;
   const int S = c->chunk + (c->state_dim > 0);
-  if (c->d_model % 64) return fail(nullptr, FM_ERR_UNSUPPORTED, "d_model must be a multiple of 64");
+  if (c->d_model % 64 || c->d_model > 1024)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "d_model must be a multiple of 64 and at most 1024");
   if (c->action_dim != 16 && c->action_dim != 32) return fail(nullptr, FM_ERR_UNSUPPORTED, "action_dim must be 16 or 32");
   if ((c->n_q_heads * c->head_dim) % 32 || ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 16)
     return fail(nullptr, FM_ERR_UNSUPPORTED, "head sizes must give multiples of 32 columns");
@@ -185,14 +186,23 @@ void derive(fm_ctx* x) {
   x->F = c.d_mlp; x->N = c.n_steps; x->HD = x->Hkv * x->Dh;
   x->Nqkv = (x->Hq + 2 * x->Hkv) * x->Dh;
   x->Tcap = c.prefix_static + c.n_frames * c.frame_tokens;
-  x->P = x->d / 16;
+  x->P = 128;  // h^2 partial slots per row (one per 16 columns; unused slots stay zero)
   x->mtiles = (x->M + 63) / 64;
   x->esplit = x->d / 64;
   const int unit = x->wt == ELT_FP8 ? 2 : 1;
-  x->ks_o = pick_split(x->Hq * x->Dh, std::max(1, x->Hq * x->Dh / 512), unit);
-  x->ks_d = pick_split(x->F, std::max(1, x->F / 1024), unit);
-  x->nqblk = (x->S * (x->Hq / x->Hkv) + 15) / 16;
-  x->nsplit = (x->Tcap + x->S + 127) / 128;
+  (void)unit;
+  x->ks_o = 1;
+  x->ks_d = 1;
+  x->nqblk = (x->S * (x->Hq / x->Hkv) + 63) / 64;
+  {
+    // key ranges: about 64 workgroups or more, each range >= 64 keys
+    const int keys = x->Tcap + x->S;
+    const int groups = x->B * x->Hkv * x->nqblk;
+    int ns = std::min(std::min((keys + 63) / 64, (64 + groups - 1) / groups), 8);
+    x->nsplit = std::max(1, ns);
+    x->kps = ((keys + x->nsplit - 1) / x->nsplit + 31) / 32 * 32;
+    x->nsplit = (keys + x->kps - 1) / x->kps;
+  }
 }
 
 // carve every buffer from the arena (plan pass when a.plan)
@@ -227,6 +237,9 @@ void carve(fm_ctx* x, Arena& a) {
   x->bqkv = ada ? (float*)a.take(N * L * x->Nqkv * 4) : nullptr;
   x->bgu = ada ? (float*)a.take(N * L * 2 * x->F * 4) : nullptr;
   x->bout = (float*)a.take((ada ? N * x->A : x->A) * 4);
+  const long ncol = std::max(std::max((long)x->Nqkv, 2L * x->F), std::max(d, (long)x->A));
+  x->ones = (float*)a.take(ncol * 4);
+  x->zeros = (float*)a.take(ncol * 4);
   x->st_g = ada ? L * d : 0;
   x->st_gf = ada ? d : 0;
   x->st_bqkv = L * x->Nqkv;
@@ -252,7 +265,7 @@ void carve(fm_ctx* x, Arena& a) {
   x->partials = (float*)a.take(ks > 1 ? ks * Mp * d * 4 : 16);
   x->attn_part = (float*)a.take(x->act == ELT_F32 || x->nsplit == 1
                                     ? 16
-                                    : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 2) * 4);
+                                    : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 64 * (x->Dh + 2) * 4);
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
                                    (size_t)x->B * x->Hkv * x->nqblk) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);
@@ -260,22 +273,22 @@ void carve(fm_ctx* x, Arena& a) {
 
 Tab T(const float* base, long stride) { return Tab{base, stride}; }
 
-// the launches of one Euler step's transformer layers
-fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
+// one phase kernel of step k, layer l
+fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
   const float eps = x->cfg.rms_eps, inv_d = 1.f / (float)x->d;
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
   const long Tl = (long)x->Tcap * x->HD;  // elements per (robot, layer) of prefix K
-  for (int l = 0; l < x->L; ++l) {
-    const LayerW& w = x->lw[l];
-    GemmArgs g{};
-    g.M = x->M; g.mtiles = x->mtiles; g.ssq = x->ssq; g.P = x->P; g.inv_d = inv_d; g.eps = eps; g.step = k;
-    g.partials = x->partials; g.counters = x->counters;
-    // 1. norm1 -> QKV
+  const LayerW& w = x->lw[l];
+  GemmArgs g{};
+  g.M = x->M; g.mtiles = x->mtiles; g.ssq = x->ssq; g.P = x->P; g.inv_d = inv_d; g.eps = eps; g.step = k;
+  g.partials = x->partials; g.counters = x->counters;
+  g.h = x->h;
+  if (phase == FM_PHASE_QKV) {  // norm1 -> QKV
     g.A = x->u; g.W = w.wqkv; g.wscale = w.sqkv; g.N = x->Nqkv; g.K = x->d; g.nt = 16; g.ksplit = 1;
     g.out = x->qkv;
-    g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(nullptr, 0);
+    g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(x->zeros, 0);
     HIPCHK(x, launch_gemm(x->act, x->wt, EPI_QKV, g, st), "qkv gemm");
-    // 2. attention over [prefix | suffix]
+  } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     AttnArgs at{};
     at.qkv = x->qkv;
     at.kpre = (const char*)x->kpre + (size_t)l * Tl * elt_size(x->act);
@@ -285,34 +298,41 @@ fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
     at.B = x->B; at.S = x->S; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
     at.n_static = x->cfg.prefix_static; at.frame_tokens = std::max(1, x->cfg.frame_tokens);
     at.n_frames = std::max(1, x->cfg.n_frames);
-    at.nqblk = x->nqblk; at.nsplit = x->nsplit;
+    at.nqblk = x->nqblk; at.nsplit = x->nsplit; at.keys_per_split = x->kps;
     at.scale = 1.f / sqrtf((float)x->Dh);
     at.part = x->attn_part; at.counters = x->counters;
     at.out = x->o;
     HIPCHK(x, launch_attn(x->act, at, st), "attention");
-    // 3. O projection + residual; writes u = act(h * g2), ssq
-    GemmArgs r = g;
-    r.A = x->o; r.W = w.wo; r.wscale = w.so; r.N = x->d; r.K = x->Hq * x->Dh; r.ksplit = x->ks_o;
-    r.h = x->h; r.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(nullptr, 0);
-    r.gnext = T(x->g2 + (long)l * x->d, x->st_g);
-    r.u_out = x->u; r.ssq_out = x->ssq;
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, r, st), "o gemm");
-    // 4. norm2 -> gate/up -> GELU gate
-    GemmArgs gu = g;
-    gu.A = x->u; gu.W = w.wgu; gu.wscale = w.sgu; gu.N = 2 * x->F; gu.K = x->d; gu.nt = 32;
-    gu.out = x->z;
-    gu.bias = ada ? T(x->bgu + (long)l * 2 * x->F, x->st_bgu) : T(nullptr, 0);
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_GELU, gu, st), "gate/up gemm");
-    // 5. down + residual; writes the next norm's input
-    GemmArgs dn = r;
-    dn.A = x->z; dn.W = w.wd; dn.wscale = w.sd; dn.N = x->d; dn.K = x->F; dn.ksplit = x->ks_d;
-    dn.alpha = ada ? T(x->a2 + (long)l * x->d, x->st_g) : T(nullptr, 0);
+  } else if (phase == FM_PHASE_OPROJ) {  // O projection + residual; u = act(h * g2), ssq
+    g.A = x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16; g.ksplit = x->ks_o;
+    g.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(x->ones, 0);
+    g.gnext = T(x->g2 + (long)l * x->d, x->st_g);
+    g.u_out = x->u; g.ssq_out = x->ssq;
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, g, st), "o gemm");
+  } else if (phase == FM_PHASE_GATEUP) {  // norm2 -> gate/up -> GELU gate
+    g.A = x->u; g.W = w.wgu; g.wscale = w.sgu; g.N = 2 * x->F; g.K = x->d; g.nt = 32; g.ksplit = 1;
+    g.out = x->z;
+    g.bias = ada ? T(x->bgu + (long)l * 2 * x->F, x->st_bgu) : T(x->zeros, 0);
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_GELU, g, st), "gate/up gemm");
+  } else {  // down + residual; writes the next norm's input
+    g.A = x->z; g.W = w.wd; g.wscale = w.sd; g.N = x->d; g.K = x->F; g.nt = 16; g.ksplit = x->ks_d;
+    g.alpha = ada ? T(x->a2 + (long)l * x->d, x->st_g) : T(x->ones, 0);
     const bool last = l + 1 == x->L;
-    dn.gnext = last ? T(x->gf, x->st_gf) : T(x->g1 + (long)(l + 1) * x->d, x->st_g);
-    dn.u_out = last ? x->uf : x->u;
-    dn.ssq_out = last ? x->ssqf : x->ssq;
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, dn, st), "down gemm");
+    g.gnext = last ? T(x->gf, x->st_gf) : T(x->g1 + (long)(l + 1) * x->d, x->st_g);
+    g.u_out = last ? x->uf : x->u;
+    g.ssq_out = last ? x->ssqf : x->ssq;
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, g, st), "down gemm");
   }
+  return FM_OK;
+}
+
+// the launches of one Euler step's transformer layers
+fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
+  for (int l = 0; l < x->L; ++l)
+    for (int ph = FM_PHASE_QKV; ph <= FM_PHASE_DOWN; ++ph) {
+      fm_status s = enqueue_phase(x, k, l, ph, st);
+      if (s != FM_OK) return s;
+    }
   return FM_OK;
 }
 
@@ -329,7 +349,7 @@ fm_status enqueue_tail(fm_ctx* x, int k, hipStream_t st, float* x_final) {
   o.mtiles = x->mtiles; o.esplit = x->esplit;
   o.do_embed = k + 1 < x->N;
   o.w_in = x->w_in; o.b_in = x->b_in;
-  o.temb = ada ? T(nullptr, 0) : T(x->temb, x->d);
+  o.temb = ada ? T(x->zeros, 0) : T(x->temb, x->d);
   o.embed_step = k + 1;
   o.hs = x->hs; o.h = x->h; o.u = x->u; o.g1 = T(x->g1, x->st_g); o.ssq_out = x->ssq;
   HIPCHK(x, launch_out(x->act, x->ge, o, st), "out/euler");
@@ -341,7 +361,7 @@ fm_status enqueue_embed(fm_ctx* x, const float* noise, const void* state, hipStr
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
   e.noise = noise; e.state = state; e.w_state = x->w_state; e.b_state = x->b_state;
   e.w_in = x->w_in; e.b_in = x->b_in;
-  e.temb = ada ? T(nullptr, 0) : T(x->temb, x->d);
+  e.temb = ada ? T(x->zeros, 0) : T(x->temb, x->d);
   e.x0 = x->xbuf0; e.hs = x->hs; e.h = x->h; e.u = x->u; e.g1 = T(x->g1, x->st_g); e.ssq_out = x->ssq;
   e.B = x->B; e.S = x->S; e.C = x->C; e.A = x->A; e.SD = x->SD; e.d = x->d; e.M = x->M; e.has_state = x->hasS;
   e.mtiles = x->mtiles; e.esplit = x->esplit;
@@ -397,16 +417,16 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
   }
   // one matrix: [rows][cols] in caller dtype -> packed (quantised for fp8);
   // Ada: add beta W to the bias table of this GEMM
-  auto put = [&](const void* m, int rows, int cols, RowMap rm, void* dst, float* dscale, const float* beta,
-                 float* btab, long bstride) -> hipError_t {
+  auto put = [&](const void* m, int rows, int cols, RowMap rm, int ntot, void* dst, float* dscale,
+                 const float* beta, float* btab, long bstride) -> hipError_t {
     hipError_t r;
     if (fp8) {
       if ((r = launch_quantize_e4m3(m, rows, cols, codes, scales, st)) != hipSuccess) return r;
-      if ((r = launch_pack(codes, ELT_FP8, rows, cols, rm, dst, ELT_FP8, 0, st)) != hipSuccess) return r;
+      if ((r = launch_pack(codes, ELT_FP8, rows, cols, rm, dst, ELT_FP8, ntot, st)) != hipSuccess) return r;
       if ((r = launch_scatter_scales(scales, rows, rm, dscale, st)) != hipSuccess) return r;
       if (beta) return launch_bias_gemv(codes, ELT_FP8, scales, rows, cols, beta, L * d, x->N, rm, btab, bstride, st);
     } else {
-      if ((r = launch_pack(m, src, rows, cols, rm, dst, src, 0, st)) != hipSuccess) return r;
+      if ((r = launch_pack(m, src, rows, cols, rm, dst, src, ntot, st)) != hipSuccess) return r;
       if (beta) return launch_bias_gemv(m, src, nullptr, rows, cols, beta, L * d, x->N, rm, btab, bstride, st);
     }
     return hipSuccess;
@@ -428,13 +448,15 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     const float* b2 = ada ? beta2 + l * d : nullptr;
     float* bq = ada ? x->bqkv + l * x->Nqkv : nullptr;
     float* bg = ada ? x->bgu + l * 2 * x->F : nullptr;
-    CHK(put(lp[FM_LW_WQ], qd, x->d, RowMap{qd, 0, 0}, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wq");
-    CHK(put(lp[FM_LW_WK], x->HD, x->d, RowMap{x->HD, 0, qd}, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wk");
-    CHK(put(lp[FM_LW_WV], x->HD, x->d, RowMap{x->HD, 0, qd + x->HD}, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wv");
-    CHK(put(lp[FM_LW_WO], x->d, qd, RowMap{x->d, 0, 0}, lw.wo, lw.so, nullptr, nullptr, 0), "pack wo");
-    CHK(put(lp[FM_LW_WG], x->F, x->d, RowMap{16, 32, 0}, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wg");
-    CHK(put(lp[FM_LW_WU], x->F, x->d, RowMap{16, 32, 16}, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wu");
-    CHK(put(lp[FM_LW_WD], x->d, x->F, RowMap{x->d, 0, 0}, lw.wd, lw.sd, nullptr, nullptr, 0), "pack wd");
+    const int nq = x->Nqkv, nd = x->d, ngu = 2 * x->F;
+    CHK(put(lp[FM_LW_WQ], qd, x->d, RowMap{qd, 0, 0}, nq, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wq");
+    CHK(put(lp[FM_LW_WK], x->HD, x->d, RowMap{x->HD, 0, qd}, nq, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv), "pack wk");
+    CHK(put(lp[FM_LW_WV], x->HD, x->d, RowMap{x->HD, 0, qd + x->HD}, nq, lw.wqkv, lw.sqkv, b1, bq, x->st_bqkv),
+        "pack wv");
+    CHK(put(lp[FM_LW_WO], x->d, qd, RowMap{x->d, 0, 0}, nd, lw.wo, lw.so, nullptr, nullptr, 0), "pack wo");
+    CHK(put(lp[FM_LW_WG], x->F, x->d, RowMap{16, 32, 0}, ngu, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wg");
+    CHK(put(lp[FM_LW_WU], x->F, x->d, RowMap{16, 32, 16}, ngu, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wu");
+    CHK(put(lp[FM_LW_WD], x->d, x->F, RowMap{x->d, 0, 0}, nd, lw.wd, lw.sd, nullptr, nullptr, 0), "pack wd");
   }
   // final norm and the action head
   for (int k = 0; k < (ada ? x->N : 1); ++k)
@@ -447,7 +469,7 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     CHK(launch_copy_convert(w->norm_f, src, d, x->gf, st), "final gain");
     CHK(launch_time_add(x->temb, x->N, x->d, st), "time features");
   }
-  CHK(launch_pack(w->w_out, src, x->A, x->d, RowMap{x->A, 0, 0}, x->wout, src, 0, st), "pack w_out");
+  CHK(launch_pack(w->w_out, src, x->A, x->d, RowMap{x->A, 0, 0}, x->wout, src, x->A, st), "pack w_out");
   CHK(hipMemcpyAsync(x->w_in, w->w_in, (size_t)d * x->A * eg, hipMemcpyDeviceToDevice, st), "copy w_in");
   CHK(hipMemcpyAsync(x->b_in, w->b_in, (size_t)d * eg, hipMemcpyDeviceToDevice, st), "copy b_in");
   if (x->hasS) {
@@ -518,6 +540,13 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
   if ((e = hipMemsetAsync(x->arena, 0, x->arena_bytes, st)) != hipSuccess) {
     hip_fail(x, e, "arena clear");
     return bail(FM_ERR_DEVICE);
+  }
+  {
+    const long ncol = std::max(std::max((long)x->Nqkv, 2L * x->F), std::max((long)x->d, (long)x->A));
+    if ((e = hipMemsetD32Async((hipDeviceptr_t)x->ones, 0x3F800000, ncol, st)) != hipSuccess) {
+      hip_fail(x, e, "ones table");
+      return bail(FM_ERR_DEVICE);
+    }
   }
   if ((s = load_weights(x, w, st)) != FM_OK) return bail(s);
   // the graph: every step's layers and tails except the last tail
@@ -619,6 +648,16 @@ fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* ac
   if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
   HIPCHK(x, hipGraphLaunch(x->gexec, x->stream), "graph launch");
   return enqueue_tail(x, x->N - 1, x->stream, actions);
+}
+
+fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase) {
+  fm_status s = check_ctx(x);
+  if (s != FM_OK) return s;
+  if (step < 0 || step >= x->N || phase < FM_PHASE_QKV || phase > FM_PHASE_TAIL ||
+      (phase != FM_PHASE_TAIL && (layer < 0 || layer >= x->L)))
+    return fail(x, FM_ERR_ARG, "step %d layer %d phase %d out of range", step, layer, phase);
+  if (phase == FM_PHASE_TAIL) return enqueue_tail(x, step, x->stream, step + 1 < x->N ? nullptr : x->xbuf0);
+  return enqueue_phase(x, step, layer, phase, x->stream);
 }
 
 fm_status fm_get_info(const fm_ctx* x, fm_info* info) {

@@ -55,7 +55,8 @@ struct AttnArgs {
   const int* meta;        // [B][2] = (valid prefix tokens, ring head)
   int B, S, Hq, Hkv, Dh, Nqkv;
   int n_static, frame_tokens, n_frames;
-  int nqblk, nsplit;      // query blocks of 16 per (b, kv head); key splits of 128
+  int nqblk, nsplit;      // query blocks of 64 per (b, kv head); key ranges
+  int keys_per_split;     // logical keys per range (multiple of 32)
   float scale;
   float* part;            // partials
   unsigned* counters;

@@ -127,12 +127,14 @@ __device__ __forceinline__ Frag<ACT> load_a(const void* A, int lda, int row, int
   return f;
 }
 
-// Packed weights.  bf16/f32: tile (nb, kb) of 16 columns x 32 k holds, for
-// lane l, column nb*16 + (l & 15) and k = kb*32 + (l >> 4)*8 + [0, 8):
-//   element offset ((nb * KB + kb) * 64 + l) * 8.
-// fp8: tile (nb, kq) of 16 columns x 64 k: lane l holds 16 bytes, bytes
-// [0,8) for k = kq*64 + (l>>4)*8 + j and [8,16) for k + 32:
-//   byte offset ((nb * (K/64) + kq) * 64 + l) * 16.
+// Packed weights, k-major over 1 KB tiles so that the workgroups of a GEMM,
+// which own different column blocks, read interleaved addresses at any
+// moment (spreading HBM channels).  bf16/f32: tile (kb, nb) of 32 k x 16
+// columns holds, for lane l, column nb*16 + (l & 15) and k = kb*32 +
+// (l >> 4)*8 + [0, 8):  element offset ((kb * NBT + nb) * 64 + l) * 8,
+// NBT = N/16.  fp8: tile (kq, nb) of 64 k x 16 columns: lane l holds 16
+// bytes, bytes [0,8) for k = kq*64 + (l>>4)*8 + j and [8,16) for k + 32:
+//   byte offset ((kq * NBT + nb) * 64 + l) * 16.
 template <int ACT, int WT>
 struct WFrag;
 template <>
@@ -143,15 +145,16 @@ template <>
 struct WFrag<ELT_BF16, ELT_FP8> { uint4 v; };  // 16 bytes = two k-blocks of codes
 
 template <int ACT, int WT>
-__device__ __forceinline__ WFrag<ACT, WT> load_w(const void* W, int K, int nb, int kunit, int lane) {
+__device__ __forceinline__ WFrag<ACT, WT> load_w(const void* W, int NBT, int nb, int kunit, int lane) {
   WFrag<ACT, WT> f;
+  const long tile = (long)kunit * NBT + nb;
   if constexpr (WT == ELT_F32) {
-    const float4* p = (const float4*)((const float*)W + (((long)nb * (K >> 5) + kunit) * 64 + lane) * 8);
+    const float4* p = (const float4*)((const float*)W + (tile * 64 + lane) * 8);
     f.lo = p[0]; f.hi = p[1];
   } else if constexpr (WT == ELT_BF16) {
-    f.v = *(const uint4*)((const uint16_t*)W + (((long)nb * (K >> 5) + kunit) * 64 + lane) * 8);
+    f.v = *(const uint4*)((const uint16_t*)W + (tile * 64 + lane) * 8);
   } else {
-    f.v = *(const uint4*)((const uint8_t*)W + (((long)nb * (K >> 6) + kunit) * 64 + lane) * 16);
+    f.v = *(const uint4*)((const uint8_t*)W + (tile * 64 + lane) * 16);
   }
   return f;
 }
@@ -173,176 +176,280 @@ __device__ __forceinline__ f32x4 mma_unit(const Frag<ACT>* a, const WFrag<ACT, W
   }
 }
 
-// Skinny GEMM core: the 64-row tile [m0, m0+64) of A times packed columns
-// [n0, n0 + 16*NB) over k-blocks [kb0, kb0 + nkb).  The 4 waves take k-units
-// round robin; the sum over waves is formed in a fixed order into red.
-template <int ACT, int WT, int NB>
-__device__ __forceinline__ void gemm_core(const void* A, int M, int m0, const void* W, int K, int n0,
-                                          int kb0, int nkb, float (*red)[64][33]) {
-  constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  f32x4 acc[4][NB];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int units = nkb / KU;
-  const int nb0 = n0 >> 4;
-  const int kq0 = kb0 / KU;
+// ---------------------------------------------------------------------------
+// Latency discipline.  On MI355X a dependent global-memory round trip costs
+// about a microsecond, so every kernel below issues all of its global loads
+// (weights, activations and epilogue operands) before it waits on any, uses
+// branch-free address arithmetic (clamped indices, masked values) so the
+// compiler never has to wait inside a guarded load, and writes its results
+// once at the end.
+// ---------------------------------------------------------------------------
 
-  for (int u = wave; u < units; u += 4) {
-    WFrag<ACT, WT> w[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) w[nb] = load_w<ACT, WT>(W, K, nb0 + nb, kq0 + u, lane);
-    Frag<ACT> a[4][KU];
-    const int kb = kb0 + u * KU;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int q = 0; q < KU; ++q)
-        a[mb][q] = load_a<ACT>(A, K, m0 + mb * 16 + (lane & 15), M, (kb + q) * 32 + (lane >> 4) * 8);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mma_unit<ACT, WT>(a[mb], w[nb], acc[mb][nb]);
+constexpr int PM = 128;  // slots of h^2 partial sums per row (one per 16 columns, d <= 2048)
+constexpr int GW = 8;    // waves per GEMM / tail workgroup (512 threads)
+
+__device__ __forceinline__ uint32_t mask_if(bool ok) { return ok ? 0xFFFFFFFFu : 0u; }
+__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+__device__ __forceinline__ float4 and4f(float4 v, uint32_t m) {
+  return make_float4(__uint_as_float(__float_as_uint(v.x) & m), __uint_as_float(__float_as_uint(v.y) & m),
+                     __uint_as_float(__float_as_uint(v.z) & m), __uint_as_float(__float_as_uint(v.w) & m));
+}
+
+// A fragment (rows clamped into [0, M), values of rows >= M zeroed)
+template <int ACT>
+__device__ __forceinline__ Frag<ACT> load_a_m(const void* A, int lda, int row, int M, int k) {
+  const int r = min(row, M - 1);
+  Frag<ACT> f;
+  if constexpr (ACT == ELT_F32) {
+    const float4* p = (const float4*)((const float*)A + (long)r * lda + k);
+    f.lo = p[0];
+    f.hi = p[1];
+  } else {
+    f.v = *(const uint4*)((const uint16_t*)A + (long)r * lda + k);
   }
+  return f;
+}
+template <int ACT>
+__device__ __forceinline__ Frag<ACT> mask_frag(Frag<ACT> f, uint32_t m) {
+  if constexpr (ACT == ELT_F32) {
+    f.lo = and4f(f.lo, m);
+    f.hi = and4f(f.hi, m);
+  } else {
+    f.v = and4(f.v, m);
+  }
+  return f;
+}
+
+// Packed activation layout of a GEMM A operand [M][K] (u, u_f, o, z): MFMA
+// fragment order, so that a wave's fragment load is 1 KB (bf16) contiguous
+// and rows past M (never written, zero since creation) need no masking.
+// Element (row, k) lives at (((mt*KB + kb)*4 + mb)*64 + lane)*8 + (k & 7),
+// mt = row / 64, mb = (row / 16) % 4, kb = k / 32, lane = row % 16 + 16*((k % 32) / 8).
+__device__ __forceinline__ long pk(int row, int k, int K) {
+  return ((((long)(row >> 6) * (K >> 5) + (k >> 5)) * 4 + ((row >> 4) & 3)) * 64 + (row & 15) +
+          16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
+template <int ACT>
+__device__ __forceinline__ Frag<ACT> load_a_pk(const void* A, int K, int mt, int kb, int mb, int lane) {
+  const long off = ((((long)mt * (K >> 5) + kb) * 4 + mb) * 64 + lane) * 8;
+  Frag<ACT> f;
+  if constexpr (ACT == ELT_F32) {
+    const float4* p = (const float4*)((const float*)A + off);
+    f.lo = p[0];
+    f.hi = p[1];
+  } else {
+    f.v = *(const uint4*)((const uint16_t*)A + off);
+  }
+  return f;
+}
+
+// h^2 partials of the 64 rows of a tile, [M][PM]: thread t reads 16 slots of
+// row t >> 3 (4 float4), the sum is finished by rstd_finish.
+__device__ __forceinline__ void rstd_load(const float* ssq, int M, int m0, float4 (&q)[4]) {
+  const int tid = threadIdx.x;
+  const int row = min(m0 + (tid >> 3), M - 1);
+  const float4* p = (const float4*)(ssq + (long)row * PM + (tid & 7) * 16);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int i = 0; i < 4; ++i) q[i] = p[i];
+}
+// fixed-order sum: 16 slots in order, then a butterfly over the 8 lanes of the row
+__device__ __forceinline__ void rstd_finish(const float4 (&q)[4], int M, int m0, float inv_d, float eps,
+                                            float* s_rstd) {
+  const int tid = threadIdx.x;
+  float s = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+  for (int i = 0; i < 4; ++i) s += ((q[i].x + q[i].y) + q[i].z) + q[i].w;
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if ((tid & 7) == 0) s_rstd[tid >> 3] = (m0 + (tid >> 3) < M) ? rsqrtf(s * inv_d + eps) : 0.f;
+}
+
+// sum of the GW waves' accumulators in a fixed order: red[w] = acc(w+4) + acc(w), then ((r0+r1)+r2)+r3
+template <int NB>
+__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[4][NB], float (*red)[64][33]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= 4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][mb * 16 + (lane >> 4) * 4 + r][nb * 16 + (lane & 15)] = acc[mb][nb][r];
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave - 4][mb * 16 + (lane >> 4) * 4 + r][nb * 16 + (lane & 15)] = acc[mb][nb][r];
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* p = &red[wave][mb * 16 + (lane >> 4) * 4 + r][nb * 16 + (lane & 15)];
+          *p = *p + acc[mb][nb][r];
+        }
+  }
   __syncthreads();
 }
 
-// rstd of the 64 rows of a tile from the [M][P] partial sums of h^2
-__device__ __forceinline__ void tile_rstd(const float* ssq, int P, int M, int m0, float inv_d, float eps,
-                                          float* s_rstd) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 2, q = tid & 3;
-  float s = 0.f;
-  if (m0 + row < M) {
-    const float* p = ssq + (long)(m0 + row) * P + q * (P >> 2);
-    for (int i = 0; i < (P >> 2); ++i) s += p[i];
+// One 64-row tile times 16*NB packed columns over k-units [0, units): wave w
+// owns the contiguous units [w*UPW*NPASS, (w+1)*UPW*NPASS), NPASS passes of
+// UPW.  The weights of every pass are loaded first, then pass 0's A
+// fragments; a later pass's A fragments are loaded after the previous
+// pass's MFMAs.
+template <int ACT, int WT, int NB, int UPW, int NPASS>
+struct SkinnyTile {
+  static constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
+  WFrag<ACT, WT> w[NPASS][UPW][NB];
+  Frag<ACT> a[UPW][4][KU];
+  f32x4 acc[4][NB];
+
+  int rw;  // k-range of this wave: rotated by workgroup so that workgroups read different A lines at once
+  __device__ __forceinline__ void set_range(int rot) { rw = ((threadIdx.x >> 6) + rot) & (GW - 1); }
+  __device__ __forceinline__ void load_w_all(const void* W, int NBT, int nb0, int units) {
+    const int lane = threadIdx.x & 63, wave = rw;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int u = min((wave * NPASS + p) * UPW + i, units - 1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) w[p][i][nb] = load_w<ACT, WT>(W, NBT, nb0 + nb, u, lane);
+      }
   }
-  // fixed-order combine of the four quarters
-  const int base = (tid & 63) & ~3;
-  const float s0 = __shfl(s, base + 0), s1 = __shfl(s, base + 1), s2 = __shfl(s, base + 2),
-              s3 = __shfl(s, base + 3);
-  if (q == 0) s_rstd[row] = (m0 + row < M) ? rsqrtf(((s0 + s1) + s2 + s3) * inv_d + eps) : 0.f;
-}
+  // A is in the packed layout (pk)
+  __device__ __forceinline__ void load_a_pass(const void* A, int K, int mt, int units, int p) {
+    const int lane = threadIdx.x & 63, wave = rw;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int u = min((wave * NPASS + p) * UPW + i, units - 1);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < KU; ++q) a[i][mb][q] = load_a_pk<ACT>(A, K, mt, u * KU + q, mb, lane);
+    }
+  }
+  __device__ __forceinline__ void mma_pass(int units, int p) {
+    const int wave = rw;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      if ((wave * NPASS + p) * UPW + i < units) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mma_unit<ACT, WT>(a[i][mb], w[p][i][nb], acc[mb][nb]);
+      }
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
 
 // ---------------------------------------------------------------------------
-// Skinny GEMM with fused epilogues
+// Skinny GEMM with fused epilogues (512 threads per workgroup, one 64-row x
+// 16*NB-column output tile per workgroup, the whole K in the workgroup)
 // ---------------------------------------------------------------------------
-template <int ACT, int WT, int EPI, int NB>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+template <int ACT, int WT, int EPI, int NB, int UPW, int NPASS>
+__global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
+  constexpr int NT = 512, nt = NB * 16, PER = NB * 2;
+  constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
   __shared__ float red[4][64][33];
   __shared__ float s_rstd[64];
-  __shared__ int s_last;
+  __shared__ float s_col[3][32];  // per column: bias or alpha, gnext, fp8 scale
   const int tid = threadIdx.x;
-  const int nt = NB * 16;
   const int ntiles = g.N / nt;
-  int item = blockIdx.x;
-  const int ks = item % g.ksplit;
-  item /= g.ksplit;
-  const int nti = item % ntiles;
-  const int mt = item / ntiles;
+  const int nti = blockIdx.x % ntiles, mt = blockIdx.x / ntiles;
   const int n0 = nti * nt, m0 = mt * 64;
-  const int KB = g.K >> 5;
-  const int kb_split = KB / g.ksplit;
+  const int units = (g.K >> 5) / KU;
 
-  if (EPI != EPI_RESID) tile_rstd(g.ssq, g.P, g.M, m0, g.inv_d, g.eps, s_rstd);
-  gemm_core<ACT, WT, NB>(g.A, g.M, m0, g.W, g.K, n0, ks * kb_split, kb_split, red);
+  // epilogue operands first (registers), then the GEMM operands
+  const int ccol = n0 + min(tid, nt - 1);
+  const float c0 = EPI == EPI_RESID ? g.alpha.base[(long)g.step * g.alpha.step_stride + ccol]
+                                    : g.bias.base[(long)g.step * g.bias.step_stride + ccol];
+  const float c1 = EPI == EPI_RESID ? g.gnext.base[(long)g.step * g.gnext.step_stride + ccol] : 0.f;
+  const float c2 = WT == ELT_FP8 ? g.wscale[ccol] : 1.f;
+  float4 q[4];
+  if (EPI != EPI_RESID) rstd_load(g.ssq, g.M, m0, q);
+  float hold[PER];
+  if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + NT * i;
+      hold[i] = g.h[(long)min(m0 + (idx >> 4), g.M - 1) * g.N + n0 + (idx & 15)];
+    }
+  }
+  SkinnyTile<ACT, WT, NB, UPW, NPASS> t;
+  t.zero();
+  t.set_range(blockIdx.x);
+  t.load_w_all(g.W, g.N >> 4, n0 >> 4, units);
+  t.load_a_pass(g.A, g.K, mt, units, 0);
+  t.mma_pass(units, 0);
+#pragma unroll
+  for (int p = 1; p < NPASS; ++p) {
+    t.load_a_pass(g.A, g.K, mt, units, p);
+    t.mma_pass(units, p);
+  }
+  if (tid < nt) {
+    s_col[0][tid] = c0;
+    s_col[1][tid] = c1;
+    s_col[2][tid] = c2;
+  }
+  if (EPI != EPI_RESID) rstd_finish(q, g.M, m0, g.inv_d, g.eps, s_rstd);
+  reduce_waves<NB>(t.acc, red);
 
-  // sum over waves in a fixed order; thread owns outputs idx = tid + 256 i
-  constexpr int PER = NB * 4;  // 64*nt/256
   float v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int idx = tid + 256 * i, row = idx / nt, col = idx % nt;
+    const int idx = tid + NT * i, row = idx / nt, col = idx % nt;
     v[i] = ((red[0][row][col] + red[1][row][col]) + red[2][row][col]) + red[3][row][col];
   }
-  if (g.ksplit > 1) {
-    float* P = g.partials + ((long)ks * g.mtiles * 64 + m0) * g.N + n0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, row = idx / nt, col = idx % nt;
-      st_dev(P + (long)row * g.N + col, v[i]);
-    }
-    drain_vm();
-    __syncthreads();
-    if (tid == 0) {
-      unsigned* c = g.counters + mt * ntiles + nti;
-      const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (old == (unsigned)g.ksplit - 1);
-      if (s_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    const float* P0 = g.partials + (long)m0 * g.N + n0;
-    const long kstride = (long)g.mtiles * 64 * g.N;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, row = idx / nt, col = idx % nt;
-      float s = 0.f;
-      for (int k = 0; k < g.ksplit; ++k) s += ld_dev(P0 + k * kstride + (long)row * g.N + col);
-      v[i] = s;
-    }
-  }
-  __syncthreads();  // s_rstd visible
 
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, row = idx / nt, col = n0 + idx % nt;
+      const int idx = tid + NT * i, row = idx / nt, c = idx % nt;
       const int r = m0 + row;
-      if (r >= g.M) continue;
-      float a = v[i];
-      if (WT == ELT_FP8) a *= g.wscale[col];
-      st_act<ACT>(g.out, (long)r * g.N + col, a * s_rstd[row] + tab(g.bias, g.step, col));
+      if (r < g.M) st_act<ACT>(g.out, (long)r * g.N + n0 + c, v[i] * s_col[2][c] * s_rstd[row] + s_col[0][c]);
     }
   } else if constexpr (EPI == EPI_GELU) {
-    // tile = [16 gate | 16 up]: thread pairs (row, j) with j < 16; NB == 2
-    __shared__ float s_t[64][33];
+    // tile = [16 gate | 16 up] (NB == 2): pair them through red[0]
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i;
-      s_t[idx / nt][idx % nt] = v[i];
+      const int idx = tid + NT * i;
+      red[0][idx / nt][idx % nt] = v[i];
     }
     __syncthreads();
     const int F = g.N >> 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 4, j = idx & 15;
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + NT * i, row = idx >> 4, j = idx & 15;
       const int r = m0 + row;
-      if (r >= g.M) continue;
-      float gv = s_t[row][j], uv = s_t[row][16 + j];
-      if (WT == ELT_FP8) { gv *= g.wscale[n0 + j]; uv *= g.wscale[n0 + 16 + j]; }
-      gv = gv * s_rstd[row] + tab(g.bias, g.step, n0 + j);
-      uv = uv * s_rstd[row] + tab(g.bias, g.step, n0 + 16 + j);
-      st_act<ACT>(g.out, (long)r * F + nti * 16 + j, gelu_erf(gv) * uv);
+      const float gv = red[0][row][j] * s_col[2][j] * s_rstd[row] + s_col[0][j];
+      const float uv = red[0][row][16 + j] * s_col[2][16 + j] * s_rstd[row] + s_col[0][16 + j];
+      if (r < g.M) st_act<ACT>(g.out, pk(r, nti * 16 + j, F), gelu_erf(gv) * uv);
     }
-  } else {  // EPI_RESID, NB == 1: 16 threads of a row are consecutive lanes
+  } else {  // EPI_RESID (NB == 1): the 16 threads of a row are consecutive lanes
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, row = idx / nt, col = n0 + idx % nt;
+      const int idx = tid + NT * i, row = idx >> 4, c = idx & 15;
       const int r = m0 + row;
-      float a = v[i];
-      if (WT == ELT_FP8) a *= g.wscale[col];
-      float hn = 0.f;
+      const float hn = (r < g.M) ? hold[i] + s_col[0][c] * (v[i] * s_col[2][c]) : 0.f;
+      float qq = hn * hn;
+      qq += __shfl_xor(qq, 1);
+      qq += __shfl_xor(qq, 2);
+      qq += __shfl_xor(qq, 4);
+      qq += __shfl_xor(qq, 8);
       if (r < g.M) {
-        const long o = (long)r * g.N + col;
-        hn = g.h[o] + tab_or1(g.alpha, g.step, col) * a;
+        const long o = (long)r * g.N + n0 + c;
         g.h[o] = hn;
-        st_act<ACT>(g.u_out, o, hn * tab_or1(g.gnext, g.step, col));
+        st_act<ACT>(g.u_out, pk(r, n0 + c, g.N), hn * s_col[1][c]);
+        if (c == 0) g.ssq_out[(long)r * PM + (n0 >> 4)] = qq;
       }
-      float q = hn * hn;
-      q += __shfl_xor(q, 1);
-      q += __shfl_xor(q, 2);
-      q += __shfl_xor(q, 4);
-      q += __shfl_xor(q, 8);
-      if (r < g.M && (idx % nt) == 0) g.ssq_out[(long)r * (g.N >> 4) + (col >> 4)] = q;
     }
   }
 }
@@ -350,34 +457,38 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Attention of the suffix queries over [prefix (logical order) | suffix]
 // ---------------------------------------------------------------------------
-// pointer to key/value row `key` (logical index) of robot b, kv head j
+// K or V row of logical key `key` (robot b, kv head j), branch-free: prefix
+// keys go through the static region and the frame ring (logical frame f of
+// the window lives in slot (head + f) mod n_frames), suffix keys come from
+// this step's QKV output.
 template <typename T>
-__device__ __forceinline__ const T* kv_row(const AttnArgs& a, const void* pre, int b, int j, int key, int tv,
-                                           int head, int which /*0 K, 1 V*/) {
-  if (key < tv) {
-    int phys = key;
-    if (key >= a.n_static) {
-      const int f = (key - a.n_static) / a.frame_tokens, off = (key - a.n_static) % a.frame_tokens;
-      phys = a.n_static + ((head + f) % a.n_frames) * a.frame_tokens + off;
-    }
-    return (const T*)pre + b * a.b_stride + ((long)phys * a.Hkv + j) * a.Dh;
-  }
-  const int s = key - tv;
-  return (const T*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)(a.Hq + which * a.Hkv + j) * a.Dh;
+__device__ __forceinline__ const T* kv_ptr(const AttnArgs& a, const void* pre, int b, int j, int key, int tv,
+                                           int head, int which) {
+  const int rel = max(key - a.n_static, 0);
+  const int f = rel / a.frame_tokens, off = rel - f * a.frame_tokens;
+  int slot = head + f;
+  slot -= (slot >= a.n_frames) ? a.n_frames : 0;
+  const int phys = key < a.n_static ? key : a.n_static + slot * a.frame_tokens + off;
+  const T* pp = (const T*)pre + b * a.b_stride + ((long)phys * a.Hkv + j) * a.Dh;
+  const int s = max(key - tv, 0);
+  const T* sp = (const T*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)(a.Hq + which * a.Hkv + j) * a.Dh;
+  return key < tv ? pp : sp;
 }
 
-// bf16 MFMA attention.  Workgroup = one block of 16 queries (suffix row x
-// head of one KV group) against 128 logical keys; each wave takes 32 keys,
-// the 4 waves combine through LDS, and key splits across workgroups are
-// combined by the last arriver in split order.
+// bf16 MFMA attention, flash style.  Workgroup = 64 queries (4 waves x 16
+// rows; a query is one suffix row of one head of the KV group) against one
+// contiguous range of logical keys, walked in tiles of 32 keys.  K and V^T
+// of a tile are staged in LDS and shared by the 4 waves; two tiles are in
+// flight in registers ahead of the one in use.  Online softmax per row.
+// Several key ranges are merged by k_attn_combine in range order.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-  constexpr int KBD = DH / 32, NBD = DH / 16;
-  __shared__ __align__(16) uint16_t s_p[4][16][40];
-  __shared__ float s_m[4][16], s_l[4][16];
-  __shared__ float s_o[16][DH + 4];
-  __shared__ float s_row[2][16];
-  __shared__ int s_last;
+__global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
+  constexpr int KBD = DH / 32, NBD = DH / 16, KT = 32;
+  constexpr int CH = KT * DH / 8;  // 16-byte chunks per K (or V) tile
+  constexpr int CPT = (CH + 255) / 256;
+  __shared__ __align__(16) uint16_t sK[KT][DH + 8];
+  __shared__ __align__(16) uint16_t sVt[DH][KT + 8];
+  __shared__ __align__(16) uint16_t sP[4][16][KT + 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int item = blockIdx.x;
   const int sp = item % a.nsplit;
@@ -388,175 +499,199 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int G = a.Hq / a.Hkv, nq = a.S * G;
   const int tv = a.meta[2 * b], head = a.meta[2 * b + 1];
   const int nkeys = tv + a.S;
-  const int kbeg = sp * 128 + wave * 32;
+  const int kbeg = sp * a.keys_per_split, kend = min(nkeys, kbeg + a.keys_per_split);
+  const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
 
-  // Q fragments (A operand): query qi = qb*16 + (lane & 15)
+  // tile loader: chunk c -> key c / (DH/8), dims (c % (DH/8)) * 8 .. +8
+  uint4 kr[2][CPT], vr[2][CPT];
+  uint32_t km[2][CPT];  // zero mask of keys past the range, applied when the tile reaches LDS
+  auto load_tile = [&](int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = min(tid + 256 * i, CH - 1);
+      const int key = kbeg + t * KT + c / (DH / 8), d0 = (c % (DH / 8)) * 8;
+      const int kc = min(key, kend - 1);
+      km[slot][i] = mask_if(key < kend);
+      kr[slot][i] = *(const uint4*)(kv_ptr<uint16_t>(a, a.kpre, b, j, kc, tv, head, 0) + d0);
+      vr[slot][i] = *(const uint4*)(kv_ptr<uint16_t>(a, a.vpre, b, j, kc, tv, head, 1) + d0);
+    }
+  };
+  if (ntile > 0) load_tile(0, 0);
+  if (ntile > 1) load_tile(1, 1);
+  // this wave's 16 queries as A fragments
   uint4 qf[KBD];
   {
-    const int qi = qb * 16 + (lane & 15);
-    if (qi < nq) {
-      const int s = qi / G, h = j * G + qi % G;
-      const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
+    const int qi = min(qb * 64 + wave * 16 + (lane & 15), nq - 1);
+    const int s = qi / G, h = j * G + qi % G;
+    const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
 #pragma unroll
-      for (int kb = 0; kb < KBD; ++kb) qf[kb] = *(const uint4*)(qp + kb * 32);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KBD; ++kb) qf[kb] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  // scores for this wave's 32 keys
-  f32x4 sacc[2];
-  bool kval[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    sacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int key = kbeg + nb * 16 + (lane & 15);
-    kval[nb] = key < nkeys;
-    const uint16_t* kp = kval[nb] ? kv_row<uint16_t>(a, a.kpre, b, j, key, tv, head, 0) : nullptr;
-#pragma unroll
-    for (int kb = 0; kb < KBD; ++kb) {
-      const uint4 kf = kp ? *(const uint4*)(kp + kb * 32 + (lane >> 4) * 8) : make_uint4(0, 0, 0, 0);
-      sacc[nb] = mma_bf16(qf[kb], kf, sacc[nb]);
-    }
-  }
-  float mrow[4], lrow[4], p[2][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      p[nb][r] = kval[nb] ? sacc[nb][r] * a.scale : -INFINITY;
-      m = fmaxf(m, p[nb][r]);
-    }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    m = fmaxf(m, __shfl_xor(m, 8));
-    float l = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      p[nb][r] = (m == -INFINITY) ? 0.f : __expf(p[nb][r] - m);
-      l += p[nb][r];
-    }
-    l += __shfl_xor(l, 1);
-    l += __shfl_xor(l, 2);
-    l += __shfl_xor(l, 4);
-    l += __shfl_xor(l, 8);
-    mrow[r] = m;
-    lrow[r] = l;
-  }
-  // P (bf16) to the A layout through LDS
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_p[wave][(lane >> 4) * 4 + r][nb * 16 + (lane & 15)] = (uint16_t)f2bf(p[nb][r]);
-  __syncthreads();
-  const uint4 pf = *(const uint4*)&s_p[wave][lane & 15][(lane >> 4) * 8];
-  // V fragments: lane l needs V[key0 + (l>>4)*8 + jj][dh = nbd*16 + (l & 15)]
-  const uint16_t* vrow[8];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int key = kbeg + (lane >> 4) * 8 + jj;
-    vrow[jj] = key < nkeys ? kv_row<uint16_t>(a, a.vpre, b, j, key, tv, head, 1) : nullptr;
+    for (int kb = 0; kb < KBD; ++kb) qf[kb] = *(const uint4*)(qp + kb * 32);
   }
   f32x4 oacc[NBD];
 #pragma unroll
-  for (int nbd = 0; nbd < NBD; ++nbd) {
-    const int dh = nbd * 16 + (lane & 15);
-    uint32_t e[8];
+  for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrow[4] = {0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int t, int slot) {
+    __syncthreads();  // the previous tile is no longer read
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) e[jj] = vrow[jj] ? vrow[jj][dh] : 0u;
-    const uint4 vf = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
-    oacc[nbd] = mma_bf16(pf, vf, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
-  // combine the 4 waves in a fixed order
-  if ((lane & 15) == 0) {
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      if (c < CH) {
+        const int key = c / (DH / 8), d0 = (c % (DH / 8)) * 8;
+        *(uint4*)&sK[key][d0] = and4(kr[slot][i], km[slot][i]);
+        const uint4 vm = and4(vr[slot][i], km[slot][i]);
+        const uint32_t vv[4] = {vm.x, vm.y, vm.z, vm.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sVt[d0 + 2 * e][key] = (uint16_t)(vv[e] & 0xFFFF);
+          sVt[d0 + 2 * e + 1][key] = (uint16_t)(vv[e] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    if (t + 2 < ntile) load_tile(t + 2, slot);
+    f32x4 sacc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      sacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KBD; ++kb) {
+        const uint4 kf = *(const uint4*)&sK[nb * 16 + (lane & 15)][kb * 32 + (lane >> 4) * 8];
+        sacc[nb] = mma_bf16(qf[kb], kf, sacc[nb]);
+      }
+    }
+    float p[2][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s_m[wave][(lane >> 4) * 4 + r] = mrow[r];
-      s_l[wave][(lane >> 4) * 4 + r] = lrow[r];
+      float m = mrow[r];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int key = kbeg + t * KT + nb * 16 + (lane & 15);
+        p[nb][r] = key < kend ? sacc[nb][r] * a.scale : -INFINITY;
+        m = fmaxf(m, p[nb][r]);
+      }
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 8));
+      const float corr = (mrow[r] == -INFINITY) ? 0.f : __expf(mrow[r] - m);
+      float l = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        p[nb][r] = (m == -INFINITY) ? 0.f : __expf(p[nb][r] - m);
+        l += p[nb][r];
+      }
+      l += __shfl_xor(l, 1);
+      l += __shfl_xor(l, 2);
+      l += __shfl_xor(l, 4);
+      l += __shfl_xor(l, 8);
+      lrow[r] = lrow[r] * corr + l;
+      mrow[r] = m;
+#pragma unroll
+      for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd][r] *= corr;
     }
+    // P (bf16) into the A layout through this wave's LDS rows
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sP[wave][(lane >> 4) * 4 + r][nb * 16 + (lane & 15)] = (uint16_t)f2bf(p[nb][r]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    const uint4 pf = *(const uint4*)&sP[wave][lane & 15][(lane >> 4) * 8];
+#pragma unroll
+    for (int nbd = 0; nbd < NBD; ++nbd) {
+      const uint4 vf = *(const uint4*)&sVt[nbd * 16 + (lane & 15)][(lane >> 4) * 8];
+      oacc[nbd] = mma_bf16(pf, vf, oacc[nbd]);
+    }
+  };
+  for (int t = 0; t < ntile; t += 2) {
+    step(t, 0);
+    if (t + 1 < ntile) step(t + 1, 1);
   }
-  __syncthreads();
-  float sc[4];
+
+  // normalise by this range's row sums
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = (lane >> 4) * 4 + r;
-    float M = fmaxf(fmaxf(s_m[0][row], s_m[1][row]), fmaxf(s_m[2][row], s_m[3][row]));
-    sc[r] = (s_m[wave][row] == -INFINITY) ? 0.f : __expf(s_m[wave][row] - M);
-  }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+    const float inv = lrow[r] > 0.f ? 1.f / lrow[r] : 0.f;
 #pragma unroll
-      for (int nbd = 0; nbd < NBD; ++nbd)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* o = &s_o[(lane >> 4) * 4 + r][nbd * 16 + (lane & 15)];
-          *o = (w == 0 ? 0.f : *o) + sc[r] * oacc[nbd][r];
-        }
-    }
-    __syncthreads();
+    for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd][r] *= inv;
   }
-  if (tid < 16) {
-    const int row = tid;
-    float M = fmaxf(fmaxf(s_m[0][row], s_m[1][row]), fmaxf(s_m[2][row], s_m[3][row]));
-    float L = 0.f;
-    for (int w = 0; w < 4; ++w) L += (s_m[w][row] == -INFINITY) ? 0.f : __expf(s_m[w][row] - M) * s_l[w][row];
-    s_row[0][row] = M;
-    s_row[1][row] = L;
-  }
-  __syncthreads();
-
-  const long grp = ((long)b * a.Hkv + j) * a.nqblk + qb;
   if (a.nsplit > 1) {
-    const long blk = 16 * (DH + 2);
+    // partial block for k_attn_combine: [64 rows][DH] normalised O, then (m, l) per row
+    const long grp = ((long)b * a.Hkv + j) * a.nqblk + qb;
+    const long blk = 64L * (DH + 2);
     float* part = a.part + (grp * a.nsplit + sp) * blk;
-    for (int i = tid; i < 16 * DH; i += 256) st_dev(part + 32 + i, s_o[i / DH][i % DH]);
-    if (tid < 32) st_dev(part + tid, s_row[tid >> 4][tid & 15]);
-    drain_vm();
-    __syncthreads();
-    if (tid == 0) {
-      unsigned* c = a.counters + grp;
-      const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (old == (unsigned)a.nsplit - 1);
-      if (s_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    const float* p0 = a.part + grp * a.nsplit * blk;
-    if (tid < 16) {
-      float M = -INFINITY;
-      for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ld_dev(p0 + s * blk + tid));
-      float L = 0.f;
-      for (int s = 0; s < a.nsplit; ++s) {
-        const float ms = ld_dev(p0 + s * blk + tid);
-        L += (ms == -INFINITY) ? 0.f : __expf(ms - M) * ld_dev(p0 + s * blk + 16 + tid);
+#pragma unroll
+    for (int nbd = 0; nbd < NBD; ++nbd)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        part[(long)(wave * 16 + (lane >> 4) * 4 + r) * DH + nbd * 16 + (lane & 15)] = oacc[nbd][r];
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 16 + (lane >> 4) * 4 + r;
+        *(float2*)(part + 64L * DH + 2 * row) = make_float2(mrow[r], lrow[r]);
       }
-      s_row[0][tid] = M;
-      s_row[1][tid] = L;
     }
-    __syncthreads();
-    for (int i = tid; i < 16 * DH; i += 256) {
-      const int row = i / DH;
-      const float M = s_row[0][row];
-      float o = 0.f;
-      for (int s = 0; s < a.nsplit; ++s) {
-        const float ms = ld_dev(p0 + s * blk + row);
-        const float w = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-        o += w * ld_dev(p0 + s * blk + 32 + i);
-      }
-      s_o[row][i % DH] = o;
-    }
-    __syncthreads();
+    return;
   }
-  for (int i = tid; i < 16 * DH; i += 256) {
-    const int row = i / DH, dh = i % DH;
-    const int qi = qb * 16 + row;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qi = qb * 64 + wave * 16 + (lane >> 4) * 4 + r;
     if (qi >= nq) continue;
     const int s = qi / G, h = j * G + qi % G;
-    ((uint16_t*)a.out)[(long)(b * a.S + s) * (a.Hq * DH) + (long)h * DH + dh] =
-        (uint16_t)f2bf(s_o[row][dh] / s_row[1][row]);
+    const int row = b * a.S + s;
+#pragma unroll
+    for (int nbd = 0; nbd < NBD; ++nbd)
+      ((uint16_t*)a.out)[pk(row, h * DH + nbd * 16 + (lane & 15), a.Hq * DH)] = (uint16_t)f2bf(oacc[nbd][r]);
   }
+}
+
+constexpr int NSPLIT_MAX = 8;
+
+// Combine the key ranges of k_attn_flash in range order: O = sum_s w_s O_s /
+// sum_s w_s with w_s = l_s exp(m_s - max m).  Workgroup = 8 query rows of
+// one block; thread = 8 head dims of one row; all ranges loaded at once.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+  const int grp = blockIdx.x >> 3, rg = blockIdx.x & 7;
+  const int qb = grp % a.nqblk, j = (grp / a.nqblk) % a.Hkv, b = grp / (a.nqblk * a.Hkv);
+  const int row = rg * 8 + (threadIdx.x >> 5), c8 = (threadIdx.x & 31) * 8;
+  const int G = a.Hq / a.Hkv, nq = a.S * G;
+  const int qi = qb * 64 + row;
+  if (c8 >= DH || qi >= nq) return;
+  const long blk = 64L * (DH + 2);
+  const float* p0 = a.part + (long)grp * a.nsplit * blk;
+  float2 ml[NSPLIT_MAX];
+  float4 o[NSPLIT_MAX][2];
+#pragma unroll
+  for (int s = 0; s < NSPLIT_MAX; ++s) {
+    const int sc = min(s, a.nsplit - 1);
+    ml[s] = *(const float2*)(p0 + sc * blk + 64L * DH + 2 * row);
+    const float4* op = (const float4*)(p0 + sc * blk + (long)row * DH + c8);
+    o[s][0] = op[0];
+    o[s][1] = op[1];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NSPLIT_MAX; ++s) M = fmaxf(M, s < a.nsplit ? ml[s].x : -INFINITY);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < NSPLIT_MAX; ++s) {
+    const float w = (s >= a.nsplit || ml[s].x == -INFINITY) ? 0.f : ml[s].y * __expf(ml[s].x - M);
+    wsum += w;
+    acc[0] += w * o[s][0].x; acc[1] += w * o[s][0].y; acc[2] += w * o[s][0].z; acc[3] += w * o[s][0].w;
+    acc[4] += w * o[s][1].x; acc[5] += w * o[s][1].y; acc[6] += w * o[s][1].z; acc[7] += w * o[s][1].w;
+  }
+  const float inv = 1.f / wsum;
+  const int s = qi / G, h = j * G + qi % G;
+  uint4 r;
+  r.x = f2bf(acc[0] * inv) | (f2bf(acc[1] * inv) << 16);
+  r.y = f2bf(acc[2] * inv) | (f2bf(acc[3] * inv) << 16);
+  r.z = f2bf(acc[4] * inv) | (f2bf(acc[5] * inv) << 16);
+  r.w = f2bf(acc[6] * inv) | (f2bf(acc[7] * inv) << 16);
+  *(uint4*)((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH)) = r;
 }
 
 // fp32 attention (small head dims): one workgroup per (robot, query head),
@@ -573,8 +708,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     for (int c = 0; c < Dh; ++c) { q[c] = qp[c]; o[c] = 0.f; }
     float m = -INFINITY, l = 0.f;
     for (int key = 0; key < nkeys; ++key) {
-      const float* kp = kv_row<float>(a, a.kpre, b, j, key, tv, head, 0);
-      const float* vp = kv_row<float>(a, a.vpre, b, j, key, tv, head, 1);
+      const float* kp = kv_ptr<float>(a, a.kpre, b, j, key, tv, head, 0);
+      const float* vp = kv_ptr<float>(a, a.vpre, b, j, key, tv, head, 1);
       float sc = 0.f;
       for (int c = 0; c < Dh; ++c) sc += q[c] * kp[c];
       sc *= a.scale;
@@ -585,126 +720,159 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       for (int c = 0; c < Dh; ++c) o[c] = o[c] * corr + pe * vp[c];
       m = mn;
     }
-    float* op = (float*)a.out + (long)(b * a.S + s) * (a.Hq * Dh) + (long)h * Dh;
-    for (int c = 0; c < Dh; ++c) op[c] = o[c] / l;
+    for (int c = 0; c < Dh; ++c) ((float*)a.out)[pk(b * a.S + s, h * Dh + c, a.Hq * Dh)] = o[c] / l;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Embedding of the suffix rows (shared by the first embed and the step tail)
+// Embedding of the suffix rows (first embed and the step tail)
 // ---------------------------------------------------------------------------
-// rows [m0, m0+64) x columns [c0, c0+64): state rows take hs, action rows
-// take x W_in^T + b_in + temb.  Writes h, u = act(h * g1) and ssq partials.
-template <int ACT, int WE>
-__device__ __forceinline__ void embed_tile(int m0, int c0, int M, int S, int has_state, int A, int d,
-                                           const float (*s_x)[33], const float* hs_src, const void* w_in,
-                                           const void* b_in, const Tab& temb, int step, float* h, void* u,
-                                           const Tab& g1, float* ssq_out) {
-  const int tid = threadIdx.x;
-  const int col = c0 + (tid & 63);
+// Operands of the 64-row x 64-column embedding tile owned by a thread: one
+// column, 8 rows (tid >> 6) + 8 i.  Loaded before any wait.
+template <int WE>
+struct EmbedCol {
   float w[32];
+  float bias, gain;
+  float hsv[8];
+  __device__ __forceinline__ void load(int c0, int A, const void* w_in, const void* b_in, const Tab& temb,
+                                       const Tab& g1, int step, const float* hs, int m0, int M, int S, int d) {
+    const int col = c0 + (threadIdx.x & 63);
 #pragma unroll
-  for (int a = 0; a < 32; ++a) w[a] = a < A ? ld_w(w_in, WE, (long)col * A + a) : 0.f;
-  const float bias = ld_w(b_in, WE, col) + tab(temb, step, col);
-  const float gain = tab_or1(g1, step, col);
-  const int P = d >> 4;
-  for (int i = 0; i < 16; ++i) {
-    const int lr = (tid >> 6) + 4 * i, r = m0 + lr;
-    float hv = 0.f;
-    if (r < M) {
-      const int b = r / S, s = r % S;
-      if (has_state && s == 0) {
-        hv = hs_src[(long)b * d + col];
-      } else {
-        float acc = 0.f;
+    for (int a = 0; a < 32; ++a) w[a] = ld_w(w_in, WE, (long)col * A + min(a, A - 1));
+    bias = ld_w(b_in, WE, col) + temb.base[(long)step * temb.step_stride + col];
+    gain = g1.base[(long)step * g1.step_stride + col];
 #pragma unroll
-        for (int a = 0; a < 32; ++a) acc += s_x[lr][a] * w[a];
-        hv = acc + bias;
-      }
-      h[(long)r * d + col] = hv;
-      st_act<ACT>(u, (long)r * d + col, hv * gain);
+    for (int i = 0; i < 8; ++i) {
+      const int r = min(m0 + (threadIdx.x >> 6) + 8 * i, M - 1);
+      hsv[i] = hs[(long)(r / S) * d + col];
     }
-    float q = hv * hv;
-    q += __shfl_xor(q, 1);
-    q += __shfl_xor(q, 2);
-    q += __shfl_xor(q, 4);
-    q += __shfl_xor(q, 8);
-    if (r < M && (tid & 15) == 0) ssq_out[(long)r * P + (col >> 4)] = q;
   }
-}
+  // h, u = act(h * gain) and the h^2 partial of this 16-column group
+  template <int ACT>
+  __device__ __forceinline__ void emit(int c0, int m0, int M, int S, int has_state, int A, int d,
+                                       const float (*s_x)[33], float* h, void* u, float* ssq_out) {
+    const int col = c0 + (threadIdx.x & 63);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int lr = (threadIdx.x >> 6) + 8 * i, r = m0 + lr;
+      float acc = 0.f;
+#pragma unroll
+      for (int a = 0; a < 32; ++a) acc += (a < A ? s_x[lr][a] : 0.f) * w[a];
+      const bool st = has_state && (r % S) == 0;
+      const float hv = (r < M) ? (st ? hsv[i] : acc + bias) : 0.f;
+      float q = hv * hv;
+      q += __shfl_xor(q, 1);
+      q += __shfl_xor(q, 2);
+      q += __shfl_xor(q, 4);
+      q += __shfl_xor(q, 8);
+      if (r < M) {
+        h[(long)r * d + col] = hv;
+        st_act<ACT>(u, pk(r, col, d), hv * gain);
+        if ((threadIdx.x & 15) == 0) ssq_out[(long)r * PM + (col >> 4)] = q;
+      }
+    }
+  }
+};
 
+// First embedding of a chunk: x0 = noise, state rows h = state W_s^T + b_s,
+// action rows h = x0 W_in^T + b_in (+ time feature of step 0).
 template <int ACT, int WE>
-__global__ __launch_bounds__(256) void k_embed(EmbedArgs e) {
+__global__ __launch_bounds__(512) void k_embed(EmbedArgs e) {
   __shared__ float s_x[64][33];
   const int mt = blockIdx.x / e.esplit, es = blockIdx.x % e.esplit;
-  const int m0 = mt * 64;
-  const int cw = e.d / e.esplit, c0 = es * cw;
+  const int m0 = mt * 64, c0 = es * 64;
   const int tid = threadIdx.x;
-  // x rows of the tile (action rows); copy of the noise into x0
-  for (int i = tid; i < 64 * 32; i += 256) {
-    const int lr = i >> 5, a = i & 31, r = m0 + lr;
-    float xv = 0.f;
-    if (r < e.M && a < e.A) {
-      const int b = r / e.S, s = r % e.S;
-      if (!(e.has_state && s == 0)) {
-        const long ar = (long)b * e.C + (s - e.has_state);
-        xv = e.noise[ar * e.A + a];
-        if (es == 0) e.x0[ar * e.A + a] = xv;
-      }
+  // noise rows of the tile (action rows); copy of the noise into x0
+  float xv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const int rc = min(r, e.M - 1), b = rc / e.S, s = rc % e.S;
+    const int ar = b * e.C + max(s - e.has_state, 0);
+    xv[i] = e.noise[(long)ar * e.A + min(a, e.A - 1)];
+  }
+  // state rows: hs = state W_s^T + b_s for this workgroup's 64 columns
+  {
+    const int col = c0 + (tid & 63);
+    for (int lr = tid >> 6; lr < 64; lr += 8) {
+      const int r = m0 + lr;
+      if (r >= e.M || !e.has_state || (r % e.S) != 0) continue;
+      const int b = r / e.S;
+      float acc = 0.f;
+      for (int k = 0; k < e.SD; ++k)
+        acc += ld_act<ACT>(e.state, (long)b * e.SD + k) * ld_w(e.w_state, WE, (long)col * e.SD + k);
+      e.hs[(long)b * e.d + col] = acc + ld_w(e.b_state, WE, col);
     }
-    s_x[lr][a] = xv;
   }
-  // state rows of this tile: hs = state W_s^T + b_s for this workgroup's columns
-  for (int i = tid; i < 64 * cw; i += 256) {
-    const int lr = i / cw, col = c0 + i % cw, r = m0 + lr;
-    if (r >= e.M || !e.has_state || (r % e.S) != 0) continue;
-    const int b = r / e.S;
-    float acc = 0.f;
-    for (int k = 0; k < e.SD; ++k) acc += ld_act<ACT>(e.state, (long)b * e.SD + k) * ld_w(e.w_state, WE, (long)col * e.SD + k);
-    e.hs[(long)b * e.d + col] = acc + ld_w(e.b_state, WE, col);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const bool act_row = r < e.M && a < e.A && !(e.has_state && (r % e.S) == 0);
+    s_x[lr][a] = act_row ? xv[i] : 0.f;
+    if (act_row && es == 0) {
+      const int b = r / e.S, s = r % e.S;
+      e.x0[(long)(b * e.C + s - e.has_state) * e.A + a] = xv[i];
+    }
   }
-  __syncthreads();
-  for (int cc = 0; cc < cw; cc += 64)
-    embed_tile<ACT, WE>(m0, c0 + cc, e.M, e.S, e.has_state, e.A, e.d, s_x, e.hs, e.w_in, e.b_in, e.temb, 0, e.h,
-                        e.u, e.g1, e.ssq_out);
+  __syncthreads();  // s_x and hs of this tile complete
+  EmbedCol<WE> ec;
+  ec.load(c0, e.A, e.w_in, e.b_in, e.temb, e.g1, 0, e.hs, m0, e.M, e.S, e.d);
+  ec.template emit<ACT>(c0, m0, e.M, e.S, e.has_state, e.A, e.d, s_x, e.h, e.u, e.ssq_out);
 }
 
-// final norm + action head + Euler update, then the next step's embedding
-template <int ACT, int WT>
-__global__ __launch_bounds__(256) void k_out(OutArgs o) {
+// Step tail: final norm + action head + Euler update, then the next step's
+// embedding.  Workgroup (m-tile, 64-column slice): every slice recomputes the
+// 64 x A head tile (K = d) and embeds its own columns.
+template <int ACT, int WE, int NB>
+__global__ __launch_bounds__(512) void k_out(OutArgs o) {
+  constexpr int UPW = 4;
   __shared__ float red[4][64][33];
   __shared__ float s_rstd[64];
   __shared__ float s_x[64][33];
   const int mt = blockIdx.x / o.esplit, es = blockIdx.x % o.esplit;
-  const int m0 = mt * 64;
+  const int m0 = mt * 64, c0 = es * 64;
   const int tid = threadIdx.x;
-  tile_rstd(o.ssq, o.P, o.M, m0, o.inv_d, o.eps, s_rstd);
-  if (o.A == 32)
-    gemm_core<ACT, WT, 2>(o.uf, o.M, m0, o.Wout, o.d, 0, 0, o.d >> 5, red);
-  else
-    gemm_core<ACT, WT, 1>(o.uf, o.M, m0, o.Wout, o.d, 0, 0, o.d >> 5, red);
-  for (int i = tid; i < 64 * 32; i += 256) {
-    const int lr = i >> 5, a = i & 31, r = m0 + lr;
+  const int units = o.d >> 5;
+  // every operand first: head weights, u_f, h^2 partials, x, b_out, the embedding's operands
+  float4 q[4];
+  rstd_load(o.ssq, o.M, m0, q);
+  float xin[4], bo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = min(m0 + lr, o.M - 1);
+    const int b = r / o.S, s = r % o.S;
+    const int ar = b * o.C + max(s - o.has_state, 0);
+    xin[i] = o.x_in[(long)ar * o.A + min(a, o.A - 1)];
+    bo[i] = o.bout.base[(long)(o.embed_step - 1) * o.bout.step_stride + min(a, o.A - 1)];
+  }
+  EmbedCol<WE> ec;
+  if (o.do_embed) ec.load(c0, o.A, o.w_in, o.b_in, o.temb, o.g1, o.embed_step, o.hs, m0, o.M, o.S, o.d);
+  SkinnyTile<ACT, WE, NB, UPW, 1> t;
+  t.zero();
+  t.set_range(blockIdx.x);
+  t.load_w_all(o.Wout, NB, 0, units);
+  t.load_a_pass(o.uf, o.d, mt, units, 0);
+  t.mma_pass(units, 0);
+  rstd_finish(q, o.M, m0, o.inv_d, o.eps, s_rstd);
+  reduce_waves<NB>(t.acc, red);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const bool act_row = r < o.M && a < o.A && !(o.has_state && (r % o.S) == 0);
     float xv = 0.f;
-    if (r < o.M && a < o.A) {
-      const int b = r / o.S, s = r % o.S;
-      if (!(o.has_state && s == 0)) {
-        const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
-        const float vel = acc * s_rstd[lr] + tab(o.bout, o.embed_step - 1, a);
-        const long ar = (long)b * o.C + (s - o.has_state);
-        xv = o.x_in[ar * o.A + a] + o.dt * vel;
-        if (es == 0) o.x_out[ar * o.A + a] = xv;
+    if (act_row) {
+      const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
+      xv = xin[i] + o.dt * (acc * s_rstd[lr] + bo[i]);
+      if (es == 0) {
+        const int b = r / o.S, s = r % o.S;
+        o.x_out[(long)(b * o.C + s - o.has_state) * o.A + a] = xv;
       }
     }
     s_x[lr][a] = xv;
   }
   if (!o.do_embed) return;
   __syncthreads();
-  const int cw = o.d / o.esplit, c0 = es * cw;
-  for (int cc = 0; cc < cw; cc += 64)
-    embed_tile<ACT, WT == ELT_F32 ? ELT_F32 : ELT_BF16>(m0, c0 + cc, o.M, o.S, o.has_state, o.A, o.d, s_x, o.hs,
-                                                      o.w_in, o.b_in, o.temb, o.embed_step, o.h, o.u, o.g1,
-                                                      o.ssq_out);
+  ec.template emit<ACT>(c0, m0, o.M, o.S, o.has_state, o.A, o.d, s_x, o.h, o.u, o.ssq_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,18 +938,18 @@ __global__ void k_pack(const void* src, int src_elt, int rows, int cols, RowMap 
     const int r = (int)(i / cols), k = (int)(i % cols);
     const int nd = (r / rm.blk) * rm.stride + rm.off + r % rm.blk;
     const int nb = nd >> 4, ln = nd & 15;
+    const int NBT = Ntot >> 4;
     if (dst_elt == ELT_FP8) {
       const int kq = k >> 6, kk = k & 63, half = kk >> 5, lane = ln + 16 * ((kk & 31) >> 3);
-      const long off = (((long)nb * (cols >> 6) + kq) * 64 + lane) * 16 + half * 8 + (k & 7);
+      const long off = (((long)kq * NBT + nb) * 64 + lane) * 16 + half * 8 + (k & 7);
       ((uint8_t*)dst)[off] = ((const uint8_t*)src)[i];
     } else {
       const int kb = k >> 5, lane = ln + 16 * ((k & 31) >> 3);
-      const long off = (((long)nb * (cols >> 5) + kb) * 64 + lane) * 8 + (k & 7);
+      const long off = (((long)kb * NBT + nb) * 64 + lane) * 8 + (k & 7);
       if (dst_elt == ELT_F32) ((float*)dst)[off] = ((const float*)src)[i];
       else ((uint16_t*)dst)[off] = ((const uint16_t*)src)[i];
     }
   }
-  (void)Ntot;
 }
 
 __global__ void k_scatter_scales(const float* s, int rows, RowMap rm, float* dst) {
@@ -877,16 +1045,35 @@ __global__ void k_kv_copy(const uint8_t* k, const uint8_t* v, uint8_t* kd, uint8
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, __VA_ARGS__); \
     return hipGetLastError();                                         \
   } while (0)
+#define FM_LAUNCH_N(kern, grid, nthreads, ...)                              \
+  do {                                                                      \
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(nthreads), 0, st, __VA_ARGS__); \
+    return hipGetLastError();                                               \
+  } while (0)
+
+template <int ACT, int WT, int EPI, int NB>
+static hipError_t gemm_upw(const GemmArgs& g, int grid, hipStream_t st) {
+  constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
+  const int units = (g.K >> 5) / KU;
+  const int per_wave = (units + GW - 1) / GW;
+  if (per_wave <= 1) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 1, 1>), grid, 512, g);
+  if (per_wave <= 2) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 2, 1>), grid, 512, g);
+  if (per_wave <= 4) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 4, 1>), grid, 512, g);
+  if (NB == 1 && per_wave <= 8) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, 1, 8, 1>), grid, 512, g);
+  if (per_wave <= 8) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 4, 2>), grid, 512, g);
+  if (NB == 1 && per_wave <= 16) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, 1, 8, 2>), grid, 512, g);
+  if (per_wave <= 16) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 4, 4>), grid, 512, g);
+  return hipErrorInvalidValue;
+}
 
 template <int ACT, int WT>
 static hipError_t gemm_dispatch(int epi, const GemmArgs& g, hipStream_t st) {
   const int nt = epi == EPI_GELU ? 32 : 16;
-  if (g.nt != nt) return hipErrorInvalidValue;
-  const int grid = g.mtiles * (g.N / nt) * g.ksplit;
-  if (epi == EPI_QKV) FM_LAUNCH((k_gemm<ACT, WT, EPI_QKV, 1>), grid, g);
-  if (epi == EPI_RESID) FM_LAUNCH((k_gemm<ACT, WT, EPI_RESID, 1>), grid, g);
-  if (g.ksplit != 1) return hipErrorInvalidValue;
-  FM_LAUNCH((k_gemm<ACT, WT, EPI_GELU, 2>), grid, g);
+  if (g.nt != nt || g.ksplit != 1) return hipErrorInvalidValue;
+  const int grid = g.mtiles * (g.N / nt);
+  if (epi == EPI_QKV) return gemm_upw<ACT, WT, EPI_QKV, 1>(g, grid, st);
+  if (epi == EPI_RESID) return gemm_upw<ACT, WT, EPI_RESID, 1>(g, grid, st);
+  return gemm_upw<ACT, WT, EPI_GELU, 2>(g, grid, st);
 }
 
 hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t st) {
@@ -896,29 +1083,43 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+template <int DH>
+static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
+  const int groups = a.B * a.Hkv * a.nqblk;
+  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(groups * a.nsplit), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine<DH>, dim3(groups * 8), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st) {
-  if (act == ELT_F32) FM_LAUNCH(k_attn_f32, a.B * a.Hq, a);
-  const int grid = a.B * a.Hkv * a.nqblk * a.nsplit;
-  switch (a.Dh) {
-    case 32: FM_LAUNCH(k_attn_bf16<32>, grid, a);
-    case 64: FM_LAUNCH(k_attn_bf16<64>, grid, a);
-    case 128: FM_LAUNCH(k_attn_bf16<128>, grid, a);
-    case 256: FM_LAUNCH(k_attn_bf16<256>, grid, a);
+  switch (act == ELT_F32 ? 0 : a.Dh) {
+    case 32: return attn_bf16<32>(a, st);
+    case 64: return attn_bf16<64>(a, st);
+    case 128: return attn_bf16<128>(a, st);
+    case 256: return attn_bf16<256>(a, st);
   }
+  if (act == ELT_F32) FM_LAUNCH(k_attn_f32, a.B * a.Hq, a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st) {
   const int grid = o.mtiles * o.esplit;
-  if (act == ELT_F32) FM_LAUNCH((k_out<ELT_F32, ELT_F32>), grid, o);
+  if ((o.d >> 5) > GW * 4) return hipErrorInvalidValue;
   (void)wt_out;
-  FM_LAUNCH((k_out<ELT_BF16, ELT_BF16>), grid, o);
+  if (act == ELT_F32) {
+    if (o.A == 32) FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 2>), grid, 512, o);
+    FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 1>), grid, 512, o);
+  }
+  if (o.A == 32) FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 2>), grid, 512, o);
+  FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 1>), grid, 512, o);
 }
 
 hipError_t launch_embed(int act, const EmbedArgs& e, hipStream_t st) {
   const int grid = e.mtiles * e.esplit;
-  if (act == ELT_F32) FM_LAUNCH((k_embed<ELT_F32, ELT_F32>), grid, e);
-  FM_LAUNCH((k_embed<ELT_BF16, ELT_BF16>), grid, e);
+  if (act == ELT_F32) FM_LAUNCH_N((k_embed<ELT_F32, ELT_F32>), grid, 512, e);
+  FM_LAUNCH_N((k_embed<ELT_BF16, ELT_BF16>), grid, 512, e);
 }
 
 hipError_t launch_pack(const void* src, int src_elt, int rows, int cols, RowMap rm, void* dst, int dst_elt, int Ntot,

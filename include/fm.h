@@ -208,6 +208,27 @@ void fm_destroy(fm_ctx* ctx);
  */
 const char* fm_last_error(const fm_ctx* ctx);
 
+/* Phases of one Euler step, for fm_launch_phase. */
+typedef enum {
+  FM_PHASE_QKV = 0,      /* norm1 folded into the QKV GEMM                     */
+  FM_PHASE_ATTN = 1,     /* attention over [cached prefix | suffix]            */
+  FM_PHASE_OPROJ = 2,    /* O GEMM + residual (+ next norm's input)            */
+  FM_PHASE_GATEUP = 3,   /* norm2 folded into the gate/up GEMM + GELU gate     */
+  FM_PHASE_DOWN = 4,     /* down GEMM + residual (+ next norm's input)         */
+  FM_PHASE_TAIL = 5      /* final norm, action head, Euler, next embedding     */
+} fm_phase;
+
+/*
+ * Profiling aid: enqueue the single kernel of phase `phase` of Euler step
+ * `step` and layer `layer` (ignored for FM_PHASE_TAIL) with exactly the
+ * arguments fm_denoise uses, on the context's stream.  It reads and writes
+ * the context's activation buffers, so results of a later fm_denoise are
+ * unaffected (fm_denoise rewrites them from its inputs).  Lets a caller time
+ * one kernel with events on the stream.  FM_ERR_ARG for an out-of-range
+ * step, layer or phase.
+ */
+fm_status fm_launch_phase(fm_ctx* ctx, int32_t step, int32_t layer, int32_t phase);
+
 /*
  * The per-output-row E4M3 quantiser fm_create applies to an fp8 model's
  * per-layer matrices, exposed for checking.  w: [rows][cols] bf16 (device);
