@@ -59,6 +59,7 @@ struct fm_ctx {
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
   int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
   int ks_o, ks_d, nqblk, nsplit, kps;
+  int NS8, TP, S8;  // padded static region, padded physical prefix capacity, padded suffix
 
   // arena
   void* arena = nullptr;
@@ -67,7 +68,7 @@ struct fm_ctx {
   void *wout, *w_in, *b_in, *w_state, *b_state;
   float *temb, *g1, *g2, *gf, *a1, *a2, *bqkv, *bgu, *bout, *ones, *zeros;
   long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
-  void *kpre, *vpre;
+  void *kpre, *vtpre, *vts;
   int* meta;
   float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
@@ -186,6 +187,9 @@ void derive(fm_ctx* x) {
   x->F = c.d_mlp; x->N = c.n_steps; x->HD = x->Hkv * x->Dh;
   x->Nqkv = (x->Hq + 2 * x->Hkv) * x->Dh;
   x->Tcap = c.prefix_static + c.n_frames * c.frame_tokens;
+  x->NS8 = (c.prefix_static + 7) / 8 * 8;
+  x->TP = x->NS8 + c.n_frames * c.frame_tokens;
+  x->S8 = (x->C + (c.state_dim > 0) + 7) / 8 * 8;
   x->P = 128;  // h^2 partial slots per row (one per 16 columns; unused slots stay zero)
   x->mtiles = (x->M + 63) / 64;
   x->esplit = x->d / 64;
@@ -193,12 +197,12 @@ void derive(fm_ctx* x) {
   (void)unit;
   x->ks_o = 1;
   x->ks_d = 1;
-  x->nqblk = (x->S * (x->Hq / x->Hkv) + 63) / 64;
+  x->nqblk = (x->S * (x->Hq / x->Hkv) + 15) / 16;
   {
     // key ranges: about 64 workgroups or more, each range >= 64 keys
-    const int keys = x->Tcap + x->S;
+    const int keys = x->TP + x->S8;
     const int groups = x->B * x->Hkv * x->nqblk;
-    int ns = std::min(std::min((keys + 63) / 64, (64 + groups - 1) / groups), 8);
+    int ns = std::min(std::min((keys + 63) / 64, (64 + groups - 1) / groups), 16);
     x->nsplit = std::max(1, ns);
     x->kps = ((keys + x->nsplit - 1) / x->nsplit + 31) / 32 * 32;
     x->nsplit = (keys + x->kps - 1) / x->kps;
@@ -245,9 +249,10 @@ void carve(fm_ctx* x, Arena& a) {
   x->st_bqkv = L * x->Nqkv;
   x->st_bgu = L * 2 * x->F;
   x->st_bout = ada ? x->A : 0;
-  const size_t kv = (size_t)x->B * L * x->Tcap * x->HD * ea;
+  const size_t kv = (size_t)x->B * L * x->TP * x->HD * ea;
   x->kpre = a.take(kv > 0 ? kv : 16);
-  x->vpre = a.take(kv > 0 ? kv : 16);
+  x->vtpre = a.take(kv > 0 ? kv : 16);
+  x->vts = a.take((size_t)x->B * x->HD * x->S8 * ea);
   x->meta = (int*)a.take(x->B * 2 * sizeof(int));
   const long Mp = (long)x->mtiles * 64;
   x->h = (float*)a.take(Mp * d * 4);
@@ -277,7 +282,7 @@ Tab T(const float* base, long stride) { return Tab{base, stride}; }
 fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
   const float eps = x->cfg.rms_eps, inv_d = 1.f / (float)x->d;
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
-  const long Tl = (long)x->Tcap * x->HD;  // elements per (robot, layer) of prefix K
+  const long Tl = (long)x->TP * x->HD;  // elements per (robot, layer) of prefix K (and of V^T)
   const LayerW& w = x->lw[l];
   GemmArgs g{};
   g.M = x->M; g.mtiles = x->mtiles; g.ssq = x->ssq; g.P = x->P; g.inv_d = inv_d; g.eps = eps; g.step = k;
@@ -287,17 +292,21 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
     g.A = x->u; g.W = w.wqkv; g.wscale = w.sqkv; g.N = x->Nqkv; g.K = x->d; g.nt = 16; g.ksplit = 1;
     g.out = x->qkv;
     g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(x->zeros, 0);
+    g.vts = x->vts; g.S = x->S; g.S8 = x->S8; g.Hq = x->Hq; g.Hkv = x->Hkv; g.Dh = x->Dh;
     HIPCHK(x, launch_gemm(x->act, x->wt, EPI_QKV, g, st), "qkv gemm");
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     AttnArgs at{};
     at.qkv = x->qkv;
     at.kpre = (const char*)x->kpre + (size_t)l * Tl * elt_size(x->act);
-    at.vpre = (const char*)x->vpre + (size_t)l * Tl * elt_size(x->act);
+    at.vtpre = (const char*)x->vtpre + (size_t)l * Tl * elt_size(x->act);
+    at.vts = x->vts;
     at.b_stride = (long)x->L * Tl;
     at.meta = x->meta;
-    at.B = x->B; at.S = x->S; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
-    at.n_static = x->cfg.prefix_static; at.frame_tokens = std::max(1, x->cfg.frame_tokens);
+    at.B = x->B; at.S = x->S; at.S8 = x->S8; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
+    at.n_static = x->cfg.prefix_static; at.NS8 = x->NS8; at.TP = x->TP;
+    at.frame_tokens = std::max(1, x->cfg.frame_tokens);
     at.n_frames = std::max(1, x->cfg.n_frames);
+    at.ring = x->cfg.n_frames > 0;
     at.nqblk = x->nqblk; at.nsplit = x->nsplit; at.keys_per_split = x->kps;
     at.scale = 1.f / sqrtf((float)x->Dh);
     at.part = x->attn_part; at.counters = x->counters;
@@ -604,13 +613,14 @@ fm_status fm_set_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* 
                 ring ? x->Tcap : x->cfg.prefix_static);
   if (n_tokens > 0 && (!k || !v)) return fail(x, FM_ERR_ARG, "k or v is NULL");
   if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k and v must be 16-byte aligned");
-  const long row = (long)n_tokens * x->HD;
-  const long Tl = (long)x->Tcap * x->HD;
   const size_t ea = elt_size(x->act);
-  char* kd = (char*)x->kpre + (size_t)robot * x->L * Tl * ea;
-  char* vd = (char*)x->vpre + (size_t)robot * x->L * Tl * ea;
-  HIPCHK(x, launch_kv_copy(k, v, kd, vd, x->act, x->L, row, row, Tl, x->meta, robot, n_tokens, 0, x->stream),
-         "prefix copy");
+  const size_t rb = (size_t)robot * x->L * x->TP * x->HD * ea;
+  KvCopy c{};
+  c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vtd = (char*)x->vtpre + rb;
+  c.elt = x->act; c.layers = x->L; c.n = n_tokens; c.HD = x->HD; c.TP = x->TP;
+  c.phys0 = 0; c.split_t = ring ? x->cfg.prefix_static : n_tokens; c.phys1 = x->NS8;
+  c.meta = x->meta; c.robot = robot; c.valid = n_tokens; c.head = 0;
+  HIPCHK(x, launch_kv_copy(c, x->stream), "prefix copy");
   x->valid[robot] = n_tokens;
   x->head[robot] = 0;
   x->is_set[robot] = 1;
@@ -627,13 +637,14 @@ fm_status fm_append_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const voi
   if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k_frame and v_frame must be 16-byte aligned");
   const int slot = x->head[robot];
   const int nh = (slot + 1) % x->cfg.n_frames;
-  const long row = (long)x->cfg.frame_tokens * x->HD;
-  const long Tl = (long)x->Tcap * x->HD;
   const size_t ea = elt_size(x->act);
-  const size_t off = ((size_t)robot * x->L * Tl + (size_t)(x->cfg.prefix_static + slot * x->cfg.frame_tokens) * x->HD) * ea;
-  HIPCHK(x, launch_kv_copy(k, v, (char*)x->kpre + off, (char*)x->vpre + off, x->act, x->L, row, row, Tl, x->meta,
-                           robot, x->valid[robot], nh, x->stream),
-         "frame append");
+  const size_t rb = (size_t)robot * x->L * x->TP * x->HD * ea;
+  KvCopy c{};
+  c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vtd = (char*)x->vtpre + rb;
+  c.elt = x->act; c.layers = x->L; c.n = x->cfg.frame_tokens; c.HD = x->HD; c.TP = x->TP;
+  c.phys0 = x->NS8 + slot * x->cfg.frame_tokens; c.split_t = c.n; c.phys1 = 0;
+  c.meta = x->meta; c.robot = robot; c.valid = x->valid[robot]; c.head = nh;
+  HIPCHK(x, launch_kv_copy(c, x->stream), "frame append");
   x->head[robot] = nh;
   return FM_OK;
 }

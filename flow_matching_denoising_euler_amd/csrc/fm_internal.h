@@ -38,7 +38,9 @@ struct GemmArgs {
   float inv_d, eps;
   // epilogue operands
   void* out;              // QKV: [M][N] act ; GELU: [M][N/2] act
-  Tab bias;               // QKV / GELU: per packed column (Ada beta W), or base null
+  Tab bias;               // QKV / GELU: per packed column (Ada beta W)
+  void* vts;              // QKV: suffix V^T [B][Hkv][Dh][S8] (also written)
+  int S, S8, Hq, Hkv, Dh; // QKV: shapes for vts
   float* h;               // RESID: [M][N] fp32 residual stream (in/out)
   Tab alpha;              // RESID: per column (Ada alpha) or null
   Tab gnext;              // RESID: gain of the next norm per column
@@ -47,16 +49,24 @@ struct GemmArgs {
   int step;
 };
 
+// Prefix K/V storage per (robot, layer): K rows [TP][Hkv][Dh] and V
+// transposed [Hkv][Dh][TP], at physical positions of a padded layout: the
+// static region padded to NS8 (a multiple of 8), then n_frames slots of
+// frame_tokens.  The suffix V of the current step is kept transposed too,
+// vts [B][Hkv][Dh][S8].  Attention enumerates keys in a padded logical
+// order (prefix span, then the suffix padded to S8) in which every group of
+// 8 keys is contiguous in storage.
 struct AttnArgs {
-  const void* qkv;        // [B*S][Nqkv] act
-  const void* kpre;       // layer-l base of K: [B] blocks of stride b_stride elements, [Tcap][Hkv][Dh]
-  const void* vpre;
-  long b_stride;          // elements between robots in kpre / vpre
+  const void* qkv;        // [B*S][Nqkv] act (Q and suffix K)
+  const void* kpre;       // layer-l base of prefix K; robots b_stride elements apart
+  const void* vtpre;      // layer-l base of prefix V^T; robots b_stride elements apart
+  const void* vts;        // suffix V^T [B][Hkv][Dh][S8]
+  long b_stride;          // elements between robots in kpre / vtpre
   const int* meta;        // [B][2] = (valid prefix tokens, ring head)
-  int B, S, Hq, Hkv, Dh, Nqkv;
-  int n_static, frame_tokens, n_frames;
+  int B, S, S8, Hq, Hkv, Dh, Nqkv;
+  int n_static, NS8, TP, frame_tokens, n_frames, ring;
   int nqblk, nsplit;      // query blocks of 64 per (b, kv head); key ranges
-  int keys_per_split;     // logical keys per range (multiple of 32)
+  int keys_per_split;     // padded logical keys per range (multiple of 32)
   float scale;
   float* part;            // partials
   unsigned* counters;
@@ -130,9 +140,19 @@ hipError_t launch_ada_mod(const float* c, int n_steps, int d, const void* w_n, c
 hipError_t launch_bias_gemv(const void* w, int w_elt, const float* scales, int rows, int cols,
                             const float* beta, long beta_step_stride, int n_steps, RowMap rm,
                             float* out, long out_step_stride, hipStream_t st);
-// prefix K/V copy + meta update
-hipError_t launch_kv_copy(const void* k, const void* v, void* kd, void* vd, int elt, int layers,
-                          long row_elems, long src_pitch, long dst_pitch, int* meta, int robot,
-                          int valid, int head, hipStream_t st);
+// prefix K/V copy into the padded physical layout + meta update: tokens
+// [0, n) of src (per layer [n][Hkv*Dh]) go to physical rows phys0 + t, except
+// that tokens t >= split_t go to phys1 + (t - split_t) (static vs frames).
+struct KvCopy {
+  const void* k;
+  const void* v;
+  void* kd;               // robot base of K: layer pitch TP*HD
+  void* vtd;              // robot base of V^T: layer pitch HD*TP
+  int elt, layers, n, HD, TP;
+  int phys0, split_t, phys1;
+  int* meta;
+  int robot, valid, head;
+};
+hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st);
 
 }  // namespace fm

@@ -30,6 +30,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace fm {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -409,11 +411,19 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
   }
 
   if constexpr (EPI == EPI_QKV) {
+    const int vcol0 = (g.Hq + g.Hkv) * g.Dh;  // suffix V columns are also stored transposed
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = tid + NT * i, row = idx / nt, c = idx % nt;
-      const int r = m0 + row;
-      if (r < g.M) st_act<ACT>(g.out, (long)r * g.N + n0 + c, v[i] * s_col[2][c] * s_rstd[row] + s_col[0][c]);
+      const int r = m0 + row, col = n0 + c;
+      const float val = v[i] * s_col[2][c] * s_rstd[row] + s_col[0][c];
+      if (r < g.M) {
+        st_act<ACT>(g.out, (long)r * g.N + col, val);
+        if (col >= vcol0) {
+          const int jv = (col - vcol0) / g.Dh, dh = (col - vcol0) % g.Dh, b = r / g.S, sr = r % g.S;
+          st_act<ACT>(g.vts, ((long)(b * g.Hkv + jv) * g.Dh + dh) * g.S8 + sr, val);
+        }
+      }
     }
   } else if constexpr (EPI == EPI_GELU) {
     // tile = [16 gate | 16 up] (NB == 2): pair them through red[0]
@@ -457,75 +467,98 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Attention of the suffix queries over [prefix (logical order) | suffix]
 // ---------------------------------------------------------------------------
-// K or V row of logical key `key` (robot b, kv head j), branch-free: prefix
-// keys go through the static region and the frame ring (logical frame f of
-// the window lives in slot (head + f) mod n_frames), suffix keys come from
-// this step's QKV output.
-template <typename T>
-__device__ __forceinline__ const T* kv_ptr(const AttnArgs& a, const void* pre, int b, int j, int key, int tv,
-                                           int head, int which) {
-  const int rel = max(key - a.n_static, 0);
+// Padded logical keys (see AttnArgs): physical prefix position of prefix
+// position p, branch-free (logical frame f of the window lives in slot
+// (head + f) mod n_frames).
+__device__ __forceinline__ int pre_phys(const AttnArgs& a, int p, int head) {
+  const int rel = max(p - a.NS8, 0);
   const int f = rel / a.frame_tokens, off = rel - f * a.frame_tokens;
   int slot = head + f;
   slot -= (slot >= a.n_frames) ? a.n_frames : 0;
-  const int phys = key < a.n_static ? key : a.n_static + slot * a.frame_tokens + off;
-  const T* pp = (const T*)pre + b * a.b_stride + ((long)phys * a.Hkv + j) * a.Dh;
-  const int s = max(key - tv, 0);
-  const T* sp = (const T*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)(a.Hq + which * a.Hkv + j) * a.Dh;
-  return key < tv ? pp : sp;
+  return p < a.NS8 ? p : a.NS8 + slot * a.frame_tokens + off;
 }
+struct KeySpace {
+  int pspan, kp, tv, head;
+  // The suffix starts at the fixed position TP (the padded prefix capacity),
+  // so key addresses depend on the stored prefix only through the ring head
+  // (ring configurations); the valid length only masks scores.
+  __device__ __forceinline__ KeySpace(const AttnArgs& a, int b) {
+    tv = a.meta[2 * b];
+    head = a.ring ? a.meta[2 * b + 1] : 0;
+    pspan = a.TP;
+    kp = pspan + a.S8;
+  }
+  __device__ __forceinline__ bool valid(const AttnArgs& a, int p) const {
+    const bool pre_ok = a.ring ? (p >= a.NS8 || p < a.n_static) : (p < tv);
+    return p < pspan ? pre_ok : (p - pspan < a.S);
+  }
+  template <typename T>
+  __device__ __forceinline__ const T* krow(const AttnArgs& a, int b, int j, int p) const {
+    const T* pp = (const T*)a.kpre + b * a.b_stride + ((long)pre_phys(a, p, head) * a.Hkv + j) * a.Dh;
+    const int s = min(max(p - pspan, 0), a.S - 1);
+    const T* sp = (const T*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)(a.Hq + j) * a.Dh;
+    return p < pspan ? pp : sp;
+  }
+  // V^T of keys p8 .. p8+7 (p8 a multiple of 8) for head dim dh: contiguous
+  template <typename T>
+  __device__ __forceinline__ const T* vcol(const AttnArgs& a, int b, int j, int p8, int dh) const {
+    const T* pp = (const T*)a.vtpre + b * a.b_stride + ((long)j * a.Dh + dh) * a.TP + pre_phys(a, p8, head);
+    const T* sp = (const T*)a.vts + ((long)(b * a.Hkv + j) * a.Dh + dh) * a.S8 + max(p8 - pspan, 0);
+    return p8 < pspan ? pp : sp;
+  }
+};
 
-// bf16 MFMA attention, flash style.  Workgroup = 64 queries (4 waves x 16
-// rows; a query is one suffix row of one head of the KV group) against one
-// contiguous range of logical keys, walked in tiles of 32 keys.  K and V^T
-// of a tile are staged in LDS and shared by the 4 waves; two tiles are in
-// flight in registers ahead of the one in use.  Online softmax per row.
-// Several key ranges are merged by k_attn_combine in range order.
+// bf16 MFMA attention, flash style.  Workgroup = 16 queries (one suffix row
+// and one head of the KV group each); its 4 waves split the padded logical
+// keys in 32-key tiles (wave w takes tiles w, w+4, ...), each with its own
+// online softmax, and merge through LDS in a fixed order.  Every wave loads
+// its K fragments (K rows) and V fragments (8 keys of V^T per lane) straight
+// from memory: the next tile's K while the current tile's softmax runs, its
+// V after the current PV product.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   constexpr int KBD = DH / 32, NBD = DH / 16, KT = 32;
-  constexpr int CH = KT * DH / 8;  // 16-byte chunks per K (or V) tile
-  constexpr int CPT = (CH + 255) / 256;
-  __shared__ __align__(16) uint16_t sK[KT][DH + 8];
-  __shared__ __align__(16) uint16_t sVt[DH][KT + 8];
   __shared__ __align__(16) uint16_t sP[4][16][KT + 8];
+  __shared__ float s_o[16][DH + 4];
+  __shared__ float s_m[4][16], s_l[4][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int item = blockIdx.x;
-  const int sp = item % a.nsplit;
-  item /= a.nsplit;
-  const int qb = item % a.nqblk;
-  item /= a.nqblk;
-  const int j = item % a.Hkv, b = item / a.Hkv;
+  const int qb = blockIdx.x % a.nqblk, jb = blockIdx.x / a.nqblk;
+  const int j = jb % a.Hkv, b = jb / a.Hkv;
   const int G = a.Hq / a.Hkv, nq = a.S * G;
-  const int tv = a.meta[2 * b], head = a.meta[2 * b + 1];
-  const int nkeys = tv + a.S;
-  const int kbeg = sp * a.keys_per_split, kend = min(nkeys, kbeg + a.keys_per_split);
-  const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
 
-  // tile loader: chunk c -> key c / (DH/8), dims (c % (DH/8)) * 8 .. +8
-  uint4 kr[2][CPT], vr[2][CPT];
-  uint32_t km[2][CPT];  // zero mask of keys past the range, applied when the tile reaches LDS
-  auto load_tile = [&](int t, int slot) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = min(tid + 256 * i, CH - 1);
-      const int key = kbeg + t * KT + c / (DH / 8), d0 = (c % (DH / 8)) * 8;
-      const int kc = min(key, kend - 1);
-      km[slot][i] = mask_if(key < kend);
-      kr[slot][i] = *(const uint4*)(kv_ptr<uint16_t>(a, a.kpre, b, j, kc, tv, head, 0) + d0);
-      vr[slot][i] = *(const uint4*)(kv_ptr<uint16_t>(a, a.vpre, b, j, kc, tv, head, 1) + d0);
-    }
-  };
-  if (ntile > 0) load_tile(0, 0);
-  if (ntile > 1) load_tile(1, 1);
-  // this wave's 16 queries as A fragments
+  // the 16 queries as A fragments (independent of the prefix state)
   uint4 qf[KBD];
   {
-    const int qi = min(qb * 64 + wave * 16 + (lane & 15), nq - 1);
+    const int qi = min(qb * 16 + (lane & 15), nq - 1);
     const int s = qi / G, h = j * G + qi % G;
     const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb) qf[kb] = *(const uint4*)(qp + kb * 32);
+  }
+  const KeySpace ks(a, b);
+  const int ntile_all = (ks.kp + KT - 1) / KT;
+  const int ntile = ntile_all > wave ? (ntile_all - wave + 3) / 4 : 0;  // tiles of this wave
+
+  uint4 kf[2][2][KBD], vf[NBD];
+  auto load_k = [&](int t, int slot) {
+    const int base = (wave + 4 * t) * KT;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int p = min(base + nb * 16 + (lane & 15), ks.kp - 1);
+      const uint16_t* kp = ks.krow<uint16_t>(a, b, j, p) + (lane >> 4) * 8;
+#pragma unroll
+      for (int kb = 0; kb < KBD; ++kb) kf[slot][nb][kb] = *(const uint4*)(kp + kb * 32);
+    }
+  };
+  auto load_v = [&](int t) {
+    const int p8 = min((wave + 4 * t) * KT + (lane >> 4) * 8, ks.kp - 8);
+#pragma unroll
+    for (int nbd = 0; nbd < NBD; ++nbd)
+      vf[nbd] = *(const uint4*)ks.vcol<uint16_t>(a, b, j, p8, nbd * 16 + (lane & 15));
+  };
+  if (ntile > 0) {
+    load_k(0, 0);
+    load_v(0);
   }
   f32x4 oacc[NBD];
 #pragma unroll
@@ -533,42 +566,23 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrow[4] = {0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](int t, int slot) {
-    __syncthreads();  // the previous tile is no longer read
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < CH) {
-        const int key = c / (DH / 8), d0 = (c % (DH / 8)) * 8;
-        *(uint4*)&sK[key][d0] = and4(kr[slot][i], km[slot][i]);
-        const uint4 vm = and4(vr[slot][i], km[slot][i]);
-        const uint32_t vv[4] = {vm.x, vm.y, vm.z, vm.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sVt[d0 + 2 * e][key] = (uint16_t)(vv[e] & 0xFFFF);
-          sVt[d0 + 2 * e + 1][key] = (uint16_t)(vv[e] >> 16);
-        }
-      }
-    }
-    __syncthreads();
-    if (t + 2 < ntile) load_tile(t + 2, slot);
+    const bool more = t + 1 < ntile;
     f32x4 sacc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       sacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KBD; ++kb) {
-        const uint4 kf = *(const uint4*)&sK[nb * 16 + (lane & 15)][kb * 32 + (lane >> 4) * 8];
-        sacc[nb] = mma_bf16(qf[kb], kf, sacc[nb]);
-      }
+      for (int kb = 0; kb < KBD; ++kb) sacc[nb] = mma_bf16(qf[kb], kf[slot][nb][kb], sacc[nb]);
     }
+    if (more) load_k(t + 1, slot ^ 1);
     float p[2][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float m = mrow[r];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int key = kbeg + t * KT + nb * 16 + (lane & 15);
-        p[nb][r] = key < kend ? sacc[nb][r] * a.scale : -INFINITY;
+        const int key = (wave + 4 * t) * KT + nb * 16 + (lane & 15);
+        p[nb][r] = (key < ks.kp && ks.valid(a, key)) ? sacc[nb][r] * a.scale : -INFINITY;
         m = fmaxf(m, p[nb][r]);
       }
       m = fmaxf(m, __shfl_xor(m, 1));
@@ -591,7 +605,6 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 #pragma unroll
       for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd][r] *= corr;
     }
-    // P (bf16) into the A layout through this wave's LDS rows
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -600,116 +613,80 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     const uint4 pf = *(const uint4*)&sP[wave][lane & 15][(lane >> 4) * 8];
 #pragma unroll
-    for (int nbd = 0; nbd < NBD; ++nbd) {
-      const uint4 vf = *(const uint4*)&sVt[nbd * 16 + (lane & 15)][(lane >> 4) * 8];
-      oacc[nbd] = mma_bf16(pf, vf, oacc[nbd]);
-    }
+    for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd] = mma_bf16(pf, vf[nbd], oacc[nbd]);
+    __builtin_amdgcn_wave_barrier();
+    if (more) load_v(t + 1);
   };
   for (int t = 0; t < ntile; t += 2) {
     step(t, 0);
     if (t + 1 < ntile) step(t + 1, 1);
   }
 
-  // normalise by this range's row sums
+  // merge the 4 waves in a fixed order: weights exp(m_w - max m)
+  if ((lane & 15) == 0) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float inv = lrow[r] > 0.f ? 1.f / lrow[r] : 0.f;
-#pragma unroll
-    for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd][r] *= inv;
-  }
-  if (a.nsplit > 1) {
-    // partial block for k_attn_combine: [64 rows][DH] normalised O, then (m, l) per row
-    const long grp = ((long)b * a.Hkv + j) * a.nqblk + qb;
-    const long blk = 64L * (DH + 2);
-    float* part = a.part + (grp * a.nsplit + sp) * blk;
-#pragma unroll
-    for (int nbd = 0; nbd < NBD; ++nbd)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        part[(long)(wave * 16 + (lane >> 4) * 4 + r) * DH + nbd * 16 + (lane & 15)] = oacc[nbd][r];
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wave * 16 + (lane >> 4) * 4 + r;
-        *(float2*)(part + 64L * DH + 2 * row) = make_float2(mrow[r], lrow[r]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      s_m[wave][(lane >> 4) * 4 + r] = mrow[r];
+      s_l[wave][(lane >> 4) * 4 + r] = lrow[r];
     }
-    return;
   }
+  __syncthreads();
+  float sc[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int qi = qb * 64 + wave * 16 + (lane >> 4) * 4 + r;
+    const int row = (lane >> 4) * 4 + r;
+    const float M = fmaxf(fmaxf(s_m[0][row], s_m[1][row]), fmaxf(s_m[2][row], s_m[3][row]));
+    sc[r] = (s_m[wave][row] == -INFINITY) ? 0.f : __expf(s_m[wave][row] - M);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int nbd = 0; nbd < NBD; ++nbd)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* o = &s_o[(lane >> 4) * 4 + r][nbd * 16 + (lane & 15)];
+          *o = (w == 0 ? 0.f : *o) + sc[r] * oacc[nbd][r];
+        }
+    }
+    __syncthreads();
+  }
+  // normalise and store 8 head dims per thread (packed layout)
+  for (int i = tid; i < 16 * DH / 8; i += 256) {
+    const int row = i / (DH / 8), c8 = (i % (DH / 8)) * 8;
+    const int qi = qb * 16 + row;
     if (qi >= nq) continue;
+    const float M = fmaxf(fmaxf(s_m[0][row], s_m[1][row]), fmaxf(s_m[2][row], s_m[3][row]));
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += (s_m[w][row] == -INFINITY) ? 0.f : __expf(s_m[w][row] - M) * s_l[w][row];
+    const float inv = 1.f / L;
+    const float* o = &s_o[row][c8];
+    uint4 r;
+    r.x = f2bf(o[0] * inv) | (f2bf(o[1] * inv) << 16);
+    r.y = f2bf(o[2] * inv) | (f2bf(o[3] * inv) << 16);
+    r.z = f2bf(o[4] * inv) | (f2bf(o[5] * inv) << 16);
+    r.w = f2bf(o[6] * inv) | (f2bf(o[7] * inv) << 16);
     const int s = qi / G, h = j * G + qi % G;
-    const int row = b * a.S + s;
-#pragma unroll
-    for (int nbd = 0; nbd < NBD; ++nbd)
-      ((uint16_t*)a.out)[pk(row, h * DH + nbd * 16 + (lane & 15), a.Hq * DH)] = (uint16_t)f2bf(oacc[nbd][r]);
+    *(uint4*)((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH)) = r;
   }
-}
-
-constexpr int NSPLIT_MAX = 8;
-
-// Combine the key ranges of k_attn_flash in range order: O = sum_s w_s O_s /
-// sum_s w_s with w_s = l_s exp(m_s - max m).  Workgroup = 8 query rows of
-// one block; thread = 8 head dims of one row; all ranges loaded at once.
-template <int DH>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  const int grp = blockIdx.x >> 3, rg = blockIdx.x & 7;
-  const int qb = grp % a.nqblk, j = (grp / a.nqblk) % a.Hkv, b = grp / (a.nqblk * a.Hkv);
-  const int row = rg * 8 + (threadIdx.x >> 5), c8 = (threadIdx.x & 31) * 8;
-  const int G = a.Hq / a.Hkv, nq = a.S * G;
-  const int qi = qb * 64 + row;
-  if (c8 >= DH || qi >= nq) return;
-  const long blk = 64L * (DH + 2);
-  const float* p0 = a.part + (long)grp * a.nsplit * blk;
-  float2 ml[NSPLIT_MAX];
-  float4 o[NSPLIT_MAX][2];
-#pragma unroll
-  for (int s = 0; s < NSPLIT_MAX; ++s) {
-    const int sc = min(s, a.nsplit - 1);
-    ml[s] = *(const float2*)(p0 + sc * blk + 64L * DH + 2 * row);
-    const float4* op = (const float4*)(p0 + sc * blk + (long)row * DH + c8);
-    o[s][0] = op[0];
-    o[s][1] = op[1];
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < NSPLIT_MAX; ++s) M = fmaxf(M, s < a.nsplit ? ml[s].x : -INFINITY);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
-#pragma unroll
-  for (int s = 0; s < NSPLIT_MAX; ++s) {
-    const float w = (s >= a.nsplit || ml[s].x == -INFINITY) ? 0.f : ml[s].y * __expf(ml[s].x - M);
-    wsum += w;
-    acc[0] += w * o[s][0].x; acc[1] += w * o[s][0].y; acc[2] += w * o[s][0].z; acc[3] += w * o[s][0].w;
-    acc[4] += w * o[s][1].x; acc[5] += w * o[s][1].y; acc[6] += w * o[s][1].z; acc[7] += w * o[s][1].w;
-  }
-  const float inv = 1.f / wsum;
-  const int s = qi / G, h = j * G + qi % G;
-  uint4 r;
-  r.x = f2bf(acc[0] * inv) | (f2bf(acc[1] * inv) << 16);
-  r.y = f2bf(acc[2] * inv) | (f2bf(acc[3] * inv) << 16);
-  r.z = f2bf(acc[4] * inv) | (f2bf(acc[5] * inv) << 16);
-  r.w = f2bf(acc[6] * inv) | (f2bf(acc[7] * inv) << 16);
-  *(uint4*)((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH)) = r;
 }
 
 // fp32 attention (small head dims): one workgroup per (robot, query head),
-// one thread per suffix row, online softmax over the logical key order.
+// one thread per suffix row, online softmax over the padded logical keys.
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int G = a.Hq / a.Hkv, j = h / G;
-  const int tv = a.meta[2 * b], head = a.meta[2 * b + 1];
-  const int nkeys = tv + a.S;
+  const KeySpace ks(a, b);
   const int Dh = a.Dh;
   for (int s = threadIdx.x; s < a.S; s += blockDim.x) {
     float q[64], o[64];
     const float* qp = (const float*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * Dh;
     for (int c = 0; c < Dh; ++c) { q[c] = qp[c]; o[c] = 0.f; }
     float m = -INFINITY, l = 0.f;
-    for (int key = 0; key < nkeys; ++key) {
-      const float* kp = kv_ptr<float>(a, a.kpre, b, j, key, tv, head, 0);
-      const float* vp = kv_ptr<float>(a, a.vpre, b, j, key, tv, head, 1);
+    for (int p = 0; p < ks.kp; ++p) {
+      if (!ks.valid(a, p)) continue;
+      const float* kp = ks.krow<float>(a, b, j, p);
+      const int p8 = p & ~7;
       float sc = 0.f;
       for (int c = 0; c < Dh; ++c) sc += q[c] * kp[c];
       sc *= a.scale;
@@ -717,7 +694,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       const float corr = (m == -INFINITY) ? 0.f : expf(m - mn);
       const float pe = expf(sc - mn);
       l = l * corr + pe;
-      for (int c = 0; c < Dh; ++c) o[c] = o[c] * corr + pe * vp[c];
+      for (int c = 0; c < Dh; ++c) o[c] = o[c] * corr + pe * ks.vcol<float>(a, b, j, p8, c)[p - p8];
       m = mn;
     }
     for (int c = 0; c < Dh; ++c) ((float*)a.out)[pk(b * a.S + s, h * Dh + c, a.Hq * Dh)] = o[c] / l;
@@ -1021,19 +998,33 @@ __global__ void k_bias_gemv(const void* w, int w_elt, const float* scales, int r
   out[(long)k * out_stride + nd] += (float)acc;
 }
 
-// prefix K/V rows -> arena (per layer pitch), and the robot's (valid, head)
-__global__ void k_kv_copy(const uint8_t* k, const uint8_t* v, uint8_t* kd, uint8_t* vd, int layers, long row_bytes,
-                          long src_pitch, long dst_pitch, int* meta, int robot, int valid, int head) {
-  const long n16 = row_bytes / 16;
-  const long total = n16 * layers;
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
-    const long l = i / n16, o = (i % n16) * 16;
-    *(uint4*)(kd + l * dst_pitch + o) = *(const uint4*)(k + l * src_pitch + o);
-    *(uint4*)(vd + l * dst_pitch + o) = *(const uint4*)(v + l * src_pitch + o);
+// prefix K rows and V^T columns -> the padded physical layout, and the robot's (valid, head)
+template <typename T>
+__global__ void k_kv_copy(KvCopy c) {
+  const long HD = c.HD;
+  const long n8 = HD / 8;  // 16-byte chunks of a K row (bf16) / 32-byte (fp32): copy in 8-element units
+  const long total_k = (long)c.layers * c.n * n8;
+  const long total_v = (long)c.layers * c.n * HD;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_k; i += stride) {
+    const long l = i / (c.n * n8), rem = i % (c.n * n8);
+    const int t = (int)(rem / n8), c8 = (int)(rem % n8) * 8;
+    const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
+    const T* src = (const T*)c.k + (l * c.n + t) * HD + c8;
+    T* dst = (T*)c.kd + (l * c.TP + phys) * HD + c8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = src[e];
+  }
+  // V^T: consecutive threads take consecutive tokens of one (layer, column)
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_v; i += stride) {
+    const long l = i / (c.n * HD), rem = i % (c.n * HD);
+    const int col = (int)(rem / c.n), t = (int)(rem % c.n);
+    const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
+    ((T*)c.vtd)[(l * HD + col) * c.TP + phys] = ((const T*)c.v)[(l * c.n + t) * HD + col];
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    meta[2 * robot] = valid;
-    meta[2 * robot + 1] = head;
+    c.meta[2 * c.robot] = c.valid;
+    c.meta[2 * c.robot + 1] = c.head;
   }
 }
 
@@ -1085,11 +1076,7 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
 
 template <int DH>
 static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
-  const int groups = a.B * a.Hkv * a.nqblk;
-  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(groups * a.nsplit), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine<DH>, dim3(groups * 8), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1167,14 +1154,11 @@ hipError_t launch_bias_gemv(const void* w, int w_elt, const float* scales, int r
   return hipGetLastError();
 }
 
-hipError_t launch_kv_copy(const void* k, const void* v, void* kd, void* vd, int elt, int layers, long row_elems,
-                          long src_pitch, long dst_pitch, int* meta, int robot, int valid, int head, hipStream_t st) {
-  const long es = elt == ELT_F32 ? 4 : 2;
-  const long n16 = row_elems * es / 16 * layers;
-  const int grid = (int)((n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096);
-  hipLaunchKernelGGL(k_kv_copy, dim3(grid > 0 ? grid : 1), dim3(256), 0, st, (const uint8_t*)k, (const uint8_t*)v,
-                     (uint8_t*)kd, (uint8_t*)vd, layers, row_elems * es, src_pitch * es, dst_pitch * es, meta, robot,
-                     valid, head);
+hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st) {
+  const long work = (long)c.layers * c.n * c.HD;
+  const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
+  if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_copy<float>, dim3(grid), dim3(256), 0, st, c);
+  else hipLaunchKernelGGL(k_kv_copy<uint16_t>, dim3(grid), dim3(256), 0, st, c);
   return hipGetLastError();
 }
 
