@@ -59,7 +59,7 @@ struct fm_ctx {
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
   int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
   int ks_o, ks_d, nqblk, nsplit, kps;
-  int NS8, TP, S8;  // padded static region, padded physical prefix capacity, padded suffix
+  int NSP, TP, SP;  // static region padded to 32, padded physical prefix capacity, suffix padded to 32
 
   // arena
   void* arena = nullptr;
@@ -68,7 +68,7 @@ struct fm_ctx {
   void *wout, *w_in, *b_in, *w_state, *b_state;
   float *temb, *g1, *g2, *gf, *a1, *a2, *bqkv, *bgu, *bout, *ones, *zeros;
   long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
-  void *kpre, *vtpre, *vts;
+  void *kpre, *vpre, *ksuf, *vsuf;
   int* meta;
   float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
@@ -154,7 +154,8 @@ fm_status validate_config(const fm_config* c) {
     return fail(nullptr, FM_ERR_UNSUPPORTED, "bf16 path: head_dim must be 32, 64, 128 or 256");
   }
   if (c->head_dim % 8) return fail(nullptr, FM_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
-  if (c->n_frames > 0 && c->frame_tokens % 8) return fail(nullptr, FM_ERR_UNSUPPORTED, "frame_tokens % 8 != 0");
+  if (c->n_frames > 0 && c->frame_tokens % 32)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "frame_tokens must be a multiple of 32");
   const long tcap = (long)c->prefix_static + (long)c->n_frames * c->frame_tokens;
   if (tcap > (1 << 24)) return fail(nullptr, FM_ERR_SHAPE, "prefix capacity too large");
   return FM_OK;
@@ -187,20 +188,27 @@ void derive(fm_ctx* x) {
   x->F = c.d_mlp; x->N = c.n_steps; x->HD = x->Hkv * x->Dh;
   x->Nqkv = (x->Hq + 2 * x->Hkv) * x->Dh;
   x->Tcap = c.prefix_static + c.n_frames * c.frame_tokens;
-  x->NS8 = (c.prefix_static + 7) / 8 * 8;
-  x->TP = x->NS8 + c.n_frames * c.frame_tokens;
-  x->S8 = (x->C + (c.state_dim > 0) + 7) / 8 * 8;
+  x->NSP = (c.prefix_static + 31) / 32 * 32;
+  x->TP = x->NSP + c.n_frames * c.frame_tokens;
+  x->SP = (x->C + (c.state_dim > 0) + 31) / 32 * 32;
   x->P = 128;  // h^2 partial slots per row (one per 16 columns; unused slots stay zero)
   x->mtiles = (x->M + 63) / 64;
   x->esplit = x->d / 64;
   const int unit = x->wt == ELT_FP8 ? 2 : 1;
   (void)unit;
+  // residual GEMMs on the large-M path may split K (shared tile plan)
   x->ks_o = 1;
   x->ks_d = 1;
+  if (x->act == ELT_BF16 && x->wt == ELT_BF16) {
+    const BigPlan po = big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh);
+    const BigPlan pd = big_plan(EPI_RESID, x->M, x->d, x->F);
+    if (po.used) x->ks_o = po.ks;
+    if (pd.used) x->ks_d = pd.ks;
+  }
   x->nqblk = (x->S * (x->Hq / x->Hkv) + 15) / 16;
   {
     // key ranges: about 64 workgroups or more, each range >= 64 keys
-    const int keys = x->TP + x->S8;
+    const int keys = x->TP + x->SP;
     const int groups = x->B * x->Hkv * x->nqblk;
     int ns = std::min(std::min((keys + 63) / 64, (64 + groups - 1) / groups), 16);
     x->nsplit = std::max(1, ns);
@@ -251,8 +259,9 @@ void carve(fm_ctx* x, Arena& a) {
   x->st_bout = ada ? x->A : 0;
   const size_t kv = (size_t)x->B * L * x->TP * x->HD * ea;
   x->kpre = a.take(kv > 0 ? kv : 16);
-  x->vtpre = a.take(kv > 0 ? kv : 16);
-  x->vts = a.take((size_t)x->B * x->HD * x->S8 * ea);
+  x->vpre = a.take(kv > 0 ? kv : 16);
+  x->ksuf = a.take((size_t)x->B * x->HD * x->SP * ea);
+  x->vsuf = a.take((size_t)x->B * x->HD * x->SP * ea);
   x->meta = (int*)a.take(x->B * 2 * sizeof(int));
   const long Mp = (long)x->mtiles * 64;
   x->h = (float*)a.take(Mp * d * 4);
@@ -267,7 +276,8 @@ void carve(fm_ctx* x, Arena& a) {
   x->o = a.take(Mp * x->Hq * x->Dh * ea);
   x->z = a.take(Mp * x->F * ea);
   const long ks = std::max(x->ks_o, x->ks_d);
-  x->partials = (float*)a.take(ks > 1 ? ks * Mp * d * 4 : 16);
+  const long Mp128 = (x->M + 127) / 128 * 128;  // rows covered by the large-M tiles
+  x->partials = (float*)a.take(ks > 1 ? ks * Mp128 * d * 4 : 16);
   x->attn_part = (float*)a.take(x->act == ELT_F32 || x->nsplit == 1
                                     ? 16
                                     : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 64 * (x->Dh + 2) * 4);
@@ -292,18 +302,19 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
     g.A = x->u; g.W = w.wqkv; g.wscale = w.sqkv; g.N = x->Nqkv; g.K = x->d; g.nt = 16; g.ksplit = 1;
     g.out = x->qkv;
     g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(x->zeros, 0);
-    g.vts = x->vts; g.S = x->S; g.S8 = x->S8; g.Hq = x->Hq; g.Hkv = x->Hkv; g.Dh = x->Dh;
+    g.ksuf = x->ksuf; g.vsuf = x->vsuf; g.S = x->S; g.SP = x->SP; g.Hq = x->Hq; g.Hkv = x->Hkv; g.Dh = x->Dh;
     HIPCHK(x, launch_gemm(x->act, x->wt, EPI_QKV, g, st), "qkv gemm");
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     AttnArgs at{};
     at.qkv = x->qkv;
     at.kpre = (const char*)x->kpre + (size_t)l * Tl * elt_size(x->act);
-    at.vtpre = (const char*)x->vtpre + (size_t)l * Tl * elt_size(x->act);
-    at.vts = x->vts;
+    at.vpre = (const char*)x->vpre + (size_t)l * Tl * elt_size(x->act);
+    at.ksuf = x->ksuf;
+    at.vsuf = x->vsuf;
     at.b_stride = (long)x->L * Tl;
     at.meta = x->meta;
-    at.B = x->B; at.S = x->S; at.S8 = x->S8; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
-    at.n_static = x->cfg.prefix_static; at.NS8 = x->NS8; at.TP = x->TP;
+    at.B = x->B; at.S = x->S; at.SP = x->SP; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
+    at.n_static = x->cfg.prefix_static; at.NSP = x->NSP; at.TP = x->TP;
     at.frame_tokens = std::max(1, x->cfg.frame_tokens);
     at.n_frames = std::max(1, x->cfg.n_frames);
     at.ring = x->cfg.n_frames > 0;
@@ -616,9 +627,9 @@ fm_status fm_set_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* 
   const size_t ea = elt_size(x->act);
   const size_t rb = (size_t)robot * x->L * x->TP * x->HD * ea;
   KvCopy c{};
-  c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vtd = (char*)x->vtpre + rb;
-  c.elt = x->act; c.layers = x->L; c.n = n_tokens; c.HD = x->HD; c.TP = x->TP;
-  c.phys0 = 0; c.split_t = ring ? x->cfg.prefix_static : n_tokens; c.phys1 = x->NS8;
+  c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vd = (char*)x->vpre + rb;
+  c.elt = x->act; c.layers = x->L; c.n = n_tokens; c.HD = x->HD; c.Dh = x->Dh; c.TP = x->TP;
+  c.phys0 = 0; c.split_t = ring ? x->cfg.prefix_static : n_tokens; c.phys1 = x->NSP;
   c.meta = x->meta; c.robot = robot; c.valid = n_tokens; c.head = 0;
   HIPCHK(x, launch_kv_copy(c, x->stream), "prefix copy");
   x->valid[robot] = n_tokens;
@@ -640,9 +651,9 @@ fm_status fm_append_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const voi
   const size_t ea = elt_size(x->act);
   const size_t rb = (size_t)robot * x->L * x->TP * x->HD * ea;
   KvCopy c{};
-  c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vtd = (char*)x->vtpre + rb;
-  c.elt = x->act; c.layers = x->L; c.n = x->cfg.frame_tokens; c.HD = x->HD; c.TP = x->TP;
-  c.phys0 = x->NS8 + slot * x->cfg.frame_tokens; c.split_t = c.n; c.phys1 = 0;
+  c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vd = (char*)x->vpre + rb;
+  c.elt = x->act; c.layers = x->L; c.n = x->cfg.frame_tokens; c.HD = x->HD; c.Dh = x->Dh; c.TP = x->TP;
+  c.phys0 = x->NSP + slot * x->cfg.frame_tokens; c.split_t = c.n; c.phys1 = 0;
   c.meta = x->meta; c.robot = robot; c.valid = x->valid[robot]; c.head = nh;
   HIPCHK(x, launch_kv_copy(c, x->stream), "frame append");
   x->head[robot] = nh;

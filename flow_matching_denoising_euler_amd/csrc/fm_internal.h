@@ -39,8 +39,9 @@ struct GemmArgs {
   // epilogue operands
   void* out;              // QKV: [M][N] act ; GELU: [M][N/2] act
   Tab bias;               // QKV / GELU: per packed column (Ada beta W)
-  void* vts;              // QKV: suffix V^T [B][Hkv][Dh][S8] (also written)
-  int S, S8, Hq, Hkv, Dh; // QKV: shapes for vts
+  void* ksuf;             // QKV: suffix K of this step, kv layout (written)
+  void* vsuf;             // QKV: suffix V of this step, kv layout (written)
+  int S, SP, Hq, Hkv, Dh; // QKV: suffix rows, suffix keys padded to 32, heads
   float* h;               // RESID: [M][N] fp32 residual stream (in/out)
   Tab alpha;              // RESID: per column (Ada alpha) or null
   Tab gnext;              // RESID: gain of the next norm per column
@@ -49,22 +50,43 @@ struct GemmArgs {
   int step;
 };
 
-// Prefix K/V storage per (robot, layer): K rows [TP][Hkv][Dh] and V
-// transposed [Hkv][Dh][TP], at physical positions of a padded layout: the
-// static region padded to NS8 (a multiple of 8), then n_frames slots of
-// frame_tokens.  The suffix V of the current step is kept transposed too,
-// vts [B][Hkv][Dh][S8].  Attention enumerates keys in a padded logical
-// order (prefix span, then the suffix padded to S8) in which every group of
-// 8 keys is contiguous in storage.
+// K/V storage ("kv layout").  A key block of NK keys (NK a multiple of 32)
+// of one kv head holds, for bf16 activations, MFMA fragment tiles of 1 KB:
+//   K: tile (16 keys, 32 dims), lane l = key % 16 + 16 * (dim % 32 / 8),
+//      element (key p, dim c) at (((j*NK/16 + p/16)*Dh/32 + c/32)*64 + l)*8 + c%8
+//   V: tile (32 keys, 16 dims), lane l = dim % 16 + 16 * (key % 32 / 8),
+//      element (p, c) at (((j*NK/32 + p/32)*Dh/16 + c/16)*64 + l)*8 + p%8
+// so that every fragment load of the attention reads 1 KB contiguous; for
+// fp32 activations K rows [NK][Hkv][Dh] and V transposed [Hkv][Dh][NK].
+// The prefix of one (robot, layer) is a block of TP keys at physical
+// positions: the static region padded to NSP (a multiple of 32), then
+// n_frames slots of frame_tokens (a multiple of 32), so no tile straddles
+// two regions.  The suffix K/V of the current step are a block of SP keys
+// (S padded to 32) per robot.  Attention enumerates keys in a padded logical
+// order: prefix span TP, then the SP suffix keys.
+__host__ __device__ inline long kv_k_off(bool packed, int NK, int Hkv, int Dh, int j, int p, int c) {
+  if (packed)
+    return ((((long)j * (NK >> 4) + (p >> 4)) * (Dh >> 5) + (c >> 5)) * 64 + (p & 15) + 16 * ((c & 31) >> 3)) * 8 +
+           (c & 7);
+  return ((long)p * Hkv + j) * Dh + c;
+}
+__host__ __device__ inline long kv_v_off(bool packed, int NK, int Hkv, int Dh, int j, int p, int c) {
+  if (packed)
+    return ((((long)j * (NK >> 5) + (p >> 5)) * (Dh >> 4) + (c >> 4)) * 64 + (c & 15) + 16 * ((p & 31) >> 3)) * 8 +
+           (p & 7);
+  return ((long)j * Dh + c) * NK + p;
+}
+
 struct AttnArgs {
-  const void* qkv;        // [B*S][Nqkv] act (Q and suffix K)
+  const void* qkv;        // [B*S][Nqkv] act (Q is read from it)
   const void* kpre;       // layer-l base of prefix K; robots b_stride elements apart
-  const void* vtpre;      // layer-l base of prefix V^T; robots b_stride elements apart
-  const void* vts;        // suffix V^T [B][Hkv][Dh][S8]
-  long b_stride;          // elements between robots in kpre / vtpre
+  const void* vpre;       // layer-l base of prefix V; robots b_stride elements apart
+  const void* ksuf;       // suffix K, one SP-key block per robot
+  const void* vsuf;       // suffix V, one SP-key block per robot
+  long b_stride;          // elements between robots in kpre / vpre
   const int* meta;        // [B][2] = (valid prefix tokens, ring head)
-  int B, S, S8, Hq, Hkv, Dh, Nqkv;
-  int n_static, NS8, TP, frame_tokens, n_frames, ring;
+  int B, S, SP, Hq, Hkv, Dh, Nqkv;
+  int n_static, NSP, TP, frame_tokens, n_frames, ring;
   int nqblk, nsplit;      // query blocks of 64 per (b, kv head); key ranges
   int keys_per_split;     // padded logical keys per range (multiple of 32)
   float scale;
@@ -115,6 +137,26 @@ struct EmbedArgs {
   int B, S, C, A, SD, d, M, has_state, mtiles, esplit;
 };
 
+// Tile plan of the large-M GEMM (bf16 activations and weights): tiles of
+// BM rows x BN packed columns, K split over ks workgroups (residual GEMMs
+// only, reduced by the last-arriving workgroup in a fixed order).  used =
+// false selects the skinny GEMM.
+struct BigPlan {
+  bool used;
+  int BM, BN, ks;
+};
+inline BigPlan big_plan(int epi, int M, int N, int K) {
+  BigPlan p{false, 128, epi == EPI_GELU ? 256 : 128, 1};
+  if (M < 256 || K % 64 || N % p.BN) return p;
+  if (epi == EPI_RESID) {
+    const int tiles = (M + p.BM - 1) / p.BM * (N / p.BN), stages = K / 64;
+    if (stages % 4 == 0 && tiles * 4 <= 256) p.ks = 4;
+    else if (stages % 2 == 0 && tiles * 2 <= 256) p.ks = 2;
+  }
+  p.used = true;
+  return p;
+}
+
 // --- launchers (fm_kernels.hip) --------------------------------------------
 hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t st);
 hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st);
@@ -140,15 +182,15 @@ hipError_t launch_ada_mod(const float* c, int n_steps, int d, const void* w_n, c
 hipError_t launch_bias_gemv(const void* w, int w_elt, const float* scales, int rows, int cols,
                             const float* beta, long beta_step_stride, int n_steps, RowMap rm,
                             float* out, long out_step_stride, hipStream_t st);
-// prefix K/V copy into the padded physical layout + meta update: tokens
-// [0, n) of src (per layer [n][Hkv*Dh]) go to physical rows phys0 + t, except
-// that tokens t >= split_t go to phys1 + (t - split_t) (static vs frames).
+// prefix K/V copy into the kv layout + meta update: tokens [0, n) of src
+// (per layer [n][Hkv*Dh]) go to physical positions phys0 + t, except that
+// tokens t >= split_t go to phys1 + (t - split_t) (static vs frames).
 struct KvCopy {
   const void* k;
   const void* v;
   void* kd;               // robot base of K: layer pitch TP*HD
-  void* vtd;              // robot base of V^T: layer pitch HD*TP
-  int elt, layers, n, HD, TP;
+  void* vd;               // robot base of V: layer pitch TP*HD
+  int elt, layers, n, HD, Dh, TP;
   int phys0, split_t, phys1;
   int* meta;
   int robot, valid, head;

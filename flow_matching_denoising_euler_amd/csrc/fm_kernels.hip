@@ -82,7 +82,20 @@ __device__ __forceinline__ float tab_or1(const Tab& t, int step, int i) {
   return t.base ? t.base[(long)step * t.step_stride + i] : 1.f;
 }
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (absolute error <= 1.5e-7): for x >= 0, erf x = 1 - t (a1 + t (a2 +
+// t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x); odd in x.  A dozen
+// instructions instead of a general erf, far below the bf16 rounding of the
+// GEMM outputs it feeds.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.f));
+  const float poly = fmaf(fmaf(fmaf(fmaf(1.061405429f, t, -1.453152027f), t, 1.421413741f), t, -0.284496736f), t,
+                          0.254829592f) * t;
+  return copysignf(1.f - poly * __expf(-ax * ax), x);
+}
+// exact-form GELU, x Phi(x) = x/2 (1 + erf(x / sqrt 2))
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.f + erf_as(x * 0.70710678118654752f)); }
 
 // OCP E4M3FN code -> bf16 bits (exact; the quantiser never emits NaN codes)
 __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
@@ -411,17 +424,25 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
   }
 
   if constexpr (EPI == EPI_QKV) {
-    const int vcol0 = (g.Hq + g.Hkv) * g.Dh;  // suffix V columns are also stored transposed
+    // Q columns -> out (row-major); suffix K and V -> their kv-layout blocks
+    const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
+    constexpr bool packed = ACT != ELT_F32;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = tid + NT * i, row = idx / nt, c = idx % nt;
       const int r = m0 + row, col = n0 + c;
       const float val = v[i] * s_col[2][c] * s_rstd[row] + s_col[0][c];
       if (r < g.M) {
-        st_act<ACT>(g.out, (long)r * g.N + col, val);
-        if (col >= vcol0) {
-          const int jv = (col - vcol0) / g.Dh, dh = (col - vcol0) % g.Dh, b = r / g.S, sr = r % g.S;
-          st_act<ACT>(g.vts, ((long)(b * g.Hkv + jv) * g.Dh + dh) * g.S8 + sr, val);
+        const int b = r / g.S, sr = r % g.S;
+        const long sb = (long)b * g.Hkv * g.Dh * g.SP;
+        if (col < kcol0) {
+          st_act<ACT>(g.out, (long)r * g.N + col, val);
+        } else if (col < vcol0) {
+          const int jk = (col - kcol0) / g.Dh, dh = (col - kcol0) % g.Dh;
+          st_act<ACT>(g.ksuf, sb + kv_k_off(packed, g.SP, g.Hkv, g.Dh, jk, sr, dh), val);
+        } else {
+          const int jv = (col - vcol0) / g.Dh, dh = (col - vcol0) % g.Dh;
+          st_act<ACT>(g.vsuf, sb + kv_v_off(packed, g.SP, g.Hkv, g.Dh, jv, sr, dh), val);
         }
       }
     }
@@ -465,46 +486,424 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Large-M GEMM (batched robots, MFMA-bound), bf16 activations and weights,
+// the same fused epilogues as the skinny GEMM.
+//
+// Workgroup = 4 waves in a 2 x 2 grid over a BM x BN tile (BM = 32 TMW rows,
+// BN = 32 TNW packed columns); wave (wm, wn) owns TMW row blocks x TNW
+// column blocks of 16.  Both operands are in MFMA fragment order in memory
+// (1 KB per 16 x 32 fragment), so each stage (BIG_KS k-blocks of 32) is
+// copied fragment by fragment straight into LDS (global_load_lds_dwordx4:
+// lane i's 16 bytes land at M0 + 16 i) into a ring of three slots, and the
+// waves read their fragments with conflict-free 16-byte LDS reads.  The
+// weight fragment is the MFMA's first operand, so a lane's accumulator holds
+// 4 consecutive output columns of one row: the epilogues load and store
+// 8- and 16-byte vectors.  Residual GEMMs may split K over ks workgroups;
+// each writes its partial tile (device-scope stores), and the last to arrive
+// sums the partials in split order and runs the epilogue (deterministic).
+// ---------------------------------------------------------------------------
+constexpr int BIG_STAGES = 3, BIG_KS = 2;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 1 KB fragment copy into LDS at lds (wave-uniform address).  Written
+// as inline asm so that the compiler, which would otherwise make every LDS
+// read wait for all copies in flight, leaves the waiting to wait_vmcnt; the
+// memory clobber keeps it in program order with the LDS accesses.  No other
+// code in the kernels that use it touches M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_off) : "memory", "m0");
+}
+// LDS address (offset in the workgroup's LDS) of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Workgroup barrier without a memory fence: each wave has waited for its own
+// copies (wait_vmcnt) and LDS is coherent within the workgroup.  The signal
+// fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// 64-bit device-scope store / load (coherent across XCDs, see st_dev)
+__device__ __forceinline__ void st_dev2(float* p, float a, float b) {
+  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const unsigned long long v = __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2(f2bf(a) | (f2bf(b) << 16), f2bf(c) | (f2bf(d) << 16));
+}
+
+// Copies of one stage.  Fragment f = wave + 4 i of a stage: the first
+// MB * KS are activations (k-block f / MB, row block f % MB), the rest
+// weights; since MB * KS is a multiple of 4, loop index i < TMW gives
+// activations.  src[i] is this lane's source of fragment i in the split's
+// first stage; stage sc (relative) adds sc * stride (A or W).
+template <int TMW, int TNW>
+struct BigSrc {
+  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, LPW = (MB + NBK) * BIG_KS / 4;
+  const uint16_t* src[LPW];
+  long stride_a, stride_w;  // elements per stage
+  __device__ __forceinline__ BigSrc(const uint16_t* A, const uint16_t* W, int wave, int lane, int st0, int rb0,
+                                    int nb0, int KB, int RB, int NBT) {
+    stride_a = (long)BIG_KS * 4 * 512;
+    stride_w = (long)BIG_KS * NBT * 512;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int f = wave + 4 * i;
+      if (i < TMW) {
+        const int qk = f / MB, mi = f % MB;
+        const int rb = min(rb0 + mi, RB - 1), kb = st0 * BIG_KS + qk;
+        src[i] = A + ((((long)(rb >> 2) * KB + kb) * 4 + (rb & 3)) * 64 + lane) * 8;
+      } else {
+        const int ff = f - MB * BIG_KS, qk = ff / NBK, ni = ff % NBK;
+        src[i] = W + (((long)(st0 * BIG_KS + qk) * NBT + nb0 + ni) * 64 + lane) * 8;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(uint32_t base, int wave, int sc) const {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      lds_dma16(src[i] + sc * (i < TMW ? stride_a : stride_w), base + (uint32_t)(wave + 4 * i) * 1024u);
+  }
+};
+// acc[ni][mi] += W(column block) x A(row block)^T over the stage
+template <int TMW, int TNW>
+__device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TNW][TMW], int wm, int wn, int lane) {
+  constexpr int MB = 2 * TMW, NBK = 2 * TNW;
+#pragma unroll
+  for (int qk = 0; qk < BIG_KS; ++qk) {
+    uint4 af[TMW], bf[TNW];
+#pragma unroll
+    for (int mi = 0; mi < TMW; ++mi) af[mi] = *(const uint4*)(base + (qk * MB + wm * TMW + mi) * 1024 + lane * 16);
+#pragma unroll
+    for (int ni = 0; ni < TNW; ++ni)
+      bf[ni] = *(const uint4*)(base + (MB * BIG_KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
+#pragma unroll
+    for (int ni = 0; ni < TNW; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = mma_bf16(bf[ni], af[mi], acc[ni][mi]);
+  }
+}
+
+template <int EPI, int TMW, int TNW>
+__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
+  constexpr int MB = 2 * TMW, NBK = 2 * TNW;          // row / column blocks of the tile
+  constexpr int BM = 16 * MB, BN = 16 * NBK;
+  constexpr int FPS = (MB + NBK) * BIG_KS;            // fragments per stage
+  constexpr int LPW = FPS / 4;                        // copies per wave per stage
+  constexpr int NJ = TNW * TMW;                       // accumulator blocks per wave
+  static_assert((MB * BIG_KS) % 4 == 0 && BIG_STAGES == 3, "stage split");
+  __shared__ __align__(16) uint8_t lds0[FPS * 1024], lds1[FPS * 1024], lds2[FPS * 1024];
+  __shared__ float s_rstd[BM];
+  __shared__ __align__(16) float s_col[2][BN];        // bias or alpha, gnext
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: fragment choice and LDS address are scalar
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = g.N / BN, T = tiles_m * tiles_n;
+  const int ks = blockIdx.x % g.ksplit;
+  // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
+  // a contiguous range of tiles, m fastest, so it shares weight columns
+  int t = blockIdx.x / g.ksplit;
+  const int q8 = T / 8;
+  if (t < 8 * q8) t = (t % 8) * q8 + t / 8;
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int rb0 = tm * MB, nb0 = tn * NBK, m0 = tm * BM, n0 = tn * BN;
+  const int KB = g.K >> 5, RB = g.mtiles * 4, NBT = g.N >> 4;
+  const int nstage = KB / BIG_KS / g.ksplit, st0 = ks * nstage;
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* W = (const uint16_t*)g.W;
+
+  // epilogue column operands and the rows' norm statistics (issued first)
+  float cv0 = 0.f, cv1 = 0.f;
+  if (tid < BN) {
+    const int col = n0 + tid;
+    cv0 = EPI == EPI_RESID ? g.alpha.base[(long)g.step * g.alpha.step_stride + col]
+                           : g.bias.base[(long)g.step * g.bias.step_stride + col];
+    cv1 = EPI == EPI_RESID ? g.gnext.base[(long)g.step * g.gnext.step_stride + col] : 0.f;
+  }
+  float4 q[4][BM / 32];
+  if (EPI != EPI_RESID) {
+    // 8 threads per row, 16 slots each (the skinny kernel's order)
+#pragma unroll
+    for (int rr = 0; rr < BM / 32; ++rr) {
+      const int row = min(m0 + rr * 32 + (tid >> 3), g.M - 1);
+      const float4* p = (const float4*)(g.ssq + (long)row * PM + (tid & 7) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i][rr] = p[i];
+    }
+  }
+  const BigSrc<TMW, TNW> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
+  const uint32_t a0 = lds_addr(lds0), a1 = lds_addr(lds1), a2 = lds_addr(lds2);
+  srcs.issue(a0, wave, 0);
+  srcs.issue(a1, wave, min(1, nstage - 1));
+
+  f32x4 acc[TNW][TMW];
+#pragma unroll
+  for (int ni = 0; ni < TNW; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // stage s lives in slot s % 3; at stage s: wait for this wave's copies of
+  // it, barrier (everyone's copies landed, everyone is done with stage
+  // s - 1), refill the slot of stage s - 1 with stage s + 2 (past the end: a
+  // harmless reload of the last stage), compute stage s
+  const int last = nstage - 1;
+  for (int s = 0; s < nstage; s += 3) {
+    wait_vmcnt<LPW>();
+    barrier_nofence();
+    srcs.issue(a2, wave, min(s + 2, last));
+    big_compute<TMW, TNW>(lds0, acc, wm, wn, lane);
+    if (s + 1 < nstage) {
+      wait_vmcnt<LPW>();
+      barrier_nofence();
+      srcs.issue(a0, wave, min(s + 3, last));
+      big_compute<TMW, TNW>(lds1, acc, wm, wn, lane);
+    }
+    if (s + 2 < nstage) {
+      wait_vmcnt<LPW>();
+      barrier_nofence();
+      srcs.issue(a1, wave, min(s + 4, last));
+      big_compute<TMW, TNW>(lds2, acc, wm, wn, lane);
+    }
+  }
+  wait_vmcnt<0>();  // the trailing reloads
+
+  // split K: every workgroup stores its partial tile; the last to arrive
+  // adds the partials in split order and goes on to the epilogue
+  if constexpr (EPI == EPI_RESID) if (g.ksplit > 1) {
+    float* mine = g.partials + (((long)t * g.ksplit + ks) * NJ * 256 + tid) * 4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const f32x4 v = acc[j / TMW][j % TMW];
+      st_dev2(mine + j * 1024, v[0], v[1]);
+      st_dev2(mine + j * 1024 + 2, v[2], v[3]);
+    }
+    drain_vm();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(g.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)g.ksplit - 1;
+      if (s_last) __hip_atomic_store(g.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // partials two splits at a time (ksplit <= 4), every load of a pair
+    // issued before any is used; the own split comes from the registers
+    f32x4 sum[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < 4; k0 += 2) {
+      if (k0 >= g.ksplit) break;
+      const float* pa = g.partials + (((long)t * g.ksplit + k0) * NJ * 256 + tid) * 4;
+      const float* pb = g.partials + (((long)t * g.ksplit + min(k0 + 1, g.ksplit - 1)) * NJ * 256 + tid) * 4;
+      f32x4 va[NJ], vb[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float2 a0 = ld_dev2(pa + j * 1024), a1 = ld_dev2(pa + j * 1024 + 2);
+        const float2 b0 = ld_dev2(pb + j * 1024), b1 = ld_dev2(pb + j * 1024 + 2);
+        va[j] = f32x4{a0.x, a0.y, a1.x, a1.y};
+        vb[j] = f32x4{b0.x, b0.y, b1.x, b1.y};
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const f32x4 own = acc[j / TMW][j % TMW];
+        sum[j] += (k0 == ks) ? own : va[j];
+        if (k0 + 1 < g.ksplit) sum[j] += (k0 + 1 == ks) ? own : vb[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j / TMW][j % TMW] = sum[j];
+  }
+
+  // the epilogue's LDS tables
+  if (tid < BN) {
+    s_col[0][tid] = cv0;
+    s_col[1][tid] = cv1;
+  }
+  if (EPI != EPI_RESID) {
+#pragma unroll
+    for (int rr = 0; rr < BM / 32; ++rr) {
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sq += ((q[i][rr].x + q[i][rr].y) + q[i][rr].z) + q[i][rr].w;
+      sq += __shfl_xor(sq, 1);
+      sq += __shfl_xor(sq, 2);
+      sq += __shfl_xor(sq, 4);
+      const int r = rr * 32 + (tid >> 3);
+      if ((tid & 7) == 0) s_rstd[r] = (m0 + r < g.M) ? rsqrtf(sq * g.inv_d + g.eps) : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // epilogue: block (ni, mi) of this lane = row m0 + (wm TMW + mi) 16 + (lane & 15),
+  // columns n0 + (wn TNW + ni) 16 + (lane >> 4) 4 + [0, 4)
+  const int c4 = (lane >> 4) * 4;
+  if constexpr (EPI == EPI_QKV) {
+    const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
+    const int dsh = __builtin_ctz(g.Dh);  // head_dim is 32, 64, 128 or 256 on the bf16 path
+#pragma unroll
+    for (int mi = 0; mi < TMW; ++mi) {
+      const int rt = (wm * TMW + mi) * 16 + (lane & 15), row = m0 + rt;
+      if (row >= g.M) continue;
+      const float rs = s_rstd[rt];
+      const int b = row / g.S, sr = row % g.S;
+      const long sb = (long)b * g.Hkv * g.Dh * g.SP;
+#pragma unroll
+      for (int ni = 0; ni < TNW; ++ni) {
+        const int ct = (wn * TNW + ni) * 16 + c4, col = n0 + ct;
+        const float4 bias = *(const float4*)&s_col[0][ct];
+        const f32x4 a = acc[ni][mi];
+        const float v0 = a[0] * rs + bias.x, v1 = a[1] * rs + bias.y, v2 = a[2] * rs + bias.z, v3 = a[3] * rs + bias.w;
+        if (col < kcol0) {
+          *(uint2*)((uint16_t*)g.out + (long)row * g.N + col) = pack4_bf16(v0, v1, v2, v3);
+        } else if (col < vcol0) {
+          const int jk = (col - kcol0) >> dsh, dh = (col - kcol0) & (g.Dh - 1);
+          *(uint2*)((uint16_t*)g.ksuf + sb + kv_k_off(true, g.SP, g.Hkv, g.Dh, jk, sr, dh)) = pack4_bf16(v0, v1, v2, v3);
+        } else {
+          const int jv = (col - vcol0) >> dsh, dh = (col - vcol0) & (g.Dh - 1);
+          uint16_t* vp = (uint16_t*)g.vsuf + sb + kv_v_off(true, g.SP, g.Hkv, g.Dh, jv, sr, dh);
+          vp[0] = (uint16_t)f2bf(v0);  // consecutive dims are 8 elements apart
+          vp[8] = (uint16_t)f2bf(v1);
+          vp[16] = (uint16_t)f2bf(v2);
+          vp[24] = (uint16_t)f2bf(v3);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_GELU) {
+    // packed columns come in [16 gate | 16 up] pairs: block 2i is gate, 2i+1 up
+    static_assert(TNW % 2 == 0, "gate/up pairs");
+    const int F = g.N >> 1;
+#pragma unroll
+    for (int mi = 0; mi < TMW; ++mi) {
+      const int rt = (wm * TMW + mi) * 16 + (lane & 15), row = m0 + rt;
+      if (row >= g.M) continue;
+      const float rs = s_rstd[rt];
+#pragma unroll
+      for (int pi = 0; pi < TNW / 2; ++pi) {
+        const int cg = (wn * TNW + 2 * pi) * 16 + c4;
+        const float4 bg = *(const float4*)&s_col[0][cg], bu = *(const float4*)&s_col[0][cg + 16];
+        const f32x4 ga = acc[2 * pi][mi], ua = acc[2 * pi + 1][mi];
+        const float z0 = gelu_erf(ga[0] * rs + bg.x) * (ua[0] * rs + bu.x);
+        const float z1 = gelu_erf(ga[1] * rs + bg.y) * (ua[1] * rs + bu.y);
+        const float z2 = gelu_erf(ga[2] * rs + bg.z) * (ua[2] * rs + bu.z);
+        const float z3 = gelu_erf(ga[3] * rs + bg.w) * (ua[3] * rs + bu.w);
+        const int zc = ((n0 + cg) >> 5) * 16 + c4;
+        *(uint2*)((uint16_t*)g.out + pk(row, zc, F)) = pack4_bf16(z0, z1, z2, z3);
+      }
+    }
+  } else {  // EPI_RESID: h += alpha * acc; u = act(h * gnext); h^2 partials per 16 columns
+    float4 hv[TMW][TNW];
+#pragma unroll
+    for (int mi = 0; mi < TMW; ++mi) {
+      const int row = min(m0 + (wm * TMW + mi) * 16 + (lane & 15), g.M - 1);
+#pragma unroll
+      for (int ni = 0; ni < TNW; ++ni)
+        hv[mi][ni] = *(const float4*)(g.h + (long)row * g.N + n0 + (wn * TNW + ni) * 16 + c4);
+    }
+#pragma unroll
+    for (int mi = 0; mi < TMW; ++mi) {
+      const int row = m0 + (wm * TMW + mi) * 16 + (lane & 15);
+#pragma unroll
+      for (int ni = 0; ni < TNW; ++ni) {
+        const int ct = (wn * TNW + ni) * 16 + c4, col = n0 + ct;
+        const float4 al = *(const float4*)&s_col[0][ct], gn = *(const float4*)&s_col[1][ct];
+        const f32x4 a = acc[ni][mi];
+        const float4 h = hv[mi][ni];
+        const float4 hn = make_float4(h.x + al.x * a[0], h.y + al.y * a[1], h.z + al.z * a[2], h.w + al.w * a[3]);
+        float qq = ((hn.x * hn.x + hn.y * hn.y) + hn.z * hn.z) + hn.w * hn.w;
+        qq += __shfl_xor(qq, 16);
+        qq += __shfl_xor(qq, 32);
+        if (row < g.M) {
+          *(float4*)(g.h + (long)row * g.N + col) = hn;
+          *(uint2*)((uint16_t*)g.u_out + pk(row, col, g.N)) =
+              pack4_bf16(hn.x * gn.x, hn.y * gn.y, hn.z * gn.z, hn.w * gn.w);
+          if (c4 == 0) g.ssq_out[(long)row * PM + (col >> 4)] = qq;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Attention of the suffix queries over [prefix (logical order) | suffix]
 // ---------------------------------------------------------------------------
-// Padded logical keys (see AttnArgs): physical prefix position of prefix
-// position p, branch-free (logical frame f of the window lives in slot
-// (head + f) mod n_frames).
-__device__ __forceinline__ int pre_phys(const AttnArgs& a, int p, int head) {
-  const int rel = max(p - a.NS8, 0);
-  const int f = rel / a.frame_tokens, off = rel - f * a.frame_tokens;
-  int slot = head + f;
-  slot -= (slot >= a.n_frames) ? a.n_frames : 0;
-  return p < a.NS8 ? p : a.NS8 + slot * a.frame_tokens + off;
-}
 struct KeySpace {
-  int pspan, kp, tv, head;
+  // Everything the key addressing needs, copied out of the kernel arguments
+  // once: the prefix-or-suffix choice below then selects between register
+  // values (a select between two loads of argument fields would become a
+  // per-lane pointer load in front of every tile load).
+  const void *kpre, *vpre, *ksuf, *vsuf;  // bases
+  long boff, soff;                        // this robot's offsets in the prefix / suffix blocks
+  int kp, tv, head, TP, SP, NSP, S, n_static, ring, Hkv, Dh, frame_tokens, n_frames;
   // The suffix starts at the fixed position TP (the padded prefix capacity),
   // so key addresses depend on the stored prefix only through the ring head
   // (ring configurations); the valid length only masks scores.
   __device__ __forceinline__ KeySpace(const AttnArgs& a, int b) {
     tv = a.meta[2 * b];
     head = a.ring ? a.meta[2 * b + 1] : 0;
-    pspan = a.TP;
-    kp = pspan + a.S8;
+    TP = a.TP; SP = a.SP; NSP = a.NSP; S = a.S; n_static = a.n_static; ring = a.ring; Hkv = a.Hkv; Dh = a.Dh;
+    frame_tokens = a.frame_tokens; n_frames = a.n_frames;
+    kp = TP + SP;
+    kpre = a.kpre; vpre = a.vpre; ksuf = a.ksuf; vsuf = a.vsuf;
+    boff = b * a.b_stride;
+    soff = (long)b * Hkv * Dh * SP;
   }
-  __device__ __forceinline__ bool valid(const AttnArgs& a, int p) const {
-    const bool pre_ok = a.ring ? (p >= a.NS8 || p < a.n_static) : (p < tv);
-    return p < pspan ? pre_ok : (p - pspan < a.S);
+  // physical prefix position of prefix position p, branch-free (logical
+  // frame f of the window lives in slot (head + f) mod n_frames)
+  __device__ __forceinline__ int phys(int p) const {
+    const int rel = max(p - NSP, 0);
+    const int f = rel / frame_tokens, off = rel - f * frame_tokens;
+    int slot = head + f;
+    slot -= (slot >= n_frames) ? n_frames : 0;
+    return p < NSP ? p : NSP + slot * frame_tokens + off;
   }
-  template <typename T>
-  __device__ __forceinline__ const T* krow(const AttnArgs& a, int b, int j, int p) const {
-    const T* pp = (const T*)a.kpre + b * a.b_stride + ((long)pre_phys(a, p, head) * a.Hkv + j) * a.Dh;
-    const int s = min(max(p - pspan, 0), a.S - 1);
-    const T* sp = (const T*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)(a.Hq + j) * a.Dh;
-    return p < pspan ? pp : sp;
+  __device__ __forceinline__ bool valid(int p) const {
+    const bool pre_ok = ring ? (p >= NSP || p < n_static) : (p < tv);
+    return p < TP ? pre_ok : (p - TP < S);
   }
-  // V^T of keys p8 .. p8+7 (p8 a multiple of 8) for head dim dh: contiguous
-  template <typename T>
-  __device__ __forceinline__ const T* vcol(const AttnArgs& a, int b, int j, int p8, int dh) const {
-    const T* pp = (const T*)a.vtpre + b * a.b_stride + ((long)j * a.Dh + dh) * a.TP + pre_phys(a, p8, head);
-    const T* sp = (const T*)a.vts + ((long)(b * a.Hkv + j) * a.Dh + dh) * a.S8 + max(p8 - pspan, 0);
-    return p8 < pspan ? pp : sp;
+  // bf16 kv layout: this lane's 8 elements of the K tile (16-key block kb16,
+  // 32-dim block kb) and of the V tile (32-key block kb32, 16-dim block nbd)
+  __device__ __forceinline__ const uint16_t* ktile(int j, int kb16, int kb, int lane) const {
+    const int p = kb16 * 16, KBD = Dh >> 5;
+    const long pre = boff + ((((long)j * (TP >> 4) + (phys(p) >> 4)) * KBD + kb) * 64 + lane) * 8;
+    const long suf = soff + ((((long)j * (SP >> 4) + (max(p - TP, 0) >> 4)) * KBD + kb) * 64 + lane) * 8;
+    const uint16_t* base = p < TP ? (const uint16_t*)kpre : (const uint16_t*)ksuf;
+    return base + (p < TP ? pre : suf);
+  }
+  __device__ __forceinline__ const uint16_t* vtile(int j, int kb32, int nbd, int lane) const {
+    const int p = kb32 * 32, NBD = Dh >> 4;
+    const long pre = boff + ((((long)j * (TP >> 5) + (phys(p) >> 5)) * NBD + nbd) * 64 + lane) * 8;
+    const long suf = soff + ((((long)j * (SP >> 5) + (max(p - TP, 0) >> 5)) * NBD + nbd) * 64 + lane) * 8;
+    const uint16_t* base = p < TP ? (const uint16_t*)vpre : (const uint16_t*)vsuf;
+    return base + (p < TP ? pre : suf);
+  }
+  // fp32 kv layout: K element (p, c) and V element (p, c)
+  __device__ __forceinline__ float kel(int j, int p, int c) const {
+    return p < TP ? ((const float*)kpre)[boff + kv_k_off(false, TP, Hkv, Dh, j, phys(p), c)]
+                  : ((const float*)ksuf)[soff + kv_k_off(false, SP, Hkv, Dh, j, p - TP, c)];
+  }
+  __device__ __forceinline__ float vel(int j, int p, int c) const {
+    return p < TP ? ((const float*)vpre)[boff + kv_v_off(false, TP, Hkv, Dh, j, phys(p), c)]
+                  : ((const float*)vsuf)[soff + kv_v_off(false, SP, Hkv, Dh, j, p - TP, c)];
   }
 };
 
@@ -541,20 +940,16 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 
   uint4 kf[2][2][KBD], vf[NBD];
   auto load_k = [&](int t, int slot) {
-    const int base = (wave + 4 * t) * KT;
+    const int tt = min(wave + 4 * t, ntile_all - 1);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int p = min(base + nb * 16 + (lane & 15), ks.kp - 1);
-      const uint16_t* kp = ks.krow<uint16_t>(a, b, j, p) + (lane >> 4) * 8;
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int kb = 0; kb < KBD; ++kb) kf[slot][nb][kb] = *(const uint4*)(kp + kb * 32);
-    }
+      for (int kb = 0; kb < KBD; ++kb) kf[slot][nb][kb] = *(const uint4*)ks.ktile(j, tt * 2 + nb, kb, lane);
   };
   auto load_v = [&](int t) {
-    const int p8 = min((wave + 4 * t) * KT + (lane >> 4) * 8, ks.kp - 8);
+    const int tt = min(wave + 4 * t, ntile_all - 1);
 #pragma unroll
-    for (int nbd = 0; nbd < NBD; ++nbd)
-      vf[nbd] = *(const uint4*)ks.vcol<uint16_t>(a, b, j, p8, nbd * 16 + (lane & 15));
+    for (int nbd = 0; nbd < NBD; ++nbd) vf[nbd] = *(const uint4*)ks.vtile(j, tt, nbd, lane);
   };
   if (ntile > 0) {
     load_k(0, 0);
@@ -582,7 +977,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int key = (wave + 4 * t) * KT + nb * 16 + (lane & 15);
-        p[nb][r] = (key < ks.kp && ks.valid(a, key)) ? sacc[nb][r] * a.scale : -INFINITY;
+        p[nb][r] = (key < ks.kp && ks.valid(key)) ? sacc[nb][r] * a.scale : -INFINITY;
         m = fmaxf(m, p[nb][r]);
       }
       m = fmaxf(m, __shfl_xor(m, 1));
@@ -671,6 +1066,194 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   }
 }
 
+// bf16 MFMA attention with the scores held in registers, for padded key
+// counts up to 1024.  Workgroup = 16 queries (suffix rows x heads of one KV
+// group) and 8 waves:
+//  1. wave w computes the scores of the 16-key blocks nb = w + 8 i (i < R)
+//     and keeps them in registers; its K fragments are streamed KQ blocks
+//     ahead of the MFMAs;
+//  2. the row maxima, then the row sums of exp(s - max), are combined over
+//     the waves through LDS (two barriers); P = exp(s - max) goes to LDS in
+//     bf16, zero for masked and padding keys;
+//  3. wave w computes O for its head-dim blocks (for DH < 128 also only a
+//     share of the keys, summed through LDS in a fixed order) from P and
+//     V^T fragments streamed VQ blocks ahead, scales by 1 / sum and stores.
+// Every global load of a phase is issued before its first use; there is no
+// online rescaling and, for DH >= 128, no merge of partial outputs.
+template <int DH, int R>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
+  constexpr int KBD = DH / 32, NBD = DH / 16;
+  // K and V blocks in flight per wave, within about 240 registers
+  constexpr int KQ0 = (R <= 4 ? 24 : 16) / KBD, KQ = KQ0 < R ? KQ0 : R;
+  constexpr int KPAD = 128 * R + 8;                    // P row: keys of blocks nb < 8R, padded
+  constexpr int NBW = NBD >= 8 ? NBD / 8 : 1;          // head-dim blocks per wave
+  constexpr int KG = NBD >= 8 ? 1 : 8 / NBD;           // key groups of phase 3
+  constexpr int KBW = 4 * R / KG;                      // 32-key blocks per wave in phase 3
+  constexpr int VQ0 = (R <= 3 ? 16 : 8) / NBW, VQ = VQ0 < KBW ? VQ0 : KBW;
+  __shared__ __align__(16) uint16_t sP[16][KPAD];
+  __shared__ float s_max[8][16], s_sum[8][16];
+  __shared__ __align__(16) float s_o[KG > 1 ? KG * 16 * (DH + 4) : 4];
+  __shared__ __align__(16) uint16_t s_out[16][DH + 8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qb = blockIdx.x % a.nqblk, jb = blockIdx.x / a.nqblk;
+  const int j = jb % a.Hkv, b = jb / a.Hkv;
+  const int G = a.Hq / a.Hkv, nq = a.S * G;
+
+  uint4 qf[KBD];
+  {
+    const int qi = min(qb * 16 + (lane & 15), nq - 1);
+    const int s = qi / G, h = j * G + qi % G;
+    const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb) qf[kb] = *(const uint4*)(qp + kb * 32);
+  }
+  const KeySpace ks(a, b);
+  const int nk16 = ks.kp >> 4, nk32 = ks.kp >> 5;  // kp is a multiple of 32
+
+  // ---- 1. scores of this wave's key blocks
+  uint4 kf[KQ][KBD];
+  auto load_k = [&](int i, int slot) {
+    const int nb = min(w + 8 * i, nk16 - 1);
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb) kf[slot][kb] = *(const uint4*)ks.ktile(j, nb, kb, lane);
+  };
+  // phase 3's first V fragments go out with the first K fragments, before
+  // any wait; the scheduling barriers keep the compiler from sinking loads
+  // towards their uses (which would serialise the round trips)
+  const int kg = w / (8 / KG), nbd0 = (w % (8 / KG)) * NBW;
+  uint4 vf[VQ][NBW];
+  auto load_v = [&](int i, int slot) {
+    const int kb32 = min(kg + KG * i, nk32 - 1);
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) vf[slot][n] = *(const uint4*)ks.vtile(j, kb32, nbd0 + n, lane);
+  };
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) load_k(i, i);
+#pragma unroll
+  for (int i = 0; i < VQ; ++i) load_v(i, i);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 sc[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBD; ++kb) acc = mma_bf16(qf[kb], kf[i % KQ][kb], acc);
+    sc[i] = acc;
+    if (i + KQ < R) {
+      load_k(i + KQ, i % KQ);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- 2. softmax over all keys: max, then exp and sums
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int key = (w + 8 * i) * 16 + (lane & 15);
+    const bool ok = key < ks.kp && ks.valid(key);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[i][r] = ok ? sc[i][r] * a.scale : -INFINITY;
+      mx[r] = fmaxf(mx[r], sc[i][r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 1));
+    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 2));
+    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 4));
+    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 8));
+    if ((lane & 15) == 0) s_max[w][(lane >> 4) * 4 + r] = mx[r];
+  }
+  __syncthreads();
+  float sm[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (lane >> 4) * 4 + r;
+    float M = s_max[0][row];
+#pragma unroll
+    for (int v = 1; v < 8; ++v) M = fmaxf(M, s_max[v][row]);
+    mx[r] = M;
+    sm[r] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int key = (w + 8 * i) * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = (mx[r] == -INFINITY) ? 0.f : __expf(sc[i][r] - mx[r]);
+      sm[r] += p;
+      sP[(lane >> 4) * 4 + r][key] = (uint16_t)f2bf(p);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sm[r] += __shfl_xor(sm[r], 1);
+    sm[r] += __shfl_xor(sm[r], 2);
+    sm[r] += __shfl_xor(sm[r], 4);
+    sm[r] += __shfl_xor(sm[r], 8);
+    if ((lane & 15) == 0) s_sum[w][(lane >> 4) * 4 + r] = sm[r];
+  }
+  __syncthreads();
+
+  // ---- 3. O = P V for this wave's head-dim blocks and key group
+  f32x4 oacc[NBW];
+#pragma unroll
+  for (int n = 0; n < NBW; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    const uint4 pf = *(const uint4*)&sP[lane & 15][(kg + KG * i) * 32 + (lane >> 4) * 8];
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) oacc[n] = mma_bf16(pf, vf[i % VQ][n], oacc[n]);
+    if (i + VQ < KBW) {
+      load_v(i + VQ, i % VQ);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // 1 / row sum (waves in a fixed order)
+  float inv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (lane >> 4) * 4 + r;
+    float L = s_sum[0][row];
+#pragma unroll
+    for (int v = 1; v < 8; ++v) L += s_sum[v][row];
+    inv[r] = 1.f / L;
+  }
+  if constexpr (KG == 1) {
+#pragma unroll
+    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_out[(lane >> 4) * 4 + r][(nbd0 + n) * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[n][r] * inv[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* o = &s_o[(kg * 16 + (lane >> 4) * 4 + r) * (DH + 4) + nbd0 * 16 + (lane & 15)];
+      *o = oacc[0][r] * inv[r];
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * DH; e += 512) {
+      const int row = e / DH, c = e % DH;
+      float v = 0.f;
+#pragma unroll
+      for (int g = 0; g < KG; ++g) v += s_o[(g * 16 + row) * (DH + 4) + c];
+      s_out[row][c] = (uint16_t)f2bf(v);
+    }
+  }
+  __syncthreads();
+  // packed stores, 8 head dims per thread
+  for (int i = tid; i < 2 * DH; i += 512) {
+    const int row = i / (DH / 8), c8 = (i % (DH / 8)) * 8;
+    const int qi = qb * 16 + row;
+    if (qi < nq) {
+      const int s = qi / G, h = j * G + qi % G;
+      *(uint4*)((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH)) = *(const uint4*)&s_out[row][c8];
+    }
+  }
+}
+
 // fp32 attention (small head dims): one workgroup per (robot, query head),
 // one thread per suffix row, online softmax over the padded logical keys.
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
@@ -684,17 +1267,15 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     for (int c = 0; c < Dh; ++c) { q[c] = qp[c]; o[c] = 0.f; }
     float m = -INFINITY, l = 0.f;
     for (int p = 0; p < ks.kp; ++p) {
-      if (!ks.valid(a, p)) continue;
-      const float* kp = ks.krow<float>(a, b, j, p);
-      const int p8 = p & ~7;
+      if (!ks.valid(p)) continue;
       float sc = 0.f;
-      for (int c = 0; c < Dh; ++c) sc += q[c] * kp[c];
+      for (int c = 0; c < Dh; ++c) sc += q[c] * ks.kel(j, p, c);
       sc *= a.scale;
       const float mn = fmaxf(m, sc);
       const float corr = (m == -INFINITY) ? 0.f : expf(m - mn);
       const float pe = expf(sc - mn);
       l = l * corr + pe;
-      for (int c = 0; c < Dh; ++c) o[c] = o[c] * corr + pe * ks.vcol<float>(a, b, j, p8, c)[p - p8];
+      for (int c = 0; c < Dh; ++c) o[c] = o[c] * corr + pe * ks.vel(j, p, c);
       m = mn;
     }
     for (int c = 0; c < Dh; ++c) ((float*)a.out)[pk(b * a.S + s, h * Dh + c, a.Hq * Dh)] = o[c] / l;
@@ -1001,26 +1582,29 @@ __global__ void k_bias_gemv(const void* w, int w_elt, const float* scales, int r
 // prefix K rows and V^T columns -> the padded physical layout, and the robot's (valid, head)
 template <typename T>
 __global__ void k_kv_copy(KvCopy c) {
-  const long HD = c.HD;
-  const long n8 = HD / 8;  // 16-byte chunks of a K row (bf16) / 32-byte (fp32): copy in 8-element units
+  constexpr bool packed = sizeof(T) == 2;
+  const int HD = c.HD, Dh = c.Dh, Hkv = HD / Dh;
+  const long n8 = HD / 8;  // K: 8-element units (contiguous in both layouts)
   const long total_k = (long)c.layers * c.n * n8;
   const long total_v = (long)c.layers * c.n * HD;
   const long stride = (long)gridDim.x * blockDim.x;
+  const long pitch = (long)c.TP * HD;  // elements per layer
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_k; i += stride) {
     const long l = i / (c.n * n8), rem = i % (c.n * n8);
-    const int t = (int)(rem / n8), c8 = (int)(rem % n8) * 8;
+    const int t = (int)(rem / n8), col = (int)(rem % n8) * 8;
     const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
-    const T* src = (const T*)c.k + (l * c.n + t) * HD + c8;
-    T* dst = (T*)c.kd + (l * c.TP + phys) * HD + c8;
+    const T* src = (const T*)c.k + (l * c.n + t) * HD + col;
+    T* dst = (T*)c.kd + l * pitch + kv_k_off(packed, c.TP, Hkv, Dh, col / Dh, phys, col % Dh);
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = src[e];
   }
-  // V^T: consecutive threads take consecutive tokens of one (layer, column)
+  // V: consecutive threads take consecutive tokens of one (layer, column)
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_v; i += stride) {
     const long l = i / (c.n * HD), rem = i % (c.n * HD);
     const int col = (int)(rem / c.n), t = (int)(rem % c.n);
     const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
-    ((T*)c.vtd)[(l * HD + col) * c.TP + phys] = ((const T*)c.v)[(l * c.n + t) * HD + col];
+    ((T*)c.vd)[l * pitch + kv_v_off(packed, c.TP, Hkv, Dh, col / Dh, phys, col % Dh)] =
+        ((const T*)c.v)[(l * c.n + t) * HD + col];
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     c.meta[2 * c.robot] = c.valid;
@@ -1057,9 +1641,25 @@ static hipError_t gemm_upw(const GemmArgs& g, int grid, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// large M, bf16: the LDS-staged MFMA GEMM (tile plan shared with the engine)
+static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err) {
+  const BigPlan p = big_plan(epi, g.M, g.N, g.K);
+  if (!p.used || g.ksplit != p.ks) return false;
+  const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN) * p.ks;
+  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8>), dim3(grid), dim3(256), 0, st, g);
+  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 4>), dim3(grid), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 4, 4>), dim3(grid), dim3(256), 0, st, g);
+  *err = hipGetLastError();
+  return true;
+}
+
 template <int ACT, int WT>
 static hipError_t gemm_dispatch(int epi, const GemmArgs& g, hipStream_t st) {
   const int nt = epi == EPI_GELU ? 32 : 16;
+  if constexpr (ACT == ELT_BF16 && WT == ELT_BF16) {
+    hipError_t e;
+    if (gemm_big(epi, g, st, &e)) return e;
+  }
   if (g.nt != nt || g.ksplit != 1) return hipErrorInvalidValue;
   const int grid = g.mtiles * (g.N / nt);
   if (epi == EPI_QKV) return gemm_upw<ACT, WT, EPI_QKV, 1>(g, grid, st);
@@ -1076,7 +1676,19 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
 
 template <int DH>
 static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
+  const int grid = a.B * a.Hkv * a.nqblk;
+  const int nk32 = (a.TP + a.SP) / 32;  // padded logical keys in 32-key blocks
+  switch ((nk32 + 3) / 4) {
+    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1>), grid, 512, a);
+    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2>), grid, 512, a);
+    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3>), grid, 512, a);
+    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4>), grid, 512, a);
+    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5>), grid, 512, a);
+    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6>), grid, 512, a);
+    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7>), grid, 512, a);
+    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8>), grid, 512, a);
+  }
+  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -96,7 +96,8 @@ typedef enum {
  *
  * The prefix holds prefix_static + n_frames * frame_tokens tokens per layer
  * per robot (the static region, then a ring of frames: Reflex abstract).
- * n_frames = 0 gives a static-only prefix.
+ * n_frames = 0 gives a static-only prefix; with n_frames > 0, frame_tokens
+ * must be a multiple of 32 (a frame fills whole 32-key attention tiles).
  *
  * weight_dtype: FM_F32 (act_dtype must be FM_F32), FM_BF16, or FM_FP8_E4M3
  *   (bf16 activations; the caller passes bf16 weights and the library

@@ -60,6 +60,7 @@ def _create(c):
     (lambda c: (setattr(c, "d_model", 96), setattr(c, "time_dim", 96)), _abi.FM_ERR_UNSUPPORTED),
     (lambda c: setattr(c, "action_dim", 7), _abi.FM_ERR_UNSUPPORTED),
     (lambda c: setattr(c, "n_frames", 2), _abi.FM_ERR_SHAPE),   # frames without frame_tokens
+    (lambda c: (setattr(c, "n_frames", 2), setattr(c, "frame_tokens", 16)), _abi.FM_ERR_UNSUPPORTED),  # frames % 32
     (lambda c: setattr(c, "rms_eps", float("nan")), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "exec_mode", 9), _abi.FM_ERR_ARG),
 ])

@@ -36,6 +36,10 @@ def test_tiny_fp32():
     dict(batch=3, chunk=7, state_dim=0, prefix_static=0, prefix_len=0),  # no state token, empty prefix
     dict(n_kv_heads=2, n_q_heads=4, n_layers=3, n_steps=4),  # 2 KV heads, other step count
     dict(n_q_heads=4, head_dim=256, d_mlp=2048, chunk=30, prefix_static=300, prefix_len=300),  # split-K GEMMs
+    dict(head_dim=32),                                       # attention: 4 key groups in P.V
+    dict(head_dim=128, prefix_static=1000, prefix_len=1000), # attention: 1016 padded keys, largest register tile
+    dict(prefix_static=1100, prefix_len=1100, chunk=9),      # attention: > 1024 keys, flash kernel
+    dict(batch=12, chunk=30, prefix_static=150, prefix_len=150),  # 372 rows: LDS-staged MFMA GEMMs, ragged m-tile
 ])
 def test_small_bf16(kw):
     cfg = small_cfg(**kw)
@@ -54,7 +58,8 @@ def test_small_prefix_shorter_than_capacity():
     check("prefix 37/64", got, O.denoise(cfg, W, k[:, :, :n], v[:, :, :n], x0, st), 1e-2, 3e-2)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(batch=4, chunk=25, prefix_static=90, prefix_len=90)])
+@pytest.mark.parametrize("kw", [dict(), dict(batch=4, chunk=25, prefix_static=90, prefix_len=90),
+                                dict(batch=10, chunk=40, prefix_static=64, prefix_len=64)])  # last: 400 rows, large-M GEMMs
 def test_small_ada(kw):
     cfg = small_cfg(norm="ada", time_dim=32, state_dim=0, **kw)
     announce(f"small_ada {kw}")
@@ -174,13 +179,13 @@ def _ring_run(cfg, ticks, oracle_ticks):
 
 
 def test_small_ring_fp8():
-    cfg = small_cfg(name="small_ring", weight_dtype="fp8", prefix_static=20, frame_tokens=16, n_frames=3,
-                    prefix_len=68, batch=2)
+    cfg = small_cfg(name="small_ring", weight_dtype="fp8", prefix_static=20, frame_tokens=32, n_frames=3,
+                    prefix_len=116, batch=2)
     _ring_run(cfg, ticks=9, oracle_ticks={0, 4, 8})
 
 
 def test_small_ring_bf16():
-    cfg = small_cfg(name="small_ring_bf16", prefix_static=5, frame_tokens=40, n_frames=4, prefix_len=165)
+    cfg = small_cfg(name="small_ring_bf16", prefix_static=5, frame_tokens=64, n_frames=3, prefix_len=197)
     _ring_run(cfg, ticks=6, oracle_ticks={5})
 
 
