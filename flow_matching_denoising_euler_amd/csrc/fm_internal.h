@@ -146,12 +146,13 @@ struct BigPlan {
   int BM, BN, ks;
 };
 inline BigPlan big_plan(int epi, int M, int N, int K) {
-  BigPlan p{false, 128, epi == EPI_GELU ? 256 : 128, 1};
+  // gate/up 128 x 256, QKV 128 x 128, residual 64 x 128 (their N is d_model,
+  // so smaller tiles and a 2-way K split to cover the CUs)
+  BigPlan p{false, epi == EPI_RESID ? 64 : 128, epi == EPI_GELU ? 256 : 128, 1};
   if (M < 256 || K % 64 || N % p.BN) return p;
   if (epi == EPI_RESID) {
     const int tiles = (M + p.BM - 1) / p.BM * (N / p.BN), stages = K / 64;
-    if (stages % 4 == 0 && tiles * 4 <= 256) p.ks = 4;
-    else if (stages % 2 == 0 && tiles * 2 <= 256) p.ks = 2;
+    if (stages % 2 == 0 && tiles * 2 <= 256) p.ks = 2;
   }
   p.used = true;
   return p;

@@ -1067,8 +1067,10 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 }
 
 // bf16 MFMA attention with the scores held in registers, for padded key
-// counts up to 1024.  Workgroup = 16 queries (suffix rows x heads of one KV
-// group) and 8 waves:
+// counts up to 1024.  Workgroup = QB blocks of 16 queries (suffix rows x
+// heads of one KV group) and 8 waves; the K and V fragments a wave loads
+// serve all QB query blocks (QB = 2 halves the K/V traffic of batched runs,
+// QB = 1 gives batch-1 runs twice the workgroups):
 //  1. wave w computes the scores of the 16-key blocks nb = w + 8 i (i < R)
 //     and keeps them in registers; its K fragments are streamed KQ blocks
 //     ahead of the MFMAs;
@@ -1077,35 +1079,37 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 //     bf16, zero for masked and padding keys;
 //  3. wave w computes O for its head-dim blocks (for DH < 128 also only a
 //     share of the keys, summed through LDS in a fixed order) from P and
-//     V^T fragments streamed VQ blocks ahead, scales by 1 / sum and stores.
+//     V fragments streamed VQ blocks ahead, scales by 1 / sum and stores.
 // Every global load of a phase is issued before its first use; there is no
 // online rescaling and, for DH >= 128, no merge of partial outputs.
-template <int DH, int R>
+template <int DH, int R, int QB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
-  constexpr int KBD = DH / 32, NBD = DH / 16;
+  constexpr int KBD = DH / 32, NBD = DH / 16, QR = 16 * QB;
   // K and V blocks in flight per wave, within about 240 registers
-  constexpr int KQ0 = (R <= 4 ? 24 : 16) / KBD, KQ = KQ0 < R ? KQ0 : R;
+  constexpr int KQ0 = (QB == 1 ? (R <= 4 ? 24 : 16) : (R <= 4 ? 16 : 8)) / KBD;
+  constexpr int KQ = KQ0 < 1 ? 1 : (KQ0 < R ? KQ0 : R);
   constexpr int KPAD = 128 * R + 8;                    // P row: keys of blocks nb < 8R, padded
   constexpr int NBW = NBD >= 8 ? NBD / 8 : 1;          // head-dim blocks per wave
   constexpr int KG = NBD >= 8 ? 1 : 8 / NBD;           // key groups of phase 3
   constexpr int KBW = 4 * R / KG;                      // 32-key blocks per wave in phase 3
-  constexpr int VQ0 = (R <= 3 ? 16 : 8) / NBW, VQ = VQ0 < KBW ? VQ0 : KBW;
-  __shared__ __align__(16) uint16_t sP[16][KPAD];
-  __shared__ float s_max[8][16], s_sum[8][16];
-  __shared__ __align__(16) float s_o[KG > 1 ? KG * 16 * (DH + 4) : 4];
-  __shared__ __align__(16) uint16_t s_out[16][DH + 8];
+  constexpr int VQ0 = (QB == 1 ? (R <= 3 ? 16 : 8) : 8) / NBW, VQ = VQ0 < KBW ? VQ0 : KBW;
+  __shared__ __align__(16) uint16_t sP[QR][KPAD];
+  __shared__ float s_max[8][QR], s_sum[8][QR];
+  __shared__ __align__(16) float s_o[KG > 1 ? KG * QR * (DH + 4) : 4];
+  __shared__ __align__(16) uint16_t s_out[QR][DH + 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qb = blockIdx.x % a.nqblk, jb = blockIdx.x / a.nqblk;
   const int j = jb % a.Hkv, b = jb / a.Hkv;
   const int G = a.Hq / a.Hkv, nq = a.S * G;
 
-  uint4 qf[KBD];
-  {
-    const int qi = min(qb * 16 + (lane & 15), nq - 1);
+  uint4 qf[QB][KBD];
+#pragma unroll
+  for (int u = 0; u < QB; ++u) {
+    const int qi = min((qb * QB + u) * 16 + (lane & 15), nq - 1);
     const int s = qi / G, h = j * G + qi % G;
     const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
 #pragma unroll
-    for (int kb = 0; kb < KBD; ++kb) qf[kb] = *(const uint4*)(qp + kb * 32);
+    for (int kb = 0; kb < KBD; ++kb) qf[u][kb] = *(const uint4*)(qp + kb * 32);
   }
   const KeySpace ks(a, b);
   const int nk16 = ks.kp >> 4, nk32 = ks.kp >> 5;  // kp is a multiple of 32
@@ -1132,13 +1136,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int i = 0; i < VQ; ++i) load_v(i, i);
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 sc[R];
+  f32x4 sc[R][QB];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KBD; ++kb) acc = mma_bf16(qf[kb], kf[i % KQ][kb], acc);
-    sc[i] = acc;
+    for (int u = 0; u < QB; ++u) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KBD; ++kb) acc = mma_bf16(qf[u][kb], kf[i % KQ][kb], acc);
+      sc[i][u] = acc;
+    }
     if (i + KQ < R) {
       load_k(i + KQ, i % KQ);
       __builtin_amdgcn_sched_barrier(0);
@@ -1146,65 +1153,86 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- 2. softmax over all keys: max, then exp and sums
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float mx[QB][4];
+#pragma unroll
+  for (int u = 0; u < QB; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx[u][r] = -INFINITY;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int key = (w + 8 * i) * 16 + (lane & 15);
     const bool ok = key < ks.kp && ks.valid(key);
 #pragma unroll
+    for (int u = 0; u < QB; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[i][u][r] = ok ? sc[i][u][r] * a.scale : -INFINITY;
+        mx[u][r] = fmaxf(mx[u][r], sc[i][u][r]);
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < QB; ++u)
+#pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[i][r] = ok ? sc[i][r] * a.scale : -INFINITY;
-      mx[r] = fmaxf(mx[r], sc[i][r]);
+      float m = mx[u][r];
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 8));
+      if ((lane & 15) == 0) s_max[w][u * 16 + (lane >> 4) * 4 + r] = m;
     }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 1));
-    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 2));
-    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 4));
-    mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 8));
-    if ((lane & 15) == 0) s_max[w][(lane >> 4) * 4 + r] = mx[r];
-  }
   __syncthreads();
-  float sm[4];
+  float sm[QB][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = (lane >> 4) * 4 + r;
-    float M = s_max[0][row];
+  for (int u = 0; u < QB; ++u)
 #pragma unroll
-    for (int v = 1; v < 8; ++v) M = fmaxf(M, s_max[v][row]);
-    mx[r] = M;
-    sm[r] = 0.f;
-  }
+    for (int r = 0; r < 4; ++r) {
+      const int row = u * 16 + (lane >> 4) * 4 + r;
+      float M = s_max[0][row];
+#pragma unroll
+      for (int v = 1; v < 8; ++v) M = fmaxf(M, s_max[v][row]);
+      mx[u][r] = M;
+      sm[u][r] = 0.f;
+    }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int key = (w + 8 * i) * 16 + (lane & 15);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = (mx[r] == -INFINITY) ? 0.f : __expf(sc[i][r] - mx[r]);
-      sm[r] += p;
-      sP[(lane >> 4) * 4 + r][key] = (uint16_t)f2bf(p);
-    }
+    for (int u = 0; u < QB; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = (mx[u][r] == -INFINITY) ? 0.f : __expf(sc[i][u][r] - mx[u][r]);
+        sm[u][r] += p;
+        sP[u * 16 + (lane >> 4) * 4 + r][key] = (uint16_t)f2bf(p);
+      }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    sm[r] += __shfl_xor(sm[r], 1);
-    sm[r] += __shfl_xor(sm[r], 2);
-    sm[r] += __shfl_xor(sm[r], 4);
-    sm[r] += __shfl_xor(sm[r], 8);
-    if ((lane & 15) == 0) s_sum[w][(lane >> 4) * 4 + r] = sm[r];
-  }
+  for (int u = 0; u < QB; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = sm[u][r];
+      t += __shfl_xor(t, 1);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 8);
+      if ((lane & 15) == 0) s_sum[w][u * 16 + (lane >> 4) * 4 + r] = t;
+    }
   __syncthreads();
 
   // ---- 3. O = P V for this wave's head-dim blocks and key group
-  f32x4 oacc[NBW];
+  f32x4 oacc[QB][NBW];
 #pragma unroll
-  for (int n = 0; n < NBW; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < QB; ++u)
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) oacc[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
-    const uint4 pf = *(const uint4*)&sP[lane & 15][(kg + KG * i) * 32 + (lane >> 4) * 8];
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) oacc[n] = mma_bf16(pf, vf[i % VQ][n], oacc[n]);
+    for (int u = 0; u < QB; ++u) {
+      const uint4 pf = *(const uint4*)&sP[u * 16 + (lane & 15)][(kg + KG * i) * 32 + (lane >> 4) * 8];
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) oacc[u][n] = mma_bf16(pf, vf[i % VQ][n], oacc[u][n]);
+    }
     if (i + VQ < KBW) {
       load_v(i + VQ, i % VQ);
       __builtin_amdgcn_sched_barrier(0);
@@ -1212,41 +1240,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // 1 / row sum (waves in a fixed order)
-  float inv[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = (lane >> 4) * 4 + r;
-    float L = s_sum[0][row];
-#pragma unroll
-    for (int v = 1; v < 8; ++v) L += s_sum[v][row];
-    inv[r] = 1.f / L;
-  }
-  if constexpr (KG == 1) {
-#pragma unroll
-    for (int n = 0; n < NBW; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s_out[(lane >> 4) * 4 + r][(nbd0 + n) * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[n][r] * inv[r]);
-  } else {
+  for (int u = 0; u < QB; ++u) {
+    float inv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float* o = &s_o[(kg * 16 + (lane >> 4) * 4 + r) * (DH + 4) + nbd0 * 16 + (lane & 15)];
-      *o = oacc[0][r] * inv[r];
+      const int row = u * 16 + (lane >> 4) * 4 + r;
+      float L = s_sum[0][row];
+#pragma unroll
+      for (int v = 1; v < 8; ++v) L += s_sum[v][row];
+      inv[r] = 1.f / L;
     }
+    if constexpr (KG == 1) {
+#pragma unroll
+      for (int n = 0; n < NBW; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_out[u * 16 + (lane >> 4) * 4 + r][(nbd0 + n) * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[u][n][r] * inv[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_o[(kg * QR + u * 16 + (lane >> 4) * 4 + r) * (DH + 4) + nbd0 * 16 + (lane & 15)] = oacc[u][0][r] * inv[r];
+    }
+  }
+  if constexpr (KG > 1) {
     __syncthreads();
-    for (int e = tid; e < 16 * DH; e += 512) {
+    for (int e = tid; e < QR * DH; e += 512) {
       const int row = e / DH, c = e % DH;
       float v = 0.f;
 #pragma unroll
-      for (int g = 0; g < KG; ++g) v += s_o[(g * 16 + row) * (DH + 4) + c];
+      for (int g = 0; g < KG; ++g) v += s_o[(g * QR + row) * (DH + 4) + c];
       s_out[row][c] = (uint16_t)f2bf(v);
     }
   }
   __syncthreads();
   // packed stores, 8 head dims per thread
-  for (int i = tid; i < 2 * DH; i += 512) {
+  for (int i = tid; i < 2 * QR * DH / 16; i += 512) {
     const int row = i / (DH / 8), c8 = (i % (DH / 8)) * 8;
-    const int qi = qb * 16 + row;
+    const int qi = qb * QR + row;
     if (qi < nq) {
       const int s = qi / G, h = j * G + qi % G;
       *(uint4*)((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH)) = *(const uint4*)&s_out[row][c8];
@@ -1648,7 +1679,7 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN) * p.ks;
   if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8>), dim3(grid), dim3(256), 0, st, g);
   else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 4>), dim3(grid), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 4, 4>), dim3(grid), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 4>), dim3(grid), dim3(256), 0, st, g);
   *err = hipGetLastError();
   return true;
 }
@@ -1674,21 +1705,31 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+template <int DH, int QB>
+static hipError_t attn_sf(AttnArgs a, int nk32, hipStream_t st) {
+  a.nqblk = (a.S * (a.Hq / a.Hkv) + 16 * QB - 1) / (16 * QB);
+  const int grid = a.B * a.Hkv * a.nqblk;
+  switch ((nk32 + 3) / 4) {
+    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB>), grid, 512, a);
+    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB>), grid, 512, a);
+    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB>), grid, 512, a);
+    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB>), grid, 512, a);
+    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB>), grid, 512, a);
+    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB>), grid, 512, a);
+    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB>), grid, 512, a);
+    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB>), grid, 512, a);
+  }
+  return hipErrorInvalidValue;
+}
+
+// up to 1024 padded keys: the register-resident kernel, two query blocks per
+// workgroup once one block per workgroup would exceed the 256 CUs; beyond:
+// the flash kernel
 template <int DH>
 static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
-  const int grid = a.B * a.Hkv * a.nqblk;
   const int nk32 = (a.TP + a.SP) / 32;  // padded logical keys in 32-key blocks
-  switch ((nk32 + 3) / 4) {
-    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1>), grid, 512, a);
-    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2>), grid, 512, a);
-    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3>), grid, 512, a);
-    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4>), grid, 512, a);
-    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5>), grid, 512, a);
-    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6>), grid, 512, a);
-    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7>), grid, 512, a);
-    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8>), grid, 512, a);
-  }
-  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(grid), dim3(256), 0, st, a);
+  if (nk32 <= 32) return a.B * a.Hkv * a.nqblk > 256 ? attn_sf<DH, 2>(a, nk32, st) : attn_sf<DH, 1>(a, nk32, st);
+  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

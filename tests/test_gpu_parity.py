@@ -40,6 +40,7 @@ def test_tiny_fp32():
     dict(head_dim=128, prefix_static=1000, prefix_len=1000), # attention: 1016 padded keys, largest register tile
     dict(prefix_static=1100, prefix_len=1100, chunk=9),      # attention: > 1024 keys, flash kernel
     dict(batch=12, chunk=30, prefix_static=150, prefix_len=150),  # 372 rows: LDS-staged MFMA GEMMs, ragged m-tile
+    dict(batch=20, chunk=60, n_q_heads=8, prefix_static=100, prefix_len=100),  # attention: 2 query blocks/workgroup
 ])
 def test_small_bf16(kw):
     cfg = small_cfg(**kw)
