@@ -550,14 +550,16 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   return make_uint2(f2bf(a) | (f2bf(b) << 16), f2bf(c) | (f2bf(d) << 16));
 }
 
-// Copies of one stage.  Fragment f = wave + 4 i of a stage: the first
-// MB * KS are activations (k-block f / MB, row block f % MB), the rest
-// weights; since MB * KS is a multiple of 4, loop index i < TMW gives
-// activations.  src[i] is this lane's source of fragment i in the split's
-// first stage; stage sc (relative) adds sc * stride (A or W).
-template <int TMW, int TNW>
+// Copies of one stage (BIG_KS k-blocks) by the NW waves of a workgroup.
+// Fragment f = wave + NW i of a stage: the first MB * KS are activations
+// (k-block f / MB, row block f % MB), the rest weights; since MB * KS is a
+// multiple of NW, loop index i < MB * KS / NW gives activations.  src[i] is
+// this lane's source of fragment i in the split's first stage; stage sc
+// (relative) adds sc * stride (A or W).
+template <int TMW, int TNW, int NW>
 struct BigSrc {
-  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, LPW = (MB + NBK) * BIG_KS / 4;
+  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, LPW = (MB + NBK) * BIG_KS / NW, LA = MB * BIG_KS / NW;
+  static_assert((MB * BIG_KS) % NW == 0 && (NBK * BIG_KS) % NW == 0, "fragments split evenly over the waves");
   const uint16_t* src[LPW];
   long stride_a, stride_w;  // elements per stage
   __device__ __forceinline__ BigSrc(const uint16_t* A, const uint16_t* W, int wave, int lane, int st0, int rb0,
@@ -566,8 +568,8 @@ struct BigSrc {
     stride_w = (long)BIG_KS * NBT * 512;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int f = wave + 4 * i;
-      if (i < TMW) {
+      const int f = wave + NW * i;
+      if (i < LA) {
         const int qk = f / MB, mi = f % MB;
         const int rb = min(rb0 + mi, RB - 1), kb = st0 * BIG_KS + qk;
         src[i] = A + ((((long)(rb >> 2) * KB + kb) * 4 + (rb & 3)) * 64 + lane) * 8;
@@ -580,43 +582,75 @@ struct BigSrc {
   __device__ __forceinline__ void issue(uint32_t base, int wave, int sc) const {
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
-      lds_dma16(src[i] + sc * (i < TMW ? stride_a : stride_w), base + (uint32_t)(wave + 4 * i) * 1024u);
+      lds_dma16(src[i] + sc * (i < LA ? stride_a : stride_w), base + (uint32_t)(wave + NW * i) * 1024u);
   }
 };
-// acc[ni][mi] += W(column block) x A(row block)^T over the stage
+// The fragments of k-block qk of a stage for wave (wm, wn)
 template <int TMW, int TNW>
-__device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TNW][TMW], int wm, int wn, int lane) {
+__device__ __forceinline__ void big_read(const uint8_t* base, int qk, uint4 (&af)[TMW], uint4 (&bf)[TNW], int wm,
+                                         int wn, int lane) {
   constexpr int MB = 2 * TMW, NBK = 2 * TNW;
 #pragma unroll
-  for (int qk = 0; qk < BIG_KS; ++qk) {
+  for (int mi = 0; mi < TMW; ++mi) af[mi] = *(const uint4*)(base + (qk * MB + wm * TMW + mi) * 1024 + lane * 16);
+#pragma unroll
+  for (int ni = 0; ni < TNW; ++ni)
+    bf[ni] = *(const uint4*)(base + (MB * BIG_KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
+}
+// acc[ni][mi] += W(column block) x A(row block)^T over the k-blocks of the
+// stage this wave takes: all BIG_KS of them (KG = 1), or k-block kg (KG = 2,
+// one k-group per half of the workgroup).  With KG = 1 the fragments of
+// k-block qk + 1 are read while the MFMAs of qk run; the scheduling barriers
+// keep the reads ahead of the MFMAs.
+template <int TMW, int TNW, int KG>
+__device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TNW][TMW], int kg, int wm, int wn,
+                                            int lane) {
+  if constexpr (KG == 2) {
     uint4 af[TMW], bf[TNW];
-#pragma unroll
-    for (int mi = 0; mi < TMW; ++mi) af[mi] = *(const uint4*)(base + (qk * MB + wm * TMW + mi) * 1024 + lane * 16);
-#pragma unroll
-    for (int ni = 0; ni < TNW; ++ni)
-      bf[ni] = *(const uint4*)(base + (MB * BIG_KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
+    big_read<TMW, TNW>(base, kg, af, bf, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ni = 0; ni < TNW; ++ni)
 #pragma unroll
       for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = mma_bf16(bf[ni], af[mi], acc[ni][mi]);
+  } else {
+    uint4 af[2][TMW], bf[2][TNW];
+    big_read<TMW, TNW>(base, 0, af[0], bf[0], wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qk = 0; qk < BIG_KS; ++qk) {
+      if (qk + 1 < BIG_KS) {
+        big_read<TMW, TNW>(base, qk + 1, af[(qk + 1) & 1], bf[(qk + 1) & 1], wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int ni = 0; ni < TNW; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = mma_bf16(bf[qk & 1][ni], af[qk & 1][mi], acc[ni][mi]);
+    }
   }
 }
 
-template <int EPI, int TMW, int TNW>
-__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
+// KG k-groups of 4 waves (KG = 2: 512 threads, two waves per SIMD to keep
+// more LDS reads in flight; the halves sum their accumulators through LDS in
+// a fixed order and each runs the epilogue of half the row blocks).
+template <int EPI, int TMW, int TNW, int KG>
+__global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
+  constexpr int NT = 256 * KG, NW = 4 * KG;
   constexpr int MB = 2 * TMW, NBK = 2 * TNW;          // row / column blocks of the tile
   constexpr int BM = 16 * MB, BN = 16 * NBK;
   constexpr int FPS = (MB + NBK) * BIG_KS;            // fragments per stage
-  constexpr int LPW = FPS / 4;                        // copies per wave per stage
+  constexpr int LPW = FPS / NW;                       // copies per wave per stage
   constexpr int NJ = TNW * TMW;                       // accumulator blocks per wave
-  static_assert((MB * BIG_KS) % 4 == 0 && BIG_STAGES == 3, "stage split");
+  constexpr int TME = TMW / KG;                       // row blocks of this wave's epilogue
+  static_assert(KG == 1 || (KG == 2 && EPI != EPI_RESID && TMW % 2 == 0), "k-groups: no split K, even row blocks");
+  static_assert(BM * 8 % NT == 0, "norm-statistics pass");
   __shared__ __align__(16) uint8_t lds0[FPS * 1024], lds1[FPS * 1024], lds2[FPS * 1024];
   __shared__ float s_rstd[BM];
   __shared__ __align__(16) float s_col[2][BN];        // bias or alpha, gnext
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: fragment choice and LDS address are scalar
-  const int wm = wave >> 1, wn = wave & 1;
+  const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = g.N / BN, T = tiles_m * tiles_n;
   const int ks = blockIdx.x % g.ksplit;
   // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
@@ -639,21 +673,26 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
                            : g.bias.base[(long)g.step * g.bias.step_stride + col];
     cv1 = EPI == EPI_RESID ? g.gnext.base[(long)g.step * g.gnext.step_stride + col] : 0.f;
   }
-  float4 q[4][BM / 32];
+  constexpr int RP = BM * 8 / NT;  // rows per thread group pass: 8 threads per row, 16 slots each
+  float4 q[4][RP];
   if (EPI != EPI_RESID) {
-    // 8 threads per row, 16 slots each (the skinny kernel's order)
 #pragma unroll
-    for (int rr = 0; rr < BM / 32; ++rr) {
-      const int row = min(m0 + rr * 32 + (tid >> 3), g.M - 1);
+    for (int rr = 0; rr < RP; ++rr) {
+      const int row = min(m0 + rr * (NT / 8) + (tid >> 3), g.M - 1);
       const float4* p = (const float4*)(g.ssq + (long)row * PM + (tid & 7) * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[i][rr] = p[i];
     }
   }
-  const BigSrc<TMW, TNW> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
+  const BigSrc<TMW, TNW, NW> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
   const uint32_t a0 = lds_addr(lds0), a1 = lds_addr(lds1), a2 = lds_addr(lds2);
-  srcs.issue(a0, wave, 0);
-  srcs.issue(a1, wave, min(1, nstage - 1));
+  // Rotated k order: the tiles that share weight columns (same tn) start at
+  // stages spread over K, so the workgroups of an XCD touch different
+  // k-slices at a time.  The order is fixed per tile (deterministic).
+  const int rot = (tm * nstage / tiles_m + 3 * tn) % nstage;
+  auto kst = [&](int s2) { const int r = min(s2, nstage - 1) + rot; return r >= nstage ? r - nstage : r; };
+  srcs.issue(a0, wave, kst(0));
+  srcs.issue(a1, wave, kst(1));
 
   f32x4 acc[TNW][TMW];
 #pragma unroll
@@ -665,26 +704,61 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
   // it, barrier (everyone's copies landed, everyone is done with stage
   // s - 1), refill the slot of stage s - 1 with stage s + 2 (past the end: a
   // harmless reload of the last stage), compute stage s
-  const int last = nstage - 1;
   for (int s = 0; s < nstage; s += 3) {
     wait_vmcnt<LPW>();
     barrier_nofence();
-    srcs.issue(a2, wave, min(s + 2, last));
-    big_compute<TMW, TNW>(lds0, acc, wm, wn, lane);
+    srcs.issue(a2, wave, kst(s + 2));
+    big_compute<TMW, TNW, KG>(lds0, acc, kg, wm, wn, lane);
     if (s + 1 < nstage) {
       wait_vmcnt<LPW>();
       barrier_nofence();
-      srcs.issue(a0, wave, min(s + 3, last));
-      big_compute<TMW, TNW>(lds1, acc, wm, wn, lane);
+      srcs.issue(a0, wave, kst(s + 3));
+      big_compute<TMW, TNW, KG>(lds1, acc, kg, wm, wn, lane);
     }
     if (s + 2 < nstage) {
       wait_vmcnt<LPW>();
       barrier_nofence();
-      srcs.issue(a1, wave, min(s + 4, last));
-      big_compute<TMW, TNW>(lds2, acc, wm, wn, lane);
+      srcs.issue(a1, wave, kst(s + 4));
+      big_compute<TMW, TNW, KG>(lds2, acc, kg, wm, wn, lane);
     }
   }
   wait_vmcnt<0>();  // the trailing reloads
+
+  // k-groups: each half sends the row blocks the other half finishes (one
+  // 16-byte accumulator slice per lane and block), then adds the received
+  // slice as acc(k-group 0) + acc(k-group 1) in both halves
+  f32x4 fin[TNW][TME];
+  if constexpr (KG == 2) {
+    constexpr int RS = TNW * TME * 1024;               // bytes one wave sends
+    constexpr int PER = FPS * 1024 / RS;               // send regions per ring slot
+    static_assert(PER * 3 >= 8, "exchange fits in the ring");
+    __syncthreads();                                    // every wave is done reading the ring
+    auto region = [&](int w) -> uint8_t* {
+      uint8_t* base = w / PER == 0 ? lds0 : (w / PER == 1 ? lds1 : lds2);
+      return base + (w % PER) * RS;
+    };
+    uint8_t* out = region(wave);
+#pragma unroll
+    for (int ni = 0; ni < TNW; ++ni)
+#pragma unroll
+      for (int m = 0; m < TME; ++m)
+        *(f32x4*)(out + (ni * TME + m) * 1024 + lane * 16) = kg == 0 ? acc[ni][TME + m] : acc[ni][m];
+    __syncthreads();
+    const uint8_t* in = region(wave ^ 4);
+#pragma unroll
+    for (int ni = 0; ni < TNW; ++ni)
+#pragma unroll
+      for (int m = 0; m < TME; ++m) {
+        const f32x4 other = *(const f32x4*)(in + (ni * TME + m) * 1024 + lane * 16);
+        fin[ni][m] = kg == 0 ? acc[ni][m] + other : other + acc[ni][TME + m];
+      }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < TNW; ++ni)
+#pragma unroll
+      for (int m = 0; m < TME; ++m) fin[ni][m] = acc[ni][m];
+  }
+  const int mb0 = kg * TME;  // first row block of this wave's epilogue (KG = 2: by k-group)
 
   // split K: every workgroup stores its partial tile; the last to arrive
   // adds the partials in split order and goes on to the epilogue
@@ -692,7 +766,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
     float* mine = g.partials + (((long)t * g.ksplit + ks) * NJ * 256 + tid) * 4;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const f32x4 v = acc[j / TMW][j % TMW];
+      const f32x4 v = fin[j / TMW][j % TMW];
       st_dev2(mine + j * 1024, v[0], v[1]);
       st_dev2(mine + j * 1024 + 2, v[2], v[3]);
     }
@@ -718,20 +792,20 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
       f32x4 va[NJ], vb[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const float2 a0 = ld_dev2(pa + j * 1024), a1 = ld_dev2(pa + j * 1024 + 2);
-        const float2 b0 = ld_dev2(pb + j * 1024), b1 = ld_dev2(pb + j * 1024 + 2);
-        va[j] = f32x4{a0.x, a0.y, a1.x, a1.y};
-        vb[j] = f32x4{b0.x, b0.y, b1.x, b1.y};
+        const float2 x0 = ld_dev2(pa + j * 1024), x1 = ld_dev2(pa + j * 1024 + 2);
+        const float2 y0 = ld_dev2(pb + j * 1024), y1 = ld_dev2(pb + j * 1024 + 2);
+        va[j] = f32x4{x0.x, x0.y, x1.x, x1.y};
+        vb[j] = f32x4{y0.x, y0.y, y1.x, y1.y};
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const f32x4 own = acc[j / TMW][j % TMW];
+        const f32x4 own = fin[j / TMW][j % TMW];
         sum[j] += (k0 == ks) ? own : va[j];
         if (k0 + 1 < g.ksplit) sum[j] += (k0 + 1 == ks) ? own : vb[j];
       }
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j / TMW][j % TMW] = sum[j];
+    for (int j = 0; j < NJ; ++j) fin[j / TMW][j % TMW] = sum[j];
   }
 
   // the epilogue's LDS tables
@@ -741,28 +815,28 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
   }
   if (EPI != EPI_RESID) {
 #pragma unroll
-    for (int rr = 0; rr < BM / 32; ++rr) {
+    for (int rr = 0; rr < RP; ++rr) {
       float sq = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sq += ((q[i][rr].x + q[i][rr].y) + q[i][rr].z) + q[i][rr].w;
       sq += __shfl_xor(sq, 1);
       sq += __shfl_xor(sq, 2);
       sq += __shfl_xor(sq, 4);
-      const int r = rr * 32 + (tid >> 3);
+      const int r = rr * (NT / 8) + (tid >> 3);
       if ((tid & 7) == 0) s_rstd[r] = (m0 + r < g.M) ? rsqrtf(sq * g.inv_d + g.eps) : 0.f;
     }
   }
   __syncthreads();
 
-  // epilogue: block (ni, mi) of this lane = row m0 + (wm TMW + mi) 16 + (lane & 15),
+  // epilogue: block (ni, m) of this lane = row m0 + (wm TMW + mb0 + m) 16 + (lane & 15),
   // columns n0 + (wn TNW + ni) 16 + (lane >> 4) 4 + [0, 4)
   const int c4 = (lane >> 4) * 4;
   if constexpr (EPI == EPI_QKV) {
     const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
     const int dsh = __builtin_ctz(g.Dh);  // head_dim is 32, 64, 128 or 256 on the bf16 path
 #pragma unroll
-    for (int mi = 0; mi < TMW; ++mi) {
-      const int rt = (wm * TMW + mi) * 16 + (lane & 15), row = m0 + rt;
+    for (int m = 0; m < TME; ++m) {
+      const int rt = (wm * TMW + mb0 + m) * 16 + (lane & 15), row = m0 + rt;
       if (row >= g.M) continue;
       const float rs = s_rstd[rt];
       const int b = row / g.S, sr = row % g.S;
@@ -771,7 +845,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
       for (int ni = 0; ni < TNW; ++ni) {
         const int ct = (wn * TNW + ni) * 16 + c4, col = n0 + ct;
         const float4 bias = *(const float4*)&s_col[0][ct];
-        const f32x4 a = acc[ni][mi];
+        const f32x4 a = fin[ni][m];
         const float v0 = a[0] * rs + bias.x, v1 = a[1] * rs + bias.y, v2 = a[2] * rs + bias.z, v3 = a[3] * rs + bias.w;
         if (col < kcol0) {
           *(uint2*)((uint16_t*)g.out + (long)row * g.N + col) = pack4_bf16(v0, v1, v2, v3);
@@ -793,15 +867,15 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
     static_assert(TNW % 2 == 0, "gate/up pairs");
     const int F = g.N >> 1;
 #pragma unroll
-    for (int mi = 0; mi < TMW; ++mi) {
-      const int rt = (wm * TMW + mi) * 16 + (lane & 15), row = m0 + rt;
+    for (int m = 0; m < TME; ++m) {
+      const int rt = (wm * TMW + mb0 + m) * 16 + (lane & 15), row = m0 + rt;
       if (row >= g.M) continue;
       const float rs = s_rstd[rt];
 #pragma unroll
       for (int pi = 0; pi < TNW / 2; ++pi) {
         const int cg = (wn * TNW + 2 * pi) * 16 + c4;
         const float4 bg = *(const float4*)&s_col[0][cg], bu = *(const float4*)&s_col[0][cg + 16];
-        const f32x4 ga = acc[2 * pi][mi], ua = acc[2 * pi + 1][mi];
+        const f32x4 ga = fin[2 * pi][m], ua = fin[2 * pi + 1][m];
         const float z0 = gelu_erf(ga[0] * rs + bg.x) * (ua[0] * rs + bu.x);
         const float z1 = gelu_erf(ga[1] * rs + bg.y) * (ua[1] * rs + bu.y);
         const float z2 = gelu_erf(ga[2] * rs + bg.z) * (ua[2] * rs + bu.z);
@@ -811,23 +885,23 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
       }
     }
   } else {  // EPI_RESID: h += alpha * acc; u = act(h * gnext); h^2 partials per 16 columns
-    float4 hv[TMW][TNW];
+    float4 hv[TME][TNW];
 #pragma unroll
-    for (int mi = 0; mi < TMW; ++mi) {
-      const int row = min(m0 + (wm * TMW + mi) * 16 + (lane & 15), g.M - 1);
+    for (int m = 0; m < TME; ++m) {
+      const int row = min(m0 + (wm * TMW + mb0 + m) * 16 + (lane & 15), g.M - 1);
 #pragma unroll
       for (int ni = 0; ni < TNW; ++ni)
-        hv[mi][ni] = *(const float4*)(g.h + (long)row * g.N + n0 + (wn * TNW + ni) * 16 + c4);
+        hv[m][ni] = *(const float4*)(g.h + (long)row * g.N + n0 + (wn * TNW + ni) * 16 + c4);
     }
 #pragma unroll
-    for (int mi = 0; mi < TMW; ++mi) {
-      const int row = m0 + (wm * TMW + mi) * 16 + (lane & 15);
+    for (int m = 0; m < TME; ++m) {
+      const int row = m0 + (wm * TMW + mb0 + m) * 16 + (lane & 15);
 #pragma unroll
       for (int ni = 0; ni < TNW; ++ni) {
         const int ct = (wn * TNW + ni) * 16 + c4, col = n0 + ct;
         const float4 al = *(const float4*)&s_col[0][ct], gn = *(const float4*)&s_col[1][ct];
-        const f32x4 a = acc[ni][mi];
-        const float4 h = hv[mi][ni];
+        const f32x4 a = fin[ni][m];
+        const float4 h = hv[m][ni];
         const float4 hn = make_float4(h.x + al.x * a[0], h.y + al.y * a[1], h.z + al.z * a[2], h.w + al.w * a[3]);
         float qq = ((hn.x * hn.x + hn.y * hn.y) + hn.z * hn.z) + hn.w * hn.w;
         qq += __shfl_xor(qq, 16);
@@ -1677,9 +1751,9 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   const BigPlan p = big_plan(epi, g.M, g.N, g.K);
   if (!p.used || g.ksplit != p.ks) return false;
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN) * p.ks;
-  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8>), dim3(grid), dim3(256), 0, st, g);
-  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 4>), dim3(grid), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 4>), dim3(grid), dim3(256), 0, st, g);
+  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2>), dim3(grid), dim3(512), 0, st, g);
+  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 4, 2>), dim3(grid), dim3(512), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 4, 1>), dim3(grid), dim3(256), 0, st, g);
   *err = hipGetLastError();
   return true;
 }
