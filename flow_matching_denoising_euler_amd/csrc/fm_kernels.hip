@@ -686,11 +686,10 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   }
   const BigSrc<TMW, TNW, NW> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
   const uint32_t a0 = lds_addr(lds0), a1 = lds_addr(lds1), a2 = lds_addr(lds2);
-  // Rotated k order: the tiles that share weight columns (same tn) start at
-  // stages spread over K, so the workgroups of an XCD touch different
-  // k-slices at a time.  The order is fixed per tile (deterministic).
-  const int rot = (tm * nstage / tiles_m + 3 * tn) % nstage;
-  auto kst = [&](int s2) { const int r = min(s2, nstage - 1) + rot; return r >= nstage ? r - nstage : r; };
+  // The workgroups of an XCD walk K together, so each k-slice of their
+  // operands is fetched into that XCD's L2 once and only a few stages of it
+  // need to stay resident.
+  auto kst = [&](int s2) { return min(s2, nstage - 1); };
   srcs.issue(a0, wave, kst(0));
   srcs.issue(a1, wave, kst(1));
 
@@ -1172,7 +1171,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __align__(16) float s_o[KG > 1 ? KG * QR * (DH + 4) : 4];
   __shared__ __align__(16) uint16_t s_out[QR][DH + 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int qb = blockIdx.x % a.nqblk, jb = blockIdx.x / a.nqblk;
+  // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
+  // a contiguous range of (robot, kv head, query block), so a robot's K/V
+  // are fetched into one XCD's L2 rather than into all eight
+  int wg = blockIdx.x;
+  const int q8 = gridDim.x / 8;
+  if (wg < 8 * q8) wg = (wg % 8) * q8 + wg / 8;
+  const int qb = wg % a.nqblk, jb = wg / a.nqblk;
   const int j = jb % a.Hkv, b = jb / a.Hkv;
   const int G = a.Hq / a.Hkv, nq = a.S * G;
 
