@@ -207,13 +207,17 @@ void derive(fm_ctx* x) {
   }
   x->nqblk = (x->S * (x->Hq / x->Hkv) + 15) / 16;
   {
-    // key ranges: about 64 workgroups or more, each range >= 64 keys
-    const int keys = x->TP + x->SP;
+    // Attention key split (bf16, head_dim >= 128, few query groups): the
+    // padded keys are cut into nsplit ranges of kps 16-key blocks (even, so
+    // ranges start on 32-key blocks), each range one workgroup, merged by the
+    // last to arrive.  Batch-1 grids have a few dozen query groups and each
+    // workgroup would otherwise pull the whole prefix through one CU.
+    const int nk16 = (x->TP + x->SP) / 16;
     const int groups = x->B * x->Hkv * x->nqblk;
-    int ns = std::min(std::min((keys + 63) / 64, (64 + groups - 1) / groups), 16);
-    x->nsplit = std::max(1, ns);
-    x->kps = ((keys + x->nsplit - 1) / x->nsplit + 31) / 32 * 32;
-    x->nsplit = (keys + x->kps - 1) / x->kps;
+    int ns = 1;  // below 512 keys the merge costs more than the fill it saves; at most 4 ranges
+    if (x->act == ELT_BF16 && x->Dh >= 128 && groups <= 64 && nk16 > 32) ns = std::min(4, (nk16 + 13) / 14);
+    x->kps = ((nk16 + ns - 1) / ns + 1) / 2 * 2;
+    x->nsplit = (nk16 + x->kps - 1) / x->kps;
   }
 }
 
@@ -278,9 +282,8 @@ void carve(fm_ctx* x, Arena& a) {
   const long ks = std::max(x->ks_o, x->ks_d);
   const long Mp128 = (x->M + 127) / 128 * 128;  // rows covered by the large-M tiles
   x->partials = (float*)a.take(ks > 1 ? ks * Mp128 * d * 4 : 16);
-  x->attn_part = (float*)a.take(x->act == ELT_F32 || x->nsplit == 1
-                                    ? 16
-                                    : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 64 * (x->Dh + 2) * 4);
+  // per (query group, key range): 16 rows x Dh partial output, row max, row sum
+  x->attn_part = (float*)a.take(x->nsplit == 1 ? 16 : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 2) * 4);
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
                                    (size_t)x->B * x->Hkv * x->nqblk) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);

@@ -87,10 +87,11 @@ struct AttnArgs {
   const int* meta;        // [B][2] = (valid prefix tokens, ring head)
   int B, S, SP, Hq, Hkv, Dh, Nqkv;
   int n_static, NSP, TP, frame_tokens, n_frames, ring;
-  int nqblk, nsplit;      // query blocks of 64 per (b, kv head); key ranges
-  int keys_per_split;     // padded logical keys per range (multiple of 32)
+  int nqblk;              // query blocks of 16 per (b, kv head)
+  int nsplit;             // key ranges per query block (merged by the last to arrive)
+  int keys_per_split;     // 16-key blocks per range (even)
   float scale;
-  float* part;            // partials
+  float* part;            // key-range partials: per (query group, range) 16 x Dh outputs, 16 maxima, 16 sums
   unsigned* counters;
   void* out;              // [B*S][Hq*Dh] act
 };

@@ -1170,6 +1170,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float s_max[8][QR], s_sum[8][QR];
   __shared__ __align__(16) float s_o[KG > 1 ? KG * QR * (DH + 4) : 4];
   __shared__ __align__(16) uint16_t s_out[QR][DH + 8];
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
   // a contiguous range of (robot, kv head, query block), so a robot's K/V
@@ -1177,7 +1178,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int wg = blockIdx.x;
   const int q8 = gridDim.x / 8;
   if (wg < 8 * q8) wg = (wg % 8) * q8 + wg / 8;
-  const int qb = wg % a.nqblk, jb = wg / a.nqblk;
+  const int sp = wg % a.nsplit, grp = wg / a.nsplit;  // key range, query group
+  const int qb = grp % a.nqblk, jb = grp / a.nqblk;
   const int j = jb % a.Hkv, b = jb / a.Hkv;
   const int G = a.Hq / a.Hkv, nq = a.S * G;
 
@@ -1192,11 +1194,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const KeySpace ks(a, b);
   const int nk16 = ks.kp >> 4, nk32 = ks.kp >> 5;  // kp is a multiple of 32
+  // this workgroup's key range: 16-key blocks [kb0, kb0 + keys_per_split)
+  // (one range covers all keys unless the key split is on); its local key
+  // index is the P column
+  const int kb0 = sp * a.keys_per_split;
+  const int kend = min((kb0 + a.keys_per_split) * 16, ks.kp);
 
   // ---- 1. scores of this wave's key blocks
   uint4 kf[KQ][KBD];
   auto load_k = [&](int i, int slot) {
-    const int nb = min(w + 8 * i, nk16 - 1);
+    const int nb = min(kb0 + w + 8 * i, nk16 - 1);
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb) kf[slot][kb] = *(const uint4*)ks.ktile(j, nb, kb, lane);
   };
@@ -1206,7 +1213,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kg = w / (8 / KG), nbd0 = (w % (8 / KG)) * NBW;
   uint4 vf[VQ][NBW];
   auto load_v = [&](int i, int slot) {
-    const int kb32 = min(kg + KG * i, nk32 - 1);
+    const int kb32 = min((kb0 >> 1) + kg + KG * i, nk32 - 1);
 #pragma unroll
     for (int n = 0; n < NBW; ++n) vf[slot][n] = *(const uint4*)ks.vtile(j, kb32, nbd0 + n, lane);
   };
@@ -1239,8 +1246,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 4; ++r) mx[u][r] = -INFINITY;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const int key = (w + 8 * i) * 16 + (lane & 15);
-    const bool ok = key < ks.kp && ks.valid(key);
+    const int key = (kb0 + w + 8 * i) * 16 + (lane & 15);
+    const bool ok = key < kend && ks.valid(key);
 #pragma unroll
     for (int u = 0; u < QB; ++u)
 #pragma unroll
@@ -1316,6 +1323,95 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       load_v(i + VQ, i % VQ);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // key split: every range stores its unnormalised output, row maxima and
+  // row sums (device scope); the last range to arrive merges them in range
+  // order, O = sum_r e^(m_r - M) O_r / sum_r e^(m_r - M) l_r
+  if constexpr (QB == 1 && KG == 1) if (a.nsplit > 1) {
+    constexpr int PO = 8 * NBW * 64 * 4;  // floats of partial output per range (= 16 x DH)
+    float* mine = a.part + ((long)grp * a.nsplit + sp) * (PO + 32);
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) {
+      float* o = mine + ((w * NBW + n) * 64 + lane) * 4;
+      st_dev2(o, oacc[0][n][0], oacc[0][n][1]);
+      st_dev2(o + 2, oacc[0][n][2], oacc[0][n][3]);
+    }
+    if (w == 0 && (lane & 15) == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const int row = (lane >> 4) * 4 + r;
+        float L0 = s_sum[0][row], L1 = s_sum[0][row + 1];
+#pragma unroll
+        for (int v = 1; v < 8; ++v) { L0 += s_sum[v][row]; L1 += s_sum[v][row + 1]; }
+        st_dev2(mine + PO + row, mx[0][r], mx[0][r + 1]);
+        st_dev2(mine + PO + 16 + row, L0, L1);
+      }
+    }
+    drain_vm();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(a.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)a.nsplit - 1;
+      if (s_last) __hip_atomic_store(a.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // every range's statistics and output slice (up to 4 ranges), all loads
+    // issued first
+    constexpr int MAXS = 4;
+    float pm[MAXS][4], pl[MAXS][4];
+    f32x4 po[MAXS][NBW];
+#pragma unroll
+    for (int r2 = 0; r2 < MAXS; ++r2) {
+      const float* src = a.part + ((long)grp * a.nsplit + min(r2, a.nsplit - 1)) * (PO + 32);
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const float2 m2 = ld_dev2(src + PO + (lane >> 4) * 4 + r), l2 = ld_dev2(src + PO + 16 + (lane >> 4) * 4 + r);
+        pm[r2][r] = m2.x; pm[r2][r + 1] = m2.y;
+        pl[r2][r] = l2.x; pl[r2][r + 1] = l2.y;
+      }
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) {
+        const float* o = src + ((w * NBW + n) * 64 + lane) * 4;
+        const float2 x0 = ld_dev2(o), x1 = ld_dev2(o + 2);
+        po[r2][n] = f32x4{x0.x, x0.y, x1.x, x1.y};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float M = pm[0][r];
+#pragma unroll
+      for (int r2 = 1; r2 < MAXS; ++r2) M = r2 < a.nsplit ? fmaxf(M, pm[r2][r]) : M;
+      float L = 0.f, on[NBW];
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) on[n] = 0.f;
+#pragma unroll
+      for (int r2 = 0; r2 < MAXS; ++r2) {
+        const float e = (r2 < a.nsplit && pm[r2][r] != -INFINITY) ? __expf(pm[r2][r] - M) : 0.f;
+        L += e * pl[r2][r];
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) on[n] += e * po[r2][n][r];
+      }
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) oacc[0][n][r] = on[n] * inv;
+    }
+#pragma unroll
+    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_out[(lane >> 4) * 4 + r][(nbd0 + n) * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[0][n][r]);
+    __syncthreads();
+    for (int i = tid; i < 2 * DH; i += 512) {
+      const int row = i / (DH / 8), c8 = (i % (DH / 8)) * 8;
+      const int qi = qb * 16 + row;
+      if (qi < nq) {
+        const int s2 = qi / G, h = j * G + qi % G;
+        *(uint4*)((uint16_t*)a.out + pk(b * a.S + s2, h * DH + c8, a.Hq * DH)) = *(const uint4*)&s_out[row][c8];
+      }
+    }
+    return;
   }
 
   // 1 / row sum (waves in a fixed order)
@@ -1744,9 +1840,15 @@ static hipError_t gemm_upw(const GemmArgs& g, int grid, hipStream_t st) {
   if (per_wave <= 1) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 1, 1>), grid, 512, g);
   if (per_wave <= 2) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 2, 1>), grid, 512, g);
   if (per_wave <= 4) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 4, 1>), grid, 512, g);
-  if (NB == 1 && per_wave <= 8) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, 1, 8, 1>), grid, 512, g);
+  // 8 units in one pass only where a unit is one k-block: fp8 units carry
+  // two, and 8 of them would not fit the registers (the loads would serialise)
+  if constexpr (KU == 1 && NB == 1) {
+    if (per_wave <= 8) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, 1, 8, 1>), grid, 512, g);
+  }
   if (per_wave <= 8) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 4, 2>), grid, 512, g);
-  if (NB == 1 && per_wave <= 16) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, 1, 8, 2>), grid, 512, g);
+  if constexpr (KU == 1 && NB == 1) {
+    if (per_wave <= 16) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, 1, 8, 2>), grid, 512, g);
+  }
   if (per_wave <= 16) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 4, 4>), grid, 512, g);
   return hipErrorInvalidValue;
 }
@@ -1785,10 +1887,12 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
 }
 
 template <int DH, int QB>
-static hipError_t attn_sf(AttnArgs a, int nk32, hipStream_t st) {
+static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
+  if (QB > 1 || DH < 128) a.nsplit = 1;  // the key split runs with one query block, head_dim >= 128
+  if (a.nsplit == 1) a.keys_per_split = ((a.TP + a.SP) / 16 + 1) / 2 * 2;
   a.nqblk = (a.S * (a.Hq / a.Hkv) + 16 * QB - 1) / (16 * QB);
-  const int grid = a.B * a.Hkv * a.nqblk;
-  switch ((nk32 + 3) / 4) {
+  const int grid = a.B * a.Hkv * a.nqblk * a.nsplit;
+  switch ((a.keys_per_split + 7) / 8) {  // R: 16-key blocks per wave
     case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB>), grid, 512, a);
     case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB>), grid, 512, a);
     case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB>), grid, 512, a);
@@ -1807,7 +1911,7 @@ static hipError_t attn_sf(AttnArgs a, int nk32, hipStream_t st) {
 template <int DH>
 static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
   const int nk32 = (a.TP + a.SP) / 32;  // padded logical keys in 32-key blocks
-  if (nk32 <= 32) return a.B * a.Hkv * a.nqblk > 256 ? attn_sf<DH, 2>(a, nk32, st) : attn_sf<DH, 1>(a, nk32, st);
+  if (nk32 <= 32) return a.B * a.Hkv * a.nqblk > 256 ? attn_sf<DH, 2>(a, st) : attn_sf<DH, 1>(a, st);
   hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -41,6 +41,8 @@ def test_tiny_fp32():
     dict(prefix_static=1100, prefix_len=1100, chunk=9),      # attention: > 1024 keys, flash kernel
     dict(batch=12, chunk=30, prefix_static=150, prefix_len=150),  # 372 rows: LDS-staged MFMA GEMMs, ragged m-tile
     dict(batch=20, chunk=60, n_q_heads=8, prefix_static=100, prefix_len=100),  # attention: 2 query blocks/workgroup
+    dict(head_dim=128, prefix_static=600, prefix_len=200),  # attention key split, ranges mostly masked
+    dict(head_dim=256, n_q_heads=2, prefix_static=600, prefix_len=0),  # key split, whole ranges masked
 ])
 def test_small_bf16(kw):
     cfg = small_cfg(**kw)
@@ -188,6 +190,12 @@ def test_small_ring_fp8():
 def test_small_ring_bf16():
     cfg = small_cfg(name="small_ring_bf16", prefix_static=5, frame_tokens=64, n_frames=3, prefix_len=197)
     _ring_run(cfg, ticks=6, oracle_ticks={5})
+
+
+def test_small_ring_bf16_key_split():
+    cfg = small_cfg(name="small_ring_split", head_dim=128, prefix_static=20, frame_tokens=192, n_frames=3,
+                    prefix_len=596)
+    _ring_run(cfg, ticks=5, oracle_ticks={4})
 
 
 # --- full-size workloads ---------------------------------------------------------------------
