@@ -199,11 +199,22 @@ void derive(fm_ctx* x) {
   // residual GEMMs on the large-M path may split K (shared tile plan)
   x->ks_o = 1;
   x->ks_d = 1;
-  if (x->act == ELT_BF16 && x->wt == ELT_BF16) {
-    const BigPlan po = big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh);
-    const BigPlan pd = big_plan(EPI_RESID, x->M, x->d, x->F);
-    if (po.used) x->ks_o = po.ks;
-    if (pd.used) x->ks_d = pd.ks;
+  const BigPlan po = big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh);
+  const BigPlan pd = big_plan(EPI_RESID, x->M, x->d, x->F);
+  if (x->act == ELT_BF16 && x->wt == ELT_BF16 && po.used) {
+    x->ks_o = po.ks;
+    x->ks_d = pd.ks;
+  } else if (x->act == ELT_BF16) {
+    // skinny residual GEMMs: split K so that about 256 workgroups each read a
+    // quarter of the shared activation operand (it dominates their bytes)
+    const int tiles = x->mtiles * (x->d / 16), unit = x->wt == ELT_FP8 ? 64 : 32;
+    auto pick = [&](int K) {
+      for (int ks = 4; ks > 1; ks /= 2)
+        if (tiles * ks <= 256 && (K / unit) % ks == 0 && K / unit / ks >= 2) return ks;
+      return 1;
+    };
+    x->ks_o = pick(x->Hq * x->Dh);
+    x->ks_d = pick(x->F);
   }
   x->nqblk = (x->S * (x->Hq / x->Hkv) + 15) / 16;
   {

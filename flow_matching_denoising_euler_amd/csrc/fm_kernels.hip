@@ -319,7 +319,8 @@ struct SkinnyTile {
   Frag<ACT> a[UPW][4][KU];
   f32x4 acc[4][NB];
 
-  int rw;  // k-range of this wave: rotated by workgroup so that workgroups read different A lines at once
+  int rw;      // k-range of this wave: rotated by workgroup so that workgroups read different A lines at once
+  int u0 = 0;  // first k-unit of the workgroup's range (split K)
   __device__ __forceinline__ void set_range(int rot) { rw = ((threadIdx.x >> 6) + rot) & (GW - 1); }
   __device__ __forceinline__ void load_w_all(const void* W, int NBT, int nb0, int units) {
     const int lane = threadIdx.x & 63, wave = rw;
@@ -329,7 +330,7 @@ struct SkinnyTile {
       for (int i = 0; i < UPW; ++i) {
         const int u = min((wave * NPASS + p) * UPW + i, units - 1);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) w[p][i][nb] = load_w<ACT, WT>(W, NBT, nb0 + nb, u, lane);
+        for (int nb = 0; nb < NB; ++nb) w[p][i][nb] = load_w<ACT, WT>(W, NBT, nb0 + nb, u0 + u, lane);
       }
   }
   // A is in the packed layout (pk)
@@ -341,7 +342,7 @@ struct SkinnyTile {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int q = 0; q < KU; ++q) a[i][mb][q] = load_a_pk<ACT>(A, K, mt, u * KU + q, mb, lane);
+        for (int q = 0; q < KU; ++q) a[i][mb][q] = load_a_pk<ACT>(A, K, mt, (u0 + u) * KU + q, mb, lane);
     }
   }
   __device__ __forceinline__ void mma_pass(int units, int p) {
@@ -375,11 +376,15 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
   __shared__ float red[4][64][33];
   __shared__ float s_rstd[64];
   __shared__ float s_col[3][32];  // per column: bias or alpha, gnext, fp8 scale
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int ntiles = g.N / nt;
-  const int nti = blockIdx.x % ntiles, mt = blockIdx.x / ntiles;
+  // split K (residual GEMMs): workgroup = (tile, k-range); the ranges of a
+  // tile are summed in range order by the last to arrive
+  const int ks = blockIdx.x % g.ksplit, tb = blockIdx.x / g.ksplit;
+  const int nti = tb % ntiles, mt = tb / ntiles;
   const int n0 = nti * nt, m0 = mt * 64;
-  const int units = (g.K >> 5) / KU;
+  const int units = (g.K >> 5) / KU / g.ksplit;
 
   // epilogue operands first (registers), then the GEMM operands
   const int ccol = n0 + min(tid, nt - 1);
@@ -400,6 +405,7 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
   SkinnyTile<ACT, WT, NB, UPW, NPASS> t;
   t.zero();
   t.set_range(blockIdx.x);
+  t.u0 = ks * units;
   t.load_w_all(g.W, g.N >> 4, n0 >> 4, units);
   t.load_a_pass(g.A, g.K, mt, units, 0);
   t.mma_pass(units, 0);
@@ -421,6 +427,36 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
   for (int i = 0; i < PER; ++i) {
     const int idx = tid + NT * i, row = idx / nt, col = idx % nt;
     v[i] = ((red[0][row][col] + red[1][row][col]) + red[2][row][col]) + red[3][row][col];
+  }
+  if constexpr (EPI == EPI_RESID) if (g.ksplit > 1) {
+    // every range stores its partial tile (device scope); the last to arrive
+    // adds the ranges in order (ksplit <= 4), own range from the registers
+    float* mine = g.partials + ((long)tb * g.ksplit + ks) * (64 * nt);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) st_dev(mine + tid + NT * i, v[i]);
+    drain_vm();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(g.counters + tb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)g.ksplit - 1;
+      if (s_last) __hip_atomic_store(g.counters + tb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    float pv[4][PER];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        pv[k2][i] = ld_dev(g.partials + ((long)tb * g.ksplit + min(k2, g.ksplit - 1)) * (64 * nt) + tid + NT * i);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float sum = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2)
+        if (k2 < g.ksplit) sum += (k2 == ks) ? v[i] : pv[k2][i];
+      v[i] = sum;
+    }
   }
 
   if constexpr (EPI == EPI_QKV) {
@@ -1835,7 +1871,7 @@ __global__ void k_kv_copy(KvCopy c) {
 template <int ACT, int WT, int EPI, int NB>
 static hipError_t gemm_upw(const GemmArgs& g, int grid, hipStream_t st) {
   constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
-  const int units = (g.K >> 5) / KU;
+  const int units = (g.K >> 5) / KU / g.ksplit;  // k-units of one split range
   const int per_wave = (units + GW - 1) / GW;
   if (per_wave <= 1) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 1, 1>), grid, 512, g);
   if (per_wave <= 2) FM_LAUNCH_N((k_gemm<ACT, WT, EPI, NB, 2, 1>), grid, 512, g);
@@ -1872,8 +1908,9 @@ static hipError_t gemm_dispatch(int epi, const GemmArgs& g, hipStream_t st) {
     hipError_t e;
     if (gemm_big(epi, g, st, &e)) return e;
   }
-  if (g.nt != nt || g.ksplit != 1) return hipErrorInvalidValue;
-  const int grid = g.mtiles * (g.N / nt);
+  if (g.nt != nt || g.ksplit < 1 || g.ksplit > 4 || (g.ksplit != 1 && epi != EPI_RESID)) return hipErrorInvalidValue;
+  if (((g.K >> 5) / (WT == ELT_FP8 ? 2 : 1)) % g.ksplit) return hipErrorInvalidValue;
+  const int grid = g.mtiles * (g.N / nt) * g.ksplit;
   if (epi == EPI_QKV) return gemm_upw<ACT, WT, EPI_QKV, 1>(g, grid, st);
   if (epi == EPI_RESID) return gemm_upw<ACT, WT, EPI_RESID, 1>(g, grid, st);
   return gemm_upw<ACT, WT, EPI_GELU, 2>(g, grid, st);
