@@ -1537,8 +1537,32 @@ struct EmbedCol {
   __device__ __forceinline__ void load(int c0, int A, const void* w_in, const void* b_in, const Tab& temb,
                                        const Tab& g1, int step, const float* hs, int m0, int M, int S, int d) {
     const int col = c0 + (threadIdx.x & 63);
+    // the column's A weights are contiguous (A = 16 or 32): 16-byte vector loads
+    if constexpr (WE == ELT_F32) {
+      const float4* p = (const float4*)((const float*)w_in + (long)col * A);
 #pragma unroll
-    for (int a = 0; a < 32; ++a) w[a] = ld_w(w_in, WE, (long)col * A + min(a, A - 1));
+      for (int j = 0; j < 8; ++j) {
+        const float4 v = p[min(j, A / 4 - 1)];
+        const bool ok = 4 * j < A;
+        w[4 * j] = ok ? v.x : 0.f;
+        w[4 * j + 1] = ok ? v.y : 0.f;
+        w[4 * j + 2] = ok ? v.z : 0.f;
+        w[4 * j + 3] = ok ? v.w : 0.f;
+      }
+    } else {
+      const uint4* p = (const uint4*)((const uint16_t*)w_in + (long)col * A);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = p[min(j, A / 8 - 1)];
+        const uint32_t m = mask_if(8 * j < A);
+        const uint32_t x[4] = {v.x & m, v.y & m, v.z & m, v.w & m};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[8 * j + 2 * e] = bf2f(x[e] & 0xFFFFu);
+          w[8 * j + 2 * e + 1] = bf2f(x[e] >> 16);
+        }
+      }
+    }
     bias = ld_w(b_in, WE, col) + temb.base[(long)step * temb.step_stride + col];
     gain = g1.base[(long)step * g1.step_stride + col];
 #pragma unroll
