@@ -321,6 +321,7 @@ struct SkinnyTile {
 
   int rw;      // k-range of this wave: rotated by workgroup so that workgroups read different A lines at once
   int u0 = 0;  // first k-unit of the workgroup's range (split K)
+  int mv = 64; // rows of the tile below M: lanes of rows past it load nothing (those rows hold zeros)
   __device__ __forceinline__ void set_range(int rot) { rw = ((threadIdx.x >> 6) + rot) & (GW - 1); }
   __device__ __forceinline__ void load_w_all(const void* W, int NBT, int nb0, int units) {
     const int lane = threadIdx.x & 63, wave = rw;
@@ -336,13 +337,27 @@ struct SkinnyTile {
   // A is in the packed layout (pk)
   __device__ __forceinline__ void load_a_pass(const void* A, int K, int mt, int units, int p) {
     const int lane = threadIdx.x & 63, wave = rw;
+    // this tile's 64 rows x K block of the packed layout
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)A + (long)mt * K * 64), (short)0, K * 128, 0x00020000);
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       const int u = min((wave * NPASS + p) * UPW + i, units - 1);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int q = 0; q < KU; ++q) a[i][mb][q] = load_a_pk<ACT>(A, K, mt, (u0 + u) * KU + q, mb, lane);
+        for (int q = 0; q < KU; ++q) {
+          if constexpr (ACT == ELT_F32) {
+            a[i][mb][q] = load_a_pk<ACT>(A, K, mt, (u0 + u) * KU + q, mb, lane);
+          } else {
+            // bounds-checked buffer load: an offset past the range returns
+            // zeros without a memory access
+            const int kb = (u0 + u) * KU + q;
+            const uint32_t off = mb * 16 + (lane & 15) < mv ? (uint32_t)(((kb * 4 + mb) * 64 + lane) * 16) : 0x7FFFFFF0u;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            a[i][mb][q].v = make_uint4(v[0], v[1], v[2], v[3]);
+          }
+        }
     }
   }
   __device__ __forceinline__ void mma_pass(int units, int p) {
@@ -406,6 +421,7 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
   t.zero();
   t.set_range(blockIdx.x);
   t.u0 = ks * units;
+  t.mv = g.M - m0;
   t.load_w_all(g.W, g.N >> 4, n0 >> 4, units);
   t.load_a_pass(g.A, g.K, mt, units, 0);
   t.mma_pass(units, 0);
@@ -1674,6 +1690,7 @@ __global__ __launch_bounds__(512) void k_out(OutArgs o) {
   SkinnyTile<ACT, WE, NB, UPW, 1> t;
   t.zero();
   t.set_range(blockIdx.x);
+  t.mv = o.M - m0;
   t.load_w_all(o.Wout, NB, 0, units);
   t.load_a_pass(o.uf, o.d, mt, units, 0);
   t.mma_pass(units, 0);
