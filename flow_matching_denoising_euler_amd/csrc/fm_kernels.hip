@@ -203,6 +203,35 @@ __device__ __forceinline__ f32x4 mma_unit(const Frag<ACT>* a, const WFrag<ACT, W
 constexpr int PM = 128;  // slots of h^2 partial sums per row (one per 16 columns, d <= 2048)
 constexpr int GW = 8;    // waves per GEMM / tail workgroup (512 threads)
 
+// Cross-lane reductions inside aligned groups of 8 or 16 lanes with DPP
+// moves (VALU operations, no trip through the LDS pipe): quad_perm
+// [1,0,3,2] and [2,3,0,1] pair lanes i and i^1, i^2; after them every lane
+// of a quad holds the quad's value, so the half-row mirror (i <-> 7-i) and
+// the row mirror (i <-> 15-i) combine the same pairs of values as i^4 and
+// i^8 would: results equal those of the xor butterfly bit for bit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// (no contraction into the caller's products: every step adds two rounded values)
+__device__ __forceinline__ float sum8(float x) {
+#pragma clang fp contract(off)
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  return x + dpp_mov<0x141>(x);  // row_half_mirror
+}
+__device__ __forceinline__ float sum16(float x) {
+#pragma clang fp contract(off)
+  x = sum8(x);
+  return x + dpp_mov<0x140>(x);  // row_mirror
+}
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  return fmaxf(x, dpp_mov<0x140>(x));
+}
+
 __device__ __forceinline__ uint32_t mask_if(bool ok) { return ok ? 0xFFFFFFFFu : 0u; }
 __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 __device__ __forceinline__ float4 and4f(float4 v, uint32_t m) {
@@ -274,9 +303,7 @@ __device__ __forceinline__ void rstd_finish(const float4 (&q)[4], int M, int m0,
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) s += ((q[i].x + q[i].y) + q[i].z) + q[i].w;
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
+  s = sum8(s);
   if ((tid & 7) == 0) s_rstd[tid >> 3] = (m0 + (tid >> 3) < M) ? rsqrtf(s * inv_d + eps) : 0.f;
 }
 
@@ -523,10 +550,7 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
       const int r = m0 + row;
       const float hn = (r < g.M) ? hold[i] + s_col[0][c] * (v[i] * s_col[2][c]) : 0.f;
       float qq = hn * hn;
-      qq += __shfl_xor(qq, 1);
-      qq += __shfl_xor(qq, 2);
-      qq += __shfl_xor(qq, 4);
-      qq += __shfl_xor(qq, 8);
+      qq = sum16(qq);
       if (r < g.M) {
         const long o = (long)r * g.N + n0 + c;
         g.h[o] = hn;
@@ -586,6 +610,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // fences keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_nofence() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete (lgkmcnt 0), global loads in flight stay in flight (a plain
+// __syncthreads would also wait for those).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // gfx9 encoding: lgkmcnt 0, vmcnt 63, expcnt 7 (no wait)
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
@@ -870,9 +903,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
       float sq = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sq += ((q[i][rr].x + q[i][rr].y) + q[i][rr].z) + q[i][rr].w;
-      sq += __shfl_xor(sq, 1);
-      sq += __shfl_xor(sq, 2);
-      sq += __shfl_xor(sq, 4);
+      sq = sum8(sq);
       const int r = rr * (NT / 8) + (tid >> 3);
       if ((tid & 7) == 0) s_rstd[r] = (m0 + r < g.M) ? rsqrtf(sq * g.inv_d + g.eps) : 0.f;
     }
@@ -1105,10 +1136,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
         p[nb][r] = (key < ks.kp && ks.valid(key)) ? sacc[nb][r] * a.scale : -INFINITY;
         m = fmaxf(m, p[nb][r]);
       }
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 8));
+      m = max16(m);
       const float corr = (mrow[r] == -INFINITY) ? 0.f : __expf(mrow[r] - m);
       float l = 0.f;
 #pragma unroll
@@ -1116,10 +1144,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
         p[nb][r] = (m == -INFINITY) ? 0.f : __expf(p[nb][r] - m);
         l += p[nb][r];
       }
-      l += __shfl_xor(l, 1);
-      l += __shfl_xor(l, 2);
-      l += __shfl_xor(l, 4);
-      l += __shfl_xor(l, 8);
+      l = sum16(l);
       lrow[r] = lrow[r] * corr + l;
       mrow[r] = m;
 #pragma unroll
@@ -1313,13 +1338,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float m = mx[u][r];
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 8));
+      m = max16(m);
       if ((lane & 15) == 0) s_max[w][u * 16 + (lane >> 4) * 4 + r] = m;
     }
-  __syncthreads();
+  lds_barrier();  // V loads stay in flight
   float sm[QB][4];
 #pragma unroll
   for (int u = 0; u < QB; ++u)
@@ -1349,13 +1371,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float t = sm[u][r];
-      t += __shfl_xor(t, 1);
-      t += __shfl_xor(t, 2);
-      t += __shfl_xor(t, 4);
-      t += __shfl_xor(t, 8);
+      t = sum16(t);
       if ((lane & 15) == 0) s_sum[w][u * 16 + (lane >> 4) * 4 + r] = t;
     }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 3. O = P V for this wave's head-dim blocks and key group
   f32x4 oacc[QB][NBW];
@@ -1601,10 +1620,7 @@ struct EmbedCol {
       const bool st = has_state && (r % S) == 0;
       const float hv = (r < M) ? (st ? hsv[i] : acc + bias) : 0.f;
       float q = hv * hv;
-      q += __shfl_xor(q, 1);
-      q += __shfl_xor(q, 2);
-      q += __shfl_xor(q, 4);
-      q += __shfl_xor(q, 8);
+      q = sum16(q);
       if (r < M) {
         h[(long)r * d + col] = hv;
         st_act<ACT>(u, pk(r, col, d), hv * gain);
