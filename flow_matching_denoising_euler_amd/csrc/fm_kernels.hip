@@ -1232,15 +1232,20 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 //     V fragments streamed VQ blocks ahead, scales by 1 / sum and stores.
 // Every global load of a phase is issued before its first use; there is no
 // online rescaling and, for DH >= 128, no merge of partial outputs.
-template <int DH, int R, int QB>
+template <int DH, int R, int QB, int DS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
   constexpr int KBD = DH / 32, NBD = DH / 16, QR = 16 * QB;
+  // DS workgroups share a query block: each computes all scores and the
+  // softmax, and the P V product for its 1/DS of the head dims (V traffic per
+  // workgroup / DS, no merge)
+  constexpr int NBD3 = NBD / DS;
+  static_assert(DS == 1 || (QB == 1 && NBD3 >= 8), "dim split: one query block, 8 or more output blocks");
   // K and V blocks in flight per wave, within about 240 registers
   constexpr int KQ0 = (QB == 1 ? (R <= 4 ? 24 : 16) : (R <= 4 ? 16 : 8)) / KBD;
   constexpr int KQ = KQ0 < 1 ? 1 : (KQ0 < R ? KQ0 : R);
   constexpr int KPAD = 128 * R + 8;                    // P row: keys of blocks nb < 8R, padded
-  constexpr int NBW = NBD >= 8 ? NBD / 8 : 1;          // head-dim blocks per wave
-  constexpr int KG = NBD >= 8 ? 1 : 8 / NBD;           // key groups of phase 3
+  constexpr int NBW = NBD3 >= 8 ? NBD3 / 8 : 1;        // head-dim blocks per wave
+  constexpr int KG = NBD3 >= 8 ? 1 : 8 / NBD3;         // key groups of phase 3
   constexpr int KBW = 4 * R / KG;                      // 32-key blocks per wave in phase 3
   constexpr int VQ0 = (QB == 1 ? (R <= 3 ? 16 : 8) : 8) / NBW, VQ = VQ0 < KBW ? VQ0 : KBW;
   __shared__ __align__(16) uint16_t sP[QR][KPAD];
@@ -1255,6 +1260,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int wg = blockIdx.x;
   const int q8 = gridDim.x / 8;
   if (wg < 8 * q8) wg = (wg % 8) * q8 + wg / 8;
+  const int ds = wg % DS;                              // head-dim part of the output
+  wg /= DS;
   const int sp = wg % a.nsplit, grp = wg / a.nsplit;  // key range, query group
   const int qb = grp % a.nqblk, jb = grp / a.nqblk;
   const int j = jb % a.Hkv, b = jb / a.Hkv;
@@ -1287,7 +1294,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // phase 3's first V fragments go out with the first K fragments, before
   // any wait; the scheduling barriers keep the compiler from sinking loads
   // towards their uses (which would serialise the round trips)
-  const int kg = w / (8 / KG), nbd0 = (w % (8 / KG)) * NBW;
+  const int kg = w / (8 / KG), nbd0 = ds * NBD3 + (w % (8 / KG)) * NBW;
   uint4 vf[VQ][NBW];
   auto load_v = [&](int i, int slot) {
     const int kb32 = min((kb0 >> 1) + kg + KG * i, nk32 - 1);
@@ -1399,7 +1406,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // key split: every range stores its unnormalised output, row maxima and
   // row sums (device scope); the last range to arrive merges them in range
   // order, O = sum_r e^(m_r - M) O_r / sum_r e^(m_r - M) l_r
-  if constexpr (QB == 1 && KG == 1) if (a.nsplit > 1) {
+  if constexpr (QB == 1 && KG == 1 && DS == 1) if (a.nsplit > 1) {
     constexpr int PO = 8 * NBW * 64 * 4;  // floats of partial output per range (= 16 x DH)
     float* mine = a.part + ((long)grp * a.nsplit + sp) * (PO + 32);
 #pragma unroll
@@ -1521,8 +1528,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
   // packed stores, 8 head dims per thread
-  for (int i = tid; i < 2 * QR * DH / 16; i += 512) {
-    const int row = i / (DH / 8), c8 = (i % (DH / 8)) * 8;
+  for (int i = tid; i < QR * DH / 8 / DS; i += 512) {
+    const int row = i / (DH / DS / 8), c8 = ds * (DH / DS) + (i % (DH / DS / 8)) * 8;
     const int qi = qb * QR + row;
     if (qi < nq) {
       const int s = qi / G, h = j * G + qi % G;
@@ -1980,21 +1987,21 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-template <int DH, int QB>
+template <int DH, int QB, int DS>
 static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
   if (QB > 1 || DH < 128) a.nsplit = 1;  // the key split runs with one query block, head_dim >= 128
   if (a.nsplit == 1) a.keys_per_split = ((a.TP + a.SP) / 16 + 1) / 2 * 2;
   a.nqblk = (a.S * (a.Hq / a.Hkv) + 16 * QB - 1) / (16 * QB);
-  const int grid = a.B * a.Hkv * a.nqblk * a.nsplit;
+  const int grid = a.B * a.Hkv * a.nqblk * a.nsplit * DS;
   switch ((a.keys_per_split + 7) / 8) {  // R: 16-key blocks per wave
-    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB>), grid, 512, a);
-    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB>), grid, 512, a);
-    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB>), grid, 512, a);
-    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB>), grid, 512, a);
-    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB>), grid, 512, a);
-    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB>), grid, 512, a);
-    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB>), grid, 512, a);
-    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB>), grid, 512, a);
+    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS>), grid, 512, a);
+    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS>), grid, 512, a);
+    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS>), grid, 512, a);
+    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS>), grid, 512, a);
+    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS>), grid, 512, a);
+    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS>), grid, 512, a);
+    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS>), grid, 512, a);
+    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS>), grid, 512, a);
   }
   return hipErrorInvalidValue;
 }
@@ -2005,7 +2012,13 @@ static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
 template <int DH>
 static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
   const int nk32 = (a.TP + a.SP) / 32;  // padded logical keys in 32-key blocks
-  if (nk32 <= 32) return a.B * a.Hkv * a.nqblk > 256 ? attn_sf<DH, 2>(a, st) : attn_sf<DH, 1>(a, st);
+  if (nk32 <= 32) {
+    const int groups = a.B * a.Hkv * a.nqblk;
+    if (groups > 256) return attn_sf<DH, 2, 1>(a, st);
+    // few query groups and no key split: two workgroups per query block
+    if constexpr (DH == 256) if (a.nsplit == 1 && groups <= 128) return attn_sf<DH, 1, 2>(a, st);
+    return attn_sf<DH, 1, 1>(a, st);
+  }
   hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
