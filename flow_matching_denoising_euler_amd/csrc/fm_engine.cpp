@@ -293,10 +293,11 @@ void carve(fm_ctx* x, Arena& a) {
   const long ks = std::max(x->ks_o, x->ks_d);
   const long Mp128 = (x->M + 127) / 128 * 128;  // rows covered by the large-M tiles
   x->partials = (float*)a.take(ks > 1 ? ks * Mp128 * d * 4 : 16);
-  // per (query group, key range): 16 rows x Dh partial output, row max, row sum
-  x->attn_part = (float*)a.take(x->nsplit == 1 ? 16 : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 2) * 4);
+  // per (query group, head-dim part (up to 2), key range): 16 rows x Dh / parts
+  // partial output, row max, row sum
+  x->attn_part = (float*)a.take(x->nsplit == 1 ? 16 : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 4) * 4);
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
-                                   (size_t)x->B * x->Hkv * x->nqblk) + 64;
+                                   (size_t)x->B * x->Hkv * x->nqblk * 2) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);
 }
 

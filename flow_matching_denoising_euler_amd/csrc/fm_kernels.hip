@@ -1406,9 +1406,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // key split: every range stores its unnormalised output, row maxima and
   // row sums (device scope); the last range to arrive merges them in range
   // order, O = sum_r e^(m_r - M) O_r / sum_r e^(m_r - M) l_r
-  if constexpr (QB == 1 && KG == 1 && DS == 1) if (a.nsplit > 1) {
-    constexpr int PO = 8 * NBW * 64 * 4;  // floats of partial output per range (= 16 x DH)
-    float* mine = a.part + ((long)grp * a.nsplit + sp) * (PO + 32);
+  if constexpr (QB == 1 && KG == 1) if (a.nsplit > 1) {
+    constexpr int PO = 8 * NBW * 64 * 4;  // floats of partial output per range (= 16 x DH / DS)
+    const long gd = (long)grp * DS + ds;  // (query group, head-dim part)
+    float* mine = a.part + (gd * a.nsplit + sp) * (PO + 32);
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
       float* o = mine + ((w * NBW + n) * 64 + lane) * 4;
@@ -1429,9 +1430,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     drain_vm();
     __syncthreads();
     if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(a.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned prev = __hip_atomic_fetch_add(a.counters + gd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev == (unsigned)a.nsplit - 1;
-      if (s_last) __hip_atomic_store(a.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (s_last) __hip_atomic_store(a.counters + gd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!s_last) return;
@@ -1442,7 +1443,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x4 po[MAXS][NBW];
 #pragma unroll
     for (int r2 = 0; r2 < MAXS; ++r2) {
-      const float* src = a.part + ((long)grp * a.nsplit + min(r2, a.nsplit - 1)) * (PO + 32);
+      const float* src = a.part + (gd * a.nsplit + min(r2, a.nsplit - 1)) * (PO + 32);
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
         const float2 m2 = ld_dev2(src + PO + (lane >> 4) * 4 + r), l2 = ld_dev2(src + PO + 16 + (lane >> 4) * 4 + r);
@@ -1481,8 +1482,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 4; ++r)
         s_out[(lane >> 4) * 4 + r][(nbd0 + n) * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[0][n][r]);
     __syncthreads();
-    for (int i = tid; i < 2 * DH; i += 512) {
-      const int row = i / (DH / 8), c8 = (i % (DH / 8)) * 8;
+    for (int i = tid; i < 2 * DH / DS; i += 512) {
+      const int row = i / (DH / DS / 8), c8 = ds * (DH / DS) + (i % (DH / DS / 8)) * 8;
       const int qi = qb * 16 + row;
       if (qi < nq) {
         const int s2 = qi / G, h = j * G + qi % G;
@@ -2015,8 +2016,8 @@ static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (nk32 <= 32) {
     const int groups = a.B * a.Hkv * a.nqblk;
     if (groups > 256) return attn_sf<DH, 2, 1>(a, st);
-    // few query groups and no key split: two workgroups per query block
-    if constexpr (DH == 256) if (a.nsplit == 1 && groups <= 128) return attn_sf<DH, 1, 2>(a, st);
+    // few query groups: two workgroups per query block (and key range)
+    if constexpr (DH == 256) if (groups <= 128) return attn_sf<DH, 1, 2>(a, st);
     return attn_sf<DH, 1, 1>(a, st);
   }
   hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
