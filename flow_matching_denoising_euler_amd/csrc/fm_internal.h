@@ -147,9 +147,10 @@ struct BigPlan {
   int BM, BN, ks;
 };
 inline BigPlan big_plan(int epi, int M, int N, int K) {
-  // gate/up 128 x 256, QKV 128 x 128, residual 64 x 128 (their N is d_model,
-  // so smaller tiles and a 2-way K split to cover the CUs)
-  BigPlan p{false, epi == EPI_RESID ? 64 : 128, epi == EPI_GELU ? 256 : 128, 1};
+  // gate/up 128 x 256; QKV and residual 128 x 64 (narrow tiles to cover the
+  // CUs, the residual ones also with a 2-way K split since their N is
+  // d_model); 128-row tiles everywhere, like the GEMMs that read the output
+  BigPlan p{false, 128, epi == EPI_GELU ? 256 : 64, 1};
   if (M < 256 || K % 64 || N % p.BN) return p;
   if (epi == EPI_RESID) {
     const int tiles = (M + p.BM - 1) / p.BM * (N / p.BN), stages = K / 64;

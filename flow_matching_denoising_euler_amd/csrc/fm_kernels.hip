@@ -1960,8 +1960,8 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   if (!p.used || g.ksplit != p.ks) return false;
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN) * p.ks;
   if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2>), dim3(grid), dim3(512), 0, st, g);
-  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 4, 2>), dim3(grid), dim3(512), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 4, 1>), dim3(grid), dim3(256), 0, st, g);
+  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1>), dim3(grid), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 4, 2, 1>), dim3(grid), dim3(256), 0, st, g);
   *err = hipGetLastError();
   return true;
 }
