@@ -147,14 +147,15 @@ struct BigPlan {
   int BM, BN, ks;
 };
 inline BigPlan big_plan(int epi, int M, int N, int K) {
-  // gate/up 128 x 256; QKV and residual 128 x 64 (narrow tiles to cover the
-  // CUs, the residual ones also with a 2-way K split since their N is
-  // d_model); 128-row tiles everywhere, like the GEMMs that read the output
-  BigPlan p{false, 128, epi == EPI_GELU ? 256 : 64, 1};
+  // gate/up 128 x 256 and QKV 128 x 64 (128-row tiles, like the GEMMs that
+  // read their output); the residual GEMMs (N = d_model) 64 x 64, which
+  // covers the CUs without splitting K, except for deep K (down projection,
+  // K >= 4096), which splits K over 2 workgroups (two per CU)
+  BigPlan p{false, epi == EPI_RESID ? 64 : 128, epi == EPI_GELU ? 256 : 64, 1};
   if (M < 256 || K % 64 || N % p.BN) return p;
   if (epi == EPI_RESID) {
     const int tiles = (M + p.BM - 1) / p.BM * (N / p.BN), stages = K / 64;
-    if (stages % 2 == 0 && tiles * 2 <= 256) p.ks = 2;
+    if (K >= 4096 && stages % 2 == 0 && tiles * 2 <= 512) p.ks = 2;
   }
   p.used = true;
   return p;

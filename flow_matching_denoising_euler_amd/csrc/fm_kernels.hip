@@ -727,7 +727,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   constexpr int LPW = FPS / NW;                       // copies per wave per stage
   constexpr int NJ = TNW * TMW;                       // accumulator blocks per wave
   constexpr int TME = TMW / KG;                       // row blocks of this wave's epilogue
-  static_assert(KG == 1 || (KG == 2 && EPI != EPI_RESID && TMW % 2 == 0), "k-groups: no split K, even row blocks");
+  static_assert(KG == 1 || (KG == 2 && TMW % 2 == 0), "k-groups: even row blocks (and no split K, below)");
   static_assert(BM * 8 % NT == 0, "norm-statistics pass");
   __shared__ __align__(16) uint8_t lds0[FPS * 1024], lds1[FPS * 1024], lds2[FPS * 1024];
   __shared__ float s_rstd[BM];
@@ -846,7 +846,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
 
   // split K: every workgroup stores its partial tile; the last to arrive
   // adds the partials in split order and goes on to the epilogue
-  if constexpr (EPI == EPI_RESID) if (g.ksplit > 1) {
+  if constexpr (EPI == EPI_RESID && KG == 1) if (g.ksplit > 1) {
     float* mine = g.partials + (((long)t * g.ksplit + ks) * NJ * 256 + tid) * 4;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -1961,7 +1961,8 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN) * p.ks;
   if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2>), dim3(grid), dim3(512), 0, st, g);
   else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1>), dim3(grid), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 4, 2, 1>), dim3(grid), dim3(256), 0, st, g);
+  else if (p.ks == 1) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 1>), dim3(grid), dim3(256), 0, st, g);
   *err = hipGetLastError();
   return true;
 }
