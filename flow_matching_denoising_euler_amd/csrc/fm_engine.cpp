@@ -196,14 +196,11 @@ void derive(fm_ctx* x) {
   x->esplit = x->d / 64;
   const int unit = x->wt == ELT_FP8 ? 2 : 1;
   (void)unit;
-  // residual GEMMs on the large-M path may split K (shared tile plan)
+  // K splits of the residual GEMMs: none on the large-M path
   x->ks_o = 1;
   x->ks_d = 1;
   const BigPlan po = big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh);
-  const BigPlan pd = big_plan(EPI_RESID, x->M, x->d, x->F);
   if (x->act == ELT_BF16 && x->wt == ELT_BF16 && po.used) {
-    x->ks_o = po.ks;
-    x->ks_d = pd.ks;
   } else if (x->act == ELT_BF16) {
     // skinny residual GEMMs: split K so that about 256 workgroups each read a
     // quarter of the shared activation operand (it dominates their bytes)

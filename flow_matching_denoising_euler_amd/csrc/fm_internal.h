@@ -144,19 +144,16 @@ struct EmbedArgs {
 // false selects the skinny GEMM.
 struct BigPlan {
   bool used;
-  int BM, BN, ks;
+  int BM, BN, kst;  // tile, k-blocks of 32 per LDS stage
 };
 inline BigPlan big_plan(int epi, int M, int N, int K) {
   // gate/up 128 x 256 and QKV 128 x 64 (128-row tiles, like the GEMMs that
-  // read their output); the residual GEMMs (N = d_model) 64 x 64, which
-  // covers the CUs without splitting K, except for deep K (down projection,
-  // K >= 4096), which splits K over 2 workgroups (two per CU)
-  BigPlan p{false, epi == EPI_RESID ? 64 : 128, epi == EPI_GELU ? 256 : 64, 1};
+  // read their output), stages of 64 k; the residual GEMMs (N = d_model)
+  // 64 x 64 with stages of 128 k (where K allows), which covers the CUs
+  // without splitting K
+  BigPlan p{false, epi == EPI_RESID ? 64 : 128, epi == EPI_GELU ? 256 : 64, 2};
   if (M < 256 || K % 64 || N % p.BN) return p;
-  if (epi == EPI_RESID) {
-    const int tiles = (M + p.BM - 1) / p.BM * (N / p.BN), stages = K / 64;
-    if (K >= 4096 && stages % 2 == 0 && tiles * 2 <= 512) p.ks = 2;
-  }
+  if (epi == EPI_RESID && K % 128 == 0) p.kst = 4;
   p.used = true;
   return p;
 }

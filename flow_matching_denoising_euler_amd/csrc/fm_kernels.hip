@@ -568,17 +568,15 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
 // Workgroup = 4 waves in a 2 x 2 grid over a BM x BN tile (BM = 32 TMW rows,
 // BN = 32 TNW packed columns); wave (wm, wn) owns TMW row blocks x TNW
 // column blocks of 16.  Both operands are in MFMA fragment order in memory
-// (1 KB per 16 x 32 fragment), so each stage (BIG_KS k-blocks of 32) is
+// (1 KB per 16 x 32 fragment), so each stage (KS k-blocks of 32) is
 // copied fragment by fragment straight into LDS (global_load_lds_dwordx4:
 // lane i's 16 bytes land at M0 + 16 i) into a ring of three slots, and the
 // waves read their fragments with conflict-free 16-byte LDS reads.  The
 // weight fragment is the MFMA's first operand, so a lane's accumulator holds
 // 4 consecutive output columns of one row: the epilogues load and store
-// 8- and 16-byte vectors.  Residual GEMMs may split K over ks workgroups;
-// each writes its partial tile (device-scope stores), and the last to arrive
-// sums the partials in split order and runs the epilogue (deterministic).
+// 8- and 16-byte vectors.  KG = 2 runs two k-groups of 4 waves over
+// alternate k-blocks of each stage; they add their accumulators through LDS.
 // ---------------------------------------------------------------------------
-constexpr int BIG_STAGES = 3, BIG_KS = 2;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -635,32 +633,32 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   return make_uint2(f2bf(a) | (f2bf(b) << 16), f2bf(c) | (f2bf(d) << 16));
 }
 
-// Copies of one stage (BIG_KS k-blocks) by the NW waves of a workgroup.
+// Copies of one stage (KS k-blocks) by the NW waves of a workgroup.
 // Fragment f = wave + NW i of a stage: the first MB * KS are activations
 // (k-block f / MB, row block f % MB), the rest weights; since MB * KS is a
 // multiple of NW, loop index i < MB * KS / NW gives activations.  src[i] is
 // this lane's source of fragment i in the split's first stage; stage sc
 // (relative) adds sc * stride (A or W).
-template <int TMW, int TNW, int NW>
+template <int TMW, int TNW, int NW, int KS>
 struct BigSrc {
-  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, LPW = (MB + NBK) * BIG_KS / NW, LA = MB * BIG_KS / NW;
-  static_assert((MB * BIG_KS) % NW == 0 && (NBK * BIG_KS) % NW == 0, "fragments split evenly over the waves");
+  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, LPW = (MB + NBK) * KS / NW, LA = MB * KS / NW;
+  static_assert((MB * KS) % NW == 0 && (NBK * KS) % NW == 0, "fragments split evenly over the waves");
   const uint16_t* src[LPW];
   long stride_a, stride_w;  // elements per stage
   __device__ __forceinline__ BigSrc(const uint16_t* A, const uint16_t* W, int wave, int lane, int st0, int rb0,
                                     int nb0, int KB, int RB, int NBT) {
-    stride_a = (long)BIG_KS * 4 * 512;
-    stride_w = (long)BIG_KS * NBT * 512;
+    stride_a = (long)KS * 4 * 512;
+    stride_w = (long)KS * NBT * 512;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int f = wave + NW * i;
       if (i < LA) {
         const int qk = f / MB, mi = f % MB;
-        const int rb = min(rb0 + mi, RB - 1), kb = st0 * BIG_KS + qk;
+        const int rb = min(rb0 + mi, RB - 1), kb = st0 * KS + qk;
         src[i] = A + ((((long)(rb >> 2) * KB + kb) * 4 + (rb & 3)) * 64 + lane) * 8;
       } else {
-        const int ff = f - MB * BIG_KS, qk = ff / NBK, ni = ff % NBK;
-        src[i] = W + (((long)(st0 * BIG_KS + qk) * NBT + nb0 + ni) * 64 + lane) * 8;
+        const int ff = f - MB * KS, qk = ff / NBK, ni = ff % NBK;
+        src[i] = W + (((long)(st0 * KS + qk) * NBT + nb0 + ni) * 64 + lane) * 8;
       }
     }
   }
@@ -671,7 +669,7 @@ struct BigSrc {
   }
 };
 // The fragments of k-block qk of a stage for wave (wm, wn)
-template <int TMW, int TNW>
+template <int TMW, int TNW, int KS>
 __device__ __forceinline__ void big_read(const uint8_t* base, int qk, uint4 (&af)[TMW], uint4 (&bf)[TNW], int wm,
                                          int wn, int lane) {
   constexpr int MB = 2 * TMW, NBK = 2 * TNW;
@@ -679,74 +677,62 @@ __device__ __forceinline__ void big_read(const uint8_t* base, int qk, uint4 (&af
   for (int mi = 0; mi < TMW; ++mi) af[mi] = *(const uint4*)(base + (qk * MB + wm * TMW + mi) * 1024 + lane * 16);
 #pragma unroll
   for (int ni = 0; ni < TNW; ++ni)
-    bf[ni] = *(const uint4*)(base + (MB * BIG_KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
+    bf[ni] = *(const uint4*)(base + (MB * KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
 }
 // acc[ni][mi] += W(column block) x A(row block)^T over the k-blocks of the
-// stage this wave takes: all BIG_KS of them (KG = 1), or k-block kg (KG = 2,
-// one k-group per half of the workgroup).  With KG = 1 the fragments of
-// k-block qk + 1 are read while the MFMAs of qk run; the scheduling barriers
-// keep the reads ahead of the MFMAs.
-template <int TMW, int TNW, int KG>
+// stage this wave takes: kg, kg + KG, ... (KG k-groups of waves share a
+// stage).  The fragments of the next k-block are read while the MFMAs of the
+// current one run; the scheduling barriers keep the reads ahead of the MFMAs.
+template <int TMW, int TNW, int KG, int KS>
 __device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TNW][TMW], int kg, int wm, int wn,
                                             int lane) {
-  if constexpr (KG == 2) {
-    uint4 af[TMW], bf[TNW];
-    big_read<TMW, TNW>(base, kg, af, bf, wm, wn, lane);
-    __builtin_amdgcn_sched_barrier(0);
+  constexpr int NQ = KS / KG;
+  static_assert(KS % KG == 0, "k-blocks of a stage split evenly over the k-groups");
+  uint4 af[2][TMW], bf[2][TNW];
+  big_read<TMW, TNW, KS>(base, kg, af[0], bf[0], wm, wn, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (q + 1 < NQ) {
+      big_read<TMW, TNW, KS>(base, kg + KG * (q + 1), af[(q + 1) & 1], bf[(q + 1) & 1], wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int ni = 0; ni < TNW; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = mma_bf16(bf[ni], af[mi], acc[ni][mi]);
-  } else {
-    uint4 af[2][TMW], bf[2][TNW];
-    big_read<TMW, TNW>(base, 0, af[0], bf[0], wm, wn, lane);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int qk = 0; qk < BIG_KS; ++qk) {
-      if (qk + 1 < BIG_KS) {
-        big_read<TMW, TNW>(base, qk + 1, af[(qk + 1) & 1], bf[(qk + 1) & 1], wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int ni = 0; ni < TNW; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = mma_bf16(bf[qk & 1][ni], af[qk & 1][mi], acc[ni][mi]);
-    }
+      for (int mi = 0; mi < TMW; ++mi) acc[ni][mi] = mma_bf16(bf[q & 1][ni], af[q & 1][mi], acc[ni][mi]);
   }
 }
 
 // KG k-groups of 4 waves (KG = 2: 512 threads, two waves per SIMD to keep
 // more LDS reads in flight; the halves sum their accumulators through LDS in
 // a fixed order and each runs the epilogue of half the row blocks).
-template <int EPI, int TMW, int TNW, int KG>
+template <int EPI, int TMW, int TNW, int KG, int KS>
 __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   constexpr int NT = 256 * KG, NW = 4 * KG;
   constexpr int MB = 2 * TMW, NBK = 2 * TNW;          // row / column blocks of the tile
   constexpr int BM = 16 * MB, BN = 16 * NBK;
-  constexpr int FPS = (MB + NBK) * BIG_KS;            // fragments per stage
+  constexpr int FPS = (MB + NBK) * KS;                // fragments per stage (KS k-blocks of 32)
   constexpr int LPW = FPS / NW;                       // copies per wave per stage
-  constexpr int NJ = TNW * TMW;                       // accumulator blocks per wave
   constexpr int TME = TMW / KG;                       // row blocks of this wave's epilogue
-  static_assert(KG == 1 || (KG == 2 && TMW % 2 == 0), "k-groups: even row blocks (and no split K, below)");
+  static_assert(KG == 1 || (KG == 2 && TMW % 2 == 0), "k-groups: even row blocks");
   static_assert(BM * 8 % NT == 0, "norm-statistics pass");
   __shared__ __align__(16) uint8_t lds0[FPS * 1024], lds1[FPS * 1024], lds2[FPS * 1024];
   __shared__ float s_rstd[BM];
   __shared__ __align__(16) float s_col[2][BN];        // bias or alpha, gnext
-  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: fragment choice and LDS address are scalar
   const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = g.N / BN, T = tiles_m * tiles_n;
-  const int ks = blockIdx.x % g.ksplit;
   // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
   // a contiguous range of tiles, m fastest, so it shares weight columns
-  int t = blockIdx.x / g.ksplit;
+  int t = blockIdx.x;
   const int q8 = T / 8;
   if (t < 8 * q8) t = (t % 8) * q8 + t / 8;
   const int tm = t % tiles_m, tn = t / tiles_m;
   const int rb0 = tm * MB, nb0 = tn * NBK, m0 = tm * BM, n0 = tn * BN;
   const int KB = g.K >> 5, RB = g.mtiles * 4, NBT = g.N >> 4;
-  const int nstage = KB / BIG_KS / g.ksplit, st0 = ks * nstage;
+  const int nstage = KB / KS, st0 = 0;
   const uint16_t* A = (const uint16_t*)g.A;
   const uint16_t* W = (const uint16_t*)g.W;
 
@@ -769,7 +755,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
       for (int i = 0; i < 4; ++i) q[i][rr] = p[i];
     }
   }
-  const BigSrc<TMW, TNW, NW> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
+  const BigSrc<TMW, TNW, NW, KS> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
   const uint32_t a0 = lds_addr(lds0), a1 = lds_addr(lds1), a2 = lds_addr(lds2);
   // The workgroups of an XCD walk K together, so each k-slice of their
   // operands is fetched into that XCD's L2 once and only a few stages of it
@@ -792,18 +778,18 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
     wait_vmcnt<LPW>();
     barrier_nofence();
     srcs.issue(a2, wave, kst(s + 2));
-    big_compute<TMW, TNW, KG>(lds0, acc, kg, wm, wn, lane);
+    big_compute<TMW, TNW, KG, KS>(lds0, acc, kg, wm, wn, lane);
     if (s + 1 < nstage) {
       wait_vmcnt<LPW>();
       barrier_nofence();
       srcs.issue(a0, wave, kst(s + 3));
-      big_compute<TMW, TNW, KG>(lds1, acc, kg, wm, wn, lane);
+      big_compute<TMW, TNW, KG, KS>(lds1, acc, kg, wm, wn, lane);
     }
     if (s + 2 < nstage) {
       wait_vmcnt<LPW>();
       barrier_nofence();
       srcs.issue(a1, wave, kst(s + 4));
-      big_compute<TMW, TNW, KG>(lds2, acc, kg, wm, wn, lane);
+      big_compute<TMW, TNW, KG, KS>(lds2, acc, kg, wm, wn, lane);
     }
   }
   wait_vmcnt<0>();  // the trailing reloads
@@ -843,54 +829,6 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
       for (int m = 0; m < TME; ++m) fin[ni][m] = acc[ni][m];
   }
   const int mb0 = kg * TME;  // first row block of this wave's epilogue (KG = 2: by k-group)
-
-  // split K: every workgroup stores its partial tile; the last to arrive
-  // adds the partials in split order and goes on to the epilogue
-  if constexpr (EPI == EPI_RESID && KG == 1) if (g.ksplit > 1) {
-    float* mine = g.partials + (((long)t * g.ksplit + ks) * NJ * 256 + tid) * 4;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const f32x4 v = fin[j / TMW][j % TMW];
-      st_dev2(mine + j * 1024, v[0], v[1]);
-      st_dev2(mine + j * 1024 + 2, v[2], v[3]);
-    }
-    drain_vm();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(g.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == (unsigned)g.ksplit - 1;
-      if (s_last) __hip_atomic_store(g.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // partials two splits at a time (ksplit <= 4), every load of a pair
-    // issued before any is used; the own split comes from the registers
-    f32x4 sum[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k0 = 0; k0 < 4; k0 += 2) {
-      if (k0 >= g.ksplit) break;
-      const float* pa = g.partials + (((long)t * g.ksplit + k0) * NJ * 256 + tid) * 4;
-      const float* pb = g.partials + (((long)t * g.ksplit + min(k0 + 1, g.ksplit - 1)) * NJ * 256 + tid) * 4;
-      f32x4 va[NJ], vb[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const float2 x0 = ld_dev2(pa + j * 1024), x1 = ld_dev2(pa + j * 1024 + 2);
-        const float2 y0 = ld_dev2(pb + j * 1024), y1 = ld_dev2(pb + j * 1024 + 2);
-        va[j] = f32x4{x0.x, x0.y, x1.x, x1.y};
-        vb[j] = f32x4{y0.x, y0.y, y1.x, y1.y};
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const f32x4 own = fin[j / TMW][j % TMW];
-        sum[j] += (k0 == ks) ? own : va[j];
-        if (k0 + 1 < g.ksplit) sum[j] += (k0 + 1 == ks) ? own : vb[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) fin[j / TMW][j % TMW] = sum[j];
-  }
 
   // the epilogue's LDS tables
   if (tid < BN) {
@@ -1957,12 +1895,12 @@ static hipError_t gemm_upw(const GemmArgs& g, int grid, hipStream_t st) {
 // large M, bf16: the LDS-staged MFMA GEMM (tile plan shared with the engine)
 static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err) {
   const BigPlan p = big_plan(epi, g.M, g.N, g.K);
-  if (!p.used || g.ksplit != p.ks) return false;
-  const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN) * p.ks;
-  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2>), dim3(grid), dim3(512), 0, st, g);
-  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1>), dim3(grid), dim3(256), 0, st, g);
-  else if (p.ks == 1) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 1>), dim3(grid), dim3(256), 0, st, g);
+  if (!p.used || g.ksplit != 1) return false;
+  const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
+  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2, 2>), dim3(grid), dim3(512), 0, st, g);
+  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+  else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 4>), dim3(grid), dim3(512), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
   *err = hipGetLastError();
   return true;
 }
