@@ -40,6 +40,8 @@ def test_tiny_fp32():
     dict(head_dim=128, prefix_static=1000, prefix_len=1000), # attention: 1016 padded keys, largest register tile
     dict(prefix_static=1100, prefix_len=1100, chunk=9),      # attention: > 1024 keys, flash kernel
     dict(batch=12, chunk=30, prefix_static=150, prefix_len=150),  # 372 rows: LDS-staged MFMA GEMMs, ragged m-tile
+    dict(batch=12, chunk=30, n_q_heads=3, d_mlp=320, prefix_static=150, prefix_len=150),  # residual GEMMs with
+    #   64-k stages (K % 128 = 64), gate/up on the skinny path next to large-M QKV / residual GEMMs
     dict(batch=20, chunk=60, n_q_heads=8, prefix_static=100, prefix_len=100),  # attention: 2 query blocks/workgroup
     dict(head_dim=128, prefix_static=600, prefix_len=200),  # attention key split, ranges mostly masked
     dict(head_dim=256, n_q_heads=2, prefix_static=600, prefix_len=0),  # key split, whole ranges masked
