@@ -334,6 +334,18 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
     at.scale = 1.f / sqrtf((float)x->Dh);
     at.part = x->attn_part; at.counters = x->counters;
     at.out = x->o;
+    if (x->mtiles == 1 && x->act == ELT_BF16) {
+      // one row tile: the O and gate/up GEMMs run skinny, workgroup u reading
+      // column tile u / ks and k-range u % ks; the idle CUs prefetch them
+      const int ku = x->wt == ELT_FP8 ? 64 : 32;  // k per 1 KB weight tile
+      at.pf_cus = x->n_cu;
+      at.pf_w[0] = (const uint8_t*)w.wo;
+      at.pf_nbt[0] = x->d / 16; at.pf_ku[0] = x->Hq * x->Dh / ku; at.pf_nb[0] = 1; at.pf_ks[0] = x->ks_o;
+      at.pf_units[0] = x->d / 16 * x->ks_o;
+      at.pf_w[1] = (const uint8_t*)w.wgu;
+      at.pf_nbt[1] = 2 * x->F / 16; at.pf_ku[1] = x->d / ku; at.pf_nb[1] = 2; at.pf_ks[1] = 1;
+      at.pf_units[1] = x->F / 16;
+    }
     HIPCHK(x, launch_attn(x->act, at, st), "attention");
   } else if (phase == FM_PHASE_OPROJ) {  // O projection + residual; u = act(h * g2), ssq
     g.A = x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16; g.ksplit = x->ks_o;

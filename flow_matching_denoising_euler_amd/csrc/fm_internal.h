@@ -94,6 +94,16 @@ struct AttnArgs {
   float* part;            // key-range partials: per (query group, range) 16 x Dh outputs, 16 maxima, 16 sums
   unsigned* counters;
   void* out;              // [B*S][Hq*Dh] act
+  // Weight prefetch by the CUs the attention grid leaves idle (one row tile,
+  // skinny GEMMs next): workgroups past the attention grid read the packed
+  // weights of the following GEMMs (1 KB tiles) into the L2 of the XCD whose
+  // workgroups will read them.  Matrix i is read by nunits[i] workgroups;
+  // workgroup u (on XCD u % 8) reads column blocks [(u / ks) * nb, + nb) and
+  // k-units [(u % ks) * ku / ks, + ku / ks).
+  int pf_cus;             // CUs of the device (0: no prefetch)
+  int grid;               // attention workgroups (set by the launcher)
+  const uint8_t* pf_w[2]; // packed weights (null: none)
+  int pf_nbt[2], pf_ku[2], pf_nb[2], pf_ks[2], pf_units[2];
 };
 
 struct OutArgs {

@@ -1170,8 +1170,42 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 //     V fragments streamed VQ blocks ahead, scales by 1 / sum and stores.
 // Every global load of a phase is issued before its first use; there is no
 // online rescaling and, for DH >= 128, no merge of partial outputs.
-template <int DH, int R, int QB, int DS>
+// Workgroups past the attention grid: read the tiles of the next GEMMs'
+// packed weights that the workgroups of this XCD will read into this XCD's
+// L2 (the consuming workgroup u runs on XCD u % 8).  The prefetchers of an
+// XCD take its units round robin; each wave reads every 8th tile of a unit.
+__device__ __forceinline__ void attn_weight_prefetch(const AttnArgs& a) {
+  const int x = blockIdx.x & 7;
+  const int first = (a.grid - x + 7) >> 3;           // attention workgroups on this XCD
+  const int total = ((int)gridDim.x - x + 7) >> 3;   // all workgroups on this XCD
+  const int j = ((int)blockIdx.x >> 3) - first, nx = total - first;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (!a.pf_w[m]) continue;
+    const int ks = a.pf_ks[m], nb = a.pf_nb[m], kur = a.pf_ku[m] / ks, tiles = nb * kur;
+    for (int u = x + 8 * j; u < a.pf_units[m]; u += 8 * nx) {
+      const int nb0 = (u / ks) * nb, ku0 = (u % ks) * kur;
+#pragma unroll 8
+      for (int t = w; t < tiles; t += 8) {
+        const int kb = ku0 + t / nb, c = nb0 + t % nb;
+        const uint4 v = *(const uint4*)(a.pf_w[m] + ((long)kb * a.pf_nbt[m] + c) * 1024 + lane * 16);
+        acc ^= v.x ^ v.w;
+      }
+    }
+  }
+  asm volatile("" ::"v"(acc));  // the loaded values are used: the loads stay
+}
+
+template <int DH, int R, int QB, int DS, bool PF>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
+  // weight prefetch workgroups (a separate instantiation: the test needs a
+  // kernel argument before the first load)
+  if constexpr (PF) if ((int)blockIdx.x >= a.grid) {
+    attn_weight_prefetch(a);
+    return;
+  }
   constexpr int KBD = DH / 32, NBD = DH / 16, QR = 16 * QB;
   // DS workgroups share a query block: each computes all scores and the
   // softmax, and the P V product for its 1/DS of the head dims (V traffic per
@@ -1196,7 +1230,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // a contiguous range of (robot, kv head, query block), so a robot's K/V
   // are fetched into one XCD's L2 rather than into all eight
   int wg = blockIdx.x;
-  const int q8 = gridDim.x / 8;
+  const int q8 = a.grid / 8;
   if (wg < 8 * q8) wg = (wg % 8) * q8 + wg / 8;
   const int ds = wg % DS;                              // head-dim part of the output
   wg /= DS;
@@ -1927,23 +1961,32 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   return hipErrorInvalidValue;
 }
 
+template <int DH, int QB, int DS, bool PF>
+static hipError_t attn_sf_r(const AttnArgs& a, int grid, hipStream_t st) {
+  switch ((a.keys_per_split + 7) / 8) {  // R: 16-key blocks per wave
+    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS, PF>), grid, 512, a);
+    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS, PF>), grid, 512, a);
+    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS, PF>), grid, 512, a);
+    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS, PF>), grid, 512, a);
+    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS, PF>), grid, 512, a);
+    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS, PF>), grid, 512, a);
+    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS, PF>), grid, 512, a);
+    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS, PF>), grid, 512, a);
+  }
+  return hipErrorInvalidValue;
+}
 template <int DH, int QB, int DS>
 static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
   if (QB > 1 || DH < 128) a.nsplit = 1;  // the key split runs with one query block, head_dim >= 128
   if (a.nsplit == 1) a.keys_per_split = ((a.TP + a.SP) / 16 + 1) / 2 * 2;
   a.nqblk = (a.S * (a.Hq / a.Hkv) + 16 * QB - 1) / (16 * QB);
-  const int grid = a.B * a.Hkv * a.nqblk * a.nsplit * DS;
-  switch ((a.keys_per_split + 7) / 8) {  // R: 16-key blocks per wave
-    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS>), grid, 512, a);
-    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS>), grid, 512, a);
-    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS>), grid, 512, a);
-    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS>), grid, 512, a);
-    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS>), grid, 512, a);
-    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS>), grid, 512, a);
-    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS>), grid, 512, a);
-    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS>), grid, 512, a);
-  }
-  return hipErrorInvalidValue;
+  a.grid = a.B * a.Hkv * a.nqblk * a.nsplit * DS;
+  // weight prefetchers on the idle CUs, if at least half of them are idle
+  // (fewer would stretch the attention launch by more than they save)
+  const int idle = a.pf_cus - a.grid;
+  if constexpr (DS == 2)
+    if ((a.pf_w[0] || a.pf_w[1]) && 2 * idle >= a.pf_cus) return attn_sf_r<DH, QB, DS, true>(a, a.grid + idle, st);
+  return attn_sf_r<DH, QB, DS, false>(a, a.grid, st);
 }
 
 // up to 1024 padded keys: the register-resident kernel, two query blocks per
