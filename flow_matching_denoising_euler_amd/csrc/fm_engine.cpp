@@ -194,14 +194,11 @@ void derive(fm_ctx* x) {
   x->P = 128;  // h^2 partial slots per row (one per 16 columns; unused slots stay zero)
   x->mtiles = (x->M + 63) / 64;
   x->esplit = x->d / 64;
-  const int unit = x->wt == ELT_FP8 ? 2 : 1;
-  (void)unit;
   // K splits of the residual GEMMs: none on the large-M path
   x->ks_o = 1;
   x->ks_d = 1;
-  const BigPlan po = big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh);
-  if (x->act == ELT_BF16 && x->wt == ELT_BF16 && po.used) {
-  } else if (x->act == ELT_BF16) {
+  const bool large_m = x->wt == ELT_BF16 && big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh).used;
+  if (x->act == ELT_BF16 && !large_m) {
     // skinny residual GEMMs: split K so that about 256 workgroups each read a
     // quarter of the shared activation operand (it dominates their bytes)
     const int tiles = x->mtiles * (x->d / 16), unit = x->wt == ELT_FP8 ? 64 : 32;
