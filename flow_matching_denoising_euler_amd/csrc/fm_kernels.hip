@@ -1211,7 +1211,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // softmax, and the P V product for its 1/DS of the head dims (V traffic per
   // workgroup / DS, no merge)
   constexpr int NBD3 = NBD / DS;
-  static_assert(DS == 1 || (QB == 1 && NBD3 >= 8), "dim split: one query block, 8 or more output blocks");
+  static_assert(DS == 1 || (QB == 1 && NBD3 >= 4), "dim split: one query block, 4 or more output blocks");
   // K and V blocks in flight per wave, within about 240 registers
   constexpr int KQ0 = (QB == 1 ? (R <= 4 ? 24 : 16) : (R <= 4 ? 16 : 8)) / KBD;
   constexpr int KQ = KQ0 < 1 ? 1 : (KQ0 < R ? KQ0 : R);
@@ -1491,8 +1491,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if constexpr (KG > 1) {
     __syncthreads();
-    for (int e = tid; e < QR * DH; e += 512) {
-      const int row = e / DH, c = e % DH;
+    for (int e = tid; e < QR * DH / DS; e += 512) {
+      const int row = e / (DH / DS), c = ds * (DH / DS) + e % (DH / DS);
       float v = 0.f;
 #pragma unroll
       for (int g = 0; g < KG; ++g) v += s_o[(g * QR + row) * (DH + 4) + c];
@@ -1980,11 +1980,12 @@ static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
   if (QB > 1 || DH < 128) a.nsplit = 1;  // the key split runs with one query block, head_dim >= 128
   if (a.nsplit == 1) a.keys_per_split = ((a.TP + a.SP) / 16 + 1) / 2 * 2;
   a.nqblk = (a.S * (a.Hq / a.Hkv) + 16 * QB - 1) / (16 * QB);
+  if (DS > 2 && a.nsplit > 1) return hipErrorInvalidValue;  // the range merge needs one key group in P V
   a.grid = a.B * a.Hkv * a.nqblk * a.nsplit * DS;
   // weight prefetchers on the idle CUs, if at least half of them are idle
   // (fewer would stretch the attention launch by more than they save)
   const int idle = a.pf_cus - a.grid;
-  if constexpr (DS == 2)
+  if constexpr (DS >= 2)
     if ((a.pf_w[0] || a.pf_w[1]) && 2 * idle >= a.pf_cus) return attn_sf_r<DH, QB, DS, true>(a, a.grid + idle, st);
   return attn_sf_r<DH, QB, DS, false>(a, a.grid, st);
 }
@@ -1998,8 +1999,12 @@ static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (nk32 <= 32) {
     const int groups = a.B * a.Hkv * a.nqblk;
     if (groups > 256) return attn_sf<DH, 2, 1>(a, st);
-    // few query groups: two workgroups per query block (and key range)
-    if constexpr (DH == 256) if (groups <= 128) return attn_sf<DH, 1, 2>(a, st);
+    // few query groups: two workgroups per query block (and key range), four
+    // when there is no key split (two key groups of waves in P V)
+    if constexpr (DH == 256) {
+      if (groups <= 64 && a.nsplit == 1) return attn_sf<DH, 1, 4>(a, st);
+      if (groups <= 128) return attn_sf<DH, 1, 2>(a, st);
+    }
     return attn_sf<DH, 1, 1>(a, st);
   }
   hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
