@@ -539,7 +539,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
   if (s != FM_OK) return s;
   if ((s = validate_weights(cfg, w)) != FM_OK) return s;
   if (cfg->exec_mode == FM_EXEC_PERSISTENT)
-    return fail(nullptr, FM_ERR_UNSUPPORTED, "persistent execution is not available in this build");
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "persistent execution is not implemented; the loop runs as a graph of kernels");
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -716,7 +716,11 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
   info->kv_bytes_per_step = kv * x->L * x->HD * ea * 2;
   info->exec_mode = x->exec_mode;
   info->n_phases = x->N * (5 * x->L + 1) + 1;
-  info->grid = x->mtiles * (2 * x->F / 32);
+  {
+    const BigPlan pg = big_plan(EPI_GELU, x->M, 2 * x->F, x->d);
+    const bool big = x->act == ELT_BF16 && x->wt == ELT_BF16 && pg.used;
+    info->grid = big ? (x->M + pg.BM - 1) / pg.BM * (2 * x->F / pg.BN) : x->mtiles * (2 * x->F / 32);
+  }
   info->n_cu = x->n_cu;
   return FM_OK;
 }

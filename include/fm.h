@@ -68,13 +68,16 @@ typedef enum {
 typedef enum { FM_F32 = 0, FM_BF16 = 1, FM_FP8_E4M3 = 2 } fm_dtype;
 typedef enum { FM_RMSNORM = 0, FM_ADARMSNORM = 1 } fm_norm;
 
-/* How fm_denoise issues the loop.  FM_EXEC_AUTO picks the persistent
- * kernel when the device can hold its grid, else the graph of kernels.
- * Both run the same device code and give bitwise-identical results. */
+/* How fm_denoise issues the loop.  FM_EXEC_AUTO and FM_EXEC_GRAPH run one
+ * hipGraph of per-phase kernel launches.  FM_EXEC_PERSISTENT (one cooperative
+ * kernel with grid barriers between phases) is reserved: fm_create rejects
+ * it with FM_ERR_UNSUPPORTED, because on MI355X a grid barrier plus the
+ * re-read of the activations each phase needs costs more than a graph
+ * node. */
 typedef enum {
   FM_EXEC_AUTO = 0,
   FM_EXEC_GRAPH = 1,       /* one hipGraph of per-phase kernel launches   */
-  FM_EXEC_PERSISTENT = 2   /* one cooperative kernel for the whole loop   */
+  FM_EXEC_PERSISTENT = 2   /* reserved; rejected (FM_ERR_UNSUPPORTED)     */
 } fm_exec;
 
 /*
@@ -152,9 +155,9 @@ typedef struct {
   size_t arena_bytes;               /* device memory held by the context    */
   size_t weight_bytes_per_step;     /* weight bytes one Euler step streams  */
   size_t kv_bytes_per_step;         /* prefix K/V bytes one step reads      */
-  int32_t exec_mode;                /* mode actually used (GRAPH/PERSISTENT) */
+  int32_t exec_mode;                /* mode actually used (FM_EXEC_GRAPH)   */
   int32_t n_phases;                 /* device phases per fm_denoise         */
-  int32_t grid;                     /* workgroups per phase / persistent grid */
+  int32_t grid;                     /* workgroups of the gate/up GEMM launch */
   int32_t n_cu;                     /* compute units of the device          */
 } fm_info;
 
