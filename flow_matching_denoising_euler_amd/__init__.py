@@ -51,6 +51,11 @@ def make_config(cfg, exec_mode: int = FM_EXEC_AUTO) -> fm_config:
     c.act_dtype = _DT[cfg.act_dtype]
     c.rms_eps = float(cfg.rms_eps)
     c.exec_mode = int(exec_mode)
+    sched = getattr(cfg, "t_schedule", None)
+    if sched is not None:
+        arr = (ctypes.c_float * len(sched))(*[float(t) for t in sched])
+        c.t_schedule = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+        c._t_schedule_keep = arr  # alive as long as the config
     return c
 
 

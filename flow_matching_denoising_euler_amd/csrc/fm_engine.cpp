@@ -77,6 +77,9 @@ struct fm_ctx {
 
   // host mirror of the prefix state
   std::vector<int> valid, head;
+  std::vector<double> tk;   // t_k of step k (N values)
+  std::vector<float> dtk;   // dt_k = t_(k+1) - t_k, applied by step k's tail
+  double* tkd = nullptr;    // device copy of tk
   std::vector<char> is_set;
 
   hipGraph_t graph = nullptr;
@@ -131,6 +134,13 @@ fm_status validate_config(const fm_config* c) {
   if ((c->n_frames > 0) != (c->frame_tokens > 0))
     return fail(nullptr, FM_ERR_SHAPE, "n_frames and frame_tokens must both be zero or both positive");
   if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, FM_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+  if (c->t_schedule) {
+    // t_0 = 1 > t_1 > ... > t_N = 0, all finite
+    const float* t = c->t_schedule;
+    if (t[0] != 1.f || t[c->n_steps] != 0.f) return fail(nullptr, FM_ERR_ARG, "t_schedule must run from 1 to 0");
+    for (int k = 0; k < c->n_steps; ++k)
+      if (!(t[k + 1] < t[k])) return fail(nullptr, FM_ERR_ARG, "t_schedule must decrease strictly (step %d)", k);
+  }
   if (c->norm == FM_RMSNORM && c->time_dim != c->d_model)
     return fail(nullptr, FM_ERR_SHAPE, "RMSNorm expert: time_dim must equal d_model");
   if (c->norm == FM_ADARMSNORM && (c->time_dim <= 0 || c->time_dim % 2))
@@ -186,6 +196,18 @@ void derive(fm_ctx* x) {
   x->S = x->C + x->hasS; x->M = x->B * x->S;
   x->d = c.d_model; x->L = c.n_layers; x->Hq = c.n_q_heads; x->Hkv = c.n_kv_heads; x->Dh = c.head_dim;
   x->F = c.d_mlp; x->N = c.n_steps; x->HD = x->Hkv * x->Dh;
+  // step schedule: t_k = 1 - k/N and dt = -1/N, or the caller's times (dt_k
+  // from the difference of two fp32 times, exact in double, rounded once)
+  x->tk.assign(x->N, 0.0);
+  x->dtk.assign(x->N, -1.f / (float)x->N);
+  for (int k = 0; k < x->N; ++k) {
+    if (c.t_schedule) {
+      x->tk[k] = (double)c.t_schedule[k];
+      x->dtk[k] = (float)((double)c.t_schedule[k + 1] - (double)c.t_schedule[k]);
+    } else {
+      x->tk[k] = 1.0 - (double)k / (double)x->N;
+    }
+  }
   x->Nqkv = (x->Hq + 2 * x->Hkv) * x->Dh;
   x->Tcap = c.prefix_static + c.n_frames * c.frame_tokens;
   x->NSP = (c.prefix_static + 31) / 32 * 32;
@@ -249,6 +271,7 @@ void carve(fm_ctx* x, Arena& a) {
   x->w_state = x->hasS ? a.take((size_t)d * x->SD * eg) : nullptr;
   x->b_state = x->hasS ? a.take(d * eg) : nullptr;
   x->temb = ada ? nullptr : (float*)a.take(N * d * 4);
+  x->tkd = (double*)a.take(N * 8);
   const long gsz = ada ? N * L * d : L * d;
   x->g1 = (float*)a.take(gsz * 4);
   x->g2 = (float*)a.take(gsz * 4);
@@ -385,7 +408,7 @@ fm_status enqueue_tail(fm_ctx* x, int k, hipStream_t st, float* x_final) {
   o.bout = T(x->bout, x->st_bout);
   o.x_in = (k & 1) ? x->xbuf1 : x->xbuf0;
   o.x_out = x_final ? x_final : ((k & 1) ? x->xbuf0 : x->xbuf1);
-  o.dt = -1.f / (float)x->N;
+  o.dt = x->dtk[k];
   o.B = x->B; o.S = x->S; o.C = x->C; o.A = x->A; o.d = x->d; o.M = x->M; o.has_state = x->hasS;
   o.mtiles = x->mtiles; o.esplit = x->esplit;
   o.do_embed = k + 1 < x->N;
@@ -443,7 +466,7 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     beta2 = (float*)tmalloc(N * L * d * 4);
     betaf = (float*)tmalloc(N * d * 4);
     if (!c || !beta1 || !beta2 || !betaf) { cleanup(); return fail(x, FM_ERR_OOM, "temporary time tables"); }
-    hipError_t e = launch_ada_c(w->w_time, w->b_time, src, x->N, x->cfg.time_dim, x->d, c, st);
+    hipError_t e = launch_ada_c(w->w_time, w->b_time, src, x->tkd, x->N, x->cfg.time_dim, x->d, c, st);
     if (e != hipSuccess) { cleanup(); return hip_fail(x, e, "ada time mlp"); }
   }
   hipError_t e = hipSuccess;
@@ -508,7 +531,7 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
         "beta_f W_out");
   } else {
     CHK(launch_copy_convert(w->norm_f, src, d, x->gf, st), "final gain");
-    CHK(launch_time_add(x->temb, x->N, x->d, st), "time features");
+    CHK(launch_time_add(x->temb, x->tkd, x->N, x->d, st), "time features");
   }
   CHK(launch_pack(w->w_out, src, x->A, x->d, RowMap{x->A, 0, 0}, x->wout, src, x->A, st), "pack w_out");
   CHK(hipMemcpyAsync(x->w_in, w->w_in, (size_t)d * x->A * eg, hipMemcpyDeviceToDevice, st), "copy w_in");
@@ -556,6 +579,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
   x->n_cu = prop.multiProcessorCount;
   x->exec_mode = FM_EXEC_GRAPH;
   derive(x);
+  x->cfg.t_schedule = nullptr;  // the caller's array is read during fm_create only
   Arena a;
   carve(x, a);
   x->arena_bytes = a.off;
@@ -588,6 +612,11 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
       hip_fail(x, e, "ones table");
       return bail(FM_ERR_DEVICE);
     }
+  }
+  if ((e = hipMemcpyAsync(x->tkd, x->tk.data(), x->tk.size() * sizeof(double), hipMemcpyHostToDevice, st)) !=
+      hipSuccess) {
+    hip_fail(x, e, "schedule table");
+    return bail(FM_ERR_DEVICE);
   }
   if ((s = load_weights(x, w, st)) != FM_OK) return bail(s);
   // the graph: every step's layers and tails except the last tail

@@ -184,8 +184,8 @@ hipError_t launch_quantize_e4m3(const void* w_bf16, int rows, int cols, uint8_t*
 hipError_t launch_scatter_scales(const float* s, int rows, RowMap rm, float* dst, hipStream_t st);
 hipError_t launch_copy_convert(const void* src, int src_elt, long n, float* dst, hipStream_t st);
 // time tables
-hipError_t launch_time_add(float* temb, int n_steps, int d, hipStream_t st);
-hipError_t launch_ada_c(const void* w_t, const void* b_t, int wt, int n_steps, int time_dim, int d,
+hipError_t launch_time_add(float* temb, const double* tk, int n_steps, int d, hipStream_t st);
+hipError_t launch_ada_c(const void* w_t, const void* b_t, int wt, const double* tk, int n_steps, int time_dim, int d,
                         float* c, hipStream_t st);
 hipError_t launch_ada_mod(const float* c, int n_steps, int d, const void* w_n, const void* b_n, int wt,
                           float* gam1p, float* beta, float* alpha, long tab_step_stride, hipStream_t st);

@@ -1799,27 +1799,29 @@ __global__ void k_copy_convert(const void* src, int src_elt, long n, float* dst)
     dst[i] = ld_w(src, src_elt, i);
 }
 
-// sinusoidal features [sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(D/2)), t_k = 1 - k/N
-__device__ __forceinline__ double sinusoid_d(int k, int n_steps, int D, int i) {
-  const double t = 1.0 - (double)k / (double)n_steps;
+// sinusoidal features [sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(D/2))
+__device__ __forceinline__ double sinusoid_d(double t, int D, int i) {
   const int half = D / 2, jj = i < half ? i : i - half;
   const double w = pow(10000.0, -(double)jj / (double)half);
   return i < half ? sin(t * w) : cos(t * w);
 }
 
-__global__ void k_time_add(float* temb, int n_steps, int d) {
+// step k's feature row, t_k from the schedule tk
+__global__ void k_time_add(float* temb, const double* tk, int d) {
   const int k = blockIdx.y;
+  const double t = tk[k];
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < d; i += gridDim.x * blockDim.x)
-    temb[(long)k * d + i] = (float)sinusoid_d(k, n_steps, d, i);
+    temb[(long)k * d + i] = (float)sinusoid_d(t, d, i);
 }
 
-// c[k][j] = SiLU(sum_i tau_k[i] W_t[j][i] + b_t[j])
-__global__ void k_ada_c(const void* w_t, const void* b_t, int wt, int n_steps, int time_dim, int d, float* c) {
+// c[k][j] = SiLU(sum_i tau(t_k)[i] W_t[j][i] + b_t[j])
+__global__ void k_ada_c(const void* w_t, const void* b_t, int wt, const double* tk, int time_dim, int d, float* c) {
   const int k = blockIdx.y;
   const int jj = blockIdx.x * blockDim.x + threadIdx.x;
   if (jj >= d) return;
+  const double t = tk[k];
   double acc = 0.0;
-  for (int i = 0; i < time_dim; ++i) acc += sinusoid_d(k, n_steps, time_dim, i) * (double)ld_w(w_t, wt, (long)jj * time_dim + i);
+  for (int i = 0; i < time_dim; ++i) acc += sinusoid_d(t, time_dim, i) * (double)ld_w(w_t, wt, (long)jj * time_dim + i);
   acc += (double)ld_w(b_t, wt, jj);
   c[(long)k * d + jj] = (float)(acc / (1.0 + exp(-acc)));
 }
@@ -2060,14 +2062,14 @@ hipError_t launch_copy_convert(const void* src, int src_elt, long n, float* dst,
   FM_LAUNCH(k_copy_convert, grid > 0 ? grid : 1, src, src_elt, n, dst);
 }
 
-hipError_t launch_time_add(float* temb, int n_steps, int d, hipStream_t st) {
-  hipLaunchKernelGGL(k_time_add, dim3((d + 255) / 256, n_steps), dim3(256), 0, st, temb, n_steps, d);
+hipError_t launch_time_add(float* temb, const double* tk, int n_steps, int d, hipStream_t st) {
+  hipLaunchKernelGGL(k_time_add, dim3((d + 255) / 256, n_steps), dim3(256), 0, st, temb, tk, d);
   return hipGetLastError();
 }
 
-hipError_t launch_ada_c(const void* w_t, const void* b_t, int wt, int n_steps, int time_dim, int d, float* c,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(k_ada_c, dim3((d + 255) / 256, n_steps), dim3(256), 0, st, w_t, b_t, wt, n_steps, time_dim, d, c);
+hipError_t launch_ada_c(const void* w_t, const void* b_t, int wt, const double* tk, int n_steps, int time_dim, int d,
+                        float* c, hipStream_t st) {
+  hipLaunchKernelGGL(k_ada_c, dim3((d + 255) / 256, n_steps), dim3(256), 0, st, w_t, b_t, wt, tk, time_dim, d, c);
   return hipGetLastError();
 }
 

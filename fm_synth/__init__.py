@@ -19,7 +19,7 @@ Shapes follow the pages' workloads:
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -61,6 +61,7 @@ class FMConfig:
     act_dtype: str          # "f32", "bf16"
     rms_eps: float = 1e-6
     ticks: int = 0          # streaming ticks (0: not a streaming workload)
+    t_schedule: Optional[Tuple[float, ...]] = None  # n_steps + 1 times, 1 -> 0 (None: uniform)
 
     @property
     def has_state(self) -> int:

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 1
+#define FM_ABI_VERSION 2
 
 typedef struct fm_ctx fm_ctx;
 
@@ -86,8 +86,12 @@ typedef enum {
  * L n_layers, Hq/Hkv heads, Dh head_dim, F d_mlp, N n_steps.
  *
  * Time runs from t = 1 (the noise) to t = 0 (the actions): step k = 0..N-1
- * evaluates the velocity at t_k = 1 - k/N and applies dt = -1/N (the pages
- * fix the step count, not the direction; this is the reading taken).
+ * evaluates the velocity at t_k and applies dt_k = t_(k+1) - t_k.  By default
+ * t_k = 1 - k/N (uniform steps, dt = -1/N; the pages fix the step count, not
+ * the direction: this is the reading taken).  t_schedule, when not NULL, is a
+ * HOST array of the N + 1 times t_0 = 1 > t_1 > ... > t_N = 0 (fp32, read
+ * during fm_create only; anything else is FM_ERR_ARG): the step schedule,
+ * chosen separately from the model (InstinctFlash README, "Load a model").
  *
  * norm = FM_RMSNORM: RMSNorm with a gain; sinusoidal features of t, d wide
  *   ([sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(d/2))), are added to the
@@ -121,6 +125,7 @@ typedef struct {
   int32_t act_dtype;                 /* fm_dtype: FM_F32 or FM_BF16 */
   float rms_eps;                     /* e.g. 1e-6 */
   int32_t exec_mode;                 /* fm_exec  */
+  const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
 } fm_config;
 
 /* Per-layer weight slots of fm_weights.layers. */

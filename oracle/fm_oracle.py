@@ -29,7 +29,11 @@ What the method computes, and where the pages fix it
 Readings taken where the pages are silent
 -----------------------------------------
 * Time runs from t=1 (noise) to t=0 (action); dt = -1/N; the velocity at
-  step k is evaluated at the left end t_k = 1 - k/N, computed directly.
+  step k is evaluated at the left end t_k = 1 - k/N, computed directly.  A
+  caller may instead give the step schedule (step schedules are chosen
+  separately from the model: InstinctFlash README, "Load a model"): N + 1
+  times 1 = s_0 > ... > s_N = 0, step k evaluating at s_k with dt_k =
+  s_(k+1) - s_k.
 * Sinusoidal time features: [sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(D/2)),
   j < D/2, t unscaled.  Additive experts add the d-wide feature to the
   action tokens only (not the state token); the AdaRMSNorm expert takes
@@ -72,12 +76,19 @@ F64 = np.float64
 # ---------------------------------------------------------------------------
 # Schedule and time features
 # ---------------------------------------------------------------------------
-def time_grid(n_steps: int) -> Tuple[np.ndarray, float]:
-    """Euler schedule t_k = 1 - k/N, k = 0..N-1, and dt = -1/N (see module
-    docstring: direction and left-endpoint evaluation are this code's
-    reading; the step count is the pages' 10 flow steps)."""
-    k = np.arange(n_steps, dtype=F64)
-    return 1.0 - k / n_steps, -1.0 / n_steps
+def time_grid(n_steps: int, schedule: Optional[Sequence[float]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Euler schedule: the times t_k and steps dt_k, k = 0..N-1.  Default
+    t_k = 1 - k/N and dt_k = -1/N (see module docstring: direction and
+    left-endpoint evaluation are this code's reading; the step count is the
+    pages' 10 flow steps).  With a schedule s (N + 1 times from 1 down to 0,
+    rounded to fp32 as at the library boundary): t_k = s_k, dt_k = s_(k+1) - s_k."""
+    if schedule is None:
+        k = np.arange(n_steps, dtype=F64)
+        return 1.0 - k / n_steps, np.full(n_steps, -1.0 / n_steps)
+    s = np.asarray(schedule, dtype=np.float32).astype(F64)
+    if s.shape != (n_steps + 1,) or s[0] != 1.0 or s[-1] != 0.0 or not np.all(np.diff(s) < 0):
+        raise ValueError("schedule: n_steps + 1 strictly decreasing times from 1 to 0")
+    return s[:-1], np.diff(s)
 
 
 def sinusoid(t: float, dim: int) -> np.ndarray:
@@ -308,11 +319,11 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
 
 
 def euler(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
-          n_steps: int) -> np.ndarray:
-    """x_{k+1} = x_k + dt * v(x_k, t_k) over the schedule of time_grid."""
-    ts, dt = time_grid(n_steps)
+          n_steps: int, schedule: Optional[Sequence[float]] = None) -> np.ndarray:
+    """x_{k+1} = x_k + dt_k * v(x_k, t_k) over the schedule of time_grid."""
+    ts, dts = time_grid(n_steps, schedule)
     x = np.asarray(x0, F64).copy()
-    for t in ts:
+    for t, dt in zip(ts, dts):
         x = x + dt * velocity(x, float(t))
     return x
 
@@ -320,7 +331,7 @@ def euler(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
 def denoise_robot(cfg, W64: dict, k_pre, v_pre, noise, state) -> np.ndarray:
     """One robot's action chunk x at t=0 from its noise at t=1."""
     return euler(lambda x, t: expert_velocity(cfg, W64, x, t, k_pre, v_pre, state),
-                 noise, cfg.n_steps)
+                 noise, cfg.n_steps, getattr(cfg, "t_schedule", None))
 
 
 def denoise(cfg, W: dict, k_pre, v_pre, noise, state=None,
@@ -439,5 +450,5 @@ def denoise_joint(cfg, W: dict, Wp: dict, tokens, noise, state=None) -> np.ndarr
     for b in range(noise.shape[0]):
         st = None if state is None else state[b]
         out.append(euler(lambda x, t: joint_velocity(cfg, W64, Wp64, tokens[b], x, t, st),
-                         noise[b], cfg.n_steps))
+                         noise[b], cfg.n_steps, getattr(cfg, "t_schedule", None)))
     return np.stack(out)

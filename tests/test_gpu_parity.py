@@ -200,6 +200,44 @@ def test_small_ring_bf16_key_split():
     _ring_run(cfg, ticks=5, oracle_ticks={4})
 
 
+# --- step schedules (InstinctFlash README, "Load a model": chosen separately from the model) ---
+def shifted_schedule(n, shift=3.0):
+    """t = shift u / (1 + (shift - 1) u) at u = 1 - k/n: more steps near t = 0."""
+    u = [1.0 - k / n for k in range(n + 1)]
+    return tuple(shift * x / (1.0 + (shift - 1.0) * x) for x in u)
+
+
+def test_schedule_of_exact_uniform_times_is_the_default_bitwise():
+    cfg = small_cfg(n_steps=8)
+    W, k, v, x0, st = _inputs(cfg)
+    announce("schedule k/8 vs default")
+    a = run_denoiser(cfg, W, k, v, x0, st)[0]
+    b = run_denoiser(cfg.replace(t_schedule=tuple(1.0 - i / 8 for i in range(9))), W, k, v, x0, st)[0]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("norm", ["rms", "ada"])
+def test_small_shifted_schedule(norm):
+    kw = dict(norm="ada", time_dim=32, state_dim=0) if norm == "ada" else {}
+    cfg = small_cfg(n_steps=6, t_schedule=shifted_schedule(6), **kw)
+    announce(f"small {norm}, shifted schedule")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check(f"small {norm} shifted schedule", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+    uni = run_denoiser(cfg.replace(t_schedule=None), W, k, v, x0, st)[0]
+    assert not np.allclose(got, uni, rtol=1e-3, atol=1e-3)  # the schedule is used
+
+
+def test_full_pi0_1view_shifted_schedule():
+    cfg = S.workload("pi0_1view").replace(t_schedule=shifted_schedule(10))
+    announce("pi0_1view shifted schedule: generating")
+    W, k, v, x0, st = _inputs(cfg)
+    announce("pi0_1view shifted schedule: gpu")
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    announce("pi0_1view shifted schedule: oracle")
+    check("pi0_1view shifted schedule", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
 # --- full-size workloads ---------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["pi0_1view", "pi0_3view"])
 def test_full_pi0(name):

@@ -30,7 +30,7 @@ def _inputs(cfg):
 # --- P1: the integrator and its schedule -----------------------------------
 def test_time_grid_is_left_endpoints_from_one():
     ts, dt = O.time_grid(10)
-    assert dt == -0.1
+    assert np.all(dt == -0.1)
     assert np.allclose(ts, [1.0, 0.9, 0.8, 0.7, 0.6, 0.5, 0.4, 0.3, 0.2, 0.1], atol=0, rtol=1e-15)
     assert ts[0] == 1.0
 
@@ -50,6 +50,50 @@ def test_euler_time_field_displacement():
     assert abs(got[0] - (-0.55)) < 1e-15
     got = O.euler(lambda x, t: np.full_like(x, t), np.zeros(1), 4)
     assert abs(got[0] - (-5 / 8)) < 1e-15
+
+
+def test_schedule_of_exact_uniform_times_equals_default():
+    # k/8 is exact in fp32 and fp64: the explicit schedule is the default one
+    ts, dt = O.time_grid(8, [1.0 - k / 8 for k in range(9)])
+    t0, d0 = O.time_grid(8)
+    assert np.array_equal(ts, t0) and np.array_equal(dt, d0)
+
+
+def test_euler_linear_field_nonuniform_closed_form():
+    # v = lam * x  =>  x_N = prod_k (1 + lam dt_k) x0
+    s = [1.0, 0.875, 0.625, 0.5, 0.25, 0.0]
+    x0 = np.array([1.5, -2.0, 0.25])
+    for lam in (0.7, -1.3):
+        got = O.euler(lambda x, t: lam * x, x0, 5, s)
+        assert np.allclose(got, np.prod([1 + lam * (b - a) for a, b in zip(s[:-1], s[1:])]) * x0, rtol=1e-14, atol=0)
+
+
+def test_euler_time_field_nonuniform_left_sum():
+    # v = t: displacement sum_k t_k (t_(k+1) - t_k) = 1(-1/4) + 3/4(-1/4) + 1/2(-1/2) = -11/16
+    got = O.euler(lambda x, t: np.full_like(x, t), np.zeros(1), 3, [1.0, 0.75, 0.5, 0.0])
+    assert got[0] == -11 / 16
+
+
+def test_schedule_validation():
+    for bad in ([1.0, 0.5, 0.5, 0.0], [0.9, 0.5, 0.2, 0.0], [1.0, 0.5, 0.2, 0.1], [1.0, 0.0]):
+        with pytest.raises(ValueError):
+            O.time_grid(3, bad)
+
+
+def test_schedule_enters_the_model_through_t():
+    # a schedule moves both where v is evaluated and the step sizes: the
+    # tiny loop with a non-uniform schedule differs from the uniform one,
+    # and equals an Euler loop written out here with the same velocity
+    cfg = TINY.replace(n_steps=4, t_schedule=(1.0, 0.75, 0.5, 0.25, 0.0))
+    W, k, v, x0, st = _inputs(cfg)
+    W64 = O.effective_weights(cfg, W)
+    ref = np.asarray(x0[0], np.float64).copy()
+    for t, dt in ((1.0, -0.25), (0.75, -0.25), (0.5, -0.25), (0.25, -0.25)):
+        ref = ref + dt * O.expert_velocity(cfg, W64, ref, t, k[0], v[0], st[0])
+    got = O.denoise(cfg, W, k, v, x0, st)[0]
+    assert np.array_equal(got, ref)
+    skew = cfg.replace(t_schedule=(1.0, 0.9, 0.6, 0.3, 0.0))
+    assert not np.allclose(O.denoise(skew, W, k, v, x0, st)[0], got, rtol=1e-6, atol=0)
 
 
 # --- P2 / P3: output plumbing of the head ------------------------------------
