@@ -34,17 +34,19 @@ def log(*a):
 
 
 def algorithmic(cfg, info):
-    """Per-chunk algorithmic bytes (weights streamed once per Euler step plus
-    the prefix K/V read once per step) and flops (2*M per matrix parameter
-    plus attention), the figures the roofline is priced on."""
+    """Per-chunk algorithmic bytes (weights streamed once per velocity
+    evaluation plus the prefix K/V read once per evaluation) and flops (2*M
+    per matrix parameter plus attention), the figures the roofline is priced
+    on.  Euler evaluates once per step, Heun twice."""
     d, L, F, Hq, Hkv, Dh = cfg.d_model, cfg.n_layers, cfg.d_mlp, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     S = cfg.suffix
     M = cfg.batch * S
     mat = L * (d * (Hq + 2 * Hkv) * Dh + d * Hq * Dh + 3 * d * F) + 2 * cfg.action_dim * d
     T = cfg.prefix_len
     attn = 4 * cfg.batch * L * S * Hq * Dh * (T + S)
-    flops = cfg.n_steps * (2 * M * mat + attn)
-    byts = cfg.n_steps * (info.weight_bytes_per_step + info.kv_bytes_per_step)
+    evals = cfg.n_steps * (2 if cfg.sampler == "heun" else 1)
+    flops = evals * (2 * M * mat + attn)
+    byts = evals * (info.weight_bytes_per_step + info.kv_bytes_per_step)
     return byts, flops
 
 
@@ -101,6 +103,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi0_1view")
+    ap.add_argument("--sampler", choices=("euler", "heun"), default=None,
+                    help="override the workload's sampler (Heun: two velocity evaluations per step)")
+    ap.add_argument("--n-steps", type=int, default=None, help="override the workload's step count")
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
@@ -120,6 +125,10 @@ def main():
     import flow_matching_denoising_euler_amd as fm
 
     cfg = S.workload(args.workload)
+    if args.sampler is not None:
+        cfg = cfg.replace(sampler=args.sampler)
+    if args.n_steps is not None:
+        cfg = cfg.replace(n_steps=args.n_steps)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     log(f"bench: generating {cfg.name}")
@@ -231,7 +240,8 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) prefix K/V and noise)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "chunk": cfg.chunk, "state_tokens": cfg.has_state,
-                   "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps, "d_model": cfg.d_model,
+                   "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps, "sampler": cfg.sampler,
+                   "d_model": cfg.d_model,
                    "layers": cfg.n_layers, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),
                    "parallelism": "single GPU"},

@@ -17,6 +17,7 @@ STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_ARG", 2: "FM_ERR_SHAPE", 3: "FM_ERR_STATE
 FM_F32, FM_BF16, FM_FP8_E4M3 = 0, 1, 2
 FM_RMSNORM, FM_ADARMSNORM = 0, 1
 FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC_PERSISTENT = 0, 1, 2
+FM_SAMPLER_EULER, FM_SAMPLER_HEUN = 0, 1
 (FM_LW_WQ, FM_LW_WK, FM_LW_WV, FM_LW_WO, FM_LW_WG, FM_LW_WU, FM_LW_WD,
  FM_LW_NORM1, FM_LW_NORM1_B, FM_LW_NORM2, FM_LW_NORM2_B, FM_LW_COUNT) = range(12)
 
@@ -30,7 +31,7 @@ class fm_config(ctypes.Structure):
         "abi_version", "d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "d_mlp",
         "action_dim", "chunk", "state_dim", "batch", "n_steps", "prefix_static", "frame_tokens",
         "n_frames", "norm", "time_dim", "weight_dtype", "act_dtype")] + [
-        ("rms_eps", ctypes.c_float), ("exec_mode", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float), ("exec_mode", ctypes.c_int32), ("sampler", ctypes.c_int32),
         ("t_schedule", ctypes.POINTER(ctypes.c_float))]
 
 

@@ -58,6 +58,8 @@ struct fm_ctx {
   // dims
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
   int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
+  bool heun;  // Heun sampler: two evaluations per step, time rows t_0..t_N
+  int NT;     // time rows of the t-dependent tables (N, or N + 1 for Heun)
   int ks_o, ks_d, nqblk, nsplit, kps;
   int NSP, TP, SP;  // static region padded to 32, padded physical prefix capacity, suffix padded to 32
 
@@ -70,7 +72,7 @@ struct fm_ctx {
   long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
   void *kpre, *vpre, *ksuf, *vsuf;
   int* meta;
-  float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *partials, *attn_part;
+  float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *vbuf, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
   unsigned* counters;
   size_t n_counters;
@@ -134,6 +136,7 @@ fm_status validate_config(const fm_config* c) {
   if ((c->n_frames > 0) != (c->frame_tokens > 0))
     return fail(nullptr, FM_ERR_SHAPE, "n_frames and frame_tokens must both be zero or both positive");
   if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, FM_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
+  if (c->sampler != FM_SAMPLER_EULER && c->sampler != FM_SAMPLER_HEUN) return fail(nullptr, FM_ERR_ARG, "bad sampler");
   if (c->t_schedule) {
     // t_0 = 1 > t_1 > ... > t_N = 0, all finite
     const float* t = c->t_schedule;
@@ -198,7 +201,9 @@ void derive(fm_ctx* x) {
   x->F = c.d_mlp; x->N = c.n_steps; x->HD = x->Hkv * x->Dh;
   // step schedule: t_k = 1 - k/N and dt = -1/N, or the caller's times (dt_k
   // from the difference of two fp32 times, exact in double, rounded once)
-  x->tk.assign(x->N, 0.0);
+  x->heun = c.sampler == FM_SAMPLER_HEUN;
+  x->NT = x->N + (x->heun ? 1 : 0);
+  x->tk.assign(x->NT, 0.0);  // t_N = 0 (the Heun corrector of the last step)
   x->dtk.assign(x->N, -1.f / (float)x->N);
   for (int k = 0; k < x->N; ++k) {
     if (c.t_schedule) {
@@ -252,7 +257,7 @@ void derive(fm_ctx* x) {
 void carve(fm_ctx* x, Arena& a) {
   const size_t ew = elt_size(x->wt), ea = elt_size(x->act), eg = elt_size(x->ge);
   const bool ada = x->cfg.norm == FM_ADARMSNORM, fp8 = x->wt == ELT_FP8;
-  const long N = x->N, L = x->L, d = x->d;
+  const long N = x->NT, L = x->L, d = x->d;  // N: time rows of the tables
   x->lw.resize(x->L);
   for (int l = 0; l < x->L; ++l) {
     LayerW& w = x->lw[l];
@@ -302,6 +307,7 @@ void carve(fm_ctx* x, Arena& a) {
   x->ssqf = (float*)a.take(Mp * x->P * 4);
   x->xbuf0 = (float*)a.take((long)x->B * x->C * x->A * 4);
   x->xbuf1 = (float*)a.take((long)x->B * x->C * x->A * 4);
+  x->vbuf = x->heun ? (float*)a.take((long)x->B * x->C * x->A * 4) : nullptr;
   x->u = a.take(Mp * d * ea);
   x->uf = a.take(Mp * d * ea);
   x->qkv = a.take(Mp * x->Nqkv * ea);
@@ -400,18 +406,24 @@ fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
   return FM_OK;
 }
 
-// final norm + head + Euler (+ the next step's embedding) of step k
-fm_status enqueue_tail(fm_ctx* x, int k, hipStream_t st, float* x_final) {
+// final norm + head + the update of step k (+ the next evaluation's
+// embedding).  stage 0: Euler; 1: Heun predictor (evaluation at t_k); 2: Heun
+// corrector (evaluation at t_(k+1)).
+fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_final) {
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
   OutArgs o{};
   o.uf = x->uf; o.Wout = x->wout; o.ssq = x->ssqf; o.P = x->P; o.inv_d = 1.f / (float)x->d; o.eps = x->cfg.rms_eps;
   o.bout = T(x->bout, x->st_bout);
   o.x_in = (k & 1) ? x->xbuf1 : x->xbuf0;
-  o.x_out = x_final ? x_final : ((k & 1) ? x->xbuf0 : x->xbuf1);
+  o.x_out = stage == 1 ? nullptr : (x_final ? x_final : ((k & 1) ? x->xbuf0 : x->xbuf1));
   o.dt = x->dtk[k];
+  o.t_idx = stage == 2 ? k + 1 : k;
+  o.heun = stage;
+  o.v_save = stage == 1 ? x->vbuf : nullptr;
+  o.v_prev = stage == 2 ? x->vbuf : nullptr;
   o.B = x->B; o.S = x->S; o.C = x->C; o.A = x->A; o.d = x->d; o.M = x->M; o.has_state = x->hasS;
   o.mtiles = x->mtiles; o.esplit = x->esplit;
-  o.do_embed = k + 1 < x->N;
+  o.do_embed = stage == 1 || k + 1 < x->N;  // the corrector's evaluation follows a predictor
   o.w_in = x->w_in; o.b_in = x->b_in;
   o.temb = ada ? T(x->zeros, 0) : T(x->temb, x->d);
   o.embed_step = k + 1;
@@ -437,7 +449,7 @@ fm_status enqueue_embed(fm_ctx* x, const float* noise, const void* state, hipStr
 fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
   const bool ada = x->cfg.norm == FM_ADARMSNORM, fp8 = x->wt == ELT_FP8;
   const int src = x->ge;  // dtype the caller passes matrices in (bf16 for fp8 models)
-  const long N = x->N, L = x->L, d = x->d;
+  const long N = x->NT, L = x->L, d = x->d;  // N: time rows of the tables
   const size_t eg = elt_size(x->ge);
   // temporaries for create only
   uint8_t* codes = nullptr;
@@ -466,7 +478,7 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     beta2 = (float*)tmalloc(N * L * d * 4);
     betaf = (float*)tmalloc(N * d * 4);
     if (!c || !beta1 || !beta2 || !betaf) { cleanup(); return fail(x, FM_ERR_OOM, "temporary time tables"); }
-    hipError_t e = launch_ada_c(w->w_time, w->b_time, src, x->tkd, x->N, x->cfg.time_dim, x->d, c, st);
+    hipError_t e = launch_ada_c(w->w_time, w->b_time, src, x->tkd, x->NT, x->cfg.time_dim, x->d, c, st);
     if (e != hipSuccess) { cleanup(); return hip_fail(x, e, "ada time mlp"); }
   }
   hipError_t e = hipSuccess;
@@ -488,10 +500,10 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
       if ((r = launch_quantize_e4m3(m, rows, cols, codes, scales, st)) != hipSuccess) return r;
       if ((r = launch_pack(codes, ELT_FP8, rows, cols, rm, dst, ELT_FP8, ntot, st)) != hipSuccess) return r;
       if ((r = launch_scatter_scales(scales, rows, rm, dscale, st)) != hipSuccess) return r;
-      if (beta) return launch_bias_gemv(codes, ELT_FP8, scales, rows, cols, beta, L * d, x->N, rm, btab, bstride, st);
+      if (beta) return launch_bias_gemv(codes, ELT_FP8, scales, rows, cols, beta, L * d, x->NT, rm, btab, bstride, st);
     } else {
       if ((r = launch_pack(m, src, rows, cols, rm, dst, src, ntot, st)) != hipSuccess) return r;
-      if (beta) return launch_bias_gemv(m, src, nullptr, rows, cols, beta, L * d, x->N, rm, btab, bstride, st);
+      if (beta) return launch_bias_gemv(m, src, nullptr, rows, cols, beta, L * d, x->NT, rm, btab, bstride, st);
     }
     return hipSuccess;
   };
@@ -500,9 +512,9 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     const void* const* lp = w->layers + (size_t)l * FM_LW_COUNT;
     LayerW& lw = x->lw[l];
     if (ada) {
-      CHK(launch_ada_mod(c, x->N, x->d, lp[FM_LW_NORM1], lp[FM_LW_NORM1_B], src, x->g1 + l * d, beta1 + l * d,
+      CHK(launch_ada_mod(c, x->NT, x->d, lp[FM_LW_NORM1], lp[FM_LW_NORM1_B], src, x->g1 + l * d, beta1 + l * d,
                          x->a1 + l * d, L * d, st), "ada norm1");
-      CHK(launch_ada_mod(c, x->N, x->d, lp[FM_LW_NORM2], lp[FM_LW_NORM2_B], src, x->g2 + l * d, beta2 + l * d,
+      CHK(launch_ada_mod(c, x->NT, x->d, lp[FM_LW_NORM2], lp[FM_LW_NORM2_B], src, x->g2 + l * d, beta2 + l * d,
                          x->a2 + l * d, L * d, st), "ada norm2");
     } else {
       CHK(launch_copy_convert(lp[FM_LW_NORM1], src, d, x->g1 + l * d, st), "gain1");
@@ -523,15 +535,15 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     CHK(put(lp[FM_LW_WD], x->d, x->F, RowMap{x->d, 0, 0}, nd, lw.wd, lw.sd, nullptr, nullptr, 0), "pack wd");
   }
   // final norm and the action head
-  for (int k = 0; k < (ada ? x->N : 1); ++k)
+  for (int k = 0; k < (ada ? x->NT : 1); ++k)
     CHK(launch_copy_convert(w->b_out, src, x->A, x->bout + k * x->A, st), "b_out");
   if (ada) {
-    CHK(launch_ada_mod(c, x->N, x->d, w->norm_f, w->norm_f_b, src, x->gf, betaf, nullptr, d, st), "ada final norm");
-    CHK(launch_bias_gemv(w->w_out, src, nullptr, x->A, x->d, betaf, d, x->N, RowMap{x->A, 0, 0}, x->bout, x->A, st),
+    CHK(launch_ada_mod(c, x->NT, x->d, w->norm_f, w->norm_f_b, src, x->gf, betaf, nullptr, d, st), "ada final norm");
+    CHK(launch_bias_gemv(w->w_out, src, nullptr, x->A, x->d, betaf, d, x->NT, RowMap{x->A, 0, 0}, x->bout, x->A, st),
         "beta_f W_out");
   } else {
     CHK(launch_copy_convert(w->norm_f, src, d, x->gf, st), "final gain");
-    CHK(launch_time_add(x->temb, x->tkd, x->N, x->d, st), "time features");
+    CHK(launch_time_add(x->temb, x->tkd, x->NT, x->d, st), "time features");
   }
   CHK(launch_pack(w->w_out, src, x->A, x->d, RowMap{x->A, 0, 0}, x->wout, src, x->A, st), "pack w_out");
   CHK(hipMemcpyAsync(x->w_in, w->w_in, (size_t)d * x->A * eg, hipMemcpyDeviceToDevice, st), "copy w_in");
@@ -634,8 +646,14 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
   }
   fm_status cs = FM_OK;
   for (int k = 0; k < x->N && cs == FM_OK; ++k) {
-    cs = enqueue_layers(x, k, x->cap);
-    if (cs == FM_OK && k + 1 < x->N) cs = enqueue_tail(x, k, x->cap, nullptr);
+    cs = enqueue_layers(x, k, x->cap);  // the evaluation at t_k
+    if (x->heun) {
+      if (cs == FM_OK) cs = enqueue_tail(x, k, 1, x->cap, nullptr);
+      if (cs == FM_OK) cs = enqueue_layers(x, k + 1, x->cap);  // the evaluation at t_(k+1)
+      if (cs == FM_OK && k + 1 < x->N) cs = enqueue_tail(x, k, 2, x->cap, nullptr);
+    } else if (cs == FM_OK && k + 1 < x->N) {
+      cs = enqueue_tail(x, k, 0, x->cap, nullptr);
+    }
   }
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(x->cap, &g);
@@ -719,7 +737,7 @@ fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* ac
     if (!x->is_set[b]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", b);
   if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
   HIPCHK(x, hipGraphLaunch(x->gexec, x->stream), "graph launch");
-  return enqueue_tail(x, x->N - 1, x->stream, actions);
+  return enqueue_tail(x, x->N - 1, x->heun ? 2 : 0, x->stream, actions);
 }
 
 fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase) {
@@ -728,7 +746,7 @@ fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase)
   if (step < 0 || step >= x->N || phase < FM_PHASE_QKV || phase > FM_PHASE_TAIL ||
       (phase != FM_PHASE_TAIL && (layer < 0 || layer >= x->L)))
     return fail(x, FM_ERR_ARG, "step %d layer %d phase %d out of range", step, layer, phase);
-  if (phase == FM_PHASE_TAIL) return enqueue_tail(x, step, x->stream, step + 1 < x->N ? nullptr : x->xbuf0);
+  if (phase == FM_PHASE_TAIL) return enqueue_tail(x, step, x->heun ? 2 : 0, x->stream, step + 1 < x->N ? nullptr : x->xbuf0);
   return enqueue_phase(x, step, layer, phase, x->stream);
 }
 
@@ -744,7 +762,7 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
   for (int b = 0; b < x->B; ++b) kv += (size_t)x->valid[b];
   info->kv_bytes_per_step = kv * x->L * x->HD * ea * 2;
   info->exec_mode = x->exec_mode;
-  info->n_phases = x->N * (5 * x->L + 1) + 1;
+  info->n_phases = (x->heun ? 2 : 1) * x->N * (5 * x->L + 1) + 1;
   {
     const BigPlan pg = big_plan(EPI_GELU, x->M, 2 * x->F, x->d);
     const bool big = x->act == ELT_BF16 && x->wt == ELT_BF16 && pg.used;

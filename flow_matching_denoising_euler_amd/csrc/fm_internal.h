@@ -114,9 +114,14 @@ struct OutArgs {
   int P;
   float inv_d, eps;
   Tab bout;               // [A] per step: b_out (+ Ada beta_f W_out)
-  const float* x_in;      // [B*C][A]
-  float* x_out;           // [B*C][A]
-  float dt;
+  const float* x_in;      // [B*C][A]  x_k
+  float* x_out;           // [B*C][A]  x_(k+1) (not written by a Heun predictor)
+  float dt;               // dt_k
+  int t_idx;              // time row of this evaluation (bout table)
+  int heun;               // 0 Euler; 1 Heun predictor: v -> v_save, embeds x_k + dt v;
+                          // 2 Heun corrector: x_(k+1) = x_k + dt (v_prev + v) / 2
+  float* v_save;          // [B*C][A]
+  const float* v_prev;    // [B*C][A]
   int B, S, C, A, d, M, has_state, mtiles, esplit;
   int do_embed;           // 0 on the last step
   // embedding of the next step (same fields as EmbedArgs)

@@ -1656,8 +1656,8 @@ __global__ __launch_bounds__(512) void k_embed(EmbedArgs e) {
   ec.template emit<ACT>(c0, m0, e.M, e.S, e.has_state, e.A, e.d, s_x, e.h, e.u, e.ssq_out);
 }
 
-// Step tail: final norm + action head + Euler update, then the next step's
-// embedding.  Workgroup (m-tile, 64-column slice): every slice recomputes the
+// Step tail: final norm + action head + Euler (or Heun stage) update, then
+// the next evaluation's embedding.  Workgroup (m-tile, 64-column slice): every slice recomputes the
 // 64 x A head tile (K = d) and embeds its own columns.
 template <int ACT, int WE, int NB>
 __global__ __launch_bounds__(512) void k_out(OutArgs o) {
@@ -1672,14 +1672,15 @@ __global__ __launch_bounds__(512) void k_out(OutArgs o) {
   // every operand first: head weights, u_f, h^2 partials, x, b_out, the embedding's operands
   float4 q[4];
   rstd_load(o.ssq, o.M, m0, q);
-  float xin[4], bo[4];
+  float xin[4], bo[4], vp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = min(m0 + lr, o.M - 1);
     const int b = r / o.S, s = r % o.S;
     const int ar = b * o.C + max(s - o.has_state, 0);
     xin[i] = o.x_in[(long)ar * o.A + min(a, o.A - 1)];
-    bo[i] = o.bout.base[(long)(o.embed_step - 1) * o.bout.step_stride + min(a, o.A - 1)];
+    bo[i] = o.bout.base[(long)o.t_idx * o.bout.step_stride + min(a, o.A - 1)];
+    vp[i] = o.heun == 2 ? o.v_prev[(long)ar * o.A + min(a, o.A - 1)] : 0.f;
   }
   EmbedCol<WE> ec;
   if (o.do_embed) ec.load(c0, o.A, o.w_in, o.b_in, o.temb, o.g1, o.embed_step, o.hs, m0, o.M, o.S, o.d);
@@ -1699,10 +1700,13 @@ __global__ __launch_bounds__(512) void k_out(OutArgs o) {
     float xv = 0.f;
     if (act_row) {
       const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
-      xv = xin[i] + o.dt * (acc * s_rstd[lr] + bo[i]);
+      const float v = acc * s_rstd[lr] + bo[i];
+      xv = o.heun == 2 ? xin[i] + o.dt * (0.5f * (vp[i] + v)) : xin[i] + o.dt * v;
       if (es == 0) {
         const int b = r / o.S, s = r % o.S;
-        o.x_out[(long)(b * o.C + s - o.has_state) * o.A + a] = xv;
+        const long xo = (long)(b * o.C + s - o.has_state) * o.A + a;
+        if (o.heun == 1) o.v_save[xo] = v;
+        else o.x_out[xo] = xv;
       }
     }
     s_x[lr][a] = xv;

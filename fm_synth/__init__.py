@@ -62,6 +62,7 @@ class FMConfig:
     rms_eps: float = 1e-6
     ticks: int = 0          # streaming ticks (0: not a streaming workload)
     t_schedule: Optional[Tuple[float, ...]] = None  # n_steps + 1 times, 1 -> 0 (None: uniform)
+    sampler: str = "euler"  # "euler" or "heun"
 
     @property
     def has_state(self) -> int:

@@ -68,6 +68,13 @@ typedef enum {
 typedef enum { FM_F32 = 0, FM_BF16 = 1, FM_FP8_E4M3 = 2 } fm_dtype;
 typedef enum { FM_RMSNORM = 0, FM_ADARMSNORM = 1 } fm_norm;
 
+/* Sampler of the flow ODE over the step schedule.  FM_SAMPLER_EULER: x_(k+1)
+ * = x_k + dt_k v(x_k, t_k), one velocity evaluation per step.
+ * FM_SAMPLER_HEUN (Heun's method, the explicit trapezoidal rule): v1 =
+ * v(x_k, t_k), v2 = v(x_k + dt_k v1, t_(k+1)), x_(k+1) = x_k + dt_k (v1 +
+ * v2) / 2, two evaluations per step (the last step evaluates at t = 0). */
+typedef enum { FM_SAMPLER_EULER = 0, FM_SAMPLER_HEUN = 1 } fm_sampler;
+
 /* How fm_denoise issues the loop.  FM_EXEC_AUTO and FM_EXEC_GRAPH run one
  * hipGraph of per-phase kernel launches.  FM_EXEC_PERSISTENT (one cooperative
  * kernel with grid barriers between phases) is reserved: fm_create rejects
@@ -125,6 +132,7 @@ typedef struct {
   int32_t act_dtype;                 /* fm_dtype: FM_F32 or FM_BF16 */
   float rms_eps;                     /* e.g. 1e-6 */
   int32_t exec_mode;                 /* fm_exec  */
+  int32_t sampler;                   /* fm_sampler */
   const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
 } fm_config;
 
@@ -158,7 +166,7 @@ typedef struct {
 /* Sizes of a created context (for accounting and benchmarks). */
 typedef struct {
   size_t arena_bytes;               /* device memory held by the context    */
-  size_t weight_bytes_per_step;     /* weight bytes one Euler step streams  */
+  size_t weight_bytes_per_step;     /* weight bytes one velocity evaluation streams */
   size_t kv_bytes_per_step;         /* prefix K/V bytes one step reads      */
   int32_t exec_mode;                /* mode actually used (FM_EXEC_GRAPH)   */
   int32_t n_phases;                 /* device phases per fm_denoise         */

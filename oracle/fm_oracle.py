@@ -64,7 +64,7 @@ from scipy.special import erf as _erf
 __all__ = [
     "time_grid", "sinusoid", "linear", "rms_inv", "rmsnorm", "ada_rmsnorm",
     "silu", "gelu", "softmax_rows", "attention", "masked_attention",
-    "ada_modulation", "euler", "expert_velocity", "denoise", "denoise_robot",
+    "ada_modulation", "euler", "heun", "integrate", "expert_velocity", "denoise", "denoise_robot",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_e4m3_per_channel",
     "effective_weights", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
     "joint_velocity", "denoise_joint", "rel_l2", "max_abs",
@@ -328,10 +328,31 @@ def euler(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
     return x
 
 
+def heun(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
+         n_steps: int, schedule: Optional[Sequence[float]] = None) -> np.ndarray:
+    """Heun's method (the explicit trapezoidal rule) over the same schedule:
+    v1 = v(x_k, t_k); v2 = v(x_k + dt_k v1, t_(k+1)); x_(k+1) = x_k +
+    dt_k (v1 + v2) / 2.  Every step, the last included, evaluates v at its
+    right end t_(k+1) as well (t = 0 on the last step)."""
+    ts, dts = time_grid(n_steps, schedule)
+    t_next = np.append(ts[1:], 0.0)  # t_(k+1): the next grid time, 0 after the last
+    x = np.asarray(x0, F64).copy()
+    for t, tn, dt in zip(ts, t_next, dts):
+        v1 = velocity(x, float(t))
+        v2 = velocity(x + dt * v1, float(tn))
+        x = x + dt * 0.5 * (v1 + v2)
+    return x
+
+
+def integrate(cfg, velocity, x0) -> np.ndarray:
+    """The workload's sampler (cfg.sampler: "euler", the default, or "heun")."""
+    step = heun if getattr(cfg, "sampler", "euler") == "heun" else euler
+    return step(velocity, x0, cfg.n_steps, getattr(cfg, "t_schedule", None))
+
+
 def denoise_robot(cfg, W64: dict, k_pre, v_pre, noise, state) -> np.ndarray:
     """One robot's action chunk x at t=0 from its noise at t=1."""
-    return euler(lambda x, t: expert_velocity(cfg, W64, x, t, k_pre, v_pre, state),
-                 noise, cfg.n_steps, getattr(cfg, "t_schedule", None))
+    return integrate(cfg, lambda x, t: expert_velocity(cfg, W64, x, t, k_pre, v_pre, state), noise)
 
 
 def denoise(cfg, W: dict, k_pre, v_pre, noise, state=None,
@@ -449,6 +470,5 @@ def denoise_joint(cfg, W: dict, Wp: dict, tokens, noise, state=None) -> np.ndarr
     out = []
     for b in range(noise.shape[0]):
         st = None if state is None else state[b]
-        out.append(euler(lambda x, t: joint_velocity(cfg, W64, Wp64, tokens[b], x, t, st),
-                         noise[b], cfg.n_steps, getattr(cfg, "t_schedule", None)))
+        out.append(integrate(cfg, lambda x, t: joint_velocity(cfg, W64, Wp64, tokens[b], x, t, st), noise[b]))
     return np.stack(out)

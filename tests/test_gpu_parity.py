@@ -228,6 +228,29 @@ def test_small_shifted_schedule(norm):
     assert not np.allclose(got, uni, rtol=1e-3, atol=1e-3)  # the schedule is used
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(norm="ada", time_dim=32, state_dim=0),
+                                dict(t_schedule=shifted_schedule(5)),
+                                dict(batch=10, chunk=40, prefix_static=64, prefix_len=64)])  # last: large-M GEMMs
+def test_small_heun(kw):
+    cfg = small_cfg(n_steps=5, sampler="heun", **kw)
+    announce(f"small heun {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check(f"small heun {kw}", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+    eul = run_denoiser(cfg.replace(sampler="euler"), W, k, v, x0, st)[0]
+    assert not np.allclose(got, eul, rtol=1e-3, atol=1e-3)  # the sampler is used
+
+
+def test_full_pi0_1view_heun():
+    cfg = S.workload("pi0_1view").replace(sampler="heun", n_steps=5)
+    announce("pi0_1view heun 5 steps: generating")
+    W, k, v, x0, st = _inputs(cfg)
+    announce("pi0_1view heun: gpu")
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    announce("pi0_1view heun: oracle")
+    check("pi0_1view heun 5 steps", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
 def test_full_pi0_1view_shifted_schedule():
     cfg = S.workload("pi0_1view").replace(t_schedule=shifted_schedule(10))
     announce("pi0_1view shifted schedule: generating")

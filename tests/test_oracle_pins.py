@@ -74,6 +74,30 @@ def test_euler_time_field_nonuniform_left_sum():
     assert got[0] == -11 / 16
 
 
+def test_heun_linear_field_closed_form():
+    # v = lam * x: one Heun step multiplies by 1 + lam dt + (lam dt)^2 / 2
+    s = [1.0, 0.875, 0.625, 0.5, 0.25, 0.0]
+    x0 = np.array([1.5, -2.0, 0.25])
+    for lam in (0.7, -1.3):
+        f = np.prod([1 + lam * (b - a) + (lam * (b - a)) ** 2 / 2 for a, b in zip(s[:-1], s[1:])])
+        assert np.allclose(O.heun(lambda x, t: lam * x, x0, 5, s), f * x0, rtol=1e-14, atol=0)
+        f = (1 - lam / 10 + (lam / 10) ** 2 / 2) ** 10
+        assert np.allclose(O.heun(lambda x, t: lam * x, x0, 10), f * x0, rtol=1e-14, atol=0)
+
+
+def test_heun_is_exact_for_a_velocity_linear_in_t():
+    # v = a + b t: the trapezoidal rule integrates it exactly, x_N = x_0 - a - b/2
+    for sched, n in ((None, 10), ([1.0, 0.75, 0.5, 0.0], 3), (None, 1)):
+        got = O.heun(lambda x, t: np.full_like(x, 0.3 - 1.7 * t), np.zeros(1), n, sched)
+        assert abs(got[0] - (-0.3 + 1.7 / 2)) < 1e-15
+
+
+def test_heun_uses_the_right_end_times():
+    seen = []
+    O.heun(lambda x, t: (seen.append(t), np.zeros_like(x))[1], np.zeros(1), 4)
+    assert seen == [1.0, 0.75, 0.75, 0.5, 0.5, 0.25, 0.25, 0.0]
+
+
 def test_schedule_validation():
     for bad in ([1.0, 0.5, 0.5, 0.0], [0.9, 0.5, 0.2, 0.0], [1.0, 0.5, 0.2, 0.1], [1.0, 0.0]):
         with pytest.raises(ValueError):
