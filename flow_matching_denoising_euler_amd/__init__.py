@@ -14,7 +14,7 @@ from ._abi import (FM_ABI_VERSION, FM_BF16, FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC
 
 __all__ = ["FMError", "make_config", "fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv",
            "fm_denoise", "fm_get_info", "fm_launch_phase", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
-           "Denoiser", "lib"]
+           "fm_encoder_create", "fm_encode_prefix", "Denoiser", "Encoder", "lib"]
 
 lib = _abi.lib
 
@@ -103,19 +103,56 @@ def fm_create(cfg, weights: dict, stream=None, exec_mode: int = FM_EXEC_AUTO, de
         w.norm_f, w.norm_f_b = put(weights["norm_f_w"]), put(weights["norm_f_b"])
     else:
         w.norm_f = put(weights["norm_f"])
-    names = ["wq", "wk", "wv", "wo", "wg", "wu", "wd"]
-    norms = (["norm1", None, "norm2", None] if cfg.norm == "rms"
-             else ["norm1_w", "norm1_b", "norm2_w", "norm2_b"])
-    arr = (ctypes.c_void_p * (cfg.n_layers * _abi.FM_LW_COUNT))()
-    for li, L in enumerate(weights["layers"]):
-        for si, n in enumerate(names + norms):
-            arr[li * _abi.FM_LW_COUNT + si] = put(L[n]) if n else None
-    w.layers = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    w.layers = _layer_table(weights["layers"], cfg.norm == "rms", put)
     ctx = ctypes.c_void_p()
     st = lib().fm_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(_stream(stream)), ctypes.byref(ctx))
     _check(st)
     del keep
     return ctx
+
+
+def _layer_table(layers, rms: bool, put):
+    names = ["wq", "wk", "wv", "wo", "wg", "wu", "wd"]
+    norms = ["norm1", None, "norm2", None] if rms else ["norm1_w", "norm1_b", "norm2_w", "norm2_b"]
+    arr = (ctypes.c_void_p * (len(layers) * _abi.FM_LW_COUNT))()
+    for li, L in enumerate(layers):
+        for si, n in enumerate(names + norms):
+            arr[li * _abi.FM_LW_COUNT + si] = put(L[n]) if n else None
+    ptr = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    ptr._keep = arr
+    return ptr
+
+
+def fm_encoder_create(cfg, weights: dict, n_tokens: int, n_seqs: int = 1, stream=None,
+                      exec_mode: int = FM_EXEC_AUTO, device="cuda"):
+    """Create a prefix-encoder context for `n_seqs` sequences of `n_tokens`
+    tokens each.  `cfg` supplies the layer shape and dtypes (its other fields
+    are ignored); `weights` is fm_synth.make_prefix_stack's {"layers": [...]}."""
+    import torch
+    c = make_config(cfg, exec_mode)
+    c.chunk, c.batch = int(n_tokens), int(n_seqs)
+    wdt = torch.float32 if cfg.weight_dtype == "f32" else torch.bfloat16
+    keep = []
+
+    def put(a):
+        t = _dev_tensor(a, wdt, device)
+        keep.append(t)
+        return _ptr(t)
+
+    w = fm_weights()
+    w.layers = _layer_table(weights["layers"], True, put)
+    ctx = ctypes.c_void_p()
+    st = lib().fm_encoder_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(_stream(stream)),
+                                 ctypes.byref(ctx))
+    _check(st)
+    del keep
+    return ctx
+
+
+def fm_encode_prefix(ctx, tokens, k_out, v_out):
+    """tokens: fp32 device [seqs][tokens][d_model]; k_out, v_out: device
+    [seqs][layers][tokens][kv_heads][head_dim] in the activation dtype."""
+    _check(lib().fm_encode_prefix(ctx, _ptr(tokens), _ptr(k_out), _ptr(v_out)), ctx)
 
 
 def fm_set_prefix_kv(ctx, robot: int, k, v, n_tokens: int):
@@ -153,18 +190,40 @@ def fm_quantize_e4m3(w, codes, scales, stream=None):
                                   ctypes.c_void_p(_stream(stream))))
 
 
-class Denoiser:
-    """Owns one context: load the prefix, then call `denoise` per chunk."""
+class _Context:
+    """Owns one library context (released by close() or on collection)."""
+    ctx = None
 
-    def __init__(self, cfg, weights: dict, stream=None, exec_mode: int = FM_EXEC_AUTO, device="cuda"):
+    def _setup(self, cfg, device):
         import torch
         self.cfg = cfg
         self.device = device
         self.act_dtype = torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16
-        self.ctx = fm_create(cfg, weights, stream, exec_mode, device)
 
     def _act(self, a):
         return _dev_tensor(a, self.act_dtype, self.device)
+
+    def info(self) -> fm_info:
+        return fm_get_info(self.ctx)
+
+    def close(self):
+        if self.ctx is not None:
+            fm_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Denoiser(_Context):
+    """Owns one context: load the prefix, then call `denoise` per chunk."""
+
+    def __init__(self, cfg, weights: dict, stream=None, exec_mode: int = FM_EXEC_AUTO, device="cuda"):
+        self._setup(cfg, device)
+        self.ctx = fm_create(cfg, weights, stream, exec_mode, device)
 
     def set_prefix_kv(self, robot: int, k, v):
         """k, v [layers][tokens][kv_heads][head_dim] (host or device)."""
@@ -186,16 +245,27 @@ class Denoiser:
         fm_denoise(self.ctx, n, s, out)
         return out
 
-    def info(self) -> fm_info:
-        return fm_get_info(self.ctx)
 
-    def close(self):
-        if self.ctx is not None:
-            fm_destroy(self.ctx)
-            self.ctx = None
+class Encoder(_Context):
+    """Owns one prefix-encoder context: `encode` turns token embeddings into
+    the per-layer K/V that Denoiser.set_prefix_kv / append_prefix_kv take."""
 
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+    def __init__(self, cfg, weights: dict, n_tokens: int, n_seqs: int = 1, stream=None,
+                 exec_mode: int = FM_EXEC_AUTO, device="cuda"):
+        self._setup(cfg, device)
+        self.n_tokens, self.n_seqs = int(n_tokens), int(n_seqs)
+        self.ctx = fm_encoder_create(cfg, weights, n_tokens, n_seqs, stream, exec_mode, device)
+
+    def encode(self, tokens, k_out=None, v_out=None):
+        """tokens [seqs][tokens][d_model] (host or device) -> (k, v) device
+        tensors [seqs][layers][tokens][kv_heads][head_dim]."""
+        import torch
+        t = _dev_tensor(tokens, torch.float32, self.device)
+        shape = (self.n_seqs, self.cfg.n_layers, self.n_tokens, self.cfg.n_kv_heads, self.cfg.head_dim)
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=self.act_dtype, device=self.device)
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=self.act_dtype, device=self.device)
+        fm_encode_prefix(self.ctx, t, k_out, v_out)
+        self._tokens = t  # alive until the next call
+        return k_out, v_out

@@ -22,7 +22,8 @@ FM_SAMPLER_EULER, FM_SAMPLER_HEUN = 0, 1
  FM_LW_NORM1, FM_LW_NORM1_B, FM_LW_NORM2, FM_LW_NORM2_B, FM_LW_COUNT) = range(12)
 
 EXPORTS = ("fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv", "fm_denoise", "fm_get_info",
-           "fm_destroy", "fm_last_error", "fm_quantize_e4m3", "fm_launch_phase")
+           "fm_destroy", "fm_last_error", "fm_quantize_e4m3", "fm_launch_phase", "fm_encoder_create",
+           "fm_encode_prefix")
 FM_PHASE_QKV, FM_PHASE_ATTN, FM_PHASE_OPROJ, FM_PHASE_GATEUP, FM_PHASE_DOWN, FM_PHASE_TAIL = range(6)
 
 
@@ -77,5 +78,9 @@ def lib() -> ctypes.CDLL:
         L.fm_quantize_e4m3.restype = ctypes.c_int
         L.fm_launch_phase.argtypes = [vp, i32, i32, i32]
         L.fm_launch_phase.restype = ctypes.c_int
+        L.fm_encoder_create.argtypes = [ctypes.POINTER(fm_config), ctypes.POINTER(fm_weights), vp, ctypes.POINTER(vp)]
+        L.fm_encoder_create.restype = ctypes.c_int
+        L.fm_encode_prefix.argtypes = [vp, vp, vp, vp]
+        L.fm_encode_prefix.restype = ctypes.c_int
         _LIB = L
     return _LIB

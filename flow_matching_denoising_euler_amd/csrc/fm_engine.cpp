@@ -54,6 +54,7 @@ struct fm_ctx {
   bool poisoned = false;
   int exec_mode = FM_EXEC_GRAPH;
   int n_cu = 0;
+  bool encoder = false;  // prefix encoder: layers only, K/V of every layer out
 
   // dims
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
@@ -76,6 +77,7 @@ struct fm_ctx {
   void *u, *uf, *qkv, *o, *z;
   unsigned* counters;
   size_t n_counters;
+  void *enc_k, *enc_v;  // encoder output rows [B][L][S][HD] act
 
   // host mirror of the prefix state
   std::vector<int> valid, head;
@@ -174,10 +176,12 @@ fm_status validate_config(const fm_config* c) {
   return FM_OK;
 }
 
-fm_status validate_weights(const fm_config* c, const fm_weights* w) {
+// encoder: the layers only
+fm_status validate_weights(const fm_config* c, const fm_weights* w, bool encoder) {
   if (!w) return fail(nullptr, FM_ERR_ARG, "weights is NULL");
-  if (!w->w_in || !w->b_in || !w->w_out || !w->b_out || !w->norm_f || !w->layers)
-    return fail(nullptr, FM_ERR_ARG, "missing weight pointer (w_in, b_in, w_out, b_out, norm_f, layers)");
+  if (!encoder && (!w->w_in || !w->b_in || !w->w_out || !w->b_out || !w->norm_f))
+    return fail(nullptr, FM_ERR_ARG, "missing weight pointer (w_in, b_in, w_out, b_out, norm_f)");
+  if (!w->layers) return fail(nullptr, FM_ERR_ARG, "missing weight pointer: layers is NULL");
   if (c->state_dim > 0 && (!w->w_state || !w->b_state)) return fail(nullptr, FM_ERR_ARG, "missing w_state / b_state");
   if (c->norm == FM_ADARMSNORM && (!w->w_time || !w->b_time || !w->norm_f_b))
     return fail(nullptr, FM_ERR_ARG, "AdaRMSNorm needs w_time, b_time, norm_f_b");
@@ -322,6 +326,9 @@ void carve(fm_ctx* x, Arena& a) {
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
                                    (size_t)x->B * x->Hkv * x->nqblk * 2) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);
+  const size_t kvo = x->encoder ? (size_t)x->B * L * x->S * x->HD * ea : 16;
+  x->enc_k = a.take(kvo);
+  x->enc_v = a.take(kvo);
 }
 
 Tab T(const float* base, long stride) { return Tab{base, stride}; }
@@ -432,6 +439,42 @@ fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_fin
   return FM_OK;
 }
 
+// encoder: layer l's K and V out of the suffix blocks into the output rows
+fm_status enqueue_unpack(fm_ctx* x, int l, hipStream_t st) {
+  KvUnpack c{};
+  c.ks = x->ksuf; c.vs = x->vsuf; c.kd = x->enc_k; c.vd = x->enc_v;
+  c.elt = x->act; c.B = x->B; c.S = x->S; c.SP = x->SP; c.HD = x->HD; c.Dh = x->Dh; c.layers = x->L; c.layer = l;
+  HIPCHK(x, launch_kv_unpack(c, st), "kv unpack");
+  return FM_OK;
+}
+
+// the graph body.  Denoiser: every step's layers and tails except the last
+// tail.  Encoder: every layer, the last one only up to its K and V (nothing
+// after them reaches the output).
+fm_status enqueue_graph_body(fm_ctx* x, hipStream_t cap) {
+  fm_status cs = FM_OK;
+  if (x->encoder) {
+    for (int l = 0; l < x->L && cs == FM_OK; ++l) {
+      cs = enqueue_phase(x, 0, l, FM_PHASE_QKV, cap);
+      if (cs == FM_OK) cs = enqueue_unpack(x, l, cap);
+      for (int ph = FM_PHASE_ATTN; ph <= FM_PHASE_DOWN && cs == FM_OK && l + 1 < x->L; ++ph)
+        cs = enqueue_phase(x, 0, l, ph, cap);
+    }
+    return cs;
+  }
+  for (int k = 0; k < x->N && cs == FM_OK; ++k) {
+    cs = enqueue_layers(x, k, cap);  // the evaluation at t_k
+    if (x->heun) {
+      if (cs == FM_OK) cs = enqueue_tail(x, k, 1, cap, nullptr);
+      if (cs == FM_OK) cs = enqueue_layers(x, k + 1, cap);  // the evaluation at t_(k+1)
+      if (cs == FM_OK && k + 1 < x->N) cs = enqueue_tail(x, k, 2, cap, nullptr);
+    } else if (cs == FM_OK && k + 1 < x->N) {
+      cs = enqueue_tail(x, k, 0, cap, nullptr);
+    }
+  }
+  return cs;
+}
+
 fm_status enqueue_embed(fm_ctx* x, const float* noise, const void* state, hipStream_t st) {
   EmbedArgs e{};
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
@@ -534,6 +577,10 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     CHK(put(lp[FM_LW_WU], x->F, x->d, RowMap{16, 32, 16}, ngu, lw.wgu, lw.sgu, b2, bg, x->st_bgu), "pack wu");
     CHK(put(lp[FM_LW_WD], x->d, x->F, RowMap{x->d, 0, 0}, nd, lw.wd, lw.sd, nullptr, nullptr, 0), "pack wd");
   }
+  if (x->encoder) {
+    cleanup();
+    return FM_OK;
+  }
   // final norm and the action head
   for (int k = 0; k < (ada ? x->NT : 1); ++k)
     CHK(launch_copy_convert(w->b_out, src, x->A, x->bout + k * x->A, st), "b_out");
@@ -557,22 +604,16 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
   return FM_OK;
 }
 
-fm_status check_ctx(fm_ctx* x) {
+fm_status check_ctx(fm_ctx* x, bool encoder = false) {
   if (!x) return fail(nullptr, FM_ERR_ARG, "ctx is NULL");
   if (x->poisoned) return fail(x, FM_ERR_STATE, "context poisoned by an earlier device error");
+  if (x->encoder != encoder)
+    return fail(x, FM_ERR_STATE, encoder ? "not an encoder context" : "an encoder context only encodes prefixes");
   return FM_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream, fm_ctx** out) {
-  if (!out) return fail(nullptr, FM_ERR_ARG, "out is NULL");
-  *out = nullptr;
-  fm_status s = validate_config(cfg);
-  if (s != FM_OK) return s;
-  if ((s = validate_weights(cfg, w)) != FM_OK) return s;
+// set-up shared by the denoiser and the encoder; cfg and w validated
+fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream, bool encoder, fm_ctx** out) {
   if (cfg->exec_mode == FM_EXEC_PERSISTENT)
     return fail(nullptr, FM_ERR_UNSUPPORTED, "persistent execution is not implemented; the loop runs as a graph of kernels");
 
@@ -587,6 +628,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
 
   fm_ctx* x = new fm_ctx();
   x->cfg = *cfg;
+  x->encoder = encoder;
   x->stream = (hipStream_t)hip_stream;
   x->n_cu = prop.multiProcessorCount;
   x->exec_mode = FM_EXEC_GRAPH;
@@ -630,7 +672,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
     hip_fail(x, e, "schedule table");
     return bail(FM_ERR_DEVICE);
   }
-  if ((s = load_weights(x, w, st)) != FM_OK) return bail(s);
+  if (const fm_status s = load_weights(x, w, st); s != FM_OK) return bail(s);
   // the graph: every step's layers and tails except the last tail
   if ((e = hipStreamCreateWithFlags(&x->cap, hipStreamNonBlocking)) != hipSuccess) {
     hip_fail(x, e, "capture stream");
@@ -644,17 +686,7 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
     hip_fail(x, e, "begin capture");
     return bail(FM_ERR_DEVICE);
   }
-  fm_status cs = FM_OK;
-  for (int k = 0; k < x->N && cs == FM_OK; ++k) {
-    cs = enqueue_layers(x, k, x->cap);  // the evaluation at t_k
-    if (x->heun) {
-      if (cs == FM_OK) cs = enqueue_tail(x, k, 1, x->cap, nullptr);
-      if (cs == FM_OK) cs = enqueue_layers(x, k + 1, x->cap);  // the evaluation at t_(k+1)
-      if (cs == FM_OK && k + 1 < x->N) cs = enqueue_tail(x, k, 2, x->cap, nullptr);
-    } else if (cs == FM_OK && k + 1 < x->N) {
-      cs = enqueue_tail(x, k, 0, x->cap, nullptr);
-    }
-  }
+  const fm_status cs = enqueue_graph_body(x, x->cap);
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(x->cap, &g);
   if (cs != FM_OK) {
@@ -676,6 +708,44 @@ fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream,
   }
   *out = x;
   return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fm_status fm_create(const fm_config* cfg, const fm_weights* w, void* hip_stream, fm_ctx** out) {
+  if (!out) return fail(nullptr, FM_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  fm_status s = validate_config(cfg);
+  if (s != FM_OK) return s;
+  if ((s = validate_weights(cfg, w, false)) != FM_OK) return s;
+  return create_ctx(cfg, w, hip_stream, false, out);
+}
+
+fm_status fm_encoder_create(const fm_config* cfg, const fm_weights* w, void* hip_stream, fm_ctx** out) {
+  if (!out) return fail(nullptr, FM_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(nullptr, FM_ERR_ARG, "cfg is NULL");
+  // fields the encoder does not read take fixed values: no time, no state, no
+  // prefix of its own, RMSNorm layers
+  fm_config c = *cfg;
+  c.norm = FM_RMSNORM;
+  c.time_dim = c.d_model;
+  c.action_dim = 16;
+  c.state_dim = 0;
+  c.n_steps = 1;
+  c.prefix_static = 0;
+  c.frame_tokens = 0;
+  c.n_frames = 0;
+  c.sampler = FM_SAMPLER_EULER;
+  c.t_schedule = nullptr;
+  fm_status s = validate_config(&c);
+  if (s != FM_OK) return s;
+  if (c.act_dtype == FM_BF16 && c.chunk > 1024)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "encoder: at most 1024 tokens per sequence");
+  if ((s = validate_weights(&c, w, true)) != FM_OK) return s;
+  return create_ctx(&c, w, hip_stream, true, out);
 }
 
 }  // extern "C"
@@ -740,6 +810,21 @@ fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* ac
   return enqueue_tail(x, x->N - 1, x->heun ? 2 : 0, x->stream, actions);
 }
 
+fm_status fm_encode_prefix(fm_ctx* x, const float* tokens, void* k_out, void* v_out) {
+  fm_status s = check_ctx(x, true);
+  if (s != FM_OK) return s;
+  if (!tokens || !k_out || !v_out) return fail(x, FM_ERR_ARG, "tokens, k_out or v_out is NULL");
+  TokensIn t{};
+  t.tokens = tokens; t.g1 = x->g1; t.h = x->h; t.u = x->u; t.ssq = x->ssq;
+  t.M = x->M; t.d = x->d; t.esplit = x->esplit;
+  HIPCHK(x, launch_tokens_in(x->act, t, x->stream), "tokens in");
+  HIPCHK(x, hipGraphLaunch(x->gexec, x->stream), "graph launch");
+  const size_t bytes = (size_t)x->B * x->L * x->S * x->HD * elt_size(x->act);
+  HIPCHK(x, hipMemcpyAsync(k_out, x->enc_k, bytes, hipMemcpyDeviceToDevice, x->stream), "k out");
+  HIPCHK(x, hipMemcpyAsync(v_out, x->enc_v, bytes, hipMemcpyDeviceToDevice, x->stream), "v out");
+  return FM_OK;
+}
+
 fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase) {
   fm_status s = check_ctx(x);
   if (s != FM_OK) return s;
@@ -753,16 +838,22 @@ fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase)
 fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
   if (!x || !info) return fail(nullptr, FM_ERR_ARG, "ctx or info is NULL");
   const size_t ew = elt_size(x->wt), eg = elt_size(x->ge), ea = elt_size(x->act);
-  size_t wb = (size_t)x->L * ((size_t)x->Nqkv * x->d + (size_t)x->d * x->Hq * x->Dh + 3ull * x->F * x->d) * ew;
-  if (x->wt == ELT_FP8) wb += (size_t)x->L * (x->Nqkv + 2 * x->d + 2 * x->F) * 4;
-  wb += (size_t)(2 * x->A * x->d + x->d) * eg;  // w_in, w_out, b_in
+  const size_t wqkv = (size_t)x->Nqkv * x->d, wrest = (size_t)x->d * x->Hq * x->Dh + 3ull * x->F * x->d;
+  const size_t srest = x->wt == ELT_FP8 ? (size_t)2 * x->d + 2 * x->F : 0, sqkv = x->wt == ELT_FP8 ? x->Nqkv : 0;
   info->arena_bytes = x->arena_bytes;
-  info->weight_bytes_per_step = wb;
-  size_t kv = 0;
-  for (int b = 0; b < x->B; ++b) kv += (size_t)x->valid[b];
-  info->kv_bytes_per_step = kv * x->L * x->HD * ea * 2;
   info->exec_mode = x->exec_mode;
-  info->n_phases = (x->heun ? 2 : 1) * x->N * (5 * x->L + 1) + 1;
+  if (x->encoder) {
+    // the last layer streams its QKV weights only; K/V out of every layer
+    info->weight_bytes_per_step = (x->L * wqkv + (x->L - 1) * wrest) * ew + (x->L * sqkv + (x->L - 1) * srest) * 4;
+    info->kv_bytes_per_step = (size_t)2 * x->B * x->L * x->S * x->HD * ea;
+    info->n_phases = 1 + 2 * x->L + 4 * (x->L - 1);
+  } else {
+    info->weight_bytes_per_step = x->L * ((wqkv + wrest) * ew + (sqkv + srest) * 4) + (size_t)(2 * x->A * x->d + x->d) * eg;
+    size_t kv = 0;
+    for (int b = 0; b < x->B; ++b) kv += (size_t)x->valid[b];
+    info->kv_bytes_per_step = kv * x->L * x->HD * ea * 2;
+    info->n_phases = (x->heun ? 2 : 1) * x->N * (5 * x->L + 1) + 1;
+  }
   {
     const BigPlan pg = big_plan(EPI_GELU, x->M, 2 * x->F, x->d);
     const bool big = x->act == ELT_BF16 && x->wt == ELT_BF16 && pg.used;

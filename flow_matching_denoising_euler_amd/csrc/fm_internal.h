@@ -159,14 +159,20 @@ struct EmbedArgs {
 // false selects the skinny GEMM.
 struct BigPlan {
   bool used;
+  bool mid;         // a few hundred rows: the smaller tiles
   int BM, BN, kst;  // tile, k-blocks of 32 per LDS stage
 };
+constexpr int BIG_MID_ROWS = 512;  // below: the smaller tiles
 inline BigPlan big_plan(int epi, int M, int N, int K) {
-  // gate/up 128 x 256 and QKV 128 x 64 (128-row tiles, like the GEMMs that
-  // read their output), stages of 64 k; the residual GEMMs (N = d_model)
-  // 64 x 64 with stages of 128 k (where K allows), which covers the CUs
-  // without splitting K
-  BigPlan p{false, epi == EPI_RESID ? 64 : 128, epi == EPI_GELU ? 256 : 64, 2};
+  // From 512 rows: gate/up 128 x 256 and QKV 128 x 64 (128-row tiles, like
+  // the GEMMs that read their output), stages of 64 k; the residual GEMMs
+  // (N = d_model) 64 x 64 with stages of 128 k (where K allows), which covers
+  // the CUs without splitting K.  From 256 to 511 rows (one prefix frame, a
+  // few robots): gate/up 64 x 128, QKV 64 x 32, residual 32 x 32, so that a
+  // launch still has about one workgroup per CU.
+  const bool mid = M < BIG_MID_ROWS;
+  BigPlan p{false, mid, mid ? (epi == EPI_RESID ? 32 : 64) : (epi == EPI_RESID ? 64 : 128),
+            mid ? (epi == EPI_GELU ? 128 : 32) : (epi == EPI_GELU ? 256 : 64), 2};
   if (M < 256 || K % 64 || N % p.BN) return p;
   if (epi == EPI_RESID && K % 128 == 0) p.kst = 4;
   p.used = true;
@@ -212,5 +218,26 @@ struct KvCopy {
   int robot, valid, head;
 };
 hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st);
+
+// prefix encoder: token rows in (h = tokens, u = act(h * g), h^2 partials)
+struct TokensIn {
+  const float* tokens;    // [M][d] fp32
+  const float* g1;        // [d] first norm gain
+  float* h;
+  void* u;
+  float* ssq;
+  int M, d, esplit;
+};
+hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st);
+// prefix encoder: one layer's suffix K/V (kv layout, SP keys per sequence)
+// -> rows [B][layers][S][HD] at layer `layer`
+struct KvUnpack {
+  const void* ks;
+  const void* vs;
+  void* kd;
+  void* vd;
+  int elt, B, S, SP, HD, Dh, layers, layer;
+};
+hipError_t launch_kv_unpack(const KvUnpack& c, hipStream_t st);
 
 }  // namespace fm

@@ -1898,6 +1898,57 @@ __global__ void k_kv_copy(KvCopy c) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefix encoder.  The prefix K/V that the loop reads is produced before the
+// loop by the vision/language stack (realtime-vla write-up, "The problem is a
+// policy that thinks too long": vision encoder, LLM, action expert as three
+// components; InstinctFlash README, "Framework overview": prefill extraction
+// as a graph-level optimisation).  The encoder runs the layer kernels above
+// over the prefix tokens as the "suffix" of an empty prefix; these two
+// kernels are its input and output.
+// ---------------------------------------------------------------------------
+// Token rows in: the residual stream is the token embedding itself; writes
+// h, the first norm's operand u = act(h * g) in the packed GEMM layout and
+// the h^2 partial of every 16-column group.  Workgroup = (64-row tile,
+// 64-column slice), 512 threads.
+template <int ACT>
+__global__ __launch_bounds__(512) void k_tokens_in(TokensIn t) {
+  const int mt = blockIdx.x / t.esplit, es = blockIdx.x % t.esplit;
+  const int col = es * 64 + (threadIdx.x & 63);
+  const float gain = t.g1[col];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = mt * 64 + (threadIdx.x >> 6) + 8 * i;
+    const float hv = r < t.M ? t.tokens[(long)r * t.d + col] : 0.f;
+    const float q = sum16(hv * hv);
+    if (r < t.M) {
+      t.h[(long)r * t.d + col] = hv;
+      st_act<ACT>(t.u, pk(r, col, t.d), hv * gain);
+      if ((threadIdx.x & 15) == 0) t.ssq[(long)r * PM + (col >> 4)] = q;
+    }
+  }
+}
+
+// One layer's K and V of every sequence, from the kv layout the QKV GEMM
+// writes (SP-key block per sequence) to rows [b][layer][t][HD]: the layout
+// fm_set_prefix_kv / fm_append_prefix_kv take.  Thread = one (b, t, column).
+template <typename T>
+__global__ void k_kv_unpack(KvUnpack c) {
+  constexpr bool packed = sizeof(T) == 2;
+  const int HD = c.HD, Dh = c.Dh, Hkv = HD / Dh;
+  const long total = (long)c.B * c.S * HD;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int col = (int)(i % HD);
+    const long bt = i / HD;
+    const int b = (int)(bt / c.S), t = (int)(bt % c.S);
+    const long src = (long)b * HD * c.SP;
+    const long dst = (((long)b * c.layers + c.layer) * c.S + t) * HD + col;
+    ((T*)c.kd)[dst] = ((const T*)c.ks)[src + kv_k_off(packed, c.SP, Hkv, Dh, col / Dh, t, col % Dh)];
+    ((T*)c.vd)[dst] = ((const T*)c.vs)[src + kv_v_off(packed, c.SP, Hkv, Dh, col / Dh, t, col % Dh)];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 #define FM_LAUNCH(kern, grid, ...)                                    \
@@ -1937,6 +1988,14 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   const BigPlan p = big_plan(epi, g.M, g.N, g.K);
   if (!p.used || g.ksplit != 1) return false;
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
+  if (p.mid) {
+    if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 2, 4, 2, 2>), dim3(grid), dim3(512), 0, st, g);
+    else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+    else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 4>), dim3(grid), dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+    *err = hipGetLastError();
+    return true;
+  }
   if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2, 2>), dim3(grid), dim3(512), 0, st, g);
   else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, st, g);
   else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 4>), dim3(grid), dim3(512), 0, st, g);
@@ -2096,6 +2155,20 @@ hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st) {
   const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
   if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_copy<float>, dim3(grid), dim3(256), 0, st, c);
   else hipLaunchKernelGGL(k_kv_copy<uint16_t>, dim3(grid), dim3(256), 0, st, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st) {
+  const int grid = (t.M + 63) / 64 * t.esplit;
+  if (act == ELT_F32) FM_LAUNCH_N(k_tokens_in<ELT_F32>, grid, 512, t);
+  FM_LAUNCH_N(k_tokens_in<ELT_BF16>, grid, 512, t);
+}
+
+hipError_t launch_kv_unpack(const KvUnpack& c, hipStream_t st) {
+  const long work = (long)c.B * c.S * c.HD;
+  const int grid = (int)std::max(1L, std::min(2048L, (work + 255) / 256));
+  if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_unpack<float>, dim3(grid), dim3(256), 0, st, c);
+  else hipLaunchKernelGGL(k_kv_unpack<uint16_t>, dim3(grid), dim3(256), 0, st, c);
   return hipGetLastError();
 }
 

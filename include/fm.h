@@ -213,7 +213,44 @@ fm_status fm_append_prefix_kv(fm_ctx* ctx, int32_t robot, const void* k_frame,
  */
 fm_status fm_denoise(fm_ctx* ctx, const float* noise, const void* state, float* actions);
 
-/* Fill *info.  Never fails on a valid context. */
+/*
+ * Prefix encoder: the step before the loop that produces the prefix K/V
+ * (realtime-vla write-up, "The problem is a policy that thinks too long":
+ * vision encoder and LLM ahead of the action expert; InstinctFlash README,
+ * "Framework overview": prefill extraction).  A synthetic stack of the same
+ * layer shape as the expert runs over `batch` independent sequences of
+ * `chunk` prefix tokens each; tokens attend to every token of their own
+ * sequence (no mask, no positions) and the K and V of every layer are the
+ * output.  Each sequence is one frame or one prompt: a frame's K/V depends on
+ * that frame alone, so fm_append_prefix_kv can take it unchanged.
+ *
+ * fm_encoder_create reads abi_version, d_model, n_layers, n_q_heads,
+ * n_kv_heads, head_dim, d_mlp, rms_eps, weight_dtype, act_dtype, exec_mode,
+ * batch (sequences per call) and chunk (tokens per sequence; at most 1024 for
+ * bf16, 256 for fp32); it ignores every other field.  Weights: `layers` only
+ * (wq, wk, wv, wo, wg, wu, wd, norm1, norm2 of every layer; the other
+ * pointers may be NULL), in the same dtypes and layouts as fm_create's.  The
+ * context accepts fm_encode_prefix, fm_get_info and fm_destroy only; the
+ * denoising calls return FM_ERR_STATE on it, and fm_encode_prefix returns
+ * FM_ERR_STATE on a denoising context.
+ */
+fm_status fm_encoder_create(const fm_config* cfg, const fm_weights* w, void* hip_stream, fm_ctx** out);
+
+/*
+ * Encode `batch` sequences.  tokens: [batch][chunk][d_model] fp32 (the
+ * token embeddings, i.e. the first layer's input); k_out, v_out:
+ * [batch][n_layers][chunk][n_kv_heads][head_dim] in act_dtype, owned by the
+ * caller.  Sequence b's block (n_layers * chunk * n_kv_heads * head_dim
+ * elements) is the k / v argument of fm_set_prefix_kv or
+ * fm_append_prefix_kv for a denoising context of the same n_layers,
+ * n_kv_heads, head_dim and act_dtype (16-byte aligned if the buffers are).
+ * Asynchronous; allocates nothing.
+ */
+fm_status fm_encode_prefix(fm_ctx* enc, const float* tokens, void* k_out, void* v_out);
+
+/* Fill *info.  Never fails on a valid context.  For an encoder context the
+ * per-step fields describe one fm_encode_prefix call (weights streamed, K/V
+ * bytes written). */
 fm_status fm_get_info(const fm_ctx* ctx, fm_info* info);
 
 /* Release the context and its arena (synchronises its stream). NULL-safe. */

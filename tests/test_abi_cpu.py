@@ -99,3 +99,50 @@ def test_null_context_calls_fail_cleanly():
     L.fm_destroy(None)
     assert L.fm_quantize_e4m3(None, 4, 4, None, None, None) == _abi.FM_ERR_ARG
     assert isinstance(fm.fm_last_error(), str)
+
+
+def _encoder_create(c, layers=True):
+    w = _abi.fm_weights()
+    keep = None
+    if layers:  # non-NULL dummy host pointers: validation only looks at presence
+        keep = (ctypes.c_float * 4)()
+        arr = (ctypes.c_void_p * (c.n_layers * _abi.FM_LW_COUNT))()
+        for i in range(len(arr)):
+            arr[i] = ctypes.addressof(keep)
+        w.layers = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    ctx = ctypes.c_void_p()
+    st = fm.lib().fm_encoder_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(ctx))
+    return st, ctx
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda c: setattr(c, "abi_version", 99), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "chunk", 0), _abi.FM_ERR_SHAPE),            # tokens per sequence
+    (lambda c: setattr(c, "n_kv_heads", 3), _abi.FM_ERR_SHAPE),
+    (lambda c: setattr(c, "chunk", 300), _abi.FM_ERR_UNSUPPORTED),    # fp32 path: <= 256 tokens
+    (lambda c: (setattr(c, "act_dtype", _abi.FM_BF16), setattr(c, "weight_dtype", _abi.FM_BF16),
+                setattr(c, "head_dim", 64), setattr(c, "chunk", 1025)), _abi.FM_ERR_UNSUPPORTED),  # bf16: <= 1024
+    (lambda c: setattr(c, "exec_mode", _abi.FM_EXEC_PERSISTENT), _abi.FM_ERR_UNSUPPORTED),
+])
+def test_encoder_create_rejects_bad_config_before_device_work(mutate, status):
+    c = _cfg()
+    mutate(c)
+    st, ctx = _encoder_create(c)
+    assert st == status, (st, fm.fm_last_error())
+    assert ctx.value is None
+
+
+def test_encoder_create_ignores_the_expert_only_fields():
+    # fields the encoder does not read may hold values fm_create would refuse;
+    # validation then passes and stops at the (absent) layers or the device
+    c = _cfg(action_dim=7, n_frames=2, norm="ada", time_dim=3)
+    c.sampler = 9
+    st, ctx = _encoder_create(c, layers=False)
+    assert st == _abi.FM_ERR_ARG and "layers" in fm.fm_last_error(), fm.fm_last_error()
+    assert ctx.value is None
+
+
+def test_encoder_null_calls_fail_cleanly():
+    L = fm.lib()
+    assert L.fm_encoder_create(None, None, None, None) == _abi.FM_ERR_ARG
+    assert L.fm_encode_prefix(None, None, None, None) == _abi.FM_ERR_ARG
