@@ -97,6 +97,106 @@ def cpu_baseline(cfg, W, k, v, x0, st, budget_s):
                       f"scaled x{cfg.batch} robots"}
 
 
+def pipeline_bench(args, cfg):
+    """Ticks of the streaming loop with the frame encoder in it.  serial: on
+    one stream, encode frame t (256 tokens through the Pi0-shaped stack) ->
+    append -> denoise.  pipelined: the encoder on its own stream encodes frame
+    t + 1 while tick t denoises; the tick ends with the device-side hand-off
+    (fm_append_encoded).  Both run K timed ticks after W warmup ticks."""
+    import numpy as np
+    import torch
+
+    import fm_synth as S
+    import flow_matching_denoising_euler_amd as fm
+
+    if cfg.n_frames <= 0:
+        print("bench.py --pipeline needs a streaming workload (one with a frame ring)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    log(f"bench: generating {cfg.name} and its prefix stack")
+    W = S.make_weights(cfg)
+    Wp, _ = S.make_prefix_stack(cfg.replace(batch=1), 1)
+    k, v = S.make_prefix(cfg)
+    g = np.random.default_rng(cfg.seed + 100)
+    ftok = [torch.from_numpy(S.round_bf16(g.standard_normal((cfg.batch, cfg.frame_tokens, cfg.d_model)))).cuda()
+            for _ in range(4)]
+    x0 = torch.from_numpy(S.make_noise(cfg)).cuda()
+    st = S.make_state(cfg)
+    res = {}
+    for mode in ("serial", "pipelined"):
+        sD = torch.cuda.Stream()
+        sE = torch.cuda.Stream() if mode == "pipelined" else sD
+        with torch.cuda.stream(sD):
+            den = fm.Denoiser(cfg, W, stream=sD)
+            keep = [den.set_prefix_kv(b, k[b], v[b]) for b in range(cfg.batch)]
+            state = None if st is None else den._act(st)
+            out = torch.empty_like(x0)
+        with torch.cuda.stream(sE):
+            enc = fm.Encoder(cfg, Wp, n_tokens=cfg.frame_tokens, n_seqs=cfg.batch, stream=sE)
+        torch.cuda.synchronize()
+
+        def tick(i):
+            with torch.cuda.stream(sE):
+                enc.encode_in_place(ftok[i % 4])
+            with torch.cuda.stream(sD):
+                if mode == "serial":  # the new frame first, then the denoise that sees it
+                    for b in range(cfg.batch):
+                        den.append_encoded(b, enc, b)
+                    fm.fm_denoise(den.ctx, x0, state, out)
+                else:  # denoise with the frames so far while the encoder runs, then hand off
+                    fm.fm_denoise(den.ctx, x0, state, out)
+                    for b in range(cfg.batch):
+                        den.append_encoded(b, enc, b)
+
+        for i in range(args.warmup):
+            tick(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(sD)
+        for i in range(args.steps):
+            tick(i)
+        t1.record(sD)
+        torch.cuda.synchronize()
+        res[mode] = t0.elapsed_time(t1) / args.steps
+        # the parts alone, on the same contexts
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(sE):
+            e0.record(sE)
+            for i in range(20):
+                enc.encode_in_place(ftok[i % 4])
+            e1.record(sE)
+        torch.cuda.synchronize()
+        res["encode_ms"] = e0.elapsed_time(e1) / 20
+        with torch.cuda.stream(sD):
+            e0.record(sD)
+            for i in range(20):
+                fm.fm_denoise(den.ctx, x0, state, out)
+            e1.record(sD)
+        torch.cuda.synchronize()
+        res["denoise_ms"] = e0.elapsed_time(e1) / 20
+        assert torch.isfinite(out).all().item(), "non-finite actions"
+        log(f"bench: {mode} {res[mode]:.4f} ms/tick (encode {res['encode_ms']:.4f}, denoise {res['denoise_ms']:.4f})")
+        enc.close()
+        den.close()
+        del keep
+    line = {
+        "metric": "streaming tick ms (encode the new 256-token frame + append + denoise), async pipeline",
+        "value": round(res["pipelined"], 4),
+        "unit": "ms per tick",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["pipelined"], 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
+        "data": "synthetic (seeded weights for the expert and the prefix stack, N(0,1) frame tokens)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "frame_tokens": cfg.frame_tokens,
+                   "n_frames": cfg.n_frames, "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps,
+                   "parallelism": "single GPU, two streams"},
+        "serial_ms_per_tick": round(res["serial"], 4),
+        "encode_ms": round(res["encode_ms"], 4),
+        "denoise_ms": round(res["denoise_ms"], 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +211,10 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 256 MiB device copy (reference for PMC byte counters)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="streaming workloads: time whole ticks (encode the new frame through the prefix "
+                         "encoder, append it, denoise), serial on one stream and as the two-stream async "
+                         "pipeline; prints that line instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -125,6 +229,8 @@ def main():
     import flow_matching_denoising_euler_amd as fm
 
     cfg = S.workload(args.workload)
+    if args.pipeline:
+        return pipeline_bench(args, cfg)
     if args.sampler is not None:
         cfg = cfg.replace(sampler=args.sampler)
     if args.n_steps is not None:

@@ -14,7 +14,7 @@ from ._abi import (FM_ABI_VERSION, FM_BF16, FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC
 
 __all__ = ["FMError", "make_config", "fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv",
            "fm_denoise", "fm_get_info", "fm_launch_phase", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
-           "fm_encoder_create", "fm_encode_prefix", "Denoiser", "Encoder", "lib"]
+           "fm_encoder_create", "fm_encode_prefix", "fm_append_encoded", "Denoiser", "Encoder", "lib"]
 
 lib = _abi.lib
 
@@ -149,10 +149,17 @@ def fm_encoder_create(cfg, weights: dict, n_tokens: int, n_seqs: int = 1, stream
     return ctx
 
 
-def fm_encode_prefix(ctx, tokens, k_out, v_out):
+def fm_encode_prefix(ctx, tokens, k_out=None, v_out=None):
     """tokens: fp32 device [seqs][tokens][d_model]; k_out, v_out: device
-    [seqs][layers][tokens][kv_heads][head_dim] in the activation dtype."""
+    [seqs][layers][tokens][kv_heads][head_dim] in the activation dtype, or
+    both None (the output stays in the encoder for fm_append_encoded)."""
     _check(lib().fm_encode_prefix(ctx, _ptr(tokens), _ptr(k_out), _ptr(v_out)), ctx)
+
+
+def fm_append_encoded(ctx, robot: int, enc_ctx, seq: int = 0):
+    """Append sequence `seq` of the encoder's latest output to `robot`'s ring,
+    on ctx's stream behind the encode."""
+    _check(lib().fm_append_encoded(ctx, int(robot), enc_ctx, int(seq)), ctx)
 
 
 def fm_set_prefix_kv(ctx, robot: int, k, v, n_tokens: int):
@@ -236,6 +243,10 @@ class Denoiser(_Context):
         fm_append_prefix_kv(self.ctx, robot, k, v)
         return k, v
 
+    def append_encoded(self, robot: int, encoder, seq: int = 0):
+        """Append sequence `seq` of `encoder`'s latest output (see fm_append_encoded)."""
+        fm_append_encoded(self.ctx, robot, encoder.ctx, seq)
+
     def denoise(self, noise, state=None, out=None):
         import torch
         n = _dev_tensor(noise, torch.float32, self.device)
@@ -269,3 +280,11 @@ class Encoder(_Context):
         fm_encode_prefix(self.ctx, t, k_out, v_out)
         self._tokens = t  # alive until the next call
         return k_out, v_out
+
+    def encode_in_place(self, tokens):
+        """Encode without copying the K/V out: the output stays in the encoder
+        for Denoiser.append_encoded (the async-pipeline hand-off)."""
+        import torch
+        t = _dev_tensor(tokens, torch.float32, self.device)
+        fm_encode_prefix(self.ctx, t)
+        self._tokens = t

@@ -23,7 +23,7 @@ FM_SAMPLER_EULER, FM_SAMPLER_HEUN = 0, 1
 
 EXPORTS = ("fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv", "fm_denoise", "fm_get_info",
            "fm_destroy", "fm_last_error", "fm_quantize_e4m3", "fm_launch_phase", "fm_encoder_create",
-           "fm_encode_prefix")
+           "fm_encode_prefix", "fm_append_encoded")
 FM_PHASE_QKV, FM_PHASE_ATTN, FM_PHASE_OPROJ, FM_PHASE_GATEUP, FM_PHASE_DOWN, FM_PHASE_TAIL = range(6)
 
 
@@ -82,5 +82,7 @@ def lib() -> ctypes.CDLL:
         L.fm_encoder_create.restype = ctypes.c_int
         L.fm_encode_prefix.argtypes = [vp, vp, vp, vp]
         L.fm_encode_prefix.restype = ctypes.c_int
+        L.fm_append_encoded.argtypes = [vp, i32, vp, i32]
+        L.fm_append_encoded.restype = ctypes.c_int
         _LIB = L
     return _LIB

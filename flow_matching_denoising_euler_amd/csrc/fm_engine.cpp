@@ -77,7 +77,8 @@ struct fm_ctx {
   void *u, *uf, *qkv, *o, *z;
   unsigned* counters;
   size_t n_counters;
-  void *enc_k, *enc_v;  // encoder output rows [B][L][S][HD] act
+  void *enc_k[2], *enc_v[2];  // encoder output rows [B][L][S][HD] act, two slots used in turn
+  int enc_slot = 0;            // slot the graph being captured writes
 
   // host mirror of the prefix state
   std::vector<int> valid, head;
@@ -86,8 +87,16 @@ struct fm_ctx {
   double* tkd = nullptr;    // device copy of tk
   std::vector<char> is_set;
 
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t gexec = nullptr;
+  hipGraph_t graph[2] = {nullptr, nullptr};  // the loop; an encoder has one per output slot
+  hipGraphExec_t gexec[2] = {nullptr, nullptr};
+
+  // encoder hand-off to fm_append_encoded: encode n writes slot n % 2; `done`
+  // follows the latest encode on this context's stream, consumed[j] the
+  // latest append that read slot j.  Two slots let encode n + 1 run while
+  // encode n's output is still waiting to be appended.
+  hipEvent_t done = nullptr, consumed[2] = {nullptr, nullptr};
+  bool consumed_rec[2] = {false, false};
+  long n_enc = 0;
 };
 
 namespace {
@@ -327,8 +336,10 @@ void carve(fm_ctx* x, Arena& a) {
                                    (size_t)x->B * x->Hkv * x->nqblk * 2) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);
   const size_t kvo = x->encoder ? (size_t)x->B * L * x->S * x->HD * ea : 16;
-  x->enc_k = a.take(kvo);
-  x->enc_v = a.take(kvo);
+  for (int j = 0; j < 2; ++j) {
+    x->enc_k[j] = a.take(kvo);
+    x->enc_v[j] = a.take(kvo);
+  }
 }
 
 Tab T(const float* base, long stride) { return Tab{base, stride}; }
@@ -442,7 +453,7 @@ fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_fin
 // encoder: layer l's K and V out of the suffix blocks into the output rows
 fm_status enqueue_unpack(fm_ctx* x, int l, hipStream_t st) {
   KvUnpack c{};
-  c.ks = x->ksuf; c.vs = x->vsuf; c.kd = x->enc_k; c.vd = x->enc_v;
+  c.ks = x->ksuf; c.vs = x->vsuf; c.kd = x->enc_k[x->enc_slot]; c.vd = x->enc_v[x->enc_slot];
   c.elt = x->act; c.B = x->B; c.S = x->S; c.SP = x->SP; c.HD = x->HD; c.Dh = x->Dh; c.layers = x->L; c.layer = l;
   HIPCHK(x, launch_kv_unpack(c, st), "kv unpack");
   return FM_OK;
@@ -678,30 +689,42 @@ fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream
     hip_fail(x, e, "capture stream");
     return bail(FM_ERR_DEVICE);
   }
+  if (encoder && ((e = hipEventCreateWithFlags(&x->done, hipEventDisableTiming)) != hipSuccess ||
+                  (e = hipEventCreateWithFlags(&x->consumed[0], hipEventDisableTiming)) != hipSuccess ||
+                  (e = hipEventCreateWithFlags(&x->consumed[1], hipEventDisableTiming)) != hipSuccess)) {
+    hip_fail(x, e, "encoder events");
+    return bail(FM_ERR_DEVICE);
+  }
   if ((e = hipStreamSynchronize(st)) != hipSuccess) {
     hip_fail(x, e, "create sync");
     return bail(FM_ERR_DEVICE);
   }
-  if ((e = hipStreamBeginCapture(x->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
-    hip_fail(x, e, "begin capture");
-    return bail(FM_ERR_DEVICE);
+  for (int gi = 0; gi < (encoder ? 2 : 1); ++gi) {
+    x->enc_slot = gi;
+    if ((e = hipStreamBeginCapture(x->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
+      hip_fail(x, e, "begin capture");
+      return bail(FM_ERR_DEVICE);
+    }
+    const fm_status cs = enqueue_graph_body(x, x->cap);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(x->cap, &g);
+    if (cs != FM_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return bail(cs);
+    }
+    if (e != hipSuccess) {
+      hip_fail(x, e, "end capture");
+      return bail(FM_ERR_DEVICE);
+    }
+    x->graph[gi] = g;
+    if ((e = hipGraphInstantiate(&x->gexec[gi], g, nullptr, nullptr, 0)) != hipSuccess) {
+      hip_fail(x, e, "graph instantiate");
+      return bail(FM_ERR_DEVICE);
+    }
   }
-  const fm_status cs = enqueue_graph_body(x, x->cap);
-  hipGraph_t g = nullptr;
-  e = hipStreamEndCapture(x->cap, &g);
-  if (cs != FM_OK) {
-    if (g) (void)hipGraphDestroy(g);
-    return bail(cs);
-  }
-  if (e != hipSuccess) {
-    hip_fail(x, e, "end capture");
-    return bail(FM_ERR_DEVICE);
-  }
-  x->graph = g;
-  if ((e = hipGraphInstantiate(&x->gexec, g, nullptr, nullptr, 0)) != hipSuccess) {
-    hip_fail(x, e, "graph instantiate");
-    return bail(FM_ERR_DEVICE);
-  }
+  // the capture stream has done its work
+  (void)hipStreamDestroy(x->cap);
+  x->cap = nullptr;
   if ((e = hipStreamSynchronize(st)) != hipSuccess) {
     hip_fail(x, e, "create sync");
     return bail(FM_ERR_DEVICE);
@@ -776,14 +799,19 @@ fm_status fm_set_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* 
   return FM_OK;
 }
 
-fm_status fm_append_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* v) {
-  fm_status s = check_ctx(x);
-  if (s != FM_OK) return s;
+}  // extern "C"
+
+namespace {
+
+fm_status check_append(fm_ctx* x, int32_t robot) {
   if (robot < 0 || robot >= x->B) return fail(x, FM_ERR_ARG, "robot %d out of range [0, %d)", robot, x->B);
   if (x->cfg.n_frames <= 0) return fail(x, FM_ERR_STATE, "the context has no frame ring");
   if (!x->is_set[robot]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", robot);
-  if (!k || !v) return fail(x, FM_ERR_ARG, "k_frame or v_frame is NULL");
-  if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k_frame and v_frame must be 16-byte aligned");
+  return FM_OK;
+}
+
+// frame rows [L][frame_tokens][HD] -> the oldest ring slot, which becomes the newest
+fm_status enqueue_append(fm_ctx* x, int32_t robot, const void* k, const void* v) {
   const int slot = x->head[robot];
   const int nh = (slot + 1) % x->cfg.n_frames;
   const size_t ea = elt_size(x->act);
@@ -798,6 +826,41 @@ fm_status fm_append_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const voi
   return FM_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+fm_status fm_append_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* v) {
+  fm_status s = check_ctx(x);
+  if (s != FM_OK) return s;
+  if ((s = check_append(x, robot)) != FM_OK) return s;
+  if (!k || !v) return fail(x, FM_ERR_ARG, "k_frame or v_frame is NULL");
+  if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k_frame and v_frame must be 16-byte aligned");
+  return enqueue_append(x, robot, k, v);
+}
+
+fm_status fm_append_encoded(fm_ctx* x, int32_t robot, fm_ctx* enc, int32_t seq) {
+  fm_status s = check_ctx(x);
+  if (s != FM_OK) return s;
+  if ((s = check_append(x, robot)) != FM_OK) return s;
+  if (!enc || !enc->encoder || enc->poisoned) return fail(x, FM_ERR_ARG, "enc is not a usable encoder context");
+  if (enc->n_enc == 0) return fail(x, FM_ERR_STATE, "the encoder has not encoded anything yet");
+  if (seq < 0 || seq >= enc->B) return fail(x, FM_ERR_ARG, "seq %d out of range [0, %d)", seq, enc->B);
+  if (enc->L != x->L || enc->Hkv != x->Hkv || enc->Dh != x->Dh || enc->act != x->act ||
+      enc->S != x->cfg.frame_tokens)
+    return fail(x, FM_ERR_SHAPE, "encoder output (%d layers, %d tokens, %d x %d, dtype %d) does not fit a frame "
+                "(%d layers, %d tokens, %d x %d, dtype %d)", enc->L, enc->S, enc->Hkv, enc->Dh, enc->act, x->L,
+                x->cfg.frame_tokens, x->Hkv, x->Dh, x->act);
+  const size_t off = (size_t)seq * x->L * enc->S * x->HD * elt_size(x->act);
+  const int j = (int)((enc->n_enc - 1) % 2);  // the latest encode's slot
+  HIPCHK(x, hipStreamWaitEvent(x->stream, enc->done, 0), "wait for the encoder");
+  if ((s = enqueue_append(x, robot, (const char*)enc->enc_k[j] + off, (const char*)enc->enc_v[j] + off)) != FM_OK)
+    return s;
+  HIPCHK(x, hipEventRecord(enc->consumed[j], x->stream), "record the hand-off");
+  enc->consumed_rec[j] = true;
+  return FM_OK;
+}
+
 fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* actions) {
   fm_status s = check_ctx(x);
   if (s != FM_OK) return s;
@@ -806,22 +869,31 @@ fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* ac
   for (int b = 0; b < x->B; ++b)
     if (!x->is_set[b]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", b);
   if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
-  HIPCHK(x, hipGraphLaunch(x->gexec, x->stream), "graph launch");
+  HIPCHK(x, hipGraphLaunch(x->gexec[0], x->stream), "graph launch");
   return enqueue_tail(x, x->N - 1, x->heun ? 2 : 0, x->stream, actions);
 }
 
 fm_status fm_encode_prefix(fm_ctx* x, const float* tokens, void* k_out, void* v_out) {
   fm_status s = check_ctx(x, true);
   if (s != FM_OK) return s;
-  if (!tokens || !k_out || !v_out) return fail(x, FM_ERR_ARG, "tokens, k_out or v_out is NULL");
+  if (!tokens) return fail(x, FM_ERR_ARG, "tokens is NULL");
+  if (!k_out != !v_out) return fail(x, FM_ERR_ARG, "k_out and v_out must both be given or both be NULL");
+  // this encode's slot held the output of two encodes ago, which an
+  // fm_append_encoded on another stream may still be reading
+  const int j = (int)(x->n_enc % 2);
+  if (x->consumed_rec[j]) HIPCHK(x, hipStreamWaitEvent(x->stream, x->consumed[j], 0), "wait for the hand-off");
   TokensIn t{};
   t.tokens = tokens; t.g1 = x->g1; t.h = x->h; t.u = x->u; t.ssq = x->ssq;
   t.M = x->M; t.d = x->d; t.esplit = x->esplit;
   HIPCHK(x, launch_tokens_in(x->act, t, x->stream), "tokens in");
-  HIPCHK(x, hipGraphLaunch(x->gexec, x->stream), "graph launch");
-  const size_t bytes = (size_t)x->B * x->L * x->S * x->HD * elt_size(x->act);
-  HIPCHK(x, hipMemcpyAsync(k_out, x->enc_k, bytes, hipMemcpyDeviceToDevice, x->stream), "k out");
-  HIPCHK(x, hipMemcpyAsync(v_out, x->enc_v, bytes, hipMemcpyDeviceToDevice, x->stream), "v out");
+  HIPCHK(x, hipGraphLaunch(x->gexec[j], x->stream), "graph launch");
+  if (k_out) {
+    const size_t bytes = (size_t)x->B * x->L * x->S * x->HD * elt_size(x->act);
+    HIPCHK(x, hipMemcpyAsync(k_out, x->enc_k[j], bytes, hipMemcpyDeviceToDevice, x->stream), "k out");
+    HIPCHK(x, hipMemcpyAsync(v_out, x->enc_v[j], bytes, hipMemcpyDeviceToDevice, x->stream), "v out");
+  }
+  HIPCHK(x, hipEventRecord(x->done, x->stream), "record the encode");
+  ++x->n_enc;
   return FM_OK;
 }
 
@@ -866,9 +938,14 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
 void fm_destroy(fm_ctx* x) {
   if (!x) return;
   if (x->stream || x->arena) (void)hipStreamSynchronize(x->stream);
-  if (x->gexec) (void)hipGraphExecDestroy(x->gexec);
-  if (x->graph) (void)hipGraphDestroy(x->graph);
+  for (int j = 0; j < 2; ++j) {
+    if (x->gexec[j]) (void)hipGraphExecDestroy(x->gexec[j]);
+    if (x->graph[j]) (void)hipGraphDestroy(x->graph[j]);
+  }
   if (x->cap) (void)hipStreamDestroy(x->cap);
+  if (x->done) (void)hipEventDestroy(x->done);
+  for (hipEvent_t ev : x->consumed)
+    if (ev) (void)hipEventDestroy(ev);
   if (x->arena) (void)hipFree(x->arena);
   delete x;
 }

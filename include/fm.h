@@ -244,9 +244,30 @@ fm_status fm_encoder_create(const fm_config* cfg, const fm_weights* w, void* hip
  * elements) is the k / v argument of fm_set_prefix_kv or
  * fm_append_prefix_kv for a denoising context of the same n_layers,
  * n_kv_heads, head_dim and act_dtype (16-byte aligned if the buffers are).
- * Asynchronous; allocates nothing.
+ * k_out and v_out may both be NULL: the output then stays in the encoder,
+ * for fm_append_encoded.  The encoder keeps the outputs of its latest two
+ * calls, in two slots used in turn; a call first waits (on the device) for
+ * the last fm_append_encoded that read its slot, i.e. the output of two calls
+ * before.  Asynchronous; allocates nothing.
  */
 fm_status fm_encode_prefix(fm_ctx* enc, const float* tokens, void* k_out, void* v_out);
+
+/*
+ * Async pipeline hand-off (Reflex abstract: an asynchronous pipeline that
+ * decouples visual encoding from action generation).  Appends sequence `seq`
+ * of the encoder's latest output to robot `robot`'s frame ring in `ctx`, as
+ * fm_append_prefix_kv would, enqueued on ctx's stream behind the encode (a
+ * device-side wait on the encoder's stream, no host synchronisation).  The
+ * encoder may therefore run on its own stream and encode frame t + 1 while
+ * ctx denoises with frames up to t; each tick then ends with this call.
+ * Both contexts live on one device; the encoder's chunk must equal ctx's
+ * frame_tokens, and n_layers, n_kv_heads, head_dim and act_dtype must match
+ * (FM_ERR_SHAPE).  FM_ERR_STATE if the encoder has not encoded yet, or as
+ * fm_append_prefix_kv.  Reads the output of the encoder's latest call.  One
+ * consuming stream per encoder output: a later encode into the same slot
+ * waits for the latest hand-off from it only.
+ */
+fm_status fm_append_encoded(fm_ctx* ctx, int32_t robot, fm_ctx* enc, int32_t seq);
 
 /* Fill *info.  Never fails on a valid context.  For an encoder context the
  * per-step fields describe one fm_encode_prefix call (weights streamed, K/V

@@ -146,3 +146,4 @@ def test_encoder_null_calls_fail_cleanly():
     L = fm.lib()
     assert L.fm_encoder_create(None, None, None, None) == _abi.FM_ERR_ARG
     assert L.fm_encode_prefix(None, None, None, None) == _abi.FM_ERR_ARG
+    assert L.fm_append_encoded(None, 0, None, 0) == _abi.FM_ERR_ARG

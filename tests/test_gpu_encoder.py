@@ -202,3 +202,116 @@ def test_encoded_frames_stream_through_the_ring():
         kr = np.concatenate([pk_] + [k for k, _ in win], axis=1)[None]
         vr = np.concatenate([pv_] + [v for _, v in win], axis=1)[None]
         check(f"encoder ring tick {tick}", out, O.denoise(cfg, W, kr, vr, x0, st), 1e-2, 3e-2)
+
+
+# --- the async pipeline: encode on its own stream, hand off on the device -----------
+def _ring_inputs(batch=1):
+    cfg = small_cfg(name="enc_pipe", prefix_static=20, frame_tokens=32, n_frames=3, prefix_len=116, batch=batch)
+    W = S.make_weights(cfg)
+    Wp, _ = S.make_prefix_stack(cfg, 1)
+    g = np.random.default_rng(12)
+    tok = lambda n: S.round_bf16(g.standard_normal((batch, n, cfg.d_model))).astype(np.float32)
+    return cfg, W, Wp, tok(20), [tok(32) for _ in range(7)]
+
+
+def _pipeline(cfg, W, Wp, prompt, frames, two_streams):
+    """Set [prompt | frames 0..2], then per tick t: denoise, and encode frame
+    t + 3 and append it.  two_streams: the encode runs on its own stream,
+    overlapping the denoise, and reaches the ring through fm_append_encoded;
+    otherwise everything is serial on one stream through caller buffers."""
+    import torch
+    import flow_matching_denoising_euler_amd as fm
+    sD = torch.cuda.Stream()
+    sE = torch.cuda.Stream() if two_streams else sD
+    x0, st = S.make_noise(cfg), S.make_state(cfg)
+    outs = []
+    with torch.cuda.stream(sD):
+        den = fm.Denoiser(cfg, W, stream=sD)
+        penc = fm.Encoder(cfg, Wp, n_tokens=20, n_seqs=cfg.batch, stream=sD)
+    with torch.cuda.stream(sE):
+        fenc = fm.Encoder(cfg, Wp, n_tokens=32, n_seqs=cfg.batch, stream=sE)
+        ftok = [torch.from_numpy(f).cuda() for f in frames]
+    torch.cuda.synchronize()
+    try:
+        with torch.cuda.stream(sE):
+            kf, vf = zip(*[fenc.encode(f) for f in ftok[:3]])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sD):
+            kp, vp = penc.encode(prompt)
+            for b in range(cfg.batch):
+                k0 = torch.cat([kp[b]] + [x[b] for x in kf], dim=1).contiguous()
+                v0 = torch.cat([vp[b]] + [x[b] for x in vf], dim=1).contiguous()
+                fm.fm_set_prefix_kv(den.ctx, b, k0, v0, k0.shape[1])
+            noise = torch.from_numpy(x0).cuda()
+            state = None if st is None else den._act(st)
+            torch.cuda.synchronize()
+        keep = []
+        for t in range(len(frames) - 3):
+            with torch.cuda.stream(sE):
+                if two_streams:
+                    fenc.encode_in_place(ftok[t + 3])
+                else:
+                    keep.append(fenc.encode(ftok[t + 3]))
+            with torch.cuda.stream(sD):
+                out = torch.empty_like(noise)
+                fm.fm_denoise(den.ctx, noise, state, out)
+                outs.append(out)
+                for b in range(cfg.batch):
+                    if two_streams:
+                        den.append_encoded(b, fenc, b)
+                    else:
+                        fm.fm_append_prefix_kv(den.ctx, b, keep[-1][0][b], keep[-1][1][b])
+        torch.cuda.synchronize()
+        return [o.cpu().numpy() for o in outs], x0, st
+    finally:
+        den.close()
+        fenc.close()
+        penc.close()
+
+
+def test_pipeline_equals_serial_bitwise_and_oracle():
+    cfg, W, Wp, prompt, frames = _ring_inputs(batch=2)
+    announce("async pipeline: 4 ticks, two robots")
+    pipe, x0, st = _pipeline(cfg, W, Wp, prompt, frames, two_streams=True)
+    ser, _, _ = _pipeline(cfg, W, Wp, prompt, frames, two_streams=False)
+    for t, (a, b) in enumerate(zip(pipe, ser)):
+        assert np.array_equal(a, b), f"tick {t}: pipelined != serial"
+    # tick t denoises with frames t .. t + 2
+    W64 = _prefix_weights(cfg, Wp)
+    for t in (0, 3):
+        kr, vr = [], []
+        for b in range(cfg.batch):
+            parts = [O.prefix_stack_kv(cfg, W64, x[b]) for x in [prompt] + frames[t:t + 3]]
+            kr.append(np.concatenate([p[0] for p in parts], axis=1))
+            vr.append(np.concatenate([p[1] for p in parts], axis=1))
+        check(f"pipeline tick {t}", pipe[t], O.denoise(cfg, W, np.stack(kr), np.stack(vr), x0, st), 1e-2, 3e-2)
+
+
+def test_append_encoded_rejects_mismatches():
+    import flow_matching_denoising_euler_amd as fm
+    from flow_matching_denoising_euler_amd import _abi
+    cfg, W, Wp, prompt, frames = _ring_inputs()
+    announce("fm_append_encoded errors")
+    den = fm.Denoiser(cfg, W)
+    enc = fm.Encoder(cfg, Wp, n_tokens=32)
+    bad = fm.Encoder(cfg, Wp, n_tokens=20)
+    plain = fm.Denoiser(small_cfg(), S.make_weights(small_cfg()))
+    try:
+        L = fm.lib()
+        k0 = np.zeros((cfg.n_layers, 116, cfg.n_kv_heads, cfg.head_dim), np.float32)
+        keep = den.set_prefix_kv(0, k0, k0)
+        assert L.fm_append_encoded(den.ctx, 0, enc.ctx, 0) == _abi.FM_ERR_STATE  # nothing encoded yet
+        enc.encode_in_place(frames[0])
+        bad.encode_in_place(prompt)
+        assert L.fm_append_encoded(den.ctx, 0, bad.ctx, 0) == _abi.FM_ERR_SHAPE  # 20 tokens, frames of 32
+        assert L.fm_append_encoded(den.ctx, 0, enc.ctx, 1) == _abi.FM_ERR_ARG    # one sequence
+        assert L.fm_append_encoded(den.ctx, 1, enc.ctx, 0) == _abi.FM_ERR_ARG    # one robot
+        assert L.fm_append_encoded(den.ctx, 0, den.ctx, 0) == _abi.FM_ERR_ARG    # not an encoder
+        assert L.fm_append_encoded(plain.ctx, 0, enc.ctx, 0) == _abi.FM_ERR_STATE  # no ring
+        assert L.fm_append_encoded(den.ctx, 0, enc.ctx, 0) == _abi.FM_OK
+        import torch
+        torch.cuda.synchronize()
+        del keep
+    finally:
+        for c in (den, enc, bad, plain):
+            c.close()
