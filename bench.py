@@ -97,6 +97,61 @@ def cpu_baseline(cfg, W, k, v, x0, st, budget_s):
                       f"scaled x{cfg.batch} robots"}
 
 
+def encode_bench(args, cfg):
+    """The prefix encoder alone: ms per fm_encode_prefix call (output left in
+    the encoder), and the dominant kernel against its roofline.  Its GEMMs
+    have M = batch x frame_tokens rows; at 256 rows and bf16 the arithmetic
+    intensity (2 x 256 / 2 = 256 flop/B) is below the ridge (312), so the
+    encode is priced on its weight stream."""
+    import numpy as np
+    import torch
+
+    import fm_synth as S
+    import flow_matching_denoising_euler_amd as fm
+
+    torch.cuda.set_device(0)
+    n_tok = cfg.frame_tokens or 256
+    log(f"bench: prefix stack of {cfg.name}, {cfg.batch} x {n_tok} tokens")
+    Wp, tokens = S.make_prefix_stack(cfg, n_tok)
+    stream = torch.cuda.current_stream()
+    enc = fm.Encoder(cfg, Wp, n_tokens=n_tok, n_seqs=cfg.batch, stream=stream)
+    tok = torch.from_numpy(tokens).cuda()
+    for _ in range(args.warmup):
+        enc.encode_in_place(tok)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        enc.encode_in_place(tok)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    info = enc.info()
+    byts = info.weight_bytes_per_step + info.kv_bytes_per_step
+    achieved = byts / (ms * 1e-3) / 1e9
+    d, L, F, Hq, Hkv, Dh = cfg.d_model, cfg.n_layers, cfg.d_mlp, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    M = cfg.batch * n_tok
+    flops = 2 * M * (L * d * (Hq + 2 * Hkv) * Dh + (L - 1) * (d * Hq * Dh + 3 * d * F)) + \
+        4 * cfg.batch * (L - 1) * n_tok * Hq * Dh * n_tok
+    log(f"bench: encode {ms:.4f} ms -> {achieved:.1f} GB/s of weights + K/V, {flops / ms / 1e9:.1f} TFLOP/s")
+    line = {
+        "metric": "prefix encoder ms per call (frames through the expert-shaped stack)",
+        "value": round(ms, 4), "unit": "ms per encode", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
+        "data": "synthetic (seeded prefix-stack weights, N(0,1) tokens)",
+        "config": {"workload": cfg.name, "sequences": cfg.batch, "tokens": n_tok, "d_model": d, "layers": L,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole encode (weights streamed once, K/V written once)",
+                     "per_launch": {"bytes": byts, "flops": flops, "avg_us": round(ms * 1e3, 3)}},
+        "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+    }
+    enc.close()
+    print(json.dumps(line), flush=True)
+
+
 def pipeline_bench(args, cfg):
     """Ticks of the streaming loop with the frame encoder in it.  serial: on
     one stream, encode frame t (256 tokens through the Pi0-shaped stack) ->
@@ -215,6 +270,9 @@ def main():
                     help="streaming workloads: time whole ticks (encode the new frame through the prefix "
                          "encoder, append it, denoise), serial on one stream and as the two-stream async "
                          "pipeline; prints that line instead")
+    ap.add_argument("--encode", action="store_true",
+                    help="time the prefix encoder instead: one call encodes `batch` frames of frame_tokens "
+                         "(256 if the workload has no ring) through the expert-shaped stack; prints that line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -231,6 +289,8 @@ def main():
     cfg = S.workload(args.workload)
     if args.pipeline:
         return pipeline_bench(args, cfg)
+    if args.encode:
+        return encode_bench(args, cfg)
     if args.sampler is not None:
         cfg = cfg.replace(sampler=args.sampler)
     if args.n_steps is not None:

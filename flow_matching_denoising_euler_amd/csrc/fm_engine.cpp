@@ -359,7 +359,13 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
     g.out = x->qkv;
     g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(x->zeros, 0);
     g.ksuf = x->ksuf; g.vsuf = x->vsuf; g.S = x->S; g.SP = x->SP; g.Hq = x->Hq; g.Hkv = x->Hkv; g.Dh = x->Dh;
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_QKV, g, st), "qkv gemm");
+    if (x->encoder) {  // layer l's K and V rows of the output slot being captured
+      const size_t lo = (size_t)l * x->S * x->HD * elt_size(x->act);
+      g.krow = (char*)x->enc_k[x->enc_slot] + lo;
+      g.vrow = (char*)x->enc_v[x->enc_slot] + lo;
+      g.row_bstride = (long)x->L * x->S * x->HD;
+    }
+    HIPCHK(x, launch_gemm(x->act, x->wt, x->encoder ? EPI_QKVR : EPI_QKV, g, st), "qkv gemm");
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     AttnArgs at{};
     at.qkv = x->qkv;
@@ -450,15 +456,6 @@ fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_fin
   return FM_OK;
 }
 
-// encoder: layer l's K and V out of the suffix blocks into the output rows
-fm_status enqueue_unpack(fm_ctx* x, int l, hipStream_t st) {
-  KvUnpack c{};
-  c.ks = x->ksuf; c.vs = x->vsuf; c.kd = x->enc_k[x->enc_slot]; c.vd = x->enc_v[x->enc_slot];
-  c.elt = x->act; c.B = x->B; c.S = x->S; c.SP = x->SP; c.HD = x->HD; c.Dh = x->Dh; c.layers = x->L; c.layer = l;
-  HIPCHK(x, launch_kv_unpack(c, st), "kv unpack");
-  return FM_OK;
-}
-
 // the graph body.  Denoiser: every step's layers and tails except the last
 // tail.  Encoder: every layer, the last one only up to its K and V (nothing
 // after them reaches the output).
@@ -467,7 +464,6 @@ fm_status enqueue_graph_body(fm_ctx* x, hipStream_t cap) {
   if (x->encoder) {
     for (int l = 0; l < x->L && cs == FM_OK; ++l) {
       cs = enqueue_phase(x, 0, l, FM_PHASE_QKV, cap);
-      if (cs == FM_OK) cs = enqueue_unpack(x, l, cap);
       for (int ph = FM_PHASE_ATTN; ph <= FM_PHASE_DOWN && cs == FM_OK && l + 1 < x->L; ++ph)
         cs = enqueue_phase(x, 0, l, ph, cap);
     }
@@ -918,7 +914,7 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
     // the last layer streams its QKV weights only; K/V out of every layer
     info->weight_bytes_per_step = (x->L * wqkv + (x->L - 1) * wrest) * ew + (x->L * sqkv + (x->L - 1) * srest) * 4;
     info->kv_bytes_per_step = (size_t)2 * x->B * x->L * x->S * x->HD * ea;
-    info->n_phases = 1 + 2 * x->L + 4 * (x->L - 1);
+    info->n_phases = 1 + x->L + 4 * (x->L - 1);
   } else {
     info->weight_bytes_per_step = x->L * ((wqkv + wrest) * ew + (sqkv + srest) * 4) + (size_t)(2 * x->A * x->d + x->d) * eg;
     size_t kv = 0;

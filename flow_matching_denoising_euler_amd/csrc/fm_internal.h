@@ -14,6 +14,7 @@ enum Epi : int {
   EPI_QKV = 0,    // out = act(acc * rstd[row] + bias[col])
   EPI_RESID = 1,  // h += alpha[col] * acc ; u = act(h * gnext[col]) ; ssq partials
   EPI_GELU = 2,   // z = act(gelu(g * rstd + bg) * (u * rstd + bu)), tile = [16 gate | 16 up]
+  EPI_QKVR = 3,   // EPI_QKV, and K and V also as rows (krow / vrow: the prefix encoder)
 };
 
 // Per-step table: element (step, i) lives at base[step * step_stride + i].
@@ -48,6 +49,10 @@ struct GemmArgs {
   void* u_out;            // RESID: [M][N] act = act(h * gnext)
   float* ssq_out;         // RESID: [M][N/16]
   int step;
+  // last, so that the fields every launch reads keep their kernel-argument offsets
+  void* krow;             // EPI_QKVR: K and V also as rows [b][S][Hkv*Dh]
+  void* vrow;             //   (sequence b at b * row_bstride elements)
+  long row_bstride;
 };
 
 // K/V storage ("kv layout").  A key block of NK keys (NK a multiple of 32)
@@ -229,15 +234,5 @@ struct TokensIn {
   int M, d, esplit;
 };
 hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st);
-// prefix encoder: one layer's suffix K/V (kv layout, SP keys per sequence)
-// -> rows [B][layers][S][HD] at layer `layer`
-struct KvUnpack {
-  const void* ks;
-  const void* vs;
-  void* kd;
-  void* vd;
-  int elt, B, S, SP, HD, Dh, layers, layer;
-};
-hipError_t launch_kv_unpack(const KvUnpack& c, hipStream_t st);
 
 }  // namespace fm

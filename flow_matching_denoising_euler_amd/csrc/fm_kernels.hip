@@ -502,7 +502,7 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
     }
   }
 
-  if constexpr (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_QKV || EPI == EPI_QKVR) {
     // Q columns -> out (row-major); suffix K and V -> their kv-layout blocks
     const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
     constexpr bool packed = ACT != ELT_F32;
@@ -514,14 +514,17 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
       if (r < g.M) {
         const int b = r / g.S, sr = r % g.S;
         const long sb = (long)b * g.Hkv * g.Dh * g.SP;
+        const long rw = EPI == EPI_QKVR ? (long)b * g.row_bstride + (long)sr * (g.Hkv * g.Dh) : 0;  // encoder rows
         if (col < kcol0) {
           st_act<ACT>(g.out, (long)r * g.N + col, val);
         } else if (col < vcol0) {
           const int jk = (col - kcol0) / g.Dh, dh = (col - kcol0) % g.Dh;
           st_act<ACT>(g.ksuf, sb + kv_k_off(packed, g.SP, g.Hkv, g.Dh, jk, sr, dh), val);
+          if constexpr (EPI == EPI_QKVR) st_act<ACT>(g.krow, rw + (col - kcol0), val);
         } else {
           const int jv = (col - vcol0) / g.Dh, dh = (col - vcol0) % g.Dh;
           st_act<ACT>(g.vsuf, sb + kv_v_off(packed, g.SP, g.Hkv, g.Dh, jv, sr, dh), val);
+          if constexpr (EPI == EPI_QKVR) st_act<ACT>(g.vrow, rw + (col - vcol0), val);
         }
       }
     }
@@ -851,7 +854,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   // epilogue: block (ni, m) of this lane = row m0 + (wm TMW + mb0 + m) 16 + (lane & 15),
   // columns n0 + (wn TNW + ni) 16 + (lane >> 4) 4 + [0, 4)
   const int c4 = (lane >> 4) * 4;
-  if constexpr (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_QKV || EPI == EPI_QKVR) {
     const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
     const int dsh = __builtin_ctz(g.Dh);  // head_dim is 32, 64, 128 or 256 on the bf16 path
 #pragma unroll
@@ -867,11 +870,13 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
         const float4 bias = *(const float4*)&s_col[0][ct];
         const f32x4 a = fin[ni][m];
         const float v0 = a[0] * rs + bias.x, v1 = a[1] * rs + bias.y, v2 = a[2] * rs + bias.z, v3 = a[3] * rs + bias.w;
+        const long rw = EPI == EPI_QKVR ? (long)b * g.row_bstride + (long)sr * (g.Hkv * g.Dh) : 0;  // encoder rows
         if (col < kcol0) {
           *(uint2*)((uint16_t*)g.out + (long)row * g.N + col) = pack4_bf16(v0, v1, v2, v3);
         } else if (col < vcol0) {
           const int jk = (col - kcol0) >> dsh, dh = (col - kcol0) & (g.Dh - 1);
           *(uint2*)((uint16_t*)g.ksuf + sb + kv_k_off(true, g.SP, g.Hkv, g.Dh, jk, sr, dh)) = pack4_bf16(v0, v1, v2, v3);
+          if constexpr (EPI == EPI_QKVR) *(uint2*)((uint16_t*)g.krow + rw + (col - kcol0)) = pack4_bf16(v0, v1, v2, v3);
         } else {
           const int jv = (col - vcol0) >> dsh, dh = (col - vcol0) & (g.Dh - 1);
           uint16_t* vp = (uint16_t*)g.vsuf + sb + kv_v_off(true, g.SP, g.Hkv, g.Dh, jv, sr, dh);
@@ -879,6 +884,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
           vp[8] = (uint16_t)f2bf(v1);
           vp[16] = (uint16_t)f2bf(v2);
           vp[24] = (uint16_t)f2bf(v3);
+          if constexpr (EPI == EPI_QKVR) *(uint2*)((uint16_t*)g.vrow + rw + (col - vcol0)) = pack4_bf16(v0, v1, v2, v3);
         }
       }
     }
@@ -1903,8 +1909,8 @@ __global__ void k_kv_copy(KvCopy c) {
 // policy that thinks too long": vision encoder, LLM, action expert as three
 // components; InstinctFlash README, "Framework overview": prefill extraction
 // as a graph-level optimisation).  The encoder runs the layer kernels above
-// over the prefix tokens as the "suffix" of an empty prefix; these two
-// kernels are its input and output.
+// over the prefix tokens as the "suffix" of an empty prefix; its QKV GEMMs
+// also write K and V as rows (EPI_QKVR), and this kernel is its input.
 // ---------------------------------------------------------------------------
 // Token rows in: the residual stream is the token embedding itself; writes
 // h, the first norm's operand u = act(h * g) in the packed GEMM layout and
@@ -1925,26 +1931,6 @@ __global__ __launch_bounds__(512) void k_tokens_in(TokensIn t) {
       st_act<ACT>(t.u, pk(r, col, t.d), hv * gain);
       if ((threadIdx.x & 15) == 0) t.ssq[(long)r * PM + (col >> 4)] = q;
     }
-  }
-}
-
-// One layer's K and V of every sequence, from the kv layout the QKV GEMM
-// writes (SP-key block per sequence) to rows [b][layer][t][HD]: the layout
-// fm_set_prefix_kv / fm_append_prefix_kv take.  Thread = one (b, t, column).
-template <typename T>
-__global__ void k_kv_unpack(KvUnpack c) {
-  constexpr bool packed = sizeof(T) == 2;
-  const int HD = c.HD, Dh = c.Dh, Hkv = HD / Dh;
-  const long total = (long)c.B * c.S * HD;
-  const long stride = (long)gridDim.x * blockDim.x;
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int col = (int)(i % HD);
-    const long bt = i / HD;
-    const int b = (int)(bt / c.S), t = (int)(bt % c.S);
-    const long src = (long)b * HD * c.SP;
-    const long dst = (((long)b * c.layers + c.layer) * c.S + t) * HD + col;
-    ((T*)c.kd)[dst] = ((const T*)c.ks)[src + kv_k_off(packed, c.SP, Hkv, Dh, col / Dh, t, col % Dh)];
-    ((T*)c.vd)[dst] = ((const T*)c.vs)[src + kv_v_off(packed, c.SP, Hkv, Dh, col / Dh, t, col % Dh)];
   }
 }
 
@@ -1991,6 +1977,7 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   if (p.mid) {
     if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 2, 4, 2, 2>), dim3(grid), dim3(512), 0, st, g);
     else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+    else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 2, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
     else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 4>), dim3(grid), dim3(256), 0, st, g);
     else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
     *err = hipGetLastError();
@@ -1998,6 +1985,7 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   }
   if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2, 2>), dim3(grid), dim3(512), 0, st, g);
   else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+  else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, st, g);
   else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 4>), dim3(grid), dim3(512), 0, st, g);
   else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
   *err = hipGetLastError();
@@ -2015,6 +2003,7 @@ static hipError_t gemm_dispatch(int epi, const GemmArgs& g, hipStream_t st) {
   if (((g.K >> 5) / (WT == ELT_FP8 ? 2 : 1)) % g.ksplit) return hipErrorInvalidValue;
   const int grid = g.mtiles * (g.N / nt) * g.ksplit;
   if (epi == EPI_QKV) return gemm_upw<ACT, WT, EPI_QKV, 1>(g, grid, st);
+  if (epi == EPI_QKVR) return gemm_upw<ACT, WT, EPI_QKVR, 1>(g, grid, st);
   if (epi == EPI_RESID) return gemm_upw<ACT, WT, EPI_RESID, 1>(g, grid, st);
   return gemm_upw<ACT, WT, EPI_GELU, 2>(g, grid, st);
 }
@@ -2162,14 +2151,6 @@ hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st) {
   const int grid = (t.M + 63) / 64 * t.esplit;
   if (act == ELT_F32) FM_LAUNCH_N(k_tokens_in<ELT_F32>, grid, 512, t);
   FM_LAUNCH_N(k_tokens_in<ELT_BF16>, grid, 512, t);
-}
-
-hipError_t launch_kv_unpack(const KvUnpack& c, hipStream_t st) {
-  const long work = (long)c.B * c.S * c.HD;
-  const int grid = (int)std::max(1L, std::min(2048L, (work + 255) / 256));
-  if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_unpack<float>, dim3(grid), dim3(256), 0, st, c);
-  else hipLaunchKernelGGL(k_kv_unpack<uint16_t>, dim3(grid), dim3(256), 0, st, c);
-  return hipGetLastError();
 }
 
 }  // namespace fm
