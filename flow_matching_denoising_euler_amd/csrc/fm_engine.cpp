@@ -148,6 +148,7 @@ fm_status validate_config(const fm_config* c) {
     return fail(nullptr, FM_ERR_SHAPE, "n_frames and frame_tokens must both be zero or both positive");
   if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, FM_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
   if (c->sampler != FM_SAMPLER_EULER && c->sampler != FM_SAMPLER_HEUN) return fail(nullptr, FM_ERR_ARG, "bad sampler");
+  if (c->state_causal != 0 && c->state_causal != 1) return fail(nullptr, FM_ERR_ARG, "state_causal must be 0 or 1");
   if (c->t_schedule) {
     // t_0 = 1 > t_1 > ... > t_N = 0, all finite
     const float* t = c->t_schedule;
@@ -384,6 +385,7 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
     at.scale = 1.f / sqrtf((float)x->Dh);
     at.part = x->attn_part; at.counters = x->counters;
     at.out = x->o;
+    at.state_causal = x->cfg.state_causal && x->hasS;
     if (x->mtiles == 1 && x->act == ELT_BF16) {
       // one row tile: the O and gate/up GEMMs run skinny, workgroup u reading
       // column tile u / ks and k-range u % ks; the idle CUs prefetch them

@@ -109,6 +109,9 @@ struct AttnArgs {
   int grid;               // attention workgroups (set by the launcher)
   const uint8_t* pf_w[2]; // packed weights (null: none)
   int pf_nbt[2], pf_ku[2], pf_nb[2], pf_ks[2], pf_units[2];
+  // block-causal suffix: the state row (suffix row 0, the first Hq/Hkv query
+  // rows of a kv group) sees no suffix key past itself
+  int state_causal;
 };
 
 struct OutArgs {

@@ -1014,7 +1014,7 @@ struct KeySpace {
 // its K fragments (K rows) and V fragments (8 keys of V^T per lane) straight
 // from memory: the next tile's K while the current tile's softmax runs, its
 // V after the current PV product.
-template <int DH>
+template <int DH, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   constexpr int KBD = DH / 32, NBD = DH / 16, KT = 32;
   __shared__ __align__(16) uint16_t sP[4][16][KT + 8];
@@ -1059,6 +1059,9 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 #pragma unroll
   for (int nbd = 0; nbd < NBD; ++nbd) oacc[nbd] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrow[4] = {0.f, 0.f, 0.f, 0.f};
+  bool st_row[4];  // CAUSAL: score rows of the state token (block-causal suffix)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st_row[r] = CAUSAL && qb * 16 + (lane >> 4) * 4 + r < G;
 
   auto step = [&](int t, int slot) {
     const bool more = t + 1 < ntile;
@@ -1077,7 +1080,8 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int key = (wave + 4 * t) * KT + nb * 16 + (lane & 15);
-        p[nb][r] = (key < ks.kp && ks.valid(key)) ? sacc[nb][r] * a.scale : -INFINITY;
+        const bool ok = key < ks.kp && ks.valid(key) && !(CAUSAL && st_row[r] && key > ks.TP);
+        p[nb][r] = ok ? sacc[nb][r] * a.scale : -INFINITY;
         m = fmaxf(m, p[nb][r]);
       }
       m = max16(m);
@@ -1204,7 +1208,7 @@ __device__ __forceinline__ void attn_weight_prefetch(const AttnArgs& a) {
   asm volatile("" ::"v"(acc));  // the loaded values are used: the loads stay
 }
 
-template <int DH, int R, int QB, int DS, bool PF>
+template <int DH, int R, int QB, int DS, bool PF, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
   // weight prefetch workgroups (a separate instantiation: the test needs a
   // kernel argument before the first load)
@@ -1306,6 +1310,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int u = 0; u < QB; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) mx[u][r] = -INFINITY;
+  // CAUSAL: the block-causal suffix, where the state token's rows (the
+  // first G query rows of a kv group) see no suffix key past itself
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int key = (kb0 + w + 8 * i) * 16 + (lane & 15);
@@ -1314,7 +1320,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int u = 0; u < QB; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sc[i][u][r] = ok ? sc[i][u][r] * a.scale : -INFINITY;
+        const bool okr = ok && !(CAUSAL && key > ks.TP && (qb * QB + u) * 16 + (lane >> 4) * 4 + r < G);
+        sc[i][u][r] = okr ? sc[i][u][r] * a.scale : -INFINITY;
         mx[u][r] = fmaxf(mx[u][r], sc[i][u][r]);
       }
   }
@@ -1530,7 +1537,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     for (int c = 0; c < Dh; ++c) { q[c] = qp[c]; o[c] = 0.f; }
     float m = -INFINITY, l = 0.f;
     for (int p = 0; p < ks.kp; ++p) {
-      if (!ks.valid(p)) continue;
+      if (!ks.valid(p) || (a.state_causal && s == 0 && p > ks.TP)) continue;
       float sc = 0.f;
       for (int c = 0; c < Dh; ++c) sc += q[c] * ks.kel(j, p, c);
       sc *= a.scale;
@@ -2015,17 +2022,17 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-template <int DH, int QB, int DS, bool PF>
+template <int DH, int QB, int DS, bool PF, bool CAUSAL = false>
 static hipError_t attn_sf_r(const AttnArgs& a, int grid, hipStream_t st) {
   switch ((a.keys_per_split + 7) / 8) {  // R: 16-key blocks per wave
-    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS, PF>), grid, 512, a);
-    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS, PF>), grid, 512, a);
-    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS, PF>), grid, 512, a);
-    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS, PF>), grid, 512, a);
-    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS, PF>), grid, 512, a);
-    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS, PF>), grid, 512, a);
-    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS, PF>), grid, 512, a);
-    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS, PF>), grid, 512, a);
+    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS, PF, CAUSAL>), grid, 512, a);
   }
   return hipErrorInvalidValue;
 }
@@ -2039,6 +2046,7 @@ static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
   // weight prefetchers on the idle CUs, if at least half of them are idle
   // (fewer would stretch the attention launch by more than they save)
   const int idle = a.pf_cus - a.grid;
+  if (a.state_causal) return attn_sf_r<DH, QB, DS, false, true>(a, a.grid, st);  // (no weight prefetch)
   if constexpr (DS >= 2)
     if ((a.pf_w[0] || a.pf_w[1]) && 2 * idle >= a.pf_cus) return attn_sf_r<DH, QB, DS, true>(a, a.grid + idle, st);
   return attn_sf_r<DH, QB, DS, false>(a, a.grid, st);
@@ -2061,7 +2069,8 @@ static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
     }
     return attn_sf<DH, 1, 1>(a, st);
   }
-  hipLaunchKernelGGL(k_attn_flash<DH>, dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
+  if (a.state_causal) hipLaunchKernelGGL((k_attn_flash<DH, true>), dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_flash<DH, false>), dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

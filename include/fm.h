@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 2
+#define FM_ABI_VERSION 3
 
 typedef struct fm_ctx fm_ctx;
 
@@ -119,6 +119,13 @@ typedef enum {
  *   scale per output row, see fm_quantize_e4m3; the other weights stay bf16).
  * act_dtype: dtype of GEMM operands, prefix K/V and the state vector.  The
  *   residual stream, softmax statistics and x are always fp32.
+ *
+ * state_causal (with state_dim > 0): 0 = every suffix token attends to the
+ *   whole prefix and the whole suffix; 1 = the state token attends to the
+ *   prefix and to itself only, the action tokens to everything (the
+ *   block-causal suffix of Pi0-style experts: the state token's values then
+ *   do not depend on x or t).  The pages fix no suffix mask; 0 is the
+ *   default reading and 1 the Pi0-style variant.
  */
 typedef struct {
   int32_t abi_version;               /* FM_ABI_VERSION */
@@ -133,6 +140,7 @@ typedef struct {
   float rms_eps;                     /* e.g. 1e-6 */
   int32_t exec_mode;                 /* fm_exec  */
   int32_t sampler;                   /* fm_sampler */
+  int32_t state_causal;              /* 0 or 1, see above */
   const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
 } fm_config;
 

@@ -281,12 +281,17 @@ def _norm(cfg, h, gain, mod):
 
 
 def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
-                    v_pre: np.ndarray, state: Optional[np.ndarray]) -> np.ndarray:
+                    v_pre: np.ndarray, state: Optional[np.ndarray], return_kv: bool = False):
     """Velocity v(x, t) of one robot.
 
     x [chunk][A]; k_pre, v_pre [layers][T][Hkv][Dh] in logical order; state
     [state_dim] or None.  W holds float64 weights (see effective_weights).
-    Returns v [chunk][A].
+    Returns v [chunk][A] (and, with return_kv, the suffix K and V of every
+    layer, [layers][S][Hkv][Dh]).
+
+    Suffix mask: none, or with cfg.state_causal the block-causal suffix of
+    Pi0-style experts (a reading; the pages fix no suffix mask): the state
+    token attends to the prefix and itself, the action tokens to everything.
     """
     S_has = 1 if cfg.state_dim else 0
     hq, hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -298,16 +303,24 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
     else:
         h = act
     S = h.shape[0]
+    T = np.asarray(k_pre[0]).shape[0] if len(k_pre) else 0
+    causal = bool(getattr(cfg, "state_causal", False)) and S_has
+    if causal:
+        allowed = np.ones((S, T + S), bool)
+        allowed[0, T + 1:] = False
     mods, mod_f = ada_modulation(cfg, W, t) if cfg.norm == "ada" else (None, None)
+    ks, vs = [], []
     for li, L in enumerate(W["layers"]):
         m1, m2 = mods[li] if mods else (None, None)
         u = _norm(cfg, h, L.get("norm1"), m1)
         q = linear(u, L["wq"]).reshape(S, hq, dh)
         k = linear(u, L["wk"]).reshape(S, hkv, dh)
         v = linear(u, L["wv"]).reshape(S, hkv, dh)
+        ks.append(k)
+        vs.append(v)
         K = np.concatenate([np.asarray(k_pre[li], F64), k], axis=0)
         V = np.concatenate([np.asarray(v_pre[li], F64), v], axis=0)
-        o = attention(q, K, V).reshape(S, hq * dh)
+        o = (masked_attention(q, K, V, allowed) if causal else attention(q, K, V)).reshape(S, hq * dh)
         a1 = m1[2] if m1 else 1.0
         h = h + a1 * linear(o, L["wo"])
         u = _norm(cfg, h, L.get("norm2"), m2)
@@ -315,7 +328,8 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
         a2 = m2[2] if m2 else 1.0
         h = h + a2 * linear(z, L["wd"])
     u = _norm(cfg, h[S_has:], W.get("norm_f"), mod_f)
-    return linear(u, W["w_out"], W["b_out"])
+    out = linear(u, W["w_out"], W["b_out"])
+    return (out, np.stack(ks), np.stack(vs)) if return_kv else out
 
 
 def euler(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
@@ -443,6 +457,8 @@ def joint_velocity(cfg, W64: dict, Wp: dict, tokens, x, t, state) -> np.ndarray:
     S = hs.shape[0]
     allowed = np.ones((T + S, T + S), bool)
     allowed[:T, T:] = False
+    if getattr(cfg, "state_causal", False) and S_has:  # see expert_velocity
+        allowed[T, T + 1:] = False
     mods, mod_f = ada_modulation(cfg, W64, t) if cfg.norm == "ada" else (None, None)
     for li, (L, Lp) in enumerate(zip(W64["layers"], Wp["layers"])):
         m1, m2 = mods[li] if mods else (None, None)

@@ -288,3 +288,52 @@ def test_full_pi05_ada_b16_sampled_robots():
 def test_full_stream_fp8_ticks():
     cfg = S.workload("stream_fp8")
     _ring_run(cfg, ticks=5, oracle_ticks={0, 3, 4})
+
+
+# --- block-causal state token (Pi0-style suffix) -------------------------------------
+# A few valid prefix tokens in a larger capacity keep each kernel path (the
+# paths follow the capacity) while the suffix, and with it the mask, weighs
+# in the attention.
+@pytest.mark.parametrize("kw", [
+    dict(prefix_len=8),                                          # one query block per workgroup
+    dict(batch=20, chunk=60, n_q_heads=8, prefix_static=100, prefix_len=8),  # two query blocks per workgroup
+    dict(head_dim=128, prefix_static=600, prefix_len=8),        # key split (ranges past the prefix masked)
+    dict(prefix_static=1100, prefix_len=8, chunk=9),             # flash kernel
+    dict(n_q_heads=2, head_dim=256, d_mlp=512, chunk=20, prefix_len=8),  # head-dim split in 4
+    dict(prefix_static=0, prefix_len=0),                         # empty prefix: the state sees itself only
+])
+def test_small_state_causal(kw):
+    cfg = small_cfg(state_causal=True, **kw)
+    announce(f"small state_causal {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    ref = O.denoise(cfg, W, k, v, x0, st)
+    check(f"small state_causal {kw}", got, ref, 1e-2, 3e-2)
+    # The mask moves the actions by less than the bf16 bar (the state is one
+    # key among many), so the bar alone would not notice a missing mask.
+    # The same inputs without the mask: the change the mask makes on the GPU
+    # must be the change it makes in the oracle (the two GPU runs share most
+    # of their roundings, so their difference is far less noisy than either).
+    cfg_f = cfg.replace(state_causal=False)
+    got_f = run_denoiser(cfg_f, W, k, v, x0, st)[0]
+    ref_f = O.denoise(cfg_f, W, k, v, x0, st)
+    d_gpu, d_ref = got.astype(np.float64) - got_f, ref - ref_f
+    err = O.rel_l2(d_gpu, d_ref)
+    announce(f"  mask effect: oracle {O.rel_l2(ref, ref_f):.3e} of the output; GPU effect vs oracle effect rel-L2 {err:.3e}")
+    assert err < 0.5, err  # no mask: 1
+
+
+def test_tiny_fp32_state_causal():
+    cfg = S.workload("tiny_fp32").replace(state_causal=True)
+    announce("tiny_fp32 state_causal")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("tiny_fp32 state_causal", got, O.denoise(cfg, W, k, v, x0, st), 1e-4)
+
+
+def test_full_pi0_1view_state_causal():
+    cfg = S.workload("pi0_1view").replace(state_causal=True)
+    announce("pi0_1view state_causal")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("pi0_1view state_causal", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)

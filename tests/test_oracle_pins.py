@@ -299,10 +299,11 @@ def test_sinusoid_values():
 
 
 # --- P7: cached timestep-invariant prefix equals joint recompute ----------------
-@pytest.mark.parametrize("kind", ["rms_mha", "rms_gqa", "ada"])
+@pytest.mark.parametrize("kind", ["rms_mha", "rms_gqa", "ada", "state_causal"])
 def test_cached_prefix_equals_joint_recompute(kind):
     cfg = {"rms_mha": TINY, "rms_gqa": _tiny(n_kv_heads=1, batch=2),
-           "ada": _tiny(norm="ada", time_dim=16, state_dim=0)}[kind]
+           "ada": _tiny(norm="ada", time_dim=16, state_dim=0),
+           "state_causal": _tiny(n_kv_heads=1, state_causal=True)}[kind]
     W = S.make_weights(cfg)
     x0, st = S.make_noise(cfg), S.make_state(cfg)
     Wp, tokens = S.make_prefix_stack(cfg, 32)
@@ -310,6 +311,41 @@ def test_cached_prefix_equals_joint_recompute(kind):
     cached = O.denoise(cfg, W, np.stack(ks), np.stack(vs), x0, st)
     joint = O.denoise_joint(cfg, W, Wp, tokens, x0, st)
     assert O.rel_l2(cached, joint) < 1e-12
+
+
+# --- block-causal state token (Pi0-style suffix) ------------------------------------
+def _one_robot(cfg):
+    W64 = O.effective_weights(cfg, S.make_weights(cfg))
+    k, v = S.make_prefix(cfg)
+    return W64, k[0], v[0], S.make_noise(cfg)[0], S.make_state(cfg)[0]
+
+
+@pytest.mark.parametrize("norm", ["rms", "ada"])
+def test_block_causal_state_is_a_cached_prefix_token(norm):
+    # Under the block-causal suffix the state token sees only the prefix and
+    # itself, so it can be run alone and its per-layer K/V appended to the
+    # prefix: the action tokens of an expert without a state token then give
+    # the same velocity.  Without the mask they do not.
+    cfg = _tiny(state_causal=True, norm=norm, time_dim=16 if norm == "ada" else TINY.time_dim)
+    W64, kp, vp, x, s0 = _one_robot(cfg)
+    t = 0.37
+    vel = O.expert_velocity(cfg, W64, x, t, kp, vp, s0)
+    _, ks, vs = O.expert_velocity(cfg, W64, x[:0], t, kp, vp, s0, return_kv=True)  # the state token alone
+    assert ks.shape[1] == 1
+    kp2, vp2 = np.concatenate([kp, ks], axis=1), np.concatenate([vp, vs], axis=1)
+    vel2 = O.expert_velocity(cfg.replace(state_dim=0, state_causal=False), W64, x, t, kp2, vp2, None)
+    assert np.allclose(vel, vel2, rtol=1e-12, atol=1e-12)
+    full = O.expert_velocity(cfg.replace(state_causal=False), W64, x, t, kp, vp, s0)
+    assert O.rel_l2(full, vel2) > 1e-4
+
+
+def test_block_causal_state_kv_ignores_x_and_t():
+    cfg = _tiny(state_causal=True)
+    W64, kp, vp, x, s0 = _one_robot(cfg)
+    _, k1, v1 = O.expert_velocity(cfg, W64, x, 0.9, kp, vp, s0, return_kv=True)
+    _, k2, v2 = O.expert_velocity(cfg, W64, -3.0 * x, 0.1, kp, vp, s0, return_kv=True)
+    assert np.array_equal(k1[:, 0], k2[:, 0]) and np.array_equal(v1[:, 0], v2[:, 0])  # the state row
+    assert not np.allclose(k1[:, 1:], k2[:, 1:])                                      # action rows
 
 
 # --- P8: ring buffer in logical order ---------------------------------------------
