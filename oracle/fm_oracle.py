@@ -64,7 +64,7 @@ from scipy.special import erf as _erf
 __all__ = [
     "time_grid", "sinusoid", "linear", "rms_inv", "rmsnorm", "ada_rmsnorm",
     "silu", "gelu", "softmax_rows", "attention", "masked_attention",
-    "ada_modulation", "euler", "heun", "integrate", "expert_velocity", "denoise", "denoise_robot",
+    "ada_modulation", "euler", "heun", "ab2", "integrate", "expert_velocity", "denoise", "denoise_robot",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_e4m3_per_channel",
     "effective_weights", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
     "joint_velocity", "denoise_joint", "rel_l2", "max_abs",
@@ -358,9 +358,32 @@ def heun(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
     return x
 
 
+def ab2(velocity: Callable[[np.ndarray, float], np.ndarray], x0: np.ndarray,
+        n_steps: int, schedule: Optional[Sequence[float]] = None) -> np.ndarray:
+    """The two-step Adams-Bashforth method (a linear multistep sampler, one
+    evaluation per step) over the same schedule.  Step k integrates, over
+    [t_k, t_(k+1)], the line through the last two velocities (t_(k-1),
+    v_(k-1)) and (t_k, v_k): with h_k = dt_k and r = h_k / (2 h_(k-1)),
+    x_(k+1) = x_k + h_k ((1 + r) v_k - r v_(k-1)).  The first step, with one
+    velocity only, is an Euler step."""
+    ts, dts = time_grid(n_steps, schedule)
+    x = np.asarray(x0, F64).copy()
+    v_prev, h_prev = None, None
+    for t, h in zip(ts, dts):
+        v = velocity(x, float(t))
+        if v_prev is None:
+            x = x + h * v
+        else:
+            r = h / (2.0 * h_prev)
+            x = x + h * ((1.0 + r) * v - r * v_prev)
+        v_prev, h_prev = v, h
+    return x
+
+
 def integrate(cfg, velocity, x0) -> np.ndarray:
-    """The workload's sampler (cfg.sampler: "euler", the default, or "heun")."""
-    step = heun if getattr(cfg, "sampler", "euler") == "heun" else euler
+    """The workload's sampler (cfg.sampler: "euler", the default, "heun" or
+    "ab2")."""
+    step = {"euler": euler, "heun": heun, "ab2": ab2}[getattr(cfg, "sampler", "euler")]
     return step(velocity, x0, cfg.n_steps, getattr(cfg, "t_schedule", None))
 
 

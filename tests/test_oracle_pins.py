@@ -92,6 +92,36 @@ def test_heun_is_exact_for_a_velocity_linear_in_t():
         assert abs(got[0] - (-0.3 + 1.7 / 2)) < 1e-15
 
 
+def test_ab2_linear_in_t_field_errs_only_in_its_euler_start():
+    # v = a + b t: every two-step Adams-Bashforth step after the first
+    # integrates the line through its last two velocities, which is v itself,
+    # exactly; the first (Euler) step misses b h_0^2 / 2.  So x_N = x_0 + the
+    # integral of v from 1 to 0 (= -a - b/2) - b h_0^2 / 2, on uniform and
+    # non-uniform schedules (the latter test the ratio of step sizes; their
+    # times are exact in fp32, the precision the schedule is taken in).
+    a, b = 0.3, -1.7
+    for sched, n in ((None, 10), ([1.0, 0.75, 0.5, 0.0], 3), ([1.0, 0.875, 0.625, 0.5625, 0.1875, 0.0], 5), (None, 1)):
+        h0 = (sched[1] - sched[0]) if sched else -1.0 / n
+        got = O.ab2(lambda x, t: np.full_like(x, a + b * t), np.zeros(1), n, sched)
+        assert abs(got[0] - (-a - b / 2 - b * h0 ** 2 / 2)) < 1e-14, (sched, n)
+
+
+def test_ab2_is_second_order():
+    # v = lam x from x(1) = 1: the error at t = 0 falls 4x per halving of the
+    # step (a first-order slip, e.g. a wrong coefficient, gives 2x)
+    lam = 1.3
+    exact = np.exp(-lam)
+    errs = [abs(O.ab2(lambda x, t: lam * x, np.ones(1), n)[0] - exact) for n in (40, 80, 160)]
+    for e1, e2 in zip(errs, errs[1:]):
+        assert 3.6 < e1 / e2 < 4.4, errs
+
+
+def test_ab2_uses_one_evaluation_per_step_at_the_left_ends():
+    seen = []
+    O.ab2(lambda x, t: (seen.append(t), np.zeros_like(x))[1], np.zeros(1), 4)
+    assert seen == [1.0, 0.75, 0.5, 0.25]
+
+
 def test_heun_uses_the_right_end_times():
     seen = []
     O.heun(lambda x, t: (seen.append(t), np.zeros_like(x))[1], np.zeros(1), 4)
