@@ -258,7 +258,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi0_1view")
-    ap.add_argument("--sampler", choices=("euler", "heun"), default=None,
+    ap.add_argument("--sampler", choices=("euler", "heun", "ab2"), default=None,
                     help="override the workload's sampler (Heun: two velocity evaluations per step)")
     ap.add_argument("--n-steps", type=int, default=None, help="override the workload's step count")
     ap.add_argument("--exec-mode", type=int, default=0)

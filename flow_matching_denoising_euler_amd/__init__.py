@@ -51,7 +51,8 @@ def make_config(cfg, exec_mode: int = FM_EXEC_AUTO) -> fm_config:
     c.act_dtype = _DT[cfg.act_dtype]
     c.rms_eps = float(cfg.rms_eps)
     c.exec_mode = int(exec_mode)
-    c.sampler = _abi.FM_SAMPLER_HEUN if getattr(cfg, "sampler", "euler") == "heun" else _abi.FM_SAMPLER_EULER
+    c.sampler = {"euler": _abi.FM_SAMPLER_EULER, "heun": _abi.FM_SAMPLER_HEUN,
+                 "ab2": _abi.FM_SAMPLER_AB2}[getattr(cfg, "sampler", "euler")]
     c.state_causal = 1 if getattr(cfg, "state_causal", False) else 0
     sched = getattr(cfg, "t_schedule", None)
     if sched is not None:

@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_ARG", 2: "FM_ERR_SHAPE", 3: "FM_ERR_STATE
 FM_F32, FM_BF16, FM_FP8_E4M3 = 0, 1, 2
 FM_RMSNORM, FM_ADARMSNORM = 0, 1
 FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC_PERSISTENT = 0, 1, 2
-FM_SAMPLER_EULER, FM_SAMPLER_HEUN = 0, 1
+FM_SAMPLER_EULER, FM_SAMPLER_HEUN, FM_SAMPLER_AB2 = 0, 1, 2
 (FM_LW_WQ, FM_LW_WK, FM_LW_WV, FM_LW_WO, FM_LW_WG, FM_LW_WU, FM_LW_WD,
  FM_LW_NORM1, FM_LW_NORM1_B, FM_LW_NORM2, FM_LW_NORM2_B, FM_LW_COUNT) = range(12)
 

@@ -60,6 +60,8 @@ struct fm_ctx {
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
   int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
   bool heun;  // Heun sampler: two evaluations per step, time rows t_0..t_N
+  bool ab2;   // two-step Adams-Bashforth: v_(k-1) kept, ping-pong buffers
+  std::vector<float> ab_cur, ab_prev;  // its weights of v_k and v_(k-1) per step
   int NT;     // time rows of the t-dependent tables (N, or N + 1 for Heun)
   int ks_o, ks_d, nqblk, nsplit, kps;
   int NSP, TP, SP;  // static region padded to 32, padded physical prefix capacity, suffix padded to 32
@@ -73,7 +75,7 @@ struct fm_ctx {
   long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
   void *kpre, *vpre, *ksuf, *vsuf;
   int* meta;
-  float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *vbuf, *partials, *attn_part;
+  float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *vbuf, *vbuf2, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
   unsigned* counters;
   size_t n_counters;
@@ -147,7 +149,8 @@ fm_status validate_config(const fm_config* c) {
   if ((c->n_frames > 0) != (c->frame_tokens > 0))
     return fail(nullptr, FM_ERR_SHAPE, "n_frames and frame_tokens must both be zero or both positive");
   if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, FM_ERR_SHAPE, "n_q_heads %% n_kv_heads != 0");
-  if (c->sampler != FM_SAMPLER_EULER && c->sampler != FM_SAMPLER_HEUN) return fail(nullptr, FM_ERR_ARG, "bad sampler");
+  if (c->sampler != FM_SAMPLER_EULER && c->sampler != FM_SAMPLER_HEUN && c->sampler != FM_SAMPLER_AB2)
+    return fail(nullptr, FM_ERR_ARG, "bad sampler");
   if (c->state_causal != 0 && c->state_causal != 1) return fail(nullptr, FM_ERR_ARG, "state_causal must be 0 or 1");
   if (c->t_schedule) {
     // t_0 = 1 > t_1 > ... > t_N = 0, all finite
@@ -216,6 +219,7 @@ void derive(fm_ctx* x) {
   // step schedule: t_k = 1 - k/N and dt = -1/N, or the caller's times (dt_k
   // from the difference of two fp32 times, exact in double, rounded once)
   x->heun = c.sampler == FM_SAMPLER_HEUN;
+  x->ab2 = c.sampler == FM_SAMPLER_AB2;
   x->NT = x->N + (x->heun ? 1 : 0);
   x->tk.assign(x->NT, 0.0);  // t_N = 0 (the Heun corrector of the last step)
   x->dtk.assign(x->N, -1.f / (float)x->N);
@@ -226,6 +230,16 @@ void derive(fm_ctx* x) {
     } else {
       x->tk[k] = 1.0 - (double)k / (double)x->N;
     }
+  }
+  // Adams-Bashforth: with r = dt_k / (2 dt_(k-1)), x_(k+1) = x_k + dt_k ((1 + r) v_k - r v_(k-1)); the first
+  // step is Euler (weights 1, 0).  r from the fp32 times in double, rounded once.
+  x->ab_cur.assign(x->N, 1.f);
+  x->ab_prev.assign(x->N, 0.f);
+  for (int k = 1; k < x->N; ++k) {
+    auto tt = [&](int i) { return c.t_schedule ? (double)c.t_schedule[i] : 1.0 - (double)i / (double)x->N; };
+    const double r = (tt(k + 1) - tt(k)) / (2.0 * (tt(k) - tt(k - 1)));
+    x->ab_cur[k] = (float)(1.0 + r);
+    x->ab_prev[k] = (float)r;
   }
   x->Nqkv = (x->Hq + 2 * x->Hkv) * x->Dh;
   x->Tcap = c.prefix_static + c.n_frames * c.frame_tokens;
@@ -321,7 +335,8 @@ void carve(fm_ctx* x, Arena& a) {
   x->ssqf = (float*)a.take(Mp * x->P * 4);
   x->xbuf0 = (float*)a.take((long)x->B * x->C * x->A * 4);
   x->xbuf1 = (float*)a.take((long)x->B * x->C * x->A * 4);
-  x->vbuf = x->heun ? (float*)a.take((long)x->B * x->C * x->A * 4) : nullptr;
+  x->vbuf = x->heun || x->ab2 ? (float*)a.take((long)x->B * x->C * x->A * 4) : nullptr;
+  x->vbuf2 = x->ab2 ? (float*)a.take((long)x->B * x->C * x->A * 4) : nullptr;
   x->u = a.take(Mp * d * ea);
   x->uf = a.take(Mp * d * ea);
   x->qkv = a.take(Mp * x->Nqkv * ea);
@@ -434,7 +449,9 @@ fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
 
 // final norm + head + the update of step k (+ the next evaluation's
 // embedding).  stage 0: Euler; 1: Heun predictor (evaluation at t_k); 2: Heun
-// corrector (evaluation at t_(k+1)).
+// corrector (evaluation at t_(k+1)); 3: Adams-Bashforth (v_k kept in one of two
+// buffers, by step parity: the slices of a tail launch read v_(k-1) while one
+// of them writes v_k).
 fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_final) {
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
   OutArgs o{};
@@ -445,8 +462,10 @@ fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_fin
   o.dt = x->dtk[k];
   o.t_idx = stage == 2 ? k + 1 : k;
   o.heun = stage;
-  o.v_save = stage == 1 ? x->vbuf : nullptr;
-  o.v_prev = stage == 2 ? x->vbuf : nullptr;
+  o.v_save = stage == 1 ? x->vbuf : (stage == 3 ? ((k & 1) ? x->vbuf2 : x->vbuf) : nullptr);
+  o.v_prev = stage == 2 ? x->vbuf : (stage == 3 && k > 0 ? ((k & 1) ? x->vbuf : x->vbuf2) : nullptr);
+  o.c_cur = x->ab_cur[k];
+  o.c_prev = x->ab_prev[k];
   o.B = x->B; o.S = x->S; o.C = x->C; o.A = x->A; o.d = x->d; o.M = x->M; o.has_state = x->hasS;
   o.mtiles = x->mtiles; o.esplit = x->esplit;
   o.do_embed = stage == 1 || k + 1 < x->N;  // the corrector's evaluation follows a predictor
@@ -478,7 +497,7 @@ fm_status enqueue_graph_body(fm_ctx* x, hipStream_t cap) {
       if (cs == FM_OK) cs = enqueue_layers(x, k + 1, cap);  // the evaluation at t_(k+1)
       if (cs == FM_OK && k + 1 < x->N) cs = enqueue_tail(x, k, 2, cap, nullptr);
     } else if (cs == FM_OK && k + 1 < x->N) {
-      cs = enqueue_tail(x, k, 0, cap, nullptr);
+      cs = enqueue_tail(x, k, x->ab2 ? 3 : 0, cap, nullptr);
     }
   }
   return cs;
@@ -868,7 +887,7 @@ fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* ac
     if (!x->is_set[b]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", b);
   if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
   HIPCHK(x, hipGraphLaunch(x->gexec[0], x->stream), "graph launch");
-  return enqueue_tail(x, x->N - 1, x->heun ? 2 : 0, x->stream, actions);
+  return enqueue_tail(x, x->N - 1, x->heun ? 2 : (x->ab2 ? 3 : 0), x->stream, actions);
 }
 
 fm_status fm_encode_prefix(fm_ctx* x, const float* tokens, void* k_out, void* v_out) {
@@ -901,7 +920,8 @@ fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase)
   if (step < 0 || step >= x->N || phase < FM_PHASE_QKV || phase > FM_PHASE_TAIL ||
       (phase != FM_PHASE_TAIL && (layer < 0 || layer >= x->L)))
     return fail(x, FM_ERR_ARG, "step %d layer %d phase %d out of range", step, layer, phase);
-  if (phase == FM_PHASE_TAIL) return enqueue_tail(x, step, x->heun ? 2 : 0, x->stream, step + 1 < x->N ? nullptr : x->xbuf0);
+  if (phase == FM_PHASE_TAIL)
+    return enqueue_tail(x, step, x->heun ? 2 : (x->ab2 ? 3 : 0), x->stream, step + 1 < x->N ? nullptr : x->xbuf0);
   return enqueue_phase(x, step, layer, phase, x->stream);
 }
 

@@ -127,7 +127,9 @@ struct OutArgs {
   float dt;               // dt_k
   int t_idx;              // time row of this evaluation (bout table)
   int heun;               // 0 Euler; 1 Heun predictor: v -> v_save, embeds x_k + dt v;
-                          // 2 Heun corrector: x_(k+1) = x_k + dt (v_prev + v) / 2
+                          // 2 Heun corrector: x_(k+1) = x_k + dt (v_prev + v) / 2;
+                          // 3 two-step Adams-Bashforth: x_(k+1) = x_k + dt (c_cur v - c_prev v_prev)
+                          //   (v_prev null on the first step), v -> v_save
   float* v_save;          // [B*C][A]
   const float* v_prev;    // [B*C][A]
   int B, S, C, A, d, M, has_state, mtiles, esplit;
@@ -142,6 +144,7 @@ struct OutArgs {
   void* u;                // [M][d] act = act(h * g1)
   Tab g1;                 // layer-0 norm1 gain per step
   float* ssq_out;         // [M][P]
+  float c_cur, c_prev;    // heun == 3: the Adams-Bashforth weights of v_k and v_(k-1) (last: argument offsets)
 };
 
 struct EmbedArgs {

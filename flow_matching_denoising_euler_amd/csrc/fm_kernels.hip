@@ -1693,7 +1693,7 @@ __global__ __launch_bounds__(512) void k_out(OutArgs o) {
     const int ar = b * o.C + max(s - o.has_state, 0);
     xin[i] = o.x_in[(long)ar * o.A + min(a, o.A - 1)];
     bo[i] = o.bout.base[(long)o.t_idx * o.bout.step_stride + min(a, o.A - 1)];
-    vp[i] = o.heun == 2 ? o.v_prev[(long)ar * o.A + min(a, o.A - 1)] : 0.f;
+    vp[i] = o.v_prev ? o.v_prev[(long)ar * o.A + min(a, o.A - 1)] : 0.f;
   }
   EmbedCol<WE> ec;
   if (o.do_embed) ec.load(c0, o.A, o.w_in, o.b_in, o.temb, o.g1, o.embed_step, o.hs, m0, o.M, o.S, o.d);
@@ -1714,12 +1714,14 @@ __global__ __launch_bounds__(512) void k_out(OutArgs o) {
     if (act_row) {
       const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
       const float v = acc * s_rstd[lr] + bo[i];
-      xv = o.heun == 2 ? xin[i] + o.dt * (0.5f * (vp[i] + v)) : xin[i] + o.dt * v;
+      xv = o.heun == 2   ? xin[i] + o.dt * (0.5f * (vp[i] + v))
+           : o.heun == 3 ? xin[i] + o.dt * (o.c_cur * v - o.c_prev * vp[i])
+                         : xin[i] + o.dt * v;
       if (es == 0) {
         const int b = r / o.S, s = r % o.S;
         const long xo = (long)(b * o.C + s - o.has_state) * o.A + a;
-        if (o.heun == 1) o.v_save[xo] = v;
-        else o.x_out[xo] = xv;
+        if (o.heun == 1 || o.heun == 3) o.v_save[xo] = v;
+        if (o.heun != 1) o.x_out[xo] = xv;
       }
     }
     s_x[lr][a] = xv;

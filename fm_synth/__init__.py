@@ -62,7 +62,7 @@ class FMConfig:
     rms_eps: float = 1e-6
     ticks: int = 0          # streaming ticks (0: not a streaming workload)
     t_schedule: Optional[Tuple[float, ...]] = None  # n_steps + 1 times, 1 -> 0 (None: uniform)
-    sampler: str = "euler"  # "euler" or "heun"
+    sampler: str = "euler"  # "euler", "heun" or "ab2"
     state_causal: bool = False  # Pi0-style suffix: the state token sees only the prefix and itself
 
     @property

@@ -72,8 +72,12 @@ typedef enum { FM_RMSNORM = 0, FM_ADARMSNORM = 1 } fm_norm;
  * = x_k + dt_k v(x_k, t_k), one velocity evaluation per step.
  * FM_SAMPLER_HEUN (Heun's method, the explicit trapezoidal rule): v1 =
  * v(x_k, t_k), v2 = v(x_k + dt_k v1, t_(k+1)), x_(k+1) = x_k + dt_k (v1 +
- * v2) / 2, two evaluations per step (the last step evaluates at t = 0). */
-typedef enum { FM_SAMPLER_EULER = 0, FM_SAMPLER_HEUN = 1 } fm_sampler;
+ * v2) / 2, two evaluations per step (the last step evaluates at t = 0).
+ * FM_SAMPLER_AB2 (the two-step Adams-Bashforth method, a linear multistep
+ * sampler): one evaluation per step; step k integrates the line through
+ * (t_(k-1), v_(k-1)) and (t_k, v_k): with r = dt_k / (2 dt_(k-1)), x_(k+1) =
+ * x_k + dt_k ((1 + r) v_k - r v_(k-1)); the first step is an Euler step. */
+typedef enum { FM_SAMPLER_EULER = 0, FM_SAMPLER_HEUN = 1, FM_SAMPLER_AB2 = 2 } fm_sampler;
 
 /* How fm_denoise issues the loop.  FM_EXEC_AUTO and FM_EXEC_GRAPH run one
  * hipGraph of per-phase kernel launches.  FM_EXEC_PERSISTENT (one cooperative

@@ -69,7 +69,7 @@ def _create(c):
     (lambda c: (setattr(c, "n_frames", 2), setattr(c, "frame_tokens", 16)), _abi.FM_ERR_UNSUPPORTED),  # frames % 32
     (lambda c: setattr(c, "rms_eps", float("nan")), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "exec_mode", 9), _abi.FM_ERR_ARG),
-    (lambda c: setattr(c, "sampler", 2), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "sampler", 3), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "state_causal", 2), _abi.FM_ERR_ARG),
     (lambda c: _set_schedule(c, [1.0, 0.5, 0.25, 0.5] + [0.1] * 6 + [0.0]), _abi.FM_ERR_ARG),  # not decreasing
     (lambda c: _set_schedule(c, [0.9] + [0.8 - 0.08 * k for k in range(9)] + [0.0]), _abi.FM_ERR_ARG),  # t_0 != 1

@@ -251,6 +251,37 @@ def test_full_pi0_1view_heun():
     check("pi0_1view heun 5 steps", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(norm="ada", time_dim=32, state_dim=0),
+                                dict(t_schedule=shifted_schedule(8)),
+                                dict(batch=10, chunk=40, prefix_static=64, prefix_len=64)])  # last: large-M GEMMs
+def test_small_ab2(kw):
+    cfg = small_cfg(n_steps=8, sampler="ab2", **kw)
+    announce(f"small ab2 {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check(f"small ab2 {kw}", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+    eul = run_denoiser(cfg.replace(sampler="euler"), W, k, v, x0, st)[0]
+    assert not np.allclose(got, eul, rtol=1e-3, atol=1e-3)  # the sampler is used
+
+
+def test_ab2_single_step_is_the_euler_step_bitwise():
+    # its first step has weights (1, 0) and no previous velocity
+    cfg = small_cfg(n_steps=1, sampler="ab2")
+    announce("ab2 one step == euler")
+    W, k, v, x0, st = _inputs(cfg)
+    a = run_denoiser(cfg, W, k, v, x0, st)[0]
+    b = run_denoiser(cfg.replace(sampler="euler"), W, k, v, x0, st)[0]
+    assert np.array_equal(a, b)
+
+
+def test_full_pi0_1view_ab2():
+    cfg = S.workload("pi0_1view").replace(sampler="ab2")
+    announce("pi0_1view ab2 10 steps")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("pi0_1view ab2 10 steps", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
 def test_full_pi0_1view_shifted_schedule():
     cfg = S.workload("pi0_1view").replace(t_schedule=shifted_schedule(10))
     announce("pi0_1view shifted schedule: generating")
