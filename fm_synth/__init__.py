@@ -64,6 +64,7 @@ class FMConfig:
     t_schedule: Optional[Tuple[float, ...]] = None  # n_steps + 1 times, 1 -> 0 (None: uniform)
     sampler: str = "euler"  # "euler", "heun" or "ab2"
     state_causal: bool = False  # Pi0-style suffix: the state token sees only the prefix and itself
+    kv_fp8: bool = False        # prefix K/V cached as fp8 E4M3 with a scale per (token, kv head)
 
     @property
     def has_state(self) -> int:

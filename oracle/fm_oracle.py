@@ -66,7 +66,7 @@ __all__ = [
     "silu", "gelu", "softmax_rows", "attention", "masked_attention",
     "ada_modulation", "euler", "heun", "ab2", "integrate", "expert_velocity", "denoise", "denoise_robot",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_e4m3_per_channel",
-    "effective_weights", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
+    "effective_weights", "prefix_kv_e4m3", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
     "joint_velocity", "denoise_joint", "rel_l2", "max_abs",
 ]
 
@@ -237,6 +237,16 @@ def quantize_e4m3_per_channel(w) -> Tuple[np.ndarray, np.ndarray]:
     return e4m3_encode(q), s
 
 
+def prefix_kv_e4m3(kv) -> np.ndarray:
+    """An fp8 prefix cache as the loop reads it: every (token, kv head) row
+    of K or V [..][Dh] quantised like a weight row (scale = row max / 448 in
+    float32, E4M3 codes of the float32 quotient), returned dequantised in
+    float64 (code * scale).  The suffix K/V of each step stay unquantised."""
+    kv = np.asarray(kv, np.float32)
+    codes, s = quantize_e4m3_per_channel(kv.reshape(-1, kv.shape[-1]))
+    return (e4m3_decode(codes) * s.astype(F64)[:, None]).reshape(kv.shape)
+
+
 def effective_weights(cfg, W: dict) -> dict:
     """Weights as the loop uses them, in float64.  For an fp8 workload the
     seven per-layer matrices are replaced by their dequantised fp8 values
@@ -399,6 +409,8 @@ def denoise(cfg, W: dict, k_pre, v_pre, noise, state=None,
     subset (the result then has len(robots) rows)."""
     W64 = effective_weights(cfg, W)
     idx = range(noise.shape[0]) if robots is None else robots
+    if getattr(cfg, "kv_fp8", False):  # the prefix cache held in fp8
+        k_pre, v_pre = [prefix_kv_e4m3(k) for k in k_pre], [prefix_kv_e4m3(v) for v in v_pre]
     return np.stack([denoise_robot(cfg, W64, k_pre[b], v_pre[b], noise[b],
                                    None if state is None else state[b]) for b in idx])
 

@@ -493,6 +493,35 @@ def test_e4m3_per_channel_quantisation_error_bound():
     assert np.all(np.max(np.abs(O.e4m3_decode(codes[[0, 1, 2]])), axis=1) == 448.0)
 
 
+def test_fp8_prefix_cache_rows():
+    # each (token, kv head) row of a [layers][T][Hkv][Dh] cache has its own
+    # scale: a row of E4M3 values with max |x| = 448 is kept exactly, and any
+    # row scaled by a power of two comes back scaled by the same power
+    g = np.random.default_rng(13)
+    vals = O.e4m3_values()
+    ok = np.isfinite(vals) & (np.abs(vals) <= 448)
+    rows = g.choice(vals[ok], size=(2, 5, 3, 32)).astype(np.float32)
+    rows[..., 0] = 448.0
+    assert np.array_equal(O.prefix_kv_e4m3(rows), rows)
+    scaled = rows * np.float32(2.0) ** g.integers(-6, 6, size=(2, 5, 3, 1)).astype(np.float32)
+    assert np.array_equal(O.prefix_kv_e4m3(scaled), scaled)
+    # a generic cache: every element within half an E4M3 step of its row's grid
+    x = (g.standard_normal((2, 7, 1, 64)) * np.exp(g.standard_normal((2, 7, 1, 1)))).astype(np.float32)
+    deq = O.prefix_kv_e4m3(x)
+    amax = np.max(np.abs(x), axis=-1, keepdims=True).astype(np.float64)
+    assert np.all(np.abs(deq - x) <= amax / 448 * 2.0 ** -4 * np.maximum(np.abs(x) / amax * 448, 2.0 ** -6) * 1.01 + 1e-30)
+
+
+def test_fp8_prefix_cache_changes_the_loop_only_through_the_prefix():
+    cfg = _tiny(act_dtype="bf16", weight_dtype="bf16")
+    W, k, v, x0, st = _inputs(cfg)
+    a = O.denoise(cfg.replace(kv_fp8=True), W, k, v, x0, st)
+    b = O.denoise(cfg, W, O.prefix_kv_e4m3(k), O.prefix_kv_e4m3(v), x0, st)
+    assert np.array_equal(a, b)
+    c = O.denoise(cfg, W, k, v, x0, st)
+    assert 1e-5 < O.rel_l2(a, c) < 5e-2
+
+
 def test_fp8_workload_uses_dequantised_matrices_only():
     cfg = _tiny(weight_dtype="fp8", act_dtype="bf16")
     W = S.make_weights(cfg)
