@@ -261,6 +261,7 @@ def main():
     ap.add_argument("--sampler", choices=("euler", "heun", "ab2"), default=None,
                     help="override the workload's sampler (Heun: two velocity evaluations per step)")
     ap.add_argument("--n-steps", type=int, default=None, help="override the workload's step count")
+    ap.add_argument("--kv-fp8", action="store_true", help="hold the prefix K/V cache in fp8 E4M3 (per token and kv head scales)")
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
@@ -295,6 +296,8 @@ def main():
         cfg = cfg.replace(sampler=args.sampler)
     if args.n_steps is not None:
         cfg = cfg.replace(n_steps=args.n_steps)
+    if args.kv_fp8:
+        cfg = cfg.replace(kv_fp8=True)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     log(f"bench: generating {cfg.name}")
@@ -407,6 +410,7 @@ def main():
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) prefix K/V and noise)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "chunk": cfg.chunk, "state_tokens": cfg.has_state,
                    "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps, "sampler": cfg.sampler,
+                   "kv_cache": "fp8-e4m3" if cfg.kv_fp8 else cfg.act_dtype,
                    "d_model": cfg.d_model,
                    "layers": cfg.n_layers, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),

@@ -74,6 +74,8 @@ struct fm_ctx {
   float *temb, *g1, *g2, *gf, *a1, *a2, *bqkv, *bgu, *bout, *ones, *zeros;
   long st_g, st_gf, st_bqkv, st_bgu, st_bout;  // per-step strides (0: constant)
   void *kpre, *vpre, *ksuf, *vsuf;
+  bool kv8;               // prefix cache in E4M3 with per (token, kv head) scales
+  float *kscale, *vscale; // [B][L][TP][Hkv] when kv8
   int* meta;
   float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *vbuf, *vbuf2, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
@@ -152,6 +154,7 @@ fm_status validate_config(const fm_config* c) {
   if (c->sampler != FM_SAMPLER_EULER && c->sampler != FM_SAMPLER_HEUN && c->sampler != FM_SAMPLER_AB2)
     return fail(nullptr, FM_ERR_ARG, "bad sampler");
   if (c->state_causal != 0 && c->state_causal != 1) return fail(nullptr, FM_ERR_ARG, "state_causal must be 0 or 1");
+  if (c->kv_fp8 != 0 && c->kv_fp8 != 1) return fail(nullptr, FM_ERR_ARG, "kv_fp8 must be 0 or 1");
   if (c->t_schedule) {
     // t_0 = 1 > t_1 > ... > t_N = 0, all finite
     const float* t = c->t_schedule;
@@ -176,6 +179,12 @@ fm_status validate_config(const fm_config* c) {
   if (c->weight_dtype == FM_FP8_E4M3 &&
       (c->d_model % 64 || (c->n_q_heads * c->head_dim) % 64 || c->d_mlp % 64))
     return fail(nullptr, FM_ERR_UNSUPPORTED, "fp8 weights need reduction sizes that are multiples of 64");
+  if (c->kv_fp8) {
+    // the register attention kernel reads the fp8 cache (up to 1024 padded keys)
+    const long keys = ((long)c->prefix_static + 31) / 32 * 32 + (long)c->n_frames * c->frame_tokens + (S + 31) / 32 * 32;
+    if (f32) return fail(nullptr, FM_ERR_UNSUPPORTED, "kv_fp8 needs bf16 activations");
+    if (keys > 1024) return fail(nullptr, FM_ERR_UNSUPPORTED, "kv_fp8: %ld padded keys, at most 1024", keys);
+  }
   if (f32) {
     if (c->head_dim > 64 || S > 256) return fail(nullptr, FM_ERR_UNSUPPORTED, "fp32 path: head_dim <= 64, suffix <= 256");
   } else if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) {
@@ -219,6 +228,7 @@ void derive(fm_ctx* x) {
   // step schedule: t_k = 1 - k/N and dt = -1/N, or the caller's times (dt_k
   // from the difference of two fp32 times, exact in double, rounded once)
   x->heun = c.sampler == FM_SAMPLER_HEUN;
+  x->kv8 = c.kv_fp8 != 0;
   x->ab2 = c.sampler == FM_SAMPLER_AB2;
   x->NT = x->N + (x->heun ? 1 : 0);
   x->tk.assign(x->NT, 0.0);  // t_N = 0 (the Heun corrector of the last step)
@@ -322,9 +332,12 @@ void carve(fm_ctx* x, Arena& a) {
   x->st_bqkv = L * x->Nqkv;
   x->st_bgu = L * 2 * x->F;
   x->st_bout = ada ? x->A : 0;
-  const size_t kv = (size_t)x->B * L * x->TP * x->HD * ea;
+  const size_t kv = (size_t)x->B * L * x->TP * x->HD * (x->kv8 ? 1 : ea);
   x->kpre = a.take(kv > 0 ? kv : 16);
   x->vpre = a.take(kv > 0 ? kv : 16);
+  const size_t nsc = x->kv8 && x->TP > 0 ? (size_t)x->B * L * x->TP * x->Hkv : 4;
+  x->kscale = (float*)a.take(nsc * 4);
+  x->vscale = (float*)a.take(nsc * 4);
   x->ksuf = a.take((size_t)x->B * x->HD * x->SP * ea);
   x->vsuf = a.take((size_t)x->B * x->HD * x->SP * ea);
   x->meta = (int*)a.take(x->B * 2 * sizeof(int));
@@ -385,8 +398,14 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     AttnArgs at{};
     at.qkv = x->qkv;
-    at.kpre = (const char*)x->kpre + (size_t)l * Tl * elt_size(x->act);
-    at.vpre = (const char*)x->vpre + (size_t)l * Tl * elt_size(x->act);
+    const size_t ekv = x->kv8 ? 1 : elt_size(x->act);
+    at.kpre = (const char*)x->kpre + (size_t)l * Tl * ekv;
+    at.vpre = (const char*)x->vpre + (size_t)l * Tl * ekv;
+    if (x->kv8) {
+      at.kscale = x->kscale + (size_t)l * x->TP * x->Hkv;
+      at.vscale = x->vscale + (size_t)l * x->TP * x->Hkv;
+      at.sc_bstride = (long)x->L * x->TP * x->Hkv;
+    }
     at.ksuf = x->ksuf;
     at.vsuf = x->vsuf;
     at.b_stride = (long)x->L * Tl;
@@ -780,6 +799,8 @@ fm_status fm_encoder_create(const fm_config* cfg, const fm_weights* w, void* hip
   c.n_frames = 0;
   c.sampler = FM_SAMPLER_EULER;
   c.t_schedule = nullptr;
+  c.state_causal = 0;
+  c.kv_fp8 = 0;
   fm_status s = validate_config(&c);
   if (s != FM_OK) return s;
   if (c.act_dtype == FM_BF16 && c.chunk > 1024)
@@ -802,11 +823,13 @@ fm_status fm_set_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* 
                 ring ? x->Tcap : x->cfg.prefix_static);
   if (n_tokens > 0 && (!k || !v)) return fail(x, FM_ERR_ARG, "k or v is NULL");
   if (((uintptr_t)k | (uintptr_t)v) % 16) return fail(x, FM_ERR_ARG, "k and v must be 16-byte aligned");
-  const size_t ea = elt_size(x->act);
-  const size_t rb = (size_t)robot * x->L * x->TP * x->HD * ea;
+  const size_t rb = (size_t)robot * x->L * x->TP * x->HD * (x->kv8 ? 1 : elt_size(x->act));
   KvCopy c{};
   c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vd = (char*)x->vpre + rb;
   c.elt = x->act; c.layers = x->L; c.n = n_tokens; c.HD = x->HD; c.Dh = x->Dh; c.TP = x->TP;
+  c.fp8 = x->kv8;
+  c.ksd = x->kscale + (size_t)robot * x->L * x->TP * x->Hkv;
+  c.vsd = x->vscale + (size_t)robot * x->L * x->TP * x->Hkv;
   c.phys0 = 0; c.split_t = ring ? x->cfg.prefix_static : n_tokens; c.phys1 = x->NSP;
   c.meta = x->meta; c.robot = robot; c.valid = n_tokens; c.head = 0;
   HIPCHK(x, launch_kv_copy(c, x->stream), "prefix copy");
@@ -831,11 +854,13 @@ fm_status check_append(fm_ctx* x, int32_t robot) {
 fm_status enqueue_append(fm_ctx* x, int32_t robot, const void* k, const void* v) {
   const int slot = x->head[robot];
   const int nh = (slot + 1) % x->cfg.n_frames;
-  const size_t ea = elt_size(x->act);
-  const size_t rb = (size_t)robot * x->L * x->TP * x->HD * ea;
+  const size_t rb = (size_t)robot * x->L * x->TP * x->HD * (x->kv8 ? 1 : elt_size(x->act));
   KvCopy c{};
   c.k = k; c.v = v; c.kd = (char*)x->kpre + rb; c.vd = (char*)x->vpre + rb;
   c.elt = x->act; c.layers = x->L; c.n = x->cfg.frame_tokens; c.HD = x->HD; c.Dh = x->Dh; c.TP = x->TP;
+  c.fp8 = x->kv8;
+  c.ksd = x->kscale + (size_t)robot * x->L * x->TP * x->Hkv;
+  c.vsd = x->vscale + (size_t)robot * x->L * x->TP * x->Hkv;
   c.phys0 = x->NSP + slot * x->cfg.frame_tokens; c.split_t = c.n; c.phys1 = 0;
   c.meta = x->meta; c.robot = robot; c.valid = x->valid[robot]; c.head = nh;
   HIPCHK(x, launch_kv_copy(c, x->stream), "frame append");
@@ -941,7 +966,7 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
     info->weight_bytes_per_step = x->L * ((wqkv + wrest) * ew + (sqkv + srest) * 4) + (size_t)(2 * x->A * x->d + x->d) * eg;
     size_t kv = 0;
     for (int b = 0; b < x->B; ++b) kv += (size_t)x->valid[b];
-    info->kv_bytes_per_step = kv * x->L * x->HD * ea * 2;
+    info->kv_bytes_per_step = kv * x->L * (x->kv8 ? x->HD + 4 * x->Hkv : x->HD * ea) * 2;
     info->n_phases = (x->heun ? 2 : 1) * x->N * (5 * x->L + 1) + 1;
   }
   {

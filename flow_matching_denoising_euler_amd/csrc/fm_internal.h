@@ -112,6 +112,11 @@ struct AttnArgs {
   // block-causal suffix: the state row (suffix row 0, the first Hq/Hkv query
   // rows of a kv group) sees no suffix key past itself
   int state_causal;
+  // fp8 prefix cache: per (physical position, kv head) scales of K and V,
+  // layer-l bases, robots sc_bstride floats apart (null: act-dtype cache)
+  const float* kscale;
+  const float* vscale;
+  long sc_bstride;
 };
 
 struct OutArgs {
@@ -227,6 +232,9 @@ struct KvCopy {
   int phys0, split_t, phys1;
   int* meta;
   int robot, valid, head;
+  int fp8;                // the cache in E4M3 with a scale per (token, kv head):
+  float* ksd;             //   robot base of the K / V scales, [layers][TP][Hkv]
+  float* vsd;
 };
 hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st);
 

@@ -104,6 +104,16 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
   const uint32_t sub = s | f2bf((float)m * (1.f / 512.f));
   return e ? normal : sub;
 }
+// the same with the gfx950 conversion instruction (v_cvt_scalef32_pk_bf16_fp8,
+// OCP E4M3, two codes a call; scale 1: every E4M3 value is a bf16 value, the
+// result is exact)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8_hw(uint32_t lo, uint32_t hi) {
+  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+}
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   uint4 r;
   r.x = e4m3_to_bf16(lo & 0xFF) | (e4m3_to_bf16((lo >> 8) & 0xFF) << 16);
@@ -996,6 +1006,15 @@ struct KeySpace {
     const uint16_t* base = p < TP ? (const uint16_t*)vpre : (const uint16_t*)vsuf;
     return base + (p < TP ? pre : suf);
   }
+  // fp8 cache: the same tiles of the prefix with one byte per element (8 bytes a lane)
+  __device__ __forceinline__ const uint8_t* ktile8(int j, int kb16, int kb, int lane) const {
+    const int p = kb16 * 16, KBD = Dh >> 5;
+    return (const uint8_t*)kpre + boff + ((((long)j * (TP >> 4) + (phys(p) >> 4)) * KBD + kb) * 64 + lane) * 8;
+  }
+  __device__ __forceinline__ const uint8_t* vtile8(int j, int kb32, int nbd, int lane) const {
+    const int p = kb32 * 32, NBD = Dh >> 4;
+    return (const uint8_t*)vpre + boff + ((((long)j * (TP >> 5) + (phys(p) >> 5)) * NBD + nbd) * 64 + lane) * 8;
+  }
   // fp32 kv layout: K element (p, c) and V element (p, c)
   __device__ __forceinline__ float kel(int j, int p, int c) const {
     return p < TP ? ((const float*)kpre)[boff + kv_k_off(false, TP, Hkv, Dh, j, phys(p), c)]
@@ -1208,7 +1227,7 @@ __device__ __forceinline__ void attn_weight_prefetch(const AttnArgs& a) {
   asm volatile("" ::"v"(acc));  // the loaded values are used: the loads stay
 }
 
-template <int DH, int R, int QB, int DS, bool PF, bool CAUSAL>
+template <int DH, int R, int QB, int DS, bool PF, bool CAUSAL, bool KV8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
   // weight prefetch workgroups (a separate instantiation: the test needs a
   // kernel argument before the first load)
@@ -1267,21 +1286,53 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kend = min((kb0 + a.keys_per_split) * 16, ks.kp);
 
   // ---- 1. scores of this wave's key blocks
+  // KV8: prefix blocks hold E4M3 codes (8 bytes a lane, in .x/.y until used),
+  // converted exactly to bf16 at the MFMA; their scales multiply the scores
+  // (K) and the probabilities (V) per key
   uint4 kf[KQ][KBD];
+  auto pre16 = [&](int i) { return KV8 && min(kb0 + w + 8 * i, nk16 - 1) * 16 < ks.TP; };
   auto load_k = [&](int i, int slot) {
     const int nb = min(kb0 + w + 8 * i, nk16 - 1);
+    if (pre16(i)) {
 #pragma unroll
-    for (int kb = 0; kb < KBD; ++kb) kf[slot][kb] = *(const uint4*)ks.ktile(j, nb, kb, lane);
+      for (int kb = 0; kb < KBD; ++kb) {
+        const uint2 r = *(const uint2*)ks.ktile8(j, nb, kb, lane);
+        kf[slot][kb] = uint4{r.x, r.y, 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KBD; ++kb) kf[slot][kb] = *(const uint4*)ks.ktile(j, nb, kb, lane);
+    }
   };
+  float ksc[KV8 ? R : 1], vsc[KV8 ? R : 1];  // this lane's key's scales, per block
+  if constexpr (KV8) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int key = (kb0 + w + 8 * i) * 16 + (lane & 15);
+      const long si = (long)b * a.sc_bstride + (long)ks.phys(max(0, min(key, ks.TP - 1))) * a.Hkv + j;
+      const bool pre = key < ks.TP;
+      ksc[i] = pre ? a.kscale[si] : 1.f;
+      vsc[i] = pre ? a.vscale[si] : 1.f;
+    }
+  }
   // phase 3's first V fragments go out with the first K fragments, before
   // any wait; the scheduling barriers keep the compiler from sinking loads
   // towards their uses (which would serialise the round trips)
   const int kg = w / (8 / KG), nbd0 = ds * NBD3 + (w % (8 / KG)) * NBW;
   uint4 vf[VQ][NBW];
+  auto pre32 = [&](int i) { return KV8 && min((kb0 >> 1) + kg + KG * i, nk32 - 1) * 32 < ks.TP; };
   auto load_v = [&](int i, int slot) {
     const int kb32 = min((kb0 >> 1) + kg + KG * i, nk32 - 1);
+    if (pre32(i)) {
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) vf[slot][n] = *(const uint4*)ks.vtile(j, kb32, nbd0 + n, lane);
+      for (int n = 0; n < NBW; ++n) {
+        const uint2 r = *(const uint2*)ks.vtile8(j, kb32, nbd0 + n, lane);
+        vf[slot][n] = uint4{r.x, r.y, 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) vf[slot][n] = *(const uint4*)ks.vtile(j, kb32, nbd0 + n, lane);
+    }
   };
 #pragma unroll
   for (int i = 0; i < KQ; ++i) load_k(i, i);
@@ -1291,6 +1342,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x4 sc[R][QB];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
+    if (pre16(i)) {  // KV8: the block's codes to bf16 in place, once for all query blocks
+#pragma unroll
+      for (int kb = 0; kb < KBD; ++kb) kf[i % KQ][kb] = e4m3x8_to_bf16x8_hw(kf[i % KQ][kb].x, kf[i % KQ][kb].y);
+    }
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1321,7 +1376,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool okr = ok && !(CAUSAL && key > ks.TP && (qb * QB + u) * 16 + (lane >> 4) * 4 + r < G);
-        sc[i][u][r] = okr ? sc[i][u][r] * a.scale : -INFINITY;
+        const float s0 = KV8 ? sc[i][u][r] * ksc[KV8 ? i : 0] : sc[i][u][r];
+        sc[i][u][r] = okr ? s0 * a.scale : -INFINITY;
         mx[u][r] = fmaxf(mx[u][r], sc[i][u][r]);
       }
   }
@@ -1355,7 +1411,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 4; ++r) {
         const float p = (mx[u][r] == -INFINITY) ? 0.f : __expf(sc[i][u][r] - mx[u][r]);
         sm[u][r] += p;
-        sP[u * 16 + (lane >> 4) * 4 + r][key] = (uint16_t)f2bf(p);
+        sP[u * 16 + (lane >> 4) * 4 + r][key] = (uint16_t)f2bf(KV8 ? p * vsc[KV8 ? i : 0] : p);
       }
   }
 #pragma unroll
@@ -1376,6 +1432,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int n = 0; n < NBW; ++n) oacc[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
+    if (pre32(i)) {  // KV8: the block's codes to bf16 in place
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) vf[i % VQ][n] = e4m3x8_to_bf16x8_hw(vf[i % VQ][n].x, vf[i % VQ][n].y);
+    }
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       const uint4 pf = *(const uint4*)&sP[u * 16 + (lane & 15)][(kg + KG * i) * 32 + (lane >> 4) * 8];
@@ -1912,6 +1972,43 @@ __global__ void k_kv_copy(KvCopy c) {
   }
 }
 
+// The fp8 prefix cache: one wave per (layer, token, kv head) row of K and of
+// V: the row's max |x| gives the scale (max / 448), the codes are those of
+// the fp32 quotients (the weights' rule, f32_to_e4m3), written to the same
+// physical positions of the kv layout as the act-dtype copy above, one byte
+// per element; the scales go to [layer][position][kv head].
+__global__ void k_kv_copy8(KvCopy c) {
+  const int HD = c.HD, Dh = c.Dh, Hkv = HD / Dh;
+  const int lane = threadIdx.x & 63;
+  const long rows = (long)c.layers * c.n * Hkv;
+  const long wstride = (long)gridDim.x * (blockDim.x >> 6);
+  for (long rw = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6); rw < rows; rw += wstride) {
+    const long l = rw / ((long)c.n * Hkv);
+    const int t = (int)((rw / Hkv) % c.n), j = (int)(rw % Hkv);
+    const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
+    const long src = (l * c.n + t) * HD + (long)j * Dh;
+    uint8_t* kd = (uint8_t*)c.kd + l * (long)c.TP * HD;
+    uint8_t* vd = (uint8_t*)c.vd + l * (long)c.TP * HD;
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* x = (const uint16_t*)(kv ? c.v : c.k) + src;
+      float amax = 0.f;
+      for (int e = lane; e < Dh; e += 64) amax = fmaxf(amax, fabsf(bf2f(x[e])));
+      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+      for (int e = lane; e < Dh; e += 64) {
+        const uint8_t code = (uint8_t)f32_to_e4m3(__fdiv_rn(bf2f(x[e]), sc));
+        if (kv) vd[kv_v_off(true, c.TP, Hkv, Dh, j, phys, e)] = code;
+        else kd[kv_k_off(true, c.TP, Hkv, Dh, j, phys, e)] = code;
+      }
+      if (lane == 0) (kv ? c.vsd : c.ksd)[(l * c.TP + phys) * Hkv + j] = sc;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    c.meta[2 * c.robot] = c.valid;
+    c.meta[2 * c.robot + 1] = c.head;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prefix encoder.  The prefix K/V that the loop reads is produced before the
 // loop by the vision/language stack (realtime-vla write-up, "The problem is a
@@ -2024,17 +2121,17 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-template <int DH, int QB, int DS, bool PF, bool CAUSAL = false>
+template <int DH, int QB, int DS, bool PF, bool CAUSAL = false, bool KV8 = false>
 static hipError_t attn_sf_r(const AttnArgs& a, int grid, hipStream_t st) {
   switch ((a.keys_per_split + 7) / 8) {  // R: 16-key blocks per wave
-    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS, PF, CAUSAL>), grid, 512, a);
-    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS, PF, CAUSAL>), grid, 512, a);
+    case 1: FM_LAUNCH_N((k_attn_sf<DH, 1, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 2: FM_LAUNCH_N((k_attn_sf<DH, 2, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 3: FM_LAUNCH_N((k_attn_sf<DH, 3, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 4: FM_LAUNCH_N((k_attn_sf<DH, 4, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 5: FM_LAUNCH_N((k_attn_sf<DH, 5, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 6: FM_LAUNCH_N((k_attn_sf<DH, 6, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 7: FM_LAUNCH_N((k_attn_sf<DH, 7, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
+    case 8: FM_LAUNCH_N((k_attn_sf<DH, 8, QB, DS, PF, CAUSAL, KV8>), grid, 512, a);
   }
   return hipErrorInvalidValue;
 }
@@ -2048,6 +2145,12 @@ static hipError_t attn_sf(AttnArgs a, hipStream_t st) {
   // weight prefetchers on the idle CUs, if at least half of them are idle
   // (fewer would stretch the attention launch by more than they save)
   const int idle = a.pf_cus - a.grid;
+  if (a.kscale) {  // the fp8 prefix cache
+    if (a.state_causal) return attn_sf_r<DH, QB, DS, false, true, true>(a, a.grid, st);
+    if constexpr (DS >= 2)
+      if ((a.pf_w[0] || a.pf_w[1]) && 2 * idle >= a.pf_cus) return attn_sf_r<DH, QB, DS, true, false, true>(a, a.grid + idle, st);
+    return attn_sf_r<DH, QB, DS, false, false, true>(a, a.grid, st);
+  }
   if (a.state_causal) return attn_sf_r<DH, QB, DS, false, true>(a, a.grid, st);  // (no weight prefetch)
   if constexpr (DS >= 2)
     if ((a.pf_w[0] || a.pf_w[1]) && 2 * idle >= a.pf_cus) return attn_sf_r<DH, QB, DS, true>(a, a.grid + idle, st);
@@ -2071,6 +2174,7 @@ static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
     }
     return attn_sf<DH, 1, 1>(a, st);
   }
+  if (a.kscale) return hipErrorInvalidValue;  // the fp8 cache is read by the register kernel only
   if (a.state_causal) hipLaunchKernelGGL((k_attn_flash<DH, true>), dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((k_attn_flash<DH, false>), dim3(a.B * a.Hkv * a.nqblk), dim3(256), 0, st, a);
   return hipGetLastError();
@@ -2151,6 +2255,11 @@ hipError_t launch_bias_gemv(const void* w, int w_elt, const float* scales, int r
 }
 
 hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st) {
+  if (c.fp8) {
+    const long rows = (long)c.layers * c.n * (c.HD / c.Dh);
+    hipLaunchKernelGGL(k_kv_copy8, dim3((int)std::max(1L, std::min(2048L, (rows + 3) / 4))), dim3(256), 0, st, c);
+    return hipGetLastError();
+  }
   const long work = (long)c.layers * c.n * c.HD;
   const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
   if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_copy<float>, dim3(grid), dim3(256), 0, st, c);

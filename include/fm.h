@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 3
+#define FM_ABI_VERSION 4
 
 typedef struct fm_ctx fm_ctx;
 
@@ -130,6 +130,14 @@ typedef enum {
  *   block-causal suffix of Pi0-style experts: the state token's values then
  *   do not depend on x or t).  The pages fix no suffix mask; 0 is the
  *   default reading and 1 the Pi0-style variant.
+ *
+ * kv_fp8: 0 = the prefix K/V cache in act_dtype; 1 = in OCP E4M3FN, every
+ *   (token, kv head) row with its own fp32 scale (row max / 448, codes of
+ *   the fp32 quotient, as the weights of fm_quantize_e4m3), quantised by
+ *   fm_set_prefix_kv / fm_append_prefix_kv from act_dtype inputs; half the
+ *   cache bytes.  The suffix K/V of each step stay in act_dtype.  bf16
+ *   activations and at most 1024 padded keys (prefix capacity rounded up to
+ *   32 plus the suffix rounded up to 32), else FM_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t abi_version;               /* FM_ABI_VERSION */
@@ -145,6 +153,7 @@ typedef struct {
   int32_t exec_mode;                 /* fm_exec  */
   int32_t sampler;                   /* fm_sampler */
   int32_t state_causal;              /* 0 or 1, see above */
+  int32_t kv_fp8;                    /* 0 or 1, see above */
   const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
 } fm_config;
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(_abi.fm_config) == 24 * 4 + 8  # 23 scalars, padding, the t_schedule pointer
+    assert ctypes.sizeof(_abi.fm_config) == 24 * 4 + 8  # 24 scalars, the t_schedule pointer
     assert ctypes.sizeof(_abi.fm_weights) == 11 * 8
     assert ctypes.sizeof(_abi.fm_info) == 3 * 8 + 4 * 4
 
@@ -71,6 +71,10 @@ def _create(c):
     (lambda c: setattr(c, "exec_mode", 9), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "sampler", 3), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "state_causal", 2), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "kv_fp8", 2), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "kv_fp8", 1), _abi.FM_ERR_UNSUPPORTED),   # fp32 activations
+    (lambda c: (setattr(c, "kv_fp8", 1), setattr(c, "act_dtype", _abi.FM_BF16), setattr(c, "weight_dtype", _abi.FM_BF16),
+                setattr(c, "prefix_static", 1100)), _abi.FM_ERR_UNSUPPORTED),  # > 1024 padded keys
     (lambda c: _set_schedule(c, [1.0, 0.5, 0.25, 0.5] + [0.1] * 6 + [0.0]), _abi.FM_ERR_ARG),  # not decreasing
     (lambda c: _set_schedule(c, [0.9] + [0.8 - 0.08 * k for k in range(9)] + [0.0]), _abi.FM_ERR_ARG),  # t_0 != 1
     (lambda c: _set_schedule(c, [1.0 - 0.095 * k for k in range(11)]), _abi.FM_ERR_ARG),  # t_N != 0

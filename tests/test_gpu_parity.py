@@ -174,7 +174,8 @@ def _ring_run(cfg, ticks, oracle_ticks):
             keep = keep[-4 * cfg.batch:]
             assert np.array_equal(y_ring, y_full), f"tick {t}: ring != full recompute"
             if t in oracle_ticks:
-                ref = np.stack([O.denoise_robot(cfg, W64, kl[b], vl[b], x0[b], st[b])
+                q8 = O.prefix_kv_e4m3 if cfg.kv_fp8 else (lambda a: a)  # the cache as the loop holds it
+                ref = np.stack([O.denoise_robot(cfg, W64, q8(kl[b]), q8(vl[b]), x0[b], st[b])
                                 for b in range(cfg.batch)])
                 check(f"{cfg.name} tick {t}", y_ring, ref, 5e-2 if cfg.weight_dtype == "fp8" else 1e-2)
         announce(f"{cfg.name}: {ticks} ticks ring == recompute bitwise")
@@ -368,3 +369,48 @@ def test_full_pi0_1view_state_causal():
     W, k, v, x0, st = _inputs(cfg)
     got = run_denoiser(cfg, W, k, v, x0, st)[0]
     check("pi0_1view state_causal", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
+# --- fp8 prefix cache -----------------------------------------------------------------
+@pytest.mark.parametrize("kw", [
+    dict(),                                                      # one row tile
+    dict(head_dim=128, prefix_static=600, prefix_len=200),      # key split
+    dict(batch=20, chunk=60, n_q_heads=8, prefix_static=100, prefix_len=100),  # two query blocks per workgroup
+    dict(n_q_heads=2, head_dim=256, d_mlp=512, chunk=20),        # head-dim split in 4
+    dict(state_causal=True, prefix_len=8),                       # with the block-causal suffix
+    dict(batch=10, chunk=40, prefix_static=64, prefix_len=64),  # large-M GEMMs
+])
+def test_small_kv_fp8(kw):
+    cfg = small_cfg(kv_fp8=True, **kw)
+    announce(f"small kv_fp8 {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    ref = O.denoise(cfg, W, k, v, x0, st)
+    check(f"small kv_fp8 {kw}", got, ref, 1e-2, 3e-2)
+    # the cache really is fp8: the result sits far closer to the fp8-cache
+    # oracle than to the bf16-cache one
+    ref16 = O.denoise(cfg.replace(kv_fp8=False), W, k, v, x0, st)
+    announce(f"  fp8 vs bf16 cache in the oracle: {O.rel_l2(ref, ref16):.3e}")
+    assert O.rel_l2(got, ref) < O.rel_l2(ref, ref16) / 2
+
+
+def test_small_ring_kv_fp8():
+    cfg = small_cfg(name="small_ring_kv8", prefix_static=20, frame_tokens=32, n_frames=3, prefix_len=116, kv_fp8=True)
+    _ring_run(cfg, ticks=6, oracle_ticks={0, 5})
+
+
+def test_full_pi0_1view_kv_fp8():
+    cfg = S.workload("pi0_1view").replace(kv_fp8=True)
+    announce("pi0_1view kv_fp8")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("pi0_1view kv_fp8", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)
+
+
+def test_full_pi05_ada_b16_kv_fp8_sampled_robots():
+    cfg = S.workload("pi05_ada_b16").replace(kv_fp8=True)
+    announce("pi05_ada_b16 kv_fp8")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    robots = [0, 9]
+    check("pi05_ada_b16 kv_fp8 robots 0,9", got[robots], O.denoise(cfg, W, k, v, x0, st, robots=robots), 1e-2, 3e-2)
