@@ -1,0 +1,67 @@
+"""GPU parity over a seeded sweep of small configurations: shapes, head
+layouts, prefix lengths, samplers, schedules and options drawn together, so
+that combinations no hand-written case names are exercised too.  Each case is
+compared with the fp64 oracle at the bar of its dtype (bf16: rel-L2 1e-2,
+max-abs 3e-2; fp32: 1e-4)."""
+import numpy as np
+import pytest
+
+import fm_synth as S
+import oracle as O
+from gpu_util import announce, check, run_denoiser, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    g = np.random.default_rng(1000 + seed)
+    hd = int(g.choice([32, 64, 128, 256]))
+    hkv = int(g.choice([1, 2]))
+    hq = hkv * int(g.choice([1, 2, 4, 8]))
+    while (hq * hd) % 32 or hq * hd > 2048:
+        hq //= 2
+    kw = dict(seed=seed, head_dim=hd, n_kv_heads=hkv, n_q_heads=max(hq, hkv),
+              d_model=int(g.choice([64, 128, 192, 256])), d_mlp=int(g.choice([128, 256, 384])),
+              n_layers=int(g.integers(1, 4)), chunk=int(g.integers(1, 40)), batch=int(g.integers(1, 13)),
+              state_dim=int(g.choice([0, 32])), n_steps=int(g.integers(1, 7)),
+              action_dim=int(g.choice([16, 32])))
+    kw["time_dim"] = kw["d_model"]
+    ring = g.random() < 0.25
+    if ring:
+        kw.update(prefix_static=int(g.integers(0, 40)), frame_tokens=32, n_frames=int(g.integers(1, 4)))
+        kw["prefix_len"] = kw["prefix_static"] + kw["frame_tokens"] * kw["n_frames"]
+    else:
+        cap = int(g.integers(0, 400))
+        kw.update(prefix_static=cap, prefix_len=int(g.integers(0, cap + 1)))
+    if g.random() < 0.3:
+        kw.update(norm="ada", time_dim=int(g.choice([16, 32])))
+    kw["sampler"] = str(g.choice(["euler", "heun", "ab2"]))
+    if g.random() < 0.3 and kw["n_steps"] > 1:
+        u = np.linspace(0, 1, kw["n_steps"] + 1)
+        kw["t_schedule"] = tuple(float(np.float32(x)) for x in (1 - u) / (1 + 2 * u))  # shifted, ends 1 -> 0
+    if kw["state_dim"] and g.random() < 0.4:
+        kw["state_causal"] = True
+    keys = (kw["prefix_static"] + 31) // 32 * 32 + kw.get("frame_tokens", 0) * kw.get("n_frames", 0) + \
+        (kw["chunk"] + (kw["state_dim"] > 0) + 31) // 32 * 32
+    if g.random() < 0.25 and keys <= 1024:
+        kw["kv_fp8"] = True
+    if g.random() < 0.15 and not kw.get("kv_fp8") and kw["d_model"] % 64 == 0 and kw["d_mlp"] % 64 == 0 \
+            and (kw["n_q_heads"] * hd) % 64 == 0:
+        kw["weight_dtype"] = "fp8"
+    return small_cfg(name=f"sweep{seed}", **kw)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_sweep(seed):
+    cfg = _draw(seed)
+    desc = {k: getattr(cfg, k) for k in ("batch", "chunk", "state_dim", "d_model", "n_layers", "n_q_heads", "n_kv_heads",
+                                         "head_dim", "d_mlp", "prefix_static", "prefix_len", "n_frames", "norm",
+                                         "sampler", "n_steps", "state_causal", "kv_fp8", "weight_dtype")}
+    desc["schedule"] = cfg.t_schedule is not None
+    announce(f"sweep {seed}: {desc}")
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    x0, st = S.make_noise(cfg), S.make_state(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    tol = 5e-2 if cfg.weight_dtype == "fp8" else 1e-2
+    check(f"sweep {seed}", got, O.denoise(cfg, W, k, v, x0, st), tol, None if cfg.weight_dtype == "fp8" else 3e-2)
