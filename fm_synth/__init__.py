@@ -65,6 +65,7 @@ class FMConfig:
     sampler: str = "euler"  # "euler", "heun" or "ab2"
     state_causal: bool = False  # Pi0-style suffix: the state token sees only the prefix and itself
     kv_fp8: bool = False        # prefix K/V cached as fp8 E4M3 with a scale per (token, kv head)
+    rope_theta: float = 0.0     # rotary position embedding base (0: none)
 
     @property
     def has_state(self) -> int:

@@ -63,7 +63,7 @@ from scipy.special import erf as _erf
 
 __all__ = [
     "time_grid", "sinusoid", "linear", "rms_inv", "rmsnorm", "ada_rmsnorm",
-    "silu", "gelu", "softmax_rows", "attention", "masked_attention",
+    "silu", "gelu", "softmax_rows", "attention", "masked_attention", "rope",
     "ada_modulation", "euler", "heun", "ab2", "integrate", "expert_velocity", "denoise", "denoise_robot",
     "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_e4m3_per_channel",
     "effective_weights", "prefix_kv_e4m3", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
@@ -154,6 +154,20 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
         p = softmax_rows((q[:, h, :] @ k[:, j, :].T) * scale)
         out[:, h, :] = p @ v[:, j, :]
     return out
+
+
+def rope(x, positions, theta: float) -> np.ndarray:
+    """Rotary position embedding of x [n][heads][Dh] at positions [n]: with
+    half = Dh / 2, the pair (i, i + half) of every head turns by the angle
+    position * theta^(-2 i / Dh) (the rotate-half pairing).  A reading: the
+    pages name no positional encoding; Pi0-style experts rotate q and k."""
+    x = np.asarray(x, F64)
+    dh = x.shape[-1]
+    half = dh // 2
+    ang = np.asarray(positions, F64)[:, None] * (float(theta) ** (-2.0 * np.arange(half) / dh))[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
 def masked_attention(q, k, v, allowed: np.ndarray) -> np.ndarray:
@@ -302,6 +316,8 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
     Suffix mask: none, or with cfg.state_causal the block-causal suffix of
     Pi0-style experts (a reading; the pages fix no suffix mask): the state
     token attends to the prefix and itself, the action tokens to everything.
+    With cfg.rope_theta the suffix q and k are rotated (rope) at positions
+    T + s; k_pre is then the rotated cache (see denoise).
     """
     S_has = 1 if cfg.state_dim else 0
     hq, hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -315,6 +331,7 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
     S = h.shape[0]
     T = np.asarray(k_pre[0]).shape[0] if len(k_pre) else 0
     causal = bool(getattr(cfg, "state_causal", False)) and S_has
+    theta = float(getattr(cfg, "rope_theta", 0.0))
     if causal:
         allowed = np.ones((S, T + S), bool)
         allowed[0, T + 1:] = False
@@ -326,6 +343,8 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
         q = linear(u, L["wq"]).reshape(S, hq, dh)
         k = linear(u, L["wk"]).reshape(S, hkv, dh)
         v = linear(u, L["wv"]).reshape(S, hkv, dh)
+        if theta:  # suffix row s sits at position T + s, after the prefix
+            q, k = rope(q, T + np.arange(S), theta), rope(k, T + np.arange(S), theta)
         ks.append(k)
         vs.append(v)
         K = np.concatenate([np.asarray(k_pre[li], F64), k], axis=0)
@@ -409,6 +428,9 @@ def denoise(cfg, W: dict, k_pre, v_pre, noise, state=None,
     subset (the result then has len(robots) rows)."""
     W64 = effective_weights(cfg, W)
     idx = range(noise.shape[0]) if robots is None else robots
+    theta = float(getattr(cfg, "rope_theta", 0.0))
+    if theta:  # the cache holds prefix K rotated at its token positions 0..T-1
+        k_pre = [np.stack([rope(kl, np.arange(kl.shape[0]), theta) for kl in k]) for k in k_pre]
     if getattr(cfg, "kv_fp8", False):  # the prefix cache held in fp8
         k_pre, v_pre = [prefix_kv_e4m3(k) for k in k_pre], [prefix_kv_e4m3(v) for v in v_pre]
     return np.stack([denoise_robot(cfg, W64, k_pre[b], v_pre[b], noise[b],
@@ -456,6 +478,11 @@ def _prefix_layer_qkv(cfg, Lp, hp):
             linear(u, Lp["wv"]).reshape(T, cfg.n_kv_heads, cfg.head_dim))
 
 
+def _rot(cfg, x, pos):
+    theta = float(getattr(cfg, "rope_theta", 0.0))
+    return rope(x, pos, theta) if theta else x
+
+
 def _prefix_layer_rest(cfg, Lp, hp, o):
     hp = hp + linear(o.reshape(hp.shape[0], -1), Lp["wo"])
     u = rmsnorm(hp, Lp["norm2"], cfg.rms_eps)
@@ -468,11 +495,12 @@ def prefix_stack_kv(cfg, Wp: dict, tokens: np.ndarray):
     [layers][T][Hkv][Dh]: the cache the denoise loop reads."""
     hp = np.asarray(tokens, F64)
     Ks, Vs = [], []
+    pos = np.arange(hp.shape[0])
     for Lp in Wp["layers"]:
         q, k, v = _prefix_layer_qkv(cfg, Lp, hp)
-        Ks.append(k)
+        Ks.append(k)  # unrotated: the cache input (the loop rotates it)
         Vs.append(v)
-        hp = _prefix_layer_rest(cfg, Lp, hp, attention(q, k, v))
+        hp = _prefix_layer_rest(cfg, Lp, hp, attention(_rot(cfg, q, pos), _rot(cfg, k, pos), v))
     return np.stack(Ks), np.stack(Vs)
 
 
@@ -498,10 +526,12 @@ def joint_velocity(cfg, W64: dict, Wp: dict, tokens, x, t, state) -> np.ndarray:
     for li, (L, Lp) in enumerate(zip(W64["layers"], Wp["layers"])):
         m1, m2 = mods[li] if mods else (None, None)
         qp, kp, vp = _prefix_layer_qkv(cfg, Lp, hp)
+        qp, kp = _rot(cfg, qp, np.arange(T)), _rot(cfg, kp, np.arange(T))
         u = _norm(cfg, hs, L.get("norm1"), m1)
         qs = linear(u, L["wq"]).reshape(S, hq, dh)
         ks = linear(u, L["wk"]).reshape(S, hkv, dh)
         vs = linear(u, L["wv"]).reshape(S, hkv, dh)
+        qs, ks = _rot(cfg, qs, T + np.arange(S)), _rot(cfg, ks, T + np.arange(S))
         o = masked_attention(np.concatenate([qp, qs]), np.concatenate([kp, ks]),
                              np.concatenate([vp, vs]), allowed)
         hp = _prefix_layer_rest(cfg, Lp, hp, o[:T])

@@ -329,11 +329,12 @@ def test_sinusoid_values():
 
 
 # --- P7: cached timestep-invariant prefix equals joint recompute ----------------
-@pytest.mark.parametrize("kind", ["rms_mha", "rms_gqa", "ada", "state_causal"])
+@pytest.mark.parametrize("kind", ["rms_mha", "rms_gqa", "ada", "state_causal", "rope"])
 def test_cached_prefix_equals_joint_recompute(kind):
     cfg = {"rms_mha": TINY, "rms_gqa": _tiny(n_kv_heads=1, batch=2),
            "ada": _tiny(norm="ada", time_dim=16, state_dim=0),
-           "state_causal": _tiny(n_kv_heads=1, state_causal=True)}[kind]
+           "state_causal": _tiny(n_kv_heads=1, state_causal=True),
+           "rope": _tiny(n_kv_heads=2, rope_theta=10000.0, batch=2)}[kind]
     W = S.make_weights(cfg)
     x0, st = S.make_noise(cfg), S.make_state(cfg)
     Wp, tokens = S.make_prefix_stack(cfg, 32)
@@ -341,6 +342,28 @@ def test_cached_prefix_equals_joint_recompute(kind):
     cached = O.denoise(cfg, W, np.stack(ks), np.stack(vs), x0, st)
     joint = O.denoise_joint(cfg, W, Wp, tokens, x0, st)
     assert O.rel_l2(cached, joint) < 1e-12
+
+
+# --- rotary position embedding ------------------------------------------------------
+def test_rope_pairs_and_direction():
+    # Dh = 4: pairs (0, 2) and (1, 3) turn by p and p * theta^(-1/2), counterclockwise
+    th, p = 100.0, 0.7
+    e0, e1 = np.array([[[1.0, 0, 0, 0]]]), np.array([[[0, 1.0, 0, 0]]])
+    assert np.allclose(O.rope(e0, [p], th)[0, 0], [np.cos(p), 0, np.sin(p), 0], atol=1e-15)
+    w = p * th ** -0.5
+    assert np.allclose(O.rope(e1, [p], th)[0, 0], [0, np.cos(w), 0, np.sin(w)], atol=1e-15)
+    x = np.random.default_rng(3).standard_normal((5, 2, 8))
+    assert np.array_equal(O.rope(x, np.zeros(5), th), x)                       # position 0: identity
+    assert np.allclose(np.linalg.norm(O.rope(x, np.arange(5) * 3.0, th), axis=-1), np.linalg.norm(x, axis=-1))
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    g = np.random.default_rng(4)
+    q, k = g.standard_normal((1, 1, 16)), g.standard_normal((1, 1, 16))
+    s = lambda m, n: float(np.sum(O.rope(q, [m], 1e4) * O.rope(k, [n], 1e4)))
+    for m, n, c in ((3, 1, 5), (0, 7, 11), (40, 2, -2)):
+        assert abs(s(m, n) - s(m + c, n + c)) < 1e-12
+    assert abs(s(3, 1) - s(4, 1)) > 1e-6
 
 
 # --- block-causal state token (Pi0-style suffix) ------------------------------------
