@@ -55,6 +55,7 @@ def make_config(cfg, exec_mode: int = FM_EXEC_AUTO) -> fm_config:
                  "ab2": _abi.FM_SAMPLER_AB2}[getattr(cfg, "sampler", "euler")]
     c.state_causal = 1 if getattr(cfg, "state_causal", False) else 0
     c.kv_fp8 = 1 if getattr(cfg, "kv_fp8", False) else 0
+    c.rope_theta = float(getattr(cfg, "rope_theta", 0.0))
     sched = getattr(cfg, "t_schedule", None)
     if sched is not None:
         arr = (ctypes.c_float * len(sched))(*[float(t) for t in sched])

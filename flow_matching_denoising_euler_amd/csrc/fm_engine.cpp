@@ -155,6 +155,9 @@ fm_status validate_config(const fm_config* c) {
     return fail(nullptr, FM_ERR_ARG, "bad sampler");
   if (c->state_causal != 0 && c->state_causal != 1) return fail(nullptr, FM_ERR_ARG, "state_causal must be 0 or 1");
   if (c->kv_fp8 != 0 && c->kv_fp8 != 1) return fail(nullptr, FM_ERR_ARG, "kv_fp8 must be 0 or 1");
+  if (!(c->rope_theta >= 0.f) || std::isinf(c->rope_theta)) return fail(nullptr, FM_ERR_ARG, "rope_theta must be 0 or positive");
+  if (c->rope_theta > 0.f && c->n_frames > 0)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "rotary positions with a frame ring: the window would move cached positions");
   if (c->t_schedule) {
     // t_0 = 1 > t_1 > ... > t_N = 0, all finite
     const float* t = c->t_schedule;
@@ -395,6 +398,13 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
       g.row_bstride = (long)x->L * x->S * x->HD;
     }
     HIPCHK(x, launch_gemm(x->act, x->wt, x->encoder ? EPI_QKVR : EPI_QKV, g, st), "qkv gemm");
+    if (x->cfg.rope_theta > 0.f) {  // rotary embedding of this step's suffix Q and K
+      RopeArgs r{};
+      r.qkv = x->qkv; r.ksuf = x->ksuf; r.meta = x->meta;
+      r.M = x->M; r.S = x->S; r.SP = x->SP; r.Hq = x->Hq; r.Hkv = x->Hkv; r.Dh = x->Dh; r.Nqkv = x->Nqkv;
+      r.theta = x->cfg.rope_theta;
+      HIPCHK(x, launch_rope(x->act, r, st), "rope");
+    }
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     AttnArgs at{};
     at.qkv = x->qkv;
@@ -830,6 +840,7 @@ fm_status fm_set_prefix_kv(fm_ctx* x, int32_t robot, const void* k, const void* 
   c.fp8 = x->kv8;
   c.ksd = x->kscale + (size_t)robot * x->L * x->TP * x->Hkv;
   c.vsd = x->vscale + (size_t)robot * x->L * x->TP * x->Hkv;
+  c.rope_theta = x->cfg.rope_theta;
   c.phys0 = 0; c.split_t = ring ? x->cfg.prefix_static : n_tokens; c.phys1 = x->NSP;
   c.meta = x->meta; c.robot = robot; c.valid = n_tokens; c.head = 0;
   HIPCHK(x, launch_kv_copy(c, x->stream), "prefix copy");

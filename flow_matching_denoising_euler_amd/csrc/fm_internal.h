@@ -235,7 +235,18 @@ struct KvCopy {
   int fp8;                // the cache in E4M3 with a scale per (token, kv head):
   float* ksd;             //   robot base of the K / V scales, [layers][TP][Hkv]
   float* vsd;
+  float rope_theta;       // > 0: K token t rotated at position t on the way in
 };
+// rotary embedding of the suffix Q (rows of qkv) and K (kv layout) in place:
+// row r of robot r / S at position meta[2 (r / S)] + r % S
+struct RopeArgs {
+  void* qkv;
+  void* ksuf;
+  const int* meta;
+  int M, S, SP, Hq, Hkv, Dh, Nqkv;
+  float theta;
+};
+hipError_t launch_rope(int act, const RopeArgs& r, hipStream_t st);
 hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st);
 
 // prefix encoder: token rows in (h = tokens, u = act(h * g), h^2 partials)

@@ -1940,6 +1940,59 @@ __global__ void k_bias_gemv(const void* w, int w_elt, const float* scales, int r
 }
 
 // prefix K rows and V^T columns -> the padded physical layout, and the robot's (valid, head)
+// Rotary embedding: the pair (c, c + Dh/2) of a head turns by pos *
+// theta^(-2c/Dh).  The angle is formed and reduced in double: at positions of
+// a few thousand an fp32 angle would already be off by ~1e-4 rad.
+__device__ __forceinline__ void rope_cs(double pos, int c, int Dh, float theta, float* cs, float* sn) {
+  const double ang = pos * pow((double)theta, -2.0 * (double)c / (double)Dh);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *cs = (float)cd;
+  *sn = (float)sd;
+}
+// element c of a K row at position pos after rotation (x: the row's Dh values)
+template <typename T>
+__device__ __forceinline__ float rope_elem(const T* x, int c, int Dh, double pos, float theta) {
+  const int half = Dh >> 1, i = c < half ? c : c - half;
+  float cs, sn;
+  rope_cs(pos, i, Dh, theta, &cs, &sn);
+  auto ld = [&](int e) { if constexpr (sizeof(T) == 2) return bf2f(x[e]); else return (float)x[e]; };
+  return c < half ? ld(c) * cs - ld(c + half) * sn : ld(c) * cs + ld(c - half) * sn;
+}
+
+// The suffix Q (row-major in qkv) and K (kv layout) of one step, rotated in
+// place: thread = one (row, head, pair)
+template <int ACT>
+__global__ void k_rope(RopeArgs r) {
+  constexpr bool packed = ACT != ELT_F32;
+  const int half = r.Dh >> 1, H = r.Hq + r.Hkv;
+  const long total = (long)r.M * H * half;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % half), h = (int)((i / half) % H);
+    const int row = (int)(i / ((long)half * H));
+    const int b = row / r.S, s = row % r.S;
+    float cs, sn;
+    rope_cs((double)(r.meta[2 * b] + s), c, r.Dh, r.theta, &cs, &sn);
+    void* base;
+    long o1, o2;
+    if (h < r.Hq) {
+      base = r.qkv;
+      o1 = (long)row * r.Nqkv + (long)h * r.Dh + c;
+      o2 = o1 + half;
+    } else {
+      const int j = h - r.Hq;
+      const long sb = (long)b * r.Hkv * r.Dh * r.SP;
+      base = r.ksuf;
+      o1 = sb + kv_k_off(packed, r.SP, r.Hkv, r.Dh, j, s, c);
+      o2 = sb + kv_k_off(packed, r.SP, r.Hkv, r.Dh, j, s, c + half);
+    }
+    const float x1 = ld_act<ACT>(base, o1), x2 = ld_act<ACT>(base, o2);
+    st_act<ACT>(base, o1, x1 * cs - x2 * sn);
+    st_act<ACT>(base, o2, x2 * cs + x1 * sn);
+  }
+}
+
 template <typename T>
 __global__ void k_kv_copy(KvCopy c) {
   constexpr bool packed = sizeof(T) == 2;
@@ -1955,8 +2008,17 @@ __global__ void k_kv_copy(KvCopy c) {
     const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
     const T* src = (const T*)c.k + (l * c.n + t) * HD + col;
     T* dst = (T*)c.kd + l * pitch + kv_k_off(packed, c.TP, Hkv, Dh, col / Dh, phys, col % Dh);
+    if (c.rope_theta > 0.f) {  // token t at position t (a set: no ring)
+      const T* row = src - col % Dh;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = src[e];
+      for (int e = 0; e < 8; ++e) {
+        const float y = rope_elem<T>(row, col % Dh + e, Dh, (double)t, c.rope_theta);
+        if constexpr (packed) dst[e] = (T)f2bf(y); else dst[e] = y;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = src[e];
+    }
   }
   // V: consecutive threads take consecutive tokens of one (layer, column)
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_v; i += stride) {
@@ -1991,12 +2053,14 @@ __global__ void k_kv_copy8(KvCopy c) {
     uint8_t* vd = (uint8_t*)c.vd + l * (long)c.TP * HD;
     for (int kv = 0; kv < 2; ++kv) {
       const uint16_t* x = (const uint16_t*)(kv ? c.v : c.k) + src;
+      const bool rot = !kv && c.rope_theta > 0.f;  // K token t at position t, then quantised
+      auto val = [&](int e) { return rot ? rope_elem<uint16_t>(x, e, Dh, (double)t, c.rope_theta) : bf2f(x[e]); };
       float amax = 0.f;
-      for (int e = lane; e < Dh; e += 64) amax = fmaxf(amax, fabsf(bf2f(x[e])));
+      for (int e = lane; e < Dh; e += 64) amax = fmaxf(amax, fabsf(val(e)));
       for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
       const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
       for (int e = lane; e < Dh; e += 64) {
-        const uint8_t code = (uint8_t)f32_to_e4m3(__fdiv_rn(bf2f(x[e]), sc));
+        const uint8_t code = (uint8_t)f32_to_e4m3(__fdiv_rn(val(e), sc));
         if (kv) vd[kv_v_off(true, c.TP, Hkv, Dh, j, phys, e)] = code;
         else kd[kv_k_off(true, c.TP, Hkv, Dh, j, phys, e)] = code;
       }
@@ -2264,6 +2328,14 @@ hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st) {
   const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
   if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_copy<float>, dim3(grid), dim3(256), 0, st, c);
   else hipLaunchKernelGGL(k_kv_copy<uint16_t>, dim3(grid), dim3(256), 0, st, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(int act, const RopeArgs& r, hipStream_t st) {
+  const long work = (long)r.M * (r.Hq + r.Hkv) * (r.Dh / 2);
+  const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
+  if (act == ELT_F32) hipLaunchKernelGGL(k_rope<ELT_F32>, dim3(grid), dim3(256), 0, st, r);
+  else hipLaunchKernelGGL(k_rope<ELT_BF16>, dim3(grid), dim3(256), 0, st, r);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 4
+#define FM_ABI_VERSION 5
 
 typedef struct fm_ctx fm_ctx;
 
@@ -138,6 +138,14 @@ typedef enum {
  *   cache bytes.  The suffix K/V of each step stay in act_dtype.  bf16
  *   activations and at most 1024 padded keys (prefix capacity rounded up to
  *   32 plus the suffix rounded up to 32), else FM_ERR_UNSUPPORTED.
+ *
+ * rope_theta: 0 = no positional encoding (the pages give none); > 0 = rotary
+ *   embeddings of q and k with base rope_theta (e.g. 10000): the pair (i, i +
+ *   Dh/2) of every head turns by position * rope_theta^(-2i/Dh).  Prefix
+ *   token t of fm_set_prefix_kv sits at position t (K is passed unrotated
+ *   and rotated on the way in); suffix row s at (valid prefix tokens) + s.
+ *   A frame ring would move every cached frame's position as the window
+ *   slides, so rope_theta > 0 with n_frames > 0 is FM_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t abi_version;               /* FM_ABI_VERSION */
@@ -154,6 +162,7 @@ typedef struct {
   int32_t sampler;                   /* fm_sampler */
   int32_t state_causal;              /* 0 or 1, see above */
   int32_t kv_fp8;                    /* 0 or 1, see above */
+  float rope_theta;                  /* 0 or the rotary base, see above */
   const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
 } fm_config;
 
@@ -247,8 +256,10 @@ fm_status fm_denoise(fm_ctx* ctx, const float* noise, const void* state, float* 
  *
  * fm_encoder_create reads abi_version, d_model, n_layers, n_q_heads,
  * n_kv_heads, head_dim, d_mlp, rms_eps, weight_dtype, act_dtype, exec_mode,
- * batch (sequences per call) and chunk (tokens per sequence; at most 1024 for
- * bf16, 256 for fp32); it ignores every other field.  Weights: `layers` only
+ * rope_theta (token t of a sequence at position t; the K/V it writes stay
+ * unrotated, the form fm_set_prefix_kv takes), batch (sequences per call) and
+ * chunk (tokens per sequence; at most 1024 for bf16, 256 for fp32); it
+ * ignores every other field.  Weights: `layers` only
  * (wq, wk, wv, wo, wg, wu, wd, norm1, norm2 of every layer; the other
  * pointers may be NULL), in the same dtypes and layouts as fm_create's.  The
  * context accepts fm_encode_prefix, fm_get_info and fm_destroy only; the

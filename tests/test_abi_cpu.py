@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(_abi.fm_config) == 24 * 4 + 8  # 24 scalars, the t_schedule pointer
+    assert ctypes.sizeof(_abi.fm_config) == 26 * 4 + 8  # 25 scalars, padding, the t_schedule pointer
     assert ctypes.sizeof(_abi.fm_weights) == 11 * 8
     assert ctypes.sizeof(_abi.fm_info) == 3 * 8 + 4 * 4
 
@@ -72,6 +72,10 @@ def _create(c):
     (lambda c: setattr(c, "sampler", 3), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "state_causal", 2), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "kv_fp8", 2), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "rope_theta", -1.0), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "rope_theta", float("nan")), _abi.FM_ERR_ARG),
+    (lambda c: (setattr(c, "rope_theta", 1e4), setattr(c, "n_frames", 2), setattr(c, "frame_tokens", 32)),
+     _abi.FM_ERR_UNSUPPORTED),                                        # rotary positions with a ring
     (lambda c: setattr(c, "kv_fp8", 1), _abi.FM_ERR_UNSUPPORTED),   # fp32 activations
     (lambda c: (setattr(c, "kv_fp8", 1), setattr(c, "act_dtype", _abi.FM_BF16), setattr(c, "weight_dtype", _abi.FM_BF16),
                 setattr(c, "prefix_static", 1100)), _abi.FM_ERR_UNSUPPORTED),  # > 1024 padded keys

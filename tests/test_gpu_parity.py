@@ -414,3 +414,41 @@ def test_full_pi05_ada_b16_kv_fp8_sampled_robots():
     got = run_denoiser(cfg, W, k, v, x0, st)[0]
     robots = [0, 9]
     check("pi05_ada_b16 kv_fp8 robots 0,9", got[robots], O.denoise(cfg, W, k, v, x0, st, robots=robots), 1e-2, 3e-2)
+
+
+# --- rotary position embedding -------------------------------------------------------
+@pytest.mark.parametrize("kw", [
+    dict(),                                                      # one row tile
+    dict(prefix_len=20),                                         # positions from the valid prefix length
+    dict(head_dim=128, prefix_static=600, prefix_len=200),      # key split
+    dict(batch=10, chunk=40, prefix_static=64, prefix_len=64),  # large-M GEMMs
+    dict(state_causal=True, sampler="heun", n_steps=4),
+    dict(kv_fp8=True),                                           # rotated, then quantised
+    dict(norm="ada", time_dim=32, state_dim=0),
+])
+def test_small_rope(kw):
+    cfg = small_cfg(rope_theta=10000.0, **kw)
+    announce(f"small rope {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    ref = O.denoise(cfg, W, k, v, x0, st)
+    check(f"small rope {kw}", got, ref, 1e-2, 3e-2)
+    ref0 = O.denoise(cfg.replace(rope_theta=0.0), W, k, v, x0, st)
+    announce(f"  rope vs none in the oracle: {O.rel_l2(ref, ref0):.3e}")
+    assert O.rel_l2(got, ref) < O.rel_l2(ref, ref0) / 3
+
+
+def test_tiny_fp32_rope():
+    cfg = S.workload("tiny_fp32").replace(rope_theta=100.0)
+    announce("tiny_fp32 rope")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("tiny_fp32 rope", got, O.denoise(cfg, W, k, v, x0, st), 1e-4)
+
+
+def test_full_pi0_1view_rope():
+    cfg = S.workload("pi0_1view").replace(rope_theta=10000.0)
+    announce("pi0_1view rope")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check("pi0_1view rope", got, O.denoise(cfg, W, k, v, x0, st), 1e-2, 3e-2)

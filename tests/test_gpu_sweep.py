@@ -45,6 +45,8 @@ def _draw(seed):
         (kw["chunk"] + (kw["state_dim"] > 0) + 31) // 32 * 32
     if g.random() < 0.25 and keys <= 1024:
         kw["kv_fp8"] = True
+    if not ring and g.random() < 0.3:
+        kw["rope_theta"] = float(g.choice([100.0, 10000.0]))
     if g.random() < 0.15 and not kw.get("kv_fp8") and kw["d_model"] % 64 == 0 and kw["d_mlp"] % 64 == 0 \
             and (kw["n_q_heads"] * hd) % 64 == 0:
         kw["weight_dtype"] = "fp8"
@@ -56,7 +58,7 @@ def test_sweep(seed):
     cfg = _draw(seed)
     desc = {k: getattr(cfg, k) for k in ("batch", "chunk", "state_dim", "d_model", "n_layers", "n_q_heads", "n_kv_heads",
                                          "head_dim", "d_mlp", "prefix_static", "prefix_len", "n_frames", "norm",
-                                         "sampler", "n_steps", "state_causal", "kv_fp8", "weight_dtype")}
+                                         "sampler", "n_steps", "state_causal", "kv_fp8", "weight_dtype", "rope_theta")}
     desc["schedule"] = cfg.t_schedule is not None
     announce(f"sweep {seed}: {desc}")
     W = S.make_weights(cfg)
