@@ -2,10 +2,12 @@
  * fm.h - C ABI of the MI355X (gfx950) flow-matching action-expert denoiser.
  *
  * The library runs the denoising loop of a flow-matching robot policy: N
- * explicit Euler steps x <- x + dt * v(x, t), each evaluating a small
- * transformer (the "action expert") over the suffix tokens (an optional
- * state token plus the noisy action chunk) that attend to a cached,
- * timestep-invariant prefix of keys and values (vision and prompt tokens).
+ * explicit Euler steps x <- x + dt * v(x, t) (or Heun / Adams-Bashforth
+ * steps, fm_sampler), each evaluating a small transformer (the "action
+ * expert") over the suffix tokens (an optional state token plus the noisy
+ * action chunk) that attend to a cached, timestep-invariant prefix of keys
+ * and values (vision and prompt tokens).  A prefix encoder context produces
+ * that cache from token embeddings (fm_encoder_create).
  *
  *   - Euler flow sampling with 10 steps: FlowEdge README, "Installation"
  *     (the flow sampler run as "euler 10"); realtime-vla write-up, "The
@@ -236,7 +238,7 @@ fm_status fm_append_prefix_kv(fm_ctx* ctx, int32_t robot, const void* k_frame,
                               const void* v_frame);
 
 /*
- * Run the whole N-step Euler loop for every robot.  noise: [B][C][A] fp32
+ * Run the whole N-step loop (the configured sampler) for every robot.  noise: [B][C][A] fp32
  * (x at t = 1); state: [B][state_dim] act_dtype, or NULL iff state_dim is
  * 0; actions: [B][C][A] fp32 (x at t = 0).  noise and actions may alias.
  * FM_ERR_STATE if some robot's prefix was never set.  Allocates nothing.
@@ -315,24 +317,25 @@ void fm_destroy(fm_ctx* ctx);
  */
 const char* fm_last_error(const fm_ctx* ctx);
 
-/* Phases of one Euler step, for fm_launch_phase. */
+/* Phases of one step (one velocity evaluation and its update), for fm_launch_phase. */
 typedef enum {
   FM_PHASE_QKV = 0,      /* norm1 folded into the QKV GEMM                     */
   FM_PHASE_ATTN = 1,     /* attention over [cached prefix | suffix]            */
   FM_PHASE_OPROJ = 2,    /* O GEMM + residual (+ next norm's input)            */
   FM_PHASE_GATEUP = 3,   /* norm2 folded into the gate/up GEMM + GELU gate     */
   FM_PHASE_DOWN = 4,     /* down GEMM + residual (+ next norm's input)         */
-  FM_PHASE_TAIL = 5      /* final norm, action head, Euler, next embedding     */
+  FM_PHASE_TAIL = 5      /* final norm, action head, update, next embedding    */
 } fm_phase;
 
 /*
- * Profiling aid: enqueue the single kernel of phase `phase` of Euler step
- * `step` and layer `layer` (ignored for FM_PHASE_TAIL) with exactly the
- * arguments fm_denoise uses, on the context's stream.  It reads and writes
- * the context's activation buffers, so results of a later fm_denoise are
- * unaffected (fm_denoise rewrites them from its inputs).  Lets a caller time
- * one kernel with events on the stream.  FM_ERR_ARG for an out-of-range
- * step, layer or phase.
+ * Profiling aid: enqueue the kernel of phase `phase` of step `step` and
+ * layer `layer` (ignored for FM_PHASE_TAIL) with exactly the arguments
+ * fm_denoise uses, on the context's stream (FM_PHASE_QKV with rope_theta > 0
+ * also enqueues its rotary kernel).  It reads and writes the context's
+ * activation buffers, so results of a later fm_denoise are unaffected
+ * (fm_denoise rewrites them from its inputs).  Lets a caller time one kernel
+ * with events on the stream.  FM_ERR_ARG for an out-of-range step, layer or
+ * phase; FM_ERR_STATE on an encoder context.
  */
 fm_status fm_launch_phase(fm_ctx* ctx, int32_t step, int32_t layer, int32_t phase);
 
