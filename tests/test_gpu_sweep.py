@@ -53,7 +53,7 @@ def _draw(seed):
     return small_cfg(name=f"sweep{seed}", **kw)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(64))
 def test_sweep(seed):
     cfg = _draw(seed)
     desc = {k: getattr(cfg, k) for k in ("batch", "chunk", "state_dim", "d_model", "n_layers", "n_q_heads", "n_kv_heads",
@@ -67,3 +67,42 @@ def test_sweep(seed):
     got = run_denoiser(cfg, W, k, v, x0, st)[0]
     tol = 5e-2 if cfg.weight_dtype == "fp8" else 1e-2
     check(f"sweep {seed}", got, O.denoise(cfg, W, k, v, x0, st), tol, None if cfg.weight_dtype == "fp8" else 3e-2)
+
+
+def _draw_encoder(seed):
+    g = np.random.default_rng(5000 + seed)
+    hd = int(g.choice([32, 64, 128, 256]))
+    hkv = int(g.choice([1, 2]))
+    kw = dict(seed=seed, head_dim=hd, n_kv_heads=hkv, n_q_heads=hkv * int(g.choice([1, 2, 4])),
+              d_model=int(g.choice([64, 128, 256])), d_mlp=int(g.choice([128, 256])), n_layers=int(g.integers(1, 4)))
+    kw["time_dim"] = kw["d_model"]
+    if g.random() < 0.3:
+        kw["rope_theta"] = 10000.0
+    if g.random() < 0.2 and (kw["n_q_heads"] * hd) % 64 == 0:
+        kw["weight_dtype"] = "fp8"
+    return small_cfg(name=f"encsweep{seed}", **kw), int(g.integers(1, 300)), int(g.integers(1, 5))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_encoder_sweep(seed):
+    import torch
+    import flow_matching_denoising_euler_amd as fm
+    cfg, n_tok, n_seq = _draw_encoder(seed)
+    cfg = cfg.replace(batch=n_seq)
+    announce(f"encoder sweep {seed}: {n_seq} x {n_tok} tokens, d {cfg.d_model}, {cfg.n_layers} layers, "
+             f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, {cfg.weight_dtype}, rope {cfg.rope_theta}")
+    Wp, tokens = S.make_prefix_stack(cfg, n_tok)
+    enc = fm.Encoder(cfg, Wp, n_tokens=n_tok, n_seqs=n_seq)
+    try:
+        k, v = enc.encode(tokens)
+        torch.cuda.synchronize()
+        k, v = k.float().cpu().numpy(), v.float().cpu().numpy()
+    finally:
+        enc.close()
+    W64 = O.effective_weights(cfg, {"layers": Wp["layers"]})
+    kr, vr = zip(*[O.prefix_stack_kv(cfg, W64, tokens[b]) for b in range(n_seq)])
+    tol = 5e-2 if cfg.weight_dtype == "fp8" else 1e-2
+    for name, got, ref in (("K", k, np.stack(kr)), ("V", v, np.stack(vr))):
+        rel = O.rel_l2(got, ref)
+        announce(f"  {name}: rel_l2 {rel:.3e}")
+        assert np.all(np.isfinite(got)) and rel <= tol, (name, rel)
