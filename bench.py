@@ -262,6 +262,8 @@ def main():
                     help="override the workload's sampler (Heun: two velocity evaluations per step)")
     ap.add_argument("--n-steps", type=int, default=None, help="override the workload's step count")
     ap.add_argument("--kv-fp8", action="store_true", help="hold the prefix K/V cache in fp8 E4M3 (per token and kv head scales)")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="quantise the per-layer matrices to fp8 E4M3 (per output row scales; bf16 activations)")
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
@@ -298,6 +300,11 @@ def main():
         cfg = cfg.replace(n_steps=args.n_steps)
     if args.kv_fp8:
         cfg = cfg.replace(kv_fp8=True)
+    base_weights = cfg.weight_dtype
+    if args.fp8_weights:
+        if cfg.act_dtype != "bf16":
+            raise SystemExit("--fp8-weights needs a workload with bf16 activations")
+        cfg = cfg.replace(weight_dtype="fp8")
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     log(f"bench: generating {cfg.name}")
@@ -367,16 +374,18 @@ def main():
     gu_flops = 2 * cfg.batch * cfg.suffix * 2 * cfg.d_mlp * cfg.d_model
     byts, flops = algorithmic(cfg, info)
     mfma_bound = cfg.batch * cfg.suffix * 2 > 312 * es  # arithmetic intensity above the bf16 ridge
+    # the committed counters were taken with the workload's own weight dtype
+    traffic = load_traffic(cfg.name) if cfg.weight_dtype == base_weights else None
     if mfma_bound:
         peak = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(cfg.name)}
+                "frac": round(achieved / peak, 4), "traffic": traffic}
         loop_roof_ms = flops / (peak * 1e12) * 1e3
     else:
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(cfg.name)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
         loop_roof_ms = byts / (HBM_PEAK_GBS * 1e9) * 1e3
     roof["kernel"] = "gate/up GEMM + GELU gate (one layer)"
     roof["per_launch"] = {"bytes": gu_bytes, "flops": gu_flops, "avg_us": round(gu_us, 3)}
@@ -410,7 +419,7 @@ def main():
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) prefix K/V and noise)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "chunk": cfg.chunk, "state_tokens": cfg.has_state,
                    "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps, "sampler": cfg.sampler,
-                   "kv_cache": "fp8-e4m3" if cfg.kv_fp8 else cfg.act_dtype,
+                   "kv_cache": "fp8-e4m3" if cfg.kv_fp8 else cfg.act_dtype, "weights": cfg.weight_dtype,
                    "d_model": cfg.d_model,
                    "layers": cfg.n_layers, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),

@@ -265,7 +265,7 @@ void derive(fm_ctx* x) {
   // K splits of the residual GEMMs: none on the large-M path
   x->ks_o = 1;
   x->ks_d = 1;
-  const bool large_m = x->wt == ELT_BF16 && big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh).used;
+  const bool large_m = x->wt != ELT_F32 && big_plan(EPI_RESID, x->M, x->d, x->Hq * x->Dh, x->wt == ELT_FP8).used;
   if (x->act == ELT_BF16 && !large_m) {
     // skinny residual GEMMs: split K so that about 256 workgroups each read a
     // quarter of the shared activation operand (it dominates their bytes)
@@ -981,8 +981,8 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
     info->n_phases = (x->heun ? 2 : 1) * x->N * (5 * x->L + 1) + 1;
   }
   {
-    const BigPlan pg = big_plan(EPI_GELU, x->M, 2 * x->F, x->d);
-    const bool big = x->act == ELT_BF16 && x->wt == ELT_BF16 && pg.used;
+    const BigPlan pg = big_plan(EPI_GELU, x->M, 2 * x->F, x->d, x->wt == ELT_FP8);
+    const bool big = x->act == ELT_BF16 && x->wt != ELT_F32 && pg.used;
     info->grid = big ? (x->M + pg.BM - 1) / pg.BM * (2 * x->F / pg.BN) : x->mtiles * (2 * x->F / 32);
   }
   info->n_cu = x->n_cu;

@@ -169,7 +169,7 @@ struct EmbedArgs {
   int B, S, C, A, SD, d, M, has_state, mtiles, esplit;
 };
 
-// Tile plan of the large-M GEMM (bf16 activations and weights): tiles of
+// Tile plan of the large-M GEMM (bf16 activations, bf16 or fp8 weights): tiles of
 // BM rows x BN packed columns, K split over ks workgroups (residual GEMMs
 // only, reduced by the last-arriving workgroup in a fixed order).  used =
 // false selects the skinny GEMM.
@@ -179,7 +179,7 @@ struct BigPlan {
   int BM, BN, kst;  // tile, k-blocks of 32 per LDS stage
 };
 constexpr int BIG_MID_ROWS = 512;  // below: the smaller tiles
-inline BigPlan big_plan(int epi, int M, int N, int K) {
+inline BigPlan big_plan(int epi, int M, int N, int K, bool wf8 = false) {
   // From 512 rows: gate/up 128 x 256 and QKV 128 x 64 (128-row tiles, like
   // the GEMMs that read their output), stages of 64 k; the residual GEMMs
   // (N = d_model) 64 x 64 with stages of 128 k (where K allows), which covers
@@ -191,6 +191,13 @@ inline BigPlan big_plan(int epi, int M, int N, int K) {
             mid ? (epi == EPI_GELU ? 128 : 32) : (epi == EPI_GELU ? 256 : 64), 2};
   if (M < 256 || K % 64 || N % p.BN) return p;
   if (epi == EPI_RESID && K % 128 == 0) p.kst = 4;
+  // fp8 weights: a 1 KB weight tile spans 64 k, and a stage's weight tiles
+  // split evenly over the waves only with stages of 128 k for the residual
+  // GEMMs and the mid QKV tiles
+  if (wf8 && (epi == EPI_RESID || (mid && epi != EPI_GELU))) {
+    if (K % 128) return p;
+    p.kst = 4;
+  }
   p.used = true;
   return p;
 }

@@ -652,16 +652,19 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
 // multiple of NW, loop index i < MB * KS / NW gives activations.  src[i] is
 // this lane's source of fragment i in the split's first stage; stage sc
 // (relative) adds sc * stride (A or W).
-template <int TMW, int TNW, int NW, int KS>
+// WF8: fp8 weights, whose 1 KB tiles hold two k-blocks (64 k) of 16 columns:
+// KW = KS / 2 weight tiles per column block and stage
+template <int TMW, int TNW, int NW, int KS, bool WF8 = false>
 struct BigSrc {
-  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, LPW = (MB + NBK) * KS / NW, LA = MB * KS / NW;
-  static_assert((MB * KS) % NW == 0 && (NBK * KS) % NW == 0, "fragments split evenly over the waves");
+  static constexpr int MB = 2 * TMW, NBK = 2 * TNW, KW = WF8 ? KS / 2 : KS;
+  static constexpr int LPW = (MB * KS + NBK * KW) / NW, LA = MB * KS / NW;
+  static_assert((MB * KS) % NW == 0 && (NBK * KW) % NW == 0 && KW >= 1, "fragments split evenly over the waves");
   const uint16_t* src[LPW];
   long stride_a, stride_w;  // elements per stage
   __device__ __forceinline__ BigSrc(const uint16_t* A, const uint16_t* W, int wave, int lane, int st0, int rb0,
                                     int nb0, int KB, int RB, int NBT) {
     stride_a = (long)KS * 4 * 512;
-    stride_w = (long)KS * NBT * 512;
+    stride_w = (long)KW * NBT * 512;  // 2-byte units: a 1 KB tile is 512 of them for bf16 and fp8 alike
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int f = wave + NW * i;
@@ -671,7 +674,7 @@ struct BigSrc {
         src[i] = A + ((((long)(rb >> 2) * KB + kb) * 4 + (rb & 3)) * 64 + lane) * 8;
       } else {
         const int ff = f - MB * KS, qk = ff / NBK, ni = ff % NBK;
-        src[i] = W + (((long)(st0 * KS + qk) * NBT + nb0 + ni) * 64 + lane) * 8;
+        src[i] = W + (((long)(st0 * KW + qk) * NBT + nb0 + ni) * 64 + lane) * 8;
       }
     }
   }
@@ -682,32 +685,38 @@ struct BigSrc {
   }
 };
 // The fragments of k-block qk of a stage for wave (wm, wn)
-template <int TMW, int TNW, int KS>
+template <int TMW, int TNW, int KS, bool WF8 = false>
 __device__ __forceinline__ void big_read(const uint8_t* base, int qk, uint4 (&af)[TMW], uint4 (&bf)[TNW], int wm,
                                          int wn, int lane) {
   constexpr int MB = 2 * TMW, NBK = 2 * TNW;
 #pragma unroll
   for (int mi = 0; mi < TMW; ++mi) af[mi] = *(const uint4*)(base + (qk * MB + wm * TMW + mi) * 1024 + lane * 16);
 #pragma unroll
-  for (int ni = 0; ni < TNW; ++ni)
-    bf[ni] = *(const uint4*)(base + (MB * KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
+  for (int ni = 0; ni < TNW; ++ni) {
+    if constexpr (WF8) {  // this k-block's half of the lane's 16 bytes, exactly to bf16
+      const uint2 r = *(const uint2*)(base + (MB * KS + (qk >> 1) * NBK + wn * TNW + ni) * 1024 + lane * 16 + (qk & 1) * 8);
+      bf[ni] = e4m3x8_to_bf16x8_hw(r.x, r.y);
+    } else {
+      bf[ni] = *(const uint4*)(base + (MB * KS + qk * NBK + wn * TNW + ni) * 1024 + lane * 16);
+    }
+  }
 }
 // acc[ni][mi] += W(column block) x A(row block)^T over the k-blocks of the
 // stage this wave takes: kg, kg + KG, ... (KG k-groups of waves share a
 // stage).  The fragments of the next k-block are read while the MFMAs of the
 // current one run; the scheduling barriers keep the reads ahead of the MFMAs.
-template <int TMW, int TNW, int KG, int KS>
+template <int TMW, int TNW, int KG, int KS, bool WF8 = false>
 __device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TNW][TMW], int kg, int wm, int wn,
                                             int lane) {
   constexpr int NQ = KS / KG;
   static_assert(KS % KG == 0, "k-blocks of a stage split evenly over the k-groups");
   uint4 af[2][TMW], bf[2][TNW];
-  big_read<TMW, TNW, KS>(base, kg, af[0], bf[0], wm, wn, lane);
+  big_read<TMW, TNW, KS, WF8>(base, kg, af[0], bf[0], wm, wn, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     if (q + 1 < NQ) {
-      big_read<TMW, TNW, KS>(base, kg + KG * (q + 1), af[(q + 1) & 1], bf[(q + 1) & 1], wm, wn, lane);
+      big_read<TMW, TNW, KS, WF8>(base, kg + KG * (q + 1), af[(q + 1) & 1], bf[(q + 1) & 1], wm, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -720,19 +729,20 @@ __device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TN
 // KG k-groups of 4 waves (KG = 2: 512 threads, two waves per SIMD to keep
 // more LDS reads in flight; the halves sum their accumulators through LDS in
 // a fixed order and each runs the epilogue of half the row blocks).
-template <int EPI, int TMW, int TNW, int KG, int KS>
+template <int EPI, int TMW, int TNW, int KG, int KS, bool WF8 = false>
 __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   constexpr int NT = 256 * KG, NW = 4 * KG;
   constexpr int MB = 2 * TMW, NBK = 2 * TNW;          // row / column blocks of the tile
   constexpr int BM = 16 * MB, BN = 16 * NBK;
-  constexpr int FPS = (MB + NBK) * KS;                // fragments per stage (KS k-blocks of 32)
-  constexpr int LPW = FPS / NW;                       // copies per wave per stage
+  constexpr int FPS = (MB + NBK) * KS;                // ring slot: fragments per stage (KS k-blocks of 32)
+  constexpr int LPW = BigSrc<TMW, TNW, NW, KS, WF8>::LPW;  // copies per wave per stage (fp8 weights: fewer)
   constexpr int TME = TMW / KG;                       // row blocks of this wave's epilogue
   static_assert(KG == 1 || (KG == 2 && TMW % 2 == 0), "k-groups: even row blocks");
   static_assert(BM * 8 % NT == 0, "norm-statistics pass");
   __shared__ __align__(16) uint8_t lds0[FPS * 1024], lds1[FPS * 1024], lds2[FPS * 1024];
   __shared__ float s_rstd[BM];
   __shared__ __align__(16) float s_col[2][BN];        // bias or alpha, gnext
+  __shared__ __align__(16) float s_ws[WF8 ? BN : 4];  // fp8 weights: the column scales
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: fragment choice and LDS address are scalar
   const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
@@ -750,9 +760,10 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   const uint16_t* W = (const uint16_t*)g.W;
 
   // epilogue column operands and the rows' norm statistics (issued first)
-  float cv0 = 0.f, cv1 = 0.f;
+  float cv0 = 0.f, cv1 = 0.f, cw = 1.f;
   if (tid < BN) {
     const int col = n0 + tid;
+    if constexpr (WF8) cw = g.wscale[col];
     cv0 = EPI == EPI_RESID ? g.alpha.base[(long)g.step * g.alpha.step_stride + col]
                            : g.bias.base[(long)g.step * g.bias.step_stride + col];
     cv1 = EPI == EPI_RESID ? g.gnext.base[(long)g.step * g.gnext.step_stride + col] : 0.f;
@@ -768,7 +779,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
       for (int i = 0; i < 4; ++i) q[i][rr] = p[i];
     }
   }
-  const BigSrc<TMW, TNW, NW, KS> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
+  const BigSrc<TMW, TNW, NW, KS, WF8> srcs(A, W, wave, lane, st0, rb0, nb0, KB, RB, NBT);
   const uint32_t a0 = lds_addr(lds0), a1 = lds_addr(lds1), a2 = lds_addr(lds2);
   // The workgroups of an XCD walk K together, so each k-slice of their
   // operands is fetched into that XCD's L2 once and only a few stages of it
@@ -791,18 +802,18 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
     wait_vmcnt<LPW>();
     barrier_nofence();
     srcs.issue(a2, wave, kst(s + 2));
-    big_compute<TMW, TNW, KG, KS>(lds0, acc, kg, wm, wn, lane);
+    big_compute<TMW, TNW, KG, KS, WF8>(lds0, acc, kg, wm, wn, lane);
     if (s + 1 < nstage) {
       wait_vmcnt<LPW>();
       barrier_nofence();
       srcs.issue(a0, wave, kst(s + 3));
-      big_compute<TMW, TNW, KG, KS>(lds1, acc, kg, wm, wn, lane);
+      big_compute<TMW, TNW, KG, KS, WF8>(lds1, acc, kg, wm, wn, lane);
     }
     if (s + 2 < nstage) {
       wait_vmcnt<LPW>();
       barrier_nofence();
       srcs.issue(a1, wave, kst(s + 4));
-      big_compute<TMW, TNW, KG, KS>(lds2, acc, kg, wm, wn, lane);
+      big_compute<TMW, TNW, KG, KS, WF8>(lds2, acc, kg, wm, wn, lane);
     }
   }
   wait_vmcnt<0>();  // the trailing reloads
@@ -847,6 +858,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   if (tid < BN) {
     s_col[0][tid] = cv0;
     s_col[1][tid] = cv1;
+    if constexpr (WF8) s_ws[tid] = cw;
   }
   if (EPI != EPI_RESID) {
 #pragma unroll
@@ -860,6 +872,19 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
     }
   }
   __syncthreads();
+  if constexpr (WF8) {  // per-column weight scales: acc over the fp8 codes times the column's scale
+#pragma unroll
+    for (int ni = 0; ni < TNW; ++ni) {
+      const float4 ws = *(const float4*)&s_ws[(wn * TNW + ni) * 16 + (lane >> 4) * 4];
+#pragma unroll
+      for (int m = 0; m < TME; ++m) {
+        fin[ni][m][0] *= ws.x;
+        fin[ni][m][1] *= ws.y;
+        fin[ni][m][2] *= ws.z;
+        fin[ni][m][3] *= ws.w;
+      }
+    }
+  }
 
   // epilogue: block (ni, m) of this lane = row m0 + (wm TMW + mb0 + m) 16 + (lane & 15),
   // columns n0 + (wn TNW + ni) 16 + (lane >> 4) 4 + [0, 4)
@@ -2139,25 +2164,27 @@ static hipError_t gemm_upw(const GemmArgs& g, int grid, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// large M, bf16: the LDS-staged MFMA GEMM (tile plan shared with the engine)
+// large M, bf16 activations: the LDS-staged MFMA GEMM (tile plan shared
+// with the engine); fp8 weights are widened to bf16 as they leave LDS
+template <bool WF8>
 static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err) {
-  const BigPlan p = big_plan(epi, g.M, g.N, g.K);
+  const BigPlan p = big_plan(epi, g.M, g.N, g.K, WF8);
   if (!p.used || g.ksplit != 1) return false;
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
   if (p.mid) {
-    if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 2, 4, 2, 2>), dim3(grid), dim3(512), 0, st, g);
-    else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
-    else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 2, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
-    else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 4>), dim3(grid), dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+    if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 2, 4, 2, 2, WF8>), dim3(grid), dim3(512), 0, st, g);
+    else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, 1, 1, WF8 ? 4 : 2, WF8>), dim3(grid), dim3(256), 0, st, g);
+    else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 2, 1, 1, WF8 ? 4 : 2, WF8>), dim3(grid), dim3(256), 0, st, g);
+    else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 4, WF8>), dim3(grid), dim3(256), 0, st, g);
+    else if constexpr (!WF8) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
     *err = hipGetLastError();
     return true;
   }
-  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2, 2>), dim3(grid), dim3(512), 0, st, g);
-  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, st, g);
-  else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, st, g);
-  else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 4>), dim3(grid), dim3(512), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
+  if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 4, 8, 2, 2, WF8>), dim3(grid), dim3(512), 0, st, g);
+  else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 4, 2, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);
+  else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 4, 2, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);
+  else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 4, WF8>), dim3(grid), dim3(512), 0, st, g);
+  else if constexpr (!WF8) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
   *err = hipGetLastError();
   return true;
 }
@@ -2165,9 +2192,9 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
 template <int ACT, int WT>
 static hipError_t gemm_dispatch(int epi, const GemmArgs& g, hipStream_t st) {
   const int nt = epi == EPI_GELU ? 32 : 16;
-  if constexpr (ACT == ELT_BF16 && WT == ELT_BF16) {
+  if constexpr (ACT == ELT_BF16 && WT != ELT_F32) {
     hipError_t e;
-    if (gemm_big(epi, g, st, &e)) return e;
+    if (gemm_big<WT == ELT_FP8>(epi, g, st, &e)) return e;
   }
   if (g.nt != nt || g.ksplit < 1 || g.ksplit > 4 || (g.ksplit != 1 && epi != EPI_RESID)) return hipErrorInvalidValue;
   if (((g.K >> 5) / (WT == ELT_FP8 ? 2 : 1)) % g.ksplit) return hipErrorInvalidValue;

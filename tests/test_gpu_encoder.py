@@ -64,6 +64,8 @@ def _wdtype(cfg):
     ("bf16 head_dim 256", dict(n_q_heads=2, head_dim=256, d_mlp=512), 256, 1),  # one 256-token frame
     ("bf16 head_dim 128, long", dict(head_dim=128), 1000, 1),          # 1000 tokens, largest key tile
     ("fp8", dict(weight_dtype="fp8"), 64, 2),
+    ("fp8 300 rows", dict(weight_dtype="fp8"), 150, 2),                 # fp8 weights, LDS-staged GEMMs, mid tiles
+    ("fp8 600 rows", dict(weight_dtype="fp8", n_q_heads=4, n_kv_heads=2), 300, 2),  # large tiles
 ])
 def test_encoder_kv_small(name, kw, n_tokens, n_seqs):
     cfg = S.workload("tiny_fp32") if kw is None else small_cfg(**kw)

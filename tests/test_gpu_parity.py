@@ -416,6 +416,31 @@ def test_full_pi05_ada_b16_kv_fp8_sampled_robots():
     check("pi05_ada_b16 kv_fp8 robots 0,9", got[robots], O.denoise(cfg, W, k, v, x0, st, robots=robots), 1e-2, 3e-2)
 
 
+# --- fp8 weights on the LDS-staged GEMMs (a few hundred rows and more) ----------------
+@pytest.mark.parametrize("kw", [
+    dict(batch=8, chunk=40),                                  # 328 rows: the mid tiles
+    dict(batch=8, chunk=40, d_mlp=320),                       # down projection K = 320: not a multiple of 128,
+                                                              # so that GEMM stays on the skinny kernel
+    dict(batch=14, chunk=40, n_q_heads=4, n_kv_heads=2),      # 574 rows: the large tiles
+    dict(batch=14, chunk=40, sampler="heun", norm="ada", time_dim=32),
+])
+def test_fp8_weights_many_rows(kw):
+    cfg = small_cfg(weight_dtype="fp8", **kw)
+    announce(f"fp8 weights, many rows {kw}")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    check(f"fp8 weights {kw}", got, O.denoise(cfg, W, k, v, x0, st), 5e-2)
+
+
+def test_full_pi05_ada_b16_fp8_weights_sampled_robots():
+    cfg = S.workload("pi05_ada_b16").replace(weight_dtype="fp8")
+    announce("pi05_ada_b16 fp8 weights")
+    W, k, v, x0, st = _inputs(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    robots = [0, 9]
+    check("pi05_ada_b16 fp8 weights robots 0,9", got[robots], O.denoise(cfg, W, k, v, x0, st, robots=robots), 5e-2)
+
+
 # --- rotary position embedding -------------------------------------------------------
 @pytest.mark.parametrize("kw", [
     dict(),                                                      # one row tile
