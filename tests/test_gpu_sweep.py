@@ -69,6 +69,55 @@ def test_sweep(seed):
     check(f"sweep {seed}", got, O.denoise(cfg, W, k, v, x0, st), tol, None if cfg.weight_dtype == "fp8" else 3e-2)
 
 
+def _draw_rows(seed):
+    """Batched configurations of 256-1024 rows: the LDS-staged GEMMs (mid and
+    large tile plans, ragged last row tiles), bf16 or fp8 weights."""
+    g = np.random.default_rng(3000 + seed)
+    hd = int(g.choice([64, 128, 256]))
+    hkv = int(g.choice([1, 2]))
+    hq = hkv * int(g.choice([1, 2, 4]))
+    while hq * hd > 1024:
+        hq //= 2
+    state = int(g.choice([0, 32]))
+    chunk = int(g.integers(24, 64))
+    per = chunk + (state > 0)
+    kw = dict(seed=seed, head_dim=hd, n_kv_heads=hkv, n_q_heads=max(hq, hkv), d_model=int(g.choice([128, 256])),
+              d_mlp=int(g.choice([256, 320, 512])), n_layers=int(g.integers(1, 3)), chunk=chunk,
+              batch=int(g.integers(-(-256 // per), 17)), state_dim=state, n_steps=int(g.integers(1, 5)),
+              action_dim=32)
+    kw["time_dim"] = kw["d_model"]
+    cap = int(g.integers(0, 300))
+    kw.update(prefix_static=cap, prefix_len=int(g.integers(0, cap + 1)))
+    if g.random() < 0.3:
+        kw.update(norm="ada", time_dim=32)
+    kw["sampler"] = str(g.choice(["euler", "heun", "ab2"]))
+    if state and g.random() < 0.3:
+        kw["state_causal"] = True
+    if g.random() < 0.3:
+        kw["rope_theta"] = 10000.0
+    if g.random() < 0.5:
+        kw["weight_dtype"] = "fp8"
+    elif g.random() < 0.3:
+        kw["kv_fp8"] = True
+    return small_cfg(name=f"rowsweep{seed}", **kw)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_rows_sweep(seed):
+    cfg = _draw_rows(seed)
+    rows = cfg.batch * (cfg.chunk + (cfg.state_dim > 0))
+    assert 256 <= rows <= 1024
+    announce(f"rows sweep {seed}: {rows} rows, batch {cfg.batch}, d {cfg.d_model}, mlp {cfg.d_mlp}, "
+             f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, {cfg.weight_dtype}, kv8 {cfg.kv_fp8}, "
+             f"{cfg.norm}, {cfg.sampler}, causal {cfg.state_causal}, rope {cfg.rope_theta}")
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    x0, st = S.make_noise(cfg), S.make_state(cfg)
+    got = run_denoiser(cfg, W, k, v, x0, st)[0]
+    fp8 = cfg.weight_dtype == "fp8"
+    check(f"rows sweep {seed}", got, O.denoise(cfg, W, k, v, x0, st), 5e-2 if fp8 else 1e-2, None if fp8 else 3e-2)
+
+
 def _draw_encoder(seed):
     g = np.random.default_rng(5000 + seed)
     hd = int(g.choice([32, 64, 128, 256]))
