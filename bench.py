@@ -290,6 +290,11 @@ def main():
     import flow_matching_denoising_euler_amd as fm
 
     cfg = S.workload(args.workload)
+    base_weights = cfg.weight_dtype
+    if args.fp8_weights:
+        if cfg.act_dtype != "bf16":
+            raise SystemExit("--fp8-weights needs a workload with bf16 activations")
+        cfg = cfg.replace(weight_dtype="fp8")
     if args.pipeline:
         return pipeline_bench(args, cfg)
     if args.encode:
@@ -300,11 +305,6 @@ def main():
         cfg = cfg.replace(n_steps=args.n_steps)
     if args.kv_fp8:
         cfg = cfg.replace(kv_fp8=True)
-    base_weights = cfg.weight_dtype
-    if args.fp8_weights:
-        if cfg.act_dtype != "bf16":
-            raise SystemExit("--fp8-weights needs a workload with bf16 activations")
-        cfg = cfg.replace(weight_dtype="fp8")
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     log(f"bench: generating {cfg.name}")
