@@ -279,7 +279,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the denoise loop shards by robot with no "
+        print("bench.py: the library runs on one GPU; the denoise loop shards by robot with no "
               "exchange, so there is no multi-GPU figure to measure (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
