@@ -425,6 +425,8 @@ def test_full_pi05_ada_b16_kv_fp8_sampled_robots():
     dict(batch=14, chunk=40, sampler="heun", norm="ada", time_dim=32),
     dict(batch=7, chunk=72),                                  # 511 rows: the last mid plan, a ragged last row tile
     dict(batch=16, chunk=31),                                 # 512 rows: the first large plan, whole tiles
+    dict(batch=8, chunk=40, n_q_heads=1, head_dim=64),        # O projection K = 64: the residual GEMMs stay
+                                                              # skinny, and the down projection splits K in 2
 ])
 def test_fp8_weights_many_rows(kw):
     cfg = small_cfg(weight_dtype="fp8", **kw)
