@@ -184,17 +184,17 @@ inline BigPlan big_plan(int epi, int M, int N, int K, bool wf8 = false) {
   // the GEMMs that read their output), stages of 64 k; the residual GEMMs
   // (N = d_model) 64 x 64 with stages of 128 k (where K allows), which covers
   // the CUs without splitting K.  From 256 to 511 rows (one prefix frame, a
-  // few robots): gate/up 64 x 128, QKV 64 x 32, residual 32 x 32, so that a
-  // launch still has about one workgroup per CU.
+  // few robots): gate/up 64 x 128, QKV 64 x 32 (fp8 weights: 64 x 64),
+  // residual 32 x 32, so that a launch still has about one workgroup per CU.
   const bool mid = M < BIG_MID_ROWS;
   BigPlan p{false, mid, mid ? (epi == EPI_RESID ? 32 : 64) : (epi == EPI_RESID ? 64 : 128),
-            mid ? (epi == EPI_GELU ? 128 : 32) : (epi == EPI_GELU ? 256 : 64), 2};
+            mid ? (epi == EPI_GELU ? 128 : (wf8 && epi != EPI_RESID ? 64 : 32)) : (epi == EPI_GELU ? 256 : 64), 2};
   if (M < 256 || K % 64 || N % p.BN) return p;
   if (epi == EPI_RESID && K % 128 == 0) p.kst = 4;
   // fp8 weights: a 1 KB weight tile spans 64 k, and a stage's weight tiles
-  // split evenly over the waves only with stages of 128 k for the residual
-  // GEMMs and the mid QKV tiles
-  if (wf8 && (epi == EPI_RESID || (mid && epi != EPI_GELU))) {
+  // split evenly over the waves of the residual tiles only with stages of
+  // 128 k
+  if (wf8 && epi == EPI_RESID) {
     if (K % 128) return p;
     p.kst = 4;
   }

@@ -2173,8 +2173,8 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
   if (p.mid) {
     if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 2, 4, 2, 2, WF8>), dim3(grid), dim3(512), 0, st, g);
-    else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, 1, 1, WF8 ? 4 : 2, WF8>), dim3(grid), dim3(256), 0, st, g);
-    else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 2, 1, 1, WF8 ? 4 : 2, WF8>), dim3(grid), dim3(256), 0, st, g);
+    else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, WF8 ? 2 : 1, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);
+    else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 2, WF8 ? 2 : 1, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);
     else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 4, WF8>), dim3(grid), dim3(256), 0, st, g);
     else if constexpr (!WF8) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
     *err = hipGetLastError();
