@@ -374,8 +374,8 @@ def main():
     gu_flops = 2 * cfg.batch * cfg.suffix * 2 * cfg.d_mlp * cfg.d_model
     byts, flops = algorithmic(cfg, info)
     mfma_bound = cfg.batch * cfg.suffix * 2 > 312 * es  # arithmetic intensity above the bf16 ridge
-    # the committed counters were taken with the workload's own weight dtype
-    traffic = load_traffic(cfg.name) if cfg.weight_dtype == base_weights else None
+    # committed counters: per workload, and per weight dtype where it was overridden
+    traffic = load_traffic(cfg.name if cfg.weight_dtype == base_weights else f"{cfg.name}_{cfg.weight_dtype}_weights")
     if mfma_bound:
         peak = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
