@@ -2177,6 +2177,10 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
     else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 2, WF8 ? 2 : 1, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);
     else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 4, WF8>), dim3(grid), dim3(256), 0, st, g);
     else if constexpr (!WF8) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 1, 1, 1, 2>), dim3(grid), dim3(256), 0, st, g);
+    else {  // fp8 residual tiles run 128-k stages only (big_plan)
+      *err = hipErrorInvalidValue;
+      return true;
+    }
     *err = hipGetLastError();
     return true;
   }
@@ -2185,6 +2189,10 @@ static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err
   else if (epi == EPI_QKVR) hipLaunchKernelGGL((k_gemm_big<EPI_QKVR, 4, 2, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);
   else if (p.kst == 4) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 4, WF8>), dim3(grid), dim3(512), 0, st, g);
   else if constexpr (!WF8) hipLaunchKernelGGL((k_gemm_big<EPI_RESID, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, st, g);
+  else {
+    *err = hipErrorInvalidValue;
+    return true;
+  }
   *err = hipGetLastError();
   return true;
 }
