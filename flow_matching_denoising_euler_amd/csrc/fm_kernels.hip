@@ -41,10 +41,13 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 // small helpers
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest even (finite inputs)
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// fp32 -> bf16 bits, round to nearest even: one v_cvt_pk_bf16_f32 (gfx950)
+// for two values, where the bit-level rounding takes five instructions each
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <int ACT>
@@ -108,7 +111,6 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // OCP E4M3, two codes a call; scale 1: every E4M3 value is a bf16 value, the
 // result is exact); four instructions where the bit-level decode above needs
 // about a dozen per code (it took the batch-1 fp8 loop from 7.45 to 8.23 ms)
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8_hw(uint32_t lo, uint32_t hi) {
   return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
@@ -636,7 +638,7 @@ __device__ __forceinline__ float2 ld_dev2(const float* p) {
   return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
 }
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-  return make_uint2(f2bf(a) | (f2bf(b) << 16), f2bf(c) | (f2bf(d) << 16));
+  return make_uint2(f2bf2(a, b), f2bf2(c, d));
 }
 
 // Copies of one stage (KS k-blocks) by the NW waves of a workgroup.
