@@ -36,6 +36,38 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _stream_obj(stream, device):
+    """The torch stream object of `stream` (None: the current stream of
+    `device`; an int: an external hipStream_t handle)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def stream_enter(ctx_stream, cur_stream):
+    """Before a library call on a context bound to `ctx_stream`: if the
+    caller's current stream differs, the context's stream waits for the
+    work already queued on it (the host-to-device copies and casts of the
+    call's inputs)."""
+    if cur_stream != ctx_stream:
+        ctx_stream.wait_stream(cur_stream)
+
+
+def stream_leave(ctx_stream, cur_stream, temps):
+    """After the call: tensors made on `cur_stream` and read by the library
+    on `ctx_stream` are recorded on it (the caching allocator then keeps
+    their memory until that stream's work is done), and the caller's stream
+    waits for the library's results."""
+    if cur_stream != ctx_stream:
+        for t in temps:
+            if t is not None:
+                t.record_stream(ctx_stream)
+        cur_stream.wait_stream(ctx_stream)
+
+
 _DT = {"f32": _abi.FM_F32, "bf16": _abi.FM_BF16, "fp8": _abi.FM_FP8_E4M3}
 
 
@@ -205,11 +237,21 @@ class _Context:
     """Owns one library context (released by close() or on collection)."""
     ctx = None
 
-    def _setup(self, cfg, device):
+    def _setup(self, cfg, device, stream):
         import torch
         self.cfg = cfg
         self.device = device
         self.act_dtype = torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16
+        self.stream = _stream_obj(stream, device)  # the stream the context enqueues on
+
+    def _call(self, fn, temps):
+        """Run one library call with the inputs `temps` (made on the caller's
+        current stream) safely on the context's stream."""
+        import torch
+        cur = torch.cuda.current_stream(self.device)
+        stream_enter(self.stream, cur)
+        fn()
+        stream_leave(self.stream, cur, temps)
 
     def _act(self, a):
         return _dev_tensor(a, self.act_dtype, self.device)
@@ -233,23 +275,23 @@ class Denoiser(_Context):
     """Owns one context: load the prefix, then call `denoise` per chunk."""
 
     def __init__(self, cfg, weights: dict, stream=None, exec_mode: int = FM_EXEC_AUTO, device="cuda"):
-        self._setup(cfg, device)
-        self.ctx = fm_create(cfg, weights, stream, exec_mode, device)
+        self._setup(cfg, device, stream)
+        self.ctx = fm_create(cfg, weights, self.stream, exec_mode, device)
 
     def set_prefix_kv(self, robot: int, k, v):
         """k, v [layers][tokens][kv_heads][head_dim] (host or device)."""
         k, v = self._act(k), self._act(v)
-        fm_set_prefix_kv(self.ctx, robot, k, v, k.shape[1])
-        return k, v  # caller keeps them alive until the stream has consumed them
+        self._call(lambda: fm_set_prefix_kv(self.ctx, robot, k, v, k.shape[1]), (k, v))
+        return k, v
 
     def append_prefix_kv(self, robot: int, k_frame, v_frame):
         k, v = self._act(k_frame), self._act(v_frame)
-        fm_append_prefix_kv(self.ctx, robot, k, v)
+        self._call(lambda: fm_append_prefix_kv(self.ctx, robot, k, v), (k, v))
         return k, v
 
     def append_encoded(self, robot: int, encoder, seq: int = 0):
         """Append sequence `seq` of `encoder`'s latest output (see fm_append_encoded)."""
-        fm_append_encoded(self.ctx, robot, encoder.ctx, seq)
+        self._call(lambda: fm_append_encoded(self.ctx, robot, encoder.ctx, seq), ())
 
     def denoise(self, noise, state=None, out=None):
         import torch
@@ -257,7 +299,7 @@ class Denoiser(_Context):
         s = self._act(state) if state is not None else None
         if out is None:
             out = torch.empty_like(n)
-        fm_denoise(self.ctx, n, s, out)
+        self._call(lambda: fm_denoise(self.ctx, n, s, out), (n, s, out))
         return out
 
 
@@ -267,9 +309,9 @@ class Encoder(_Context):
 
     def __init__(self, cfg, weights: dict, n_tokens: int, n_seqs: int = 1, stream=None,
                  exec_mode: int = FM_EXEC_AUTO, device="cuda"):
-        self._setup(cfg, device)
+        self._setup(cfg, device, stream)
         self.n_tokens, self.n_seqs = int(n_tokens), int(n_seqs)
-        self.ctx = fm_encoder_create(cfg, weights, n_tokens, n_seqs, stream, exec_mode, device)
+        self.ctx = fm_encoder_create(cfg, weights, n_tokens, n_seqs, self.stream, exec_mode, device)
 
     def encode(self, tokens, k_out=None, v_out=None):
         """tokens [seqs][tokens][d_model] (host or device) -> (k, v) device
@@ -281,8 +323,7 @@ class Encoder(_Context):
             k_out = torch.empty(shape, dtype=self.act_dtype, device=self.device)
         if v_out is None:
             v_out = torch.empty(shape, dtype=self.act_dtype, device=self.device)
-        fm_encode_prefix(self.ctx, t, k_out, v_out)
-        self._tokens = t  # alive until the next call
+        self._call(lambda: fm_encode_prefix(self.ctx, t, k_out, v_out), (t, k_out, v_out))
         return k_out, v_out
 
     def encode_in_place(self, tokens):
@@ -290,5 +331,4 @@ class Encoder(_Context):
         for Denoiser.append_encoded (the async-pipeline hand-off)."""
         import torch
         t = _dev_tensor(tokens, torch.float32, self.device)
-        fm_encode_prefix(self.ctx, t)
-        self._tokens = t
+        self._call(lambda: fm_encode_prefix(self.ctx, t), (t,))

@@ -156,3 +156,45 @@ def test_encoder_null_calls_fail_cleanly():
     assert L.fm_encoder_create(None, None, None, None) == _abi.FM_ERR_ARG
     assert L.fm_encode_prefix(None, None, None, None) == _abi.FM_ERR_ARG
     assert L.fm_append_encoded(None, 0, None, 0) == _abi.FM_ERR_ARG
+
+
+class _FakeStream:
+    """Stand-in for a torch stream: records the waits it is asked for."""
+
+    def __init__(self, name):
+        self.name, self.waited_on = name, []
+
+    def wait_stream(self, other):
+        self.waited_on.append(other.name)
+
+
+class _FakeTensor:
+    def __init__(self):
+        self.recorded = []
+
+    def record_stream(self, s):
+        self.recorded.append(s.name)
+
+
+def test_binding_stream_guard_orders_a_foreign_current_stream():
+    # the context enqueues on its own stream; inputs made on another current
+    # stream must be complete before the call (ctx waits on it), must stay
+    # allocated until the context's stream is done (record_stream), and the
+    # caller's stream must see the outputs (it waits on the context's stream)
+    ctx, cur = _FakeStream("ctx"), _FakeStream("cur")
+    temps = [_FakeTensor(), None, _FakeTensor()]
+    fm.stream_enter(ctx, cur)
+    assert ctx.waited_on == ["cur"]
+    fm.stream_leave(ctx, cur, temps)
+    assert temps[0].recorded == ["ctx"] and temps[2].recorded == ["ctx"]
+    assert cur.waited_on == ["ctx"]
+
+
+def test_binding_stream_guard_is_a_no_op_on_the_context_stream():
+    # same stream: the stream order alone serialises the copies, the call and
+    # the allocator's reuse of the temporaries
+    ctx = _FakeStream("ctx")
+    t = _FakeTensor()
+    fm.stream_enter(ctx, ctx)
+    fm.stream_leave(ctx, ctx, [t])
+    assert ctx.waited_on == [] and t.recorded == []

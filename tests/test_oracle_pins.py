@@ -467,6 +467,196 @@ def test_ada_gamma_minus_one_and_alpha_zero():
     assert np.max(np.abs(got - (x0 - vel))) < 1e-13
 
 
+# --- P9b: the AdaRMSNorm time MLP, written out in scalars ----------------------------
+def _silu_s(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def _tau_s(t, dim):
+    half = dim // 2
+    w = [10000.0 ** (-j / half) for j in range(half)]
+    return [math.sin(t * wj) for wj in w] + [math.cos(t * wj) for wj in w]
+
+
+def _mv_s(W, x, b=None):
+    """y_o = sum_i W[o][i] x[i] (+ b_o), exactly rounded sums."""
+    W = np.asarray(W, np.float64)
+    return [math.fsum(float(W[o, i]) * x[i] for i in range(len(x))) + (0.0 if b is None else float(b[o]))
+            for o in range(W.shape[0])]
+
+
+def _time_c_s(W, t, time_dim):
+    # c = SiLU(W_t tau(t) + b_t): the flow-phase embedding every norm reads
+    return [_silu_s(z) for z in _mv_s(W["w_time"], _tau_s(t, time_dim), W["b_time"])]
+
+
+def test_ada_modulation_matches_scalar_time_mlp():
+    # every norm's (gamma, beta, alpha) = split3(W_n c + b_n) with
+    # c = SiLU(W_t tau_time_dim(t) + b_t), per layer (norm1, norm2) then final
+    cfg = _ada_cfg()
+    W = S.make_weights(cfg)
+    d = cfg.d_model
+    for t in (1.0, 0.3):
+        per_layer, fin = O.ada_modulation(cfg, O.effective_weights(cfg, W), t)
+        c = _time_c_s(W, t, cfg.time_dim)
+        want = [[_mv_s(L[n + "_w"], c, L[n + "_b"]) for n in ("norm1", "norm2")] for L in W["layers"]]
+        for li, (m1, m2) in enumerate(per_layer):
+            for got, ref in ((m1, want[li][0]), (m2, want[li][1])):
+                for part in range(3):
+                    assert np.max(np.abs(got[part] - np.array(ref[part * d:(part + 1) * d]))) < 1e-12
+        ref_f = _mv_s(W["norm_f_w"], c, W["norm_f_b"])
+        for part in range(3):
+            assert np.max(np.abs(fin[part] - np.array(ref_f[part * d:(part + 1) * d]))) < 1e-12
+
+
+def test_ada_time_mlp_through_the_final_norm_closed_form():
+    # Every block is the identity (all per-layer modulations zero, so alpha =
+    # 0); the final norm is modulated by the flow phase: v = (rms(h0) (1 +
+    # gamma_f(t)) + beta_f(t)) W_out^T + b_out with h0 = x W_in^T + b_in.  The
+    # whole loop is rewritten here in scalars; a dropped SiLU, tau(1 - t), a
+    # swapped (gamma, beta) split or a missing (1 + .) all change x_N.
+    cfg = _ada_cfg()
+    W = S.make_weights(cfg)
+    k, v = S.make_prefix(cfg)
+    x0, st = S.make_noise(cfg), S.make_state(cfg)
+    d, A = cfg.d_model, cfg.action_dim
+    for L in W["layers"]:
+        for n in ("norm1", "norm2"):
+            L[n + "_w"][:] = 0
+            L[n + "_b"][:] = 0
+    got = O.denoise(cfg, W, k, v, x0, st)[0]
+    x = [[float(a) for a in row] for row in x0[0]]
+    for kstep in range(cfg.n_steps):
+        t = 1.0 - kstep / cfg.n_steps
+        m = _mv_s(W["norm_f_w"], _time_c_s(W, t, cfg.time_dim), W["norm_f_b"])
+        gam, bet = m[:d], m[d:2 * d]
+        new = []
+        for row in x:
+            h = _mv_s(W["w_in"], row, W["b_in"])
+            r = 1.0 / math.sqrt(math.fsum(a * a for a in h) / d + cfg.rms_eps)
+            u = [h[i] * r * (1.0 + gam[i]) + bet[i] for i in range(d)]
+            vel = _mv_s(W["w_out"], u, W["b_out"])
+            new.append([row[a] + (-1.0 / cfg.n_steps) * vel[a] for a in range(A)])
+        x = new
+    assert np.max(np.abs(got - np.array(x))) < 1e-11
+
+
+def test_ada_constant_modulation_is_rms_expert_with_gains_and_gates():
+    # W_n = 0, b_n = [g - 1 | 0 | a]: each norm is an RMSNorm with gain g and
+    # its residual branch is gated by a, which equals scaling the output rows
+    # of W_o (norm1's gate) or W_d (norm2's gate).  Distinct gains and gates per
+    # layer and per norm tell norm1 from norm2 and the two gates apart.
+    cfg_a = _ada_cfg()
+    cfg_r = TINY
+    Wa = S.make_weights(cfg_a)
+    k, v = S.make_prefix(cfg_a)
+    x0, st = S.make_noise(cfg_a), S.make_state(cfg_a)
+    d = cfg_a.d_model
+    g = np.random.default_rng(21)
+    gains = {}
+    for li, L in enumerate(Wa["layers"]):
+        for n in ("norm1", "norm2"):
+            gain, gate = 1.0 + 0.3 * g.standard_normal(d), 0.5 + g.random(d)
+            gains[(li, n)] = (gain, gate)
+            L[n + "_w"][:] = 0
+            L[n + "_b"] = np.concatenate([gain - 1.0, np.zeros(d), gate])
+    gain_f = 1.0 + 0.3 * g.standard_normal(d)
+    Wa["norm_f_w"][:] = 0
+    Wa["norm_f_b"] = np.concatenate([gain_f - 1.0, np.zeros(d), g.random(d)])
+    t = 0.4
+    Wr = {kk: vv for kk, vv in Wa.items() if not kk.startswith(("norm_f", "w_time", "b_time"))}
+    Wr["b_in"] = Wa["b_in"] - O.sinusoid(t, d)  # cancel the additive time feature at t
+    Wr["norm_f"] = gain_f
+    Wr["layers"] = []
+    for li, L in enumerate(Wa["layers"]):
+        (g1, a1), (g2, a2) = gains[(li, "norm1")], gains[(li, "norm2")]
+        Wr["layers"].append(dict(wq=L["wq"], wk=L["wk"], wv=L["wv"], wg=L["wg"], wu=L["wu"],
+                                 wo=a1[:, None] * L["wo"].astype(np.float64),
+                                 wd=a2[:, None] * L["wd"].astype(np.float64), norm1=g1, norm2=g2))
+    Wa64, Wr64 = O.effective_weights(cfg_a, Wa), O.effective_weights(cfg_r, Wr)
+    va = O.expert_velocity(cfg_a, Wa64, x0[0], t, k[0], v[0], st[0])
+    vr = O.expert_velocity(cfg_r, Wr64, x0[0], t, k[0], v[0], st[0])
+    assert O.rel_l2(va, vr) < 1e-13
+    # the gates matter: equal gates give a different velocity
+    Wr["layers"][0]["wo"] = Wa["layers"][0]["wo"]
+    vr2 = O.expert_velocity(cfg_r, O.effective_weights(cfg_r, Wr), x0[0], t, k[0], v[0], st[0])
+    assert O.rel_l2(va, vr2) > 1e-4
+
+
+# --- P7b: the prefix stack, element by element ------------------------------------------
+def _prefix_stack_scalar(cfg, Wp, tokens, theta=0.0):
+    """The prefix encoder written out with scalar loops: per layer RMSNorm ->
+    q, k, v -> (rotary positions) -> attention over the sequence -> O +
+    residual -> RMSNorm -> GELU(gate) * up -> down + residual.  Returns the
+    per-layer K and V (K unrotated)."""
+    d, hq, hkv, dh = cfg.d_model, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    T = tokens.shape[0]
+    h = [[float(a) for a in row] for row in tokens]
+
+    def rms(row, gain):
+        r = 1.0 / math.sqrt(math.fsum(a * a for a in row) / d + cfg.rms_eps)
+        return [row[i] * r * float(gain[i]) for i in range(d)]
+
+    def rot(vec, pos):
+        if not theta:
+            return vec
+        half = dh // 2
+        out = list(vec)
+        for i in range(half):
+            a = pos * theta ** (-2.0 * i / dh)
+            out[i] = vec[i] * math.cos(a) - vec[i + half] * math.sin(a)
+            out[i + half] = vec[i + half] * math.cos(a) + vec[i] * math.sin(a)
+        return out
+
+    def gelu_s(z):
+        return 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
+
+    Ks, Vs = [], []
+    for L in Wp["layers"]:
+        u = [rms(h[t], L["norm1"]) for t in range(T)]
+        q = [_mv_s(L["wq"], u[t]) for t in range(T)]
+        k = [_mv_s(L["wk"], u[t]) for t in range(T)]
+        v = [_mv_s(L["wv"], u[t]) for t in range(T)]
+        Ks.append([[k[t][j * dh:(j + 1) * dh] for j in range(hkv)] for t in range(T)])
+        Vs.append([[v[t][j * dh:(j + 1) * dh] for j in range(hkv)] for t in range(T)])
+        o = [[0.0] * (hq * dh) for _ in range(T)]
+        for t in range(T):
+            for hh in range(hq):
+                j = hh * hkv // hq
+                qv = rot(q[t][hh * dh:(hh + 1) * dh], t)
+                s = [math.fsum(a * b for a, b in zip(qv, rot(k[p][j * dh:(j + 1) * dh], p))) / math.sqrt(dh)
+                     for p in range(T)]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                z = math.fsum(e)
+                for c in range(dh):
+                    o[t][hh * dh + c] = math.fsum(e[p] / z * v[p][j * dh + c] for p in range(T))
+        for t in range(T):
+            att = _mv_s(L["wo"], o[t])
+            h[t] = [h[t][i] + att[i] for i in range(d)]
+            u2 = rms(h[t], L["norm2"])
+            gte, up = _mv_s(L["wg"], u2), _mv_s(L["wu"], u2)
+            mlp = _mv_s(L["wd"], [gelu_s(a) * b for a, b in zip(gte, up)])
+            h[t] = [h[t][i] + mlp[i] for i in range(d)]
+    return np.array(Ks), np.array(Vs)
+
+
+@pytest.mark.parametrize("theta", [0.0, 100.0])
+def test_prefix_stack_matches_scalar_loops(theta):
+    # three layers, so that the first layer's attention + MLP body reaches the
+    # K/V of the later ones (norm2 in place of norm1, a dropped residual or the
+    # GELU on the wrong branch all change them); GQA with two query heads per
+    # kv head
+    cfg = _tiny(d_model=8, n_layers=3, n_q_heads=4, n_kv_heads=2, head_dim=4, d_mlp=12,
+                rope_theta=theta)
+    Wp, tokens = S.make_prefix_stack(cfg, 3)
+    k, v = O.prefix_stack_kv(cfg, Wp, tokens[0])
+    ks, vs = _prefix_stack_scalar(cfg, Wp, tokens[0], theta)
+    assert k.shape == ks.shape == (3, 3, 2, 4)
+    assert np.max(np.abs(k - ks)) < 1e-12 and np.max(np.abs(v - vs)) < 1e-12
+    assert np.max(np.abs(k[2] - k[1])) > 1e-3  # the layers differ
+
+
 # --- P12: robots are independent ------------------------------------------------
 def test_batch_independence():
     cfg = _tiny(batch=3)
