@@ -52,49 +52,142 @@ def algorithmic(cfg, info):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("fm_kernels.hip", "fm_internal.h", "fm_engine.cpp"):
+    for f in sorted(os.listdir(os.path.join(ROOT, "flow_matching_denoising_euler_amd", "csrc"))):
         with open(os.path.join(ROOT, "flow_matching_denoising_euler_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """HBM bytes per launch of the dominant kernel from the committed PMC
-    summary, if it was taken on the current kernel sources."""
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary of
+    `workload`, if it was taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    return t.get("traffic_bytes") if t.get("source_sha") == kernel_source_sha() else None
+    if t.get("source_sha") != kernel_source_sha() or t.get("phase") != kernel:
+        return None
+    return t.get("traffic_bytes")
 
 
-def cpu_baseline(cfg, W, k, v, x0, st, budget_s):
-    """The fp64 oracle as it stands, on this host's cores, on a bounded sample."""
+PHASE_NAMES = ["QKV GEMM (norm1 folded)", "attention", "O GEMM + residual", "gate/up GEMM + GELU gate",
+               "down GEMM + residual", "tail (final norm, head, update, next embedding)"]
+
+
+def phase_work(cfg, info, ph):
+    """Algorithmic bytes and flops of one launch of phase `ph`: its weight
+    matrix streamed once (fp8: codes and per-column scales), the prefix K/V
+    of one layer read once (attention), and 2 flops per multiply-add."""
+    d, L, F, Hq, Hkv, Dh, A = (cfg.d_model, cfg.n_layers, cfg.d_mlp, cfg.n_q_heads, cfg.n_kv_heads,
+                               cfg.head_dim, cfg.action_dim)
+    M = cfg.batch * cfg.suffix
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+    sc = 4 if cfg.weight_dtype == "fp8" else 0  # fp32 scale per output column
+    eg = 4 if cfg.act_dtype == "f32" else 2
+    nq = (Hq + 2 * Hkv) * Dh
+    if ph == 0:
+        return nq * d * es + nq * sc, 2 * M * d * nq
+    if ph == 1:
+        T = cfg.prefix_len
+        return info.kv_bytes_per_step // L, 4 * cfg.batch * cfg.suffix * Hq * Dh * (T + cfg.suffix)
+    if ph == 2:
+        return d * Hq * Dh * es + d * sc, 2 * M * Hq * Dh * d
+    if ph == 3:
+        return 2 * F * d * es + 2 * F * sc, 2 * M * d * 2 * F
+    if ph == 4:
+        return d * F * es + d * sc, 2 * M * F * d
+    return (2 * A * d + d) * eg, 2 * 2 * cfg.batch * cfg.chunk * d * A
+
+
+def roofline_of(byts, flops, us, peak_f):
+    """The roofline a launch of `byts` / `flops` in `us` sits under: the
+    binding one of HBM (8 TB/s) and the MFMA peak of its dtype."""
+    t_b, t_f = byts / (HBM_PEAK_GBS * 1e9), flops / (peak_f * 1e12)
+    if t_f > t_b:
+        a = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": peak_f, "unit": "TFLOP/s", "frac": round(a / peak_f, 4)}
+    a = byts / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4)}
+
+
+def phase_table(fm, den, cfg, info, stream, persistent, chunk_ms):
+    """Average duration of every phase kernel, timed with HIP events on the
+    context's stream over back-to-back launches through fm_launch_phase
+    (cycling layers and steps), its launches per chunk, and its roofline."""
+    import torch
+    peak_f = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS
+    evals = cfg.n_steps * (2 if cfg.sampler == "heun" else 1)
+    out = {}
+    for ph in range(6):
+        reps = 4 * cfg.n_layers if ph < 5 else 4 * cfg.n_steps
+        fm.fm_launch_phase(den.ctx, 0, 0, ph)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fm.fm_launch_phase(den.ctx, i % cfg.n_steps, i % cfg.n_layers, ph)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        byts, flops = phase_work(cfg, info, ph)
+        n = evals * cfg.n_layers if ph < 5 else evals
+        out[PHASE_NAMES[ph]] = {"per_launch": {"bytes": int(byts), "flops": int(flops), "avg_us": round(us, 3)},
+                                "launches_per_chunk": n, "per_chunk_ms": round(us * n / 1e3, 4),
+                                "roofline": roofline_of(byts, flops, us, peak_f)}
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, W, k, v, x0, st, runs=3):
+    """The fp64 oracle as it stands, on this host's cores, on a bounded sample:
+    one warmup, then the median of `runs` single-robot chunks (all robots are
+    independent, so a batch costs batch x one robot); and on one thread the
+    median of `runs` single velocity evaluations, scaled to the chunk's
+    evaluations (the loop's cost is linear in them)."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
     W64 = O.effective_weights(cfg, W)
-    times = []
-    t_start = time.perf_counter()
-    tick = 0
-    while True:
-        b = tick % cfg.batch
+    stb = lambda b: None if st is None else st[b]
+
+    def chunk(b):
         t0 = time.perf_counter()
-        O.denoise_robot(cfg, W64, k[b], v[b], x0[b], None if st is None else st[b])
-        times.append(time.perf_counter() - t0)
-        tick += 1
-        if time.perf_counter() - t_start > budget_s or tick >= 5:
-            break
+        O.denoise_robot(cfg, W64, k[b], v[b], x0[b], stb(b))
+        return time.perf_counter() - t0
+
+    def one_eval(b):
+        t0 = time.perf_counter()
+        O.expert_velocity(cfg, W64, np.asarray(x0[b], np.float64), 1.0, k[b], v[b], stb(b))
+        return time.perf_counter() - t0
+
+    chunk(0)  # warmup
+    times = [chunk(i % cfg.batch) for i in range(runs)]
+    evals = cfg.n_steps * (2 if cfg.sampler == "heun" else 1)
+    with threadpool_limits(1):
+        one_eval(0)
+        t1 = [one_eval(i % cfg.batch) for i in range(runs)]
     per_robot_ms = statistics.median(times) * 1e3
-    return {"value": per_robot_ms * cfg.batch, "unit": "ms per action chunk (all robots)",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} single-robot chunks of {cfg.name} (fp64 NumPy, median), "
-                      f"scaled x{cfg.batch} robots"}
+    return {"value": round(per_robot_ms * cfg.batch, 2), "unit": "ms per action chunk (all robots)",
+            "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"fp64 NumPy oracle: 1 warmup + median of {runs} single-robot chunks of {cfg.name} "
+                      f"({evals} velocity evaluations each) on {threads} threads, scaled x{cfg.batch} robots",
+            "one_thread": {"value": round(statistics.median(t1) * 1e3 * evals * cfg.batch, 2),
+                           "unit": "ms per action chunk (all robots)", "cores": 1,
+                           "sample": f"median of {runs} single velocity evaluations on 1 thread after 1 warmup, "
+                                     f"scaled x{evals} evaluations x{cfg.batch} robots"}}
 
 
 def encode_bench(args, cfg):
@@ -255,7 +348,8 @@ def pipeline_bench(args, cfg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; a streaming workload: all of its ticks)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi0_1view")
     ap.add_argument("--sampler", choices=("euler", "heun", "ab2"), default=None,
@@ -266,7 +360,6 @@ def main():
                     help="quantise the per-layer matrices to fp8 E4M3 (per output row scales; bf16 activations)")
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 256 MiB device copy (reference for PMC byte counters)")
     ap.add_argument("--pipeline", action="store_true",
@@ -295,6 +388,8 @@ def main():
         if cfg.act_dtype != "bf16":
             raise SystemExit("--fp8-weights needs a workload with bf16 activations")
         cfg = cfg.replace(weight_dtype="fp8")
+    if args.steps is None:
+        args.steps = cfg.ticks if cfg.ticks > 0 and not (args.pipeline or args.encode) else 200
     if args.pipeline:
         return pipeline_bench(args, cfg)
     if args.encode:
@@ -358,38 +453,23 @@ def main():
     pct = lambda p: per[min(len(per) - 1, int(p * len(per)))]
     log(f"bench: {ms:.4f} ms/chunk (p10 {pct(.1):.4f} p50 {pct(.5):.4f} p90 {pct(.9):.4f} p99 {pct(.99):.4f})")
 
-    # dominant kernel: the gate/up GEMM (largest weight stream per launch)
-    fm.fm_launch_phase(den.ctx, 0, 0, fm._abi.FM_PHASE_GATEUP)
-    reps = 200
-    torch.cuda.synchronize()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record(stream)
-    for i in range(reps):
-        fm.fm_launch_phase(den.ctx, i % cfg.n_steps, i % cfg.n_layers, fm._abi.FM_PHASE_GATEUP)
-    k1.record(stream)
-    torch.cuda.synchronize()
-    gu_us = k0.elapsed_time(k1) / reps * 1e3
-    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
-    gu_bytes = 2 * cfg.d_mlp * cfg.d_model * es + (2 * cfg.d_mlp * 4 if cfg.weight_dtype == "fp8" else 0)
-    gu_flops = 2 * cfg.batch * cfg.suffix * 2 * cfg.d_mlp * cfg.d_model
     byts, flops = algorithmic(cfg, info)
-    mfma_bound = cfg.batch * cfg.suffix * 2 > 312 * es  # arithmetic intensity above the bf16 ridge
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+    peak_f = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS  # fp8 weights run bf16 MFMA
+    mfma_bound = flops / (peak_f * 1e12) > byts / (HBM_PEAK_GBS * 1e9)
+    loop_roof_ms = (flops / (peak_f * 1e12) if mfma_bound else byts / (HBM_PEAK_GBS * 1e9)) * 1e3
+    phases = phase_table(fm, den, cfg, info, stream, persistent=int(info.exec_mode) == fm.FM_EXEC_PERSISTENT,
+                         chunk_ms=ms)
+    dom = max(phases, key=lambda n: phases[n]["per_chunk_ms"])
+    roof = dict(phases[dom]["roofline"])
+    roof["kernel"] = dom
+    roof["per_launch"] = phases[dom]["per_launch"]
     # committed counters: per workload, and per weight dtype where it was overridden
-    traffic = load_traffic(cfg.name if cfg.weight_dtype == base_weights else f"{cfg.name}_{cfg.weight_dtype}_weights")
-    if mfma_bound:
-        peak = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS
-        achieved = gu_flops / (gu_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic}
-        loop_roof_ms = flops / (peak * 1e12) * 1e3
-    else:
-        achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
-        loop_roof_ms = byts / (HBM_PEAK_GBS * 1e9) * 1e3
-    roof["kernel"] = "gate/up GEMM + GELU gate (one layer)"
-    roof["per_launch"] = {"bytes": gu_bytes, "flops": gu_flops, "avg_us": round(gu_us, 3)}
-    log(f"bench: gate/up kernel {gu_us:.2f} us -> {achieved:.1f} {roof['unit']} ({roof['frac']*100:.1f}% of peak)")
+    roof["traffic"] = load_traffic(cfg.name if cfg.weight_dtype == base_weights
+                                   else f"{cfg.name}_{cfg.weight_dtype}_weights", dom)
+    log(f"bench: dominant kernel {dom}: {phases[dom]['per_launch']['avg_us']:.2f} us x "
+        f"{phases[dom]['launches_per_chunk']} = {phases[dom]['per_chunk_ms']:.3f} ms/chunk, "
+        f"{roof['achieved']} {roof['unit']} ({roof['frac'] * 100:.2f}% of peak)")
 
     if args.calib_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -401,8 +481,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host")
-        cpu = cpu_baseline(cfg, W, k, v, x0, st, args.cpu_budget_s)
-        log(f"bench: oracle {cpu['value']:.1f} ms/chunk on {cpu['cores']} threads")
+        cpu = cpu_baseline(cfg, W, k, v, x0, st)
+        log(f"bench: oracle {cpu['value']:.1f} ms/chunk on {cpu['cores']} threads, "
+            f"{cpu['one_thread']['value']:.1f} on one ({cpu['cpu_model']})")
 
     line = {
         "metric": METRIC,
@@ -425,12 +506,16 @@ def main():
                    "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),
                    "parallelism": "single GPU"},
         "chunks_per_s": round(1000.0 / ms * cfg.batch, 2),
-        "latency_ms": {"p10": round(pct(.1), 4), "p50": round(pct(.5), 4), "p90": round(pct(.9), 4),
-                       "p99": round(pct(.99), 4)},
+        "latency_ms": {"p10": round(pct(.1), 4), "p50": round(statistics.median(per), 4),
+                       "p90": round(pct(.9), 4), "p99": round(pct(.99), 4), "max": round(per[-1], 4),
+                       "per": "tick (append + denoise)" if streaming else "chunk"},
         "roofline": roof,
-        "loop_roofline": {"bound": roof["bound"], "roofline_ms": round(loop_roof_ms, 4),
+        "loop_roofline": {"bound": "mfma" if mfma_bound else "hbm", "roofline_ms": round(loop_roof_ms, 4),
                           "frac": round(loop_roof_ms / ms, 4),
                           "algorithmic_bytes_per_chunk": byts, "algorithmic_flops_per_chunk": flops},
+        "phases": {n: {kk: vv for kk, vv in p.items() if kk != "roofline"} | {"frac": p["roofline"]["frac"],
+                                                                                "bound": p["roofline"]["bound"]}
+                   for n, p in phases.items()},
         "cpu_baseline": cpu,
     }
     den.close()

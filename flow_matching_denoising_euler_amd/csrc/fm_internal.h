@@ -1,5 +1,5 @@
 // Internal launch interface between the engine (fm_engine.cpp) and the
-// gfx950 kernels (fm_kernels.hip).  Not part of the public ABI.
+// gfx950 kernels (fm_gemm.hip, fm_attn*.hip, fm_misc.hip).  Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -202,7 +202,7 @@ inline BigPlan big_plan(int epi, int M, int N, int K, bool wf8 = false) {
   return p;
 }
 
-// --- launchers (fm_kernels.hip) --------------------------------------------
+// --- launchers (fm_gemm.hip, fm_attn*.hip, fm_misc.hip) --------------------------------------------
 hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t st);
 hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st);
 hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st);

@@ -1,0 +1,520 @@
+// gfx950 kernels of the denoise loop besides the GEMMs and the attention:
+// the first embedding, the step tail (final norm, action head, update, next
+// embedding), create-time preparation (fp8 quantisation, packing, time
+// tables), rotary positions, the prefix K/V copy and the encoder's input.
+#include "fm_device.h"
+
+namespace fm {
+
+// First embedding of a chunk: x0 = noise, state rows h = state W_s^T + b_s,
+// action rows h = x0 W_in^T + b_in (+ time feature of step 0).
+template <int ACT, int WE>
+__global__ __launch_bounds__(512) void k_embed(EmbedArgs e) {
+  __shared__ float s_x[64][33];
+  const int mt = blockIdx.x / e.esplit, es = blockIdx.x % e.esplit;
+  const int m0 = mt * 64, c0 = es * 64;
+  const int tid = threadIdx.x;
+  // noise rows of the tile (action rows); copy of the noise into x0
+  float xv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const int rc = min(r, e.M - 1), b = rc / e.S, s = rc % e.S;
+    const int ar = b * e.C + max(s - e.has_state, 0);
+    xv[i] = e.noise[(long)ar * e.A + min(a, e.A - 1)];
+  }
+  // state rows: hs = state W_s^T + b_s for this workgroup's 64 columns
+  {
+    const int col = c0 + (tid & 63);
+    for (int lr = tid >> 6; lr < 64; lr += 8) {
+      const int r = m0 + lr;
+      if (r >= e.M || !e.has_state || (r % e.S) != 0) continue;
+      const int b = r / e.S;
+      float acc = 0.f;
+      for (int k = 0; k < e.SD; ++k)
+        acc += ld_act<ACT>(e.state, (long)b * e.SD + k) * ld_w(e.w_state, WE, (long)col * e.SD + k);
+      e.hs[(long)b * e.d + col] = acc + ld_w(e.b_state, WE, col);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const bool act_row = r < e.M && a < e.A && !(e.has_state && (r % e.S) == 0);
+    s_x[lr][a] = act_row ? xv[i] : 0.f;
+    if (act_row && es == 0) {
+      const int b = r / e.S, s = r % e.S;
+      e.x0[(long)(b * e.C + s - e.has_state) * e.A + a] = xv[i];
+    }
+  }
+  __syncthreads();  // s_x and hs of this tile complete
+  EmbedCol<WE> ec;
+  ec.load(c0, e.A, e.w_in, e.b_in, e.temb, e.g1, 0, e.hs, m0, e.M, e.S, e.d);
+  ec.template emit<ACT>(c0, m0, e.M, e.S, e.has_state, e.A, e.d, s_x, e.h, e.u, e.ssq_out);
+}
+
+// Step tail: final norm + action head + Euler (or Heun stage) update, then
+// the next evaluation's embedding.  Workgroup (m-tile, 64-column slice): every slice recomputes the
+// 64 x A head tile (K = d) and embeds its own columns.
+template <int ACT, int WE, int NB>
+__global__ __launch_bounds__(512) void k_out(OutArgs o) {
+  constexpr int UPW = 4;
+  __shared__ float red[4][64][33];
+  __shared__ float s_rstd[64];
+  __shared__ float s_x[64][33];
+  const int mt = blockIdx.x / o.esplit, es = blockIdx.x % o.esplit;
+  const int m0 = mt * 64, c0 = es * 64;
+  const int tid = threadIdx.x;
+  const int units = o.d >> 5;
+  // every operand first: head weights, u_f, h^2 partials, x, b_out, the embedding's operands
+  float4 q[4];
+  rstd_load(o.ssq, o.M, m0, q);
+  float xin[4], bo[4], vp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = min(m0 + lr, o.M - 1);
+    const int b = r / o.S, s = r % o.S;
+    const int ar = b * o.C + max(s - o.has_state, 0);
+    xin[i] = o.x_in[(long)ar * o.A + min(a, o.A - 1)];
+    bo[i] = o.bout.base[(long)o.t_idx * o.bout.step_stride + min(a, o.A - 1)];
+    vp[i] = o.v_prev ? o.v_prev[(long)ar * o.A + min(a, o.A - 1)] : 0.f;
+  }
+  EmbedCol<WE> ec;
+  if (o.do_embed) ec.load(c0, o.A, o.w_in, o.b_in, o.temb, o.g1, o.embed_step, o.hs, m0, o.M, o.S, o.d);
+  SkinnyTile<ACT, WE, NB, UPW, 1> t;
+  t.zero();
+  t.set_range(blockIdx.x);
+  t.mv = o.M - m0;
+  t.load_w_all(o.Wout, NB, 0, units);
+  t.load_a_pass(o.uf, o.d, mt, units, 0);
+  t.mma_pass(units, 0);
+  rstd_finish(q, o.M, m0, o.inv_d, o.eps, s_rstd);
+  reduce_waves<NB>(t.acc, red);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const bool act_row = r < o.M && a < o.A && !(o.has_state && (r % o.S) == 0);
+    float xv = 0.f;
+    if (act_row) {
+      const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
+      const float v = acc * s_rstd[lr] + bo[i];
+      xv = o.heun == 2   ? xin[i] + o.dt * (0.5f * (vp[i] + v))
+           : o.heun == 3 ? xin[i] + o.dt * (o.c_cur * v - o.c_prev * vp[i])
+                         : xin[i] + o.dt * v;
+      if (es == 0) {
+        const int b = r / o.S, s = r % o.S;
+        const long xo = (long)(b * o.C + s - o.has_state) * o.A + a;
+        if (o.heun == 1 || o.heun == 3) o.v_save[xo] = v;
+        if (o.heun != 1) o.x_out[xo] = xv;
+      }
+    }
+    s_x[lr][a] = xv;
+  }
+  if (!o.do_embed) return;
+  __syncthreads();
+  ec.template emit<ACT>(c0, m0, o.M, o.S, o.has_state, o.A, o.d, s_x, o.h, o.u, o.ssq_out);
+}
+
+// ---------------------------------------------------------------------------
+// create-time kernels: quantise, pack, time tables
+// ---------------------------------------------------------------------------
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating at +-448,
+// sign from the input's sign bit.  Works on the exact fp32 bit pattern.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float ax = fminf(fabsf(x), 448.f);
+  const uint32_t au = __float_as_uint(ax);
+  const int e = (int)(au >> 23) - 127;  // unbiased exponent of |x|
+  uint32_t code;
+  if (ax == 0.f) {
+    code = 0;
+  } else if (e < -6) {
+    // subnormal range: value = m * 2^-9, m = rne(|x| * 2^9) in [0, 8]
+    const float q = ax * 512.f;  // exact (power of two scaling)
+    uint32_t m = (uint32_t)q;
+    const float frac = q - (float)m;
+    if (frac > 0.5f || (frac == 0.5f && (m & 1u))) ++m;
+    code = m;  // m == 8 becomes the smallest normal (exp field 1, mantissa 0)
+  } else {
+    // normal: 3 mantissa bits; round the 23-bit mantissa to 3 bits
+    const uint32_t mant = au & 0x7FFFFFu;
+    uint32_t m3 = mant >> 20;
+    const uint32_t rest = mant & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
+    uint32_t ef = (uint32_t)(e + 7);
+    if (m3 == 8) { m3 = 0; ++ef; }
+    code = (ef << 3) | m3;
+    if (code > 0x7Eu) code = 0x7Eu;  // saturate (448)
+  }
+  return sign | code;
+}
+
+__global__ void k_quantize_e4m3(const uint16_t* w, int rows, int cols, uint8_t* codes, float* scales) {
+  const int r = blockIdx.x;
+  __shared__ float s_red[256];
+  float amax = 0.f;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) amax = fmaxf(amax, fabsf(bf2f(w[(long)r * cols + c])));
+  s_red[threadIdx.x] = amax;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) s_red[threadIdx.x] = fmaxf(s_red[threadIdx.x], s_red[threadIdx.x + st]);
+    __syncthreads();
+  }
+  amax = s_red[0];
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  if (threadIdx.x == 0) scales[r] = s;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+    const float q = __fdiv_rn(bf2f(w[(long)r * cols + c]), s);
+    codes[(long)r * cols + c] = (uint8_t)f32_to_e4m3(q);
+  }
+}
+
+// repack W[rows][cols] (row r -> packed column map(r), k = source column)
+__global__ void k_pack(const void* src, int src_elt, int rows, int cols, RowMap rm, void* dst, int dst_elt,
+                       int Ntot) {
+  const long n = (long)rows * cols;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const int r = (int)(i / cols), k = (int)(i % cols);
+    const int nd = (r / rm.blk) * rm.stride + rm.off + r % rm.blk;
+    const int nb = nd >> 4, ln = nd & 15;
+    const int NBT = Ntot >> 4;
+    if (dst_elt == ELT_FP8) {
+      const int kq = k >> 6, kk = k & 63, half = kk >> 5, lane = ln + 16 * ((kk & 31) >> 3);
+      const long off = (((long)kq * NBT + nb) * 64 + lane) * 16 + half * 8 + (k & 7);
+      ((uint8_t*)dst)[off] = ((const uint8_t*)src)[i];
+    } else {
+      const int kb = k >> 5, lane = ln + 16 * ((k & 31) >> 3);
+      const long off = (((long)kb * NBT + nb) * 64 + lane) * 8 + (k & 7);
+      if (dst_elt == ELT_F32) ((float*)dst)[off] = ((const float*)src)[i];
+      else ((uint16_t*)dst)[off] = ((const uint16_t*)src)[i];
+    }
+  }
+}
+
+__global__ void k_scatter_scales(const float* s, int rows, RowMap rm, float* dst) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < rows) dst[(r / rm.blk) * rm.stride + rm.off + r % rm.blk] = s[r];
+}
+
+__global__ void k_copy_convert(const void* src, int src_elt, long n, float* dst) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    dst[i] = ld_w(src, src_elt, i);
+}
+
+// sinusoidal features [sin(t w_j) | cos(t w_j)], w_j = 10000^(-j/(D/2))
+__device__ __forceinline__ double sinusoid_d(double t, int D, int i) {
+  const int half = D / 2, jj = i < half ? i : i - half;
+  const double w = pow(10000.0, -(double)jj / (double)half);
+  return i < half ? sin(t * w) : cos(t * w);
+}
+
+// step k's feature row, t_k from the schedule tk
+__global__ void k_time_add(float* temb, const double* tk, int d) {
+  const int k = blockIdx.y;
+  const double t = tk[k];
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < d; i += gridDim.x * blockDim.x)
+    temb[(long)k * d + i] = (float)sinusoid_d(t, d, i);
+}
+
+// c[k][j] = SiLU(sum_i tau(t_k)[i] W_t[j][i] + b_t[j])
+__global__ void k_ada_c(const void* w_t, const void* b_t, int wt, const double* tk, int time_dim, int d, float* c) {
+  const int k = blockIdx.y;
+  const int jj = blockIdx.x * blockDim.x + threadIdx.x;
+  if (jj >= d) return;
+  const double t = tk[k];
+  double acc = 0.0;
+  for (int i = 0; i < time_dim; ++i) acc += sinusoid_d(t, time_dim, i) * (double)ld_w(w_t, wt, (long)jj * time_dim + i);
+  acc += (double)ld_w(b_t, wt, jj);
+  c[(long)k * d + jj] = (float)(acc / (1.0 + exp(-acc)));
+}
+
+// (gamma, beta, alpha) of one norm for every step: rows [0,d) gamma, [d,2d)
+// beta, [2d,3d) alpha.  Writes 1+gamma, beta, alpha (alpha may be null).
+__global__ void k_ada_mod(const float* c, int n_steps, int d, const void* w_n, const void* b_n, int wt,
+                          float* gam1p, float* beta, float* alpha, long tab_stride) {
+  const int k = blockIdx.y;
+  const int jr = blockIdx.x * blockDim.x + threadIdx.x;
+  if (jr >= 3 * d) return;
+  double acc = 0.0;
+  const float* ck = c + (long)k * d;
+  for (int i = 0; i < d; ++i) acc += (double)ck[i] * (double)ld_w(w_n, wt, (long)jr * d + i);
+  acc += (double)ld_w(b_n, wt, jr);
+  const int part = jr / d, col = jr % d;
+  float* dst = part == 0 ? gam1p : (part == 1 ? beta : alpha);
+  if (dst) dst[(long)k * tab_stride + col] = (float)(part == 0 ? 1.0 + acc : acc);
+}
+
+// out[k][map(n)] += sum_j beta[k][j] * Weff[n][j]
+__global__ void k_bias_gemv(const void* w, int w_elt, const float* scales, int rows, int cols, const float* beta,
+                            long beta_stride, RowMap rm, float* out, long out_stride) {
+  const int k = blockIdx.y;
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= rows) return;
+  double acc = 0.0;
+  const float* bk = beta + (long)k * beta_stride;
+  for (int j = 0; j < cols; ++j) {
+    double wv;
+    if (w_elt == ELT_FP8) wv = (double)bf2f(e4m3_to_bf16(((const uint8_t*)w)[(long)n * cols + j])) * (double)scales[n];
+    else wv = (double)ld_w(w, w_elt, (long)n * cols + j);
+    acc += (double)bk[j] * wv;
+  }
+  const int nd = (n / rm.blk) * rm.stride + rm.off + n % rm.blk;
+  out[(long)k * out_stride + nd] += (float)acc;
+}
+
+// prefix K rows and V^T columns -> the padded physical layout, and the robot's (valid, head)
+// Rotary embedding: the pair (c, c + Dh/2) of a head turns by pos *
+// theta^(-2c/Dh).  The angle is formed and reduced in double: at positions of
+// a few thousand an fp32 angle would already be off by ~1e-4 rad.
+__device__ __forceinline__ void rope_cs(double pos, int c, int Dh, float theta, float* cs, float* sn) {
+  const double ang = pos * pow((double)theta, -2.0 * (double)c / (double)Dh);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *cs = (float)cd;
+  *sn = (float)sd;
+}
+// element c of a K row at position pos after rotation (x: the row's Dh values)
+template <typename T>
+__device__ __forceinline__ float rope_elem(const T* x, int c, int Dh, double pos, float theta) {
+  const int half = Dh >> 1, i = c < half ? c : c - half;
+  float cs, sn;
+  rope_cs(pos, i, Dh, theta, &cs, &sn);
+  auto ld = [&](int e) { if constexpr (sizeof(T) == 2) return bf2f(x[e]); else return (float)x[e]; };
+  return c < half ? ld(c) * cs - ld(c + half) * sn : ld(c) * cs + ld(c - half) * sn;
+}
+
+// The suffix Q (row-major in qkv) and K (kv layout) of one step, rotated in
+// place: thread = one (row, head, pair)
+template <int ACT>
+__global__ void k_rope(RopeArgs r) {
+  constexpr bool packed = ACT != ELT_F32;
+  const int half = r.Dh >> 1, H = r.Hq + r.Hkv;
+  const long total = (long)r.M * H * half;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % half), h = (int)((i / half) % H);
+    const int row = (int)(i / ((long)half * H));
+    const int b = row / r.S, s = row % r.S;
+    float cs, sn;
+    rope_cs((double)(r.meta[2 * b] + s), c, r.Dh, r.theta, &cs, &sn);
+    void* base;
+    long o1, o2;
+    if (h < r.Hq) {
+      base = r.qkv;
+      o1 = (long)row * r.Nqkv + (long)h * r.Dh + c;
+      o2 = o1 + half;
+    } else {
+      const int j = h - r.Hq;
+      const long sb = (long)b * r.Hkv * r.Dh * r.SP;
+      base = r.ksuf;
+      o1 = sb + kv_k_off(packed, r.SP, r.Hkv, r.Dh, j, s, c);
+      o2 = sb + kv_k_off(packed, r.SP, r.Hkv, r.Dh, j, s, c + half);
+    }
+    const float x1 = ld_act<ACT>(base, o1), x2 = ld_act<ACT>(base, o2);
+    st_act<ACT>(base, o1, x1 * cs - x2 * sn);
+    st_act<ACT>(base, o2, x2 * cs + x1 * sn);
+  }
+}
+
+template <typename T>
+__global__ void k_kv_copy(KvCopy c) {
+  constexpr bool packed = sizeof(T) == 2;
+  const int HD = c.HD, Dh = c.Dh, Hkv = HD / Dh;
+  const long n8 = HD / 8;  // K: 8-element units (contiguous in both layouts)
+  const long total_k = (long)c.layers * c.n * n8;
+  const long total_v = (long)c.layers * c.n * HD;
+  const long stride = (long)gridDim.x * blockDim.x;
+  const long pitch = (long)c.TP * HD;  // elements per layer
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_k; i += stride) {
+    const long l = i / (c.n * n8), rem = i % (c.n * n8);
+    const int t = (int)(rem / n8), col = (int)(rem % n8) * 8;
+    const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
+    const T* src = (const T*)c.k + (l * c.n + t) * HD + col;
+    T* dst = (T*)c.kd + l * pitch + kv_k_off(packed, c.TP, Hkv, Dh, col / Dh, phys, col % Dh);
+    if (c.rope_theta > 0.f) {  // token t at position t (a set: no ring)
+      const T* row = src - col % Dh;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = rope_elem<T>(row, col % Dh + e, Dh, (double)t, c.rope_theta);
+        if constexpr (packed) dst[e] = (T)f2bf(y); else dst[e] = y;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = src[e];
+    }
+  }
+  // V: consecutive threads take consecutive tokens of one (layer, column)
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total_v; i += stride) {
+    const long l = i / (c.n * HD), rem = i % (c.n * HD);
+    const int col = (int)(rem / c.n), t = (int)(rem % c.n);
+    const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
+    ((T*)c.vd)[l * pitch + kv_v_off(packed, c.TP, Hkv, Dh, col / Dh, phys, col % Dh)] =
+        ((const T*)c.v)[(l * c.n + t) * HD + col];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    c.meta[2 * c.robot] = c.valid;
+    c.meta[2 * c.robot + 1] = c.head;
+  }
+}
+
+// The fp8 prefix cache: one wave per (layer, token, kv head) row of K and of
+// V: the row's max |x| gives the scale (max / 448), the codes are those of
+// the fp32 quotients (the weights' rule, f32_to_e4m3), written to the same
+// physical positions of the kv layout as the act-dtype copy above, one byte
+// per element; the scales go to [layer][position][kv head].
+__global__ void k_kv_copy8(KvCopy c) {
+  const int HD = c.HD, Dh = c.Dh, Hkv = HD / Dh;
+  const int lane = threadIdx.x & 63;
+  const long rows = (long)c.layers * c.n * Hkv;
+  const long wstride = (long)gridDim.x * (blockDim.x >> 6);
+  for (long rw = blockIdx.x * (long)(blockDim.x >> 6) + (threadIdx.x >> 6); rw < rows; rw += wstride) {
+    const long l = rw / ((long)c.n * Hkv);
+    const int t = (int)((rw / Hkv) % c.n), j = (int)(rw % Hkv);
+    const int phys = t < c.split_t ? c.phys0 + t : c.phys1 + (t - c.split_t);
+    const long src = (l * c.n + t) * HD + (long)j * Dh;
+    uint8_t* kd = (uint8_t*)c.kd + l * (long)c.TP * HD;
+    uint8_t* vd = (uint8_t*)c.vd + l * (long)c.TP * HD;
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* x = (const uint16_t*)(kv ? c.v : c.k) + src;
+      const bool rot = !kv && c.rope_theta > 0.f;  // K token t at position t, then quantised
+      auto val = [&](int e) { return rot ? rope_elem<uint16_t>(x, e, Dh, (double)t, c.rope_theta) : bf2f(x[e]); };
+      float amax = 0.f;
+      for (int e = lane; e < Dh; e += 64) amax = fmaxf(amax, fabsf(val(e)));
+      for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+      for (int e = lane; e < Dh; e += 64) {
+        const uint8_t code = (uint8_t)f32_to_e4m3(__fdiv_rn(val(e), sc));
+        if (kv) vd[kv_v_off(true, c.TP, Hkv, Dh, j, phys, e)] = code;
+        else kd[kv_k_off(true, c.TP, Hkv, Dh, j, phys, e)] = code;
+      }
+      if (lane == 0) (kv ? c.vsd : c.ksd)[(l * c.TP + phys) * Hkv + j] = sc;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    c.meta[2 * c.robot] = c.valid;
+    c.meta[2 * c.robot + 1] = c.head;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefix encoder.  The prefix K/V that the loop reads is produced before the
+// loop by the vision/language stack (realtime-vla write-up, "The problem is a
+// policy that thinks too long": vision encoder, LLM, action expert as three
+// components; InstinctFlash README, "Framework overview": prefill extraction
+// as a graph-level optimisation).  The encoder runs the layer kernels above
+// over the prefix tokens as the "suffix" of an empty prefix; its QKV GEMMs
+// also write K and V as rows (EPI_QKVR), and this kernel is its input.
+// ---------------------------------------------------------------------------
+// Token rows in: the residual stream is the token embedding itself; writes
+// h, the first norm's operand u = act(h * g) in the packed GEMM layout and
+// the h^2 partial of every 16-column group.  Workgroup = (64-row tile,
+// 64-column slice), 512 threads.
+template <int ACT>
+__global__ __launch_bounds__(512) void k_tokens_in(TokensIn t) {
+  const int mt = blockIdx.x / t.esplit, es = blockIdx.x % t.esplit;
+  const int col = es * 64 + (threadIdx.x & 63);
+  const float gain = t.g1[col];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = mt * 64 + (threadIdx.x >> 6) + 8 * i;
+    const float hv = r < t.M ? t.tokens[(long)r * t.d + col] : 0.f;
+    const float q = sum16(hv * hv);
+    if (r < t.M) {
+      t.h[(long)r * t.d + col] = hv;
+      st_act<ACT>(t.u, pk(r, col, t.d), hv * gain);
+      if ((threadIdx.x & 15) == 0) t.ssq[(long)r * PM + (col >> 4)] = q;
+    }
+  }
+}
+
+hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st) {
+  const int grid = o.mtiles * o.esplit;
+  if ((o.d >> 5) > GW * 4) return hipErrorInvalidValue;
+  (void)wt_out;
+  if (act == ELT_F32) {
+    if (o.A == 32) FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 2>), grid, 512, o);
+    FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 1>), grid, 512, o);
+  }
+  if (o.A == 32) FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 2>), grid, 512, o);
+  FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 1>), grid, 512, o);
+}
+
+hipError_t launch_embed(int act, const EmbedArgs& e, hipStream_t st) {
+  const int grid = e.mtiles * e.esplit;
+  if (act == ELT_F32) FM_LAUNCH_N((k_embed<ELT_F32, ELT_F32>), grid, 512, e);
+  FM_LAUNCH_N((k_embed<ELT_BF16, ELT_BF16>), grid, 512, e);
+}
+
+hipError_t launch_pack(const void* src, int src_elt, int rows, int cols, RowMap rm, void* dst, int dst_elt, int Ntot,
+                       hipStream_t st) {
+  const long n = (long)rows * cols;
+  const int grid = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+  FM_LAUNCH(k_pack, grid, src, src_elt, rows, cols, rm, dst, dst_elt, Ntot);
+}
+
+hipError_t launch_quantize_e4m3(const void* w, int rows, int cols, uint8_t* codes, float* scales, hipStream_t st) {
+  FM_LAUNCH(k_quantize_e4m3, rows, (const uint16_t*)w, rows, cols, codes, scales);
+}
+
+hipError_t launch_scatter_scales(const float* s, int rows, RowMap rm, float* dst, hipStream_t st) {
+  FM_LAUNCH(k_scatter_scales, (rows + 255) / 256, s, rows, rm, dst);
+}
+
+hipError_t launch_copy_convert(const void* src, int src_elt, long n, float* dst, hipStream_t st) {
+  const int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  FM_LAUNCH(k_copy_convert, grid > 0 ? grid : 1, src, src_elt, n, dst);
+}
+
+hipError_t launch_time_add(float* temb, const double* tk, int n_steps, int d, hipStream_t st) {
+  hipLaunchKernelGGL(k_time_add, dim3((d + 255) / 256, n_steps), dim3(256), 0, st, temb, tk, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_ada_c(const void* w_t, const void* b_t, int wt, const double* tk, int n_steps, int time_dim, int d,
+                        float* c, hipStream_t st) {
+  hipLaunchKernelGGL(k_ada_c, dim3((d + 255) / 256, n_steps), dim3(256), 0, st, w_t, b_t, wt, tk, time_dim, d, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_ada_mod(const float* c, int n_steps, int d, const void* w_n, const void* b_n, int wt, float* gam1p,
+                          float* beta, float* alpha, long tab_stride, hipStream_t st) {
+  hipLaunchKernelGGL(k_ada_mod, dim3((3 * d + 255) / 256, n_steps), dim3(256), 0, st, c, n_steps, d, w_n, b_n, wt,
+                     gam1p, beta, alpha, tab_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_gemv(const void* w, int w_elt, const float* scales, int rows, int cols, const float* beta,
+                            long beta_stride, int n_steps, RowMap rm, float* out, long out_stride, hipStream_t st) {
+  hipLaunchKernelGGL(k_bias_gemv, dim3((rows + 255) / 256, n_steps), dim3(256), 0, st, w, w_elt, scales, rows, cols,
+                     beta, beta_stride, rm, out, out_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_copy(const KvCopy& c, hipStream_t st) {
+  if (c.fp8) {
+    const long rows = (long)c.layers * c.n * (c.HD / c.Dh);
+    hipLaunchKernelGGL(k_kv_copy8, dim3((int)std::max(1L, std::min(2048L, (rows + 3) / 4))), dim3(256), 0, st, c);
+    return hipGetLastError();
+  }
+  const long work = (long)c.layers * c.n * c.HD;
+  const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
+  if (c.elt == ELT_F32) hipLaunchKernelGGL(k_kv_copy<float>, dim3(grid), dim3(256), 0, st, c);
+  else hipLaunchKernelGGL(k_kv_copy<uint16_t>, dim3(grid), dim3(256), 0, st, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(int act, const RopeArgs& r, hipStream_t st) {
+  const long work = (long)r.M * (r.Hq + r.Hkv) * (r.Dh / 2);
+  const int grid = (int)std::max(1L, std::min(4096L, (work + 255) / 256));
+  if (act == ELT_F32) hipLaunchKernelGGL(k_rope<ELT_F32>, dim3(grid), dim3(256), 0, st, r);
+  else hipLaunchKernelGGL(k_rope<ELT_BF16>, dim3(grid), dim3(256), 0, st, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st) {
+  const int grid = (t.M + 63) / 64 * t.esplit;
+  if (act == ELT_F32) FM_LAUNCH_N(k_tokens_in<ELT_F32>, grid, 512, t);
+  FM_LAUNCH_N(k_tokens_in<ELT_BF16>, grid, 512, t);
+}
+
+}  // namespace fm
