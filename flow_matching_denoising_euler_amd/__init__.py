@@ -13,7 +13,7 @@ from ._abi import (FM_ABI_VERSION, FM_BF16, FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC
                    FM_F32, FM_FP8_E4M3, FM_OK, STATUS_NAMES, fm_config, fm_info, fm_weights)
 
 __all__ = ["FMError", "make_config", "fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv",
-           "fm_denoise", "fm_get_info", "fm_launch_phase", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
+           "fm_denoise", "fm_denoise_noalloc", "fm_get_info", "fm_launch_phase", "fm_destroy", "fm_last_error", "fm_quantize_e4m3",
            "fm_encoder_create", "fm_encode_prefix", "fm_append_encoded", "Denoiser", "Encoder", "lib"]
 
 lib = _abi.lib
@@ -210,6 +210,12 @@ def fm_append_prefix_kv(ctx, robot: int, k_frame, v_frame):
 def fm_denoise(ctx, noise, state, actions):
     """noise, actions: fp32 device tensors [batch][chunk][action_dim]; state or None."""
     _check(lib().fm_denoise(ctx, _ptr(noise), _ptr(state), _ptr(actions)), ctx)
+
+
+def fm_denoise_noalloc(ctx, noise, state, actions):
+    """fm_denoise with the loop's scratch in the library's static per-GPU
+    array (allocates nothing; concurrent calls on one GPU race)."""
+    _check(lib().fm_denoise_noalloc(ctx, _ptr(noise), _ptr(state), _ptr(actions)), ctx)
 
 
 def fm_get_info(ctx) -> fm_info:

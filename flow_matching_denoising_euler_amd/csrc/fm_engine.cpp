@@ -81,6 +81,8 @@ struct fm_ctx {
   void *u, *uf, *qkv, *o, *z;
   unsigned* counters;
   size_t n_counters;
+  size_t part_bytes = 0, attn_part_bytes = 0;  // scratch sizes (split-K and key-split partials)
+  int device = 0;
   void *enc_k[2], *enc_v[2];  // encoder output rows [B][L][S][HD] act, two slots used in turn
   int enc_slot = 0;            // slot the graph being captured writes
 
@@ -360,10 +362,12 @@ void carve(fm_ctx* x, Arena& a) {
   x->z = a.take(Mp * x->F * ea);
   const long ks = std::max(x->ks_o, x->ks_d);
   const long Mp128 = (x->M + 127) / 128 * 128;  // rows covered by the large-M tiles
-  x->partials = (float*)a.take(ks > 1 ? ks * Mp128 * d * 4 : 16);
+  x->part_bytes = ks > 1 ? ks * Mp128 * d * 4 : 16;
+  x->partials = (float*)a.take(x->part_bytes);
   // per (query group, head-dim part (up to 2), key range): 16 rows x Dh / parts
   // partial output, row max, row sum
-  x->attn_part = (float*)a.take(x->nsplit == 1 ? 16 : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 4) * 4);
+  x->attn_part_bytes = x->nsplit == 1 ? 16 : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 4) * 4;
+  x->attn_part = (float*)a.take(x->attn_part_bytes);
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
                                    (size_t)x->B * x->Hkv * x->nqblk * 2) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);
@@ -688,6 +692,7 @@ fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream
   x->encoder = encoder;
   x->stream = (hipStream_t)hip_stream;
   x->n_cu = prop.multiProcessorCount;
+  x->device = dev;
   x->exec_mode = FM_EXEC_GRAPH;
   derive(x);
   x->cfg.t_schedule = nullptr;  // the caller's array is read during fm_create only
@@ -914,13 +919,69 @@ fm_status fm_append_encoded(fm_ctx* x, int32_t robot, fm_ctx* enc, int32_t seq) 
   return FM_OK;
 }
 
-fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* actions) {
+}  // extern "C"
+
+namespace {
+
+fm_status check_denoise(fm_ctx* x, const float* noise, const void* state, const float* actions) {
   fm_status s = check_ctx(x);
   if (s != FM_OK) return s;
   if (!noise || !actions) return fail(x, FM_ERR_ARG, "noise or actions is NULL");
   if ((x->SD > 0) != (state != nullptr)) return fail(x, FM_ERR_ARG, "state must be given iff state_dim > 0");
   for (int b = 0; b < x->B; ++b)
     if (!x->is_set[b]) return fail(x, FM_ERR_STATE, "robot %d: prefix never set", b);
+  return FM_OK;
+}
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace fm {
+
+int ctx_device(const fm_ctx* x) { return x->device; }
+
+fm_status report(fm_ctx* x, fm_status s, const char* msg) { return fail(x, s, "%s", msg); }
+
+// fm_denoise with the split-K partials, the key-split partials and the
+// arrival counters in caller-given device memory (no graph: the captured one
+// holds the arena's scratch addresses, so the phases are launched one by one)
+fm_status denoise_with_scratch(fm_ctx* x, const float* noise, const void* state, float* actions, void* scratch,
+                               size_t cap) {
+  fm_status s = check_denoise(x, noise, state, actions);
+  if (s != FM_OK) return s;
+  const size_t need = up256(x->part_bytes) + up256(x->attn_part_bytes) + up256(x->n_counters * 4);
+  if (need > cap)
+    return fail(x, FM_ERR_UNSUPPORTED, "this context needs %zu bytes of scratch; the static buffer holds %zu", need, cap);
+  char* p = (char*)scratch;
+  float* part = (float*)p;
+  float* apart = (float*)(p + up256(x->part_bytes));
+  unsigned* cnt = (unsigned*)(p + up256(x->part_bytes) + up256(x->attn_part_bytes));
+  // the counters start at zero (the buffer keeps the last call's contents);
+  // a fill kernel, so that the call can be recorded into a graph
+  HIPCHK(x, launch_fill_u32(cnt, (long)x->n_counters, 0u, x->stream), "scratch counters");
+  float* keep_part = x->partials;
+  float* keep_apart = x->attn_part;
+  unsigned* keep_cnt = x->counters;
+  x->partials = part;
+  x->attn_part = apart;
+  x->counters = cnt;
+  s = enqueue_embed(x, noise, state, x->stream);
+  if (s == FM_OK) s = enqueue_graph_body(x, x->stream);
+  if (s == FM_OK) s = enqueue_tail(x, x->N - 1, x->heun ? 2 : (x->ab2 ? 3 : 0), x->stream, actions);
+  x->partials = keep_part;
+  x->attn_part = keep_apart;
+  x->counters = keep_cnt;
+  return s;
+}
+
+}  // namespace fm
+
+extern "C" {
+
+fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* actions) {
+  fm_status s = check_denoise(x, noise, state, actions);
+  if (s != FM_OK) return s;
   if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
   HIPCHK(x, hipGraphLaunch(x->gexec[0], x->stream), "graph launch");
   return enqueue_tail(x, x->N - 1, x->heun ? 2 : (x->ab2 ? 3 : 0), x->stream, actions);

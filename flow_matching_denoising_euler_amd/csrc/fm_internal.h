@@ -2,7 +2,10 @@
 // gfx950 kernels (fm_gemm.hip, fm_attn*.hip, fm_misc.hip).  Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "fm.h"
 
 namespace fm {
 
@@ -266,5 +269,14 @@ struct TokensIn {
   int M, d, esplit;
 };
 hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st);
+
+// p[0, n) = v (a kernel, not hipMemsetAsync, so that callers may record it into a graph)
+hipError_t launch_fill_u32(unsigned* p, long n, unsigned v, hipStream_t st);
+
+// engine side of the no-allocation entry point (fm_noalloc.hip)
+int ctx_device(const fm_ctx* x);
+fm_status report(fm_ctx* x, fm_status s, const char* msg);  // records msg for fm_last_error
+fm_status denoise_with_scratch(fm_ctx* x, const float* noise, const void* state, float* actions, void* scratch,
+                               size_t cap);
 
 }  // namespace fm

@@ -517,4 +517,15 @@ hipError_t launch_tokens_in(int act, const TokensIn& t, hipStream_t st) {
   FM_LAUNCH_N(k_tokens_in<ELT_BF16>, grid, 512, t);
 }
 
+__global__ void k_fill_u32(unsigned* p, long n, unsigned v) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(unsigned* p, long n, unsigned v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long grid = std::min<long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
 }  // namespace fm

@@ -317,6 +317,25 @@ void fm_destroy(fm_ctx* ctx);
  */
 const char* fm_last_error(const fm_ctx* ctx);
 
+/*
+ * fm_denoise for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same loop, with the same arguments, results (bit for bit) and errors as
+ * fm_denoise, but its scratch - the split-K partial tiles of the residual
+ * GEMMs, the attention's key-range partials and the arrival counters - lives
+ * in one static 8 MiB device array per GPU instead of the context's arena.
+ * The array is looked up on the device's first call (hipGetSymbolAddress)
+ * and held until the process ends.  It allocates nothing (no hipMalloc, no
+ * hipFree) and launches the loop's kernels one by one (no graph), clearing
+ * the counters with a kernel first, so the call may itself be recorded into
+ * a caller's graph.  A context whose scratch exceeds 8 MiB gets
+ * FM_ERR_UNSUPPORTED (none that fm_create accepts needs more than about
+ * 6.5 MiB).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other threads, other contexts)
+ * race and must be serialised by the caller.
+ */
+fm_status fm_denoise_noalloc(fm_ctx* ctx, const float* noise, const void* state, float* actions);
+
 /* Phases of one step (one velocity evaluation and its update), for fm_launch_phase. */
 typedef enum {
   FM_PHASE_QKV = 0,      /* norm1 folded into the QKV GEMM                     */
