@@ -162,31 +162,81 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   }
 }
 
-// fp32 attention (small head dims): one workgroup per (robot, query head),
-// one thread per suffix row, online softmax over the padded logical keys.
+// fp32 attention (head_dim <= 64): workgroup = (robot, query head, block of
+// 16 suffix rows), 16 threads per row.  Keys go through LDS in tiles of 64
+// (K and V rows padded against bank conflicts); each tile's scores, an online
+// softmax update and the P V product run from LDS.  Thread (row, sub) scores
+// keys sub + 16 i of the tile and accumulates output dims sub + 16 i.
+constexpr int F32_KT = 64, F32_DH = 64;
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
-  const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+  __shared__ float sK[F32_KT][F32_DH + 1], sV[F32_KT][F32_DH + 1], sP[16][F32_KT + 1];
+  const int nqb = (a.S + 15) / 16;
+  const int qb = blockIdx.x % nqb, h = (blockIdx.x / nqb) % a.Hq, b = blockIdx.x / (nqb * a.Hq);
   const int G = a.Hq / a.Hkv, j = h / G;
+  const int tid = threadIdx.x, r = tid >> 4, sub = tid & 15;
+  const int s = qb * 16 + r, sc_row = min(s, a.S - 1);
   const KeySpace ks(a, b);
   const int Dh = a.Dh;
-  for (int s = threadIdx.x; s < a.S; s += blockDim.x) {
-    float q[64], o[64];
-    const float* qp = (const float*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * Dh;
-    for (int c = 0; c < Dh; ++c) { q[c] = qp[c]; o[c] = 0.f; }
-    float m = -INFINITY, l = 0.f;
-    for (int p = 0; p < ks.kp; ++p) {
-      if (!ks.valid(p) || (a.state_causal && s == 0 && p > ks.TP)) continue;
-      float sc = 0.f;
-      for (int c = 0; c < Dh; ++c) sc += q[c] * ks.kel(j, p, c);
-      sc *= a.scale;
-      const float mn = fmaxf(m, sc);
-      const float corr = (m == -INFINITY) ? 0.f : expf(m - mn);
-      const float pe = expf(sc - mn);
-      l = l * corr + pe;
-      for (int c = 0; c < Dh; ++c) o[c] = o[c] * corr + pe * ks.vel(j, p, c);
-      m = mn;
+  float q[F32_DH], o[F32_DH / 16];
+  const float* qp = (const float*)a.qkv + (long)(b * a.S + sc_row) * a.Nqkv + (long)h * Dh;
+#pragma unroll
+  for (int c = 0; c < F32_DH; ++c) q[c] = c < Dh ? qp[c] : 0.f;
+#pragma unroll
+  for (int i = 0; i < F32_DH / 16; ++i) o[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int p0 = 0; p0 < ks.kp; p0 += F32_KT) {
+    for (int e = tid; e < F32_KT * Dh; e += 256) {
+      const int pl = e / Dh, c = e % Dh, key = p0 + pl;
+      const bool ok = key < ks.kp;
+      sK[pl][c] = ok ? ks.kel(j, key, c) : 0.f;
+      sV[pl][c] = ok ? ks.vel(j, key, c) : 0.f;
     }
-    for (int c = 0; c < Dh; ++c) ((float*)a.out)[pk(b * a.S + s, h * Dh + c, a.Hq * Dh)] = o[c] / l;
+    __syncthreads();
+    float sc[F32_KT / 16], mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < F32_KT / 16; ++i) {
+      const int pl = sub + 16 * i, key = p0 + pl;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < F32_DH; ++c)
+        if (c < Dh) dot += q[c] * sK[pl][c];
+      const bool ok = key < ks.kp && ks.valid(key) && !(a.state_causal && s == 0 && key > ks.TP);
+      sc[i] = ok ? dot * a.scale : -INFINITY;
+      mt = fmaxf(mt, sc[i]);
+    }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) mt = fmaxf(mt, __shfl_xor(mt, w));
+    const float mn = fmaxf(m, mt);
+    const float corr = (m == -INFINITY) ? 0.f : expf(m - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < F32_KT / 16; ++i) {
+      const float pe = (sc[i] == -INFINITY) ? 0.f : expf(sc[i] - mn);
+      ls += pe;
+      sP[r][sub + 16 * i] = pe;
+    }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) ls += __shfl_xor(ls, w);
+    l = l * corr + ls;
+    m = mn;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < F32_DH / 16; ++i) {
+      const int c = sub + 16 * i;
+      if (c < Dh) {
+        float acc = 0.f;
+        for (int pl = 0; pl < F32_KT; ++pl) acc += sP[r][pl] * sV[pl][c];
+        o[i] = o[i] * corr + acc;
+      }
+    }
+    __syncthreads();
+  }
+  if (s < a.S) {
+#pragma unroll
+    for (int i = 0; i < F32_DH / 16; ++i) {
+      const int c = sub + 16 * i;
+      if (c < Dh) ((float*)a.out)[pk(b * a.S + s, h * Dh + c, a.Hq * Dh)] = o[i] / l;
+    }
   }
 }
 
@@ -220,7 +270,10 @@ hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st) {
     case 128: return attn_bf16<128>(a, st);
     case 256: return attn_bf16<256>(a, st);
   }
-  if (act == ELT_F32) FM_LAUNCH(k_attn_f32, a.B * a.Hq, a);
+  if (act == ELT_F32) {
+    if (a.Dh > F32_DH) return hipErrorInvalidValue;
+    FM_LAUNCH(k_attn_f32, a.B * a.Hq * ((a.S + 15) / 16), a);
+  }
   return hipErrorInvalidValue;
 }
 
