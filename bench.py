@@ -120,6 +120,22 @@ def phase_table(fm, den, cfg, info, stream, persistent, chunk_ms):
     peak_f = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS
     evals = cfg.n_steps * (2 if cfg.sampler == "heun" else 1)
     out = {}
+    if persistent:  # the whole loop is one kernel: its work is the chunk's
+        reps = 10
+        fm.fm_launch_phase(den.ctx, 0, 0, fm._abi.FM_PHASE_LOOP)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fm.fm_launch_phase(den.ctx, 0, 0, fm._abi.FM_PHASE_LOOP)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        byts, flops = algorithmic(cfg, info)
+        out["persistent loop kernel"] = {"per_launch": {"bytes": int(byts), "flops": int(flops), "avg_us": round(us, 3)},
+                                         "launches_per_chunk": 1, "per_chunk_ms": round(us / 1e3, 4),
+                                         "roofline": roofline_of(byts, flops, us, peak_f)}
+        return out
     for ph in range(6):
         reps = 4 * cfg.n_layers if ph < 5 else 4 * cfg.n_steps
         fm.fm_launch_phase(den.ctx, 0, 0, ph)

@@ -24,7 +24,7 @@ FM_SAMPLER_EULER, FM_SAMPLER_HEUN, FM_SAMPLER_AB2 = 0, 1, 2
 EXPORTS = ("fm_create", "fm_set_prefix_kv", "fm_append_prefix_kv", "fm_denoise", "fm_get_info",
            "fm_destroy", "fm_last_error", "fm_quantize_e4m3", "fm_launch_phase", "fm_encoder_create",
            "fm_encode_prefix", "fm_append_encoded", "fm_denoise_noalloc")
-FM_PHASE_QKV, FM_PHASE_ATTN, FM_PHASE_OPROJ, FM_PHASE_GATEUP, FM_PHASE_DOWN, FM_PHASE_TAIL = range(6)
+FM_PHASE_QKV, FM_PHASE_ATTN, FM_PHASE_OPROJ, FM_PHASE_GATEUP, FM_PHASE_DOWN, FM_PHASE_TAIL, FM_PHASE_LOOP = range(7)
 
 
 class fm_config(ctypes.Structure):

@@ -51,14 +51,23 @@ __device__ __forceinline__ void attn_weight_prefetch(const AttnArgs& a) {
   asm volatile("" ::"v"(acc));  // the loaded values are used: the loads stay
 }
 
-template <int DH, int R, int QB, int DS, bool PF, bool CAUSAL, bool KV8>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
-  // weight prefetch workgroups (a separate instantiation: the test needs a
-  // kernel argument before the first load)
-  if constexpr (PF) if ((int)blockIdx.x >= a.grid) {
-    attn_weight_prefetch(a);
-    return;
-  }
+// LDS of one register-attention work item
+template <int DH, int R, int QB, int DS>
+struct AttnSfSmem {
+  static constexpr int QR = 16 * QB, NBD3 = DH / 16 / DS, KPAD = 128 * R + 8, KG = NBD3 >= 8 ? 1 : 8 / NBD3;
+  __align__(16) uint16_t sP[QR][KPAD];
+  float s_max[8][QR], s_sum[8][QR];
+  __align__(16) float s_o[KG > 1 ? KG * QR * (DH + 4) : 4];
+  __align__(16) uint16_t s_out[QR][DH + 8];
+  int s_last;
+};
+
+// One work item of the register attention: wgi is the work item's index in
+// the launch's order (the XCD-aware remap below assumes work item i runs on
+// XCD i mod 8).  COH: Q and the suffix K/V come from other workgroups of the
+// same launch, and the output goes to them (device-scope accesses).
+template <int DH, int R, int QB, int DS, bool CAUSAL, bool KV8, bool COH>
+__device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfSmem<DH, R, QB, DS>& lds) {
   constexpr int KBD = DH / 32, NBD = DH / 16, QR = 16 * QB;
   // DS workgroups share a query block: each computes all scores and the
   // softmax, and the P V product for its 1/DS of the head dims (V traffic per
@@ -73,16 +82,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KG = NBD3 >= 8 ? 1 : 8 / NBD3;         // key groups of phase 3
   constexpr int KBW = 4 * R / KG;                      // 32-key blocks per wave in phase 3
   constexpr int VQ0 = (QB == 1 ? (R <= 3 ? 16 : 8) : 8) / NBW, VQ = VQ0 < KBW ? VQ0 : KBW;
-  __shared__ __align__(16) uint16_t sP[QR][KPAD];
-  __shared__ float s_max[8][QR], s_sum[8][QR];
-  __shared__ __align__(16) float s_o[KG > 1 ? KG * QR * (DH + 4) : 4];
-  __shared__ __align__(16) uint16_t s_out[QR][DH + 8];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  auto& sP = lds.sP;
+  auto& s_max = lds.s_max;
+  auto& s_sum = lds.s_sum;
+  auto& s_o = lds.s_o;
+  auto& s_out = lds.s_out;
+  auto& s_last = lds.s_last;
+  const int tid = tid_x(), lane = tid & 63, w = tid >> 6;
   // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
   // a contiguous range of (robot, kv head, query block), so a robot's K/V
   // are fetched into one XCD's L2 rather than into all eight
-  int wg = blockIdx.x;
+  int wg = wgi;
   const int q8 = a.grid / 8;
   if (wg < 8 * q8) wg = (wg % 8) * q8 + wg / 8;
   const int ds = wg % DS;                              // head-dim part of the output
@@ -99,7 +109,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int s = qi / G, h = j * G + qi % G;
     const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
 #pragma unroll
-    for (int kb = 0; kb < KBD; ++kb) qf[u][kb] = *(const uint4*)(qp + kb * 32);
+    for (int kb = 0; kb < KBD; ++kb) qf[u][kb] = ld_u4<COH>(qp + kb * 32);
   }
   const KeySpace ks(a, b);
   const int nk16 = ks.kp >> 4, nk32 = ks.kp >> 5;  // kp is a multiple of 32
@@ -124,8 +134,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         kf[slot][kb] = uint4{r.x, r.y, 0u, 0u};
       }
     } else {
+      const bool suf = COH && nb * 16 >= ks.TP;  // this step's suffix keys: written in this launch
 #pragma unroll
-      for (int kb = 0; kb < KBD; ++kb) kf[slot][kb] = *(const uint4*)ks.ktile(j, nb, kb, lane);
+      for (int kb = 0; kb < KBD; ++kb) {
+        const uint16_t* kp = ks.ktile(j, nb, kb, lane);
+        kf[slot][kb] = suf ? ld_u4<true>(kp) : *(const uint4*)kp;
+      }
     }
   };
   float ksc[KV8 ? R : 1], vsc[KV8 ? R : 1];  // this lane's key's scales, per block
@@ -154,8 +168,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         vf[slot][n] = uint4{r.x, r.y, 0u, 0u};
       }
     } else {
+      const bool suf = COH && kb32 * 32 >= ks.TP;
 #pragma unroll
-      for (int n = 0; n < NBW; ++n) vf[slot][n] = *(const uint4*)ks.vtile(j, kb32, nbd0 + n, lane);
+      for (int n = 0; n < NBW; ++n) {
+        const uint16_t* vp = ks.vtile(j, kb32, nbd0 + n, lane);
+        vf[slot][n] = suf ? ld_u4<true>(vp) : *(const uint4*)vp;
+      }
     }
   };
 #pragma unroll
@@ -356,7 +374,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int qi = qb * 16 + row;
       if (qi < nq) {
         const int s2 = qi / G, h = j * G + qi % G;
-        *(uint4*)((uint16_t*)a.out + pk(b * a.S + s2, h * DH + c8, a.Hq * DH)) = *(const uint4*)&s_out[row][c8];
+        st_u4<COH>((uint16_t*)a.out + pk(b * a.S + s2, h * DH + c8, a.Hq * DH), *(const uint4*)&s_out[row][c8]);
       }
     }
     return;
@@ -403,9 +421,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qi = qb * QR + row;
     if (qi < nq) {
       const int s = qi / G, h = j * G + qi % G;
-      *(uint4*)((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH)) = *(const uint4*)&s_out[row][c8];
+      st_u4<COH>((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH), *(const uint4*)&s_out[row][c8]);
     }
   }
+}
+
+template <int DH, int R, int QB, int DS, bool PF, bool CAUSAL, bool KV8>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_sf(AttnArgs a) {
+  // weight prefetch workgroups (a separate instantiation: the test needs a
+  // kernel argument before the first load)
+  if constexpr (PF) if ((int)blockIdx.x >= a.grid) {
+    attn_weight_prefetch(a);
+    return;
+  }
+  __shared__ AttnSfSmem<DH, R, QB, DS> sm;
+  attn_sf_body<DH, R, QB, DS, CAUSAL, KV8, false>(a, blockIdx.x, sm);
 }
 
 template <int DH, int QB, int DS, bool PF, bool CAUSAL = false, bool KV8 = false>

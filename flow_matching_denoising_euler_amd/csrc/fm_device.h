@@ -81,6 +81,72 @@ __device__ __forceinline__ void drain_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Loads and stores of data that other workgroups of the same launch write or
+// read after a grid barrier (COH: device-scope sc1 accesses, which reach the
+// memory side of the 8 XCDs' non-coherent L2s; otherwise plain accesses,
+// ordered by kernel boundaries).
+// The thread index.  The persistent loop's unit defines FM_OPAQUE_TID: its
+// phases then recompute every value derived from the thread index instead of
+// having the optimiser hoist them out of the loop over layers and steps and
+// hold them in registers across every other phase (which spills).
+#ifdef FM_OPAQUE_TID
+__device__ __forceinline__ int tid_x() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+#else
+__device__ __forceinline__ int tid_x() { return threadIdx.x; }
+#endif
+
+template <bool COH>
+__device__ __forceinline__ float ld_f(const float* p) {
+  if constexpr (COH) return ld_dev(p);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ void st_f(float* p, float v) {
+  if constexpr (COH) st_dev(p, v);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ uint4 ld_u4(const void* p) {
+  if constexpr (COH) {
+    const unsigned long long a = __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long b =
+        __hip_atomic_load((unsigned long long*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4((unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32));
+  } else {
+    return *(const uint4*)p;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ float4 ld_f4(const float* p) {
+  const uint4 u = ld_u4<COH>(p);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+template <bool COH>
+__device__ __forceinline__ void st_u4(void* p, uint4 v) {
+  if constexpr (COH) {
+    __hip_atomic_store((unsigned long long*)p, (unsigned long long)v.x | ((unsigned long long)v.y << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((unsigned long long*)p + 1, (unsigned long long)v.z | ((unsigned long long)v.w << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *(uint4*)p = v;
+  }
+}
+template <int ACT, bool COH>
+__device__ __forceinline__ void st_act_c(void* p, long i, float v) {
+  if constexpr (!COH) {
+    st_act<ACT>(p, i, v);
+  } else if constexpr (ACT == ELT_F32) {
+    st_dev((float*)p + i, v);
+  } else {
+    __hip_atomic_store((uint16_t*)p + i, (uint16_t)f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 __device__ __forceinline__ float tab(const Tab& t, int step, int i) {
   return t.base ? t.base[(long)step * t.step_stride + i] : 0.f;
 }
@@ -209,7 +275,6 @@ __device__ __forceinline__ f32x4 mma_unit(const Frag<ACT>* a, const WFrag<ACT, W
 // ---------------------------------------------------------------------------
 
 constexpr int PM = 128;  // slots of h^2 partial sums per row (one per 16 columns, d <= 2048)
-constexpr int GW = 8;    // waves per GEMM / tail workgroup (512 threads)
 
 // Cross-lane reductions inside aligned groups of 8 or 16 lanes with DPP
 // moves (VALU operations, no trip through the LDS pipe): quad_perm
@@ -297,17 +362,18 @@ __device__ __forceinline__ Frag<ACT> load_a_pk(const void* A, int K, int mt, int
 
 // h^2 partials of the 64 rows of a tile, [M][PM]: thread t reads 16 slots of
 // row t >> 3 (4 float4), the sum is finished by rstd_finish.
+template <bool COH = false>
 __device__ __forceinline__ void rstd_load(const float* ssq, int M, int m0, float4 (&q)[4]) {
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   const int row = min(m0 + (tid >> 3), M - 1);
-  const float4* p = (const float4*)(ssq + (long)row * PM + (tid & 7) * 16);
+  const float* p = ssq + (long)row * PM + (tid & 7) * 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = p[i];
+  for (int i = 0; i < 4; ++i) q[i] = ld_f4<COH>(p + 4 * i);
 }
 // fixed-order sum: 16 slots in order, then a butterfly over the 8 lanes of the row
 __device__ __forceinline__ void rstd_finish(const float4 (&q)[4], int M, int m0, float inv_d, float eps,
                                             float* s_rstd) {
-  const int tid = threadIdx.x;
+  const int tid = tid_x();
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) s += ((q[i].x + q[i].y) + q[i].z) + q[i].w;
@@ -318,7 +384,7 @@ __device__ __forceinline__ void rstd_finish(const float4 (&q)[4], int M, int m0,
 // sum of the GW waves' accumulators in a fixed order: red[w] = acc(w+4) + acc(w), then ((r0+r1)+r2)+r3
 template <int NB>
 __device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[4][NB], float (*red)[64][33]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_x() & 63, wave = tid_x() >> 6;
   if (wave >= 4) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -341,96 +407,6 @@ __device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[4][NB], float (*
   }
   __syncthreads();
 }
-
-// One 64-row tile times 16*NB packed columns over k-units [0, units): wave w
-// owns the contiguous units [w*UPW*NPASS, (w+1)*UPW*NPASS), NPASS passes of
-// UPW.  The weights of every pass are loaded first, then pass 0's A
-// fragments; a later pass's A fragments are loaded after the previous
-// pass's MFMAs.
-template <int ACT, int WT, int NB, int UPW, int NPASS>
-struct SkinnyTile {
-  static constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
-  WFrag<ACT, WT> w[NPASS][UPW][NB];
-  Frag<ACT> a[UPW][4][KU];
-  f32x4 acc[4][NB];
-
-  int rw;      // k-range of this wave: rotated by workgroup so that workgroups read different A lines at once
-  int u0 = 0;  // first k-unit of the workgroup's range (split K)
-  int mv = 64; // rows of the tile below M: lanes of rows past it load nothing (those rows hold zeros)
-  __device__ __forceinline__ void set_range(int rot) { rw = ((threadIdx.x >> 6) + rot) & (GW - 1); }
-  __device__ __forceinline__ void load_w_all(const void* W, int NBT, int nb0, int units) {
-    const int lane = threadIdx.x & 63, wave = rw;
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p)
-#pragma unroll
-      for (int i = 0; i < UPW; ++i) {
-        const int u = min((wave * NPASS + p) * UPW + i, units - 1);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) w[p][i][nb] = load_w<ACT, WT>(W, NBT, nb0 + nb, u0 + u, lane);
-      }
-  }
-  // A is in the packed layout (pk)
-  __device__ __forceinline__ void load_a_pass(const void* A, int K, int mt, int units, int p) {
-    const int lane = threadIdx.x & 63, wave = rw;
-    // this tile's 64 rows x K block of the packed layout
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)A + (long)mt * K * 64), (short)0, K * 128, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int u = min((wave * NPASS + p) * UPW + i, units - 1);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int q = 0; q < KU; ++q) {
-          if constexpr (ACT == ELT_F32) {
-            a[i][mb][q] = load_a_pk<ACT>(A, K, mt, (u0 + u) * KU + q, mb, lane);
-          } else {
-            // bounds-checked buffer load: an offset past the range returns
-            // zeros without a memory access
-            const int kb = (u0 + u) * KU + q;
-            const uint32_t off = mb * 16 + (lane & 15) < mv ? (uint32_t)(((kb * 4 + mb) * 64 + lane) * 16) : 0x7FFFFFF0u;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-            a[i][mb][q].v = make_uint4(v[0], v[1], v[2], v[3]);
-          }
-        }
-    }
-  }
-  __device__ __forceinline__ void mma_pass(int units, int p) {
-    const int wave = rw;
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      if ((wave * NPASS + p) * UPW + i < units) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mma_unit<ACT, WT>(a[i][mb], w[p][i][nb], acc[mb][nb]);
-      }
-    }
-  }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Large-M GEMM (batched robots, MFMA-bound), bf16 activations and weights,
-// the same fused epilogues as the skinny GEMM.
-//
-// Workgroup = 4 waves in a 2 x 2 grid over a BM x BN tile (BM = 32 TMW rows,
-// BN = 32 TNW packed columns); wave (wm, wn) owns TMW row blocks x TNW
-// column blocks of 16.  Both operands are in MFMA fragment order in memory
-// (1 KB per 16 x 32 fragment), so each stage (KS k-blocks of 32) is
-// copied fragment by fragment straight into LDS (global_load_lds_dwordx4:
-// lane i's 16 bytes land at M0 + 16 i) into a ring of three slots, and the
-// waves read their fragments with conflict-free 16-byte LDS reads.  The
-// weight fragment is the MFMA's first operand, so a lane's accumulator holds
-// 4 consecutive output columns of one row: the epilogues load and store
-// 8- and 16-byte vectors.  KG = 2 runs two k-groups of 4 waves over
-// alternate k-blocks of each stage; they add their accumulators through LDS.
-// ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -474,6 +450,329 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// One 64-row tile times 16*NB packed columns over k-units [0, units): wave w
+// owns the contiguous units [w*UPW*NPASS, (w+1)*UPW*NPASS), NPASS passes of
+// UPW.  The weights of every pass are loaded first, then pass 0's A
+// fragments; a later pass's A fragments are loaded after the previous
+// pass's MFMAs.
+template <int ACT, int WT, int NB, int UPW, int NPASS>
+struct SkinnyTile {
+  static constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
+  WFrag<ACT, WT> w[NPASS][UPW][NB];
+  Frag<ACT> a[UPW][4][KU];
+  f32x4 acc[4][NB];
+
+  int rw;      // k-range of this wave: rotated by workgroup so that workgroups read different A lines at once
+  int u0 = 0;  // first k-unit of the workgroup's range (split K)
+  int mv = 64; // rows of the tile below M: lanes of rows past it load nothing (those rows hold zeros)
+  __device__ __forceinline__ void set_range(int rot) { rw = ((tid_x() >> 6) + rot) & (GW - 1); }
+  __device__ __forceinline__ void load_w_all(const void* W, int NBT, int nb0, int units) {
+    const int lane = tid_x() & 63, wave = rw;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+      for (int i = 0; i < UPW; ++i) {
+        const int u = min((wave * NPASS + p) * UPW + i, units - 1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) w[p][i][nb] = load_w<ACT, WT>(W, NBT, nb0 + nb, u0 + u, lane);
+      }
+  }
+  // A is in the packed layout (pk); COH: device-scope (sc1) loads
+  template <bool COH = false>
+  __device__ __forceinline__ void load_a_pass(const void* A, int K, int mt, int units, int p) {
+    const int lane = tid_x() & 63, wave = rw;
+    // this tile's 64 rows x K block of the packed layout
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)A + (long)mt * K * 64), (short)0, K * 128, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int u = min((wave * NPASS + p) * UPW + i, units - 1);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < KU; ++q) {
+          if constexpr (ACT == ELT_F32) {
+            a[i][mb][q] = load_a_pk<ACT>(A, K, mt, (u0 + u) * KU + q, mb, lane);
+          } else {
+            // bounds-checked buffer load: an offset past the range returns
+            // zeros without a memory access
+            const int kb = (u0 + u) * KU + q;
+            const uint32_t off = mb * 16 + (lane & 15) < mv ? (uint32_t)(((kb * 4 + mb) * 64 + lane) * 16) : 0x7FFFFFF0u;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, COH ? 16 : 0);  // 16: sc1
+            a[i][mb][q].v = make_uint4(v[0], v[1], v[2], v[3]);
+          }
+        }
+    }
+  }
+  // Persistent loops: the weight tiles go straight into LDS (1 KB slot per
+  // tile, slot ((hw * NPASS + p) * UPW + i) * NB + nb of hardware wave hw),
+  // holding no registers while they stream.  Waves 1..7 issue the copies of
+  // all eight waves' slots, so that wave 0, which polls the grid barrier,
+  // has none of them in its load counter.  Readers wait for the copies
+  // (wait_vmcnt<0> in the issuing waves, then a workgroup barrier).
+  __device__ __forceinline__ void copy_w_lds(const void* W, int NBT, int nb0, int units, uint32_t lds) {
+    constexpr int NS = GW * NPASS * UPW * NB;  // slots of the workgroup
+    const int lane = tid_x() & 63, hw = __builtin_amdgcn_readfirstlane(tid_x() >> 6);  // uniform: M0
+    if (hw == 0) return;
+    const int rot = rw - hw;  // the workgroup's rotation of the k-ranges
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += GW - 1) {
+      const int s = s0 + hw - 1;
+      if (s < NS) {
+        const int nb = s % NB, i = (s / NB) % UPW, p = (s / (NB * UPW)) % NPASS, sw = s / (NB * UPW * NPASS);
+        const int wrange = (sw + rot) & (GW - 1);
+        const int u = min((wrange * NPASS + p) * UPW + i, units - 1);
+        const uint8_t* src = (const uint8_t*)W + (((long)(u0 + u) * NBT + nb0 + nb) * 64 + lane) * 16;
+        lds_dma16(src, lds + (uint32_t)s * 1024u);
+      }
+    }
+  }
+  __device__ __forceinline__ void mma_pass_lds(int units, int p, const uint8_t* lds) {
+    const int wave = rw, lane = tid_x() & 63, hw = tid_x() >> 6;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      if ((wave * NPASS + p) * UPW + i < units) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          WFrag<ACT, WT> wf;
+          wf.v = *(const uint4*)(lds + (((hw * NPASS + p) * UPW + i) * NB + nb) * 1024 + lane * 16);
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mma_unit<ACT, WT>(a[i][mb], wf, acc[mb][nb]);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void mma_pass(int units, int p) {
+    const int wave = rw;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      if ((wave * NPASS + p) * UPW + i < units) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mma_unit<ACT, WT>(a[i][mb], w[p][i][nb], acc[mb][nb]);
+      }
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// LDS of one skinny GEMM work item
+struct GemmSmem {
+  float red[4][64][33];
+  float s_rstd[64];
+  float s_col[3][32];  // per column: bias or alpha, gnext, fp8 scale
+  int s_last;
+};
+
+// Skinny GEMM with fused epilogues: work item vb = one 64-row x 16*NB-column
+// output tile (and, for the residual GEMMs, one of ksplit k-ranges) for 512
+// threads.  pre() issues the work item's weight loads, which do not depend on
+// the activations (a persistent loop issues them before the grid barrier that
+// precedes the phase); run() does everything else.  COH: the activations,
+// norm statistics and residual stream are produced by other workgroups of the
+// same launch (device-scope loads and stores).
+template <int ACT, int WT, int EPI, int NB, int UPW, int NPASS, bool COH>
+struct SkinnyGemm {
+  static constexpr int NT = 512, nt = NB * 16, PER = NB * 2;
+  static constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
+  SkinnyTile<ACT, WT, NB, UPW, NPASS> t;
+
+  __device__ __forceinline__ void pre(const GemmArgs& g, int vb) {
+    const int ks = vb % g.ksplit, tb = vb / g.ksplit, nti = tb % (g.N / nt);
+    const int units = (g.K >> 5) / KU / g.ksplit;
+    t.set_range(vb);
+    t.u0 = ks * units;
+    t.load_w_all(g.W, g.N >> 4, (nti * nt) >> 4, units);
+  }
+
+  // persistent loops: the same work item's weights into LDS slots at lds_w
+  // (see SkinnyTile::copy_w_lds); run_lds reads them from there
+  __device__ __forceinline__ void pre_lds(const GemmArgs& g, int vb, uint32_t lds_w) {
+    const int ks = vb % g.ksplit, tb = vb / g.ksplit, nti = tb % (g.N / nt);
+    const int units = (g.K >> 5) / KU / g.ksplit;
+    t.set_range(vb);
+    t.u0 = ks * units;
+    t.copy_w_lds(g.W, g.N >> 4, (nti * nt) >> 4, units, lds_w);
+  }
+
+  template <bool WLDS = false>
+  __device__ __forceinline__ void run(const GemmArgs& g, int vb, GemmSmem& sm, const uint8_t* lds_w = nullptr) {
+  auto& red = sm.red;
+  auto& s_rstd = sm.s_rstd;
+  auto& s_col = sm.s_col;
+  auto& s_last = sm.s_last;
+  const int tid = tid_x();
+  const int ntiles = g.N / nt;
+  // split K (residual GEMMs): workgroup = (tile, k-range); the ranges of a
+  // tile are summed in range order by the last to arrive
+  const int ks = vb % g.ksplit, tb = vb / g.ksplit;
+  const int nti = tb % ntiles, mt = tb / ntiles;
+  const int n0 = nti * nt, m0 = mt * 64;
+  const int units = (g.K >> 5) / KU / g.ksplit;
+
+  // epilogue operands first (registers), then the GEMM operands
+  const int ccol = n0 + min(tid, nt - 1);
+  const float c0 = EPI == EPI_RESID ? g.alpha.base[(long)g.step * g.alpha.step_stride + ccol]
+                                    : g.bias.base[(long)g.step * g.bias.step_stride + ccol];
+  const float c1 = EPI == EPI_RESID ? g.gnext.base[(long)g.step * g.gnext.step_stride + ccol] : 0.f;
+  const float c2 = WT == ELT_FP8 ? g.wscale[ccol] : 1.f;
+  float4 q[4];
+  if (EPI != EPI_RESID) rstd_load<COH>(g.ssq, g.M, m0, q);
+  float hold[PER];
+  if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + NT * i;
+      hold[i] = ld_f<COH>(g.h + (long)min(m0 + (idx >> 4), g.M - 1) * g.N + n0 + (idx & 15));
+    }
+  }
+  t.mv = g.M - m0;
+  t.zero();
+  t.template load_a_pass<COH>(g.A, g.K, mt, units, 0);
+  if constexpr (WLDS) {
+    static_assert(NPASS == 1, "LDS weights: one pass");
+    wait_vmcnt<0>();  // this wave's weight copies (and everything else) landed
+    barrier_nofence();  // every wave's copies landed
+    t.mma_pass_lds(units, 0, lds_w);
+  } else {
+    t.mma_pass(units, 0);
+#pragma unroll
+    for (int p = 1; p < NPASS; ++p) {
+      t.template load_a_pass<COH>(g.A, g.K, mt, units, p);
+      t.mma_pass(units, p);
+    }
+  }
+  if (tid < nt) {
+    s_col[0][tid] = c0;
+    s_col[1][tid] = c1;
+    s_col[2][tid] = c2;
+  }
+  if (EPI != EPI_RESID) rstd_finish(q, g.M, m0, g.inv_d, g.eps, s_rstd);
+  reduce_waves<NB>(t.acc, red);
+
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + NT * i, row = idx / nt, col = idx % nt;
+    v[i] = ((red[0][row][col] + red[1][row][col]) + red[2][row][col]) + red[3][row][col];
+  }
+  if constexpr (EPI == EPI_RESID) if (g.ksplit > 1) {
+    // every range stores its partial tile (device scope); the last to arrive
+    // adds the ranges in order (ksplit <= 4), own range from the registers
+    float* mine = g.partials + ((long)tb * g.ksplit + ks) * (64 * nt);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) st_dev(mine + tid + NT * i, v[i]);
+    drain_vm();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(g.counters + tb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)g.ksplit - 1;
+      if (s_last) __hip_atomic_store(g.counters + tb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    float pv[4][PER];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        pv[k2][i] = ld_dev(g.partials + ((long)tb * g.ksplit + min(k2, g.ksplit - 1)) * (64 * nt) + tid + NT * i);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float sum = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2)
+        if (k2 < g.ksplit) sum += (k2 == ks) ? v[i] : pv[k2][i];
+      v[i] = sum;
+    }
+  }
+
+  if constexpr (EPI == EPI_QKV || EPI == EPI_QKVR) {
+    // Q columns -> out (row-major); suffix K and V -> their kv-layout blocks
+    const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
+    constexpr bool packed = ACT != ELT_F32;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + NT * i, row = idx / nt, c = idx % nt;
+      const int r = m0 + row, col = n0 + c;
+      const float val = v[i] * s_col[2][c] * s_rstd[row] + s_col[0][c];
+      if (r < g.M) {
+        const int b = r / g.S, sr = r % g.S;
+        const long sb = (long)b * g.Hkv * g.Dh * g.SP;
+        const long rw = EPI == EPI_QKVR ? (long)b * g.row_bstride + (long)sr * (g.Hkv * g.Dh) : 0;  // encoder rows
+        if (col < kcol0) {
+          st_act_c<ACT, COH>(g.out, (long)r * g.N + col, val);
+        } else if (col < vcol0) {
+          const int jk = (col - kcol0) / g.Dh, dh = (col - kcol0) % g.Dh;
+          st_act_c<ACT, COH>(g.ksuf, sb + kv_k_off(packed, g.SP, g.Hkv, g.Dh, jk, sr, dh), val);
+          if constexpr (EPI == EPI_QKVR) st_act<ACT>(g.krow, rw + (col - kcol0), val);
+        } else {
+          const int jv = (col - vcol0) / g.Dh, dh = (col - vcol0) % g.Dh;
+          st_act_c<ACT, COH>(g.vsuf, sb + kv_v_off(packed, g.SP, g.Hkv, g.Dh, jv, sr, dh), val);
+          if constexpr (EPI == EPI_QKVR) st_act<ACT>(g.vrow, rw + (col - vcol0), val);
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_GELU) {
+    // tile = [16 gate | 16 up] (NB == 2): pair them through red[0]
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + NT * i;
+      red[0][idx / nt][idx % nt] = v[i];
+    }
+    __syncthreads();
+    const int F = g.N >> 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + NT * i, row = idx >> 4, j = idx & 15;
+      const int r = m0 + row;
+      const float gv = red[0][row][j] * s_col[2][j] * s_rstd[row] + s_col[0][j];
+      const float uv = red[0][row][16 + j] * s_col[2][16 + j] * s_rstd[row] + s_col[0][16 + j];
+      if (r < g.M) st_act_c<ACT, COH>(g.out, pk(r, nti * 16 + j, F), gelu_erf(gv) * uv);
+    }
+  } else {  // EPI_RESID (NB == 1): the 16 threads of a row are consecutive lanes
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + NT * i, row = idx >> 4, c = idx & 15;
+      const int r = m0 + row;
+      const float hn = (r < g.M) ? hold[i] + s_col[0][c] * (v[i] * s_col[2][c]) : 0.f;
+      float qq = hn * hn;
+      qq = sum16(qq);
+      if (r < g.M) {
+        const long o = (long)r * g.N + n0 + c;
+        st_f<COH>(g.h + o, hn);
+        st_act_c<ACT, COH>(g.u_out, pk(r, n0 + c, g.N), hn * s_col[1][c]);
+        if (c == 0) st_f<COH>(g.ssq_out + (long)r * PM + (n0 >> 4), qq);
+      }
+    }
+  }
+}
+};
+
+// ---------------------------------------------------------------------------
+// Large-M GEMM (batched robots, MFMA-bound), bf16 activations and weights,
+// the same fused epilogues as the skinny GEMM.
+//
+// Workgroup = 4 waves in a 2 x 2 grid over a BM x BN tile (BM = 32 TMW rows,
+// BN = 32 TNW packed columns); wave (wm, wn) owns TMW row blocks x TNW
+// column blocks of 16.  Both operands are in MFMA fragment order in memory
+// (1 KB per 16 x 32 fragment), so each stage (KS k-blocks of 32) is
+// copied fragment by fragment straight into LDS (global_load_lds_dwordx4:
+// lane i's 16 bytes land at M0 + 16 i) into a ring of three slots, and the
+// waves read their fragments with conflict-free 16-byte LDS reads.  The
+// weight fragment is the MFMA's first operand, so a lane's accumulator holds
+// 4 consecutive output columns of one row: the epilogues load and store
+// 8- and 16-byte vectors.  KG = 2 runs two k-groups of 4 waves over
+// alternate k-blocks of each stage; they add their accumulators through LDS.
+// ---------------------------------------------------------------------------
+
 // 64-bit device-scope store / load (coherent across XCDs, see st_dev)
 __device__ __forceinline__ void st_dev2(float* p, float a, float b) {
   const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
@@ -652,7 +951,7 @@ struct EmbedCol {
   float hsv[8];
   __device__ __forceinline__ void load(int c0, int A, const void* w_in, const void* b_in, const Tab& temb,
                                        const Tab& g1, int step, const float* hs, int m0, int M, int S, int d) {
-    const int col = c0 + (threadIdx.x & 63);
+    const int col = c0 + (tid_x() & 63);
     // the column's A weights are contiguous (A = 16 or 32): 16-byte vector loads
     if constexpr (WE == ELT_F32) {
       const float4* p = (const float4*)((const float*)w_in + (long)col * A);
@@ -683,18 +982,18 @@ struct EmbedCol {
     gain = g1.base[(long)step * g1.step_stride + col];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = min(m0 + (threadIdx.x >> 6) + 8 * i, M - 1);
+      const int r = min(m0 + (tid_x() >> 6) + 8 * i, M - 1);
       hsv[i] = hs[(long)(r / S) * d + col];
     }
   }
   // h, u = act(h * gain) and the h^2 partial of this 16-column group
-  template <int ACT>
+  template <int ACT, bool COH = false>
   __device__ __forceinline__ void emit(int c0, int m0, int M, int S, int has_state, int A, int d,
                                        const float (*s_x)[33], float* h, void* u, float* ssq_out) {
-    const int col = c0 + (threadIdx.x & 63);
+    const int col = c0 + (tid_x() & 63);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int lr = (threadIdx.x >> 6) + 8 * i, r = m0 + lr;
+      const int lr = (tid_x() >> 6) + 8 * i, r = m0 + lr;
       float acc = 0.f;
 #pragma unroll
       for (int a = 0; a < 32; ++a) acc += (a < A ? s_x[lr][a] : 0.f) * w[a];
@@ -703,13 +1002,82 @@ struct EmbedCol {
       float q = hv * hv;
       q = sum16(q);
       if (r < M) {
-        h[(long)r * d + col] = hv;
-        st_act<ACT>(u, pk(r, col, d), hv * gain);
-        if ((threadIdx.x & 15) == 0) ssq_out[(long)r * PM + (col >> 4)] = q;
+        st_f<COH>(h + (long)r * d + col, hv);
+        st_act_c<ACT, COH>(u, pk(r, col, d), hv * gain);
+        if ((tid_x() & 15) == 0) st_f<COH>(ssq_out + (long)r * PM + (col >> 4), q);
       }
     }
   }
 };
+
+// LDS of one tail work item
+struct OutSmem {
+  float red[4][64][33];
+  float s_rstd[64];
+  float s_x[64][33];
+};
+
+// One tail work item vb = (64-row tile, 64-column embedding slice).  COH: its
+// inputs (final norm operand, x, the previous velocity) and outputs come
+// from and go to other workgroups of the same launch (device-scope accesses).
+template <int ACT, int WE, int NB, bool COH>
+__device__ __forceinline__ void out_body(const OutArgs& o, int vb, OutSmem& sm) {
+  constexpr int UPW = 4;
+  auto& red = sm.red;
+  auto& s_rstd = sm.s_rstd;
+  auto& s_x = sm.s_x;
+  const int mt = vb / o.esplit, es = vb % o.esplit;
+  const int m0 = mt * 64, c0 = es * 64;
+  const int tid = tid_x();
+  const int units = o.d >> 5;
+  // every operand first: head weights, u_f, h^2 partials, x, b_out, the embedding's operands
+  float4 q[4];
+  rstd_load<COH>(o.ssq, o.M, m0, q);
+  float xin[4], bo[4], vp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = min(m0 + lr, o.M - 1);
+    const int b = r / o.S, s = r % o.S;
+    const int ar = b * o.C + max(s - o.has_state, 0);
+    xin[i] = ld_f<COH>(o.x_in + (long)ar * o.A + min(a, o.A - 1));
+    bo[i] = o.bout.base[(long)o.t_idx * o.bout.step_stride + min(a, o.A - 1)];
+    vp[i] = o.v_prev ? ld_f<COH>(o.v_prev + (long)ar * o.A + min(a, o.A - 1)) : 0.f;
+  }
+  EmbedCol<WE> ec;
+  if (o.do_embed) ec.load(c0, o.A, o.w_in, o.b_in, o.temb, o.g1, o.embed_step, o.hs, m0, o.M, o.S, o.d);
+  SkinnyTile<ACT, WE, NB, UPW, 1> t;
+  t.zero();
+  t.set_range(vb);
+  t.mv = o.M - m0;
+  t.load_w_all(o.Wout, NB, 0, units);
+  t.template load_a_pass<COH>(o.uf, o.d, mt, units, 0);
+  t.mma_pass(units, 0);
+  rstd_finish(q, o.M, m0, o.inv_d, o.eps, s_rstd);
+  reduce_waves<NB>(t.acc, red);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
+    const bool act_row = r < o.M && a < o.A && !(o.has_state && (r % o.S) == 0);
+    float xv = 0.f;
+    if (act_row) {
+      const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
+      const float v = acc * s_rstd[lr] + bo[i];
+      xv = o.heun == 2   ? xin[i] + o.dt * (0.5f * (vp[i] + v))
+           : o.heun == 3 ? xin[i] + o.dt * (o.c_cur * v - o.c_prev * vp[i])
+                         : xin[i] + o.dt * v;
+      if (es == 0) {
+        const int b = r / o.S, s = r % o.S;
+        const long xo = (long)(b * o.C + s - o.has_state) * o.A + a;
+        if (o.heun == 1 || o.heun == 3) st_f<COH>(o.v_save + xo, v);
+        if (o.heun != 1) st_f<COH>(o.x_out + xo, xv);
+      }
+    }
+    s_x[lr][a] = xv;
+  }
+  if (!o.do_embed) return;
+  __syncthreads();
+  ec.template emit<ACT, COH>(c0, m0, o.M, o.S, o.has_state, o.A, o.d, s_x, o.h, o.u, o.ssq_out);
+}
 
 // ---------------------------------------------------------------------------
 // launchers

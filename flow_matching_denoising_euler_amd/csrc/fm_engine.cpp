@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -83,6 +84,17 @@ struct fm_ctx {
   size_t n_counters;
   size_t part_bytes = 0, attn_part_bytes = 0;  // scratch sizes (split-K and key-split partials)
   int device = 0;
+
+  // the persistent loop (exec mode FM_EXEC_PERSISTENT)
+  bool persist = false;
+  int p_R = 0, p_DS = 0;       // its attention instantiation
+  int n_evals = 0;             // velocity evaluations per chunk
+  PersistEval* pev = nullptr;  // [n_evals] per-evaluation scalars (arena)
+  unsigned* pbar = nullptr;    // barrier counter, time-out flag (arena)
+  PersistArgs pargs{};         // built at create; actions set per call
+  std::string trace_path;      // FM_PERSIST_TRACE: barrier stamps written at destroy
+  unsigned long long* trace = nullptr;
+  size_t trace_n = 0;
   void *enc_k[2], *enc_v[2];  // encoder output rows [B][L][S][HD] act, two slots used in turn
   int enc_slot = 0;            // slot the graph being captured writes
 
@@ -296,6 +308,44 @@ void derive(fm_ctx* x) {
   }
 }
 
+// Whether the persistent loop kernel covers this context; on false, *why
+// says which condition fails.  Its instantiations: bf16 activations, bf16 or
+// fp8 weights, one 64-row tile, head_dim 256, action_dim 32, the plain
+// attention (no block-causal state, no fp8 cache, no rotary positions) of
+// the register kernel, and the skinny GEMMs' k-units per wave of the
+// Pi0-shaped expert (persist_upw).
+bool persist_plan(fm_ctx* x, const char** why) {
+  const fm_config& c = x->cfg;
+  auto no = [&](const char* m) { *why = m; return false; };
+  if (x->encoder) return no("encoder context");
+  if (x->act != ELT_BF16 || x->wt == ELT_F32) return no("needs bf16 activations and bf16 or fp8 weights");
+  if (x->mtiles != 1) return no("needs batch x suffix <= 64 rows");
+  if (x->Dh != 256 || x->A != 32) return no("needs head_dim 256 and action_dim 32");
+  if ((c.state_causal && x->hasS) || x->kv8 || c.rope_theta > 0.f)
+    return no("the block-causal state, the fp8 cache and rotary positions run as a graph");
+  if ((x->TP + x->SP) / 32 > 32) return no("more than 1024 padded keys");
+  const int groups = x->B * x->Hkv * x->nqblk;
+  if (groups > 64) return no("more than 64 query groups");
+  const bool split = x->nsplit > 1;
+  const int kps = split ? x->kps : ((x->TP + x->SP) / 16 + 1) / 2 * 2;
+  x->p_R = (kps + 7) / 8;
+  x->p_DS = split ? 2 : 4;
+  if (!persist_attn_ok(x->p_R, x->p_DS, split)) return no("no attention instantiation for this key count");
+  const int KU = x->wt == ELT_FP8 ? 2 : 1;
+  auto pw = [&](int K, int ks) { return ((K >> 5) / KU / ks + GW - 1) / GW; };
+  const PersistUpw u = persist_upw(x->wt);
+  if (pw(x->d, 1) != u.q || pw(x->Hq * x->Dh, x->ks_o) != u.o || pw(x->d, 1) != u.gu || pw(x->F, x->ks_d) != u.d)
+    return no("GEMM shapes other than the Pi0-shaped expert's");
+  const int grids[] = {x->Nqkv / 16, groups * x->nsplit * x->p_DS, x->d / 16 * x->ks_o, 2 * x->F / 32,
+                       x->d / 16 * x->ks_d, x->mtiles * x->esplit};
+  for (int g : grids)
+    if (g > x->n_cu) return no("a phase has more work items than the device has CUs");
+  int per_cu = 0;
+  if (persist_occupancy(x->wt, x->p_R, x->p_DS, &per_cu) != hipSuccess || per_cu < 1)
+    return no("the kernel does not fit a CU");
+  return true;
+}
+
 // carve every buffer from the arena (plan pass when a.plan)
 void carve(fm_ctx* x, Arena& a) {
   const size_t ew = elt_size(x->wt), ea = elt_size(x->act), eg = elt_size(x->ge);
@@ -371,6 +421,9 @@ void carve(fm_ctx* x, Arena& a) {
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
                                    (size_t)x->B * x->Hkv * x->nqblk * 2) + 64;
   x->counters = (unsigned*)a.take(x->n_counters * 4);
+  x->n_evals = x->N * (x->heun ? 2 : 1);
+  x->pev = x->persist ? (PersistEval*)a.take(x->n_evals * sizeof(PersistEval)) : nullptr;
+  x->pbar = x->persist ? (unsigned*)a.take(1280) : nullptr;  // 8 counters 128 B apart, the time-out flag
   const size_t kvo = x->encoder ? (size_t)x->B * L * x->S * x->HD * ea : 16;
   for (int j = 0; j < 2; ++j) {
     x->enc_k[j] = a.take(kvo);
@@ -380,14 +433,13 @@ void carve(fm_ctx* x, Arena& a) {
 
 Tab T(const float* base, long stride) { return Tab{base, stride}; }
 
-// one phase kernel of step k, layer l
-fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
-  const float eps = x->cfg.rms_eps, inv_d = 1.f / (float)x->d;
+// arguments of the GEMM of phase `phase` (QKV, O, gate/up, down) of step k, layer l
+GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
-  const long Tl = (long)x->TP * x->HD;  // elements per (robot, layer) of prefix K (and of V^T)
   const LayerW& w = x->lw[l];
   GemmArgs g{};
-  g.M = x->M; g.mtiles = x->mtiles; g.ssq = x->ssq; g.P = x->P; g.inv_d = inv_d; g.eps = eps; g.step = k;
+  g.M = x->M; g.mtiles = x->mtiles; g.ssq = x->ssq; g.P = x->P; g.inv_d = 1.f / (float)x->d; g.eps = x->cfg.rms_eps;
+  g.step = k;
   g.partials = x->partials; g.counters = x->counters;
   g.h = x->h;
   if (phase == FM_PHASE_QKV) {  // norm1 -> QKV
@@ -401,7 +453,73 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
       g.vrow = (char*)x->enc_v[x->enc_slot] + lo;
       g.row_bstride = (long)x->L * x->S * x->HD;
     }
-    HIPCHK(x, launch_gemm(x->act, x->wt, x->encoder ? EPI_QKVR : EPI_QKV, g, st), "qkv gemm");
+  } else if (phase == FM_PHASE_OPROJ) {  // O projection + residual; u = act(h * g2), ssq
+    g.A = x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16; g.ksplit = x->ks_o;
+    g.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(x->ones, 0);
+    g.gnext = T(x->g2 + (long)l * x->d, x->st_g);
+    g.u_out = x->u; g.ssq_out = x->ssq;
+  } else if (phase == FM_PHASE_GATEUP) {  // norm2 -> gate/up -> GELU gate
+    g.A = x->u; g.W = w.wgu; g.wscale = w.sgu; g.N = 2 * x->F; g.K = x->d; g.nt = 32; g.ksplit = 1;
+    g.out = x->z;
+    g.bias = ada ? T(x->bgu + (long)l * 2 * x->F, x->st_bgu) : T(x->zeros, 0);
+  } else {  // down + residual; writes the next norm's input
+    g.A = x->z; g.W = w.wd; g.wscale = w.sd; g.N = x->d; g.K = x->F; g.nt = 16; g.ksplit = x->ks_d;
+    g.alpha = ada ? T(x->a2 + (long)l * x->d, x->st_g) : T(x->ones, 0);
+    const bool last = l + 1 == x->L;
+    g.gnext = last ? T(x->gf, x->st_gf) : T(x->g1 + (long)(l + 1) * x->d, x->st_g);
+    g.u_out = last ? x->uf : x->u;
+    g.ssq_out = last ? x->ssqf : x->ssq;
+  }
+  return g;
+}
+
+// arguments of the attention of layer l (the same for every step)
+AttnArgs attn_args(const fm_ctx* x, int l) {
+  const long Tl = (long)x->TP * x->HD;  // elements per (robot, layer) of prefix K (and of V^T)
+  const LayerW& w = x->lw[l];
+  AttnArgs at{};
+  at.qkv = x->qkv;
+  const size_t ekv = x->kv8 ? 1 : elt_size(x->act);
+  at.kpre = (const char*)x->kpre + (size_t)l * Tl * ekv;
+  at.vpre = (const char*)x->vpre + (size_t)l * Tl * ekv;
+  if (x->kv8) {
+    at.kscale = x->kscale + (size_t)l * x->TP * x->Hkv;
+    at.vscale = x->vscale + (size_t)l * x->TP * x->Hkv;
+    at.sc_bstride = (long)x->L * x->TP * x->Hkv;
+  }
+  at.ksuf = x->ksuf;
+  at.vsuf = x->vsuf;
+  at.b_stride = (long)x->L * Tl;
+  at.meta = x->meta;
+  at.B = x->B; at.S = x->S; at.SP = x->SP; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
+  at.n_static = x->cfg.prefix_static; at.NSP = x->NSP; at.TP = x->TP;
+  at.frame_tokens = std::max(1, x->cfg.frame_tokens);
+  at.n_frames = std::max(1, x->cfg.n_frames);
+  at.ring = x->cfg.n_frames > 0;
+  at.nqblk = x->nqblk; at.nsplit = x->nsplit; at.keys_per_split = x->kps;
+  at.scale = 1.f / sqrtf((float)x->Dh);
+  at.part = x->attn_part; at.counters = x->counters;
+  at.out = x->o;
+  at.state_causal = x->cfg.state_causal && x->hasS;
+  if (x->mtiles == 1 && x->act == ELT_BF16) {
+    // one row tile: the O and gate/up GEMMs run skinny, workgroup u reading
+    // column tile u / ks and k-range u % ks; the idle CUs prefetch them
+    const int ku = x->wt == ELT_FP8 ? 64 : 32;  // k per 1 KB weight tile
+    at.pf_cus = x->n_cu;
+    at.pf_w[0] = (const uint8_t*)w.wo;
+    at.pf_nbt[0] = x->d / 16; at.pf_ku[0] = x->Hq * x->Dh / ku; at.pf_nb[0] = 1; at.pf_ks[0] = x->ks_o;
+    at.pf_units[0] = x->d / 16 * x->ks_o;
+    at.pf_w[1] = (const uint8_t*)w.wgu;
+    at.pf_nbt[1] = 2 * x->F / 16; at.pf_ku[1] = x->d / ku; at.pf_nb[1] = 2; at.pf_ks[1] = 1;
+    at.pf_units[1] = x->F / 16;
+  }
+  return at;
+}
+
+// one phase kernel of step k, layer l
+fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
+  if (phase == FM_PHASE_QKV) {
+    HIPCHK(x, launch_gemm(x->act, x->wt, x->encoder ? EPI_QKVR : EPI_QKV, gemm_args(x, k, l, phase), st), "qkv gemm");
     if (x->cfg.rope_theta > 0.f) {  // rotary embedding of this step's suffix Q and K
       RopeArgs r{};
       r.qkv = x->qkv; r.ksuf = x->ksuf; r.meta = x->meta;
@@ -410,62 +528,13 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
       HIPCHK(x, launch_rope(x->act, r, st), "rope");
     }
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
-    AttnArgs at{};
-    at.qkv = x->qkv;
-    const size_t ekv = x->kv8 ? 1 : elt_size(x->act);
-    at.kpre = (const char*)x->kpre + (size_t)l * Tl * ekv;
-    at.vpre = (const char*)x->vpre + (size_t)l * Tl * ekv;
-    if (x->kv8) {
-      at.kscale = x->kscale + (size_t)l * x->TP * x->Hkv;
-      at.vscale = x->vscale + (size_t)l * x->TP * x->Hkv;
-      at.sc_bstride = (long)x->L * x->TP * x->Hkv;
-    }
-    at.ksuf = x->ksuf;
-    at.vsuf = x->vsuf;
-    at.b_stride = (long)x->L * Tl;
-    at.meta = x->meta;
-    at.B = x->B; at.S = x->S; at.SP = x->SP; at.Hq = x->Hq; at.Hkv = x->Hkv; at.Dh = x->Dh; at.Nqkv = x->Nqkv;
-    at.n_static = x->cfg.prefix_static; at.NSP = x->NSP; at.TP = x->TP;
-    at.frame_tokens = std::max(1, x->cfg.frame_tokens);
-    at.n_frames = std::max(1, x->cfg.n_frames);
-    at.ring = x->cfg.n_frames > 0;
-    at.nqblk = x->nqblk; at.nsplit = x->nsplit; at.keys_per_split = x->kps;
-    at.scale = 1.f / sqrtf((float)x->Dh);
-    at.part = x->attn_part; at.counters = x->counters;
-    at.out = x->o;
-    at.state_causal = x->cfg.state_causal && x->hasS;
-    if (x->mtiles == 1 && x->act == ELT_BF16) {
-      // one row tile: the O and gate/up GEMMs run skinny, workgroup u reading
-      // column tile u / ks and k-range u % ks; the idle CUs prefetch them
-      const int ku = x->wt == ELT_FP8 ? 64 : 32;  // k per 1 KB weight tile
-      at.pf_cus = x->n_cu;
-      at.pf_w[0] = (const uint8_t*)w.wo;
-      at.pf_nbt[0] = x->d / 16; at.pf_ku[0] = x->Hq * x->Dh / ku; at.pf_nb[0] = 1; at.pf_ks[0] = x->ks_o;
-      at.pf_units[0] = x->d / 16 * x->ks_o;
-      at.pf_w[1] = (const uint8_t*)w.wgu;
-      at.pf_nbt[1] = 2 * x->F / 16; at.pf_ku[1] = x->d / ku; at.pf_nb[1] = 2; at.pf_ks[1] = 1;
-      at.pf_units[1] = x->F / 16;
-    }
-    HIPCHK(x, launch_attn(x->act, at, st), "attention");
-  } else if (phase == FM_PHASE_OPROJ) {  // O projection + residual; u = act(h * g2), ssq
-    g.A = x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16; g.ksplit = x->ks_o;
-    g.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(x->ones, 0);
-    g.gnext = T(x->g2 + (long)l * x->d, x->st_g);
-    g.u_out = x->u; g.ssq_out = x->ssq;
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, g, st), "o gemm");
-  } else if (phase == FM_PHASE_GATEUP) {  // norm2 -> gate/up -> GELU gate
-    g.A = x->u; g.W = w.wgu; g.wscale = w.sgu; g.N = 2 * x->F; g.K = x->d; g.nt = 32; g.ksplit = 1;
-    g.out = x->z;
-    g.bias = ada ? T(x->bgu + (long)l * 2 * x->F, x->st_bgu) : T(x->zeros, 0);
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_GELU, g, st), "gate/up gemm");
-  } else {  // down + residual; writes the next norm's input
-    g.A = x->z; g.W = w.wd; g.wscale = w.sd; g.N = x->d; g.K = x->F; g.nt = 16; g.ksplit = x->ks_d;
-    g.alpha = ada ? T(x->a2 + (long)l * x->d, x->st_g) : T(x->ones, 0);
-    const bool last = l + 1 == x->L;
-    g.gnext = last ? T(x->gf, x->st_gf) : T(x->g1 + (long)(l + 1) * x->d, x->st_g);
-    g.u_out = last ? x->uf : x->u;
-    g.ssq_out = last ? x->ssqf : x->ssq;
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, g, st), "down gemm");
+    HIPCHK(x, launch_attn(x->act, attn_args(x, l), st), "attention");
+  } else if (phase == FM_PHASE_OPROJ) {
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, gemm_args(x, k, l, phase), st), "o gemm");
+  } else if (phase == FM_PHASE_GATEUP) {
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_GELU, gemm_args(x, k, l, phase), st), "gate/up gemm");
+  } else {
+    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, gemm_args(x, k, l, phase), st), "down gemm");
   }
   return FM_OK;
 }
@@ -485,7 +554,7 @@ fm_status enqueue_layers(fm_ctx* x, int k, hipStream_t st) {
 // corrector (evaluation at t_(k+1)); 3: Adams-Bashforth (v_k kept in one of two
 // buffers, by step parity: the slices of a tail launch read v_(k-1) while one
 // of them writes v_k).
-fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_final) {
+OutArgs tail_args(const fm_ctx* x, int k, int stage, float* x_final) {
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
   OutArgs o{};
   o.uf = x->uf; o.Wout = x->wout; o.ssq = x->ssqf; o.P = x->P; o.inv_d = 1.f / (float)x->d; o.eps = x->cfg.rms_eps;
@@ -506,7 +575,95 @@ fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_fin
   o.temb = ada ? T(x->zeros, 0) : T(x->temb, x->d);
   o.embed_step = k + 1;
   o.hs = x->hs; o.h = x->h; o.u = x->u; o.g1 = T(x->g1, x->st_g); o.ssq_out = x->ssq;
-  HIPCHK(x, launch_out(x->act, x->ge, o, st), "out/euler");
+  return o;
+}
+
+fm_status enqueue_tail(fm_ctx* x, int k, int stage, hipStream_t st, float* x_final) {
+  HIPCHK(x, launch_out(x->act, x->ge, tail_args(x, k, stage, x_final), st), "out/euler");
+  return FM_OK;
+}
+
+// The persistent loop's arguments (pargs) and evaluation table (host copy
+// returned), built from the same argument builders as the graph's phases.
+std::vector<PersistEval> persist_build(fm_ctx* x) {
+  const bool ada = x->cfg.norm == FM_ADARMSNORM;
+  PersistArgs& P = x->pargs;
+  P = PersistArgs{};
+  auto lstride = [&](const void* a0, const void* a1) { return x->L > 1 ? (long)((const char*)a1 - (const char*)a0) : 0L; };
+  const long wst = x->L > 1 ? lstride(x->lw[0].wqkv, x->lw[1].wqkv) : 0;
+  P.q.g = gemm_args(x, 0, 0, FM_PHASE_QKV);
+  P.q.w = wst; P.q.bias = ada ? (long)x->Nqkv * 4 : 0;
+  P.o.g = gemm_args(x, 0, 0, FM_PHASE_OPROJ);
+  P.o.w = wst; P.o.alpha = ada ? (long)x->d * 4 : 0; P.o.gnext = (long)x->d * 4;
+  P.gu.g = gemm_args(x, 0, 0, FM_PHASE_GATEUP);
+  P.gu.w = wst; P.gu.bias = ada ? 2L * x->F * 4 : 0;
+  P.d.g = gemm_args(x, 0, 0, FM_PHASE_DOWN);
+  P.d.w = wst; P.d.alpha = ada ? (long)x->d * 4 : 0; P.d.gnext = (long)x->d * 4;
+  // the last layer's down projection: layer-0 weights and gates (advanced
+  // by the strides), the final norm's gain and operand
+  const GemmArgs dl = gemm_args(x, 0, x->L - 1, FM_PHASE_DOWN);
+  P.d_last = P.d;
+  P.d_last.g.gnext = dl.gnext; P.d_last.gnext = 0;
+  P.d_last.g.u_out = dl.u_out;
+  P.d_last.g.ssq_out = dl.ssq_out;
+  P.a = attn_args(x, 0);
+  P.a.pf_cus = 0;
+  for (int i = 0; i < 2; ++i) P.a.pf_w[i] = nullptr;
+  if (x->nsplit == 1) P.a.keys_per_split = ((x->TP + x->SP) / 16 + 1) / 2 * 2;
+  P.a.grid = x->B * x->Hkv * x->nqblk * x->nsplit * x->p_DS;
+  P.kv_stride = (long)x->TP * x->HD * (long)elt_size(x->act);
+  P.t = tail_args(x, 0, 0, nullptr);
+  P.xb0 = x->xbuf0; P.xb1 = x->xbuf1; P.vb0 = x->vbuf; P.vb1 = x->vbuf2;
+  P.ev = x->pev;
+  P.bar = x->pbar; P.err = x->pbar + 8 * 32;
+  P.n_evals = x->n_evals; P.L = x->L; P.n_actions = x->B * x->C * x->A;
+  P.grid_q = x->Nqkv / 16; P.grid_a = P.a.grid; P.grid_o = x->d / 16 * x->ks_o; P.grid_gu = 2 * x->F / 32;
+  P.grid_d = x->d / 16 * x->ks_d; P.grid_t = x->mtiles * x->esplit;
+  P.timeout = 200000000LL;  // 2 s of the 100 MHz s_memrealtime clock
+  // evaluations in the graph's order; the last one writes the actions
+  std::vector<PersistEval> ev;
+  auto add = [&](int layer_step, int k, int stage) {
+    const OutArgs o = tail_args(x, k, stage, nullptr);
+    PersistEval e{};
+    e.step = layer_step; e.stage = stage;
+    e.x_in = o.x_in == x->xbuf1 ? 1 : 0;
+    e.x_out = !o.x_out ? 0 : (o.x_out == x->xbuf1 ? 2 : 1);
+    e.v_save = !o.v_save ? 0 : (o.v_save == x->vbuf2 ? 2 : 1);
+    e.v_prev = !o.v_prev ? 0 : (o.v_prev == x->vbuf2 ? 2 : 1);
+    e.t_idx = o.t_idx; e.do_embed = o.do_embed; e.embed_step = o.embed_step;
+    e.dt = o.dt; e.c_cur = o.c_cur; e.c_prev = o.c_prev;
+    ev.push_back(e);
+  };
+  for (int k = 0; k < x->N; ++k) {
+    if (x->heun) {
+      add(k, k, 1);
+      add(k + 1, k, 2);
+    } else {
+      add(k, k, x->ab2 ? 3 : 0);
+    }
+  }
+  ev.back().x_out = 3;
+  return ev;
+}
+
+// the strides the persistent loop advances its layer-0 arguments by hold for every layer
+bool persist_strides_ok(const fm_ctx* x) {
+  const long w = x->L > 1 ? (long)((const char*)x->lw[1].wqkv - (const char*)x->lw[0].wqkv) : 0;
+  for (int l = 0; l < x->L; ++l) {
+    const LayerW& a = x->lw[0];
+    const LayerW& b = x->lw[l];
+    const void* pa[] = {a.wqkv, a.wo, a.wgu, a.wd, a.sqkv, a.so, a.sgu, a.sd};
+    const void* pb[] = {b.wqkv, b.wo, b.wgu, b.wd, b.sqkv, b.so, b.sgu, b.sd};
+    for (int i = 0; i < 8; ++i)
+      if (pa[i] && (const char*)pb[i] - (const char*)pa[i] != l * w) return false;
+  }
+  return true;
+}
+
+fm_status enqueue_persist(fm_ctx* x, float* actions, hipStream_t st) {
+  PersistArgs P = x->pargs;
+  P.actions = actions;
+  HIPCHK(x, launch_persist(x->wt, x->p_R, x->p_DS, P, x->n_cu, st), "persistent loop");
   return FM_OK;
 }
 
@@ -545,6 +702,7 @@ fm_status enqueue_embed(fm_ctx* x, const float* noise, const void* state, hipStr
   e.x0 = x->xbuf0; e.hs = x->hs; e.h = x->h; e.u = x->u; e.g1 = T(x->g1, x->st_g); e.ssq_out = x->ssq;
   e.B = x->B; e.S = x->S; e.C = x->C; e.A = x->A; e.SD = x->SD; e.d = x->d; e.M = x->M; e.has_state = x->hasS;
   e.mtiles = x->mtiles; e.esplit = x->esplit;
+  e.zero_word = x->persist ? x->pbar : nullptr;  // the persistent loop's barrier counter
   HIPCHK(x, launch_embed(x->act, e, st), "embed");
   return FM_OK;
 }
@@ -675,9 +833,6 @@ fm_status check_ctx(fm_ctx* x, bool encoder = false) {
 
 // set-up shared by the denoiser and the encoder; cfg and w validated
 fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream, bool encoder, fm_ctx** out) {
-  if (cfg->exec_mode == FM_EXEC_PERSISTENT)
-    return fail(nullptr, FM_ERR_UNSUPPORTED, "persistent execution is not implemented; the loop runs as a graph of kernels");
-
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(nullptr, FM_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
@@ -695,6 +850,18 @@ fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream
   x->device = dev;
   x->exec_mode = FM_EXEC_GRAPH;
   derive(x);
+  // The persistent loop runs on request only: measured on MI355X it is
+  // slower than the graph (its grid barriers cost more than a graph node).
+  if (cfg->exec_mode == FM_EXEC_PERSISTENT) {
+    const char* why = "";
+    x->persist = persist_plan(x, &why);
+    if (!x->persist && cfg->exec_mode == FM_EXEC_PERSISTENT) {
+      fail(nullptr, FM_ERR_UNSUPPORTED, "persistent loop: %s", why);
+      delete x;
+      return FM_ERR_UNSUPPORTED;
+    }
+    if (x->persist) x->exec_mode = FM_EXEC_PERSISTENT;
+  }
   x->cfg.t_schedule = nullptr;  // the caller's array is read during fm_create only
   Arena a;
   carve(x, a);
@@ -735,6 +902,35 @@ fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream
     return bail(FM_ERR_DEVICE);
   }
   if (const fm_status s = load_weights(x, w, st); s != FM_OK) return bail(s);
+  if (x->persist && !persist_strides_ok(x)) {  // (cannot happen with carve's per-layer blocks)
+    if (cfg->exec_mode == FM_EXEC_PERSISTENT) {
+      fail(x, FM_ERR_UNSUPPORTED, "persistent loop: per-layer weight blocks are not evenly spaced");
+      return bail(FM_ERR_UNSUPPORTED);
+    }
+    x->persist = false;
+    x->exec_mode = FM_EXEC_GRAPH;
+  }
+  std::vector<PersistEval> pev;
+  if (x->persist) {
+    pev = persist_build(x);
+    // tracing aid: FM_PERSIST_TRACE=<file> records every workgroup's arrival
+    // and release at every barrier of the latest loop; written at fm_destroy
+    if (const char* tp = getenv("FM_PERSIST_TRACE")) {
+      const size_t nbar = (size_t)x->n_evals * (5 * x->L + 1);
+      x->trace_n = (nbar + 1) * x->n_cu * 2;
+      if (hipMalloc(&x->trace, x->trace_n * 8) == hipSuccess) {
+        x->trace_path = tp;
+        x->pargs.trace = x->trace;
+      } else {
+        x->trace = nullptr;
+      }
+    }
+    if ((e = hipMemcpyAsync(x->pev, pev.data(), pev.size() * sizeof(PersistEval), hipMemcpyHostToDevice, st)) !=
+        hipSuccess) {
+      hip_fail(x, e, "persistent evaluation table");
+      return bail(FM_ERR_DEVICE);
+    }
+  }
   // the graph: every step's layers and tails except the last tail
   if ((e = hipStreamCreateWithFlags(&x->cap, hipStreamNonBlocking)) != hipSuccess) {
     hip_fail(x, e, "capture stream");
@@ -750,7 +946,7 @@ fm_status create_ctx(const fm_config* cfg, const fm_weights* w, void* hip_stream
     hip_fail(x, e, "create sync");
     return bail(FM_ERR_DEVICE);
   }
-  for (int gi = 0; gi < (encoder ? 2 : 1); ++gi) {
+  for (int gi = 0; gi < (encoder ? 2 : (x->persist ? 0 : 1)); ++gi) {
     x->enc_slot = gi;
     if ((e = hipStreamBeginCapture(x->cap, hipStreamCaptureModeThreadLocal)) != hipSuccess) {
       hip_fail(x, e, "begin capture");
@@ -818,6 +1014,8 @@ fm_status fm_encoder_create(const fm_config* cfg, const fm_weights* w, void* hip
   c.kv_fp8 = 0;
   fm_status s = validate_config(&c);
   if (s != FM_OK) return s;
+  if (c.exec_mode == FM_EXEC_PERSISTENT)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "encoder: the persistent loop covers denoising contexts only");
   if (c.act_dtype == FM_BF16 && c.chunk > 1024)
     return fail(nullptr, FM_ERR_UNSUPPORTED, "encoder: at most 1024 tokens per sequence");
   if ((s = validate_weights(&c, w, true)) != FM_OK) return s;
@@ -983,6 +1181,7 @@ fm_status fm_denoise(fm_ctx* x, const float* noise, const void* state, float* ac
   fm_status s = check_denoise(x, noise, state, actions);
   if (s != FM_OK) return s;
   if ((s = enqueue_embed(x, noise, state, x->stream)) != FM_OK) return s;
+  if (x->persist) return enqueue_persist(x, actions, x->stream);
   HIPCHK(x, hipGraphLaunch(x->gexec[0], x->stream), "graph launch");
   return enqueue_tail(x, x->N - 1, x->heun ? 2 : (x->ab2 ? 3 : 0), x->stream, actions);
 }
@@ -1014,9 +1213,16 @@ fm_status fm_encode_prefix(fm_ctx* x, const float* tokens, void* k_out, void* v_
 fm_status fm_launch_phase(fm_ctx* x, int32_t step, int32_t layer, int32_t phase) {
   fm_status s = check_ctx(x);
   if (s != FM_OK) return s;
-  if (step < 0 || step >= x->N || phase < FM_PHASE_QKV || phase > FM_PHASE_TAIL ||
-      (phase != FM_PHASE_TAIL && (layer < 0 || layer >= x->L)))
+  if (step < 0 || step >= x->N || phase < FM_PHASE_QKV || phase > FM_PHASE_LOOP ||
+      (phase < FM_PHASE_TAIL && (layer < 0 || layer >= x->L)))
     return fail(x, FM_ERR_ARG, "step %d layer %d phase %d out of range", step, layer, phase);
+  if (phase == FM_PHASE_LOOP) {
+    if (!x->persist) return fail(x, FM_ERR_STATE, "FM_PHASE_LOOP: the context does not run the persistent loop");
+    // the loop kernel alone, on the activations of the latest embedding; the
+    // actions go to an internal buffer
+    HIPCHK(x, launch_fill_u32(x->pbar, 8 * 32, 0u, x->stream), "barrier counters");
+    return enqueue_persist(x, x->xbuf0, x->stream);
+  }
   if (phase == FM_PHASE_TAIL)
     return enqueue_tail(x, step, x->heun ? 2 : (x->ab2 ? 3 : 0), x->stream, step + 1 < x->N ? nullptr : x->xbuf0);
   return enqueue_phase(x, step, layer, phase, x->stream);
@@ -1053,6 +1259,18 @@ fm_status fm_get_info(const fm_ctx* x, fm_info* info) {
 void fm_destroy(fm_ctx* x) {
   if (!x) return;
   if (x->stream || x->arena) (void)hipStreamSynchronize(x->stream);
+  if (x->trace) {
+    std::vector<unsigned long long> h(x->trace_n);
+    if (hipMemcpy(h.data(), x->trace, x->trace_n * 8, hipMemcpyDeviceToHost) == hipSuccess) {
+      if (FILE* f = fopen(x->trace_path.c_str(), "wb")) {
+        const int hdr[4] = {x->n_cu, x->n_evals, x->L, 2};
+        fwrite(hdr, sizeof hdr, 1, f);
+        fwrite(h.data(), 8, h.size(), f);
+        fclose(f);
+      }
+    }
+    (void)hipFree(x->trace);
+  }
   for (int j = 0; j < 2; ++j) {
     if (x->gexec[j]) (void)hipGraphExecDestroy(x->gexec[j]);
     if (x->graph[j]) (void)hipGraphDestroy(x->graph[j]);

@@ -11,155 +11,10 @@ namespace fm {
 // ---------------------------------------------------------------------------
 template <int ACT, int WT, int EPI, int NB, int UPW, int NPASS>
 __global__ __launch_bounds__(512) void k_gemm(GemmArgs g) {
-  constexpr int NT = 512, nt = NB * 16, PER = NB * 2;
-  constexpr int KU = (WT == ELT_FP8) ? 2 : 1;
-  __shared__ float red[4][64][33];
-  __shared__ float s_rstd[64];
-  __shared__ float s_col[3][32];  // per column: bias or alpha, gnext, fp8 scale
-  __shared__ int s_last;
-  const int tid = threadIdx.x;
-  const int ntiles = g.N / nt;
-  // split K (residual GEMMs): workgroup = (tile, k-range); the ranges of a
-  // tile are summed in range order by the last to arrive
-  const int ks = blockIdx.x % g.ksplit, tb = blockIdx.x / g.ksplit;
-  const int nti = tb % ntiles, mt = tb / ntiles;
-  const int n0 = nti * nt, m0 = mt * 64;
-  const int units = (g.K >> 5) / KU / g.ksplit;
-
-  // epilogue operands first (registers), then the GEMM operands
-  const int ccol = n0 + min(tid, nt - 1);
-  const float c0 = EPI == EPI_RESID ? g.alpha.base[(long)g.step * g.alpha.step_stride + ccol]
-                                    : g.bias.base[(long)g.step * g.bias.step_stride + ccol];
-  const float c1 = EPI == EPI_RESID ? g.gnext.base[(long)g.step * g.gnext.step_stride + ccol] : 0.f;
-  const float c2 = WT == ELT_FP8 ? g.wscale[ccol] : 1.f;
-  float4 q[4];
-  if (EPI != EPI_RESID) rstd_load(g.ssq, g.M, m0, q);
-  float hold[PER];
-  if (EPI == EPI_RESID) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + NT * i;
-      hold[i] = g.h[(long)min(m0 + (idx >> 4), g.M - 1) * g.N + n0 + (idx & 15)];
-    }
-  }
-  SkinnyTile<ACT, WT, NB, UPW, NPASS> t;
-  t.zero();
-  t.set_range(blockIdx.x);
-  t.u0 = ks * units;
-  t.mv = g.M - m0;
-  t.load_w_all(g.W, g.N >> 4, n0 >> 4, units);
-  t.load_a_pass(g.A, g.K, mt, units, 0);
-  t.mma_pass(units, 0);
-#pragma unroll
-  for (int p = 1; p < NPASS; ++p) {
-    t.load_a_pass(g.A, g.K, mt, units, p);
-    t.mma_pass(units, p);
-  }
-  if (tid < nt) {
-    s_col[0][tid] = c0;
-    s_col[1][tid] = c1;
-    s_col[2][tid] = c2;
-  }
-  if (EPI != EPI_RESID) rstd_finish(q, g.M, m0, g.inv_d, g.eps, s_rstd);
-  reduce_waves<NB>(t.acc, red);
-
-  float v[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = tid + NT * i, row = idx / nt, col = idx % nt;
-    v[i] = ((red[0][row][col] + red[1][row][col]) + red[2][row][col]) + red[3][row][col];
-  }
-  if constexpr (EPI == EPI_RESID) if (g.ksplit > 1) {
-    // every range stores its partial tile (device scope); the last to arrive
-    // adds the ranges in order (ksplit <= 4), own range from the registers
-    float* mine = g.partials + ((long)tb * g.ksplit + ks) * (64 * nt);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) st_dev(mine + tid + NT * i, v[i]);
-    drain_vm();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(g.counters + tb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == (unsigned)g.ksplit - 1;
-      if (s_last) __hip_atomic_store(g.counters + tb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    float pv[4][PER];
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2)
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        pv[k2][i] = ld_dev(g.partials + ((long)tb * g.ksplit + min(k2, g.ksplit - 1)) * (64 * nt) + tid + NT * i);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      float sum = 0.f;
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2)
-        if (k2 < g.ksplit) sum += (k2 == ks) ? v[i] : pv[k2][i];
-      v[i] = sum;
-    }
-  }
-
-  if constexpr (EPI == EPI_QKV || EPI == EPI_QKVR) {
-    // Q columns -> out (row-major); suffix K and V -> their kv-layout blocks
-    const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
-    constexpr bool packed = ACT != ELT_F32;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + NT * i, row = idx / nt, c = idx % nt;
-      const int r = m0 + row, col = n0 + c;
-      const float val = v[i] * s_col[2][c] * s_rstd[row] + s_col[0][c];
-      if (r < g.M) {
-        const int b = r / g.S, sr = r % g.S;
-        const long sb = (long)b * g.Hkv * g.Dh * g.SP;
-        const long rw = EPI == EPI_QKVR ? (long)b * g.row_bstride + (long)sr * (g.Hkv * g.Dh) : 0;  // encoder rows
-        if (col < kcol0) {
-          st_act<ACT>(g.out, (long)r * g.N + col, val);
-        } else if (col < vcol0) {
-          const int jk = (col - kcol0) / g.Dh, dh = (col - kcol0) % g.Dh;
-          st_act<ACT>(g.ksuf, sb + kv_k_off(packed, g.SP, g.Hkv, g.Dh, jk, sr, dh), val);
-          if constexpr (EPI == EPI_QKVR) st_act<ACT>(g.krow, rw + (col - kcol0), val);
-        } else {
-          const int jv = (col - vcol0) / g.Dh, dh = (col - vcol0) % g.Dh;
-          st_act<ACT>(g.vsuf, sb + kv_v_off(packed, g.SP, g.Hkv, g.Dh, jv, sr, dh), val);
-          if constexpr (EPI == EPI_QKVR) st_act<ACT>(g.vrow, rw + (col - vcol0), val);
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_GELU) {
-    // tile = [16 gate | 16 up] (NB == 2): pair them through red[0]
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + NT * i;
-      red[0][idx / nt][idx % nt] = v[i];
-    }
-    __syncthreads();
-    const int F = g.N >> 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + NT * i, row = idx >> 4, j = idx & 15;
-      const int r = m0 + row;
-      const float gv = red[0][row][j] * s_col[2][j] * s_rstd[row] + s_col[0][j];
-      const float uv = red[0][row][16 + j] * s_col[2][16 + j] * s_rstd[row] + s_col[0][16 + j];
-      if (r < g.M) st_act<ACT>(g.out, pk(r, nti * 16 + j, F), gelu_erf(gv) * uv);
-    }
-  } else {  // EPI_RESID (NB == 1): the 16 threads of a row are consecutive lanes
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int idx = tid + NT * i, row = idx >> 4, c = idx & 15;
-      const int r = m0 + row;
-      const float hn = (r < g.M) ? hold[i] + s_col[0][c] * (v[i] * s_col[2][c]) : 0.f;
-      float qq = hn * hn;
-      qq = sum16(qq);
-      if (r < g.M) {
-        const long o = (long)r * g.N + n0 + c;
-        g.h[o] = hn;
-        st_act<ACT>(g.u_out, pk(r, n0 + c, g.N), hn * s_col[1][c]);
-        if (c == 0) g.ssq_out[(long)r * PM + (n0 >> 4)] = qq;
-      }
-    }
-  }
+  __shared__ GemmSmem sm;
+  SkinnyGemm<ACT, WT, EPI, NB, UPW, NPASS, false> G;
+  G.pre(g, blockIdx.x);
+  G.run(g, blockIdx.x, sm);
 }
 
 // KG k-groups of 4 waves (KG = 2: 512 threads, two waves per SIMD to keep

@@ -9,6 +9,8 @@
 
 namespace fm {
 
+constexpr int GW = 8;  // waves per skinny GEMM / tail workgroup (512 threads)
+
 // Element types of activations / weights inside the library.
 enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2 };
 
@@ -170,6 +172,7 @@ struct EmbedArgs {
   Tab g1;
   float* ssq_out;
   int B, S, C, A, SD, d, M, has_state, mtiles, esplit;
+  unsigned* zero_word;    // words 0, 32, ..., 224 stored 0 (the persistent loop's barrier counters), or null
 };
 
 // Tile plan of the large-M GEMM (bf16 activations, bf16 or fp8 weights): tiles of
@@ -203,6 +206,63 @@ inline BigPlan big_plan(int epi, int M, int N, int K, bool wf8 = false) {
   }
   p.used = true;
   return p;
+}
+
+// The whole denoise loop of a batch-1 context (one 64-row tile) as one
+// cooperative kernel: every phase of every velocity evaluation, separated by
+// grid barriers, with each workgroup's weight tiles of its next GEMM work item
+// copied into LDS before the barrier.  Every argument is derived from fields
+// of the kernel argument itself (so the compiler knows each pointer is
+// global memory): one argument set per GEMM at layer 0 plus per-layer byte
+// strides, the attention's at layer 0 plus the prefix K/V layer stride, a
+// tail template, and a table of per-evaluation scalars.
+struct PersistGemm {
+  GemmArgs g;                         // layer 0
+  long w, bias, alpha, gnext;         // bytes per layer: weights (and fp8 scales), bias, alpha, next gain tables
+};
+struct PersistEval {
+  int step;                           // time row of the evaluation's layers
+  int stage;                          // tail: OutArgs::heun
+  int x_in, x_out;                    // 0 / 1: xbuf 0 / 1; x_out: 0 none, 1 / 2 xbuf 0 / 1, 3 actions
+  int v_save, v_prev;                 // 0 none, 1 / 2: vbuf 0 / 1
+  int t_idx, do_embed, embed_step;
+  float dt, c_cur, c_prev;
+};
+struct PersistArgs {
+  PersistGemm q, o, gu, d, d_last;    // d_last: the last layer's down projection
+  AttnArgs a;
+  long kv_stride;                     // bytes between layers of the prefix K (and of V)
+  OutArgs t;                          // tail template; per-evaluation fields from ev
+  float *xb0, *xb1, *vb0, *vb1;
+  const PersistEval* ev;              // [n_evals]
+  float* actions;
+  unsigned* bar;                      // barrier arrival counters, one per XCD 128 bytes apart: zero on entry
+  unsigned* err;                      // set to 1 when a barrier wait times out (actions are then NaN)
+  int n_evals, L, n_actions;
+  int grid_q, grid_a, grid_o, grid_gu, grid_d, grid_t;  // work items of each phase (<= the grid)
+  long long timeout;                  // barrier wait limit in s_memrealtime ticks (100 MHz)
+  unsigned long long* trace;          // null, or [barriers + 1][grid][2] s_memrealtime stamps: each
+                                      // workgroup's arrival and release at every barrier (slot 0: start)
+};
+// skinny-GEMM k-units per wave of the persistent kernel's instantiations
+// (QKV, O, gate/up, down): the Pi0-shaped expert at batch 1
+struct PersistUpw { int q, o, gu, d; };
+inline PersistUpw persist_upw(int wt) { return wt == ELT_FP8 ? PersistUpw{2, 1, 2, 2} : PersistUpw{4, 2, 4, 4}; }
+// attention instantiations: head_dim 256, one query block per work item;
+// (R 16-key blocks per wave, head-dim split DS) in {1..4} x 4 without a key
+// split, 2 x 2 with one
+inline bool persist_attn_ok(int R, int DS, bool split) { return split ? (R == 2 && DS == 2) : (R >= 1 && R <= 4 && DS == 4); }
+hipError_t launch_persist(int wt, int R, int DS, const PersistArgs& p, int grid, hipStream_t st);
+hipError_t persist_occupancy(int wt, int R, int DS, int* blocks_per_cu);
+hipError_t launch_persist_bf16(int R, int DS, const PersistArgs& p, int grid, hipStream_t st);
+hipError_t launch_persist_fp8(int R, int DS, const PersistArgs& p, int grid, hipStream_t st);
+hipError_t persist_occupancy_bf16(int R, int DS, int* blocks_per_cu);
+hipError_t persist_occupancy_fp8(int R, int DS, int* blocks_per_cu);
+inline hipError_t launch_persist(int wt, int R, int DS, const PersistArgs& p, int grid, hipStream_t st) {
+  return wt == ELT_FP8 ? launch_persist_fp8(R, DS, p, grid, st) : launch_persist_bf16(R, DS, p, grid, st);
+}
+inline hipError_t persist_occupancy(int wt, int R, int DS, int* blocks_per_cu) {
+  return wt == ELT_FP8 ? persist_occupancy_fp8(R, DS, blocks_per_cu) : persist_occupancy_bf16(R, DS, blocks_per_cu);
 }
 
 // --- launchers (fm_gemm.hip, fm_attn*.hip, fm_misc.hip) --------------------------------------------

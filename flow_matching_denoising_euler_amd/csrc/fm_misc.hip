@@ -14,6 +14,7 @@ __global__ __launch_bounds__(512) void k_embed(EmbedArgs e) {
   const int mt = blockIdx.x / e.esplit, es = blockIdx.x % e.esplit;
   const int m0 = mt * 64, c0 = es * 64;
   const int tid = threadIdx.x;
+  if (e.zero_word && blockIdx.x == 0 && tid < 8) e.zero_word[tid * 32] = 0u;  // the persistent loop's 8 barrier counters
   // noise rows of the tile (action rows); copy of the noise into x0
   float xv[4];
 #pragma unroll
@@ -57,61 +58,8 @@ __global__ __launch_bounds__(512) void k_embed(EmbedArgs e) {
 // 64 x A head tile (K = d) and embeds its own columns.
 template <int ACT, int WE, int NB>
 __global__ __launch_bounds__(512) void k_out(OutArgs o) {
-  constexpr int UPW = 4;
-  __shared__ float red[4][64][33];
-  __shared__ float s_rstd[64];
-  __shared__ float s_x[64][33];
-  const int mt = blockIdx.x / o.esplit, es = blockIdx.x % o.esplit;
-  const int m0 = mt * 64, c0 = es * 64;
-  const int tid = threadIdx.x;
-  const int units = o.d >> 5;
-  // every operand first: head weights, u_f, h^2 partials, x, b_out, the embedding's operands
-  float4 q[4];
-  rstd_load(o.ssq, o.M, m0, q);
-  float xin[4], bo[4], vp[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = min(m0 + lr, o.M - 1);
-    const int b = r / o.S, s = r % o.S;
-    const int ar = b * o.C + max(s - o.has_state, 0);
-    xin[i] = o.x_in[(long)ar * o.A + min(a, o.A - 1)];
-    bo[i] = o.bout.base[(long)o.t_idx * o.bout.step_stride + min(a, o.A - 1)];
-    vp[i] = o.v_prev ? o.v_prev[(long)ar * o.A + min(a, o.A - 1)] : 0.f;
-  }
-  EmbedCol<WE> ec;
-  if (o.do_embed) ec.load(c0, o.A, o.w_in, o.b_in, o.temb, o.g1, o.embed_step, o.hs, m0, o.M, o.S, o.d);
-  SkinnyTile<ACT, WE, NB, UPW, 1> t;
-  t.zero();
-  t.set_range(blockIdx.x);
-  t.mv = o.M - m0;
-  t.load_w_all(o.Wout, NB, 0, units);
-  t.load_a_pass(o.uf, o.d, mt, units, 0);
-  t.mma_pass(units, 0);
-  rstd_finish(q, o.M, m0, o.inv_d, o.eps, s_rstd);
-  reduce_waves<NB>(t.acc, red);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 512 * i, lr = idx >> 5, a = idx & 31, r = m0 + lr;
-    const bool act_row = r < o.M && a < o.A && !(o.has_state && (r % o.S) == 0);
-    float xv = 0.f;
-    if (act_row) {
-      const float acc = ((red[0][lr][a] + red[1][lr][a]) + red[2][lr][a]) + red[3][lr][a];
-      const float v = acc * s_rstd[lr] + bo[i];
-      xv = o.heun == 2   ? xin[i] + o.dt * (0.5f * (vp[i] + v))
-           : o.heun == 3 ? xin[i] + o.dt * (o.c_cur * v - o.c_prev * vp[i])
-                         : xin[i] + o.dt * v;
-      if (es == 0) {
-        const int b = r / o.S, s = r % o.S;
-        const long xo = (long)(b * o.C + s - o.has_state) * o.A + a;
-        if (o.heun == 1 || o.heun == 3) o.v_save[xo] = v;
-        if (o.heun != 1) o.x_out[xo] = xv;
-      }
-    }
-    s_x[lr][a] = xv;
-  }
-  if (!o.do_embed) return;
-  __syncthreads();
-  ec.template emit<ACT>(c0, m0, o.M, o.S, o.has_state, o.A, o.d, s_x, o.h, o.u, o.ssq_out);
+  __shared__ OutSmem sm;
+  out_body<ACT, WE, NB, false>(o, blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------------------

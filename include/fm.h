@@ -81,16 +81,26 @@ typedef enum { FM_RMSNORM = 0, FM_ADARMSNORM = 1 } fm_norm;
  * x_k + dt_k ((1 + r) v_k - r v_(k-1)); the first step is an Euler step. */
 typedef enum { FM_SAMPLER_EULER = 0, FM_SAMPLER_HEUN = 1, FM_SAMPLER_AB2 = 2 } fm_sampler;
 
-/* How fm_denoise issues the loop.  FM_EXEC_AUTO and FM_EXEC_GRAPH run one
- * hipGraph of per-phase kernel launches.  FM_EXEC_PERSISTENT (one cooperative
- * kernel with grid barriers between phases) is reserved: fm_create rejects
- * it with FM_ERR_UNSUPPORTED, because on MI355X a grid barrier plus the
- * re-read of the activations each phase needs costs more than a graph
- * node. */
+/* How fm_denoise issues the loop.  FM_EXEC_GRAPH: one hipGraph of per-phase
+ * kernel launches (five per layer and a tail per velocity evaluation).
+ * FM_EXEC_PERSISTENT: the whole loop as one cooperative kernel with one
+ * workgroup per CU and device-wide barriers between the phases, each
+ * workgroup's next weight tiles streaming into LDS while it waits; it covers
+ * batch-1-sized contexts (batch x suffix <= 64 rows) of the Pi0-shaped
+ * expert (head_dim 256, d_model / MLP shapes whose skinny GEMMs take 4, 2,
+ * 4 and 4 k-units per wave with bf16 weights, 2, 1, 2 and 2 with fp8:
+ * d_model 1024, 8 x 256 query dims, MLP 4096), action_dim 32, bf16
+ * activations, up to 1024 padded keys, without state_causal, kv_fp8 or
+ * rope_theta; fm_create returns FM_ERR_UNSUPPORTED (with the reason) for
+ * other contexts.  Persistent contexts must not run concurrently with each
+ * other on one device (their workgroups would wait for each other's CUs);
+ * a barrier wait that exceeds 2 s ends the kernel with NaN actions.
+ * Measured on MI355X the graph is the faster of the two (a grid barrier
+ * costs more than a graph node), so FM_EXEC_AUTO runs the graph. */
 typedef enum {
   FM_EXEC_AUTO = 0,
   FM_EXEC_GRAPH = 1,       /* one hipGraph of per-phase kernel launches   */
-  FM_EXEC_PERSISTENT = 2   /* reserved; rejected (FM_ERR_UNSUPPORTED)     */
+  FM_EXEC_PERSISTENT = 2   /* one persistent kernel for the whole loop     */
 } fm_exec;
 
 /*
@@ -200,7 +210,7 @@ typedef struct {
   size_t arena_bytes;               /* device memory held by the context    */
   size_t weight_bytes_per_step;     /* weight bytes one velocity evaluation streams */
   size_t kv_bytes_per_step;         /* prefix K/V bytes one step reads      */
-  int32_t exec_mode;                /* mode actually used (FM_EXEC_GRAPH)   */
+  int32_t exec_mode;                /* mode actually used (GRAPH or PERSISTENT) */
   int32_t n_phases;                 /* device phases per fm_denoise         */
   int32_t grid;                     /* workgroups of the gate/up GEMM launch */
   int32_t n_cu;                     /* compute units of the device          */
@@ -343,18 +353,23 @@ typedef enum {
   FM_PHASE_OPROJ = 2,    /* O GEMM + residual (+ next norm's input)            */
   FM_PHASE_GATEUP = 3,   /* norm2 folded into the gate/up GEMM + GELU gate     */
   FM_PHASE_DOWN = 4,     /* down GEMM + residual (+ next norm's input)         */
-  FM_PHASE_TAIL = 5      /* final norm, action head, update, next embedding    */
+  FM_PHASE_TAIL = 5,     /* final norm, action head, update, next embedding    */
+  FM_PHASE_LOOP = 6      /* the whole loop's persistent kernel (step and layer ignored;
+                            FM_ERR_STATE unless the context runs it)            */
 } fm_phase;
 
 /*
  * Profiling aid: enqueue the kernel of phase `phase` of step `step` and
- * layer `layer` (ignored for FM_PHASE_TAIL) with exactly the arguments
- * fm_denoise uses, on the context's stream (FM_PHASE_QKV with rope_theta > 0
- * also enqueues its rotary kernel).  It reads and writes the context's
- * activation buffers, so results of a later fm_denoise are unaffected
- * (fm_denoise rewrites them from its inputs).  Lets a caller time one kernel
- * with events on the stream.  FM_ERR_ARG for an out-of-range step, layer or
- * phase; FM_ERR_STATE on an encoder context.
+ * layer `layer` (ignored for FM_PHASE_TAIL and FM_PHASE_LOOP) with exactly
+ * the arguments fm_denoise uses, on the context's stream (FM_PHASE_QKV with
+ * rope_theta > 0 also enqueues its rotary kernel; FM_PHASE_LOOP a one-word
+ * clear of the barrier counter before the loop kernel, which starts from
+ * the latest embedding and writes its actions to an internal buffer).  It
+ * reads and writes the context's activation buffers, so results of a later
+ * fm_denoise are unaffected (fm_denoise rewrites them from its inputs).
+ * Lets a caller time one kernel with events on the stream.  FM_ERR_ARG for
+ * an out-of-range step, layer or phase; FM_ERR_STATE on an encoder context,
+ * or for FM_PHASE_LOOP on a context that does not run the persistent loop.
  */
 fm_status fm_launch_phase(fm_ctx* ctx, int32_t step, int32_t layer, int32_t phase);
 
