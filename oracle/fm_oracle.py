@@ -52,6 +52,19 @@ Readings taken where the pages are silent
   s = max|w| / 448 (1 when the row is zero), codes = round-to-nearest-even
   of the fp32 quotient w / s, saturating at +-448.  The loop then uses the
   dequantised weights code * s exactly.
+* W8A8 (cfg.w8a8, fp8 weights only): the activation operand of each of the
+  four weight GEMMs of a layer is quantised as well, in blocks of 32
+  consecutive elements along the reduction dimension of each row, with one
+  power-of-two scale per block (the block layout of the OCP Microscaling
+  formats, E4M3 elements with an E8M0 scale).  The block exponent X is the
+  smallest integer with max|a| <= 448 * 2^X (so no element saturates),
+  floored at -126; codes are the E4M3 values of a / 2^X rounded to nearest,
+  ties to even.  The two norm-fed GEMMs quantise the gain-scaled residual
+  a = h * g (RMSNorm gain g, or 1 + gamma for AdaRMSNorm) and apply the
+  row's 1/rms factor and the Ada shift beta after the product:
+  y = rstd * (Q(a) W^T) + beta W^T, which is the unquantised norm-then-GEMM
+  by linearity.  The attention output and the GELU gate product are
+  quantised as they are.  The final norm and the action head stay unquantised.
 """
 from __future__ import annotations
 
@@ -68,6 +81,7 @@ __all__ = [
     "e4m3_values", "e4m3_decode", "e4m3_encode", "quantize_e4m3_per_channel",
     "effective_weights", "prefix_kv_e4m3", "FP8_MATRICES", "PrefixRing", "prefix_stack_kv",
     "joint_velocity", "denoise_joint", "rel_l2", "max_abs",
+    "MX_BLOCK", "mx_block_exponent", "mx_quantize_e4m3", "mx_dequantize", "mx_fake_quant",
 ]
 
 F64 = np.float64
@@ -230,7 +244,13 @@ def e4m3_encode(x) -> np.ndarray:
     """Round float32 values to E4M3FN codes: nearest, ties to the even code,
     saturating at +-448; the sign bit follows the sign of x (so negative
     values that round to zero give 0x80)."""
-    x = np.asarray(x, np.float32).astype(F64)
+    return _e4m3_encode_f64(np.asarray(x, np.float32).astype(F64))
+
+
+def _e4m3_encode_f64(x: np.ndarray) -> np.ndarray:
+    """E4M3FN codes of float64 values (nearest, ties to the even code,
+    saturating at +-448), with no intermediate rounding."""
+    x = np.asarray(x, F64)
     a = np.minimum(np.abs(x), 448.0)
     hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 126)
     lo = np.clip(hi - 1, 0, 126)
@@ -238,6 +258,55 @@ def e4m3_encode(x) -> np.ndarray:
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
     mag = np.where(pick_hi, hi, lo).astype(np.uint8)
     return (mag | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+MX_BLOCK = 32
+MX_MIN_EXP = -126
+
+
+def mx_block_exponent(amax: float) -> int:
+    """Exponent X of a block's power-of-two scale: the smallest integer with
+    amax <= 448 * 2^X, floored at -126 (an all-zero block gets -126)."""
+    amax = float(amax)
+    if not amax > 0.0:
+        return MX_MIN_EXP
+    _, e = math.frexp(amax)          # amax = f 2^e, 0.5 <= f < 1
+    x = e - 1 - 8                    # 448 2^x >= 256 2^x > amax / 2 ...
+    while amax > 448.0 * 2.0 ** x:   # ... so at most two steps up
+        x += 1
+    while x - 1 >= MX_MIN_EXP and amax <= 448.0 * 2.0 ** (x - 1):
+        x -= 1
+    return max(x, MX_MIN_EXP)
+
+
+def mx_quantize_e4m3(a) -> Tuple[np.ndarray, np.ndarray]:
+    """Block quantisation of a[..., K] (K a multiple of 32): every run of 32
+    consecutive elements along the last axis shares the scale 2^X of
+    mx_block_exponent(max |run|); codes are E4M3 of a / 2^X (exact division,
+    nearest, ties to even; never saturating, by the choice of X).  Returns
+    (codes uint8 [..., K], X int32 [..., K / 32])."""
+    a = np.asarray(a, F64)
+    K = a.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError(f"reduction length {K} is not a multiple of {MX_BLOCK}")
+    blocks = a.reshape(a.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blocks), axis=-1)
+    X = np.vectorize(mx_block_exponent, otypes=[np.int32])(amax) if amax.size else amax.astype(np.int32)
+    codes = _e4m3_encode_f64(blocks / np.exp2(X.astype(F64))[..., None])
+    return codes.reshape(a.shape), X
+
+
+def mx_dequantize(codes, X) -> np.ndarray:
+    """code value * 2^X of the block each element belongs to, in float64."""
+    codes = np.asarray(codes, np.uint8)
+    v = e4m3_decode(codes).reshape(codes.shape[:-1] + (codes.shape[-1] // MX_BLOCK, MX_BLOCK))
+    return (v * np.exp2(np.asarray(X, F64))[..., None]).reshape(codes.shape)
+
+
+def mx_fake_quant(a) -> np.ndarray:
+    """What a W8A8 GEMM consumes of the activation a: its block-quantised
+    value, dequantised (float64)."""
+    return mx_dequantize(*mx_quantize_e4m3(a))
 
 
 def quantize_e4m3_per_channel(w) -> Tuple[np.ndarray, np.ndarray]:
@@ -304,8 +373,31 @@ def _norm(cfg, h, gain, mod):
     return ada_rmsnorm(h, gamma, beta, cfg.rms_eps)
 
 
+def _norm_parts(cfg, h, gain, mod):
+    """The norm taken apart for a quantised GEMM: (1/rms(h) [S][1], the
+    gain-scaled residual a [S][d], the shift or None), with
+    norm(h) = (1/rms) a + shift."""
+    if cfg.norm == "rms":
+        return rms_inv(h, cfg.rms_eps), h * np.asarray(gain, F64), None
+    gamma, beta, _ = mod
+    return rms_inv(h, cfg.rms_eps), h * (1.0 + gamma), beta
+
+
+def _norm_gemms(parts, quant, ws):
+    """The GEMMs of one norm output on its quantised operand: for each W,
+    (1/rms) (Q(a) W^T) (+ shift W^T)."""
+    rstd, a, shift = parts
+    aq = quant(a)
+    out = []
+    for w in ws:
+        y = rstd * linear(aq, w)
+        out.append(y if shift is None else y + linear(shift, w))
+    return out
+
+
 def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
-                    v_pre: np.ndarray, state: Optional[np.ndarray], return_kv: bool = False):
+                    v_pre: np.ndarray, state: Optional[np.ndarray], return_kv: bool = False,
+                    act_quant: Optional[Callable[[np.ndarray], np.ndarray]] = None):
     """Velocity v(x, t) of one robot.
 
     x [chunk][A]; k_pre, v_pre [layers][T][Hkv][Dh] in logical order; state
@@ -318,7 +410,13 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
     token attends to the prefix and itself, the action tokens to everything.
     With cfg.rope_theta the suffix q and k are rotated (rope) at positions
     T + s; k_pre is then the rotated cache (see denoise).
+
+    W8A8 (cfg.w8a8): every weight GEMM of a layer multiplies the quantised
+    activation act_quant(a) (default mx_fake_quant), the norm-fed ones in
+    the split form of _norm_gemms.  Passing act_quant forces that form.
     """
+    if act_quant is None and getattr(cfg, "w8a8", False):
+        act_quant = mx_fake_quant
     S_has = 1 if cfg.state_dim else 0
     hq, hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     act = linear(np.asarray(x, F64), W["w_in"], W["b_in"])
@@ -339,10 +437,13 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
     ks, vs = [], []
     for li, L in enumerate(W["layers"]):
         m1, m2 = mods[li] if mods else (None, None)
-        u = _norm(cfg, h, L.get("norm1"), m1)
-        q = linear(u, L["wq"]).reshape(S, hq, dh)
-        k = linear(u, L["wk"]).reshape(S, hkv, dh)
-        v = linear(u, L["wv"]).reshape(S, hkv, dh)
+        if act_quant is None:
+            u = _norm(cfg, h, L.get("norm1"), m1)
+            q, k, v = linear(u, L["wq"]), linear(u, L["wk"]), linear(u, L["wv"])
+        else:
+            q, k, v = _norm_gemms(_norm_parts(cfg, h, L.get("norm1"), m1), act_quant,
+                                  (L["wq"], L["wk"], L["wv"]))
+        q, k, v = q.reshape(S, hq, dh), k.reshape(S, hkv, dh), v.reshape(S, hkv, dh)
         if theta:  # suffix row s sits at position T + s, after the prefix
             q, k = rope(q, T + np.arange(S), theta), rope(k, T + np.arange(S), theta)
         ks.append(k)
@@ -351,11 +452,15 @@ def expert_velocity(cfg, W: dict, x: np.ndarray, t: float, k_pre: np.ndarray,
         V = np.concatenate([np.asarray(v_pre[li], F64), v], axis=0)
         o = (masked_attention(q, K, V, allowed) if causal else attention(q, K, V)).reshape(S, hq * dh)
         a1 = m1[2] if m1 else 1.0
-        h = h + a1 * linear(o, L["wo"])
-        u = _norm(cfg, h, L.get("norm2"), m2)
-        z = gelu(linear(u, L["wg"])) * linear(u, L["wu"])
+        h = h + a1 * linear(o if act_quant is None else act_quant(o), L["wo"])
+        if act_quant is None:
+            u = _norm(cfg, h, L.get("norm2"), m2)
+            gt, up = linear(u, L["wg"]), linear(u, L["wu"])
+        else:
+            gt, up = _norm_gemms(_norm_parts(cfg, h, L.get("norm2"), m2), act_quant, (L["wg"], L["wu"]))
+        z = gelu(gt) * up
         a2 = m2[2] if m2 else 1.0
-        h = h + a2 * linear(z, L["wd"])
+        h = h + a2 * linear(z if act_quant is None else act_quant(z), L["wd"])
     u = _norm(cfg, h[S_has:], W.get("norm_f"), mod_f)
     out = linear(u, W["w_out"], W["b_out"])
     return (out, np.stack(ks), np.stack(vs)) if return_kv else out

@@ -745,6 +745,147 @@ def test_fp8_workload_uses_dequantised_matrices_only():
     assert np.array_equal(E["layers"][1]["norm1"], W["layers"][1]["norm1"].astype(np.float64))
 
 
+# --- P14: W8A8 activations, 32-element blocks with power-of-two scales -----------------
+def _pow2(x: int) -> Fraction:
+    return Fraction(2) ** x
+
+
+def test_mx_block_exponent_is_the_smallest_non_saturating_power():
+    # X is the smallest integer with amax <= 448 2^X (checked in exact
+    # rationals), floored at -126
+    g = np.random.default_rng(21)
+    amax = np.concatenate([np.exp(g.uniform(-80, 80, 400)),
+                           448.0 * 2.0 ** np.arange(-20, 21), 448.0 * 2.0 ** np.arange(-20, 21) * (1 + 2.0 ** -40),
+                           224.0 * 2.0 ** np.arange(-5, 6), [1.0, 1.75, 1.7500001, 2.0]])
+    for a in amax:
+        X = O.mx_block_exponent(a)
+        fa = Fraction(float(a))
+        assert fa <= 448 * _pow2(X), (a, X)
+        assert X == -126 or fa > 448 * _pow2(X - 1), (a, X)
+    assert O.mx_block_exponent(448.0) == 0 and O.mx_block_exponent(448.0 * (1 + 2.0 ** -40)) == 1
+    assert O.mx_block_exponent(449.0) == 1 and O.mx_block_exponent(224.0) == -1
+    assert O.mx_block_exponent(1.0) == -8 and O.mx_block_exponent(1.8) == -7
+    assert O.mx_block_exponent(0.0) == -126 and O.mx_block_exponent(2.0 ** -140) == -126
+    assert O.mx_block_exponent(448.0 * 2.0 ** -126) == -126 and O.mx_block_exponent(448.0 * 2.0 ** -125) == -125
+
+
+def test_mx_identity_on_grid_values():
+    # blocks of E4M3 values times 2^X whose largest magnitude lies in
+    # (224, 448] come back unchanged, with that X and those codes
+    g = np.random.default_rng(22)
+    vals = O.e4m3_values()
+    finite = np.array([c for c in range(256) if np.isfinite(vals[c]) and vals[c] != 0], np.uint8)
+    top = np.array([c for c in finite if 224 < abs(vals[c]) <= 448], np.uint8)
+    codes = g.choice(finite, size=(6, 128)).astype(np.uint8)
+    codes[:, ::32] = g.choice(top, size=(6, 4))          # one top-binade value per block
+    X = g.integers(-40, 40, size=(6, 4))
+    a = O.e4m3_decode(codes).reshape(6, 4, 32) * np.exp2(X.astype(np.float64))[..., None]
+    a = a.reshape(6, 128)
+    c2, X2 = O.mx_quantize_e4m3(a)
+    assert np.array_equal(X2, X) and np.array_equal(c2, codes)
+    assert np.array_equal(O.mx_fake_quant(a), a)
+
+
+def test_mx_half_step_error_bound_rounding_and_no_saturation():
+    g = np.random.default_rng(23)
+    a = g.standard_normal((40, 256)) * np.exp(g.uniform(-30, 30, (40, 8))).repeat(32, axis=1)
+    a[3, 64:96] = 0.0                                     # an all-zero block
+    codes, X = O.mx_quantize_e4m3(a)
+    deq = O.mx_dequantize(codes, X)
+    scale = np.exp2(X.astype(np.float64)).repeat(32, axis=1)
+    q = np.abs(a) / scale
+    assert np.all(q <= 448.0)                             # never beyond the E4M3 range
+    blk = np.max(q.reshape(40, 8, 32), axis=-1)
+    assert np.all((blk > 224.0) | (blk == 0.0))           # and no wasted binade
+    assert X[3, 2] == -126 and np.all(codes[3, 64:96] == 0)
+    # half a step of the E4M3 grid at |q| (2^(e-3) for normal q, 2^-9 below 2^-6)
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    assert np.all(np.abs(deq - a) <= 0.5 * 2.0 ** (e - 3) * scale)
+    # exact ties go to the even code: a block with max 448 (X = 0)
+    ties = np.zeros(32)
+    ties[:6] = [448.0, 1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, -0.5625 * 2.0 ** -6]
+    c, Xt = O.mx_quantize_e4m3(ties)
+    assert Xt[0] == 0
+    assert list(c[:6]) == [0x7E, 0x38, 0x3A, 0x00, 0x02, 0x84]
+    # a block whose max would saturate under a floor(log2) rule is scaled one binade up
+    c, Xs = O.mx_quantize_e4m3(np.full(32, 500.0))
+    assert Xs[0] == 1 and np.all(O.e4m3_decode(c) == 256.0)
+
+
+def test_mx_blocks_are_32_wide_and_independent():
+    g = np.random.default_rng(24)
+    a = g.standard_normal((3, 96))
+    c0, X0 = O.mx_quantize_e4m3(a)
+    b = a.copy()
+    b[1, 40] = 1e6                                         # only row 1, block 1 changes
+    c1, X1 = O.mx_quantize_e4m3(b)
+    same = np.ones((3, 96), bool)
+    same[1, 32:64] = False
+    assert np.array_equal(c0[same], c1[same])
+    assert X1[1, 1] != X0[1, 1] and np.array_equal(np.delete(X1.ravel(), 4), np.delete(X0.ravel(), 4))
+    with pytest.raises(ValueError):
+        O.mx_quantize_e4m3(np.ones((2, 48)))
+
+
+@pytest.mark.parametrize("norm", ["rms", "ada"])
+def test_w8a8_split_form_is_norm_then_gemm(norm):
+    # with the quantiser replaced by the identity, the W8A8 form
+    # rstd (a W^T) + shift W^T is the plain norm-then-GEMM
+    cfg = _tiny() if norm == "rms" else _ada_cfg()
+    W, k, v, x0, st = _inputs(cfg)
+    W64 = O.effective_weights(cfg, W)
+    ref = O.expert_velocity(cfg, W64, x0[0], 0.6, k[0], v[0], st[0])
+    got = O.expert_velocity(cfg, W64, x0[0], 0.6, k[0], v[0], st[0], act_quant=lambda a: a)
+    assert O.rel_l2(got, ref) < 1e-13
+
+
+@pytest.mark.parametrize("norm", ["rms", "ada"])
+def test_w8a8_quantises_all_four_gemm_operands(norm):
+    # a quantiser that zeroes its operand removes every attention and MLP
+    # contribution (only the Ada shifts survive in q, k, v, gate and up), so
+    # with alpha = 0 for Ada the velocity is the head on the final norm of the
+    # embedding; the operands are [S][d], [S][Hq Dh], [S][d], [S][F] per layer
+    cfg = _tiny() if norm == "rms" else _ada_cfg()
+    W, k, v, x0, st = _inputs(cfg)
+    if norm == "ada":  # keep the shifts, zero every alpha
+        for L in W["layers"]:
+            for n in ("norm1", "norm2"):
+                L[n + "_w"][2 * cfg.d_model:] = 0
+                L[n + "_b"][2 * cfg.d_model:] = 0
+    W64 = O.effective_weights(cfg, W)
+    shapes = []
+
+    def zero(a):
+        shapes.append(a.shape)
+        return np.zeros_like(a)
+
+    t = 0.3
+    got = O.expert_velocity(cfg, W64, x0[0], t, k[0], v[0], st[0], act_quant=zero)
+    S_ = cfg.suffix
+    one = [(S_, cfg.d_model), (S_, cfg.n_q_heads * cfg.head_dim), (S_, cfg.d_model), (S_, cfg.d_mlp)]
+    assert shapes == one * cfg.n_layers
+    act = O.linear(x0[0], W64["w_in"], W64["b_in"])
+    if norm == "rms":
+        act = act + O.sinusoid(t, cfg.d_model)
+        hf = O.rmsnorm(act, W64["norm_f"], cfg.rms_eps)
+    else:
+        _, (gf, bf, _) = O.ada_modulation(cfg, W64, t)
+        hf = O.ada_rmsnorm(act, gf, bf, cfg.rms_eps)
+    want = O.linear(hf, W64["w_out"], W64["b_out"])
+    assert O.rel_l2(got, want) < 1e-13
+    if norm == "rms":  # the alpha-free RMS expert: any residual contribution would show
+        ref = O.expert_velocity(cfg, W64, x0[0], t, k[0], v[0], st[0])
+        assert O.rel_l2(ref, want) > 1e-2
+
+
+def test_w8a8_loop_is_close_to_w8a16():
+    cfg = _tiny(weight_dtype="fp8", act_dtype="bf16")
+    W, k, v, x0, st = _inputs(cfg)
+    a = O.denoise(cfg.replace(w8a8=True), W, k, v, x0, st)
+    b = O.denoise(cfg, W, k, v, x0, st)
+    assert 1e-4 < O.rel_l2(a, b) < 5e-2
+
+
 # --- structure: suffix rows, state token, time only on action rows --------------------
 def test_state_token_reaches_actions_only_through_attention():
     cfg = TINY
