@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E spec
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA spec
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector spec
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA spec
 
 METRIC = "denoise-loop ms per action chunk (10 steps) + % of roofline, Pi0-like bs=1"
 
@@ -73,6 +74,13 @@ def load_traffic(workload, kernel):
 
 PHASE_NAMES = ["QKV GEMM (norm1 folded)", "attention", "O GEMM + residual", "gate/up GEMM + GELU gate",
                "down GEMM + residual", "tail (final norm, head, update, next embedding)"]
+
+
+def dtype_of(cfg):
+    """The arithmetic the layer GEMMs compute in."""
+    if getattr(cfg, "w8a8", False):
+        return "fp8-e4m3 weights and GEMM activations (32-element power-of-two blocks), fp32 accumulate"
+    return {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype]
 
 
 def phase_work(cfg, info, ph):
@@ -149,9 +157,10 @@ def phase_table(fm, den, cfg, info, stream, persistent, chunk_ms):
         us = e0.elapsed_time(e1) / reps * 1e3
         byts, flops = phase_work(cfg, info, ph)
         n = evals * cfg.n_layers if ph < 5 else evals
+        pk = FP8_PEAK_TFLOPS if cfg.w8a8 and ph in (0, 2, 3, 4) else peak_f
         out[PHASE_NAMES[ph]] = {"per_launch": {"bytes": int(byts), "flops": int(flops), "avg_us": round(us, 3)},
                                 "launches_per_chunk": n, "per_chunk_ms": round(us * n / 1e3, 4),
-                                "roofline": roofline_of(byts, flops, us, peak_f)}
+                                "roofline": roofline_of(byts, flops, us, pk)}
     return out
 
 
@@ -247,7 +256,7 @@ def encode_bench(args, cfg):
         "metric": "prefix encoder ms per call (frames through the expert-shaped stack)",
         "value": round(ms, 4), "unit": "ms per encode", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
+        "dtype": dtype_of(cfg),
         "data": "synthetic (seeded prefix-stack weights, N(0,1) tokens)",
         "config": {"workload": cfg.name, "sequences": cfg.batch, "tokens": n_tok, "d_model": d, "layers": L,
                    "parallelism": "single GPU"},
@@ -349,7 +358,7 @@ def pipeline_bench(args, cfg):
         "unit": "ms per tick",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["pipelined"], 4),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
+        "dtype": dtype_of(cfg),
         "data": "synthetic (seeded weights for the expert and the prefix stack, N(0,1) frame tokens)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "frame_tokens": cfg.frame_tokens,
                    "n_frames": cfg.n_frames, "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps,
@@ -374,6 +383,8 @@ def main():
     ap.add_argument("--kv-fp8", action="store_true", help="hold the prefix K/V cache in fp8 E4M3 (per token and kv head scales)")
     ap.add_argument("--fp8-weights", action="store_true",
                     help="quantise the per-layer matrices to fp8 E4M3 (per output row scales; bf16 activations)")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="fp8 weights and fp8 GEMM activations (32-element power-of-two blocks, block-scaled MFMA)")
     ap.add_argument("--exec-mode", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -404,6 +415,10 @@ def main():
         if cfg.act_dtype != "bf16":
             raise SystemExit("--fp8-weights needs a workload with bf16 activations")
         cfg = cfg.replace(weight_dtype="fp8")
+    if args.w8a8:
+        if cfg.act_dtype != "bf16":
+            raise SystemExit("--w8a8 needs a workload with bf16 activations")
+        cfg = cfg.replace(weight_dtype="fp8", w8a8=True)
     if args.steps is None:
         args.steps = cfg.ticks if cfg.ticks > 0 and not (args.pipeline or args.encode) else 200
     if args.pipeline:
@@ -481,8 +496,9 @@ def main():
     roof["kernel"] = dom
     roof["per_launch"] = phases[dom]["per_launch"]
     # committed counters: per workload, and per weight dtype where it was overridden
-    roof["traffic"] = load_traffic(cfg.name if cfg.weight_dtype == base_weights
-                                   else f"{cfg.name}_{cfg.weight_dtype}_weights", dom)
+    variant = cfg.name + ("_w8a8" if cfg.w8a8 else ("" if cfg.weight_dtype == base_weights
+                                                     else f"_{cfg.weight_dtype}_weights"))
+    roof["traffic"] = load_traffic(variant, dom)
     log(f"bench: dominant kernel {dom}: {phases[dom]['per_launch']['avg_us']:.2f} us x "
         f"{phases[dom]['launches_per_chunk']} = {phases[dom]['per_chunk_ms']:.3f} ms/chunk, "
         f"{roof['achieved']} {roof['unit']} ({roof['frac'] * 100:.2f}% of peak)")
@@ -512,11 +528,12 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.weight_dtype],
+        "dtype": dtype_of(cfg),
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) prefix K/V and noise)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "chunk": cfg.chunk, "state_tokens": cfg.has_state,
                    "prefix_tokens": cfg.prefix_len, "n_steps": cfg.n_steps, "sampler": cfg.sampler,
-                   "kv_cache": "fp8-e4m3" if cfg.kv_fp8 else cfg.act_dtype, "weights": cfg.weight_dtype,
+                   "kv_cache": "fp8-e4m3" if cfg.kv_fp8 else cfg.act_dtype,
+                   "weights": cfg.weight_dtype + (" (w8a8)" if cfg.w8a8 else ""),
                    "d_model": cfg.d_model,
                    "layers": cfg.n_layers, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),

@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfmdenoise.so")
 
-FM_ABI_VERSION = 5
+FM_ABI_VERSION = 6
 
 FM_OK, FM_ERR_ARG, FM_ERR_SHAPE, FM_ERR_STATE, FM_ERR_OOM, FM_ERR_DEVICE, FM_ERR_UNSUPPORTED = range(7)
 STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_ARG", 2: "FM_ERR_SHAPE", 3: "FM_ERR_STATE", 4: "FM_ERR_OOM",
@@ -32,7 +32,7 @@ class fm_config(ctypes.Structure):
         "abi_version", "d_model", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "d_mlp",
         "action_dim", "chunk", "state_dim", "batch", "n_steps", "prefix_static", "frame_tokens",
         "n_frames", "norm", "time_dim", "weight_dtype", "act_dtype")] + [
-        ("rms_eps", ctypes.c_float), ("exec_mode", ctypes.c_int32), ("sampler", ctypes.c_int32), ("state_causal", ctypes.c_int32), ("kv_fp8", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+        ("rms_eps", ctypes.c_float), ("exec_mode", ctypes.c_int32), ("sampler", ctypes.c_int32), ("state_causal", ctypes.c_int32), ("kv_fp8", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("w8a8", ctypes.c_int32),
         ("t_schedule", ctypes.POINTER(ctypes.c_float))]
 
 

@@ -59,6 +59,7 @@ struct fm_ctx {
 
   // dims
   int act, wt, ge;  // activation, matrix weight, embedding/gain element types
+  int gwt;          // weight type of the layer GEMMs: wt, or ELT_FP8_MX for W8A8
   int B, C, A, SD, hasS, S, M, d, L, Hq, Hkv, Dh, F, N, Nqkv, HD, Tcap, P, mtiles, esplit;
   bool heun;  // Heun sampler: two evaluations per step, time rows t_0..t_N
   bool ab2;   // two-step Adams-Bashforth: v_(k-1) kept, ping-pong buffers
@@ -80,6 +81,7 @@ struct fm_ctx {
   int* meta;
   float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *vbuf, *vbuf2, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
+  void *u_mx, *z_mx;  // W8A8: fp8 activation buffers of the next norm's input and of the GELU gate product
   unsigned* counters;
   size_t n_counters;
   size_t part_bytes = 0, attn_part_bytes = 0;  // scratch sizes (split-K and key-split partials)
@@ -169,6 +171,7 @@ fm_status validate_config(const fm_config* c) {
     return fail(nullptr, FM_ERR_ARG, "bad sampler");
   if (c->state_causal != 0 && c->state_causal != 1) return fail(nullptr, FM_ERR_ARG, "state_causal must be 0 or 1");
   if (c->kv_fp8 != 0 && c->kv_fp8 != 1) return fail(nullptr, FM_ERR_ARG, "kv_fp8 must be 0 or 1");
+  if (c->w8a8 != 0 && c->w8a8 != 1) return fail(nullptr, FM_ERR_ARG, "w8a8 must be 0 or 1");
   if (!(c->rope_theta >= 0.f) || std::isinf(c->rope_theta)) return fail(nullptr, FM_ERR_ARG, "rope_theta must be 0 or positive");
   if (c->rope_theta > 0.f && c->n_frames > 0)
     return fail(nullptr, FM_ERR_UNSUPPORTED, "rotary positions with a frame ring: the window would move cached positions");
@@ -201,6 +204,18 @@ fm_status validate_config(const fm_config* c) {
     const long keys = ((long)c->prefix_static + 31) / 32 * 32 + (long)c->n_frames * c->frame_tokens + (S + 31) / 32 * 32;
     if (f32) return fail(nullptr, FM_ERR_UNSUPPORTED, "kv_fp8 needs bf16 activations");
     if (keys > 1024) return fail(nullptr, FM_ERR_UNSUPPORTED, "kv_fp8: %ld padded keys, at most 1024", keys);
+  }
+  if (c->w8a8) {
+    // the block-scaled fp8 GEMM: 128-k MFMA steps, 64-row tiles
+    if (c->weight_dtype != FM_FP8_E4M3) return fail(nullptr, FM_ERR_UNSUPPORTED, "w8a8 needs fp8 weights");
+    if (c->d_model % 128 || (c->n_q_heads * c->head_dim) % 128 || c->d_mlp % 128 ||
+        ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim) % 128)
+      return fail(nullptr, FM_ERR_UNSUPPORTED, "w8a8: d_model, d_mlp and the head sizes must give multiples of 128");
+    if ((long)c->batch * S < 256)
+      return fail(nullptr, FM_ERR_UNSUPPORTED, "w8a8 covers the batched GEMMs: batch x suffix rows must be >= 256 (%ld)",
+                  (long)c->batch * S);
+    if (c->exec_mode == FM_EXEC_PERSISTENT)
+      return fail(nullptr, FM_ERR_UNSUPPORTED, "w8a8: the persistent loop covers batch-1 contexts only");
   }
   if (f32) {
     if (c->head_dim > 64 || S > 256) return fail(nullptr, FM_ERR_UNSUPPORTED, "fp32 path: head_dim <= 64, suffix <= 256");
@@ -237,6 +252,7 @@ void derive(fm_ctx* x) {
   const fm_config& c = x->cfg;
   x->act = elt_of(c.act_dtype);
   x->wt = elt_of(c.weight_dtype);
+  x->gwt = c.w8a8 ? ELT_FP8_MX : x->wt;
   x->ge = x->act == ELT_F32 ? ELT_F32 : ELT_BF16;
   x->B = c.batch; x->C = c.chunk; x->A = c.action_dim; x->SD = c.state_dim; x->hasS = c.state_dim > 0;
   x->S = x->C + x->hasS; x->M = x->B * x->S;
@@ -410,6 +426,11 @@ void carve(fm_ctx* x, Arena& a) {
   x->qkv = a.take(Mp * x->Nqkv * ea);
   x->o = a.take(Mp * x->Hq * x->Dh * ea);
   x->z = a.take(Mp * x->F * ea);
+  // W8A8: the residual and GELU epilogues write the activations of the GEMMs
+  // after them as fp8 codes (Mp x K bytes) and a scale byte per 32-run
+  const bool w8 = x->gwt == ELT_FP8_MX;
+  x->u_mx = w8 ? a.take(Mp * d + Mp * d / 32) : nullptr;
+  x->z_mx = w8 ? a.take(Mp * x->F + Mp * x->F / 32) : nullptr;
   const long ks = std::max(x->ks_o, x->ks_d);
   const long Mp128 = (x->M + 127) / 128 * 128;  // rows covered by the large-M tiles
   x->part_bytes = ks > 1 ? ks * Mp128 * d * 4 : 16;
@@ -442,8 +463,9 @@ GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
   g.step = k;
   g.partials = x->partials; g.counters = x->counters;
   g.h = x->h;
+  const bool w8 = x->gwt == ELT_FP8_MX;  // fp8 activations after the first layer GEMM of a step
   if (phase == FM_PHASE_QKV) {  // norm1 -> QKV
-    g.A = x->u; g.W = w.wqkv; g.wscale = w.sqkv; g.N = x->Nqkv; g.K = x->d; g.nt = 16; g.ksplit = 1;
+    g.A = w8 && l > 0 ? x->u_mx : x->u; g.W = w.wqkv; g.wscale = w.sqkv; g.N = x->Nqkv; g.K = x->d; g.nt = 16; g.ksplit = 1;
     g.out = x->qkv;
     g.bias = ada ? T(x->bqkv + (long)l * x->Nqkv, x->st_bqkv) : T(x->zeros, 0);
     g.ksuf = x->ksuf; g.vsuf = x->vsuf; g.S = x->S; g.SP = x->SP; g.Hq = x->Hq; g.Hkv = x->Hkv; g.Dh = x->Dh;
@@ -457,17 +479,17 @@ GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
     g.A = x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16; g.ksplit = x->ks_o;
     g.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(x->ones, 0);
     g.gnext = T(x->g2 + (long)l * x->d, x->st_g);
-    g.u_out = x->u; g.ssq_out = x->ssq;
+    g.u_out = w8 ? x->u_mx : x->u; g.ssq_out = x->ssq;
   } else if (phase == FM_PHASE_GATEUP) {  // norm2 -> gate/up -> GELU gate
-    g.A = x->u; g.W = w.wgu; g.wscale = w.sgu; g.N = 2 * x->F; g.K = x->d; g.nt = 32; g.ksplit = 1;
-    g.out = x->z;
+    g.A = w8 ? x->u_mx : x->u; g.W = w.wgu; g.wscale = w.sgu; g.N = 2 * x->F; g.K = x->d; g.nt = 32; g.ksplit = 1;
+    g.out = w8 ? x->z_mx : x->z;
     g.bias = ada ? T(x->bgu + (long)l * 2 * x->F, x->st_bgu) : T(x->zeros, 0);
   } else {  // down + residual; writes the next norm's input
-    g.A = x->z; g.W = w.wd; g.wscale = w.sd; g.N = x->d; g.K = x->F; g.nt = 16; g.ksplit = x->ks_d;
+    g.A = w8 ? x->z_mx : x->z; g.W = w.wd; g.wscale = w.sd; g.N = x->d; g.K = x->F; g.nt = 16; g.ksplit = x->ks_d;
     g.alpha = ada ? T(x->a2 + (long)l * x->d, x->st_g) : T(x->ones, 0);
     const bool last = l + 1 == x->L;
     g.gnext = last ? T(x->gf, x->st_gf) : T(x->g1 + (long)(l + 1) * x->d, x->st_g);
-    g.u_out = last ? x->uf : x->u;
+    g.u_out = last ? x->uf : (w8 ? x->u_mx : x->u);
     g.ssq_out = last ? x->ssqf : x->ssq;
   }
   return g;
@@ -516,10 +538,21 @@ AttnArgs attn_args(const fm_ctx* x, int l) {
   return at;
 }
 
+// one layer GEMM; W8A8 contexts take fp8 activation buffers from the GEMM
+// before (gate/up, down, and QKV after the first layer) and write them for
+// the GEMM after (O projection, gate/up, and down except at the last layer)
+hipError_t layer_gemm(const fm_ctx* x, int epi, int k, int l, int phase, hipStream_t st) {
+  const GemmArgs g = gemm_args(x, k, l, phase);
+  if (x->gwt != ELT_FP8_MX) return launch_gemm(x->act, x->gwt, epi, g, st);
+  const bool amx = phase == FM_PHASE_QKV ? l > 0 : phase != FM_PHASE_OPROJ;
+  const bool omx = phase == FM_PHASE_OPROJ || phase == FM_PHASE_GATEUP || (phase == FM_PHASE_DOWN && l + 1 < x->L);
+  return launch_gemm_mx(epi, g, amx, omx, st);
+}
+
 // one phase kernel of step k, layer l
 fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
   if (phase == FM_PHASE_QKV) {
-    HIPCHK(x, launch_gemm(x->act, x->wt, x->encoder ? EPI_QKVR : EPI_QKV, gemm_args(x, k, l, phase), st), "qkv gemm");
+    HIPCHK(x, layer_gemm(x, x->encoder ? EPI_QKVR : EPI_QKV, k, l, phase, st), "qkv gemm");
     if (x->cfg.rope_theta > 0.f) {  // rotary embedding of this step's suffix Q and K
       RopeArgs r{};
       r.qkv = x->qkv; r.ksuf = x->ksuf; r.meta = x->meta;
@@ -530,11 +563,11 @@ fm_status enqueue_phase(fm_ctx* x, int k, int l, int phase, hipStream_t st) {
   } else if (phase == FM_PHASE_ATTN) {  // attention over [prefix | suffix]
     HIPCHK(x, launch_attn(x->act, attn_args(x, l), st), "attention");
   } else if (phase == FM_PHASE_OPROJ) {
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, gemm_args(x, k, l, phase), st), "o gemm");
+    HIPCHK(x, layer_gemm(x, EPI_RESID, k, l, phase, st), "o gemm");
   } else if (phase == FM_PHASE_GATEUP) {
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_GELU, gemm_args(x, k, l, phase), st), "gate/up gemm");
+    HIPCHK(x, layer_gemm(x, EPI_GELU, k, l, phase, st), "gate/up gemm");
   } else {
-    HIPCHK(x, launch_gemm(x->act, x->wt, EPI_RESID, gemm_args(x, k, l, phase), st), "down gemm");
+    HIPCHK(x, layer_gemm(x, EPI_RESID, k, l, phase, st), "down gemm");
   }
   return FM_OK;
 }
@@ -760,7 +793,7 @@ fm_status load_weights(fm_ctx* x, const fm_weights* w, hipStream_t st) {
     hipError_t r;
     if (fp8) {
       if ((r = launch_quantize_e4m3(m, rows, cols, codes, scales, st)) != hipSuccess) return r;
-      if ((r = launch_pack(codes, ELT_FP8, rows, cols, rm, dst, ELT_FP8, ntot, st)) != hipSuccess) return r;
+      if ((r = launch_pack(codes, ELT_FP8, rows, cols, rm, dst, x->gwt, ntot, st)) != hipSuccess) return r;
       if ((r = launch_scatter_scales(scales, rows, rm, dscale, st)) != hipSuccess) return r;
       if (beta) return launch_bias_gemv(codes, ELT_FP8, scales, rows, cols, beta, L * d, x->NT, rm, btab, bstride, st);
     } else {
@@ -1012,6 +1045,8 @@ fm_status fm_encoder_create(const fm_config* cfg, const fm_weights* w, void* hip
   c.t_schedule = nullptr;
   c.state_causal = 0;
   c.kv_fp8 = 0;
+  if (cfg->abi_version == FM_ABI_VERSION && c.w8a8)
+    return fail(nullptr, FM_ERR_UNSUPPORTED, "encoder: w8a8 covers the denoise loop only");
   fm_status s = validate_config(&c);
   if (s != FM_OK) return s;
   if (c.exec_mode == FM_EXEC_PERSISTENT)

@@ -1,7 +1,7 @@
 // gfx950 GEMM kernels of the denoise loop: the skinny weight-stream GEMM
 // (batch 1, M <= a few 64-row tiles) and the LDS-staged MFMA GEMM (M >= 256),
 // both with the fused epilogues (QKV, residual + next norm, GELU gate).
-#include "fm_device.h"
+#include "fm_gemm_epi.h"
 
 namespace fm {
 
@@ -163,110 +163,7 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
     }
   }
   __syncthreads();
-  if constexpr (WF8) {  // per-column weight scales: acc over the fp8 codes times the column's scale
-#pragma unroll
-    for (int ni = 0; ni < TNW; ++ni) {
-      const float4 ws = *(const float4*)&s_ws[(wn * TNW + ni) * 16 + (lane >> 4) * 4];
-#pragma unroll
-      for (int m = 0; m < TME; ++m) {
-        fin[ni][m][0] *= ws.x;
-        fin[ni][m][1] *= ws.y;
-        fin[ni][m][2] *= ws.z;
-        fin[ni][m][3] *= ws.w;
-      }
-    }
-  }
-
-  // epilogue: block (ni, m) of this lane = row m0 + (wm TMW + mb0 + m) 16 + (lane & 15),
-  // columns n0 + (wn TNW + ni) 16 + (lane >> 4) 4 + [0, 4)
-  const int c4 = (lane >> 4) * 4;
-  if constexpr (EPI == EPI_QKV || EPI == EPI_QKVR) {
-    const int kcol0 = g.Hq * g.Dh, vcol0 = (g.Hq + g.Hkv) * g.Dh;
-    const int dsh = __builtin_ctz(g.Dh);  // head_dim is 32, 64, 128 or 256 on the bf16 path
-#pragma unroll
-    for (int m = 0; m < TME; ++m) {
-      const int rt = (wm * TMW + mb0 + m) * 16 + (lane & 15), row = m0 + rt;
-      if (row >= g.M) continue;
-      const float rs = s_rstd[rt];
-      const int b = row / g.S, sr = row % g.S;
-      const long sb = (long)b * g.Hkv * g.Dh * g.SP;
-#pragma unroll
-      for (int ni = 0; ni < TNW; ++ni) {
-        const int ct = (wn * TNW + ni) * 16 + c4, col = n0 + ct;
-        const float4 bias = *(const float4*)&s_col[0][ct];
-        const f32x4 a = fin[ni][m];
-        const float v0 = a[0] * rs + bias.x, v1 = a[1] * rs + bias.y, v2 = a[2] * rs + bias.z, v3 = a[3] * rs + bias.w;
-        const long rw = EPI == EPI_QKVR ? (long)b * g.row_bstride + (long)sr * (g.Hkv * g.Dh) : 0;  // encoder rows
-        if (col < kcol0) {
-          *(uint2*)((uint16_t*)g.out + (long)row * g.N + col) = pack4_bf16(v0, v1, v2, v3);
-        } else if (col < vcol0) {
-          const int jk = (col - kcol0) >> dsh, dh = (col - kcol0) & (g.Dh - 1);
-          *(uint2*)((uint16_t*)g.ksuf + sb + kv_k_off(true, g.SP, g.Hkv, g.Dh, jk, sr, dh)) = pack4_bf16(v0, v1, v2, v3);
-          if constexpr (EPI == EPI_QKVR) *(uint2*)((uint16_t*)g.krow + rw + (col - kcol0)) = pack4_bf16(v0, v1, v2, v3);
-        } else {
-          const int jv = (col - vcol0) >> dsh, dh = (col - vcol0) & (g.Dh - 1);
-          uint16_t* vp = (uint16_t*)g.vsuf + sb + kv_v_off(true, g.SP, g.Hkv, g.Dh, jv, sr, dh);
-          vp[0] = (uint16_t)f2bf(v0);  // consecutive dims are 8 elements apart
-          vp[8] = (uint16_t)f2bf(v1);
-          vp[16] = (uint16_t)f2bf(v2);
-          vp[24] = (uint16_t)f2bf(v3);
-          if constexpr (EPI == EPI_QKVR) *(uint2*)((uint16_t*)g.vrow + rw + (col - vcol0)) = pack4_bf16(v0, v1, v2, v3);
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_GELU) {
-    // packed columns come in [16 gate | 16 up] pairs: block 2i is gate, 2i+1 up
-    static_assert(TNW % 2 == 0, "gate/up pairs");
-    const int F = g.N >> 1;
-#pragma unroll
-    for (int m = 0; m < TME; ++m) {
-      const int rt = (wm * TMW + mb0 + m) * 16 + (lane & 15), row = m0 + rt;
-      if (row >= g.M) continue;
-      const float rs = s_rstd[rt];
-#pragma unroll
-      for (int pi = 0; pi < TNW / 2; ++pi) {
-        const int cg = (wn * TNW + 2 * pi) * 16 + c4;
-        const float4 bg = *(const float4*)&s_col[0][cg], bu = *(const float4*)&s_col[0][cg + 16];
-        const f32x4 ga = fin[2 * pi][m], ua = fin[2 * pi + 1][m];
-        const float z0 = gelu_erf(ga[0] * rs + bg.x) * (ua[0] * rs + bu.x);
-        const float z1 = gelu_erf(ga[1] * rs + bg.y) * (ua[1] * rs + bu.y);
-        const float z2 = gelu_erf(ga[2] * rs + bg.z) * (ua[2] * rs + bu.z);
-        const float z3 = gelu_erf(ga[3] * rs + bg.w) * (ua[3] * rs + bu.w);
-        const int zc = ((n0 + cg) >> 5) * 16 + c4;
-        *(uint2*)((uint16_t*)g.out + pk(row, zc, F)) = pack4_bf16(z0, z1, z2, z3);
-      }
-    }
-  } else {  // EPI_RESID: h += alpha * acc; u = act(h * gnext); h^2 partials per 16 columns
-    float4 hv[TME][TNW];
-#pragma unroll
-    for (int m = 0; m < TME; ++m) {
-      const int row = min(m0 + (wm * TMW + mb0 + m) * 16 + (lane & 15), g.M - 1);
-#pragma unroll
-      for (int ni = 0; ni < TNW; ++ni)
-        hv[m][ni] = *(const float4*)(g.h + (long)row * g.N + n0 + (wn * TNW + ni) * 16 + c4);
-    }
-#pragma unroll
-    for (int m = 0; m < TME; ++m) {
-      const int row = m0 + (wm * TMW + mb0 + m) * 16 + (lane & 15);
-#pragma unroll
-      for (int ni = 0; ni < TNW; ++ni) {
-        const int ct = (wn * TNW + ni) * 16 + c4, col = n0 + ct;
-        const float4 al = *(const float4*)&s_col[0][ct], gn = *(const float4*)&s_col[1][ct];
-        const f32x4 a = fin[ni][m];
-        const float4 h = hv[m][ni];
-        const float4 hn = make_float4(h.x + al.x * a[0], h.y + al.y * a[1], h.z + al.z * a[2], h.w + al.w * a[3]);
-        float qq = ((hn.x * hn.x + hn.y * hn.y) + hn.z * hn.z) + hn.w * hn.w;
-        qq += __shfl_xor(qq, 16);
-        qq += __shfl_xor(qq, 32);
-        if (row < g.M) {
-          *(float4*)(g.h + (long)row * g.N + col) = hn;
-          *(uint2*)((uint16_t*)g.u_out + pk(row, col, g.N)) =
-              pack4_bf16(hn.x * gn.x, hn.y * gn.y, hn.z * gn.z, hn.w * gn.w);
-          if (c4 == 0) g.ssq_out[(long)row * PM + (col >> 4)] = qq;
-        }
-      }
-    }
-  }
+  big_epilogue<EPI, TMW, TNW, TME, WF8>(g, fin, s_rstd, s_col[0], s_col[1], s_ws, m0, n0, wm, wn, mb0, lane);
 }
 
 template <int ACT, int WT, int EPI, int NB>
@@ -343,6 +240,7 @@ hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t 
   if (act == ELT_F32 && wt == ELT_F32) return gemm_dispatch<ELT_F32, ELT_F32>(epi, g, st);
   if (act == ELT_BF16 && wt == ELT_BF16) return gemm_dispatch<ELT_BF16, ELT_BF16>(epi, g, st);
   if (act == ELT_BF16 && wt == ELT_FP8) return gemm_dispatch<ELT_BF16, ELT_FP8>(epi, g, st);
+  if (act == ELT_BF16 && wt == ELT_FP8_MX) return launch_gemm_mx(epi, g, false, false, st);
   return hipErrorInvalidValue;
 }
 

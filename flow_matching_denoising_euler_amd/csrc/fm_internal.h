@@ -12,7 +12,8 @@ namespace fm {
 constexpr int GW = 8;  // waves per skinny GEMM / tail workgroup (512 threads)
 
 // Element types of activations / weights inside the library.
-enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2 };
+enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2,
+                 ELT_FP8_MX = 3 };  // fp8 weights in the W8A8 GEMM's tiles, with block-quantised bf16 activations
 
 // Epilogues of the skinny GEMM.
 enum Epi : int {
@@ -267,6 +268,14 @@ inline hipError_t persist_occupancy(int wt, int R, int DS, int* blocks_per_cu) {
 
 // --- launchers (fm_gemm.hip, fm_attn*.hip, fm_misc.hip) --------------------------------------------
 hipError_t launch_gemm(int act, int wt, int epi, const GemmArgs& g, hipStream_t st);
+// W8A8 GEMM (fm_gemm_mx.hip): its output tile per epilogue, and the launcher
+struct MxPlan {
+  int BM, BN;
+};
+MxPlan mx_plan(int epi);
+// amx: A is an fp8 activation buffer (else bf16, quantised in the GEMM); omx: the
+// epilogue writes its activation output (out or u_out) as an fp8 activation buffer
+hipError_t launch_gemm_mx(int epi, const GemmArgs& g, bool amx, bool omx, hipStream_t st);
 hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st);
 hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st);
 hipError_t launch_embed(int act, const EmbedArgs& e, hipStream_t st);

@@ -126,7 +126,11 @@ __global__ void k_pack(const void* src, int src_elt, int rows, int cols, RowMap 
     const int nd = (r / rm.blk) * rm.stride + rm.off + r % rm.blk;
     const int nb = nd >> 4, ln = nd & 15;
     const int NBT = Ntot >> 4;
-    if (dst_elt == ELT_FP8) {
+    if (dst_elt == ELT_FP8_MX) {  // 2 KB tiles of 16 columns x 128 k: lane (column, 16-k group) halves
+      const int kq = k >> 7, kk = k & 127, half = kk >> 6, lane = ln + 16 * ((kk & 63) >> 4);
+      const long off = ((long)kq * NBT + nb) * 2048 + half * 1024 + lane * 16 + (kk & 15);
+      ((uint8_t*)dst)[off] = ((const uint8_t*)src)[i];
+    } else if (dst_elt == ELT_FP8) {
       const int kq = k >> 6, kk = k & 63, half = kk >> 5, lane = ln + 16 * ((kk & 31) >> 3);
       const long off = (((long)kq * NBT + nb) * 64 + lane) * 16 + half * 8 + (k & 7);
       ((uint8_t*)dst)[off] = ((const uint8_t*)src)[i];

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 5
+#define FM_ABI_VERSION 6
 
 typedef struct fm_ctx fm_ctx;
 
@@ -151,6 +151,20 @@ typedef enum {
  *   activations and at most 1024 padded keys (prefix capacity rounded up to
  *   32 plus the suffix rounded up to 32), else FM_ERR_UNSUPPORTED.
  *
+ * w8a8 (with weight_dtype FM_FP8_E4M3): 0 = the layer GEMMs multiply fp8
+ *   weights with bf16 activations (W8A16); 1 = their activation operands are
+ *   quantised too (W8A8), on the fly in every GEMM, in runs of 32
+ *   consecutive k per row with one power-of-two scale 2^X per run (the OCP
+ *   Microscaling block layout, E4M3 elements and an E8M0 scale): X is the
+ *   smallest integer with max|a| <= 448 2^X (floored at -126) and the
+ *   elements are round-to-nearest-even E4M3 of a / 2^X, so none saturates.
+ *   The two norm-fed GEMMs quantise h * gain and apply 1/rms and the Ada
+ *   shift after the product.  The GEMMs then run on gfx950's block-scaled
+ *   fp8 MFMA (the fp8 line of the hardware layer, InstinctFlash README,
+ *   "Architecture").  Needs batch x (chunk + state) >= 256 rows, d_model,
+ *   d_mlp and the head sizes in multiples of 128, and no persistent loop,
+ *   else FM_ERR_UNSUPPORTED; the encoder rejects it.
+ *
  * rope_theta: 0 = no positional encoding (the pages give none); > 0 = rotary
  *   embeddings of q and k with base rope_theta (e.g. 10000): the pair (i, i +
  *   Dh/2) of every head turns by position * rope_theta^(-2i/Dh).  Prefix
@@ -175,6 +189,7 @@ typedef struct {
   int32_t state_causal;              /* 0 or 1, see above */
   int32_t kv_fp8;                    /* 0 or 1, see above */
   float rope_theta;                  /* 0 or the rotary base, see above */
+  int32_t w8a8;                      /* 0 or 1, see above */
   const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
 } fm_config;
 

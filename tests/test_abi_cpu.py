@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(_abi.fm_config) == 26 * 4 + 8  # 25 scalars, padding, the t_schedule pointer
+    assert ctypes.sizeof(_abi.fm_config) == 26 * 4 + 8  # 26 scalars, the t_schedule pointer
     assert ctypes.sizeof(_abi.fm_weights) == 11 * 8
     assert ctypes.sizeof(_abi.fm_info) == 3 * 8 + 4 * 4
 
@@ -72,6 +72,10 @@ def _create(c):
     (lambda c: setattr(c, "sampler", 3), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "state_causal", 2), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "kv_fp8", 2), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "w8a8", 2), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "w8a8", 1), _abi.FM_ERR_UNSUPPORTED),     # fp32 weights
+    (lambda c: (setattr(c, "w8a8", 1), setattr(c, "act_dtype", _abi.FM_BF16), setattr(c, "weight_dtype", _abi.FM_FP8_E4M3)),
+     _abi.FM_ERR_UNSUPPORTED),                                        # d_model 64 is not a multiple of 128
     (lambda c: setattr(c, "rope_theta", -1.0), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "rope_theta", float("nan")), _abi.FM_ERR_ARG),
     (lambda c: (setattr(c, "rope_theta", 1e4), setattr(c, "n_frames", 2), setattr(c, "frame_tokens", 32)),
@@ -198,3 +202,35 @@ def test_binding_stream_guard_is_a_no_op_on_the_context_stream():
     fm.stream_enter(ctx, ctx)
     fm.stream_leave(ctx, ctx, [t])
     assert ctx.waited_on == [] and t.recorded == []
+
+
+def _w8a8_cfg(**kw):
+    # fp8 weights with 128-multiple sizes: only the named field breaks the W8A8 rules
+    base = dict(d_model=128, time_dim=128, d_mlp=256, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                weight_dtype="fp8", act_dtype="bf16", batch=32, chunk=8, w8a8=True)
+    base.update(kw)
+    return fm.make_config(S.workload("tiny_fp32").replace(**base))
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(batch=28), "rows"),                       # 28 x 9 = 252 rows < 256
+    (dict(exec_mode=2), "persistent"),
+    (dict(weight_dtype="bf16"), "fp8 weights"),
+    (dict(d_mlp=192), "multiples of 128"),
+    (dict(n_q_heads=2, head_dim=32), "multiples of 128"),  # Hq Dh = 64
+])
+def test_w8a8_limits_are_rejected_before_device_work(kw, what):
+    exec_mode = kw.pop("exec_mode", None)
+    c = _w8a8_cfg(**kw)
+    if exec_mode is not None:
+        c.exec_mode = exec_mode
+    st, ctx = _create(c)
+    assert st == _abi.FM_ERR_UNSUPPORTED, (st, fm.fm_last_error())
+    assert ctx.value is None and what in fm.fm_last_error()
+
+
+def test_w8a8_config_passes_validation_and_encoder_rejects_it():
+    st, ctx = _create(_w8a8_cfg())   # valid: fails later, on the missing weights
+    assert st == _abi.FM_ERR_ARG and "missing" in fm.fm_last_error()
+    st, ctx = _encoder_create(_w8a8_cfg())
+    assert st == _abi.FM_ERR_UNSUPPORTED and "w8a8" in fm.fm_last_error() and ctx.value is None
