@@ -1,12 +1,15 @@
 // W8A8 GEMM of the batched denoise loop on gfx950's block-scaled fp8 MFMA
 // (v_mfma_scale_f32_16x16x128_f8f6f4).  Weights are OCP E4M3 codes with one
-// fp32 scale per output column (applied in the epilogue); activations stay
-// bf16 in memory and are quantised on their way into LDS: every run of 32
-// consecutive k of a row gets the power-of-two scale 2^X with X the smallest
-// integer for which the run's largest magnitude does not exceed 448 2^X
-// (floored at -126), and E4M3 codes of a / 2^X rounded to nearest even.
-// That is the block layout of the OCP Microscaling formats (E4M3 elements,
-// E8M0 scale), which the MFMA consumes directly: scale byte X + 127 per lane.
+// fp32 scale per output column (applied in the epilogue).  Activations are
+// quantised per row in runs of 32 consecutive k: the run gets the
+// power-of-two scale 2^X with X the smallest integer for which its largest
+// magnitude does not exceed 448 2^X (floored at -126), and E4M3 codes of
+// a / 2^X rounded to nearest even.  That is the block layout of the OCP
+// Microscaling formats (E4M3 elements, E8M0 scale), which the MFMA consumes
+// directly: scale byte X + 127 per lane.  The residual and GELU epilogues
+// write their activation output already in this form (fm_gemm_epi.h), so
+// gate/up, down and QKV after the first layer copy ready tiles; QKV at the
+// first layer and the O projection read bf16 and quantise here.
 //
 // Operand tiles (LDS and, for weights, HBM): 16 rows (or weight columns) x
 // 128 k in 2 KB, lane L = r + 16 g of the MFMA holding k = 16 g + [0, 16) in
@@ -16,8 +19,9 @@
 // Pipeline: global loads into registers two 128-k stages ahead (two register
 // sets), written to double-buffered LDS tiles one stage ahead; barriers wait
 // for LDS traffic only, so the loads stay in flight across them.  Each
-// thread converts one (row, 32-k run) of the activation tile per stage;
-// every wave multiplies a TMW x TNW grid of 16 x 16 blocks.
+// thread converts (or copies) one (row, 32-k run) of the activation tile per
+// stage; every wave multiplies a TMW x TNW grid of 16 x 16 blocks; KG = 2
+// runs two k-groups of waves over alternate stages, added in a fixed order.
 #include "fm_gemm_epi.h"
 
 namespace fm {
