@@ -487,8 +487,13 @@ def main():
     byts, flops = algorithmic(cfg, info)
     es = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
     peak_f = BF16_PEAK_TFLOPS if cfg.act_dtype == "bf16" else FP32_PEAK_TFLOPS  # fp8 weights run bf16 MFMA
-    mfma_bound = flops / (peak_f * 1e12) > byts / (HBM_PEAK_GBS * 1e9)
-    loop_roof_ms = (flops / (peak_f * 1e12) if mfma_bound else byts / (HBM_PEAK_GBS * 1e9)) * 1e3
+    t_flops = flops / (peak_f * 1e12)
+    if cfg.w8a8:  # the layer GEMMs run on the fp8 MFMA: their flops at the fp8 peak
+        evals = cfg.n_steps * (2 if cfg.sampler == "heun" else 1)
+        gemm = sum(phase_work(cfg, info, ph)[1] for ph in (0, 2, 3, 4)) * evals * cfg.n_layers
+        t_flops = gemm / (FP8_PEAK_TFLOPS * 1e12) + (flops - gemm) / (peak_f * 1e12)
+    mfma_bound = t_flops > byts / (HBM_PEAK_GBS * 1e9)
+    loop_roof_ms = (t_flops if mfma_bound else byts / (HBM_PEAK_GBS * 1e9)) * 1e3
     phases = phase_table(fm, den, cfg, info, stream, persistent=int(info.exec_mode) == fm.FM_EXEC_PERSISTENT,
                          chunk_ms=ms)
     dom = max(phases, key=lambda n: phases[n]["per_chunk_ms"])
