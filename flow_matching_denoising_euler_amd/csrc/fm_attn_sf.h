@@ -62,6 +62,48 @@ struct AttnSfSmem {
   int s_last;
 };
 
+// The attention output of query rows [q0, q0 + ROWS) of kv group (b, j),
+// head dims [c0, c0 + COLS), from the bf16 staging rows `so`: packed bf16
+// stores, or (a.out_mx) runs of 32 head dims quantised into the O
+// projection's fp8 activation buffer (the layout of fm_device.h), one run per
+// thread.
+template <int DH, int ROWS, int COLS, bool COH, int LDW>
+__device__ __forceinline__ void attn_store(const AttnArgs& a, const uint16_t (*so)[LDW], int b, int j, int q0, int nq,
+                                           int G, int c0, int tid) {
+  if constexpr (!COH) if (a.out_mx) {
+    static_assert(COLS % 32 == 0, "whole 32-dim runs");
+    const int RBT = (a.B * a.S + 63) / 64 * 4, K = a.Hq * DH;
+    for (int i = tid; i < ROWS * COLS / 32; i += 512) {
+      const int row = i / (COLS / 32), c32 = c0 + (i % (COLS / 32)) * 32;
+      const int qi = q0 + row;
+      if (qi < nq) {
+        uint32_t w[16], q[8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 x = *(const uint4*)&so[row][c32 + 8 * v];
+          w[4 * v] = x.x; w[4 * v + 1] = x.y; w[4 * v + 2] = x.z; w[4 * v + 3] = x.w;
+        }
+        const uint32_t sb = mx_quantize32(w, q);
+        const int grow = b * a.S + qi / G, k = (j * G + qi % G) * DH + c32;
+        uint8_t* base = (uint8_t*)a.out;
+        *(uint4*)(base + mx_code_off(grow, k, RBT)) = make_uint4(q[0], q[1], q[2], q[3]);
+        *(uint4*)(base + mx_code_off(grow, k + 16, RBT)) = make_uint4(q[4], q[5], q[6], q[7]);
+        base[mx_scale_off(grow, k, RBT, K)] = (uint8_t)sb;
+      }
+    }
+    return;
+  }
+  // packed stores, 8 head dims per thread
+  for (int i = tid; i < ROWS * COLS / 8; i += 512) {
+    const int row = i / (COLS / 8), c8 = c0 + (i % (COLS / 8)) * 8;
+    const int qi = q0 + row;
+    if (qi < nq) {
+      const int s2 = qi / G, h = j * G + qi % G;
+      st_u4<COH>((uint16_t*)a.out + pk(b * a.S + s2, h * DH + c8, a.Hq * DH), *(const uint4*)&so[row][c8]);
+    }
+  }
+}
+
 // One work item of the register attention: wgi is the work item's index in
 // the launch's order (the XCD-aware remap below assumes work item i runs on
 // XCD i mod 8).  COH: Q and the suffix K/V come from other workgroups of the
@@ -369,14 +411,7 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
       for (int r = 0; r < 4; ++r)
         s_out[(lane >> 4) * 4 + r][(nbd0 + n) * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[0][n][r]);
     __syncthreads();
-    for (int i = tid; i < 2 * DH / DS; i += 512) {
-      const int row = i / (DH / DS / 8), c8 = ds * (DH / DS) + (i % (DH / DS / 8)) * 8;
-      const int qi = qb * 16 + row;
-      if (qi < nq) {
-        const int s2 = qi / G, h = j * G + qi % G;
-        st_u4<COH>((uint16_t*)a.out + pk(b * a.S + s2, h * DH + c8, a.Hq * DH), *(const uint4*)&s_out[row][c8]);
-      }
-    }
+    attn_store<DH, 16, DH / DS, COH>(a, s_out, b, j, qb * 16, nq, G, ds * (DH / DS), tid);
     return;
   }
 
@@ -415,15 +450,7 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
     }
   }
   __syncthreads();
-  // packed stores, 8 head dims per thread
-  for (int i = tid; i < QR * DH / 8 / DS; i += 512) {
-    const int row = i / (DH / DS / 8), c8 = ds * (DH / DS) + (i % (DH / DS / 8)) * 8;
-    const int qi = qb * QR + row;
-    if (qi < nq) {
-      const int s = qi / G, h = j * G + qi % G;
-      st_u4<COH>((uint16_t*)a.out + pk(b * a.S + s, h * DH + c8, a.Hq * DH), *(const uint4*)&s_out[row][c8]);
-    }
-  }
+  attn_store<DH, QR, DH / DS, COH>(a, s_out, b, j, qb * QR, nq, G, ds * (DH / DS), tid);
 }
 
 template <int DH, int R, int QB, int DS, bool PF, bool CAUSAL, bool KV8>

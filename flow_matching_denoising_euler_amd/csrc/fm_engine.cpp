@@ -81,7 +81,8 @@ struct fm_ctx {
   int* meta;
   float *h, *hs, *ssq, *ssqf, *xbuf0, *xbuf1, *vbuf, *vbuf2, *partials, *attn_part;
   void *u, *uf, *qkv, *o, *z;
-  void *u_mx, *z_mx;  // W8A8: fp8 activation buffers of the next norm's input and of the GELU gate product
+  void *u_mx, *z_mx, *o_mx;  // W8A8: fp8 activation buffers of the next norm's input, the GELU gate product and
+                             // the attention output
   unsigned* counters;
   size_t n_counters;
   size_t part_bytes = 0, attn_part_bytes = 0;  // scratch sizes (split-K and key-split partials)
@@ -431,6 +432,8 @@ void carve(fm_ctx* x, Arena& a) {
   const bool w8 = x->gwt == ELT_FP8_MX;
   x->u_mx = w8 ? a.take(Mp * d + Mp * d / 32) : nullptr;
   x->z_mx = w8 ? a.take(Mp * x->F + Mp * x->F / 32) : nullptr;
+  const long qd = (long)x->Hq * x->Dh;
+  x->o_mx = w8 ? a.take(Mp * qd + Mp * qd / 32) : nullptr;
   const long ks = std::max(x->ks_o, x->ks_d);
   const long Mp128 = (x->M + 127) / 128 * 128;  // rows covered by the large-M tiles
   x->part_bytes = ks > 1 ? ks * Mp128 * d * 4 : 16;
@@ -454,6 +457,10 @@ void carve(fm_ctx* x, Arena& a) {
 
 Tab T(const float* base, long stride) { return Tab{base, stride}; }
 
+// W8A8 with the register attention (up to 1024 padded keys): the attention
+// writes its output as the O projection's fp8 activation buffer
+bool attn_writes_mx(const fm_ctx* x) { return x->gwt == ELT_FP8_MX && (x->TP + x->SP) / 32 <= 32; }
+
 // arguments of the GEMM of phase `phase` (QKV, O, gate/up, down) of step k, layer l
 GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
   const bool ada = x->cfg.norm == FM_ADARMSNORM;
@@ -476,7 +483,8 @@ GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
       g.row_bstride = (long)x->L * x->S * x->HD;
     }
   } else if (phase == FM_PHASE_OPROJ) {  // O projection + residual; u = act(h * g2), ssq
-    g.A = x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16; g.ksplit = x->ks_o;
+    g.A = attn_writes_mx(x) ? x->o_mx : x->o; g.W = w.wo; g.wscale = w.so; g.N = x->d; g.K = x->Hq * x->Dh; g.nt = 16;
+    g.ksplit = x->ks_o;
     g.alpha = ada ? T(x->a1 + (long)l * x->d, x->st_g) : T(x->ones, 0);
     g.gnext = T(x->g2 + (long)l * x->d, x->st_g);
     g.u_out = w8 ? x->u_mx : x->u; g.ssq_out = x->ssq;
@@ -521,7 +529,8 @@ AttnArgs attn_args(const fm_ctx* x, int l) {
   at.nqblk = x->nqblk; at.nsplit = x->nsplit; at.keys_per_split = x->kps;
   at.scale = 1.f / sqrtf((float)x->Dh);
   at.part = x->attn_part; at.counters = x->counters;
-  at.out = x->o;
+  at.out = attn_writes_mx(x) ? x->o_mx : x->o;
+  at.out_mx = attn_writes_mx(x) ? 1 : 0;
   at.state_causal = x->cfg.state_causal && x->hasS;
   if (x->mtiles == 1 && x->act == ELT_BF16) {
     // one row tile: the O and gate/up GEMMs run skinny, workgroup u reading
@@ -538,13 +547,14 @@ AttnArgs attn_args(const fm_ctx* x, int l) {
   return at;
 }
 
-// one layer GEMM; W8A8 contexts take fp8 activation buffers from the GEMM
-// before (gate/up, down, and QKV after the first layer) and write them for
-// the GEMM after (O projection, gate/up, and down except at the last layer)
+// one layer GEMM; W8A8 contexts take fp8 activation buffers from the kernel
+// before (gate/up, down, QKV after the first layer, and O after the register
+// attention) and write them for the GEMM after (O projection, gate/up, and
+// down except at the last layer)
 hipError_t layer_gemm(const fm_ctx* x, int epi, int k, int l, int phase, hipStream_t st) {
   const GemmArgs g = gemm_args(x, k, l, phase);
   if (x->gwt != ELT_FP8_MX) return launch_gemm(x->act, x->gwt, epi, g, st);
-  const bool amx = phase == FM_PHASE_QKV ? l > 0 : phase != FM_PHASE_OPROJ;
+  const bool amx = phase == FM_PHASE_QKV ? l > 0 : (phase != FM_PHASE_OPROJ || attn_writes_mx(x));
   const bool omx = phase == FM_PHASE_OPROJ || phase == FM_PHASE_GATEUP || (phase == FM_PHASE_DOWN && l + 1 < x->L);
   return launch_gemm_mx(epi, g, amx, omx, st);
 }

@@ -6,22 +6,6 @@
 
 namespace fm {
 
-// fp8 activation buffers of the W8A8 GEMMs ([mtiles * 64 rows][K] with K a
-// multiple of 128): 2 KB code tiles of 16 rows x 128 k, tile (k / 128, row /
-// 16) at ((k / 128) RBT + row / 16) 2048 (RBT = mtiles * 4 row blocks), in
-// the operand layout of the block-scaled 16 x 16 x 128 MFMA (lane L = row %
-// 16 + 16 g holds k = 16 g + [0, 16) in bytes L 16 + [0, 16) and k = 64 +
-// 16 g + [0, 16) at 1024 + L 16); after all codes, one scale byte (X + 127)
-// per run of 32 k: 64 bytes per tile, run (row, (k % 128) / 32) at byte
-// row % 16 + 16 ((k % 128) / 32), the MFMA lane that reads it.
-__device__ __forceinline__ long mx_code_off(int row, int k, int RBT) {
-  const int kk = k & 127;
-  return ((long)(k >> 7) * RBT + (row >> 4)) * 2048 + (kk >> 6) * 1024 + ((row & 15) + 16 * ((kk & 63) >> 4)) * 16 +
-         (kk & 15);
-}
-__device__ __forceinline__ long mx_scale_off(int row, int k, int RBT, int K) {
-  return (long)(K >> 7) * RBT * 2048 + ((long)(k >> 7) * RBT + (row >> 4)) * 64 + (row & 15) + 16 * ((k & 127) >> 5);
-}
 // four fp32 values -> four E4M3 codes (round to nearest even), x in byte 0
 __device__ __forceinline__ uint32_t e4m3x4(float x, float y, float z, float w) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(x, y, 0, false);

@@ -27,36 +27,6 @@
 namespace fm {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-
-// E8M0 exponent X of the run's scale from the largest bf16 magnitude bits
-// p (sign cleared): the value is (1 + m / 128) 2^(e - 127) with e = p >> 7,
-// m = p & 127, and it fits 448 2^X = 1.75 2^(8 + X) with X = e - 135 exactly
-// when m <= 96 (1.75 = 1 + 96 / 128), else one binade higher
-__device__ __forceinline__ int mx_exponent(uint32_t p) {
-  const int X = (int)(p >> 7) - 135 + ((p & 0x7fu) > 0x60u ? 1 : 0);
-  return X < -126 ? -126 : X;
-}
-
-// 32 bf16 values (16 dwords, k ascending, two per dword, low half first) ->
-// 32 E4M3 codes (8 dwords, k ascending, byte 0 first) and the scale byte
-__device__ __forceinline__ uint32_t mx_quantize32(const uint32_t (&w)[16], uint32_t (&q)[8]) {
-  u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7fff7fffu);
-#pragma unroll
-  for (int i = 1; i < 16; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
-  const uint32_t p = m.x > m.y ? m.x : m.y;
-  const int X = mx_exponent(p);
-  const float scale = __uint_as_float((uint32_t)(X + 127) << 23);  // 2^X, a normal float
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    i16x2 lo = {0, 0};
-    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, w[2 * i]), scale, false);
-    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(bf16x2_t, w[2 * i + 1]), scale, true);
-    q[i] = __builtin_bit_cast(uint32_t, lo);
-  }
-  return (uint32_t)(X + 127);
-}
 
 // Workgroup barrier for LDS hand-offs that leaves global loads in flight
 __device__ __forceinline__ void mx_barrier() {

@@ -118,6 +118,7 @@ struct AttnArgs {
   // block-causal suffix: the state row (suffix row 0, the first Hq/Hkv query
   // rows of a kv group) sees no suffix key past itself
   int state_causal;
+  int out_mx;             // 1: `out` is the O projection's fp8 activation buffer (W8A8; register kernel only)
   // fp8 prefix cache: per (physical position, kv head) scales of K and V,
   // layer-l bases, robots sc_bstride floats apart (null: act-dtype cache)
   const float* kscale;

@@ -103,7 +103,7 @@ __device__ __forceinline__ AttnArgs load_attn(const KAS AttnArgs* s) {
   for (int i = 0; i < 2; ++i) {
     CP(pf_w[i]); CP(pf_nbt[i]); CP(pf_ku[i]); CP(pf_nb[i]); CP(pf_ks[i]); CP(pf_units[i]);
   }
-  CP(state_causal); CP(kscale); CP(vscale); CP(sc_bstride);
+  CP(state_causal); CP(out_mx); CP(kscale); CP(vscale); CP(sc_bstride);
   return d;
 }
 __device__ __forceinline__ OutArgs load_out(const KAS OutArgs* s) {
