@@ -20,8 +20,9 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   __shared__ float s_m[4][16], s_l[4][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qb = blockIdx.x % a.nqblk, jb = blockIdx.x / a.nqblk;
-  const int j = jb % a.Hkv, b = jb / a.Hkv;
+  const int j = jb % a.Hkv, b = __builtin_amdgcn_readfirstlane(jb / a.Hkv);
   const int G = a.Hq / a.Hkv, nq = a.S * G;
+  const KeySpace ks(a, b);  // scalar loads of the robot's metadata, before the Q loads
 
   // the 16 queries as A fragments (independent of the prefix state)
   uint4 qf[KBD];
@@ -32,7 +33,6 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < KBD; ++kb) qf[kb] = *(const uint4*)(qp + kb * 32);
   }
-  const KeySpace ks(a, b);
   const int ntile_all = (ks.kp + KT - 1) / KT;
   const int ntile = ntile_all > wave ? (ntile_all - wave + 3) / 4 : 0;  // tiles of this wave
 
@@ -171,7 +171,8 @@ constexpr int F32_KT = 64, F32_DH = 64;
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   __shared__ float sK[F32_KT][F32_DH + 1], sV[F32_KT][F32_DH + 1], sP[16][F32_KT + 1];
   const int nqb = (a.S + 15) / 16;
-  const int qb = blockIdx.x % nqb, h = (blockIdx.x / nqb) % a.Hq, b = blockIdx.x / (nqb * a.Hq);
+  const int qb = blockIdx.x % nqb, h = (blockIdx.x / nqb) % a.Hq;
+  const int b = __builtin_amdgcn_readfirstlane(blockIdx.x / (nqb * a.Hq));
   const int G = a.Hq / a.Hkv, j = h / G;
   const int tid = threadIdx.x, r = tid >> 4, sub = tid & 15;
   const int s = qb * 16 + r, sc_row = min(s, a.S - 1);

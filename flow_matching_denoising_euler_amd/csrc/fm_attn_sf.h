@@ -130,7 +130,10 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
   auto& s_o = lds.s_o;
   auto& s_out = lds.s_out;
   auto& s_last = lds.s_last;
-  const int tid = tid_x(), lane = tid & 63, w = tid >> 6;
+  // w is uniform in a wave: the key and head-dim blocks below, and with them
+  // the tile bases, are scalar values
+  const int tid = tid_x(), lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lofs = (uint32_t)lane * 16;  // this lane's bytes in a 1 KB fragment
   // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
   // a contiguous range of (robot, kv head, query block), so a robot's K/V
   // are fetched into one XCD's L2 rather than into all eight
@@ -141,19 +144,31 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
   wg /= DS;
   const int sp = wg % a.nsplit, grp = wg / a.nsplit;  // key range, query group
   const int qb = grp % a.nqblk, jb = grp / a.nqblk;
-  const int j = jb % a.Hkv, b = jb / a.Hkv;
+  const int j = jb % a.Hkv, b = __builtin_amdgcn_readfirstlane(jb / a.Hkv);
   const int G = a.Hq / a.Hkv, nq = a.S * G;
+  // the ring head first, as a scalar load (the robot index is uniform): the
+  // K and V tile addresses wait only for it (ring configurations), and not,
+  // through the in-order vector-load counter, for the Q loads below; the
+  // valid length, which only masks scores, is loaded after the K and V loads
+  KeySpace ks(a, b, false);
 
-  uint4 qf[QB][KBD];
+  // The QB query blocks as MFMA A fragments: every wave needs all of them, so
+  // the workgroup loads each 16-byte fragment once (thread t: fragments
+  // t + 512 f, fragment e = (u, kb, lane) with e = (u * KBD + kb) * 64 + lane)
+  // and passes them through LDS, in the staging rows of the output, which are
+  // idle until the end.  Per-wave loads of the whole blocks multiplied the
+  // workgroup's global reads, and the CU's load bandwidth bounds this kernel.
+  constexpr int NQF = QB * KBD * 64, QPT = (NQF + 511) / 512;
+  static_assert(NQF * 16 <= (int)sizeof(lds.s_out), "query fragments fit the output staging rows");
+  uint4 qld[QPT];
 #pragma unroll
-  for (int u = 0; u < QB; ++u) {
-    const int qi = min((qb * QB + u) * 16 + (lane & 15), nq - 1);
+  for (int f = 0; f < QPT; ++f) {
+    const int e = min(tid + 512 * f, NQF - 1);  // (past NQF: a reload, not stored)
+    const int ln = e & 63, kb = (e >> 6) % KBD, u = (e >> 6) / KBD;
+    const int qi = min((qb * QB + u) * 16 + (ln & 15), nq - 1);
     const int s = qi / G, h = j * G + qi % G;
-    const uint16_t* qp = (const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (lane >> 4) * 8;
-#pragma unroll
-    for (int kb = 0; kb < KBD; ++kb) qf[u][kb] = ld_u4<COH>(qp + kb * 32);
+    qld[f] = ld_u4<COH>((const uint16_t*)a.qkv + (long)(b * a.S + s) * a.Nqkv + (long)h * DH + (ln >> 4) * 8 + kb * 32);
   }
-  const KeySpace ks(a, b);
   const int nk16 = ks.kp >> 4, nk32 = ks.kp >> 5;  // kp is a multiple of 32
   // this workgroup's key range: 16-key blocks [kb0, kb0 + keys_per_split)
   // (one range covers all keys unless the key split is on); its local key
@@ -170,16 +185,18 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
   auto load_k = [&](int i, int slot) {
     const int nb = min(kb0 + w + 8 * i, nk16 - 1);
     if (pre16(i)) {
+      const uint8_t* kb8 = ks.kblock8(j, nb) + lane * 8;
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) {
-        const uint2 r = *(const uint2*)ks.ktile8(j, nb, kb, lane);
+        const uint2 r = *(const uint2*)(kb8 + kb * 512);
         kf[slot][kb] = uint4{r.x, r.y, 0u, 0u};
       }
     } else {
       const bool suf = COH && nb * 16 >= ks.TP;  // this step's suffix keys: written in this launch
+      const char* kbase = (const char*)ks.kblock(j, nb);
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) {
-        const uint16_t* kp = ks.ktile(j, nb, kb, lane);
+        const uint16_t* kp = (const uint16_t*)(kbase + lofs + kb * 1024);
         kf[slot][kb] = suf ? ld_u4<true>(kp) : *(const uint4*)kp;
       }
     }
@@ -204,16 +221,18 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
   auto load_v = [&](int i, int slot) {
     const int kb32 = min((kb0 >> 1) + kg + KG * i, nk32 - 1);
     if (pre32(i)) {
+      const uint8_t* vb8 = ks.vblock8(j, kb32) + nbd0 * 512 + lane * 8;
 #pragma unroll
       for (int n = 0; n < NBW; ++n) {
-        const uint2 r = *(const uint2*)ks.vtile8(j, kb32, nbd0 + n, lane);
+        const uint2 r = *(const uint2*)(vb8 + n * 512);
         vf[slot][n] = uint4{r.x, r.y, 0u, 0u};
       }
     } else {
       const bool suf = COH && kb32 * 32 >= ks.TP;
+      const char* vbase = (const char*)(ks.vblock(j, kb32) + nbd0 * 512);
 #pragma unroll
       for (int n = 0; n < NBW; ++n) {
-        const uint16_t* vp = ks.vtile(j, kb32, nbd0 + n, lane);
+        const uint16_t* vp = (const uint16_t*)(vbase + lofs + n * 1024);
         vf[slot][n] = suf ? ld_u4<true>(vp) : *(const uint4*)vp;
       }
     }
@@ -223,6 +242,19 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
 #pragma unroll
   for (int i = 0; i < VQ; ++i) load_v(i, i);
   __builtin_amdgcn_sched_barrier(0);
+  ks.tv = a.meta[2 * b];
+  uint4 qf[QB][KBD];
+  {
+    uint4* sq = (uint4*)&s_out[0][0];
+#pragma unroll
+    for (int f = 0; f < QPT; ++f)
+      if (tid + 512 * f < NQF) sq[tid + 512 * f] = qld[f];
+    lds_barrier();  // K and V loads stay in flight
+#pragma unroll
+    for (int u = 0; u < QB; ++u)
+#pragma unroll
+      for (int kb = 0; kb < KBD; ++kb) qf[u][kb] = sq[(u * KBD + kb) * 64 + lane];
+  }
   f32x4 sc[R][QB];
 #pragma unroll
   for (int i = 0; i < R; ++i) {

@@ -929,9 +929,12 @@ struct KeySpace {
   int kp, tv, head, TP, SP, NSP, S, n_static, ring, Hkv, Dh, frame_tokens, n_frames;
   // The suffix starts at the fixed position TP (the padded prefix capacity),
   // so key addresses depend on the stored prefix only through the ring head
-  // (ring configurations); the valid length only masks scores.
-  __device__ __forceinline__ KeySpace(const AttnArgs& a, int b) {
-    tv = a.meta[2 * b];
+  // (ring configurations); the valid length only masks scores.  With
+  // with_tv = false the caller sets tv itself, after its first K and V loads
+  // are issued: without a ring, nothing then stands between the kernel's
+  // start and those loads.
+  __device__ __forceinline__ KeySpace(const AttnArgs& a, int b, bool with_tv = true) {
+    tv = with_tv ? a.meta[2 * b] : 0;
     head = a.ring ? a.meta[2 * b + 1] : 0;
     TP = a.TP; SP = a.SP; NSP = a.NSP; S = a.S; n_static = a.n_static; ring = a.ring; Hkv = a.Hkv; Dh = a.Dh;
     frame_tokens = a.frame_tokens; n_frames = a.n_frames;
@@ -943,6 +946,7 @@ struct KeySpace {
   // physical prefix position of prefix position p, branch-free (logical
   // frame f of the window lives in slot (head + f) mod n_frames)
   __device__ __forceinline__ int phys(int p) const {
+    if (!ring) return p;  // uniform: no division without a ring
     const int rel = max(p - NSP, 0);
     const int f = rel / frame_tokens, off = rel - f * frame_tokens;
     int slot = head + f;
@@ -968,6 +972,29 @@ struct KeySpace {
     const long suf = soff + ((((long)j * (SP >> 5) + (max(p - TP, 0) >> 5)) * NBD + nbd) * 64 + lane) * 8;
     const uint16_t* base = p < TP ? (const uint16_t*)vpre : (const uint16_t*)vsuf;
     return base + (p < TP ? pre : suf);
+  }
+  // The same tiles as a block base for all lanes and 32- or 16-dim blocks:
+  // ktile(j, kb16, kb, lane) = kblock(j, kb16) + kb * 512 + lane * 8 and
+  // vtile(j, kb32, nbd, lane) = vblock(j, kb32) + nbd * 512 + lane * 8.  With
+  // wave-uniform block indices the base is scalar arithmetic, and each lane's
+  // load adds only its own 32-bit offset.
+  __device__ __forceinline__ const uint16_t* kblock(int j, int kb16) const {
+    const int p = kb16 * 16, KBD = Dh >> 5;
+    return p < TP ? (const uint16_t*)kpre + boff + (long)((j * (TP >> 4) + (phys(p) >> 4)) * KBD) * 512
+                  : (const uint16_t*)ksuf + soff + (long)((j * (SP >> 4) + ((p - TP) >> 4)) * KBD) * 512;
+  }
+  __device__ __forceinline__ const uint16_t* vblock(int j, int kb32) const {
+    const int p = kb32 * 32, NBD = Dh >> 4;
+    return p < TP ? (const uint16_t*)vpre + boff + (long)((j * (TP >> 5) + (phys(p) >> 5)) * NBD) * 512
+                  : (const uint16_t*)vsuf + soff + (long)((j * (SP >> 5) + ((p - TP) >> 5)) * NBD) * 512;
+  }
+  __device__ __forceinline__ const uint8_t* kblock8(int j, int kb16) const {
+    const int p = kb16 * 16, KBD = Dh >> 5;
+    return (const uint8_t*)kpre + boff + (long)((j * (TP >> 4) + (phys(p) >> 4)) * KBD) * 512;
+  }
+  __device__ __forceinline__ const uint8_t* vblock8(int j, int kb32) const {
+    const int p = kb32 * 32, NBD = Dh >> 4;
+    return (const uint8_t*)vpre + boff + (long)((j * (TP >> 5) + (phys(p) >> 5)) * NBD) * 512;
   }
   // fp8 cache: the same tiles of the prefix with one byte per element (8 bytes a lane)
   __device__ __forceinline__ const uint8_t* ktile8(int j, int kb16, int kb, int lane) const {
