@@ -117,7 +117,7 @@ __device__ __forceinline__ void attn_sf_body(const AttnArgs& a, int wgi, AttnSfS
   constexpr int NBD3 = NBD / DS;
   static_assert(DS == 1 || (QB == 1 && NBD3 >= 4), "dim split: one query block, 4 or more output blocks");
   // K and V blocks in flight per wave, within about 240 registers
-  constexpr int KQ0 = (QB == 1 ? (R <= 4 ? 24 : 16) : (R <= 4 ? 16 : 8)) / KBD;
+  constexpr int KQ0 = (QB == 1 ? (R <= 4 ? 24 : 16) : (R <= 6 ? 16 : 8)) / KBD;
   constexpr int KQ = KQ0 < 1 ? 1 : (KQ0 < R ? KQ0 : R);
   constexpr int KPAD = 128 * R + 8;                    // P row: keys of blocks nb < 8R, padded
   constexpr int NBW = NBD3 >= 8 ? NBD3 / 8 : 1;        // head-dim blocks per wave
