@@ -386,6 +386,8 @@ def main():
     ap.add_argument("--w8a8", action="store_true",
                     help="fp8 weights and fp8 GEMM activations (32-element power-of-two blocks, block-scaled MFMA)")
     ap.add_argument("--exec-mode", type=int, default=0)
+    ap.add_argument("--attn-kernel", choices=("auto", "register", "streamed"), default="auto",
+                    help="attention kernel (auto: the register kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 256 MiB device copy (reference for PMC byte counters)")
@@ -431,6 +433,8 @@ def main():
         cfg = cfg.replace(n_steps=args.n_steps)
     if args.kv_fp8:
         cfg = cfg.replace(kv_fp8=True)
+    if args.attn_kernel != "auto":
+        cfg = cfg.replace(attn_kernel=args.attn_kernel)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     log(f"bench: generating {cfg.name}")
@@ -542,6 +546,7 @@ def main():
                    "d_model": cfg.d_model,
                    "layers": cfg.n_layers, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                    "d_mlp": cfg.d_mlp, "norm": cfg.norm, "exec_mode": int(info.exec_mode),
+                   "attention": "streamed" if cfg.attn_kernel == "streamed" else "register",
                    "parallelism": "single GPU"},
         "chunks_per_s": round(1000.0 / ms * cfg.batch, 2),
         "latency_ms": {"p10": round(pct(.1), 4), "p50": round(statistics.median(per), 4),

@@ -89,6 +89,8 @@ def make_config(cfg, exec_mode: int = FM_EXEC_AUTO) -> fm_config:
     c.kv_fp8 = 1 if getattr(cfg, "kv_fp8", False) else 0
     c.rope_theta = float(getattr(cfg, "rope_theta", 0.0))
     c.w8a8 = 1 if getattr(cfg, "w8a8", False) else 0
+    c.attn_kernel = {"auto": _abi.FM_ATTN_AUTO, "register": _abi.FM_ATTN_REGISTER,
+                     "streamed": _abi.FM_ATTN_STREAMED}[getattr(cfg, "attn_kernel", "auto")]
     sched = getattr(cfg, "t_schedule", None)
     if sched is not None:
         arr = (ctypes.c_float * len(sched))(*[float(t) for t in sched])

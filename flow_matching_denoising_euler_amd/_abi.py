@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfmdenoise.so")
 
-FM_ABI_VERSION = 6
+FM_ABI_VERSION = 7
 
 FM_OK, FM_ERR_ARG, FM_ERR_SHAPE, FM_ERR_STATE, FM_ERR_OOM, FM_ERR_DEVICE, FM_ERR_UNSUPPORTED = range(7)
 STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_ARG", 2: "FM_ERR_SHAPE", 3: "FM_ERR_STATE", 4: "FM_ERR_OOM",
@@ -18,6 +18,7 @@ FM_F32, FM_BF16, FM_FP8_E4M3 = 0, 1, 2
 FM_RMSNORM, FM_ADARMSNORM = 0, 1
 FM_EXEC_AUTO, FM_EXEC_GRAPH, FM_EXEC_PERSISTENT = 0, 1, 2
 FM_SAMPLER_EULER, FM_SAMPLER_HEUN, FM_SAMPLER_AB2 = 0, 1, 2
+FM_ATTN_AUTO, FM_ATTN_REGISTER, FM_ATTN_STREAMED = 0, 1, 2
 (FM_LW_WQ, FM_LW_WK, FM_LW_WV, FM_LW_WO, FM_LW_WG, FM_LW_WU, FM_LW_WD,
  FM_LW_NORM1, FM_LW_NORM1_B, FM_LW_NORM2, FM_LW_NORM2_B, FM_LW_COUNT) = range(12)
 
@@ -33,7 +34,7 @@ class fm_config(ctypes.Structure):
         "action_dim", "chunk", "state_dim", "batch", "n_steps", "prefix_static", "frame_tokens",
         "n_frames", "norm", "time_dim", "weight_dtype", "act_dtype")] + [
         ("rms_eps", ctypes.c_float), ("exec_mode", ctypes.c_int32), ("sampler", ctypes.c_int32), ("state_causal", ctypes.c_int32), ("kv_fp8", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("w8a8", ctypes.c_int32),
-        ("t_schedule", ctypes.POINTER(ctypes.c_float))]
+        ("t_schedule", ctypes.POINTER(ctypes.c_float)), ("attn_kernel", ctypes.c_int32)]
 
 
 class fm_weights(ctypes.Structure):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfmdenoise.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("fm_gemm.hip", "fm_gemm_mx.hip", "fm_attn.hip", "fm_attn_sf_a.hip", "fm_attn_sf_b.hip",
+SOURCES = [os.path.join(CSRC, f) for f in ("fm_gemm.hip", "fm_gemm_mx.hip", "fm_attn.hip", "fm_attn_wide.hip", "fm_attn_sf_a.hip", "fm_attn_sf_b.hip",
                                                   "fm_attn_sf_c.hip", "fm_attn_sf_d.hip", "fm_misc.hip", "fm_noalloc.hip", "fm_persist_bf16.hip",
                                                   "fm_persist_fp8.hip", "fm_engine.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -265,6 +265,15 @@ static hipError_t attn_bf16(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st) {
+  if (act != ELT_F32 && a.wide_nw > 0) {  // the streamed kernel (fm_attn_wide.hip)
+    switch (a.Dh) {
+      case 32: return attn_wide<32>(a, st);
+      case 64: return attn_wide<64>(a, st);
+      case 128: return attn_wide<128>(a, st);
+      case 256: return attn_wide<256>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (act == ELT_F32 ? 0 : a.Dh) {
     case 32: return attn_bf16<32>(a, st);
     case 64: return attn_bf16<64>(a, st);

@@ -66,14 +66,14 @@ struct AttnSfSmem {
 // head dims [c0, c0 + COLS), from the bf16 staging rows `so`: packed bf16
 // stores, or (a.out_mx) runs of 32 head dims quantised into the O
 // projection's fp8 activation buffer (the layout of fm_device.h), one run per
-// thread.
-template <int DH, int ROWS, int COLS, bool COH, int LDW>
+// thread; NT threads take part.
+template <int DH, int ROWS, int COLS, bool COH, int LDW, int NT = 512>
 __device__ __forceinline__ void attn_store(const AttnArgs& a, const uint16_t (*so)[LDW], int b, int j, int q0, int nq,
                                            int G, int c0, int tid) {
   if constexpr (!COH) if (a.out_mx) {
     static_assert(COLS % 32 == 0, "whole 32-dim runs");
     const int RBT = (a.B * a.S + 63) / 64 * 4, K = a.Hq * DH;
-    for (int i = tid; i < ROWS * COLS / 32; i += 512) {
+    for (int i = tid; i < ROWS * COLS / 32; i += NT) {
       const int row = i / (COLS / 32), c32 = c0 + (i % (COLS / 32)) * 32;
       const int qi = q0 + row;
       if (qi < nq) {
@@ -94,7 +94,7 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, const uint16_t (*s
     return;
   }
   // packed stores, 8 head dims per thread
-  for (int i = tid; i < ROWS * COLS / 8; i += 512) {
+  for (int i = tid; i < ROWS * COLS / 8; i += NT) {
     const int row = i / (COLS / 8), c8 = c0 + (i % (COLS / 8)) * 8;
     const int qi = q0 + row;
     if (qi < nq) {

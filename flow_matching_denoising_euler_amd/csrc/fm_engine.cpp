@@ -66,6 +66,8 @@ struct fm_ctx {
   std::vector<float> ab_cur, ab_prev;  // its weights of v_k and v_(k-1) per step
   int NT;     // time rows of the t-dependent tables (N, or N + 1 for Heun)
   int ks_o, ks_d, nqblk, nsplit, kps;
+  bool attn_wide = false;  // the streamed attention kernel (nqblk, nsplit, kps then follow wide_plan)
+  int wide_nw = 0;
   int NSP, TP, SP;  // static region padded to 32, padded physical prefix capacity, suffix padded to 32
 
   // arena
@@ -173,6 +175,7 @@ fm_status validate_config(const fm_config* c) {
   if (c->state_causal != 0 && c->state_causal != 1) return fail(nullptr, FM_ERR_ARG, "state_causal must be 0 or 1");
   if (c->kv_fp8 != 0 && c->kv_fp8 != 1) return fail(nullptr, FM_ERR_ARG, "kv_fp8 must be 0 or 1");
   if (c->w8a8 != 0 && c->w8a8 != 1) return fail(nullptr, FM_ERR_ARG, "w8a8 must be 0 or 1");
+  if (c->attn_kernel < FM_ATTN_AUTO || c->attn_kernel > FM_ATTN_STREAMED) return fail(nullptr, FM_ERR_ARG, "bad attn_kernel");
   if (!(c->rope_theta >= 0.f) || std::isinf(c->rope_theta)) return fail(nullptr, FM_ERR_ARG, "rope_theta must be 0 or positive");
   if (c->rope_theta > 0.f && c->n_frames > 0)
     return fail(nullptr, FM_ERR_UNSUPPORTED, "rotary positions with a frame ring: the window would move cached positions");
@@ -217,6 +220,12 @@ fm_status validate_config(const fm_config* c) {
                   (long)c->batch * S);
     if (c->exec_mode == FM_EXEC_PERSISTENT)
       return fail(nullptr, FM_ERR_UNSUPPORTED, "w8a8: the persistent loop covers batch-1 contexts only");
+  }
+  if (c->attn_kernel == FM_ATTN_STREAMED) {
+    if (f32 || c->kv_fp8)
+      return fail(nullptr, FM_ERR_UNSUPPORTED, "the streamed attention takes bf16 activations and a bf16 prefix cache");
+    if (c->exec_mode == FM_EXEC_PERSISTENT)
+      return fail(nullptr, FM_ERR_UNSUPPORTED, "the persistent loop runs the register attention");
   }
   if (f32) {
     if (c->head_dim > 64 || S > 256) return fail(nullptr, FM_ERR_UNSUPPORTED, "fp32 path: head_dim <= 64, suffix <= 256");
@@ -323,6 +332,20 @@ void derive(fm_ctx* x) {
     x->kps = ((nk16 + ns - 1) / ns + 1) / 2 * 2;
     x->nsplit = (nk16 + x->kps - 1) / x->kps;
   }
+  {
+    // The streamed attention runs on request only: measured on MI355X it is
+    // slower than the register kernel on every workload (16 robots: 46.6
+    // against 17 us per launch), see fm_attn_wide.hip.
+    const int nq = x->S * (x->Hq / x->Hkv);
+    x->attn_wide = x->act == ELT_BF16 && !x->kv8 && c.attn_kernel == FM_ATTN_STREAMED;
+    if (x->attn_wide) {
+      const WidePlan p = wide_plan(x->B, x->Hkv, nq, (x->TP + x->SP) / 16, x->n_cu);
+      x->wide_nw = p.nw;
+      x->nqblk = p.nqg;
+      x->nsplit = p.ns;
+      x->kps = p.kps;
+    }
+  }
 }
 
 // Whether the persistent loop kernel covers this context; on false, *why
@@ -337,6 +360,7 @@ bool persist_plan(fm_ctx* x, const char** why) {
   if (x->encoder) return no("encoder context");
   if (x->act != ELT_BF16 || x->wt == ELT_F32) return no("needs bf16 activations and bf16 or fp8 weights");
   if (x->mtiles != 1) return no("needs batch x suffix <= 64 rows");
+  if (x->attn_wide) return no("runs the register attention");
   if (x->Dh != 256 || x->A != 32) return no("needs head_dim 256 and action_dim 32");
   if ((c.state_causal && x->hasS) || x->kv8 || c.rope_theta > 0.f)
     return no("the block-causal state, the fp8 cache and rotary positions run as a graph");
@@ -440,7 +464,10 @@ void carve(fm_ctx* x, Arena& a) {
   x->partials = (float*)a.take(x->part_bytes);
   // per (query group, head-dim part (up to 2), key range): 16 rows x Dh / parts
   // partial output, row max, row sum
-  x->attn_part_bytes = x->nsplit == 1 ? 16 : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 4) * 4;
+  // (streamed kernel: per (query group, key range) wide_part_floats)
+  x->attn_part_bytes = x->nsplit == 1 ? 16
+                       : x->attn_wide ? (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * wide_part_floats(x->wide_nw, x->Dh) * 4
+                                      : (size_t)x->B * x->Hkv * x->nqblk * x->nsplit * 16 * (x->Dh + 4) * 4;
   x->attn_part = (float*)a.take(x->attn_part_bytes);
   x->n_counters = std::max<size_t>((size_t)x->mtiles * (std::max(std::max(x->Nqkv, 2 * x->F), x->d) / 16 + 1),
                                    (size_t)x->B * x->Hkv * x->nqblk * 2) + 64;
@@ -457,9 +484,10 @@ void carve(fm_ctx* x, Arena& a) {
 
 Tab T(const float* base, long stride) { return Tab{base, stride}; }
 
-// W8A8 with the register attention (up to 1024 padded keys): the attention
-// writes its output as the O projection's fp8 activation buffer
-bool attn_writes_mx(const fm_ctx* x) { return x->gwt == ELT_FP8_MX && (x->TP + x->SP) / 32 <= 32; }
+// W8A8 with the register attention (up to 1024 padded keys) or the streamed
+// one: the attention writes its output as the O projection's fp8 activation
+// buffer
+bool attn_writes_mx(const fm_ctx* x) { return x->gwt == ELT_FP8_MX && (x->attn_wide || (x->TP + x->SP) / 32 <= 32); }
 
 // arguments of the GEMM of phase `phase` (QKV, O, gate/up, down) of step k, layer l
 GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
@@ -532,6 +560,7 @@ AttnArgs attn_args(const fm_ctx* x, int l) {
   at.out = attn_writes_mx(x) ? x->o_mx : x->o;
   at.out_mx = attn_writes_mx(x) ? 1 : 0;
   at.state_causal = x->cfg.state_causal && x->hasS;
+  at.wide_nw = x->attn_wide ? x->wide_nw : 0;
   if (x->mtiles == 1 && x->act == ELT_BF16) {
     // one row tile: the gate/up GEMM runs skinny, workgroup u reading column
     // tile u (k-range u % ks of tile u / ks in general); the idle CUs prefetch

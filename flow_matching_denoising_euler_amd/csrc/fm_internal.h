@@ -124,6 +124,9 @@ struct AttnArgs {
   const float* kscale;
   const float* vscale;
   long sc_bstride;
+  // > 0: the streamed kernel (k_attn_wide) with wide_nw waves of 32 query
+  // rows; nqblk then counts its query groups of 32 * wide_nw rows
+  int wide_nw;
 };
 
 struct OutArgs {
@@ -278,6 +281,33 @@ MxPlan mx_plan(int epi);
 // epilogue writes its activation output (out or u_out) as an fp8 activation buffer
 hipError_t launch_gemm_mx(int epi, const GemmArgs& g, bool amx, bool omx, hipStream_t st);
 hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st);
+
+// The streamed attention (k_attn_wide, on request): a workgroup of nw waves takes 32 * nw
+// query rows of one (robot, kv head) and one of ns key ranges of kps 16-key
+// blocks (even: ranges start on 32-key chunks); the ranges of a query group
+// are merged by the last workgroup to arrive.  Key ranges are added while the
+// grid stays within one workgroup per CU and every range keeps at least four
+// 32-key chunks, up to WIDE_MAX_SPLIT.
+constexpr int WIDE_NW = 4, WIDE_MAX_SPLIT = 4;
+struct WidePlan {
+  int nw, nqg, ns, kps;
+};
+inline WidePlan wide_plan(int B, int Hkv, int nq, int nk16, int n_cu) {
+  WidePlan p{};
+  p.nw = WIDE_NW;
+  p.nqg = (nq + 32 * p.nw - 1) / (32 * p.nw);
+  const int groups = B * Hkv * p.nqg;
+  int ns = 1;
+  while (ns < WIDE_MAX_SPLIT && groups * ns * 2 <= n_cu && nk16 >= 16 * ns) ns *= 2;
+  p.kps = ((nk16 + ns - 1) / ns + 1) / 2 * 2;
+  p.ns = (nk16 + p.kps - 1) / p.kps;
+  return p;
+}
+// floats of one key range's partial result: 32 * nw rows x Dh outputs, then
+// the rows' maxima and sums
+__host__ __device__ inline long wide_part_floats(int nw, int Dh) { return 32L * nw * Dh + 64L * nw; }
+template <int DH>
+hipError_t attn_wide(const AttnArgs& a, hipStream_t st);
 hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st);
 hipError_t launch_embed(int act, const EmbedArgs& e, hipStream_t st);
 

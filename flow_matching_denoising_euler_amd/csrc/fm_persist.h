@@ -103,7 +103,7 @@ __device__ __forceinline__ AttnArgs load_attn(const KAS AttnArgs* s) {
   for (int i = 0; i < 2; ++i) {
     CP(pf_w[i]); CP(pf_nbt[i]); CP(pf_ku[i]); CP(pf_nb[i]); CP(pf_ks[i]); CP(pf_units[i]);
   }
-  CP(state_causal); CP(out_mx); CP(kscale); CP(vscale); CP(sc_bstride);
+  CP(state_causal); CP(out_mx); CP(kscale); CP(vscale); CP(sc_bstride); CP(wide_nw);
   return d;
 }
 __device__ __forceinline__ OutArgs load_out(const KAS OutArgs* s) {
@@ -115,7 +115,7 @@ __device__ __forceinline__ OutArgs load_out(const KAS OutArgs* s) {
   return d;
 }
 #undef CP
-static_assert(sizeof(Tab) == 16 && sizeof(GemmArgs) == 240 && sizeof(AttnArgs) == 248 && sizeof(OutArgs) == 240,
+static_assert(sizeof(Tab) == 16 && sizeof(GemmArgs) == 240 && sizeof(AttnArgs) == 256 && sizeof(OutArgs) == 240,
               "the field-wise loaders above copy every field");
 
 // a GEMM's arguments at layer l and time row `step`

@@ -67,6 +67,7 @@ class FMConfig:
     kv_fp8: bool = False        # prefix K/V cached as fp8 E4M3 with a scale per (token, kv head)
     rope_theta: float = 0.0     # rotary position embedding base (0: none)
     w8a8: bool = False          # fp8 weights: also quantise GEMM activations (32-element blocks, power-of-two scales)
+    attn_kernel: str = "auto"   # GPU attention kernel: "auto", "register" or "streamed" (no effect on the math)
 
     @property
     def has_state(self) -> int:

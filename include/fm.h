@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 6
+#define FM_ABI_VERSION 7
 
 typedef struct fm_ctx fm_ctx;
 
@@ -102,6 +102,19 @@ typedef enum {
   FM_EXEC_GRAPH = 1,       /* one hipGraph of per-phase kernel launches   */
   FM_EXEC_PERSISTENT = 2   /* one persistent kernel for the whole loop     */
 } fm_exec;
+
+/* Which attention kernel runs the suffix queries (bf16 activations).
+ * FM_ATTN_REGISTER: the scores of a block of 16 or 32 query rows against all
+ * keys held in registers, a two-pass softmax (up to 1024 padded keys; an
+ * online-softmax kernel beyond).  FM_ATTN_STREAMED: workgroups of 128 query
+ * rows of one (robot, kv head); 32-key chunks of K and V pass through LDS
+ * once and serve all of them, each wave keeps an online softmax of its 32
+ * rows, and up to 4 key ranges per query group are merged by the last
+ * workgroup to arrive (any prefix length; not with kv_fp8 or the
+ * persistent loop).  FM_ATTN_AUTO runs the register kernel: measured on
+ * MI355X the streamed one is slower on every workload here.  Both are
+ * bitwise deterministic; they differ in rounding. */
+typedef enum { FM_ATTN_AUTO = 0, FM_ATTN_REGISTER = 1, FM_ATTN_STREAMED = 2 } fm_attn_kernel;
 
 /*
  * Model and workload.  Notation: B batch (independent robots), C chunk,
@@ -191,6 +204,7 @@ typedef struct {
   float rope_theta;                  /* 0 or the rotary base, see above */
   int32_t w8a8;                      /* 0 or 1, see above */
   const float* t_schedule;           /* NULL: uniform; else N + 1 host times */
+  int32_t attn_kernel;               /* fm_attn_kernel */
 } fm_config;
 
 /* Per-layer weight slots of fm_weights.layers. */

@@ -33,7 +33,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(_abi.fm_config) == 26 * 4 + 8  # 26 scalars, the t_schedule pointer
+    # 26 scalars, the t_schedule pointer, attn_kernel (and 4 bytes of padding to the pointer's alignment)
+    assert ctypes.sizeof(_abi.fm_config) == 26 * 4 + 8 + 8
+    assert _abi.fm_config.attn_kernel.offset == 26 * 4 + 8
     assert ctypes.sizeof(_abi.fm_weights) == 11 * 8
     assert ctypes.sizeof(_abi.fm_info) == 3 * 8 + 4 * 4
 
@@ -76,6 +78,11 @@ def _create(c):
     (lambda c: setattr(c, "w8a8", 1), _abi.FM_ERR_UNSUPPORTED),     # fp32 weights
     (lambda c: (setattr(c, "w8a8", 1), setattr(c, "act_dtype", _abi.FM_BF16), setattr(c, "weight_dtype", _abi.FM_FP8_E4M3)),
      _abi.FM_ERR_UNSUPPORTED),                                        # d_model 64 is not a multiple of 128
+    (lambda c: setattr(c, "attn_kernel", 3), _abi.FM_ERR_ARG),
+    (lambda c: setattr(c, "attn_kernel", _abi.FM_ATTN_STREAMED), _abi.FM_ERR_UNSUPPORTED),  # fp32 activations
+    (lambda c: (setattr(c, "attn_kernel", _abi.FM_ATTN_STREAMED), setattr(c, "act_dtype", _abi.FM_BF16),
+                setattr(c, "weight_dtype", _abi.FM_BF16), setattr(c, "head_dim", 32), setattr(c, "n_q_heads", 2),
+                setattr(c, "n_kv_heads", 1), setattr(c, "kv_fp8", 1)), _abi.FM_ERR_UNSUPPORTED),  # fp8 prefix cache
     (lambda c: setattr(c, "rope_theta", -1.0), _abi.FM_ERR_ARG),
     (lambda c: setattr(c, "rope_theta", float("nan")), _abi.FM_ERR_ARG),
     (lambda c: (setattr(c, "rope_theta", 1e4), setattr(c, "n_frames", 2), setattr(c, "frame_tokens", 32)),
