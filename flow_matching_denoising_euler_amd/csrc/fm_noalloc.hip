@@ -13,10 +13,12 @@ namespace {
 // ends.  In host code `scratch` is a host-side stand-in, never a device
 // address; kernels receive the address hipGetSymbolAddress returns for the
 // current device (scratch_ptr below).  8 MiB covers every configuration
-// fm_create accepts: split-K partials only arise with at most two 64-row
-// tiles (<= 4 x 128 rows x 1024 columns fp32 = 2 MiB) and key-range
-// partials with at most 64 query groups (<= 64 x 4 ranges x 16 x 260 fp32 =
-// 4.1 MiB), plus a few KiB of counters.
+// fm_create accepts with the register attention: split-K partials only
+// arise with at most two 64-row tiles (<= 4 x 128 rows x 1024 columns fp32 =
+// 2 MiB) and key-range partials with at most 64 query groups (<= 64 x 4
+// ranges x 16 x 260 fp32 = 4.1 MiB), plus a few KiB of counters.  The
+// streamed attention's partials can exceed it (the call then returns
+// FM_ERR_UNSUPPORTED).
 constexpr size_t FM_SCRATCH_BYTES = 8u << 20;
 static __device__ __align__(256) unsigned char scratch[FM_SCRATCH_BYTES];
 

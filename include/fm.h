@@ -368,8 +368,10 @@ const char* fm_last_error(const fm_ctx* ctx);
  * hipFree) and launches the loop's kernels one by one (no graph), clearing
  * the counters with a kernel first, so the call may itself be recorded into
  * a caller's graph.  A context whose scratch exceeds 8 MiB gets
- * FM_ERR_UNSUPPORTED (none that fm_create accepts needs more than about
- * 6.5 MiB).  Every call on one GPU shares that GPU's array: calls
+ * FM_ERR_UNSUPPORTED: with the register attention none that fm_create
+ * accepts needs more than about 6.5 MiB; the streamed attention's key-range
+ * partials (128 query rows x head_dim fp32 per range) can need up to about
+ * 34 MiB.  Every call on one GPU shares that GPU's array: calls
  * that overlap on one GPU (other streams, other threads, other contexts)
  * race and must be serialised by the caller.
  */
