@@ -59,17 +59,20 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed PMC summary of
-    `workload`, if it was taken on the current kernel sources."""
+def load_traffic(workload, phase):
+    """HBM bytes per launch of `phase` from the committed PMC summary of
+    `workload` (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's
+    readings), if it was taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_sha") != kernel_source_sha() or t.get("phase") != kernel:
+    if t.get("source_sha") != kernel_source_sha():
         return None
-    return t.get("traffic_bytes")
+    if "phases" in t:
+        return t["phases"].get(phase, {}).get("traffic_bytes")
+    return t.get("traffic_bytes") if t.get("phase") == phase else None
 
 
 PHASE_NAMES = ["QKV GEMM (norm1 folded)", "attention", "O GEMM + residual", "gate/up GEMM + GELU gate",
