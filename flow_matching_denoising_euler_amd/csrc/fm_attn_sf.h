@@ -24,9 +24,10 @@ namespace fm {
 // Every global load of a phase is issued before its first use; there is no
 // online rescaling and, for DH >= 128, no merge of partial outputs.
 // Workgroups past the attention grid: read the tiles of the next GEMMs'
-// packed weights that the workgroups of this XCD will read into this XCD's
-// L2 (the consuming workgroup u runs on XCD u % 8).  The prefetchers of an
-// XCD take its units round robin; each wave reads every 8th tile of a unit.
+// packed weights that the workgroups of this XCD will read (the consuming
+// workgroup u runs on XCD u % 8), which leaves them in the last-level cache
+// for the GEMM.  The prefetchers of an XCD take its units round robin; each
+// wave reads every 8th tile of a unit.
 __device__ __forceinline__ void attn_weight_prefetch(const AttnArgs& a) {
   const int x = blockIdx.x & 7;
   const int first = (a.grid - x + 7) >> 3;           // attention workgroups on this XCD

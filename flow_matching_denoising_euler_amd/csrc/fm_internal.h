@@ -107,10 +107,12 @@ struct AttnArgs {
   void* out;              // [B*S][Hq*Dh] act
   // Weight prefetch by the CUs the attention grid leaves idle (one row tile,
   // skinny GEMMs next): workgroups past the attention grid read the packed
-  // weights of the following GEMMs (1 KB tiles) into the L2 of the XCD whose
-  // workgroups will read them.  Matrix i is read by nunits[i] workgroups;
-  // workgroup u (on XCD u % 8) reads column blocks [(u / ks) * nb, + nb) and
-  // k-units [(u % ks) * ku / ks, + ku / ks).
+  // weights of the following GEMMs (1 KB tiles) on the XCD whose workgroups
+  // will read them, so that the last-level cache holds them when the GEMM
+  // starts (L2 contents do not outlive the kernel: the GEMM still fetches
+  // them past its L2, from that cache instead of HBM).  Matrix i is read by
+  // nunits[i] workgroups; workgroup u (on XCD u % 8) reads column blocks
+  // [(u / ks) * nb, + nb) and k-units [(u % ks) * ku / ks, + ku / ks).
   int pf_cus;             // CUs of the device (0: no prefetch)
   int grid;               // attention workgroups (set by the launcher)
   const uint8_t* pf_w[2]; // packed weights (null: none)
