@@ -162,14 +162,15 @@ __global__ __launch_bounds__(256) void k_attn_flash(AttnArgs a) {
   }
 }
 
-// fp32 attention (head_dim <= 64): workgroup = (robot, query head, block of
-// 16 suffix rows), 16 threads per row.  Keys go through LDS in tiles of 64
-// (K and V rows padded against bank conflicts); each tile's scores, an online
+// fp32 attention (head_dim <= DH <= 64): workgroup = (robot, query head,
+// block of 16 suffix rows), 16 threads per row.  Keys go through LDS in tiles
+// of 64 (K and V rows padded against bank conflicts); each tile's scores, an online
 // softmax update and the P V product run from LDS.  Thread (row, sub) scores
 // keys sub + 16 i of the tile and accumulates output dims sub + 16 i.
 constexpr int F32_KT = 64, F32_DH = 64;
+template <int DH>
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
-  __shared__ float sK[F32_KT][F32_DH + 1], sV[F32_KT][F32_DH + 1], sP[16][F32_KT + 1];
+  __shared__ float sK[F32_KT][DH + 1], sV[F32_KT][DH + 1], sP[16][F32_KT + 1];
   const int nqb = (a.S + 15) / 16;
   const int qb = blockIdx.x % nqb, h = (blockIdx.x / nqb) % a.Hq;
   const int b = __builtin_amdgcn_readfirstlane(blockIdx.x / (nqb * a.Hq));
@@ -178,12 +179,12 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   const int s = qb * 16 + r, sc_row = min(s, a.S - 1);
   const KeySpace ks(a, b);
   const int Dh = a.Dh;
-  float q[F32_DH], o[F32_DH / 16];
+  float q[DH], o[(DH + 15) / 16];
   const float* qp = (const float*)a.qkv + (long)(b * a.S + sc_row) * a.Nqkv + (long)h * Dh;
 #pragma unroll
-  for (int c = 0; c < F32_DH; ++c) q[c] = c < Dh ? qp[c] : 0.f;
+  for (int c = 0; c < DH; ++c) q[c] = c < Dh ? qp[c] : 0.f;
 #pragma unroll
-  for (int i = 0; i < F32_DH / 16; ++i) o[i] = 0.f;
+  for (int i = 0; i < (DH + 15) / 16; ++i) o[i] = 0.f;
   float m = -INFINITY, l = 0.f;
   for (int p0 = 0; p0 < ks.kp; p0 += F32_KT) {
     for (int e = tid; e < F32_KT * Dh; e += 256) {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       const int pl = sub + 16 * i, key = p0 + pl;
       float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < F32_DH; ++c)
+      for (int c = 0; c < DH; ++c)
         if (c < Dh) dot += q[c] * sK[pl][c];
       const bool ok = key < ks.kp && ks.valid(key) && !(a.state_causal && s == 0 && key > ks.TP);
       sc[i] = ok ? dot * a.scale : -INFINITY;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     m = mn;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < F32_DH / 16; ++i) {
+    for (int i = 0; i < (DH + 15) / 16; ++i) {
       const int c = sub + 16 * i;
       if (c < Dh) {
         float acc = 0.f;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   }
   if (s < a.S) {
 #pragma unroll
-    for (int i = 0; i < F32_DH / 16; ++i) {
+    for (int i = 0; i < (DH + 15) / 16; ++i) {
       const int c = sub + 16 * i;
       if (c < Dh) ((float*)a.out)[pk(b * a.S + s, h * Dh + c, a.Hq * Dh)] = o[i] / l;
     }
@@ -282,7 +283,10 @@ hipError_t launch_attn(int act, const AttnArgs& a, hipStream_t st) {
   }
   if (act == ELT_F32) {
     if (a.Dh > F32_DH) return hipErrorInvalidValue;
-    FM_LAUNCH(k_attn_f32, a.B * a.Hq * ((a.S + 15) / 16), a);
+    const int grid = a.B * a.Hq * ((a.S + 15) / 16);
+    if (a.Dh <= 16) FM_LAUNCH(k_attn_f32<16>, grid, a);
+    if (a.Dh <= 32) FM_LAUNCH(k_attn_f32<32>, grid, a);
+    FM_LAUNCH(k_attn_f32<F32_DH>, grid, a);
   }
   return hipErrorInvalidValue;
 }

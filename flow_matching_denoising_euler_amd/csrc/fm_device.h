@@ -1097,9 +1097,8 @@ struct OutSmem {
 // One tail work item vb = (64-row tile, 64-column embedding slice).  COH: its
 // inputs (final norm operand, x, the previous velocity) and outputs come
 // from and go to other workgroups of the same launch (device-scope accesses).
-template <int ACT, int WE, int NB, bool COH>
+template <int ACT, int WE, int NB, bool COH, int UPW = 4>
 __device__ __forceinline__ void out_body(const OutArgs& o, int vb, OutSmem& sm) {
-  constexpr int UPW = 4;
   auto& red = sm.red;
   auto& s_rstd = sm.s_rstd;
   auto& s_x = sm.s_x;

@@ -56,10 +56,12 @@ __global__ __launch_bounds__(512) void k_embed(EmbedArgs e) {
 // Step tail: final norm + action head + Euler (or Heun stage) update, then
 // the next evaluation's embedding.  Workgroup (m-tile, 64-column slice): every slice recomputes the
 // 64 x A head tile (K = d) and embeds its own columns.
-template <int ACT, int WE, int NB>
+// UPW: k-units of 32 per wave (fp32 tiles up to d = 256 take one: four
+// fp32 units per wave do not fit the registers)
+template <int ACT, int WE, int NB, int UPW>
 __global__ __launch_bounds__(512) void k_out(OutArgs o) {
   __shared__ OutSmem sm;
-  out_body<ACT, WE, NB, false>(o, blockIdx.x, sm);
+  out_body<ACT, WE, NB, false, UPW>(o, blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -384,11 +386,15 @@ hipError_t launch_out(int act, int wt_out, const OutArgs& o, hipStream_t st) {
   if ((o.d >> 5) > GW * 4) return hipErrorInvalidValue;
   (void)wt_out;
   if (act == ELT_F32) {
-    if (o.A == 32) FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 2>), grid, 512, o);
-    FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 1>), grid, 512, o);
+    if ((o.d >> 5) <= GW) {
+      if (o.A == 32) FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 2, 1>), grid, 512, o);
+      FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 1, 1>), grid, 512, o);
+    }
+    if (o.A == 32) FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 2, 4>), grid, 512, o);
+    FM_LAUNCH_N((k_out<ELT_F32, ELT_F32, 1, 4>), grid, 512, o);
   }
-  if (o.A == 32) FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 2>), grid, 512, o);
-  FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 1>), grid, 512, o);
+  if (o.A == 32) FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 2, 4>), grid, 512, o);
+  FM_LAUNCH_N((k_out<ELT_BF16, ELT_BF16, 1, 4>), grid, 512, o);
 }
 
 hipError_t launch_embed(int act, const EmbedArgs& e, hipStream_t st) {
