@@ -1071,9 +1071,11 @@ struct EmbedCol {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int lr = (tid_x() >> 6) + 8 * i, r = m0 + lr;
+      // (columns a >= A hold zeros in s_x and in w: no per-column test, which
+      // would put every LDS read behind its own branch)
       float acc = 0.f;
 #pragma unroll
-      for (int a = 0; a < 32; ++a) acc += (a < A ? s_x[lr][a] : 0.f) * w[a];
+      for (int a = 0; a < 32; ++a) acc += s_x[lr][a] * w[a];
       const bool st = has_state && (r % S) == 0;
       const float hv = (r < M) ? (st ? hsv[i] : acc + bias) : 0.f;
       float q = hv * hv;
