@@ -431,9 +431,14 @@ __device__ __forceinline__ void rstd_finish(const float4 (&q)[4], int M, int m0,
   if ((tid & 7) == 0) s_rstd[tid >> 3] = (m0 + (tid >> 3) < M) ? rsqrtf(s * inv_d + eps) : 0.f;
 }
 
+// Row stride (floats) of the cross-wave reduction tiles: the 16-lane groups
+// of an accumulator store or load sit 4 rows apart, and 4 x 36 = 144 = 16
+// (mod 64 banks) puts the four groups on disjoint banks (a stride of 33 put
+// them 4 banks apart: four-way conflicts)
+constexpr int RED_LD = 36;
 // sum of the GW waves' accumulators in a fixed order: red[w] = acc(w+4) + acc(w), then ((r0+r1)+r2)+r3
 template <int NB>
-__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[4][NB], float (*red)[64][33]) {
+__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[4][NB], float (*red)[64][RED_LD]) {
   const int lane = tid_x() & 63, wave = tid_x() >> 6;
   if (wave >= 4) {
 #pragma unroll
@@ -614,7 +619,7 @@ struct SkinnyTile {
 
 // LDS of one skinny GEMM work item
 struct GemmSmem {
-  float red[4][64][33];
+  float red[4][64][RED_LD];
   float s_rstd[64];
   float s_col[3][32];  // per column: bias or alpha, gnext, fp8 scale
   int s_last;
@@ -1091,7 +1096,7 @@ struct EmbedCol {
 
 // LDS of one tail work item
 struct OutSmem {
-  float red[4][64][33];
+  float red[4][64][RED_LD];
   float s_rstd[64];
   float s_x[64][33];
 };
