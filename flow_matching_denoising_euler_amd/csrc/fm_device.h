@@ -921,6 +921,28 @@ __device__ __forceinline__ void big_compute(const uint8_t* base, f32x4 (&acc)[TN
   }
 }
 
+// Workgroups past an LDS-staged GEMM's tile grid: read the byte ranges
+// g.pf (packed weights of the GEMMs that follow) 16 bytes a lane, workgroup
+// j of n taking the blocks of NT * 16 bytes j, j + n, ..., so that the front
+// of each range (its GEMM's first k-slices, read first) arrives first.  The
+// values are discarded; the lines stay in the last-level cache.
+template <int NT>
+__device__ __forceinline__ void big_weight_prefetch(const GemmArgs& g, int j, int n, int tid) {
+  uint32_t acc = 0;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint4* p = (const uint4*)g.pf[m];
+    const long n16 = g.pf_bytes[m] >> 4;
+    if (!p) continue;
+#pragma unroll 8
+    for (long i = (long)j * NT + tid; i < n16; i += (long)n * NT) {
+      const uint4 v = p[i];
+      acc ^= v.x ^ v.w;
+    }
+  }
+  asm volatile("" ::"v"(acc));  // the loaded values are used: the loads stay
+}
+
 // ---------------------------------------------------------------------------
 // Attention of the suffix queries over [prefix (logical order) | suffix]
 // ---------------------------------------------------------------------------

@@ -528,6 +528,25 @@ GemmArgs gemm_args(const fm_ctx* x, int k, int l, int phase) {
     g.u_out = last ? x->uf : (w8 ? x->u_mx : x->u);
     g.ssq_out = last ? x->ssqf : x->ssq;
   }
+  if (x->M >= 256 && x->act == ELT_BF16) {
+    // the LDS-staged GEMMs (256 rows and more): their idle CUs prefetch the
+    // weights of the GEMMs that follow into the last-level cache.  O: the
+    // first half of the gate/up weights (its first k-slices; the whole of
+    // them stretches the O launch by more than it saves); gate/up: down;
+    // down: the next layer's QKV and O (layer 0's after the last, for the
+    // next step).  The QKV GEMM has no idle CUs at these sizes.
+    const long ew = (long)elt_size(x->wt);
+    const LayerW& wn = x->lw[(l + 1) % x->L];
+    g.pf_cus = x->n_cu;
+    if (phase == FM_PHASE_OPROJ) {
+      g.pf[0] = w.wgu; g.pf_bytes[0] = (long)x->F * x->d * ew;
+    } else if (phase == FM_PHASE_GATEUP) {
+      g.pf[0] = w.wd; g.pf_bytes[0] = (long)x->d * x->F * ew;
+    } else if (phase == FM_PHASE_DOWN) {
+      g.pf[0] = wn.wqkv; g.pf_bytes[0] = (long)x->Nqkv * x->d * ew;
+      g.pf[1] = wn.wo; g.pf_bytes[1] = (long)x->d * x->Hq * x->Dh * ew;
+    }
+  }
   return g;
 }
 

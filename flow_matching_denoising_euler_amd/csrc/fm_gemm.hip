@@ -38,6 +38,10 @@ __global__ __launch_bounds__(256 * KG) void k_gemm_big(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: fragment choice and LDS address are scalar
   const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = g.N / BN, T = tiles_m * tiles_n;
+  if ((int)blockIdx.x >= T) {  // a prefetching workgroup (the whole workgroup)
+    big_weight_prefetch<NT>(g, (int)blockIdx.x - T, (int)gridDim.x - T, tid);
+    return;
+  }
   // XCD-aware order: workgroups b, b + 8, ... run on one XCD; give each XCD
   // a contiguous range of tiles, m fastest, so it shares weight columns
   int t = blockIdx.x;
@@ -193,7 +197,8 @@ template <bool WF8>
 static bool gemm_big(int epi, const GemmArgs& g, hipStream_t st, hipError_t* err) {
   const BigPlan p = big_plan(epi, g.M, g.N, g.K, WF8);
   if (!p.used || g.ksplit != 1) return false;
-  const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
+  int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
+  if ((g.pf[0] || g.pf[1]) && g.pf_cus > grid) grid = g.pf_cus;  // prefetchers on the idle CUs
   if (p.mid) {
     if (epi == EPI_GELU) hipLaunchKernelGGL((k_gemm_big<EPI_GELU, 2, 4, 2, 2, WF8>), dim3(grid), dim3(512), 0, st, g);
     else if (epi == EPI_QKV) hipLaunchKernelGGL((k_gemm_big<EPI_QKV, 2, WF8 ? 2 : 1, 1, 2, WF8>), dim3(grid), dim3(256), 0, st, g);

@@ -67,6 +67,10 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void k_gemm_mx(GemmArgs g) {
   const int kg = wave / NW, wg = wave % NW, tg = tid % NTG;  // k-group, wave and thread within it
   const int wm = wg / WN, wn = wg % WN;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = g.N / BN, T = tiles_m * tiles_n;
+  if ((int)blockIdx.x >= T) {  // a prefetching workgroup (the whole workgroup)
+    big_weight_prefetch<NT>(g, (int)blockIdx.x - T, (int)gridDim.x - T, tid);
+    return;
+  }
   // XCD-aware order (workgroups b, b + 8, ... share an XCD): contiguous tile
   // ranges per XCD.  One operand is read by every XCD, the other split
   // between them: m fastest splits the weights (each XCD reads all of the
@@ -289,7 +293,8 @@ hipError_t launch_gemm_mx(int epi, const GemmArgs& g, bool amx, bool omx, hipStr
   const MxPlan p = mx_plan(epi);
   if (g.K % 128 || g.N % p.BN || g.M < 1 || g.mtiles * 64 < g.M) return hipErrorInvalidValue;
   if (omx && (epi == EPI_QKV || g.N % 128)) return hipErrorInvalidValue;  // runs of whole 128-k tiles
-  const int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
+  int grid = (g.M + p.BM - 1) / p.BM * (g.N / p.BN);
+  if ((g.pf[0] || g.pf[1]) && g.pf_cus > grid) grid = g.pf_cus;  // prefetchers on the idle CUs
 #define FM_MX(E, WM_, WN_, TMW_, TNW_, KG_, A_, O_) \
   hipLaunchKernelGGL((k_gemm_mx<E, WM_, WN_, TMW_, TNW_, KG_, A_, O_>), dim3(grid), dim3(64 * WM_ * WN_ * KG_), 0, st, g)
   if (epi == EPI_GELU) {

@@ -59,6 +59,12 @@ struct GemmArgs {
   void* krow;             // EPI_QKVR: K and V also as rows [b][S][Hkv*Dh]
   void* vrow;             //   (sequence b at b * row_bstride elements)
   long row_bstride;
+  // LDS-staged GEMM: workgroups past the tile grid, up to pf_cus in all, read
+  // these byte ranges (packed weights of the GEMMs that follow), so that they
+  // wait in the last-level cache; null: none
+  const void* pf[2];
+  long pf_bytes[2];
+  int pf_cus;
 };
 
 // K/V storage ("kv layout").  A key block of NK keys (NK a multiple of 32)

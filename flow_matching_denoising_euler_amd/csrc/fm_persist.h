@@ -93,6 +93,10 @@ __device__ __forceinline__ GemmArgs load_gemm(const KAS GemmArgs* s) {
   CP(ssq); CP(P); CP(inv_d); CP(eps); CP(out); d.bias = load_tab(&s->bias); CP(ksuf); CP(vsuf); CP(S); CP(SP);
   CP(Hq); CP(Hkv); CP(Dh); CP(h); d.alpha = load_tab(&s->alpha); d.gnext = load_tab(&s->gnext); CP(u_out);
   CP(ssq_out); CP(step); CP(krow); CP(vrow); CP(row_bstride);
+  for (int i = 0; i < 2; ++i) {
+    CP(pf[i]); CP(pf_bytes[i]);
+  }
+  CP(pf_cus);
   return d;
 }
 __device__ __forceinline__ AttnArgs load_attn(const KAS AttnArgs* s) {
@@ -115,7 +119,7 @@ __device__ __forceinline__ OutArgs load_out(const KAS OutArgs* s) {
   return d;
 }
 #undef CP
-static_assert(sizeof(Tab) == 16 && sizeof(GemmArgs) == 240 && sizeof(AttnArgs) == 256 && sizeof(OutArgs) == 240,
+static_assert(sizeof(Tab) == 16 && sizeof(GemmArgs) == 280 && sizeof(AttnArgs) == 256 && sizeof(OutArgs) == 240,
               "the field-wise loaders above copy every field");
 
 // a GEMM's arguments at layer l and time row `step`
